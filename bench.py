@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-decode path on one MI355X.
+
+A step is one decode token (M = 1) through every layer of the workload: per
+layer the route kernel (combine + residual + RMSNorm + router GEMV), the
+grouped gate_up dequant-GEMV with SwiGLU over the k chosen experts, and the
+grouped down dequant-GEMV - replayed from one captured HIP graph per token.
+Each token gets a fresh N(0,1) bf16 hidden state; all inputs and weights are
+resident in HBM before the timed region.  W untimed warmup tokens, then K
+timed tokens bracketed by stream events and device synchronisation.
+
+Prints one JSON line: the expert-path HBM rate (algorithmic packed-weight
+bytes of the chosen experts plus the router weights, over GPU time), the
+per-kernel roofline figure of the dominant kernel (gate_up), the measured
+streaming-read rate, and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published peak
+METRIC = "expert-path HBM GB/s (% of peak) + us/token, gpt-oss-20B-shape MoE at M=1"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def expert_bytes(cfg):
+    """Packed bytes (codes + scales + zeros) of one expert's gate_up and down."""
+    def mat(n, k):
+        codes = n * k // 2
+        if cfg.fmt == "mxfp4":
+            return codes + n * (k // 32)
+        groups = k // cfg.group
+        return codes + n * groups * 2 + n * ((groups + 1) // 2)
+    return mat(2 * cfg.inter, cfg.hidden), mat(cfg.hidden, cfg.inter)
+
+
+def router_bytes(cfg):
+    return cfg.n_experts * cfg.hidden * 4 + (cfg.n_experts * 4 if cfg.hot_experts else 0)
+
+
+def step_bytes(cfg, unique_experts_per_layer):
+    gu, dn = expert_bytes(cfg)
+    return sum(router_bytes(cfg) + u * (gu + dn) for u in unique_experts_per_layer)
+
+
+def cpu_baseline(cfg, sample_layers, token):
+    """The oracle as it stands, token-major, on `sample_layers` layers of one token.
+
+    Packed weights of the sampled layers are generated first (untimed), the
+    oracle then dequantizes the chosen experts on demand and runs its float64
+    layer; the per-layer time is scaled to a whole token.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import formats, moe as omoe
+
+    log(f"cpu baseline: generating {sample_layers} layers of packed weights (untimed)")
+    gen = []
+    for l in range(sample_layers):
+        w_r, b_r, _ = synth.router(cfg, l)
+        experts = [synth.expert_weights(cfg, l, e) for e in range(cfg.n_experts)]
+        gen.append((w_r, b_r, experts))
+    x = synth.hidden(cfg, token)[0][None, :].astype(np.float64)
+    log("cpu baseline: timing the oracle")
+    t0 = time.perf_counter()
+    for l in range(sample_layers):
+        w_r, b_r, experts = gen[l]
+
+        def get(e, experts=experts):
+            w = experts[e]
+            if cfg.fmt == "mxfp4":
+                return formats.mxfp4_dequant(*w["gu"]), formats.mxfp4_dequant(*w["dn"])
+            return (formats.int4g_dequant(*w["gu"], cfg.group),
+                    formats.int4g_dequant(*w["dn"], cfg.group))
+        res = omoe.moe_layer(x, w_r, get, cfg.top_k, bias=b_r, norm=cfg.norm, residual=cfg.norm)
+        x = res["y"]
+    dt = time.perf_counter() - t0
+    per_token_s = dt / sample_layers * cfg.n_layers
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    nbytes = step_bytes(cfg, [cfg.top_k] * cfg.n_layers)
+    return {
+        "value": round(nbytes / per_token_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "us_per_token": round(per_token_s * 1e6, 1),
+        "sample": (f"{sample_layers} of {cfg.n_layers} layers of token {token} (M=1), "
+                   f"{dt:.1f} s of CPU time, scaled to a whole token; float64 NumPy, "
+                   f"elementwise dequant on one thread, BLAS matvecs on {blas_threads}"),
+    }
+
+
+def stream_read_rate(torch, bdg, dev, gbytes=4.0, reps=5):
+    n = int(gbytes * (1 << 30)) // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    rates = []
+    for _ in range(reps + 1):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        bdg.stream_read(buf)
+        b.record()
+        b.synchronize()
+        rates.append(n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return max(rates[1:]), statistics.median(rates[1:])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="gptoss20b_stack")
+    ap.add_argument("--cpu-sample-layers", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-read", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the expert decode runs on one MI355X; see the sharding notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_dequant_gemv_amd as bdg
+    import synth
+    from synth import device as sdev
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.workload]
+    if cfg.m != 1:
+        raise SystemExit("bench.py times the M=1 workloads")
+    K, W = args.steps, args.warmup
+
+    t0 = time.time()
+    layers = []
+    for l in range(cfg.n_layers):
+        layers.append(sdev.upload_layer(cfg, l, dev, threads=16))
+        if l % 6 == 5 or l == cfg.n_layers - 1:
+            log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.1f} s)")
+    plan, _ = sdev.build_plan(cfg, dev, max_m=1, layers=layers)
+    x_all, _ = sdev.hidden_device(cfg, range(W + K), dev)
+    x_buf = torch.empty_like(x_all[0])
+    y_buf = torch.empty(cfg.hidden, dtype=torch.float32, device=dev)
+
+    for t in range(W):
+        x_buf.copy_(x_all[t])
+        bdg.moe_expert_decode(plan, x_buf, y=y_buf)
+    torch.cuda.synchronize()
+    log(f"warmup done ({W} tokens)")
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for t in range(W, W + K):
+        x_buf.copy_(x_all[t])                  # the next token's hidden state lands in the input buffer
+        bdg.moe_expert_decode(plan, x_buf, y=y_buf)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = start.elapsed_time(end)
+    if not torch.isfinite(y_buf).all():
+        raise SystemExit("non-finite output")
+    nbytes = step_bytes(cfg, [cfg.top_k] * cfg.n_layers)       # M=1: k distinct experts per layer
+    value = nbytes * K / (gpu_ms * 1e-3) / 1e9
+    log(f"timed {K} tokens: {gpu_ms / K * 1e3:.1f} us/token GPU, {wall / K * 1e6:.1f} us/token wall, "
+        f"{value:.1f} GB/s")
+
+    # per-kernel durations, same kernels and grids, start/stop events at each kernel
+    acc = None
+    for t in range(W, W + K):
+        x_buf.copy_(x_all[t])
+        acc = bdg.moe_expert_decode_profiled(plan, x_buf, y_buf, *(acc if acc else (None, None)))
+    kms, kcnt = acc
+    kernels = {}
+    for i, name in enumerate(bdg.KERNEL_KINDS):
+        if kcnt[i]:
+            kernels[name] = {"avg_us": round(kms[i] / kcnt[i] * 1e3, 3), "launches": int(kcnt[i])}
+    gu_bytes, dn_bytes = expert_bytes(cfg)
+    gu_launch_bytes = cfg.top_k * gu_bytes
+    gu_avg_s = kms[1] / kcnt[1] * 1e-3
+    achieved = gu_launch_bytes / gu_avg_s / 1e9
+    kernels["gate_up"]["GBps"] = round(achieved, 1)
+    kernels["down"]["GBps"] = round(cfg.top_k * dn_bytes / (kms[2] / kcnt[2] * 1e-3) / 1e9, 1)
+    kernels["route"]["GBps"] = round(router_bytes(cfg) / (kms[0] / kcnt[0] * 1e-3) / 1e9, 1)
+    sum_kernel_us = sum(kms[i] for i in range(4)) / K * 1e3
+    log(f"per-kernel: {kernels}; kernel time {sum_kernel_us:.1f} us/token of {gpu_ms / K * 1e3:.1f}")
+
+    stream = None
+    if not args.no_stream_read:
+        best, med = stream_read_rate(torch, bdg, dev)
+        stream = {"best_GBps": round(best, 1), "median_GBps": round(med, 1), "bytes": "4 GiB"}
+        log(f"stream read: best {best:.1f} GB/s, median {med:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_sample_layers, token=0)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(gpu_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "fmt": cfg.fmt, "layers": cfg.n_layers, "hidden": cfg.hidden, "inter": cfg.inter,
+            "experts": cfg.n_experts, "top_k": cfg.top_k, "m": 1,
+            "bytes_per_token": nbytes, "timing": "HIP graph per token, stream-ordered",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "us_per_token": round(gpu_ms / K * 1e3, 2),
+        "wall_us_per_token": round(wall / K * 1e6, 2),
+        "roofline": {
+            "kernel": "moe_gateup_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+        },
+        "kernels": kernels,
+        "kernel_us_per_token": round(sum_kernel_us, 2),
+        "stream_read": stream,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

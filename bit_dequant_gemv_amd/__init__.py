@@ -1,0 +1,15 @@
+"""MI355X-native sparse-MoE expert decode over MXFP4 / packed-int4 weights.
+
+The compute lives in ``libbdg.so`` (HIP kernels for gfx950, C ABI in
+``include/bdg.h``); this package is its thin Python binding.
+"""
+
+from .api import (KERNEL_KINDS, MoEPlan, QWeight, int4g_dequant, moe_expert_decode,
+                  moe_expert_decode_profiled, moe_experts_routed,
+                  moe_router_topk, mxfp4_dequant, qgemv, stream_copy, stream_read, version)
+
+__all__ = [
+    "KERNEL_KINDS", "MoEPlan", "QWeight", "int4g_dequant", "moe_expert_decode",
+    "moe_expert_decode_profiled", "moe_experts_routed",
+    "moe_router_topk", "mxfp4_dequant", "qgemv", "stream_copy", "stream_read", "version",
+]

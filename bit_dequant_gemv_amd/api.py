@@ -1,0 +1,249 @@
+"""Thin torch-facing wrappers over libbdg, one per C entry point, same names.
+
+Torch supplies device memory and the current HIP stream; every step of the
+computation runs in the HIP kernels of ``libbdg.so``.  Nothing here computes
+on the CPU, and there is no fallback path.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (BDG_BF16, BDG_F32, BDG_FMT_INT4G, BDG_FMT_MXFP4, BDG_MOE_NO_GRAPH,
+                   BDG_MOE_STACK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, check)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _x_dtype(x):
+    if x.dtype == torch.float32:
+        return BDG_F32
+    if x.dtype == torch.bfloat16:
+        return BDG_BF16
+    raise ValueError("activations must be float32 or bfloat16")
+
+
+class QWeight:
+    """A packed matrix [n][k], or a batch of experts [E][n][k], in the PLAIN layout.
+
+    MXFP4: codes uint8 [..., n, k/2], scales uint8 [..., n, k/32].
+    INT4G: codes uint8 [..., n, k/2], scales int16 (fp16 bits) [..., n, k/group],
+           zeros uint8 [..., n, ceil(k/group/2)].
+    """
+
+    def __init__(self, fmt, codes, scales, zeros=None, group=32):
+        if fmt not in ("mxfp4", "int4g"):
+            raise ValueError("fmt must be 'mxfp4' or 'int4g'")
+        self.fmt = fmt
+        self.codes, self.scales, self.zeros = codes, scales, zeros
+        self.group = 32 if fmt == "mxfp4" else int(group)
+        self.n = codes.shape[-2]
+        self.k = 2 * codes.shape[-1]
+        self.batched = codes.dim() == 3
+        self.n_experts = codes.shape[0] if self.batched else 1
+        _dev_ptr(codes, "codes", torch.uint8)
+        _dev_ptr(scales, "scales", torch.uint8 if fmt == "mxfp4" else torch.int16)
+        if fmt == "int4g":
+            _dev_ptr(zeros, "zeros", torch.uint8)
+
+    def qmat(self):
+        def stride(t):
+            return t[0].numel() * t.element_size() if (t is not None and self.batched) else 0
+        return QMat(
+            fmt=BDG_FMT_MXFP4 if self.fmt == "mxfp4" else BDG_FMT_INT4G,
+            group=self.group, n=self.n, k=self.k,
+            codes=self.codes.data_ptr(), scales=self.scales.data_ptr(),
+            zeros=self.zeros.data_ptr() if self.zeros is not None else None,
+            expert_stride_codes=stride(self.codes), expert_stride_scales=stride(self.scales),
+            expert_stride_zeros=stride(self.zeros))
+
+
+def mxfp4_dequant(codes, scales, out_dtype=torch.float32):
+    n, half_k = codes.shape
+    out = torch.empty((n, 2 * half_k), dtype=out_dtype, device=codes.device)
+    odt = BDG_F32 if out_dtype == torch.float32 else BDG_BF16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    check("mxfp4_dequant", _lib.load().mxfp4_dequant(
+        _dev_ptr(codes, "codes", torch.uint8), _dev_ptr(scales, "scales", torch.uint8),
+        n, 2 * half_k, _dev_ptr(out, "out"), odt, _stream()))
+    return out
+
+
+def int4g_dequant(codes, scales, zeros, group):
+    n, half_k = codes.shape
+    out = torch.empty((n, 2 * half_k), dtype=torch.float32, device=codes.device)
+    check("int4g_dequant", _lib.load().int4g_dequant(
+        _dev_ptr(codes, "codes", torch.uint8), _dev_ptr(scales, "scales", torch.int16),
+        _dev_ptr(zeros, "zeros", torch.uint8), n, 2 * half_k, int(group),
+        _dev_ptr(out, "out"), _stream()))
+    return out
+
+
+def qgemv(w: QWeight, x, out=None):
+    """y = W x for x [k] or [m][k]; returns fp32 [n] or [m][n]."""
+    squeeze = x.dim() == 1
+    x2 = x.reshape(1, -1) if squeeze else x
+    m = x2.shape[0]
+    if x2.shape[1] != w.k:
+        raise ValueError("x and W disagree on K")
+    y = out if out is not None else torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    qm = w.qmat()
+    check("qgemv", _lib.load().qgemv(ctypes.byref(qm), _dev_ptr(x2, "x"), _x_dtype(x2), m,
+                                     _dev_ptr(y, "y", torch.float32), _stream()))
+    return y[0] if squeeze and out is None else y
+
+
+def moe_router_topk(x, w_r, b_r=None, topk=4, rmsnorm=False, eps=1e-5):
+    """(idx [m][k] int32, wts [m][k] fp32, logits [m][E] fp32)."""
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    m, h = x2.shape
+    e = w_r.shape[0]
+    idx = torch.empty((m, topk), dtype=torch.int32, device=x.device)
+    wts = torch.empty((m, topk), dtype=torch.float32, device=x.device)
+    logits = torch.empty((m, e), dtype=torch.float32, device=x.device)
+    check("moe_router_topk", _lib.load().moe_router_topk(
+        _dev_ptr(x2, "x"), _x_dtype(x2), _dev_ptr(w_r, "w_r", torch.float32),
+        _dev_ptr(b_r, "b_r", torch.float32), m, h, e, topk,
+        BDG_ROUTER_RMSNORM if rmsnorm else 0, float(eps),
+        _dev_ptr(idx, "idx"), _dev_ptr(wts, "wts"), _dev_ptr(logits, "logits"), _stream()))
+    return idx, wts, logits
+
+
+class MoEPlan:
+    """A decode plan (moe_plan_create) over per-layer device weights.
+
+    layers: list of dicts with keys w_router [E][H] fp32, b_router [E] fp32 or
+    None, gate_up QWeight [E][2I][H], down QWeight [E][H][I].  The plan keeps
+    references to every tensor it points at.
+    """
+
+    def __init__(self, layers, hidden, inter, n_experts, top_k, fmt="mxfp4", group=32,
+                 stack=True, norm_eps=1e-5, max_m=1, use_graph=True):
+        self._layers = layers
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+        self.n_layers = len(layers)
+        self.stack = stack
+        self.max_m = max_m
+        arr = (LayerDesc * len(layers))()
+        for i, L in enumerate(layers):
+            arr[i].w_router = _dev_ptr(L["w_router"], "w_router", torch.float32).value
+            b = L.get("b_router")
+            arr[i].b_router = _dev_ptr(b, "b_router", torch.float32).value if b is not None else None
+            arr[i].gate_up = L["gate_up"].qmat()
+            arr[i].down = L["down"].qmat()
+        flags = (BDG_MOE_STACK if stack else 0) | (0 if use_graph else BDG_MOE_NO_GRAPH)
+        desc = MoEDesc(n_layers=len(layers), hidden=hidden, inter=inter, n_experts=n_experts,
+                       top_k=top_k, fmt=BDG_FMT_MXFP4 if fmt == "mxfp4" else BDG_FMT_INT4G,
+                       group=32 if fmt == "mxfp4" else group, flags=flags,
+                       norm_eps=norm_eps, max_m=max_m, layers=arr)
+        handle = ctypes.c_void_p()
+        check("moe_plan_create", _lib.load().moe_plan_create(ctypes.byref(desc), ctypes.byref(handle)))
+        self._handle = handle
+        self._desc_layers = arr
+
+    @property
+    def handle(self):
+        if self._handle is None:
+            raise RuntimeError("plan is closed")
+        return self._handle
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None:
+            _lib.load().moe_plan_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_expert_decode(plan: MoEPlan, x, y=None, traces=False):
+    """One decode step of x [m][H]; returns y [m][H] fp32 (and traces if asked).
+
+    traces=True also returns dict(topk [L][m][k] int32, wts [L][m][k] fp32,
+    resid [L][m][H] fp32), the per-layer routing and input residual.
+    """
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, plan.hidden), dtype=torch.float32, device=x.device)
+    tr = None
+    if traces:
+        L, k, H = plan.n_layers, plan.top_k, plan.hidden
+        tr = dict(topk=torch.empty((L, m, k), dtype=torch.int32, device=x.device),
+                  wts=torch.empty((L, m, k), dtype=torch.float32, device=x.device),
+                  resid=torch.empty((L, m, H), dtype=torch.float32, device=x.device))
+    check("moe_expert_decode", _lib.load().moe_expert_decode(
+        plan.handle, _dev_ptr(x2, "x"), _x_dtype(x2), m, _dev_ptr(y, "y", torch.float32),
+        _dev_ptr(tr["topk"], "topk") if tr else None,
+        _dev_ptr(tr["wts"], "wts") if tr else None,
+        _dev_ptr(tr["resid"], "resid") if tr else None, _stream()))
+    return (y, tr) if traces else y
+
+
+def moe_experts_routed(plan: MoEPlan, layer, x, idx, wts, y=None):
+    """Experts of one layer with fixed routing: y[t] = sum_j wts[t][j] FFN_{idx[t][j]}(x[t])."""
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, plan.hidden), dtype=torch.float32, device=x.device)
+    check("moe_experts_routed", _lib.load().moe_experts_routed(
+        plan.handle, int(layer), _dev_ptr(x2, "x"), _x_dtype(x2), m,
+        _dev_ptr(idx, "idx", torch.int32), _dev_ptr(wts, "wts", torch.float32),
+        _dev_ptr(y, "y", torch.float32), _stream()))
+    return y
+
+
+KERNEL_KINDS = ("route", "gate_up", "down", "finish")
+
+
+def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None):
+    """One decode step with per-kernel start/stop events; accumulates into
+    acc_ms / acc_count (ctypes double[4] / int64[4]) and returns them."""
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    if acc_ms is None:
+        acc_ms = (ctypes.c_double * 4)()
+        acc_count = (ctypes.c_int64 * 4)()
+    check("moe_expert_decode_profiled", _lib.load().moe_expert_decode_profiled(
+        plan.handle, _dev_ptr(x2, "x"), _x_dtype(x2), x2.shape[0], _dev_ptr(y, "y", torch.float32),
+        acc_ms, acc_count, _stream()))
+    return acc_ms, acc_count
+
+
+def stream_read(buf, n_blocks=0):
+    """Read every byte of buf with 16-byte loads; returns the per-block sink."""
+    nb = n_blocks if n_blocks > 0 else 2048
+    sink = torch.empty(nb, dtype=torch.float32, device=buf.device)
+    check("bdg_stream_read", _lib.load().bdg_stream_read(
+        _dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"), nb, _stream()))
+    return sink
+
+
+def stream_copy(src, dst):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    check("bdg_stream_copy", _lib.load().bdg_stream_copy(
+        _dev_ptr(src, "src"), _dev_ptr(dst, "dst"), nbytes, _stream()))
+
+
+def version():
+    return _lib.load().bdg_version().decode()

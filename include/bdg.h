@@ -1,0 +1,240 @@
+/*
+ * bdg.h - C ABI of libbdg, sparse-MoE expert decode over low-bit packed
+ * weights on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is one decode step of a mixture-of-experts layer (or a stack
+ * of them) at small M: router top-k, then for each chosen expert a fused
+ * dequant-GEMV over its packed gate_up weights, SwiGLU, a fused dequant-GEMV
+ * over its packed down weights, and the router-weighted combine.  It is the
+ * expert path of the pages:
+ *   - "Sovereign gpt-oss-20B (MXFP4) on Apple Silicon": MXFP4 experts, the
+ *     MXFP4 dequant-GEMV kernel (section 1), per token a router and 4
+ *     sequential experts x 2 GEMVs per layer (section 3 Results), and the
+ *     un-built lever of running the K active experts together (section 5);
+ *   - "Single-stream int4 decode of a 30B MoE on Apple Silicon": packed int4
+ *     weights dequantized on chip (sections 1 and 6);
+ *   - "Amortizing the per-token host-sync setup tax in fused all-layer q4
+ *     decode on Apple M1 Ultra": per-session setup tables rebuilt only on a
+ *     geometry change (section 3), GPU-side top-k;
+ *   - the TinyTitan project-tracker history, entries D108/D110 (fused int4
+ *     dequant-inside-matmul, 16-byte row loads) and D114 (a layer's experts
+ *     in one submission).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must be device memory (hipMalloc /
+ *     torch CUDA tensors); the caller owns every weight, input and output
+ *     buffer and must keep them alive while work that uses them is queued.
+ *     The library never frees or copies caller weights.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Calls only enqueue work on it and never synchronise, except
+ *     moe_plan_create / moe_plan_destroy, which may allocate, free and
+ *     synchronise.
+ *   - Return value: BDG_OK (0) or a negative BDG_E_* status.  Argument
+ *     errors are found on the host before anything is enqueued, and leave
+ *     outputs untouched.  Faults inside kernels surface at the caller's next
+ *     synchronisation of the stream.
+ *   - Layout (PLAIN, the interchange layout): row-major, K contiguous.
+ *       MXFP4: codes [n][k/2] bytes, two FP4 E2M1 codes per byte, the low
+ *              nibble holds the even K index; scales [n][k/32] E8M0 bytes,
+ *              one per 32 contiguous K-elements of a row (OCP MX v1.0).
+ *       INT4G: codes [n][k/2] bytes (unsigned q, low nibble = even k);
+ *              scales [n][k/group] fp16; zeros [n][ceil(k/group/2)] bytes,
+ *              two unsigned zero points per byte along the group axis, low
+ *              nibble = even group.  w = (q - z) * s.
+ *     Code rows are k/2 bytes; code bases and expert strides must be
+ *     16-byte aligned (BDG_E_ALIGN otherwise).
+ *   - Numerics: dequantized weights are exact (bit-exact with the IEEE fp32
+ *     product, subnormals kept); dot products accumulate in fp32 in a fixed
+ *     order, so repeated calls give identical bits.
+ */
+#ifndef BDG_H
+#define BDG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define BDG_OK 0
+#define BDG_E_INVALID -1     /* bad shape, dtype, flag, count or NULL pointer */
+#define BDG_E_ALIGN -2       /* a code buffer or stride is not 16-byte aligned */
+#define BDG_E_UNSUPPORTED -3 /* valid request outside what the kernels cover */
+#define BDG_E_HIP -4         /* a HIP runtime call or kernel launch failed */
+#define BDG_E_NOMEM -5       /* device allocation failed */
+
+/* ---- activation dtypes ---- */
+#define BDG_F32 0
+#define BDG_BF16 1
+
+/* ---- weight formats ---- */
+#define BDG_FMT_MXFP4 0
+#define BDG_FMT_INT4G 1
+
+/* Limits of the kernels (BDG_E_UNSUPPORTED beyond them). */
+#define BDG_MAX_K 8192       /* reduction length of one GEMV row */
+#define BDG_MAX_M 16         /* tokens per call */
+#define BDG_MAX_EXPERTS 1024
+#define BDG_MAX_TOPK 32
+
+/* A packed low-bit matrix [n][k] in the PLAIN layout, optionally one of a
+ * batch of experts laid out at fixed byte strides. */
+typedef struct bdg_qmat {
+  int32_t fmt;     /* BDG_FMT_MXFP4 or BDG_FMT_INT4G */
+  int32_t group;   /* MXFP4: 32; INT4G: group size, a multiple of 32 */
+  int64_t n;       /* rows (outputs) */
+  int64_t k;       /* columns (reduction), a multiple of 32 and of group */
+  const void* codes;   /* device, [n][k/2] bytes */
+  const void* scales;  /* device, MXFP4 [n][k/32] bytes, INT4G [n][k/group] fp16 */
+  const void* zeros;   /* device, INT4G [n][ceil(k/group/2)] bytes; NULL for MXFP4 */
+  int64_t expert_stride_codes;   /* bytes from expert e to e+1 (0 if single) */
+  int64_t expert_stride_scales;
+  int64_t expert_stride_zeros;
+} bdg_qmat;
+
+/* mxfp4_dequant - decode an MXFP4 matrix to fp32 (or bf16).
+ * Defines the weight values every other call multiplies with: element
+ * (r, c) = E2M1(code) * 2^(e - 127), E8M0 e = 255 giving NaN (OCP MX v1.0;
+ * the MXFP4 reader of the gpt-oss page, section 3, is bit-exact).
+ * codes [n][k/2], scales [n][k/32] as in the PLAIN layout; out [n][k] of
+ * out_dtype (BDG_F32: bit-exact IEEE product, subnormals kept, +-inf on
+ * overflow; BDG_BF16: that value rounded to nearest even).  k % 32 == 0. */
+int mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                  void* out, int32_t out_dtype, void* stream);
+
+/* int4g_dequant - decode a group-quantized int4 matrix to fp32:
+ * out[r][c] = (q - z) * s (on-chip int4 dequantisation of the 30B int4
+ * page, section 6; fused-kernel identity of tracker entry D108).  Exact.
+ * codes [n][k/2], scales_f16 [n][k/group], zeros [n][ceil(k/group/2)],
+ * out [n][k] fp32; group % 32 == 0, k % group == 0. */
+int int4g_dequant(const uint8_t* codes, const uint16_t* scales_f16, const uint8_t* zeros,
+                  int64_t n, int64_t k, int32_t group, float* out, void* stream);
+
+/* qgemv - fused dequant-GEMV: y[t][r] = sum_c W[r][c] * x[t][c] for t < m
+ * (the MXFP4 dequant-GEMV of the gpt-oss page, section 1, with 16-byte
+ * coalesced loads and on-chip dequant, section 4).  W is read packed, never
+ * materialised.  x [m][k] of x_dtype (BDG_F32 or BDG_BF16), device;
+ * y [m][n] fp32, device.  1 <= m <= BDG_MAX_M, k <= BDG_MAX_K.  W's expert
+ * strides are ignored (expert 0). */
+int qgemv(const bdg_qmat* w, const void* x, int32_t x_dtype, int32_t m, float* y,
+          void* stream);
+
+/* moe_router_topk - router GEMV + top-k + softmax over the chosen k.
+ * logits[t][e] = sum_h W_r[e][h] * xin[t][h] (+ b_r[e]), computed in fp32;
+ * idx[t][0..k) = the k largest logits in descending order, ties to the
+ * lower expert index; wts[t][j] = exp(l_j - l_0) / sum_j' exp(l_j' - l_0).
+ * xin = x, or RMSNorm(x) = x / sqrt(mean(x^2) + eps) (unit gain) when flags
+ * has BDG_ROUTER_RMSNORM.  The GPU top-k of the host-sync page, section 3.
+ * x [m][h] of x_dtype, w_r [e][h] fp32, b_r [e] fp32 or NULL; idx [m][k]
+ * int32, wts [m][k] fp32, logits [m][e] fp32 or NULL - all device. */
+#define BDG_ROUTER_RMSNORM 1
+int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r, const float* b_r,
+                    int32_t m, int32_t h, int32_t e, int32_t topk, int32_t flags,
+                    float norm_eps, int32_t* idx, float* wts, float* logits, void* stream);
+
+/* ---- MoE decode plans ---- */
+
+/* Per-layer weights: router [E][H] fp32 (+ optional bias [E]); gate_up is a
+ * batch of E experts of [2I][H] (rows 0..I-1 are the gate g, rows I..2I-1
+ * the up projection u); down is a batch of E experts of [I -> H], i.e.
+ * [H][I].  All device pointers owned by the caller. */
+typedef struct bdg_layer_desc {
+  const float* w_router;
+  const float* b_router;   /* NULL: no bias */
+  bdg_qmat gate_up;
+  bdg_qmat down;
+} bdg_layer_desc;
+
+/* flags for bdg_moe_desc.flags */
+#define BDG_MOE_STACK 1      /* x <- x + MoE(RMSNorm(x)) per layer; else bare layers: x <- MoE(x) */
+#define BDG_MOE_NO_GRAPH 2   /* launch the per-token kernels directly instead of replaying a graph
+                                (same kernels, same results; for A/B checks) */
+
+typedef struct bdg_moe_desc {
+  int32_t n_layers;
+  int32_t hidden;      /* H */
+  int32_t inter;       /* I */
+  int32_t n_experts;   /* E */
+  int32_t top_k;       /* k */
+  int32_t fmt;         /* BDG_FMT_MXFP4 or BDG_FMT_INT4G (all layers alike) */
+  int32_t group;       /* 32 for MXFP4; int4 group size */
+  int32_t flags;       /* BDG_MOE_* */
+  float norm_eps;      /* RMSNorm eps (stack only), e.g. 1e-5 */
+  int32_t max_m;       /* largest m a decode call will pass, <= BDG_MAX_M */
+  const bdg_layer_desc* layers;   /* n_layers entries; copied at create */
+} bdg_moe_desc;
+
+typedef struct bdg_plan bdg_plan;
+
+/* moe_plan_create - validate a model geometry once and build what every
+ * decode step reuses: device tables of per-layer, per-expert weight
+ * addresses, the workspace (residual, routing, intermediate activations),
+ * and a cache of captured per-token HIP graphs.  The session-keyed setup
+ * cache of the host-sync page (section 3): nothing of this is rebuilt per
+ * token; a change of any weight pointer, shape or flag needs a new plan.
+ * Allocates device memory; synchronous.  *out receives the plan. */
+int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out);
+
+/* moe_plan_destroy - free a plan and everything it allocated; waits for
+ * work queued on its internal stream.  NULL is accepted. */
+int moe_plan_destroy(bdg_plan* p);
+
+/* moe_expert_decode - one decode step of m tokens through every layer of
+ * the plan.  x [m][H] of x_dtype (device) is the input hidden state; y [m][H]
+ * fp32 (device) receives the output: for a stack, the residual stream after
+ * the last layer; for a bare layer, the combine sum_j w_j * down_j(h_j).
+ * Optional device traces (NULL to skip): topk_trace [L][m][k] int32 with
+ * each layer's chosen experts, wts_trace [L][m][k] fp32 with their weights,
+ * resid_trace [L][m][H] fp32 with each layer's input residual (stack) or
+ * input (bare layer).  The per-token path is replayed from a captured HIP
+ * graph keyed on (x, y, traces, m, x_dtype), captured at the first call with
+ * that key.  A plan is not re-entrant: calls on one plan must be ordered on
+ * one stream. */
+int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
+                      int32_t* topk_trace, float* wts_trace, float* resid_trace, void* stream);
+
+/* moe_experts_routed - the expert part of one layer with caller-fixed
+ * routing: y[t] = sum_j wts[t][j] * FFN_{idx[t][j]}(x[t]) (no router, no
+ * norm, no residual).  Runs the same grouped gate_up/SwiGLU and down kernels
+ * as moe_expert_decode.  x [m][H] of x_dtype, idx [m][k] int32 in [0, E),
+ * wts [m][k] fp32, y [m][H] fp32, all device.  Expert ids are not range
+ * checked on the host (they live on the device): out-of-range ids are
+ * clamped to E-1 by the kernels. */
+int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int32_t x_dtype, int32_t m,
+                       const int32_t* idx, const float* wts, float* y, void* stream);
+
+/* ---- measurement aids ---- */
+
+/* moe_expert_decode_profiled - one decode step exactly as moe_expert_decode
+ * computes it (same kernels, same grids), launched directly rather than from
+ * a graph, with a start/stop event pair recorded by the runtime at each
+ * kernel's start and end.  Adds each kernel's duration (ms) to
+ * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route, 1 = gate_up
+ * (+SwiGLU), 2 = down, 3 = finish (host arrays of 4).  Synchronises on the
+ * last event before returning.  Used by the benchmark for per-kernel
+ * roofline figures. */
+int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
+                               double* kernel_ms, int64_t* kernel_count, void* stream);
+
+/* bdg_stream_read - read `bytes` (a multiple of 16) of device memory with
+ * 16-byte coalesced loads and write one fp32 checksum per workgroup into
+ * sink [n_blocks] (device).  n_blocks <= 0 picks the default grid.  Used to
+ * measure the achievable HBM read rate next to the decode path. */
+int bdg_stream_read(const void* buf, int64_t bytes, float* sink, int32_t n_blocks, void* stream);
+
+/* bdg_stream_copy - copy `bytes` (a multiple of 16) device to device with
+ * 16-byte loads/stores; a kernel of known traffic for calibrating counters. */
+int bdg_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* bdg_strerror - static text for a status code. */
+const char* bdg_strerror(int32_t status);
+
+/* bdg_version - library version string. */
+const char* bdg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDG_H */

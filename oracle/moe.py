@@ -150,9 +150,10 @@ def check_routing(logits_row, scale_row, idx_gpu, k, rel=NEAR_TIE_REL):
         ties += 1
     # the order must be descending up to the band
     for a, b in zip(idx_gpu[:-1], idx_gpu[1:]):
-        if logits_row[a] < logits_row[b] and not near_tie(logits_row, scale_row, a, b, rel):
+        inverted = logits_row[a] < logits_row[b] or (logits_row[a] == logits_row[b] and a > b)
+        if inverted and not near_tie(logits_row, scale_row, a, b, rel):
             return False, ties, f"order {a} before {b} violates the logits"
-        if logits_row[a] < logits_row[b]:
+        if inverted:
             ties += 1
     return True, ties, ""
 

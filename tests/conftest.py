@@ -27,3 +27,11 @@ def dev():
     if not torch.cuda.is_available():
         pytest.fail("GPU test selected but no GPU is visible")
     return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _gpu_banner(request):
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stdout__.write(f"[gpu-test] {request.node.nodeid}\n")
+        sys.__stdout__.flush()
+    yield
