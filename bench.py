@@ -102,7 +102,9 @@ def cpu_baseline(cfg, sample_layers, token):
     }
 
 
-def stream_read_rate(torch, bdg, dev, gbytes=4.0, reps=5):
+def stream_read_rate(torch, bdg, dev, phase_bytes, gbytes=4.0, reps=5):
+    """Streaming-read rate over 4 GiB, and back-to-back reads of phase-sized
+    slices (distinct data) - the floor of a kernel that only reads that much."""
     n = int(gbytes * (1 << 30)) // 16 * 16
     buf = torch.empty(n, dtype=torch.uint8, device=dev)
     buf.fill_(1)
@@ -115,8 +117,34 @@ def stream_read_rate(torch, bdg, dev, gbytes=4.0, reps=5):
         b.record()
         b.synchronize()
         rates.append(n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    phases = {}
+    sink = torch.empty(1024, dtype=torch.float32, device=dev)
+    for name, nb in phase_bytes.items():
+        nb = nb // 256 * 256
+        cnt = min(64, n // nb)
+        views = [buf[i * nb:(i + 1) * nb] for i in range(cnt)]
+        # back-to-back reads of distinct slices replayed from a graph, so the
+        # figure is the GPU's and not the host's launch rate
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                for v in views:
+                    bdg.stream_read(v, n_blocks=1024, sink=sink)
+        torch.cuda.current_stream().wait_stream(stream)
+        graph.replay()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        b.synchronize()
+        us = a.elapsed_time(b) * 1e3 / cnt
+        del graph
+        phases[name] = {"bytes": nb, "us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
     del buf
-    return max(rates[1:]), statistics.median(rates[1:])
+    return max(rates[1:]), statistics.median(rates[1:]), phases
 
 
 def main():
@@ -210,9 +238,12 @@ def main():
 
     stream = None
     if not args.no_stream_read:
-        best, med = stream_read_rate(torch, bdg, dev)
-        stream = {"best_GBps": round(best, 1), "median_GBps": round(med, 1), "bytes": "4 GiB"}
-        log(f"stream read: best {best:.1f} GB/s, median {med:.1f} GB/s")
+        best, med, phases = stream_read_rate(
+            torch, bdg, dev, {"gate_up": gu_launch_bytes, "down": cfg.top_k * dn_bytes,
+                              "router": router_bytes(cfg)})
+        stream = {"best_GBps": round(best, 1), "median_GBps": round(med, 1), "bytes": "4 GiB",
+                  "phase_sized_reads": phases}
+        log(f"stream read: best {best:.1f} GB/s, median {med:.1f} GB/s; phase-sized: {phases}")
 
     cpu = None
     if not args.no_cpu_baseline:

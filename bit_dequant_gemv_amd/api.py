@@ -212,7 +212,7 @@ def moe_experts_routed(plan: MoEPlan, layer, x, idx, wts, y=None):
     return y
 
 
-KERNEL_KINDS = ("route", "gate_up", "down", "finish")
+KERNEL_KINDS = ("route", "gate_up", "down")
 
 
 def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None):
@@ -228,10 +228,13 @@ def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None)
     return acc_ms, acc_count
 
 
-def stream_read(buf, n_blocks=0):
+def stream_read(buf, n_blocks=0, sink=None):
     """Read every byte of buf with 16-byte loads; returns the per-block sink."""
     nb = n_blocks if n_blocks > 0 else 2048
-    sink = torch.empty(nb, dtype=torch.float32, device=buf.device)
+    if sink is None:
+        sink = torch.empty(nb, dtype=torch.float32, device=buf.device)
+    elif sink.numel() < nb:
+        raise ValueError("sink too small")
     check("bdg_stream_read", _lib.load().bdg_stream_read(
         _dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"), nb, _stream()))
     return sink

@@ -20,6 +20,38 @@ constexpr int kWave = 64;
 constexpr int kChunkElems = 32;     // elements per 16-byte code chunk
 constexpr int kXStride = 36;        // LDS floats per staged x chunk (32 + 4 pad)
 
+// ---------------------------------------------------------------- global loads
+
+// Loads through explicit global (address space 1) pointers: pointers read
+// from a device table are generic to the compiler, which would otherwise emit
+// flat loads.  Callers pass in-bounds addresses and issue these loads
+// unconditionally (no branch around a load), so the compiler waits for a
+// load's data only at its first use.
+#define BDG_GLOBAL __attribute__((address_space(1)))
+
+typedef unsigned int bdg_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int bdg_u32x2 __attribute__((ext_vector_type(2)));
+typedef float bdg_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ldg_u128(const void* p) {
+  const bdg_u32x4 v = *reinterpret_cast<const BDG_GLOBAL bdg_u32x4*>(reinterpret_cast<uintptr_t>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ldg_u8(const void* p) {
+  return *reinterpret_cast<const BDG_GLOBAL uint8_t*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ uint32_t ldg_u16(const void* p) {
+  return *reinterpret_cast<const BDG_GLOBAL uint16_t*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ float4 ldg_f4(const void* p) {
+  const bdg_f32x4 v = *reinterpret_cast<const BDG_GLOBAL bdg_f32x4*>(reinterpret_cast<uintptr_t>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ldg_u64(const void* p) {
+  const bdg_u32x2 v = *reinterpret_cast<const BDG_GLOBAL bdg_u32x2*>(reinterpret_cast<uintptr_t>(p));
+  return make_uint2(v.x, v.y);
+}
+
 // ---------------------------------------------------------------- scalars
 
 // E8M0 byte -> fp32 2^(e-127).  e = 0 is the fp32 subnormal 2^-127,
@@ -117,7 +149,17 @@ __device__ __forceinline__ float fp4_chunk_dot(const uint4 q, const float* __res
 }
 
 // int4: sum_i q_i * x_i over one 16-byte chunk (32 unsigned nibbles).
+// A nibble q placed in a byte reads as the FP8 E4M3 value q * 2^-9 exactly
+// (exponent field 0 is the subnormal m * 2^-9, exponent field 1 gives
+// (8 + m) * 2^-9), so v_cvt_scalef32_pk_f32_fp8 with scale 2^9 turns two
+// nibble bytes into two exact fp32 integers.  The even elements of a dword
+// are its low-nibble plane, the odd ones its high-nibble plane.
 // The zero point is folded by the caller: sum (q - z) x = sum q x - z sum x.
+template <bool HI_WORD>
+__device__ __forceinline__ f32x2 u4_pair(uint32_t plane) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(plane, 512.0f, HI_WORD);
+}
+
 __device__ __forceinline__ float u4_chunk_dot(const uint4 q, const float* __restrict__ x) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -125,14 +167,18 @@ __device__ __forceinline__ float u4_chunk_dot(const uint4 q, const float* __rest
   for (int d = 0; d < 4; ++d) {
     const uint32_t lo = w[d] & 0x0F0F0F0Fu;          // elements 8d + 0, 2, 4, 6
     const uint32_t hi = (w[d] >> 4) & 0x0F0F0F0Fu;   // elements 8d + 1, 3, 5, 7
-    a0 = __builtin_fmaf((float)(lo & 0xFFu), x[8 * d + 0], a0);
-    a1 = __builtin_fmaf((float)(hi & 0xFFu), x[8 * d + 1], a1);
-    a2 = __builtin_fmaf((float)((lo >> 8) & 0xFFu), x[8 * d + 2], a2);
-    a3 = __builtin_fmaf((float)((hi >> 8) & 0xFFu), x[8 * d + 3], a3);
-    a0 = __builtin_fmaf((float)((lo >> 16) & 0xFFu), x[8 * d + 4], a0);
-    a1 = __builtin_fmaf((float)((hi >> 16) & 0xFFu), x[8 * d + 5], a1);
-    a2 = __builtin_fmaf((float)(lo >> 24), x[8 * d + 6], a2);
-    a3 = __builtin_fmaf((float)(hi >> 24), x[8 * d + 7], a3);
+    const f32x2 e02 = u4_pair<false>(lo);
+    const f32x2 e46 = u4_pair<true>(lo);
+    const f32x2 e13 = u4_pair<false>(hi);
+    const f32x2 e57 = u4_pair<true>(hi);
+    a0 = __builtin_fmaf(e02.x, x[8 * d + 0], a0);
+    a1 = __builtin_fmaf(e13.x, x[8 * d + 1], a1);
+    a2 = __builtin_fmaf(e02.y, x[8 * d + 2], a2);
+    a3 = __builtin_fmaf(e13.y, x[8 * d + 3], a3);
+    a0 = __builtin_fmaf(e46.x, x[8 * d + 4], a0);
+    a1 = __builtin_fmaf(e57.x, x[8 * d + 5], a1);
+    a2 = __builtin_fmaf(e46.y, x[8 * d + 6], a2);
+    a3 = __builtin_fmaf(e57.y, x[8 * d + 7], a3);
   }
   return (a0 + a1) + (a2 + a3);
 }

@@ -31,33 +31,38 @@ template <int FMT, int S>
 struct GroupLoad {
   uint4 q[S];
   uint32_t sc[S];
-  uint32_t zn[S];
+  uint32_t zn[S];   // int4: the byte holding the zero point
+  uint32_t ok;      // bit s: slot s holds a real chunk of a real row
+  uint32_t zhi;     // bit s: int4 zero point in the high nibble
 };
 
-// Load the slots of one row for this lane.  row_ok false -> zeros.
+// Load the slots of one row for this lane.  Branch-free: a row past the end
+// (row_ok false) reads row 0 and a chunk past the end reads the row's last
+// chunk, so every load is in bounds and issued unconditionally; row_dot gives
+// such slots a neutral scale and their x registers are zero, so they add 0,
+// and results of rows past the end are never stored.
 template <int FMT, int L, int S>
 __device__ __forceinline__ void load_row(GroupLoad<FMT, S>& ld, const QMat& m, const QGeom& g,
                                          int64_t row, bool row_ok, int li) {
+  // offsets inside one matrix fit 32 bits (the plan checks matrix sizes)
+  const uint32_t r = row_ok ? (uint32_t)row : 0u;
+  ld.ok = 0;
+  ld.zhi = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int c = li + L * s;
     const bool ok = row_ok && c < g.chunks;
-    if (ok) {
-      const uint8_t* p = m.codes + row * (int64_t)(g.chunks * 16) + (int64_t)c * 16;
-      ld.q[s] = *reinterpret_cast<const uint4*>(p);
-      if constexpr (FMT == kMXFP4) {
-        ld.sc[s] = m.scales[row * (int64_t)g.chunks + c];
-        ld.zn[s] = 0;
-      } else {
-        const int gi = (c * kChunkElems) / g.group;
-        ld.sc[s] = reinterpret_cast<const uint16_t*>(m.scales)[row * (int64_t)g.groups + gi];
-        const uint32_t zb = m.zeros[row * (int64_t)g.zrow + (gi >> 1)];
-        ld.zn[s] = (gi & 1) ? (zb >> 4) : (zb & 15u);
-      }
+    const uint32_t cc = (uint32_t)(c < g.chunks ? c : g.chunks - 1);
+    ld.ok |= (ok ? 1u : 0u) << s;
+    ld.q[s] = ldg_u128(m.codes + (r * (uint32_t)g.chunks + cc) * 16u);
+    if constexpr (FMT == kMXFP4) {
+      ld.sc[s] = ldg_u8(m.scales + r * (uint32_t)g.chunks + cc);
+      ld.zn[s] = 0;
     } else {
-      ld.q[s] = make_uint4(0u, 0u, 0u, 0u);
-      ld.sc[s] = 0u;
-      ld.zn[s] = 0u;
+      const uint32_t gi = (cc * kChunkElems) / (uint32_t)g.group;
+      ld.sc[s] = ldg_u16(m.scales + (r * (uint32_t)g.groups + gi) * 2u);
+      ld.zn[s] = ldg_u8(m.zeros + r * (uint32_t)g.zrow + (gi >> 1));
+      ld.zhi |= (gi & 1u) << s;
     }
   }
 }
@@ -105,17 +110,103 @@ template <int FMT, int L, int S>
 __device__ __forceinline__ float row_dot(const GroupLoad<FMT, S>& ld, const XRegs<FMT, L, S>& xr) {
   float acc = 0.f;
 #pragma unroll
-  for (int s = 0; s < S; ++s) acc += chunk_contrib<FMT>(ld.q[s], ld.sc[s], ld.zn[s], xr.v[s], xr.sum[s]);
+  for (int s = 0; s < S; ++s) {
+    const bool ok = (ld.ok >> s) & 1u;
+    // neutral scale for padding slots: E8M0 127 = 1.0, fp16 0x3C00 = 1.0
+    const uint32_t sc = ok ? ld.sc[s] : (FMT == kMXFP4 ? 127u : 0x3C00u);
+    const uint32_t z = (ld.zn[s] >> (((ld.zhi >> s) & 1u) * 4u)) & 15u;
+    acc += chunk_contrib<FMT>(ld.q[s], sc, z, xr.v[s], xr.sum[s]);
+  }
   return group_sum<L>(acc);
 }
 
-// Stage x (fp32 or bf16, times an optional scalar) into the LDS chunk layout.
-__device__ __forceinline__ void stage_x(float* __restrict__ lds_x, const void* x, int x_is_bf16,
-                                        int64_t offset, int k, float mult) {
-  for (int i = threadIdx.x; i < k; i += blockDim.x) {
-    float v = x_is_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[offset + i])
-                        : reinterpret_cast<const float*>(x)[offset + i];
-    lds_x[(i >> 5) * kXStride + (i & 31)] = v * mult;
+// Stage n fp32 values (times `mult`) from global memory into the LDS chunk
+// layout.  Values are split into `per`-long vectors placed `region` floats
+// apart in LDS (several expert inputs at once); per % 32 == 0.  NV float4
+// loads per thread are issued before any LDS store, so a block pays the
+// memory latency once per NV * nthreads * 4 values, not once per value.
+template <int NV>
+__device__ __forceinline__ void stage_f32(float* __restrict__ lds_x, const float* __restrict__ src, int n,
+                                          int per, int region, float mult, int tid, int nthreads) {
+  for (int base = 0; base < n; base += NV * nthreads * 4) {
+    float4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = base + (i * nthreads + tid) * 4;
+      v[i] = ldg_f4(src + (idx < n ? idx : n - 4));   // in bounds; unused past n
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = base + (i * nthreads + tid) * 4;
+      if (idx < n) {
+        const int rgn = idx / per;
+        const int w = idx - rgn * per;
+        float4 o = v[i];
+        o.x *= mult;
+        o.y *= mult;
+        o.z *= mult;
+        o.w *= mult;
+        *reinterpret_cast<float4*>(lds_x + rgn * region + (w >> 5) * kXStride + (w & 31)) = o;
+      }
+    }
+  }
+}
+
+// Two-phase staging for n <= NV * nthreads * 4 values: load() issues all the
+// global loads (call it before anything whose data should arrive later, so
+// the in-order vmcnt wait for these loads does not also wait for that), and
+// store() writes them into the LDS chunk layout as stage_f32 does.
+template <int NV>
+struct StageF32 {
+  float4 v[NV];
+
+  __device__ __forceinline__ void load(const float* __restrict__ src, int n, int tid, int nthreads) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (i * nthreads + tid) * 4;
+      v[i] = ldg_f4(src + (idx < n ? idx : n - 4));   // in bounds; unused past n
+    }
+  }
+
+  __device__ __forceinline__ void store(float* __restrict__ lds_x, int n, int per, int region, float mult, int tid,
+                                        int nthreads) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (i * nthreads + tid) * 4;
+      if (idx < n) {
+        const int rgn = idx / per;
+        const int w = idx - rgn * per;
+        float4 o = v[i];
+        o.x *= mult;
+        o.y *= mult;
+        o.z *= mult;
+        o.w *= mult;
+        *reinterpret_cast<float4*>(lds_x + rgn * region + (w >> 5) * kXStride + (w & 31)) = o;
+      }
+    }
+  }
+};
+
+// The same for a bf16 source (4 values per 8-byte load), one region.
+template <int NV>
+__device__ __forceinline__ void stage_bf16(float* __restrict__ lds_x, const uint16_t* __restrict__ src, int n,
+                                           int tid, int nthreads) {
+  for (int base = 0; base < n; base += NV * nthreads * 4) {
+    uint2 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = base + (i * nthreads + tid) * 4;
+      v[i] = ldg_u64(src + (idx < n ? idx : n - 4));   // in bounds; unused past n
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = base + (i * nthreads + tid) * 4;
+      if (idx < n) {
+        const float4 o = make_float4(bf16_to_f32((uint16_t)(v[i].x & 0xFFFFu)), bf16_to_f32((uint16_t)(v[i].x >> 16)),
+                                     bf16_to_f32((uint16_t)(v[i].y & 0xFFFFu)), bf16_to_f32((uint16_t)(v[i].y >> 16)));
+        *reinterpret_cast<float4*>(lds_x + (idx >> 5) * kXStride + (idx & 31)) = o;
+      }
+    }
   }
 }
 

@@ -23,7 +23,11 @@ qgemv_kernel(QMat w, QGeom g, int64_t n_rows, const void* __restrict__ x, int x_
   const int li = lane % L;
   const int rr = lane / L;
 
-  stage_x(lds_x, x, x_bf16, (int64_t)t * g.k, g.k, 1.0f);
+  if (x_bf16)
+    stage_bf16<4>(lds_x, reinterpret_cast<const uint16_t*>(x) + (int64_t)t * g.k, g.k, threadIdx.x, kGemvThreads);
+  else
+    stage_f32<4>(lds_x, reinterpret_cast<const float*>(x) + (int64_t)t * g.k, g.k, g.k, 0, 1.0f, threadIdx.x,
+                 kGemvThreads);
   __syncthreads();
   XRegs<FMT, L, S> xr;
   xr.load(lds_x, g.chunks, li);
@@ -103,6 +107,7 @@ extern "C" int qgemv(const bdg_qmat* w, const void* x, int32_t x_dtype, int32_t 
   if (!x || !y || m < 1) return BDG_E_INVALID;
   if (m > BDG_MAX_M) return BDG_E_UNSUPPORTED;
   if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
+  if (!aligned16(x)) return BDG_E_ALIGN;
   QMat qm{static_cast<const uint8_t*>(w->codes), static_cast<const uint8_t*>(w->scales),
           static_cast<const uint8_t*>(w->zeros)};
   QGeom g;

@@ -1,5 +1,5 @@
 // Sparse-MoE expert decode: router, top-k, grouped gate_up + SwiGLU,
-// grouped down, router-weighted combine (+ RMSNorm residual stack).
+// grouped down + router-weighted combine (+ RMSNorm residual stack).
 //
 // Per layer the pages run a router and then the chosen experts one after
 // another, two small GEMVs each, one submission per GEMV ("Sovereign
@@ -8,18 +8,21 @@
 // is named there as the untried lever (section 5), and the TinyTitan tracker
 // moves a layer's experts into one submission (entry D114).  Here each layer
 // is three kernels, each over ALL chosen experts of the layer:
-//   route  : combine of the previous layer + residual, RMSNorm, router GEMV
-//   gate_up: top-k + softmax (every block, from the logits), then the
-//            grouped gate_up dequant-GEMV of all k experts with the SwiGLU
-//            epilogue h = silu(g) * u
-//   down   : grouped down dequant-GEMV of all k experts -> d_j
-// and the combine y = x + sum_j w_j d_j is folded into the next layer's
-// route kernel (or a final finish kernel).  A whole token is one captured
-// HIP graph (per-token setup amortised as in the host-sync page, section 3).
+//   route  : RMSNorm statistics of the layer input and the router GEMV, one
+//            router row per wavefront, the row's loads issued before the
+//            input is staged;
+//   gate_up: every wavefront computes the top-k + softmax itself from the
+//            logits, issues the loads of all its (g, u) row pairs at once,
+//            then stages x and runs the grouped dequant-GEMV of all k
+//            experts with the SwiGLU epilogue h = silu(g) * u;
+//   down   : one block per row block, one wavefront per chosen expert:
+//            grouped dequant-GEMV over h, then the router-weighted combine
+//            and the residual add in LDS, in a fixed expert order.
+// A whole token is one captured HIP graph (the per-token setup amortised as
+// in the host-sync page, section 3).
+#include <hip/hip_ext.h>
 #include <stdlib.h>
 #include <string.h>
-
-#include <hip/hip_ext.h>
 
 #include <new>
 
@@ -30,7 +33,9 @@ namespace bdg {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRouteRowsPerBlock = 8;
+constexpr int kDownWaves = 8;        // waves per down block
+constexpr int kGuPairsPerWave = 6;   // gate_up: (g, u) row pairs in flight per wave
+constexpr int kRouteMaxF4 = 16;      // router row float4 per lane (H <= 4096)
 
 // Weight addresses of one layer, kept in a device table by the plan.
 struct LayerDev {
@@ -55,16 +60,11 @@ __device__ __forceinline__ QMat expert_dn(const LayerDev& L, int e) {
               L.dn_zeros ? L.dn_zeros + (int64_t)e * L.dn_sz : nullptr};
 }
 
-// x_new = (residual ? x_prev : 0) + sum_j w_j d_j, in fixed j order.  Used by
-// both the route kernel (next layer's input) and the finish kernel (output),
-// so the two agree bit for bit.
-__device__ __forceinline__ float combine_elem(const float* __restrict__ x_prev, const float* __restrict__ d,
-                                              const float* __restrict__ w, int K, int H, int t, int h,
-                                              int residual) {
-  float v = residual ? x_prev[(int64_t)t * H + h] : 0.f;
-  for (int j = 0; j < K; ++j) v = __builtin_fmaf(w[t * K + j], d[((int64_t)t * K + j) * H + h], v);
-  return v;
+__device__ __forceinline__ int uniform_wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
 }
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
 // ---------------------------------------------------------------- top-k
 
@@ -72,130 +72,179 @@ __device__ __forceinline__ bool better(float a, int ea, float b, int eb) {
   return a > b || (a == b && ea < eb);
 }
 
-// One wavefront: the K largest of row[0..E) (descending, ties -> lower index)
-// and softmax weights over them.  Lane j < K writes pick j to out_idx/out_w.
-__device__ void wave_topk(const float* __restrict__ row, int E, int K, int* out_idx, float* out_w) {
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Floats of wave-private LDS scratch wave_topk needs for E experts.
+__host__ __device__ constexpr int topk_scratch_floats(int E) { return E + 2 * BDG_MAX_TOPK; }
+
+// One wavefront: the K largest of row[0..E) in descending order, ties to the
+// lower index, and softmax weights over them.  Each value's rank is the
+// number of values before it in the order (larger, or equal with a lower
+// index); the values with rank < K are the picks, in rank order.  NaN ranks
+// as -inf.  Lane j < K receives pick j in (out_e, out_w); other lanes get
+// (0, 0).  V = values per lane (E <= 64V); scr = wave-private LDS.
+template <int V>
+__device__ __forceinline__ void topk_load(const float* row, int E, float (&v)[V]) {
   const int lane = threadIdx.x & (kWave - 1);
-  constexpr int V = BDG_MAX_EXPERTS / kWave;
-  float v[V];
-  uint32_t taken = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int e = lane + kWave * i;
-    v[i] = e < E ? row[e] : -INFINITY;
-    if (e >= E) taken |= 1u << i;
-  }
-  float my_l = 0.f;
-  int my_e = 0;
-  for (int j = 0; j < K; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int e = lane + kWave * i;
-      if (!((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) {
-      const float ov = __shfl_xor(bv, msk);
-      const int oe = __shfl_xor(be, msk);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be >= E) be = E - 1;   // only when every remaining logit is NaN
-    if (lane == (be & (kWave - 1))) taken |= 1u << (be / kWave);
-    if (lane == j) {
-      my_l = bv;
-      my_e = be;
-    }
-  }
-  const float l0 = __shfl(my_l, 0);
-  const float ex = lane < K ? expf(my_l - l0) : 0.f;
-  const float sum = wave_sum(ex);
-  if (lane < K) {
-    out_idx[lane] = my_e;
-    out_w[lane] = ex / sum;
+    v[i] = row[e < E ? e : E - 1];   // in bounds; lanes past E are masked in topk_rank
   }
 }
+
+template <int V>
+__device__ __forceinline__ void topk_rank(float (&v)[V], int E, int K, float* scr, int& out_e, float& out_w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int* pick_e = reinterpret_cast<int*>(scr + E);
+  float* pick_l = scr + E + BDG_MAX_TOPK;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = lane + kWave * i;
+    float x = v[i];
+    if (x != x || e >= E) x = -INFINITY;
+    v[i] = x;
+    if (e < E) scr[e] = x;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < E; ++j) {
+        const float o = scr[j];
+        rank += (o > v[i]) | ((o == v[i]) & (j < e));
+      }
+      if (rank < K) {
+        pick_e[rank] = e;
+        pick_l[rank] = v[i];
+      }
+    }
+  }
+  wave_lds_sync();
+  const int my_e = lane < K ? pick_e[lane] : 0;
+  const float my_l = lane < K ? pick_l[lane] : 0.f;
+  const float l0 = pick_l[0];
+  const float ex = lane < K ? expf(my_l - l0) : 0.f;
+  const float sum = wave_sum(ex);
+  out_e = my_e;
+  out_w = lane < K ? ex / sum : 0.f;
+  wave_lds_sync();
+}
+
+template <int V>
+__device__ __forceinline__ void wave_topk(const float* row, int E, int K, float* scr, int& out_e, float& out_w) {
+  float v[V];
+  topk_load<V>(row, E, v);
+  topk_rank<V>(v, E, K, scr, out_e, out_w);
+}
+
+
 
 // ---------------------------------------------------------------- route
 
 struct RouteParams {
-  int M, H, E, K;
-  int combine;        // 0: x_new = x_in; 1: x_new = combine(x_prev, d_prev, w_prev)
-  int residual;       // combine adds x_prev
+  int M, H, E;
   int norm;           // RMSNorm before routing / experts
   float eps;
   int compute_logits;
-  const void* x_in;
+  const void* x_in;   // [M][H] layer input: caller x (bf16/f32) at layer 0, else the residual buffer
   int x_bf16;
-  const float* x_prev;
-  const float* d_prev;
-  const float* w_prev;
-  float* x_out;        // [M][H], written by block 0
-  float* resid_trace;  // [M][H] or NULL, written by block 0
-  float* r_out;        // [M], written by block 0
-  float* logits;       // [M][E]
+  float* x_copy;      // [M][H] fp32 copy of x_in written by block 0 (layer 0), or NULL
+  float* resid_trace; // [M][H] or NULL, written by block 0
+  float* r_out;       // [M], written by block 0
+  float* logits;      // [M][E]
   const LayerDev* layers;
   int layer;
 };
 
+// One router row per wavefront; block b handles rows 4b .. 4b+3 of token t.
 __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
   extern __shared__ float lds[];
   float* xs = lds;               // [H]
   float* red = lds + p.H;        // [kWaves]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = uniform_wave_id();
+  const int e = blockIdx.x * kWaves + wave;
+  const bool row_ok = p.compute_logits && e < p.E;
+  const LayerDev L = p.layers[p.layer];
 
+  // the router row first: its loads do not depend on x
+  // in-bounds clamped addresses, loads issued unconditionally; entries past
+  // the row end (h >= H) are never used
+  const int ec = e < p.E ? e : p.E - 1;
+  float4 wv[kRouteMaxF4];
+#pragma unroll
+  for (int i = 0; i < kRouteMaxF4; ++i) {
+    const int h = (i * kWave + lane) * 4;
+    wv[i] = ldg_f4(L.w_r + (int64_t)ec * p.H + (h < p.H ? h : p.H - 4));
+  }
   float ss = 0.f;
-  for (int h = threadIdx.x; h < p.H; h += kThreads) {
-    float v;
-    if (p.combine) {
-      v = combine_elem(p.x_prev, p.d_prev, p.w_prev, p.K, p.H, t, h, p.residual);
-    } else {
-      v = p.x_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.x_in)[(int64_t)t * p.H + h])
-                   : reinterpret_cast<const float*>(p.x_in)[(int64_t)t * p.H + h];
+  const int64_t xoff = (int64_t)t * p.H;
+  constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // float4 of x per thread (H <= 4096)
+  float4 xv4[NX];
+  uint2 xb[NX];
+  if (p.x_bf16) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int h = (i * kThreads + threadIdx.x) * 4;
+      xb[i] = ldg_u64(reinterpret_cast<const uint16_t*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
     }
-    xs[h] = v;
-    ss = __builtin_fmaf(v, v, ss);
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+      xv4[i] = make_float4(bf16_to_f32((uint16_t)(xb[i].x & 0xFFFFu)), bf16_to_f32((uint16_t)(xb[i].x >> 16)),
+                           bf16_to_f32((uint16_t)(xb[i].y & 0xFFFFu)), bf16_to_f32((uint16_t)(xb[i].y >> 16)));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int h = (i * kThreads + threadIdx.x) * 4;
+      xv4[i] = ldg_f4(reinterpret_cast<const float*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int h = (i * kThreads + threadIdx.x) * 4;
+    if (h < p.H) {
+      const float4 v = xv4[i];
+      *reinterpret_cast<float4*>(xs + h) = v;
+      ss = __builtin_fmaf(v.x, v.x, ss);
+      ss = __builtin_fmaf(v.y, v.y, ss);
+      ss = __builtin_fmaf(v.z, v.z, ss);
+      ss = __builtin_fmaf(v.w, v.w, ss);
+      if (blockIdx.x == 0) {
+        if (p.x_copy) *reinterpret_cast<float4*>(p.x_copy + xoff + h) = v;
+        if (p.resid_trace) *reinterpret_cast<float4*>(p.resid_trace + xoff + h) = v;
+      }
+    }
   }
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   float r = 1.f;
-  if (p.norm) {
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-    r = 1.0f / sqrtf(tot / (float)p.H + p.eps);
-  }
-  if (blockIdx.x == 0) {
-    for (int h = threadIdx.x; h < p.H; h += kThreads) {
-      p.x_out[(int64_t)t * p.H + h] = xs[h];
-      if (p.resid_trace) p.resid_trace[(int64_t)t * p.H + h] = xs[h];
+  if (p.norm) r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.H + p.eps);
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.r_out[t] = r;
+  if (!row_ok) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRouteMaxF4; ++i) {
+    const int h = (i * kWave + lane) * 4;
+    if (h < p.H) {
+      const float4 xv = *reinterpret_cast<const float4*>(xs + h);
+      acc = __builtin_fmaf(wv[i].x, xv.x * r, acc);
+      acc = __builtin_fmaf(wv[i].y, xv.y * r, acc);
+      acc = __builtin_fmaf(wv[i].z, xv.z * r, acc);
+      acc = __builtin_fmaf(wv[i].w, xv.w * r, acc);
     }
-    if (threadIdx.x == 0) p.r_out[t] = r;
   }
-  if (!p.compute_logits) return;
-  const LayerDev L = p.layers[p.layer];
-  const int e0 = blockIdx.x * kRouteRowsPerBlock;
-  for (int e = e0 + wave; e < e0 + kRouteRowsPerBlock && e < p.E; e += kWaves) {
-    const float* wr = L.w_r + (int64_t)e * p.H;
-    float acc = 0.f;
-    for (int h = lane * 4; h < p.H; h += kWave * 4) {
-      const float4 wv = *reinterpret_cast<const float4*>(wr + h);
-      acc = __builtin_fmaf(wv.x, xs[h] * r, acc);
-      acc = __builtin_fmaf(wv.y, xs[h + 1] * r, acc);
-      acc = __builtin_fmaf(wv.z, xs[h + 2] * r, acc);
-      acc = __builtin_fmaf(wv.w, xs[h + 3] * r, acc);
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) p.logits[(int64_t)t * p.E + e] = acc + (L.b_r ? L.b_r[e] : 0.f);
-  }
+  acc = wave_sum(acc);
+  if (lane == 0) p.logits[(int64_t)t * p.E + e] = acc + (L.b_r ? L.b_r[e] : 0.f);
 }
 
 // ---------------------------------------------------------------- gate_up + SwiGLU
@@ -218,164 +267,177 @@ struct GateUpParams {
   float* h_out;               // [M][K][I]
 };
 
-template <int FMT, int S>
+// Wave gw of token t owns the (expert slot, row pair) range
+// [P*gw/GW, P*(gw+1)/GW) of the P = K*I pairs; the grid makes it <= NP.
+// Lanes 0..31 compute the gate row i, lanes 32..63 the up row I+i.
+template <int FMT, int S, int NP, int V>
 __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
-  constexpr int L = 32;       // a wave-iteration is one (g, u) row pair
+  constexpr int L = 32;
   extern __shared__ float lds[];
   float* xs = lds;                                          // [chunks * kXStride]
-  int* s_idx = reinterpret_cast<int*>(lds + p.g.chunks * kXStride);
-  float* s_w = reinterpret_cast<float*>(s_idx + BDG_MAX_TOPK);
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = uniform_wave_id();
   const int li = lane % L;
   const bool is_up = lane >= L;
+  float* scr = lds + p.g.chunks * kXStride + wave * topk_scratch_floats(p.E);
 
-  if (wave == 0) {
-    if (p.routed) {
-      if (lane < p.K) {
-        int e = p.idx_in[t * p.K + lane];
-        e = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
-        s_idx[lane] = e;
-        s_w[lane] = p.w_in[t * p.K + lane];
-      }
-    } else {
-      wave_topk(p.logits + (int64_t)t * p.E, p.E, p.K, s_idx, s_w);
-    }
+  // load order: routing inputs, then x (independent of the routing), then
+  // the expert weights - the in-order wait for each stays short
+  float lg[V];
+  int my_e = 0;
+  float my_w = 0.f;
+  if (p.routed) {
+    my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
+    my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
+  } else {
+    topk_load<V>(p.logits + (int64_t)t * p.E, p.E, lg);
   }
+  constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // H <= 4096
+  StageF32<NX> xstage;
+  xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
   const float mult = p.r ? p.r[t] : 1.0f;
-  stage_x(xs, p.x, 0, (int64_t)t * p.H, p.H, mult);
-  __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x < p.K) {
-    p.idx_out[t * p.K + threadIdx.x] = s_idx[threadIdx.x];
-    p.w_out[t * p.K + threadIdx.x] = s_w[threadIdx.x];
-    if (p.topk_trace) p.topk_trace[t * p.K + threadIdx.x] = s_idx[threadIdx.x];
-    if (p.wts_trace) p.wts_trace[t * p.K + threadIdx.x] = s_w[threadIdx.x];
+  if (!p.routed) topk_rank<V>(lg, p.E, p.K, scr, my_e, my_w);
+  if (lane >= p.K) {
+    my_e = 0;
+    my_w = 0.f;
   }
+  if (blockIdx.x == 0 && wave == 0 && lane < p.K) {
+    p.idx_out[t * p.K + lane] = my_e;
+    p.w_out[t * p.K + lane] = my_w;
+    if (p.topk_trace) p.topk_trace[t * p.K + lane] = my_e;
+    if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
+  }
+
+  const LayerDev Ld = p.layers[p.layer];
+  const int P = p.K * p.I;
+  const int GW = gridDim.x * kWaves;
+  const int gw = blockIdx.x * kWaves + wave;
+  const int q0 = (int)((int64_t)P * gw / GW);
+  const int q1 = (int)((int64_t)P * (gw + 1) / GW);
+  const int nq = q1 - q0;                 // <= NP pairs for this wave
+  // (slot, row) of q0; later pairs step the row and wrap to the next slot
+  const int j0 = q0 / p.I;
+  const int row0 = q0 - j0 * p.I;
+
+  // every slot loads (a wave short of NP pairs repeats its last pair and
+  // stores nothing for the repeats): no branch around the loads
+  GroupLoad<FMT, S> ld[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int ii = i < nq ? i : (nq > 0 ? nq - 1 : 0);
+    int row = row0 + ii;
+    int j = j0;
+    while (row >= p.I) {                  // NP <= I: at most one wrap in practice
+      row -= p.I;
+      ++j;
+    }
+    if (j >= p.K) j = p.K - 1;
+    const int e = __builtin_amdgcn_readlane(my_e, j);
+    load_row<FMT, L, S>(ld[i], expert_gu(Ld, e), p.g, is_up ? p.I + row : row, true, li);
+  }
+
+  xstage.store(xs, p.H, p.H, 0, mult, threadIdx.x, kThreads);
+  __syncthreads();
   XRegs<FMT, L, S> xr;
   xr.load(xs, p.g.chunks, li);
-  const LayerDev Ld = p.layers[p.layer];
 
-  const int64_t P = (int64_t)p.K * p.I;
-  const int64_t p0 = P * blockIdx.x / gridDim.x;
-  const int64_t p1 = P * (blockIdx.x + 1) / gridDim.x;
-  float* ht = p.h_out + (int64_t)t * p.K * p.I;
-
-  auto load_pair = [&](GroupLoad<FMT, S>& ld, int64_t pi) {
-    const int j = (int)(pi / p.I);
-    const int i = (int)(pi - (int64_t)j * p.I);
-    const QMat m = expert_gu(Ld, s_idx[j]);
-    load_row<FMT, L, S>(ld, m, p.g, is_up ? (int64_t)p.I + i : (int64_t)i, true, li);
-  };
-  auto finish_pair = [&](const GroupLoad<FMT, S>& ld, int64_t pi) {
-    const float d = row_dot<FMT, L, S>(ld, xr);
+  // pair i: lanes 0..31 hold the gate row's dot g_i, lanes 32..63 the up
+  // row's u_i; lane i gathers (g_i, u_i) and SwiGLU runs once per wave
+  float g_sel = 0.f, u_sel = 0.f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const float d = row_dot<FMT, L, S>(ld[i], xr);
     const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 0));
     const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L));
-    if (lane == 0) ht[pi] = gv / (1.0f + expf(-gv)) * uv;
-  };
-
-  GroupLoad<FMT, S> a, b;
-  int64_t pa = p0 + wave;
-  if (pa < p1) load_pair(a, pa);
-  while (pa < p1) {
-    const int64_t pb = pa + kWaves;
-    if (pb < p1) load_pair(b, pb);
-    finish_pair(a, pa);
-    if (pb >= p1) break;
-    const int64_t pc = pb + kWaves;
-    if (pc < p1) load_pair(a, pc);
-    finish_pair(b, pb);
-    pa = pc;
+    if (lane == i) {
+      g_sel = gv;
+      u_sel = uv;
+    }
   }
+  if (lane < nq) p.h_out[(int64_t)t * P + q0 + lane] = g_sel / (1.0f + expf(-g_sel)) * u_sel;
 }
 
-// ---------------------------------------------------------------- down
+// ---------------------------------------------------------------- down + combine
 
 struct DownParams {
   int M, H, I, E, K;
+  int residual;               // add x_prev
   const int32_t* idx;         // [M][K] routing buffer
+  const float* w;             // [M][K]
   const float* h;             // [M][K][I]
+  const float* x_prev;        // [M][H] layer input (residual)
+  float* x_out;               // [M][H] next layer's input, or NULL
+  float* y_out;               // [M][H] caller output, or NULL
   const LayerDev* layers;
   int layer;
   QGeom g;                    // reduction over I
-  int rows_per_block;
-  int blocks_per_expert;
-  float* d_out;               // [M][K][H]
 };
 
-template <int FMT, int L, int S>
-__global__ void __launch_bounds__(kThreads) moe_down_kernel(DownParams p) {
+// Block (rb, t) of 8 waves: WPE = 8 / K waves per chosen expert (1 when
+// K >= 8; experts then go in groups of 8).  Wave w works on expert slot
+// j = jg + w % K' and row groups (w / K'), (w / K') + WPE, ... of the block's
+// B = NR * RPW * WPE rows.  The h_j of a group are staged into LDS by the whole
+// block (loads issued before the expert weights' loads), the partial rows
+// meet in LDS and are combined in slot order with the residual.
+template <int FMT, int L, int S, int NR, int HV>
+__global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams p) {
   constexpr int RPW = kWave / L;
   extern __shared__ float lds[];
+  const int kg = p.K < kDownWaves ? p.K : kDownWaves;      // experts per group
+  const int wpe = kDownWaves / kg;                          // waves per expert
+  const int B = NR * RPW * wpe;
+  const int stride = p.g.chunks * kXStride;
+  float* dpart = lds + kg * stride;                         // [K][B]
   const int t = blockIdx.y;
-  const int j = blockIdx.x / p.blocks_per_expert;
-  const int rb = blockIdx.x - j * p.blocks_per_expert;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = uniform_wave_id();
   const int li = lane % L;
   const int rr = lane / L;
-
-  int e = p.idx[t * p.K + j];
-  e = e < 0 ? 0 : (e >= p.E ? p.E - 1 : e);
-  stage_x(lds, p.h, 0, ((int64_t)t * p.K + j) * p.I, p.I, 1.0f);
-  __syncthreads();
-  XRegs<FMT, L, S> xr;
-  xr.load(lds, p.g.chunks, li);
+  const int r0 = blockIdx.x * B;
+  const int jw = wave % kg;                                 // expert within the group
+  const int sub = wave / kg;                                // row-group phase (sub < wpe, or idle)
+  const bool wave_on = sub < wpe;
   const LayerDev Ld = p.layers[p.layer];
-  const QMat m = expert_dn(Ld, e);
 
-  const int r0 = rb * p.rows_per_block;
-  const int r1 = min(p.H, r0 + p.rows_per_block);
-  const int ng = (r1 - r0 + RPW - 1) / RPW;
-  float* dt = p.d_out + ((int64_t)t * p.K + j) * p.H;
-
-  GroupLoad<FMT, S> a, b;
-  int ga = wave;
-  if (ga < ng) {
-    const int row = r0 + ga * RPW + rr;
-    load_row<FMT, L, S>(a, m, p.g, row, row < r1, li);
+  for (int jg = 0; jg < p.K; jg += kg) {
+    const int nj = min(kg, p.K - jg);
+    const int j = jg + (jw < nj ? jw : nj - 1);
+    const bool active = wave_on && jw < nj;
+    // expert id first, then the h loads, then the expert weights
+    const int e = clamp_expert(p.idx[t * p.K + j], p.E);
+    const int nh = nj * p.I;
+    StageF32<HV> hstage;
+    hstage.load(p.h + ((int64_t)t * p.K + jg) * p.I, nh, threadIdx.x, blockDim.x);
+    GroupLoad<FMT, S> ld[NR];
+    const QMat m = expert_dn(Ld, e);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int row = r0 + (i * wpe + sub) * RPW + rr;
+      load_row<FMT, L, S>(ld[i], m, p.g, row, active && row < p.H, li);
+    }
+    hstage.store(lds, nh, p.I, stride, 1.0f, threadIdx.x, blockDim.x);
+    __syncthreads();
+    if (active) {
+      XRegs<FMT, L, S> xr;
+      xr.load(lds + jw * stride, p.g.chunks, li);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float d = row_dot<FMT, L, S>(ld[i], xr);
+        const int b = (i * wpe + sub) * RPW + rr;
+        if (li == 0 && b < B) dpart[(jg + jw) * B + b] = d;
+      }
+    }
+    __syncthreads();
   }
-  while (ga < ng) {
-    const int gb = ga + kWaves;
-    if (gb < ng) {
-      const int row = r0 + gb * RPW + rr;
-      load_row<FMT, L, S>(b, m, p.g, row, row < r1, li);
-    }
-    {
-      const int row = r0 + ga * RPW + rr;
-      const float d = row_dot<FMT, L, S>(a, xr);
-      if (li == 0 && row < r1) dt[row] = d;
-    }
-    if (gb >= ng) break;
-    const int gc = gb + kWaves;
-    if (gc < ng) {
-      const int row = r0 + gc * RPW + rr;
-      load_row<FMT, L, S>(a, m, p.g, row, row < r1, li);
-    }
-    {
-      const int row = r0 + gb * RPW + rr;
-      const float d = row_dot<FMT, L, S>(b, xr);
-      if (li == 0 && row < r1) dt[row] = d;
-    }
-    ga = gc;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int row = r0 + b;
+    if (row >= p.H) continue;
+    float v = p.residual ? p.x_prev[(int64_t)t * p.H + row] : 0.f;
+    for (int j = 0; j < p.K; ++j) v = __builtin_fmaf(p.w[t * p.K + j], dpart[j * B + b], v);
+    if (p.x_out) p.x_out[(int64_t)t * p.H + row] = v;
+    if (p.y_out) p.y_out[(int64_t)t * p.H + row] = v;
   }
-}
-
-// ---------------------------------------------------------------- finish
-
-struct FinishParams {
-  int M, H, K, residual;
-  const float* x_prev;
-  const float* d;
-  const float* w;
-  float* y;
-};
-
-__global__ void __launch_bounds__(kThreads) moe_finish_kernel(FinishParams p) {
-  const int t = blockIdx.y;
-  const int h = blockIdx.x * kThreads + threadIdx.x;
-  if (h >= p.H) return;
-  p.y[(int64_t)t * p.H + h] = combine_elem(p.x_prev, p.d, p.w, p.K, p.H, t, h, p.residual);
 }
 
 // ---------------------------------------------------------------- plan
@@ -408,10 +470,8 @@ struct GraphEntry {
 
 struct bdg_plan {
   bdg_moe_desc d;
-  int gu_L, gu_S, dn_L, dn_S;
+  int gu_S, dn_L, dn_S, dn_NR, topk_V;
   bdg::QGeom gu_geom, dn_geom;
-  int gu_ppw;       // gate_up pairs per wave (grid sizing)
-  int dn_it;        // down row groups per wave
   // device memory
   void* dev_base;
   bdg::LayerDev* layers;
@@ -421,7 +481,6 @@ struct bdg_plan {
   int32_t* idx;
   float* w;
   float* h;
-  float* dout;
   hipStream_t cap_stream;
   hipEvent_t* prof_ev;      // timing events for moe_expert_decode_profiled (lazily created)
   int* prof_kind;
@@ -443,11 +502,11 @@ static int env_int(const char* name, int dflt, int lo, int hi) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// ---- launches of one layer / the finish step
+// ---- launches
 
 // Optional per-kernel timing: every launch takes the next start/stop event
 // pair (recorded by the runtime at kernel start and end) and notes its kind.
-enum KernelKind { kRoute = 0, kGateUp = 1, kDown = 2, kFinish = 3, kKinds = 4 };
+enum KernelKind { kRoute = 0, kGateUp = 1, kDown = 2, kKinds = 3 };
 
 struct Prof {
   hipEvent_t* ev;     // 2 * cap events
@@ -469,31 +528,32 @@ struct Prof {
     }                                                                                          \
   } while (0)
 
+// layer input: the caller's x at layer 0, else the residual buffer written
+// by the previous layer's down kernel.
 static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype, int m,
-                        float* resid_trace, int compute_logits, hipStream_t s, Prof* prof) {
+                        float* resid_trace, int compute_logits, int norm, hipStream_t s, Prof* prof) {
   RouteParams rp{};
   rp.M = m;
   rp.H = p->d.hidden;
   rp.E = p->d.n_experts;
-  rp.K = p->d.top_k;
-  const bool stack = (p->d.flags & BDG_MOE_STACK) != 0;
-  rp.combine = layer > 0 ? 1 : 0;
-  rp.residual = stack ? 1 : 0;
-  rp.norm = stack ? 1 : 0;
+  rp.norm = norm;
   rp.eps = p->d.norm_eps;
   rp.compute_logits = compute_logits;
-  rp.x_in = x;
-  rp.x_bf16 = x_dtype == BDG_BF16 ? 1 : 0;
-  rp.x_prev = p->resid[(layer + 1) & 1];
-  rp.d_prev = p->dout;
-  rp.w_prev = p->w;
-  rp.x_out = p->resid[layer & 1];
+  if (layer == 0) {
+    rp.x_in = x;
+    rp.x_bf16 = x_dtype == BDG_BF16 ? 1 : 0;
+    rp.x_copy = p->resid[0];
+  } else {
+    rp.x_in = p->resid[layer & 1];
+    rp.x_bf16 = 0;
+    rp.x_copy = nullptr;
+  }
   rp.resid_trace = resid_trace;
   rp.r_out = p->r;
   rp.logits = p->logits;
   rp.layers = p->layers;
   rp.layer = layer;
-  const int nblk = compute_logits ? (rp.E + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock : 1;
+  const int nblk = compute_logits ? (rp.E + kWaves - 1) / kWaves : 1;
   const size_t lds = (size_t)(rp.H + kWaves) * sizeof(float);
   BDG_LAUNCH(prof, kRoute, moe_route_kernel, dim3(nblk, m), dim3(kThreads), lds, s, rp);
   return launch_status();
@@ -523,73 +583,82 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, const 
   gp.g = p->gu_geom;
   gp.h_out = p->h;
   const int64_t pairs = (int64_t)gp.K * gp.I;
-  int64_t blocks = (pairs + (int64_t)kWaves * p->gu_ppw - 1) / ((int64_t)kWaves * p->gu_ppw);
-  if (blocks < 1) blocks = 1;
-  if (blocks > 65535) blocks = 65535;
-  const size_t lds = (size_t)gp.g.chunks * kXStride * sizeof(float) + 2 * BDG_MAX_TOPK * sizeof(float);
+  const int64_t per_block = (int64_t)kWaves * kGuPairsPerWave;
+  int64_t blocks = (pairs + per_block - 1) / per_block;
+  if (blocks > 65535) return BDG_E_UNSUPPORTED;
+  const size_t lds = ((size_t)gp.g.chunks * kXStride + (size_t)kWaves * topk_scratch_floats(gp.E)) * sizeof(float);
   dim3 grid((unsigned)blocks, m);
-  const int fmt = p->d.fmt;
-#define BDG_GU_CASE(F, SS)                                                                    \
-  if (fmt == F && p->gu_S == SS) {                                                            \
-    BDG_LAUNCH(prof, kGateUp, (moe_gateup_kernel<F, SS>), grid, dim3(kThreads), lds, s, gp);  \
-    return launch_status();                                                                   \
+  const int fmt = p->d.fmt, V = p->topk_V;
+#define BDG_GU_CASE(F, SS, VV)                                                                            \
+  if (fmt == F && p->gu_S == SS && V == VV) {                                                             \
+    BDG_LAUNCH(prof, kGateUp, (moe_gateup_kernel<F, SS, kGuPairsPerWave, VV>), grid, dim3(kThreads), lds, \
+               s, gp);                                                                                    \
+    return launch_status();                                                                               \
   }
-  BDG_GU_CASE(kMXFP4, 1) BDG_GU_CASE(kMXFP4, 2) BDG_GU_CASE(kMXFP4, 3) BDG_GU_CASE(kMXFP4, 4)
-  BDG_GU_CASE(kINT4G, 1) BDG_GU_CASE(kINT4G, 2) BDG_GU_CASE(kINT4G, 3) BDG_GU_CASE(kINT4G, 4)
+#define BDG_GU_V(F, SS) BDG_GU_CASE(F, SS, 1) BDG_GU_CASE(F, SS, 2) BDG_GU_CASE(F, SS, 4) BDG_GU_CASE(F, SS, 16)
+  BDG_GU_V(kMXFP4, 1) BDG_GU_V(kMXFP4, 2) BDG_GU_V(kMXFP4, 3) BDG_GU_V(kMXFP4, 4)
+  BDG_GU_V(kINT4G, 1) BDG_GU_V(kINT4G, 2) BDG_GU_V(kINT4G, 3) BDG_GU_V(kINT4G, 4)
+#undef BDG_GU_V
 #undef BDG_GU_CASE
   return BDG_E_UNSUPPORTED;
 }
 
-static int launch_down(const bdg_plan* p, int layer, int m, hipStream_t s, Prof* prof) {
+// h float4 staged per thread by a down block: a group of kg experts' inputs
+// (kg * I floats) over 8 waves, in one batch.
+static int down_stage_f4(int K, int I) {
+  const int kg = K < kDownWaves ? K : kDownWaves;
+  return (kg * I + kDownWaves * kWave * 4 - 1) / (kDownWaves * kWave * 4);
+}
+
+static int launch_down(const bdg_plan* p, int layer, int m, int residual, float* x_out, float* y_out,
+                       hipStream_t s, Prof* prof) {
   DownParams dp{};
   dp.M = m;
   dp.H = p->d.hidden;
   dp.I = p->d.inter;
   dp.E = p->d.n_experts;
   dp.K = p->d.top_k;
+  dp.residual = residual;
   dp.idx = p->idx;
+  dp.w = p->w;
   dp.h = p->h;
+  dp.x_prev = p->resid[layer & 1];
+  dp.x_out = x_out;
+  dp.y_out = y_out;
   dp.layers = p->layers;
   dp.layer = layer;
   dp.g = p->dn_geom;
   const int rpw = kWave / p->dn_L;
-  dp.rows_per_block = kWaves * rpw * p->dn_it;
-  dp.blocks_per_expert = (dp.H + dp.rows_per_block - 1) / dp.rows_per_block;
-  dp.d_out = p->dout;
-  const size_t lds = (size_t)dp.g.chunks * kXStride * sizeof(float);
-  dim3 grid((unsigned)(dp.blocks_per_expert * dp.K), m);
-  const int fmt = p->d.fmt;
-#define BDG_DN_CASE(F, LL, SS)                                                                \
-  if (fmt == F && p->dn_L == LL && p->dn_S == SS) {                                           \
-    BDG_LAUNCH(prof, kDown, (moe_down_kernel<F, LL, SS>), grid, dim3(kThreads), lds, s, dp);  \
-    return launch_status();                                                                   \
+  const int kg = dp.K < kDownWaves ? dp.K : kDownWaves;
+  const int wpe = kDownWaves / kg;
+  const int B = p->dn_NR * rpw * wpe;
+  const size_t lds = ((size_t)kg * dp.g.chunks * kXStride + (size_t)dp.K * B) * sizeof(float);
+  dim3 grid((unsigned)((dp.H + B - 1) / B), m);
+  const int fmt = p->d.fmt, NR = p->dn_NR;
+  const int hv = down_stage_f4(dp.K, dp.I);
+  const int HV = hv <= 2 ? 2 : hv <= 4 ? 4 : hv <= 6 ? 6 : hv <= 8 ? 8 : 12;
+#define BDG_DN_CASE(F, LL, SS, NN, HH)                                                                  \
+  if (fmt == F && p->dn_L == LL && p->dn_S == SS && NR == NN && HV == HH) {                            \
+    BDG_LAUNCH(prof, kDown, (moe_down_kernel<F, LL, SS, NN, HH>), grid, dim3(kDownWaves * kWave), lds, \
+               s, dp);                                                                                  \
+    return launch_status();                                                                             \
   }
-  BDG_DN_CASE(kMXFP4, 8, 1) BDG_DN_CASE(kMXFP4, 8, 2) BDG_DN_CASE(kMXFP4, 8, 3)
-  BDG_DN_CASE(kMXFP4, 16, 2) BDG_DN_CASE(kMXFP4, 16, 3)
-  BDG_DN_CASE(kMXFP4, 32, 2) BDG_DN_CASE(kMXFP4, 32, 3)
-  BDG_DN_CASE(kMXFP4, 64, 2) BDG_DN_CASE(kMXFP4, 64, 3) BDG_DN_CASE(kMXFP4, 64, 4)
-  BDG_DN_CASE(kINT4G, 8, 1) BDG_DN_CASE(kINT4G, 8, 2) BDG_DN_CASE(kINT4G, 8, 3)
-  BDG_DN_CASE(kINT4G, 16, 2) BDG_DN_CASE(kINT4G, 16, 3)
-  BDG_DN_CASE(kINT4G, 32, 2) BDG_DN_CASE(kINT4G, 32, 3)
-  BDG_DN_CASE(kINT4G, 64, 2) BDG_DN_CASE(kINT4G, 64, 3) BDG_DN_CASE(kINT4G, 64, 4)
+#define BDG_DN_HV(F, LL, SS, NN) \
+  BDG_DN_CASE(F, LL, SS, NN, 2) BDG_DN_CASE(F, LL, SS, NN, 4) BDG_DN_CASE(F, LL, SS, NN, 6) \
+  BDG_DN_CASE(F, LL, SS, NN, 8) BDG_DN_CASE(F, LL, SS, NN, 12)
+#define BDG_DN_NR(F, LL, SS) \
+  BDG_DN_HV(F, LL, SS, 1) BDG_DN_HV(F, LL, SS, 2) BDG_DN_HV(F, LL, SS, 3) BDG_DN_HV(F, LL, SS, 4)
+#define BDG_DN_ALL(F)                                                             \
+  BDG_DN_NR(F, 8, 1) BDG_DN_NR(F, 8, 2) BDG_DN_NR(F, 8, 3) BDG_DN_NR(F, 16, 2)   \
+  BDG_DN_NR(F, 16, 3) BDG_DN_NR(F, 32, 2) BDG_DN_NR(F, 32, 3) BDG_DN_NR(F, 64, 2) \
+  BDG_DN_NR(F, 64, 3) BDG_DN_NR(F, 64, 4)
+  BDG_DN_ALL(kMXFP4)
+  BDG_DN_ALL(kINT4G)
+#undef BDG_DN_ALL
+#undef BDG_DN_NR
+#undef BDG_DN_HV
 #undef BDG_DN_CASE
   return BDG_E_UNSUPPORTED;
-}
-
-static int launch_finish(const bdg_plan* p, int last_layer, int m, int residual, float* y, hipStream_t s,
-                         Prof* prof) {
-  FinishParams fp{};
-  fp.M = m;
-  fp.H = p->d.hidden;
-  fp.K = p->d.top_k;
-  fp.residual = residual;
-  fp.x_prev = p->resid[last_layer & 1];
-  fp.d = p->dout;
-  fp.w = p->w;
-  fp.y = y;
-  BDG_LAUNCH(prof, kFinish, moe_finish_kernel, dim3((fp.H + kThreads - 1) / kThreads, m), dim3(kThreads), 0, s,
-             fp);
-  return launch_status();
 }
 
 // The whole per-token path, enqueued on s.
@@ -597,20 +666,20 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
   const int L = p->d.n_layers;
   const int K = p->d.top_k;
   const int H = p->d.hidden;
-  const bool stack = (p->d.flags & BDG_MOE_STACK) != 0;
+  const int stack = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
   for (int l = 0; l < L; ++l) {
     int st = launch_route(p, l, k.x, k.x_dtype, k.m,
-                          k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr, 1, s, prof);
+                          k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr, 1, stack, s, prof);
     if (st) return st;
     st = launch_gateup(p, l, k.m, 0, nullptr, nullptr,
                        k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
-                       k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack ? 1 : 0, s,
-                       prof);
+                       k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof);
     if (st) return st;
-    st = launch_down(p, l, k.m, s, prof);
+    const bool last = l + 1 == L;
+    st = launch_down(p, l, k.m, stack, last ? nullptr : p->resid[(l + 1) & 1], last ? k.y : nullptr, s, prof);
     if (st) return st;
   }
-  return launch_finish(p, L - 1, k.m, stack ? 1 : 0, k.y, s, prof);
+  return BDG_OK;
 }
 
 static void drop_graph(GraphEntry& g) {
@@ -647,12 +716,12 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     return BDG_E_INVALID;
   if (d->fmt != BDG_FMT_MXFP4 && d->fmt != BDG_FMT_INT4G) return BDG_E_INVALID;
   if ((d->hidden % 32) || (d->inter % 32)) return BDG_E_INVALID;
-  if ((d->hidden % 4) != 0) return BDG_E_INVALID;
   if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH)) != 0) return BDG_E_INVALID;
   if ((d->flags & BDG_MOE_STACK) && !(d->norm_eps >= 0.f)) return BDG_E_INVALID;
   if (d->top_k > BDG_MAX_TOPK || d->n_experts > BDG_MAX_EXPERTS || d->max_m > BDG_MAX_M)
     return BDG_E_UNSUPPORTED;
   if (d->hidden > 4096 || d->inter > BDG_MAX_K) return BDG_E_UNSUPPORTED;
+  if (d->fmt == BDG_FMT_INT4G && ((d->hidden % d->group) || (d->inter % d->group))) return BDG_E_INVALID;
   for (int l = 0; l < d->n_layers; ++l) {
     int st = check_layer(d, d->layers[l]);
     if (st) return st;
@@ -662,11 +731,27 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->d = *d;
   p->d.layers = nullptr;
   const int hc = d->hidden / 32, ic = d->inter / 32;
-  p->gu_L = 32;
   p->gu_S = (hc + 31) / 32;
+  p->topk_V = d->n_experts <= 64 ? 1 : d->n_experts <= 128 ? 2 : d->n_experts <= 256 ? 4 : 16;
   if (!pick_lanes(ic, &p->dn_L, &p->dn_S)) {
     delete p;
     return BDG_E_UNSUPPORTED;
+  }
+  if (down_stage_f4(d->top_k, d->inter) > 12) {   // h staging must fit one batch
+    delete p;
+    return BDG_E_UNSUPPORTED;
+  }
+  {
+    // rows per down block: keep about 300+ blocks at M = 1, up to 4 row groups per wave
+    const int rpw = kWave / p->dn_L;
+    const int kg = d->top_k < kDownWaves ? d->top_k : kDownWaves;
+    const int wpe = kDownWaves / kg;
+    // the kernel is latency-bound: size the grid to one resident round of
+    // about one 8-wave block per CU
+    int nr = (d->hidden + 256 * rpw * wpe - 1) / (256 * rpw * wpe);
+    if (nr < 1) nr = 1;
+    if (nr > 4) nr = 4;
+    p->dn_NR = env_int("BDG_DN_NR", nr, 1, 4);
   }
   auto geom = [&](int k) {
     QGeom g;
@@ -677,21 +762,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     g.zrow = (g.groups + 1) / 2;
     return g;
   };
-  if (d->fmt == BDG_FMT_INT4G && ((d->hidden % d->group) || (d->inter % d->group))) {
-    delete p;
-    return BDG_E_INVALID;
-  }
   p->gu_geom = geom(d->hidden);
   p->dn_geom = geom(d->inter);
-  p->gu_ppw = env_int("BDG_GU_PPW", 6, 1, 64);
-  {
-    const int rpw = kWave / p->dn_L;
-    const int64_t groups = (int64_t)d->top_k * ((d->hidden + rpw - 1) / rpw);
-    int it = (int)(groups / 1536);
-    if (it < 1) it = 1;
-    if (it > 8) it = 8;
-    p->dn_it = env_int("BDG_DN_IT", it, 1, 64);
-  }
   // device memory: layer table + workspace
   const int M = d->max_m, H = d->hidden, I = d->inter, E = d->n_experts, K = d->top_k;
   size_t off = 0;
@@ -703,7 +775,6 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_idx = off; off = align256(off + sizeof(int32_t) * M * K);
   const size_t o_w = off; off = align256(off + sizeof(float) * M * K);
   const size_t o_h = off; off = align256(off + sizeof(float) * (size_t)M * K * I);
-  const size_t o_d = off; off = align256(off + sizeof(float) * (size_t)M * K * H);
   if (hipMalloc(&p->dev_base, off) != hipSuccess) {
     delete p;
     return BDG_E_NOMEM;
@@ -717,7 +788,6 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->idx = reinterpret_cast<int32_t*>(base + o_idx);
   p->w = reinterpret_cast<float*>(base + o_w);
   p->h = reinterpret_cast<float*>(base + o_h);
-  p->dout = reinterpret_cast<float*>(base + o_d);
   LayerDev* host = new (std::nothrow) LayerDev[d->n_layers];
   if (!host) {
     (void)hipFree(p->dev_base);
@@ -760,8 +830,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
 extern "C" int moe_plan_destroy(bdg_plan* p) {
   if (!p) return BDG_OK;
   (void)hipStreamSynchronize(p->cap_stream);
-  for (int i = 0; i < kGraphCache; ++i) drop_graph(p->graphs[i]);
   (void)hipDeviceSynchronize();
+  for (int i = 0; i < kGraphCache; ++i) drop_graph(p->graphs[i]);
   (void)hipStreamDestroy(p->cap_stream);
   if (p->prof_ev) {
     for (int i = 0; i < 2 * p->prof_cap; ++i) (void)hipEventDestroy(p->prof_ev[i]);
@@ -778,7 +848,8 @@ extern "C" int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_
   if (!p || !x || !y || !kernel_ms || !kernel_count || m < 1) return BDG_E_INVALID;
   if (m > p->d.max_m) return BDG_E_INVALID;
   if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
-  const int need = 3 * p->d.n_layers + 1;
+  if (!aligned16(x) || !aligned16(y)) return BDG_E_ALIGN;
+  const int need = 3 * p->d.n_layers;
   if (!p->prof_ev) {
     p->prof_ev = new (std::nothrow) hipEvent_t[2 * need];
     p->prof_kind = new (std::nothrow) int[need];
@@ -807,6 +878,7 @@ extern "C" int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, in
   if (!p || !x || !y || m < 1) return BDG_E_INVALID;
   if (m > p->d.max_m) return BDG_E_INVALID;
   if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
+  if (!aligned16(x) || !aligned16(y) || (resid_trace && !aligned16(resid_trace))) return BDG_E_ALIGN;
   GraphKey key{x, x_dtype, m, y, topk_trace, wts_trace, resid_trace};
   hipStream_t s = as_stream(stream);
   if (p->d.flags & BDG_MOE_NO_GRAPH) return enqueue_decode(p, key, s);
@@ -852,21 +924,19 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   if (!p || !x || !idx || !wts || !y || m < 1) return BDG_E_INVALID;
   if (m > p->d.max_m || layer < 0 || layer >= p->d.n_layers) return BDG_E_INVALID;
   if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
+  if (!aligned16(x)) return BDG_E_ALIGN;
   hipStream_t s = as_stream(stream);
   // x -> the plan's fp32 input buffer of `layer` (no norm, no logits)
   RouteParams rp{};
   rp.M = m;
   rp.H = p->d.hidden;
   rp.E = p->d.n_experts;
-  rp.K = p->d.top_k;
-  rp.combine = 0;
-  rp.residual = 0;
   rp.norm = 0;
   rp.eps = 0.f;
   rp.compute_logits = 0;
   rp.x_in = x;
   rp.x_bf16 = x_dtype == BDG_BF16 ? 1 : 0;
-  rp.x_out = p->resid[layer & 1];
+  rp.x_copy = p->resid[layer & 1];
   rp.r_out = p->r;
   rp.logits = p->logits;
   rp.layers = p->layers;
@@ -878,9 +948,7 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   // gate_up runs on the raw x (no norm), routing from the caller
   st = launch_gateup(p, layer, m, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
   if (st) return st;
-  st = launch_down(p, layer, m, s, nullptr);
-  if (st) return st;
-  return launch_finish(p, layer, m, 0, y, s, nullptr);
+  return launch_down(p, layer, m, 0, nullptr, y, s, nullptr);
 }
 
 // ---------------------------------------------------------------- standalone router
@@ -899,8 +967,6 @@ router_topk_kernel(const void* __restrict__ x, int x_bf16, const float* __restri
   float* xs = lds;             // [H]
   float* lg = lds + H;         // [E]
   float* red = lg + E;         // [kWaves]
-  __shared__ int s_idx[BDG_MAX_TOPK];
-  __shared__ float s_w[BDG_MAX_TOPK];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -930,11 +996,14 @@ router_topk_kernel(const void* __restrict__ x, int x_bf16, const float* __restri
     if (lane == 0) lg[e] = acc + (b_r ? b_r[e] : 0.f);
   }
   __syncthreads();
-  if (wave == 0) wave_topk(lg, E, K, s_idx, s_w);
-  __syncthreads();
-  if (threadIdx.x < K) {
-    idx[t * K + threadIdx.x] = s_idx[threadIdx.x];
-    wts[t * K + threadIdx.x] = s_w[threadIdx.x];
+  if (wave == 0) {
+    int my_e;
+    float my_w;
+    wave_topk<BDG_MAX_EXPERTS / kWave>(lg, E, K, red + kWaves, my_e, my_w);
+    if (lane < K) {
+      idx[t * K + lane] = my_e;
+      wts[t * K + lane] = my_w;
+    }
   }
   if (logits)
     for (int e = threadIdx.x; e < E; e += kThreads) logits[(int64_t)t * E + e] = lg[e];
@@ -951,7 +1020,7 @@ extern "C" int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r,
   if ((flags & BDG_ROUTER_RMSNORM) && !(norm_eps >= 0.f)) return BDG_E_INVALID;
   if ((reinterpret_cast<uintptr_t>(w_r) & 15u) != 0) return BDG_E_ALIGN;
   if (e > BDG_MAX_EXPERTS || topk > BDG_MAX_TOPK || h > 16384) return BDG_E_UNSUPPORTED;
-  const size_t lds = (size_t)(h + e + kWaves) * sizeof(float);
+  const size_t lds = (size_t)(h + e + kWaves + topk_scratch_floats(e)) * sizeof(float);
   hipLaunchKernelGGL(router_topk_kernel, dim3(m), dim3(kThreads), lds, as_stream(stream), x,
                      x_dtype == BDG_BF16 ? 1 : 0, w_r, b_r, h, e, topk,
                      (flags & BDG_ROUTER_RMSNORM) ? 1 : 0, norm_eps, idx, wts, logits);

@@ -115,8 +115,8 @@ int int4g_dequant(const uint8_t* codes, const uint16_t* scales_f16, const uint8_
  * (the MXFP4 dequant-GEMV of the gpt-oss page, section 1, with 16-byte
  * coalesced loads and on-chip dequant, section 4).  W is read packed, never
  * materialised.  x [m][k] of x_dtype (BDG_F32 or BDG_BF16), device;
- * y [m][n] fp32, device.  1 <= m <= BDG_MAX_M, k <= BDG_MAX_K.  W's expert
- * strides are ignored (expert 0). */
+ * y [m][n] fp32, device; x 16-byte aligned.  1 <= m <= BDG_MAX_M,
+ * k <= BDG_MAX_K.  W's expert strides are ignored (expert 0). */
 int qgemv(const bdg_qmat* w, const void* x, int32_t x_dtype, int32_t m, float* y,
           void* stream);
 
@@ -189,8 +189,9 @@ int moe_plan_destroy(bdg_plan* p);
  * resid_trace [L][m][H] fp32 with each layer's input residual (stack) or
  * input (bare layer).  The per-token path is replayed from a captured HIP
  * graph keyed on (x, y, traces, m, x_dtype), captured at the first call with
- * that key.  A plan is not re-entrant: calls on one plan must be ordered on
- * one stream. */
+ * that key (a cache of 8 graphs, least recently used evicted).  x, y and
+ * resid_trace must be 16-byte aligned.  A plan is not re-entrant: calls on
+ * one plan must be ordered on one stream. */
 int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
                       int32_t* topk_trace, float* wts_trace, float* resid_trace, void* stream);
 
@@ -210,10 +211,11 @@ int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int32_t x_dtyp
  * computes it (same kernels, same grids), launched directly rather than from
  * a graph, with a start/stop event pair recorded by the runtime at each
  * kernel's start and end.  Adds each kernel's duration (ms) to
- * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route, 1 = gate_up
- * (+SwiGLU), 2 = down, 3 = finish (host arrays of 4).  Synchronises on the
- * last event before returning.  Used by the benchmark for per-kernel
- * roofline figures. */
+ * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route (RMSNorm +
+ * router GEMV), 1 = gate_up (top-k + grouped gate_up GEMV + SwiGLU), 2 =
+ * down (grouped down GEMV + combine + residual); host arrays of at least 3.
+ * Synchronises on the last event before returning.  Used by the benchmark
+ * for per-kernel roofline figures. */
 int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
                                double* kernel_ms, int64_t* kernel_count, void* stream);
 
