@@ -53,6 +53,28 @@ def step_bytes(cfg, unique_experts_per_layer):
     return sum(router_bytes(cfg) + u * (gu + dn) for u in unique_experts_per_layer)
 
 
+KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp",
+                  "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    none or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec.get("kernel_sources_sha"):
+        return None
+    t = rec["per_launch"].get(kernel)
+    return None if t is None else t["fetch_bytes"] + t["write_bytes"]
+
+
 def cpu_baseline(cfg, sample_layers, token):
     """The oracle as it stands, token-major, on `sample_layers` layers of one token.
 
@@ -156,6 +178,9 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run the 16-byte copy kernel 4 times over BYTES (for scaling "
+                         "HBM counters against a kernel of known traffic), then exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +200,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        nb = args.copy_calibration // 256 * 256
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            bdg.stream_copy(src, dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nb, "launches": 4}), flush=True)
+        return
     cfg = synth.CONFIGS[args.workload]
     if cfg.m != 1:
         raise SystemExit("bench.py times the M=1 workloads")
@@ -279,7 +313,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, "gate_up"),
+            "traffic_algorithmic_bytes": gu_launch_bytes,
         },
         "kernels": kernels,
         "kernel_us_per_token": round(sum_kernel_us, 2),
