@@ -200,7 +200,9 @@ template <int FMT>
 __device__ __forceinline__ float chunk_contrib(const uint4 q, uint32_t scale_raw, uint32_t zero_nib,
                                                const float* __restrict__ x, float xsum) {
   if constexpr (FMT == kMXFP4) {
-    return fp4_chunk_dot(q, x) * e8m0_to_f32(scale_raw);
+    // block sum * 2^(e-127); e = 255 is NaN
+    const float r = __builtin_amdgcn_ldexpf(fp4_chunk_dot(q, x), (int)scale_raw - 127);
+    return scale_raw == 255u ? __uint_as_float(0x7FC00000u) : r;
   } else {
     const float s = f16_bits_to_f32((uint16_t)scale_raw);
     const float part = u4_chunk_dot(q, x) - (float)zero_nib * xsum;

@@ -74,23 +74,22 @@ struct XRegs {
   float v[S][kChunkElems];
   float sum[S];   // int4: sum of the chunk's x values (zero-point fold)
 
+  // Branch-free: a slot past the row end reads the last chunk and zeroes it,
+  // so no load is inside a branch (a branch here makes the compiler wait for
+  // every outstanding weight load).
   __device__ __forceinline__ void load(const float* __restrict__ lds_x, int chunks, int li) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int c = li + L * s;
-      if (c < chunks) {
-        const float4* src = reinterpret_cast<const float4*>(lds_x + c * kXStride);
+      const bool ok = c < chunks;
+      const float4* src = reinterpret_cast<const float4*>(lds_x + (ok ? c : chunks - 1) * kXStride);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 t = src[q];
-          v[s][4 * q + 0] = t.x;
-          v[s][4 * q + 1] = t.y;
-          v[s][4 * q + 2] = t.z;
-          v[s][4 * q + 3] = t.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < kChunkElems; ++q) v[s][q] = 0.f;
+      for (int q = 0; q < 8; ++q) {
+        const float4 t = src[q];
+        v[s][4 * q + 0] = ok ? t.x : 0.f;
+        v[s][4 * q + 1] = ok ? t.y : 0.f;
+        v[s][4 * q + 2] = ok ? t.z : 0.f;
+        v[s][4 * q + 3] = ok ? t.w : 0.f;
       }
       if constexpr (FMT == kINT4G) {
         float a = 0.f;
