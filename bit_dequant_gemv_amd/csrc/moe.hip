@@ -68,25 +68,37 @@ __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (
 
 // ---------------------------------------------------------------- top-k
 
-__device__ __forceinline__ bool better(float a, int ea, float b, int eb) {
-  return a > b || (a == b && ea < eb);
+// Order-preserving unsigned key of a float: larger float <-> larger key.
+// -0.0 is folded onto +0.0 (they compare equal as floats) and NaN onto -inf.
+__device__ __forceinline__ uint32_t topk_key(float x) {
+  if (x != x) x = -INFINITY;
+  x = x + 0.0f;
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+// Maximum of a per-lane unsigned value over the wavefront (uniform result):
+// quad max by DPP quad permutes, row max by DPP row rotations, then the four
+// row maxima read out.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm xor 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm xor 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
-
-// Floats of wave-private LDS scratch wave_topk needs for E experts.
-__host__ __device__ constexpr int topk_scratch_floats(int E) { return E + 2 * BDG_MAX_TOPK; }
 
 // One wavefront: the K largest of row[0..E) in descending order, ties to the
-// lower index, and softmax weights over them.  Each value's rank is the
-// number of values before it in the order (larger, or equal with a lower
-// index); the values with rank < K are the picks, in rank order.  NaN ranks
-// as -inf.  Lane j < K receives pick j in (out_e, out_w); other lanes get
-// (0, 0).  V = values per lane (E <= 64V); scr = wave-private LDS.
+// lower index, and softmax weights over them.  Each of the K rounds takes the
+// wave maximum of the untaken keys, then the lowest expert index holding it
+// (a ballot per value slot, lowest slot first), and retires that one entry.
+// NaN ranks as -inf.  Lane j < K receives pick j in (out_e, out_w); other
+// lanes get (0, 0).  V = values per lane (E <= 64V); expert e sits in lane
+// e % 64, slot e / 64.
 template <int V>
 __device__ __forceinline__ void topk_load(const float* row, int E, float (&v)[V]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -98,54 +110,53 @@ __device__ __forceinline__ void topk_load(const float* row, int E, float (&v)[V]
 }
 
 template <int V>
-__device__ __forceinline__ void topk_rank(float (&v)[V], int E, int K, float* scr, int& out_e, float& out_w) {
+__device__ __forceinline__ void topk_rank(float (&v)[V], int E, int K, int& out_e, float& out_w) {
   const int lane = threadIdx.x & (kWave - 1);
-  int* pick_e = reinterpret_cast<int*>(scr + E);
-  float* pick_l = scr + E + BDG_MAX_TOPK;
+  uint32_t key[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = lane + kWave * i;
-    float x = v[i];
-    if (x != x || e >= E) x = -INFINITY;
-    v[i] = x;
-    if (e < E) scr[e] = x;
-  }
-  wave_lds_sync();
+  for (int i = 0; i < V; ++i) key[i] = (lane + kWave * i < E) ? topk_key(v[i]) : 0u;   // 0 = retired / absent
+  int my_e = 0;
+  float my_l = 0.f;
+  float l0 = 0.f;
+  for (int j = 0; j < K; ++j) {
+    uint32_t m = key[0];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) {
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < E; ++j) {
-        const float o = scr[j];
-        rank += (o > v[i]) | ((o == v[i]) & (j < e));
-      }
-      if (rank < K) {
-        pick_e[rank] = e;
-        pick_l[rank] = v[i];
+    for (int i = 1; i < V; ++i) m = max(m, key[i]);
+    const uint32_t best = wave_max_u32(m);
+    int pick = E - 1;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(key[i] == best);
+      if (!found && hit != 0) {
+        pick = kWave * i + (int)__builtin_ctzll(hit);
+        found = true;
       }
     }
+    // the winner's value: floats ordered like their keys, so read it back from the key
+    const uint32_t kb = (best & 0x80000000u) ? (best & 0x7FFFFFFFu) : ~best;
+    const float val = best == 0u ? -INFINITY : __uint_as_float(kb);
+    if (j == 0) l0 = val;
+    if (lane == j) {
+      my_e = pick;
+      my_l = val;
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (lane + kWave * i == pick) key[i] = 0u;
   }
-  wave_lds_sync();
-  const int my_e = lane < K ? pick_e[lane] : 0;
-  const float my_l = lane < K ? pick_l[lane] : 0.f;
-  const float l0 = pick_l[0];
   const float ex = lane < K ? expf(my_l - l0) : 0.f;
   const float sum = wave_sum(ex);
-  out_e = my_e;
+  out_e = lane < K ? my_e : 0;
   out_w = lane < K ? ex / sum : 0.f;
-  wave_lds_sync();
 }
 
 template <int V>
-__device__ __forceinline__ void wave_topk(const float* row, int E, int K, float* scr, int& out_e, float& out_w) {
+__device__ __forceinline__ void wave_topk(const float* row, int E, int K, int& out_e, float& out_w) {
   float v[V];
   topk_load<V>(row, E, v);
-  topk_rank<V>(v, E, K, scr, out_e, out_w);
+  topk_rank<V>(v, E, K, out_e, out_w);
 }
-
-
 
 // ---------------------------------------------------------------- route
 
@@ -280,7 +291,6 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   const int wave = uniform_wave_id();
   const int li = lane % L;
   const bool is_up = lane >= L;
-  float* scr = lds + p.g.chunks * kXStride + wave * topk_scratch_floats(p.E);
 
   // load order: routing inputs, then x (independent of the routing), then
   // the expert weights - the in-order wait for each stays short
@@ -297,7 +307,7 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   StageF32<NX> xstage;
   xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
   const float mult = p.r ? p.r[t] : 1.0f;
-  if (!p.routed) topk_rank<V>(lg, p.E, p.K, scr, my_e, my_w);
+  if (!p.routed) topk_rank<V>(lg, p.E, p.K, my_e, my_w);
   if (lane >= p.K) {
     my_e = 0;
     my_w = 0.f;
@@ -586,7 +596,7 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, const 
   const int64_t per_block = (int64_t)kWaves * kGuPairsPerWave;
   int64_t blocks = (pairs + per_block - 1) / per_block;
   if (blocks > 65535) return BDG_E_UNSUPPORTED;
-  const size_t lds = ((size_t)gp.g.chunks * kXStride + (size_t)kWaves * topk_scratch_floats(gp.E)) * sizeof(float);
+  const size_t lds = (size_t)gp.g.chunks * kXStride * sizeof(float);
   dim3 grid((unsigned)blocks, m);
   const int fmt = p->d.fmt, V = p->topk_V;
 #define BDG_GU_CASE(F, SS, VV)                                                                            \
@@ -999,7 +1009,7 @@ router_topk_kernel(const void* __restrict__ x, int x_bf16, const float* __restri
   if (wave == 0) {
     int my_e;
     float my_w;
-    wave_topk<BDG_MAX_EXPERTS / kWave>(lg, E, K, red + kWaves, my_e, my_w);
+    wave_topk<BDG_MAX_EXPERTS / kWave>(lg, E, K, my_e, my_w);
     if (lane < K) {
       idx[t * K + lane] = my_e;
       wts[t * K + lane] = my_w;
@@ -1020,7 +1030,7 @@ extern "C" int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r,
   if ((flags & BDG_ROUTER_RMSNORM) && !(norm_eps >= 0.f)) return BDG_E_INVALID;
   if ((reinterpret_cast<uintptr_t>(w_r) & 15u) != 0) return BDG_E_ALIGN;
   if (e > BDG_MAX_EXPERTS || topk > BDG_MAX_TOPK || h > 16384) return BDG_E_UNSUPPORTED;
-  const size_t lds = (size_t)(h + e + kWaves + topk_scratch_floats(e)) * sizeof(float);
+  const size_t lds = (size_t)(h + e + kWaves) * sizeof(float);
   hipLaunchKernelGGL(router_topk_kernel, dim3(m), dim3(kThreads), lds, as_stream(stream), x,
                      x_dtype == BDG_BF16 ? 1 : 0, w_r, b_r, h, e, topk,
                      (flags & BDG_ROUTER_RMSNORM) ? 1 : 0, norm_eps, idx, wts, logits);

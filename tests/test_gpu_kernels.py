@@ -229,3 +229,24 @@ def test_router_ties_lower_index(dev):
     assert list(to_np(idx)[0]) == [5, 9, 0, 1]
     e1 = np.exp(np.float32(-1.0))
     np.testing.assert_allclose(to_np(wts)[0], np.array([1, 1, e1, e1]) / (2 + 2 * e1), atol=1e-7)
+
+
+@pytest.mark.parametrize("E,k", [(16, 4), (128, 8), (300, 32), (1024, 32)])
+def test_router_topk_ties_nan_inf(dev, E, k):
+    """Logits made of the bias alone (zero router rows) from a tiny value set:
+    long runs of equal logits, -inf and NaN.  Picks must come out in
+    descending order with ties to the lower index; NaN ranks as -inf, and
+    more than k logits are finite, so neither is ever picked."""
+    H = 64
+    rng = np.random.default_rng(E)
+    b = rng.choice(np.array([2.0, 1.0, 1.0, 0.5, 0.5, -np.inf, np.nan], dtype=np.float32), size=E)
+    b[rng.choice(E, size=k + 1, replace=False)] = 0.25     # at least k+1 finite logits
+    w_r = np.zeros((E, H), dtype=np.float32)
+    x = synth.random_input(E, (3, H))
+    banner(f"moe_router_topk ties/nan/inf E={E} k={k}")
+    idx, wts, logits = bdg.moe_router_topk(dev_t(x, dev), dev_t(w_r, dev), dev_t(b, dev), k)
+    idx, wts = to_np(idx), to_np(wts)
+    finite = np.where(np.isnan(b), -np.inf, b).astype(np.float64)
+    o_idx, o_w = omoe.topk_softmax(np.tile(finite, (3, 1)), k)
+    assert np.array_equal(idx, o_idx)
+    assert np.max(np.abs(wts - o_w)) <= WEIGHT_ABS

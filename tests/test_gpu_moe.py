@@ -187,3 +187,31 @@ def test_stack_full(dev, name, check_layers):
         for l in check_layers:
             out = resid[l + 1] if l + 1 < cfg.n_layers else y
             check_layer(cfg, l, resid[l], out, topk[l], wts[l], True, f"{name} layer {l} token {tok}")
+
+
+@pytest.mark.parametrize("E,k", [(32, 4), (128, 8), (256, 8), (300, 16)])
+def test_layer_routing_ties(dev, E, k):
+    """The expert selection inside the fused path on tie-heavy logits: zero
+    router rows, so each logit is its bias, drawn from a small value set with
+    -inf entries.  The selection must match the oracle's order exactly (ties
+    to the lower index), and the layer output the oracle's for those picks."""
+    cfg = small_cfg("mxfp4", 1500 + E, E=E, k=k, H=128, I=64, m=2)
+    rng = np.random.default_rng(E)
+    b = rng.choice(np.array([1.0, 0.5, 0.5, 0.0, -np.inf], dtype=np.float32), size=E)
+    b[rng.choice(E, size=k + 1, replace=False)] = 0.25
+    w_r = np.zeros((E, cfg.hidden), dtype=np.float32)
+    layer = sdev.upload_layer(cfg, 0, dev)
+    layer["w_router"] = torch.from_numpy(w_r).to(dev)
+    layer["b_router"] = torch.from_numpy(b).to(dev)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=2, layers=[layer])
+    x, xv = sdev.hidden_device(cfg, [0, 1], dev)
+    banner(f"moe_expert_decode routing ties E={E} k={k}")
+    y, tr = bdg.moe_expert_decode(plan, x, traces=True)
+    torch.cuda.synchronize()
+    y, topk, wts = to_np(y), to_np(tr["topk"])[0], to_np(tr["wts"])[0]
+    o_idx, o_w = omoe.topk_softmax(np.tile(b.astype(np.float64), (2, 1)), k)
+    assert np.array_equal(topk, o_idx)
+    assert np.max(np.abs(wts - o_w)) <= W_TOL
+    res = omoe.moe_layer(xv, w_r, oracle_expert_getter(cfg, 0), k, bias=b, norm=False, residual=False,
+                         forced_idx=topk)
+    assert_close(y, res["y"], res["den"], f"ties E={E}")
