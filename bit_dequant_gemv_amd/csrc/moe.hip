@@ -160,17 +160,25 @@ __device__ __forceinline__ void wave_topk(const float* row, int E, int K, int& o
 
 // ---------------------------------------------------------------- route
 
+// Router dot products travel between kernels as partial sums:
+// part[t][e][k], k < nparts (row stride pstride), holds the sum over one
+// slice of the hidden dimension of w_r[e][h] * x[h] for the layer input x,
+// before the RMSNorm scale and the bias.  The route kernel writes one slice
+// (the whole of x); a down kernel that feeds the next layer writes one slice
+// per row block.  Column E holds the matching slices of the sum of squares
+// of x.  gate_up adds the slices in a fixed order, scales by the RMSNorm
+// factor, adds the bias and selects.  (RMSNorm is a per-token scale, so
+// w_r . (x * r) = r * (w_r . x).)
+
 struct RouteParams {
   int M, H, E;
-  int norm;           // RMSNorm before routing / experts
-  float eps;
   int compute_logits;
   const void* x_in;   // [M][H] layer input: caller x (bf16/f32) at layer 0, else the residual buffer
   int x_bf16;
   float* x_copy;      // [M][H] fp32 copy of x_in written by block 0 (layer 0), or NULL
   float* resid_trace; // [M][H] or NULL, written by block 0
-  float* r_out;       // [M], written by block 0
-  float* logits;      // [M][E]
+  float* part;        // [M][E + 1][pstride]: slice 0 written
+  int pstride;
   const LayerDev* layers;
   int layer;
 };
@@ -197,7 +205,6 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
     const int h = (i * kWave + lane) * 4;
     wv[i] = ldg_f4(L.w_r + (int64_t)ec * p.H + (h < p.H ? h : p.H - 4));
   }
-  float ss = 0.f;
   const int64_t xoff = (int64_t)t * p.H;
   constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // float4 of x per thread (H <= 4096)
   float4 xv4[NX];
@@ -219,6 +226,7 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
       xv4[i] = ldg_f4(reinterpret_cast<const float*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
     }
   }
+  float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
     const int h = (i * kThreads + threadIdx.x) * 4;
@@ -238,9 +246,8 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
-  float r = 1.f;
-  if (p.norm) r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)p.H + p.eps);
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.r_out[t] = r;
+  if (p.compute_logits && blockIdx.x == 0 && threadIdx.x == 0)
+    p.part[((int64_t)t * (p.E + 1) + p.E) * p.pstride] = (red[0] + red[1]) + (red[2] + red[3]);
   if (!row_ok) return;
   float acc = 0.f;
 #pragma unroll
@@ -248,14 +255,14 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
     const int h = (i * kWave + lane) * 4;
     if (h < p.H) {
       const float4 xv = *reinterpret_cast<const float4*>(xs + h);
-      acc = __builtin_fmaf(wv[i].x, xv.x * r, acc);
-      acc = __builtin_fmaf(wv[i].y, xv.y * r, acc);
-      acc = __builtin_fmaf(wv[i].z, xv.z * r, acc);
-      acc = __builtin_fmaf(wv[i].w, xv.w * r, acc);
+      acc = __builtin_fmaf(wv[i].x, xv.x, acc);
+      acc = __builtin_fmaf(wv[i].y, xv.y, acc);
+      acc = __builtin_fmaf(wv[i].z, xv.z, acc);
+      acc = __builtin_fmaf(wv[i].w, xv.w, acc);
     }
   }
   acc = wave_sum(acc);
-  if (lane == 0) p.logits[(int64_t)t * p.E + e] = acc + (L.b_r ? L.b_r[e] : 0.f);
+  if (lane == 0) p.part[((int64_t)t * (p.E + 1) + e) * p.pstride] = acc;
 }
 
 // ---------------------------------------------------------------- gate_up + SwiGLU
@@ -263,7 +270,11 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
 struct GateUpParams {
   int M, H, I, E, K;
   int routed;                 // 1: routing given in idx_in / w_in
-  const float* logits;        // [M][E]
+  const float* part;          // [M][E + 1][pstride] router partial sums (see the route section)
+  int nparts, pstride;
+  int log2T;                  // 2^log2T threads add up one expert's slices
+  int norm;                   // RMSNorm scale on x (and on the router input)
+  float eps;
   const int32_t* idx_in;
   const float* w_in;
   int32_t* idx_out;           // [M][K] routing buffer, written by block 0
@@ -271,12 +282,13 @@ struct GateUpParams {
   int32_t* topk_trace;        // [M][K] or NULL
   float* wts_trace;
   const float* x;             // [M][H] layer input (fp32)
-  const float* r;             // [M] norm scale or NULL
   const LayerDev* layers;
   int layer;
   QGeom g;                    // reduction over H
   float* h_out;               // [M][K][I]
 };
+
+constexpr int kPartF4 = 8;    // float4 of router partial sums per thread issued up front
 
 // Wave gw of token t owns the (expert slot, row pair) range
 // [P*gw/GW, P*(gw+1)/GW) of the P = K*I pairs; the grid makes it <= NP.
@@ -286,28 +298,118 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   constexpr int L = 32;
   extern __shared__ float lds[];
   float* xs = lds;                                          // [chunks * kXStride]
+  float* red = xs + p.g.chunks * kXStride;                  // [kWaves]
+  float* psum = red + kWaves;                               // [E << log2T]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_wave_id();
   const int li = lane % L;
   const bool is_up = lane >= L;
+  const LayerDev Ld = p.layers[p.layer];
 
   // load order: routing inputs, then x (independent of the routing), then
   // the expert weights - the in-order wait for each stays short
-  float lg[V];
+  const int lt = p.log2T;
+  const int T = 1 << lt;
+  const int sub = threadIdx.x & (T - 1);
+  const int n4 = (p.nparts + 3) >> 2;                      // float4 per expert row of slices
+  const int64_t pbase = (int64_t)t * (p.E + 1) * p.pstride;
+  const bool slices = !p.routed && p.nparts > 1;
+  float4 pv[kPartF4];
+  float lg[V], bias[V];
+  float ssq = 0.f;
   int my_e = 0;
   float my_w = 0.f;
   if (p.routed) {
     my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
     my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
   } else {
-    topk_load<V>(p.logits + (int64_t)t * p.E, p.E, lg);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      bias[i] = Ld.b_r ? Ld.b_r[e < p.E ? e : p.E - 1] : 0.f;
+    }
+    if (slices) {
+      const int c = threadIdx.x >> lt;
+      const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
+#pragma unroll
+      for (int i = 0; i < kPartF4; ++i) {
+        const int k4 = sub + (i << lt);
+        pv[i] = k4 < n4 ? ldg_f4(row + 4 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      // sum-of-squares slices (column E): one float4 per thread, n4 <= kThreads
+      const int k4 = threadIdx.x;
+      const float4 q = k4 < n4 ? ldg_f4(p.part + pbase + (int64_t)p.E * p.pstride + 4 * k4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int k = 4 * k4;
+      ssq = k < p.nparts ? q.x : 0.f;
+      ssq += k + 1 < p.nparts ? q.y : 0.f;
+      ssq += k + 2 < p.nparts ? q.z : 0.f;
+      ssq += k + 3 < p.nparts ? q.w : 0.f;
+    } else {
+      // one slice (the route kernel's): each wave reads its values directly
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = lane + kWave * i;
+        lg[i] = p.part[pbase + (int64_t)(e < p.E ? e : p.E - 1) * p.pstride];
+      }
+      ssq = p.part[pbase + (int64_t)p.E * p.pstride];
+    }
   }
   constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // H <= 4096
   StageF32<NX> xstage;
   xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
-  const float mult = p.r ? p.r[t] : 1.0f;
-  if (!p.routed) topk_rank<V>(lg, p.E, p.K, my_e, my_w);
+
+  float r = 1.0f;
+  if (slices) {
+    // slices of expert c: thread sub adds slices 4*(sub + i*T) .. +3, in order
+    for (int c0 = 0; c0 < p.E; c0 += kThreads >> lt) {
+      const int c = c0 + (threadIdx.x >> lt);
+      const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
+      float a = 0.f;
+      int k4 = sub;
+      if (c0 == 0) {
+#pragma unroll
+        for (int i = 0; i < kPartF4; ++i, k4 += T) {
+          const int k = 4 * k4;
+          a += k < p.nparts ? pv[i].x : 0.f;
+          a += k + 1 < p.nparts ? pv[i].y : 0.f;
+          a += k + 2 < p.nparts ? pv[i].z : 0.f;
+          a += k + 3 < p.nparts ? pv[i].w : 0.f;
+        }
+      }
+      for (; k4 < n4; k4 += T) {   // beyond the slices loaded up front
+        const float4 v = ldg_f4(row + 4 * k4);
+        const int k = 4 * k4;
+        a += v.x;
+        a += k + 1 < p.nparts ? v.y : 0.f;
+        a += k + 2 < p.nparts ? v.z : 0.f;
+        a += k + 3 < p.nparts ? v.w : 0.f;
+      }
+      if (c < p.E) psum[(c << lt) + sub] = a;
+    }
+    {
+      const float ss = wave_sum(ssq);
+      if (lane == 0) red[wave] = ss;
+    }
+    __syncthreads();
+    if (p.norm) ssq = (red[0] + red[1]) + (red[2] + red[3]);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      const float* ps = psum + ((e < p.E ? e : p.E - 1) << lt);
+      float a = 0.f;
+      for (int q = 0; q < T; ++q) a += ps[q];
+      lg[i] = a;
+    }
+  }
+  if (!p.routed) {
+    if (p.norm) r = 1.0f / sqrtf(ssq / (float)p.H + p.eps);
+#pragma unroll
+    for (int i = 0; i < V; ++i) lg[i] = r * lg[i] + bias[i];
+    topk_rank<V>(lg, p.E, p.K, my_e, my_w);
+  }
+  const float mult = r;
   if (lane >= p.K) {
     my_e = 0;
     my_w = 0.f;
@@ -319,7 +421,6 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
     if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
   }
 
-  const LayerDev Ld = p.layers[p.layer];
   const int P = p.K * p.I;
   const int GW = gridDim.x * kWaves;
   const int gw = blockIdx.x * kWaves + wave;
@@ -379,10 +480,20 @@ struct DownParams {
   const float* x_prev;        // [M][H] layer input (residual)
   float* x_out;               // [M][H] next layer's input, or NULL
   float* y_out;               // [M][H] caller output, or NULL
+  float* trace_out;           // [M][H] copy of x_out (next layer's input trace), or NULL
+  // next layer's router partial sums over this block's rows (slice
+  // blockIdx.x of part_out) when route_next; then B <= 64 and
+  // E <= kDownWaves * kDnRouterPerWave
+  int route_next;
+  const float* wr_next;       // [E][H]
+  float* part_out;            // [M][E + 1][pstride]
+  int pstride;
   const LayerDev* layers;
   int layer;
   QGeom g;                    // reduction over I
 };
+
+constexpr int kDnRouterPerWave = 8;   // next-layer router rows per down wave
 
 // Block (rb, t) of 8 waves: WPE = 8 / K waves per chosen expert (1 when
 // K >= 8; experts then go in groups of 8).  Wave w works on expert slot
@@ -410,12 +521,29 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   const bool wave_on = sub < wpe;
   const LayerDev Ld = p.layers[p.layer];
 
+  // loads, in the order their data is needed (vmcnt retires in order):
+  // the first group's expert id, the epilogue operands (router weights of
+  // the next layer, residual row, combine weights: all in bounds, issued
+  // unconditionally so the compiler's wait counts stay exact), then per
+  // group the h vectors and the expert weights
+  int e_next = clamp_expert(p.idx[t * p.K + (jw < p.K ? jw : p.K - 1)], p.E);
+  const int orow = r0 + lane < p.H ? r0 + lane : p.H - 1;  // epilogue row of this lane (B <= 64)
+  float wr[kDnRouterPerWave];                               // wr[i] = w_r'[wave + 8i][orow]
+  {
+    const float* wsrc = p.route_next ? p.wr_next : p.x_prev;
+#pragma unroll
+    for (int i = 0; i < kDnRouterPerWave; ++i) {
+      const int er = wave + kDownWaves * i;
+      wr[i] = wsrc[(int64_t)(p.route_next ? (er < p.E ? er : p.E - 1) : 0) * p.H + orow];
+    }
+  }
+  const float xp = p.x_prev[(int64_t)t * p.H + orow];
+  const float wk = p.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
+
   for (int jg = 0; jg < p.K; jg += kg) {
     const int nj = min(kg, p.K - jg);
-    const int j = jg + (jw < nj ? jw : nj - 1);
     const bool active = wave_on && jw < nj;
-    // expert id first, then the h loads, then the expert weights
-    const int e = clamp_expert(p.idx[t * p.K + j], p.E);
+    const int e = e_next;
     const int nh = nj * p.I;
     StageF32<HV> hstage;
     hstage.load(p.h + ((int64_t)t * p.K + jg) * p.I, nh, threadIdx.x, blockDim.x);
@@ -425,6 +553,10 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
     for (int i = 0; i < NR; ++i) {
       const int row = r0 + (i * wpe + sub) * RPW + rr;
       load_row<FMT, L, S>(ld[i], m, p.g, row, active && row < p.H, li);
+    }
+    if (jg + kg < p.K) {   // next group's expert id (K > 8 only)
+      const int jn = jg + kg + (jw < p.K - jg - kg ? jw : p.K - jg - kg - 1);
+      e_next = clamp_expert(p.idx[t * p.K + jn], p.E);
     }
     hstage.store(lds, nh, p.I, stride, 1.0f, threadIdx.x, blockDim.x);
     __syncthreads();
@@ -440,6 +572,54 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
     }
     __syncthreads();
   }
+
+  if (B <= kWave) {
+    // every wave forms the block's rows (row r0 + lane) and wave 0 stores
+    // them; with route_next, wave w reduces them against router rows
+    // w, w + 8, ... of the next layer
+    const int row = r0 + lane;
+    const bool ok = lane < B && row < p.H;
+    float v = p.residual ? xp : 0.f;
+    for (int j = 0; j < p.K; ++j)
+      v = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j)),
+                         dpart[j * B + (ok ? lane : 0)], v);
+    v = ok ? v : 0.f;
+    if (wave == 0 && ok) {
+      if (p.x_out) p.x_out[(int64_t)t * p.H + row] = v;
+      if (p.y_out) p.y_out[(int64_t)t * p.H + row] = v;
+      if (p.trace_out) p.trace_out[(int64_t)t * p.H + row] = v;
+    }
+    if (!p.route_next) return;
+    // all router rows of the wave (and the rows' sum of squares, column E)
+    // reduced together, one butterfly step at a time
+    constexpr int NA = kDnRouterPerWave + 1;
+    float a[NA];
+#pragma unroll
+    for (int i = 0; i < kDnRouterPerWave; ++i) a[i] = wr[i] * v;
+    a[kDnRouterPerWave] = v * v;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor1(a[i]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor2(a[i]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] += swz_xor<4>(a[i]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] += swz_xor<8>(a[i]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] += swz_xor<16>(a[i]);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] += __shfl_xor(a[i], 32);
+    if (lane == 0) {
+      float* out = p.part_out + (int64_t)t * (p.E + 1) * p.pstride + blockIdx.x;
+#pragma unroll
+      for (int i = 0; i < kDnRouterPerWave; ++i) {
+        const int er = wave + kDownWaves * i;
+        if (er < p.E) out[(int64_t)er * p.pstride] = a[i];
+      }
+      if (wave == 0) out[(int64_t)p.E * p.pstride] = a[kDnRouterPerWave];
+    }
+    return;
+  }
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
     const int row = r0 + b;
     if (row >= p.H) continue;
@@ -447,6 +627,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
     for (int j = 0; j < p.K; ++j) v = __builtin_fmaf(p.w[t * p.K + j], dpart[j * B + b], v);
     if (p.x_out) p.x_out[(int64_t)t * p.H + row] = v;
     if (p.y_out) p.y_out[(int64_t)t * p.H + row] = v;
+    if (p.trace_out) p.trace_out[(int64_t)t * p.H + row] = v;
   }
 }
 
@@ -486,8 +667,12 @@ struct bdg_plan {
   void* dev_base;
   bdg::LayerDev* layers;
   float* resid[2];
-  float* r;
-  float* logits;
+  float* part;              // [M][E][pstride] router partial sums
+  int pstride;
+  int dn_blocks;            // down row blocks per token
+  int fuse_route;           // layers >= 1 route from the previous down kernel's partial sums
+  int log2T;
+  const float** wr;         // host copy of each layer's router pointer
   int32_t* idx;
   float* w;
   float* h;
@@ -541,13 +726,11 @@ struct Prof {
 // layer input: the caller's x at layer 0, else the residual buffer written
 // by the previous layer's down kernel.
 static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype, int m,
-                        float* resid_trace, int compute_logits, int norm, hipStream_t s, Prof* prof) {
+                        float* resid_trace, int compute_logits, hipStream_t s, Prof* prof) {
   RouteParams rp{};
   rp.M = m;
   rp.H = p->d.hidden;
   rp.E = p->d.n_experts;
-  rp.norm = norm;
-  rp.eps = p->d.norm_eps;
   rp.compute_logits = compute_logits;
   if (layer == 0) {
     rp.x_in = x;
@@ -559,8 +742,8 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
     rp.x_copy = nullptr;
   }
   rp.resid_trace = resid_trace;
-  rp.r_out = p->r;
-  rp.logits = p->logits;
+  rp.part = p->part;
+  rp.pstride = p->pstride;
   rp.layers = p->layers;
   rp.layer = layer;
   const int nblk = compute_logits ? (rp.E + kWaves - 1) / kWaves : 1;
@@ -569,7 +752,7 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
   return launch_status();
 }
 
-static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, const int32_t* idx_in,
+static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int nparts, const int32_t* idx_in,
                          const float* w_in, int32_t* topk_trace, float* wts_trace, int use_norm,
                          hipStream_t s, Prof* prof) {
   GateUpParams gp{};
@@ -579,7 +762,12 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, const 
   gp.E = p->d.n_experts;
   gp.K = p->d.top_k;
   gp.routed = routed;
-  gp.logits = p->logits;
+  gp.part = p->part;
+  gp.nparts = nparts;
+  gp.pstride = p->pstride;
+  gp.log2T = p->log2T;
+  gp.norm = use_norm;
+  gp.eps = p->d.norm_eps;
   gp.idx_in = idx_in;
   gp.w_in = w_in;
   gp.idx_out = p->idx;
@@ -587,7 +775,6 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, const 
   gp.topk_trace = topk_trace;
   gp.wts_trace = wts_trace;
   gp.x = p->resid[layer & 1];
-  gp.r = use_norm ? p->r : nullptr;
   gp.layers = p->layers;
   gp.layer = layer;
   gp.g = p->gu_geom;
@@ -596,7 +783,9 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, const 
   const int64_t per_block = (int64_t)kWaves * kGuPairsPerWave;
   int64_t blocks = (pairs + per_block - 1) / per_block;
   if (blocks > 65535) return BDG_E_UNSUPPORTED;
-  const size_t lds = (size_t)gp.g.chunks * kXStride * sizeof(float);
+  const int E = gp.E;
+  const size_t psum = (size_t)E << p->log2T;
+  const size_t lds = ((size_t)gp.g.chunks * kXStride + kWaves + psum) * sizeof(float);
   dim3 grid((unsigned)blocks, m);
   const int fmt = p->d.fmt, V = p->topk_V;
 #define BDG_GU_CASE(F, SS, VV)                                                                            \
@@ -621,7 +810,7 @@ static int down_stage_f4(int K, int I) {
 }
 
 static int launch_down(const bdg_plan* p, int layer, int m, int residual, float* x_out, float* y_out,
-                       hipStream_t s, Prof* prof) {
+                       float* trace_out, int route_next, hipStream_t s, Prof* prof) {
   DownParams dp{};
   dp.M = m;
   dp.H = p->d.hidden;
@@ -635,6 +824,11 @@ static int launch_down(const bdg_plan* p, int layer, int m, int residual, float*
   dp.x_prev = p->resid[layer & 1];
   dp.x_out = x_out;
   dp.y_out = y_out;
+  dp.trace_out = trace_out;
+  dp.route_next = route_next;
+  dp.wr_next = route_next ? p->wr[layer + 1] : nullptr;
+  dp.part_out = p->part;
+  dp.pstride = p->pstride;
   dp.layers = p->layers;
   dp.layer = layer;
   dp.g = p->dn_geom;
@@ -677,16 +871,23 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
   const int K = p->d.top_k;
   const int H = p->d.hidden;
   const int stack = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
+  auto trace = [&](int l) { return k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr; };
   for (int l = 0; l < L; ++l) {
-    int st = launch_route(p, l, k.x, k.x_dtype, k.m,
-                          k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr, 1, stack, s, prof);
-    if (st) return st;
-    st = launch_gateup(p, l, k.m, 0, nullptr, nullptr,
+    // layer l's router sums: the route kernel, or the previous down kernel
+    const bool fused = p->fuse_route && l > 0;
+    int st = BDG_OK;
+    if (!fused) {
+      st = launch_route(p, l, k.x, k.x_dtype, k.m, trace(l), 1, s, prof);
+      if (st) return st;
+    }
+    st = launch_gateup(p, l, k.m, 0, fused ? p->dn_blocks : 1, nullptr, nullptr,
                        k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
                        k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof);
     if (st) return st;
     const bool last = l + 1 == L;
-    st = launch_down(p, l, k.m, stack, last ? nullptr : p->resid[(l + 1) & 1], last ? k.y : nullptr, s, prof);
+    const bool feed = !last && p->fuse_route;
+    st = launch_down(p, l, k.m, stack, last ? nullptr : p->resid[(l + 1) & 1], last ? k.y : nullptr,
+                     feed ? trace(l + 1) : nullptr, feed ? 1 : 0, s, prof);
     if (st) return st;
   }
   return BDG_OK;
@@ -762,6 +963,17 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     if (nr < 1) nr = 1;
     if (nr > 4) nr = 4;
     p->dn_NR = env_int("BDG_DN_NR", nr, 1, 4);
+    const int B = p->dn_NR * rpw * wpe;
+    p->dn_blocks = (d->hidden + B - 1) / B;
+    // a layer routes from the previous down kernel's partial sums when the
+    // sums are small enough for every gate_up block to add them up
+    p->fuse_route = (d->flags & BDG_MOE_STACK) && d->n_layers > 1 && B <= kWave &&
+                    p->dn_blocks <= 4 * kThreads && d->n_experts <= kDownWaves * kDnRouterPerWave &&
+                    env_int("BDG_FUSE_ROUTE", 1, 0, 1);
+    p->pstride = ((p->fuse_route ? p->dn_blocks : 1) + 3) & ~3;
+    int lt = 0;
+    while (lt < 6 && (d->n_experts << (lt + 1)) <= kThreads) ++lt;
+    p->log2T = lt;
   }
   auto geom = [&](int k) {
     QGeom g;
@@ -780,8 +992,7 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_layers = off; off = align256(off + sizeof(LayerDev) * d->n_layers);
   const size_t o_res0 = off; off = align256(off + sizeof(float) * M * H);
   const size_t o_res1 = off; off = align256(off + sizeof(float) * M * H);
-  const size_t o_r = off; off = align256(off + sizeof(float) * M);
-  const size_t o_log = off; off = align256(off + sizeof(float) * M * E);
+  const size_t o_part = off; off = align256(off + sizeof(float) * (size_t)M * (E + 1) * p->pstride);
   const size_t o_idx = off; off = align256(off + sizeof(int32_t) * M * K);
   const size_t o_w = off; off = align256(off + sizeof(float) * M * K);
   const size_t o_h = off; off = align256(off + sizeof(float) * (size_t)M * K * I);
@@ -793,19 +1004,22 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->layers = reinterpret_cast<LayerDev*>(base + o_layers);
   p->resid[0] = reinterpret_cast<float*>(base + o_res0);
   p->resid[1] = reinterpret_cast<float*>(base + o_res1);
-  p->r = reinterpret_cast<float*>(base + o_r);
-  p->logits = reinterpret_cast<float*>(base + o_log);
+  p->part = reinterpret_cast<float*>(base + o_part);
   p->idx = reinterpret_cast<int32_t*>(base + o_idx);
   p->w = reinterpret_cast<float*>(base + o_w);
   p->h = reinterpret_cast<float*>(base + o_h);
   LayerDev* host = new (std::nothrow) LayerDev[d->n_layers];
-  if (!host) {
+  p->wr = new (std::nothrow) const float*[d->n_layers];
+  if (!host || !p->wr) {
+    delete[] host;
+    delete[] p->wr;
     (void)hipFree(p->dev_base);
     delete p;
     return BDG_E_NOMEM;
   }
   for (int l = 0; l < d->n_layers; ++l) {
     const bdg_layer_desc& S = d->layers[l];
+    p->wr[l] = S.w_router;
     LayerDev& D = host[l];
     D.w_r = S.w_router;
     D.b_r = S.b_router;
@@ -829,6 +1043,7 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
     if (e3 == hipSuccess) (void)hipStreamDestroy(p->cap_stream);
     (void)hipFree(p->dev_base);
+    delete[] p->wr;
     delete p;
     return BDG_E_HIP;
   }
@@ -849,6 +1064,7 @@ extern "C" int moe_plan_destroy(bdg_plan* p) {
     delete[] p->prof_kind;
   }
   (void)hipFree(p->dev_base);
+  delete[] p->wr;
   delete p;
   return BDG_OK;
 }
@@ -941,14 +1157,12 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   rp.M = m;
   rp.H = p->d.hidden;
   rp.E = p->d.n_experts;
-  rp.norm = 0;
-  rp.eps = 0.f;
   rp.compute_logits = 0;
   rp.x_in = x;
   rp.x_bf16 = x_dtype == BDG_BF16 ? 1 : 0;
   rp.x_copy = p->resid[layer & 1];
-  rp.r_out = p->r;
-  rp.logits = p->logits;
+  rp.part = p->part;
+  rp.pstride = p->pstride;
   rp.layers = p->layers;
   rp.layer = layer;
   hipLaunchKernelGGL(moe_route_kernel, dim3(1, m), dim3(kThreads), (size_t)(rp.H + kWaves) * sizeof(float), s,
@@ -956,9 +1170,9 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   int st = launch_status();
   if (st) return st;
   // gate_up runs on the raw x (no norm), routing from the caller
-  st = launch_gateup(p, layer, m, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
+  st = launch_gateup(p, layer, m, 1, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
   if (st) return st;
-  return launch_down(p, layer, m, 0, nullptr, y, s, nullptr);
+  return launch_down(p, layer, m, 0, nullptr, y, nullptr, 0, s, nullptr);
 }
 
 // ---------------------------------------------------------------- standalone router

@@ -78,7 +78,11 @@ def test_layer_small(dev, fmt, m):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4g"])
-def test_stack_small_end_to_end(dev, fmt):
+@pytest.mark.parametrize("fuse", ["1", "0"])
+def test_stack_small_end_to_end(dev, fmt, fuse, monkeypatch):
+    """fuse=1: layers after the first route from the partial router sums of
+    the previous down kernel; fuse=0: every layer runs the route kernel."""
+    monkeypatch.setenv("BDG_FUSE_ROUTE", fuse)
     cfg = small_cfg(fmt, 1100, E=16, k=4, H=512, I=256, L=3, stack=True, m=2)
     plan, layers, x, y, tr = run_and_check(cfg, dev, 2)
     # end to end without teacher forcing on the residual (routing forced only in band)
@@ -190,28 +194,32 @@ def test_stack_full(dev, name, check_layers):
 
 
 @pytest.mark.parametrize("E,k", [(32, 4), (128, 8), (256, 8), (300, 16)])
-def test_layer_routing_ties(dev, E, k):
+@pytest.mark.parametrize("L", [1, 2])
+def test_layer_routing_ties(dev, E, k, L):
     """The expert selection inside the fused path on tie-heavy logits: zero
     router rows, so each logit is its bias, drawn from a small value set with
     -inf entries.  The selection must match the oracle's order exactly (ties
-    to the lower index), and the layer output the oracle's for those picks."""
-    cfg = small_cfg("mxfp4", 1500 + E, E=E, k=k, H=128, I=64, m=2)
+    to the lower index), and the layer output the oracle's for those picks.
+    L=2 checks the second layer of a residual stack, which (for E <= 64)
+    routes from the partial sums written by the first layer's down kernel."""
+    cfg = small_cfg("mxfp4", 1500 + E, E=E, k=k, H=128, I=64, m=2, L=L, stack=L > 1)
     rng = np.random.default_rng(E)
     b = rng.choice(np.array([1.0, 0.5, 0.5, 0.0, -np.inf], dtype=np.float32), size=E)
     b[rng.choice(E, size=k + 1, replace=False)] = 0.25
     w_r = np.zeros((E, cfg.hidden), dtype=np.float32)
-    layer = sdev.upload_layer(cfg, 0, dev)
-    layer["w_router"] = torch.from_numpy(w_r).to(dev)
-    layer["b_router"] = torch.from_numpy(b).to(dev)
-    plan, _ = sdev.build_plan(cfg, dev, max_m=2, layers=[layer])
+    layers = [sdev.upload_layer(cfg, l, dev) for l in range(L)]
+    layers[-1]["w_router"] = torch.from_numpy(w_r).to(dev)
+    layers[-1]["b_router"] = torch.from_numpy(b).to(dev)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=2, layers=layers)
     x, xv = sdev.hidden_device(cfg, [0, 1], dev)
-    banner(f"moe_expert_decode routing ties E={E} k={k}")
+    banner(f"moe_expert_decode routing ties E={E} k={k} L={L}")
     y, tr = bdg.moe_expert_decode(plan, x, traces=True)
     torch.cuda.synchronize()
-    y, topk, wts = to_np(y), to_np(tr["topk"])[0], to_np(tr["wts"])[0]
+    y, topk, wts = to_np(y), to_np(tr["topk"])[L - 1], to_np(tr["wts"])[L - 1]
     o_idx, o_w = omoe.topk_softmax(np.tile(b.astype(np.float64), (2, 1)), k)
     assert np.array_equal(topk, o_idx)
     assert np.max(np.abs(wts - o_w)) <= W_TOL
-    res = omoe.moe_layer(xv, w_r, oracle_expert_getter(cfg, 0), k, bias=b, norm=False, residual=False,
-                         forced_idx=topk)
-    assert_close(y, res["y"], res["den"], f"ties E={E}")
+    xin = to_np(tr["resid"])[L - 1] if L > 1 else xv
+    res = omoe.moe_layer(xin, w_r, oracle_expert_getter(cfg, L - 1), k, bias=b, norm=L > 1,
+                         residual=L > 1, forced_idx=topk)
+    assert_close(y, res["y"], res["den"], f"ties E={E} L={L}")
