@@ -57,19 +57,28 @@ KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csr
                   "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
 
 
+def kernel_sources_sha():
+    """Hash of the kernel sources' code (comments and blank lines dropped), so a
+    counter summary stays valid across comment-only edits and no longer."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        text = open(os.path.join(ROOT, f)).read()
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
     none or the kernel sources changed since it was taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest()[:16] != rec.get("kernel_sources_sha"):
+    if kernel_sources_sha() != rec.get("kernel_sources_sha"):
         return None
     t = rec["per_launch"].get(kernel)
     return None if t is None else t["fetch_bytes"] + t["write_bytes"]

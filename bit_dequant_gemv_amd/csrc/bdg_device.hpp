@@ -23,7 +23,7 @@ constexpr int kXStride = 36;        // LDS floats per staged x chunk (32 + 4 pad
 // ---------------------------------------------------------------- global loads
 
 // Loads through explicit global (address space 1) pointers: pointers read
-// from a device table are generic to the compiler, which would otherwise emit
+// from kernel-argument structs or tables are generic to the compiler, which would otherwise emit
 // flat loads.  Callers pass in-bounds addresses and issue these loads
 // unconditionally (no branch around a load), so the compiler waits for a
 // load's data only at its first use.

@@ -6,18 +6,22 @@
 // gpt-oss-20B (MXFP4) on Apple Silicon", section 3: "4 sequential experts x
 // 2 small-block GEMVs", dispatch-bound); running the active experts together
 // is named there as the untried lever (section 5), and the TinyTitan tracker
-// moves a layer's experts into one submission (entry D114).  Here each layer
-// is three kernels, each over ALL chosen experts of the layer:
-//   route  : RMSNorm statistics of the layer input and the router GEMV, one
-//            router row per wavefront, the row's loads issued before the
-//            input is staged;
-//   gate_up: every wavefront computes the top-k + softmax itself from the
-//            logits, issues the loads of all its (g, u) row pairs at once,
-//            then stages x and runs the grouped dequant-GEMV of all k
-//            experts with the SwiGLU epilogue h = silu(g) * u;
-//   down   : one block per row block, one wavefront per chosen expert:
+// moves a layer's experts into one submission (entry D114).  Here a layer is
+// at most three kernels, each over ALL chosen experts of the layer:
+//   route  : the router GEMV (one router row per wavefront, the row's loads
+//            issued before the input is staged) and the input's sum of
+//            squares, as one slice of router partial sums; in a stack it
+//            runs for the first layer only (or every layer when E > 64);
+//   gate_up: adds the router slices, applies the RMSNorm scale and bias,
+//            and every wavefront computes the top-k + softmax itself; it
+//            issues the loads of all its (g, u) row pairs at once, then
+//            stages x and runs the grouped dequant-GEMV of all k experts
+//            with the SwiGLU epilogue h = silu(g) * u;
+//   down   : one block per row block, waves split over the chosen experts:
 //            grouped dequant-GEMV over h, then the router-weighted combine
-//            and the residual add in LDS, in a fixed expert order.
+//            and the residual add in LDS, in a fixed expert order; in a
+//            stack it also writes the next layer's router slice for its
+//            rows, which saves that layer's route kernel.
 // A whole token is one captured HIP graph (the per-token setup amortised as
 // in the host-sync page, section 3).
 #include <hip/hip_ext.h>
@@ -37,7 +41,9 @@ constexpr int kDownWaves = 8;        // waves per down block
 constexpr int kGuPairsPerWave = 6;   // gate_up: (g, u) row pairs in flight per wave
 constexpr int kRouteMaxF4 = 16;      // router row float4 per lane (H <= 4096)
 
-// Weight addresses of one layer, kept in a device table by the plan.
+// Weight addresses of one layer.  The plan keeps one per layer on the host
+// and passes it by value to each kernel launch (a kernel argument, so the
+// first weight load does not wait for a dependent table load).
 struct LayerDev {
   const float* w_r;
   const float* b_r;
@@ -179,8 +185,7 @@ struct RouteParams {
   float* resid_trace; // [M][H] or NULL, written by block 0
   float* part;        // [M][E + 1][pstride]: slice 0 written
   int pstride;
-  const LayerDev* layers;
-  int layer;
+  LayerDev L;         // this layer's weights (a kernel argument: no dependent table load)
 };
 
 // One router row per wavefront; block b handles rows 4b .. 4b+3 of token t.
@@ -193,7 +198,7 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
   const int wave = uniform_wave_id();
   const int e = blockIdx.x * kWaves + wave;
   const bool row_ok = p.compute_logits && e < p.E;
-  const LayerDev L = p.layers[p.layer];
+  const LayerDev& L = p.L;
 
   // the router row first: its loads do not depend on x
   // in-bounds clamped addresses, loads issued unconditionally; entries past
@@ -282,8 +287,7 @@ struct GateUpParams {
   int32_t* topk_trace;        // [M][K] or NULL
   float* wts_trace;
   const float* x;             // [M][H] layer input (fp32)
-  const LayerDev* layers;
-  int layer;
+  LayerDev L;                 // this layer's weights
   QGeom g;                    // reduction over H
   float* h_out;               // [M][K][I]
 };
@@ -305,7 +309,7 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   const int wave = uniform_wave_id();
   const int li = lane % L;
   const bool is_up = lane >= L;
-  const LayerDev Ld = p.layers[p.layer];
+  const LayerDev& Ld = p.L;
 
   // load order: routing inputs, then x (independent of the routing), then
   // the expert weights - the in-order wait for each stays short
@@ -488,8 +492,7 @@ struct DownParams {
   const float* wr_next;       // [E][H]
   float* part_out;            // [M][E + 1][pstride]
   int pstride;
-  const LayerDev* layers;
-  int layer;
+  LayerDev L;                 // this layer's weights
   QGeom g;                    // reduction over I
 };
 
@@ -519,7 +522,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   const int jw = wave % kg;                                 // expert within the group
   const int sub = wave / kg;                                // row-group phase (sub < wpe, or idle)
   const bool wave_on = sub < wpe;
-  const LayerDev Ld = p.layers[p.layer];
+  const LayerDev& Ld = p.L;
 
   // loads, in the order their data is needed (vmcnt retires in order):
   // the first group's expert id, the epilogue operands (router weights of
@@ -527,7 +530,9 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   // unconditionally so the compiler's wait counts stay exact), then per
   // group the h vectors and the expert weights
   int e_next = clamp_expert(p.idx[t * p.K + (jw < p.K ? jw : p.K - 1)], p.E);
-  const int orow = r0 + lane < p.H ? r0 + lane : p.H - 1;  // epilogue row of this lane (B <= 64)
+  // epilogue row of this lane (B <= 64); idle lanes repeat the block's last
+  // row, so their loads fall in lines the block reads anyway
+  const int orow = min(r0 + min(lane, B - 1), p.H - 1);
   float wr[kDnRouterPerWave];                               // wr[i] = w_r'[wave + 8i][orow]
   {
     const float* wsrc = p.route_next ? p.wr_next : p.x_prev;
@@ -595,7 +600,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
     constexpr int NA = kDnRouterPerWave + 1;
     float a[NA];
 #pragma unroll
-    for (int i = 0; i < kDnRouterPerWave; ++i) a[i] = wr[i] * v;
+    for (int i = 0; i < kDnRouterPerWave; ++i) a[i] = ok ? wr[i] * v : 0.f;
     a[kDnRouterPerWave] = v * v;
 #pragma unroll
     for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor1(a[i]);
@@ -665,7 +670,7 @@ struct bdg_plan {
   bdg::QGeom gu_geom, dn_geom;
   // device memory
   void* dev_base;
-  bdg::LayerDev* layers;
+  bdg::LayerDev* hl;        // host copy of each layer's weight pointers (passed by value to the kernels)
   float* resid[2];
   float* part;              // [M][E][pstride] router partial sums
   int pstride;
@@ -744,8 +749,7 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
   rp.resid_trace = resid_trace;
   rp.part = p->part;
   rp.pstride = p->pstride;
-  rp.layers = p->layers;
-  rp.layer = layer;
+  rp.L = p->hl[layer];
   const int nblk = compute_logits ? (rp.E + kWaves - 1) / kWaves : 1;
   const size_t lds = (size_t)(rp.H + kWaves) * sizeof(float);
   BDG_LAUNCH(prof, kRoute, moe_route_kernel, dim3(nblk, m), dim3(kThreads), lds, s, rp);
@@ -775,8 +779,7 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int np
   gp.topk_trace = topk_trace;
   gp.wts_trace = wts_trace;
   gp.x = p->resid[layer & 1];
-  gp.layers = p->layers;
-  gp.layer = layer;
+  gp.L = p->hl[layer];
   gp.g = p->gu_geom;
   gp.h_out = p->h;
   const int64_t pairs = (int64_t)gp.K * gp.I;
@@ -829,8 +832,7 @@ static int launch_down(const bdg_plan* p, int layer, int m, int residual, float*
   dp.wr_next = route_next ? p->wr[layer + 1] : nullptr;
   dp.part_out = p->part;
   dp.pstride = p->pstride;
-  dp.layers = p->layers;
-  dp.layer = layer;
+  dp.L = p->hl[layer];
   dp.g = p->dn_geom;
   const int rpw = kWave / p->dn_L;
   const int kg = dp.K < kDownWaves ? dp.K : kDownWaves;
@@ -989,7 +991,6 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   // device memory: layer table + workspace
   const int M = d->max_m, H = d->hidden, I = d->inter, E = d->n_experts, K = d->top_k;
   size_t off = 0;
-  const size_t o_layers = off; off = align256(off + sizeof(LayerDev) * d->n_layers);
   const size_t o_res0 = off; off = align256(off + sizeof(float) * M * H);
   const size_t o_res1 = off; off = align256(off + sizeof(float) * M * H);
   const size_t o_part = off; off = align256(off + sizeof(float) * (size_t)M * (E + 1) * p->pstride);
@@ -1001,7 +1002,6 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     return BDG_E_NOMEM;
   }
   char* base = static_cast<char*>(p->dev_base);
-  p->layers = reinterpret_cast<LayerDev*>(base + o_layers);
   p->resid[0] = reinterpret_cast<float*>(base + o_res0);
   p->resid[1] = reinterpret_cast<float*>(base + o_res1);
   p->part = reinterpret_cast<float*>(base + o_part);
@@ -1036,14 +1036,14 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     D.dn_ss = S.down.expert_stride_scales;
     D.dn_sz = S.down.expert_stride_zeros;
   }
-  hipError_t e1 = hipMemcpy(p->layers, host, sizeof(LayerDev) * d->n_layers, hipMemcpyHostToDevice);
-  delete[] host;
+  p->hl = host;
   hipError_t e2 = hipMemset(base + o_res0, 0, off - o_res0);
   hipError_t e3 = hipStreamCreateWithFlags(&p->cap_stream, hipStreamNonBlocking);
-  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+  if (e2 != hipSuccess || e3 != hipSuccess) {
     if (e3 == hipSuccess) (void)hipStreamDestroy(p->cap_stream);
     (void)hipFree(p->dev_base);
     delete[] p->wr;
+    delete[] p->hl;
     delete p;
     return BDG_E_HIP;
   }
@@ -1065,6 +1065,7 @@ extern "C" int moe_plan_destroy(bdg_plan* p) {
   }
   (void)hipFree(p->dev_base);
   delete[] p->wr;
+  delete[] p->hl;
   delete p;
   return BDG_OK;
 }
@@ -1163,8 +1164,7 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   rp.x_copy = p->resid[layer & 1];
   rp.part = p->part;
   rp.pstride = p->pstride;
-  rp.layers = p->layers;
-  rp.layer = layer;
+  rp.L = p->hl[layer];
   hipLaunchKernelGGL(moe_route_kernel, dim3(1, m), dim3(kThreads), (size_t)(rp.H + kWaves) * sizeof(float), s,
                      rp);
   int st = launch_status();

@@ -168,8 +168,9 @@ typedef struct bdg_moe_desc {
 typedef struct bdg_plan bdg_plan;
 
 /* moe_plan_create - validate a model geometry once and build what every
- * decode step reuses: device tables of per-layer, per-expert weight
- * addresses, the workspace (residual, routing, intermediate activations),
+ * decode step reuses: the per-layer weight addresses (baked into each
+ * captured kernel launch), the workspace (residual, routing partial sums,
+ * intermediate activations),
  * and a cache of captured per-token HIP graphs.  The session-keyed setup
  * cache of the host-sync page (section 3): nothing of this is rebuilt per
  * token; a change of any weight pointer, shape or flag needs a new plan.
