@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE expert-decode path on one MI355X.
 
-A step is one decode token (M = 1) through every layer of the workload: per
-layer the route kernel (combine + residual + RMSNorm + router GEMV), the
-grouped gate_up dequant-GEMV with SwiGLU over the k chosen experts, and the
-grouped down dequant-GEMV - replayed from one captured HIP graph per token.
-Each token gets a fresh N(0,1) bf16 hidden state; all inputs and weights are
-resident in HBM before the timed region.  W untimed warmup tokens, then K
-timed tokens bracketed by stream events and device synchronisation.
+A step is one decode step of M tokens (M = 1 for the headline stacks, M = 4
+or 16 for the 120B-shape small-M workload) through every layer: per layer the
+router (a route kernel, or partial sums from the previous down kernel), the
+grouped gate_up dequant-GEMV with SwiGLU over the chosen experts, and the
+grouped down dequant-GEMV with the weighted combine and residual - replayed
+from one captured HIP graph per step.  Every token gets a fresh N(0,1) bf16
+hidden state; all inputs and weights are resident in HBM before the timed
+region.  W untimed warmup steps, then K timed steps bracketed by stream
+events and device synchronisation.
 
 Prints one JSON line: the expert-path HBM rate (algorithmic packed-weight
-bytes of the chosen experts plus the router weights, over GPU time), the
-per-kernel roofline figure of the dominant kernel (gate_up), the measured
-streaming-read rate, and the CPU oracle timed on a bounded sample.
+bytes of every (layer, expert) matrix the step uses, once, plus the router
+weights, over GPU time), the per-kernel roofline figure of the dominant
+kernel (gate_up), the measured streaming-read rate, and the CPU oracle timed
+on a bounded sample.
 """
 
 import argparse
@@ -84,12 +87,12 @@ def measured_traffic(workload, kernel):
     return None if t is None else t["fetch_bytes"] + t["write_bytes"]
 
 
-def cpu_baseline(cfg, sample_layers, token):
-    """The oracle as it stands, token-major, on `sample_layers` layers of one token.
+def cpu_baseline(cfg, sample_layers, m):
+    """The oracle as it stands on `sample_layers` layers of one step (M tokens).
 
     Packed weights of the sampled layers are generated first (untimed), the
     oracle then dequantizes the chosen experts on demand and runs its float64
-    layer; the per-layer time is scaled to a whole token.
+    layer; the per-layer time is scaled to a whole step of every layer.
     """
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -103,8 +106,9 @@ def cpu_baseline(cfg, sample_layers, token):
         w_r, b_r, _ = synth.router(cfg, l)
         experts = [synth.expert_weights(cfg, l, e) for e in range(cfg.n_experts)]
         gen.append((w_r, b_r, experts))
-    x = synth.hidden(cfg, token)[0][None, :].astype(np.float64)
+    x = synth.hidden_batch(cfg, range(m))[0].astype(np.float64)
     log("cpu baseline: timing the oracle")
+    uniq = []
     t0 = time.perf_counter()
     for l in range(sample_layers):
         w_r, b_r, experts = gen[l]
@@ -116,20 +120,21 @@ def cpu_baseline(cfg, sample_layers, token):
             return (formats.int4g_dequant(*w["gu"], cfg.group),
                     formats.int4g_dequant(*w["dn"], cfg.group))
         res = omoe.moe_layer(x, w_r, get, cfg.top_k, bias=b_r, norm=cfg.norm, residual=cfg.norm)
+        uniq.append(len(np.unique(res["idx"])))
         x = res["y"]
     dt = time.perf_counter() - t0
-    per_token_s = dt / sample_layers * cfg.n_layers
+    per_step_s = dt / sample_layers * cfg.n_layers
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    nbytes = step_bytes(cfg, [cfg.top_k] * cfg.n_layers)
+    nbytes = step_bytes(cfg, [float(np.mean(uniq))] * cfg.n_layers)
     return {
-        "value": round(nbytes / per_token_s / 1e9, 4),
+        "value": round(nbytes / per_step_s / 1e9, 4),
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "us_per_token": round(per_token_s * 1e6, 1),
-        "sample": (f"{sample_layers} of {cfg.n_layers} layers of token {token} (M=1), "
-                   f"{dt:.1f} s of CPU time, scaled to a whole token; float64 NumPy, "
-                   f"elementwise dequant on one thread, BLAS matvecs on {blas_threads}"),
+        "us_per_token": round(per_step_s / m * 1e6, 1),
+        "sample": f"{sample_layers} of {cfg.n_layers} layers of one step of M={m} tokens, "
+                  f"{dt:.1f} s of CPU time, scaled to a whole step; float64 NumPy, elementwise "
+                  f"dequant on one thread, BLAS matvecs on {blas_threads}",
     }
 
 
@@ -181,9 +186,10 @@ def stream_read_rate(torch, bdg, dev, phase_bytes, gbytes=4.0, reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 64 at M=1, 16 at M>1)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 8 at M=1, 4 at M>1)")
     ap.add_argument("--workload", default="gptoss20b_stack")
+    ap.add_argument("--m", type=int, default=0, help="tokens per step (default: the workload's own)")
     ap.add_argument("--cpu-sample-layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
@@ -199,6 +205,7 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import bit_dequant_gemv_amd as bdg
@@ -219,9 +226,11 @@ def main():
         print(json.dumps({"copy_calibration_bytes": nb, "launches": 4}), flush=True)
         return
     cfg = synth.CONFIGS[args.workload]
-    if cfg.m != 1:
-        raise SystemExit("bench.py times the M=1 workloads")
-    K, W = args.steps, args.warmup
+    m = args.m if args.m else cfg.m
+    if not 1 <= m <= 16:
+        raise SystemExit("--m must be in 1..16")
+    K = args.steps if args.steps is not None else (64 if m == 1 else 16)
+    W = args.warmup if args.warmup is not None else (8 if m == 1 else 4)
 
     t0 = time.time()
     layers = []
@@ -229,24 +238,25 @@ def main():
         layers.append(sdev.upload_layer(cfg, l, dev, threads=16))
         if l % 6 == 5 or l == cfg.n_layers - 1:
             log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.1f} s)")
-    plan, _ = sdev.build_plan(cfg, dev, max_m=1, layers=layers)
-    x_all, _ = sdev.hidden_device(cfg, range(W + K), dev)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers)
+    x_all, _ = sdev.hidden_device(cfg, range((W + K) * m), dev)
+    x_all = x_all.reshape(W + K, m, cfg.hidden)
     x_buf = torch.empty_like(x_all[0])
-    y_buf = torch.empty(cfg.hidden, dtype=torch.float32, device=dev)
+    y_buf = torch.empty((m, cfg.hidden), dtype=torch.float32, device=dev)
 
-    for t in range(W):
-        x_buf.copy_(x_all[t])
+    for s in range(W):
+        x_buf.copy_(x_all[s])
         bdg.moe_expert_decode(plan, x_buf, y=y_buf)
     torch.cuda.synchronize()
-    log(f"warmup done ({W} tokens)")
+    log(f"warmup done ({W} steps of M={m})")
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    for t in range(W, W + K):
-        x_buf.copy_(x_all[t])                  # the next token's hidden state lands in the input buffer
+    for s in range(W, W + K):
+        x_buf.copy_(x_all[s])                  # the next step's hidden states land in the input buffer
         bdg.moe_expert_decode(plan, x_buf, y=y_buf)
     end.record()
     torch.cuda.synchronize()
@@ -254,35 +264,64 @@ def main():
     gpu_ms = start.elapsed_time(end)
     if not torch.isfinite(y_buf).all():
         raise SystemExit("non-finite output")
-    nbytes = step_bytes(cfg, [cfg.top_k] * cfg.n_layers)       # M=1: k distinct experts per layer
-    value = nbytes * K / (gpu_ms * 1e-3) / 1e9
-    log(f"timed {K} tokens: {gpu_ms / K * 1e3:.1f} us/token GPU, {wall / K * 1e6:.1f} us/token wall, "
-        f"{value:.1f} GB/s")
+
+    # unique (layer, expert) matrices per step: M=1 reads k experts per layer;
+    # for M > 1 the same steps are replayed untimed with routing traces
+    gu_bytes, dn_bytes = expert_bytes(cfg)
+    routing = None
+    if m == 1:
+        uniq = [[cfg.top_k] * cfg.n_layers for _ in range(K)]
+    else:
+        uniq, hot_frac, tpe = [], [], []
+        hot_sets = [synth.router(cfg, l)[2] for l in range(cfg.n_layers)]
+        for s in range(W, W + K):
+            x_buf.copy_(x_all[s])
+            _, tr = bdg.moe_expert_decode(plan, x_buf, y=y_buf, traces=True)
+            topk = tr["topk"].cpu().numpy()                       # [L][m][k]
+            uniq.append([len(set(topk[l].ravel().tolist())) for l in range(cfg.n_layers)])
+            if hot_sets[0] is not None:
+                hot_frac.append([float(np.isin(topk[l], hot_sets[l]).mean()) for l in range(cfg.n_layers)])
+            for l in range(cfg.n_layers):
+                tpe.extend(np.bincount(topk[l].ravel(), minlength=cfg.n_experts)[
+                    np.unique(topk[l].ravel())].tolist())
+        hist = np.bincount(np.array(tpe), minlength=m + 1)[1:].tolist()
+        routing = {
+            "unique_experts_per_layer_mean": round(float(np.mean(uniq)), 3),
+            "picks_per_layer": m * cfg.top_k,
+            "tokens_per_active_expert_hist": {str(i + 1): c for i, c in enumerate(hist) if c},
+        }
+        if hot_frac:
+            routing["hot_pick_fraction_per_layer"] = [round(v, 3) for v in np.mean(hot_frac, axis=0)]
+            routing["hot_pick_fraction_mean"] = round(float(np.mean(hot_frac)), 3)
+    nbytes = sum(step_bytes(cfg, u) for u in uniq)
+    value = nbytes / (gpu_ms * 1e-3) / 1e9
+    mean_uniq = float(np.mean(uniq))
+    log(f"timed {K} steps of M={m}: {gpu_ms / K * 1e3:.1f} us/step GPU, {gpu_ms / K / m * 1e3:.1f} us/token, "
+        f"{wall / K * 1e6:.1f} us/step wall, {value:.1f} GB/s (unique experts/layer {mean_uniq:.2f})")
 
     # per-kernel durations, same kernels and grids, start/stop events at each kernel
     acc = None
-    for t in range(W, W + K):
-        x_buf.copy_(x_all[t])
+    for s in range(W, W + K):
+        x_buf.copy_(x_all[s])
         acc = bdg.moe_expert_decode_profiled(plan, x_buf, y_buf, *(acc if acc else (None, None)))
     kms, kcnt = acc
     kernels = {}
     for i, name in enumerate(bdg.KERNEL_KINDS):
         if kcnt[i]:
             kernels[name] = {"avg_us": round(kms[i] / kcnt[i] * 1e3, 3), "launches": int(kcnt[i])}
-    gu_bytes, dn_bytes = expert_bytes(cfg)
-    gu_launch_bytes = cfg.top_k * gu_bytes
+    gu_launch_bytes = int(round(mean_uniq * gu_bytes))
     gu_avg_s = kms[1] / kcnt[1] * 1e-3
     achieved = gu_launch_bytes / gu_avg_s / 1e9
     kernels["gate_up"]["GBps"] = round(achieved, 1)
-    kernels["down"]["GBps"] = round(cfg.top_k * dn_bytes / (kms[2] / kcnt[2] * 1e-3) / 1e9, 1)
+    kernels["down"]["GBps"] = round(mean_uniq * dn_bytes / (kms[2] / kcnt[2] * 1e-3) / 1e9, 1)
     kernels["route"]["GBps"] = round(router_bytes(cfg) / (kms[0] / kcnt[0] * 1e-3) / 1e9, 1)
     sum_kernel_us = sum(kms[i] for i in range(4)) / K * 1e3
-    log(f"per-kernel: {kernels}; kernel time {sum_kernel_us:.1f} us/token of {gpu_ms / K * 1e3:.1f}")
+    log(f"per-kernel: {kernels}; kernel time {sum_kernel_us:.1f} us/step of {gpu_ms / K * 1e3:.1f}")
 
     stream = None
     if not args.no_stream_read:
         best, med, phases = stream_read_rate(
-            torch, bdg, dev, {"gate_up": gu_launch_bytes, "down": cfg.top_k * dn_bytes,
+            torch, bdg, dev, {"gate_up": gu_launch_bytes, "down": int(round(mean_uniq * dn_bytes)),
                               "router": router_bytes(cfg)})
         stream = {"best_GBps": round(best, 1), "median_GBps": round(med, 1), "bytes": "4 GiB",
                   "phase_sized_reads": phases}
@@ -290,9 +329,18 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, args.cpu_sample_layers, token=0)
+        cpu = cpu_baseline(cfg, args.cpu_sample_layers, m)
         log(f"cpu baseline: {cpu}")
 
+    config = {
+        "workload": cfg.name,
+        "fmt": cfg.fmt, "layers": cfg.n_layers, "hidden": cfg.hidden, "inter": cfg.inter,
+        "experts": cfg.n_experts, "top_k": cfg.top_k, "m": m,
+        "bytes_per_step": int(round(nbytes / K)),
+        "timing": "HIP graph per step (M tokens), stream-ordered",
+    }
+    if routing:
+        config["routing"] = routing
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -306,15 +354,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": cfg.name,
-            "fmt": cfg.fmt, "layers": cfg.n_layers, "hidden": cfg.hidden, "inter": cfg.inter,
-            "experts": cfg.n_experts, "top_k": cfg.top_k, "m": 1,
-            "bytes_per_token": nbytes, "timing": "HIP graph per token, stream-ordered",
-        },
+        "config": config,
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
-        "us_per_token": round(gpu_ms / K * 1e3, 2),
-        "wall_us_per_token": round(wall / K * 1e6, 2),
+        "us_per_token": round(gpu_ms / K / m * 1e3, 2),
+        "wall_us_per_token": round(wall / K / m * 1e6, 2),
         "roofline": {
             "kernel": "moe_gateup_kernel",
             "bound": "hbm",
@@ -322,11 +365,11 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(cfg.name, "gate_up"),
+            "traffic": measured_traffic(cfg.name, "gate_up") if m == 1 else None,
             "traffic_algorithmic_bytes": gu_launch_bytes,
         },
         "kernels": kernels,
-        "kernel_us_per_token": round(sum_kernel_us, 2),
+        "kernel_us_per_step": round(sum_kernel_us, 2),
         "stream_read": stream,
         "cpu_baseline": cpu,
     }
