@@ -67,6 +67,19 @@ __device__ __forceinline__ void load_row(GroupLoad<FMT, S>& ld, const QMat& m, c
   }
 }
 
+// Mark a loaded row's registers as rewritten (an empty asm, no instruction):
+// when one row load serves several inputs in a loop, this keeps the compiler
+// from hoisting the decode of all rows out of the loop (which would hold
+// every decoded weight in registers at once).
+template <int FMT, int S>
+__device__ __forceinline__ void pin_regs(GroupLoad<FMT, S>& ld) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    asm volatile("" : "+v"(ld.q[s].x), "+v"(ld.q[s].y), "+v"(ld.q[s].z), "+v"(ld.q[s].w), "+v"(ld.sc[s]));
+    if constexpr (FMT == kINT4G) asm volatile("" : "+v"(ld.zn[s]));
+  }
+}
+
 // The x values of a lane's slots, from the LDS chunk layout (chunk c at
 // floats [c*kXStride, c*kXStride+32)).  Chunks past the end read as 0.
 template <int FMT, int L, int S>

@@ -28,6 +28,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include "bdg_gemv.hpp"
@@ -185,6 +186,12 @@ struct RouteParams {
   float* resid_trace; // [M][H] or NULL, written by block 0
   float* part;        // [M][E + 1][pstride]: slice 0 written
   int pstride;
+  // combine (grouped path): the layer input is x_in (+ x_in when
+  // combine_residual) + sum_j wts[t][j] * dout[t*K + j], j in order
+  const float* dout;  // [M * K][H] previous layer's down output per pick, or NULL
+  const float* wts;   // [M][K]
+  int K;
+  int combine_residual;
   LayerDev L;         // this layer's weights (a kernel argument: no dependent table load)
 };
 
@@ -229,6 +236,29 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
     for (int i = 0; i < NX; ++i) {
       const int h = (i * kThreads + threadIdx.x) * 4;
       xv4[i] = ldg_f4(reinterpret_cast<const float*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
+    }
+  }
+  if (p.dout) {
+    if (!p.combine_residual) {
+#pragma unroll
+      for (int i = 0; i < NX; ++i) xv4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int j = 0; j < p.K; ++j) {
+      const float wj = p.wts[t * p.K + j];
+      const float* dj = p.dout + ((int64_t)t * p.K + j) * p.H;
+      float4 d[NX];
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int h = (i * kThreads + threadIdx.x) * 4;
+        d[i] = ldg_f4(dj + (h < p.H ? h : p.H - 4));
+      }
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        xv4[i].x = __builtin_fmaf(wj, d[i].x, xv4[i].x);
+        xv4[i].y = __builtin_fmaf(wj, d[i].y, xv4[i].y);
+        xv4[i].z = __builtin_fmaf(wj, d[i].z, xv4[i].z);
+        xv4[i].w = __builtin_fmaf(wj, d[i].w, xv4[i].w);
+      }
     }
   }
   float ss = 0.f;
@@ -636,6 +666,339 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   }
 }
 
+// ---------------------------------------------------------------- grouped path (M > 1)
+//
+// With several tokens per step, tokens share experts (the 120B small-M
+// workload reads ~36 distinct experts for 64 picks at M = 16).  The grouped
+// path reads each chosen (layer, expert) matrix once per step: every gate_up
+// block routes all M tokens and builds the same deterministic list of
+// "chunks" - one expert and up to kGroupTT of its picks (token, slot) - then
+// the blocks share the (chunk, row block) items of the layer; the weights of
+// an item are loaded once and applied to each pick's input in turn.  The
+// down kernel does the same over the chunk table gate_up wrote, and writes one
+// output row per pick; the weighted combine with the residual then happens
+// in the next layer's route kernel (or a final combine kernel), in slot
+// order, with the same arithmetic as the per-token down kernel.
+
+constexpr int kGroupTT = 2;           // picks per chunk
+
+// (g, u) row pairs per wave in the grouped gate_up, and down rows per wave:
+// as many as fit 256 VGPRs with the loaded rows held across a chunk's picks.
+__host__ __device__ constexpr int gu_group_np(int fmt, int S) {
+  return fmt == 0 ? (S <= 3 ? 6 : 4) : (S <= 2 ? 6 : 4);
+}
+__host__ __device__ constexpr int dn_group_nr(int fmt, int L, int S) {
+  return (kWave / L <= 2 && (fmt == 0 || L * S < 96)) ? 4 : 2;
+}
+constexpr int kGroupMaxPicks = 128;   // M * K bound of the grouped path
+constexpr int kChunkInts = 2 + kGroupTT;
+
+struct GroupLds {
+  int sel_e[kGroupMaxPicks];          // pick p = t*K + j -> expert
+  float rt[BDG_MAX_M];                // RMSNorm scale per token
+  unsigned used[BDG_MAX_EXPERTS / 32];
+  int ppc[BDG_MAX_EXPERTS / 32 + 1];  // prefix popcounts of used[]
+  int cnt[kGroupMaxPicks];            // picks per distinct expert (by rank)
+  int cbase[kGroupMaxPicks + 1];      // first chunk of each distinct expert
+  int n;                              // chunks
+  int ce[kGroupMaxPicks];             // expert of chunk c
+  int cn[kGroupMaxPicks];             // picks in chunk c
+  int cpk[kGroupMaxPicks][kGroupTT];  // the picks of chunk c
+};
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Chunks of the P picks in g.sel_e: distinct experts in ascending order, the
+// picks of each in pick order, kGroupTT per chunk.  The block's threads all
+// call it; the result does not depend on thread timing (the only atomics are
+// an OR and a count).  P <= kGroupMaxPicks, blockDim >= kGroupMaxPicks.
+__device__ void build_groups(GroupLds& g, int P, int E) {
+  const int tid = threadIdx.x;
+  const int nw = (E + 31) >> 5;
+  if (tid < nw) g.used[tid] = 0u;
+  if (tid < P) g.cnt[tid] = 0;
+  __syncthreads();
+  if (tid < P) atomicOr(&g.used[g.sel_e[tid] >> 5], 1u << (g.sel_e[tid] & 31));
+  __syncthreads();
+  if (tid < kWave) {
+    const int pc = wave_scan_incl(tid < nw ? __popc(g.used[tid]) : 0);
+    if (tid < nw) g.ppc[tid + 1] = pc;
+    if (tid == 0) g.ppc[0] = 0;
+  }
+  __syncthreads();
+  int my_u = 0, my_pos = 0;
+  if (tid < P) {
+    const int e = g.sel_e[tid];
+    my_u = g.ppc[e >> 5] + __popc(g.used[e >> 5] & ((1u << (e & 31)) - 1u));
+    for (int q = 0; q < tid; ++q) my_pos += g.sel_e[q] == e ? 1 : 0;
+    atomicAdd(&g.cnt[my_u], 1);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int U = g.ppc[nw];
+    const int a = tid < U ? (g.cnt[tid] + kGroupTT - 1) / kGroupTT : 0;
+    const int b = tid + kWave < U ? (g.cnt[tid + kWave] + kGroupTT - 1) / kGroupTT : 0;
+    const int sa = wave_scan_incl(a);
+    const int sb = wave_scan_incl(b);
+    const int tot_a = __shfl(sa, kWave - 1);
+    g.cbase[tid] = sa - a;
+    g.cbase[tid + kWave] = tot_a + sb - b;
+    if (tid == kWave - 1) g.n = tot_a + sb;
+  }
+  __syncthreads();
+  if (tid < P) {
+    const int c = g.cbase[my_u] + my_pos / kGroupTT;
+    const int k = my_pos % kGroupTT;
+    g.cpk[c][k] = tid;
+    if (k == 0) {
+      g.ce[c] = g.sel_e[tid];
+      g.cn[c] = min(kGroupTT, g.cnt[my_u] - my_pos);
+    }
+  }
+  __syncthreads();
+}
+
+struct GroupParams {
+  int M, H, I, E, K;
+  int routed;                 // 1: routing given in idx_in / w_in
+  const float* part;          // [M][E + 1][pstride] router sums, one slice (route kernel)
+  int pstride;
+  int norm;
+  float eps;
+  const int32_t* idx_in;
+  const float* w_in;
+  int32_t* idx_out;           // [M][K]
+  float* w_out;
+  int32_t* topk_trace;        // [M][K] or NULL
+  float* wts_trace;
+  const float* x;             // [M][H] layer input (fp32)
+  LayerDev L;
+  QGeom g;                    // reduction over H
+  float* h_out;               // [M * K][I], row p = t*K + j
+  int32_t* chunks_out;        // chunk table for the down kernel, written by block 0
+  int bpc;                    // row blocks per chunk (a multiple of 8)
+};
+
+__host__ __device__ constexpr size_t group_lds_floats() { return (sizeof(GroupLds) + 15) / 16 * 4; }
+
+// Persistent grid: block b takes items b, b + G, ... of the chunks x row
+// blocks of the layer (a row block = kWaves * NP (g, u) row pairs).  Items of
+// one row block in consecutive chunks are bpc apart, bpc % 8 == 0, so with
+// G % 8 == 0 they run on one XCD (blocks are dealt to the 8 XCDs in turn)
+// and share its L2 when a hot expert spans several chunks.
+template <int FMT, int S, int NP, int V>
+__global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p) {
+  constexpr int L = 32;
+  constexpr int NX = S;                                 // H <= 32 * L * S: float4 of x per thread
+  extern __shared__ float lds[];
+  GroupLds& gl = *reinterpret_cast<GroupLds*>(lds);
+  float* xs = lds + group_lds_floats();                 // [kGroupTT][chunks * kXStride]
+  const int xstride = p.g.chunks * kXStride;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform_wave_id();
+  const int li = lane % L;
+  const bool is_up = lane >= L;
+  const LayerDev& Ld = p.L;
+  const int P = p.M * p.K;
+
+  // routing of every token of the step, a share of the tokens per wave
+  for (int t = wave; t < p.M; t += kWaves) {
+    int my_e = 0;
+    float my_w = 0.f, r = 1.f;
+    if (p.routed) {
+      my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
+      my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
+    } else {
+      const int64_t pb = (int64_t)t * (p.E + 1) * p.pstride;
+      float lg[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = lane + kWave * i;
+        const int ec = e < p.E ? e : p.E - 1;
+        lg[i] = p.part[pb + (int64_t)ec * p.pstride];
+      }
+      const float ssq = p.part[pb + (int64_t)p.E * p.pstride];
+      if (p.norm) r = 1.0f / sqrtf(ssq / (float)p.H + p.eps);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = lane + kWave * i;
+        lg[i] = r * lg[i] + (Ld.b_r ? Ld.b_r[e < p.E ? e : p.E - 1] : 0.f);
+      }
+      topk_rank<V>(lg, p.E, p.K, my_e, my_w);
+    }
+    if (lane < p.K) {
+      gl.sel_e[t * p.K + lane] = my_e;
+      if (blockIdx.x == 0) {
+        p.idx_out[t * p.K + lane] = my_e;
+        p.w_out[t * p.K + lane] = my_w;
+        if (p.topk_trace) p.topk_trace[t * p.K + lane] = my_e;
+        if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
+      }
+    }
+    if (lane == 0) gl.rt[t] = r;
+  }
+  __syncthreads();
+  build_groups(gl, P, p.E);
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) p.chunks_out[0] = gl.n;
+    for (int c = threadIdx.x; c < gl.n; c += kThreads) {
+      int32_t* o = p.chunks_out + 1 + c * kChunkInts;
+      o[0] = gl.ce[c];
+      o[1] = gl.cn[c];
+#pragma unroll
+      for (int k = 0; k < kGroupTT; ++k) o[2 + k] = k < gl.cn[c] ? gl.cpk[c][k] : 0;
+    }
+  }
+
+  const int nitems = gl.n * p.bpc;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int c = item / p.bpc;
+    const int r0 = (item - c * p.bpc) * (kWaves * NP);
+    if (r0 >= p.I) continue;                              // block-uniform
+    const int e = gl.ce[c];
+    const int nt = gl.cn[c];
+    // the picks' inputs first, then the expert weights (vmcnt retires in order)
+    StageF32<NX> xst[kGroupTT];
+#pragma unroll
+    for (int k = 0; k < kGroupTT; ++k)
+      if (k < nt) xst[k].load(p.x + (int64_t)(gl.cpk[c][k] / p.K) * p.H, p.H, threadIdx.x, kThreads);
+    const int rw = r0 + wave * NP;                        // this wave's first pair
+    GroupLoad<FMT, S> ld[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int row = rw + i;
+      const bool ok = row < p.I;
+      load_row<FMT, L, S>(ld[i], expert_gu(Ld, e), p.g, is_up ? p.I + row : row, ok, li);
+    }
+    __syncthreads();                                      // the previous item's x reads are done
+#pragma unroll
+    for (int k = 0; k < kGroupTT; ++k)
+      if (k < nt) xst[k].store(xs + k * xstride, p.H, p.H, 0, gl.rt[gl.cpk[c][k] / p.K], threadIdx.x, kThreads);
+    __syncthreads();
+    const int nq = min(max(p.I - rw, 0), NP);
+#pragma unroll 1
+    for (int k = 0; k < nt; ++k) {
+      XRegs<FMT, L, S> xr;
+      xr.load(xs + k * xstride, p.g.chunks, li);
+      float g_sel = 0.f, u_sel = 0.f;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        pin_regs(ld[i]);
+        const float d = row_dot<FMT, L, S>(ld[i], xr);
+        const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 0));
+        const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L));
+        if (lane == i) {
+          g_sel = gv;
+          u_sel = uv;
+        }
+      }
+      if (lane < nq)
+        p.h_out[(int64_t)gl.cpk[c][k] * p.I + rw + lane] = g_sel / (1.0f + expf(-g_sel)) * u_sel;
+    }
+  }
+}
+
+struct DnGroupParams {
+  int H, I, E;
+  const int32_t* chunks;      // chunk table written by the gate_up kernel
+  const float* h;             // [M * K][I]
+  float* dout;                // [M * K][H] down output per pick
+  LayerDev L;
+  QGeom g;                    // reduction over I
+  int nrb;                    // row blocks per chunk (a multiple of 8)
+};
+
+// Persistent grid over (chunk, row block) items; a row block is
+// kWaves * NR * (64 / L) rows of the expert's down matrix, its weights loaded
+// once per item and applied to every pick of the chunk.
+template <int FMT, int L, int S, int NR>
+__global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams p) {
+  constexpr int RPW = kWave / L;
+  constexpr int NH = (L * S + 31) / 32;                // I <= 32 * L * S: float4 of h per thread
+  extern __shared__ float lds[];
+  int* tab = reinterpret_cast<int*>(lds);               // [1 + kGroupMaxPicks * kChunkInts]
+  float* hs = lds + (1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4;   // [kGroupTT][chunks * kXStride]
+  const int hstride = p.g.chunks * kXStride;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform_wave_id();
+  const int li = lane % L;
+  const int rr = lane / L;
+  const int B = NR * RPW * kWaves;
+  const LayerDev& Ld = p.L;
+
+  const int n = p.chunks[0];
+  for (int i = threadIdx.x; i < n * kChunkInts; i += kThreads) tab[1 + i] = p.chunks[1 + i];
+  __syncthreads();
+
+  const int nitems = n * p.nrb;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int c = item / p.nrb;
+    const int r0 = (item - c * p.nrb) * B;
+    if (r0 >= p.H) continue;                              // block-uniform
+    const int* ch = tab + 1 + c * kChunkInts;
+    const int e = clamp_expert(ch[0], p.E);
+    const int nt = ch[1];
+    StageF32<NH> hst[kGroupTT];
+#pragma unroll
+    for (int k = 0; k < kGroupTT; ++k)
+      if (k < nt) hst[k].load(p.h + (int64_t)ch[2 + k] * p.I, p.I, threadIdx.x, kThreads);
+    GroupLoad<FMT, S> ld[NR];
+    const QMat m = expert_dn(Ld, e);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int row = r0 + (i * kWaves + wave) * RPW + rr;
+      load_row<FMT, L, S>(ld[i], m, p.g, row, row < p.H, li);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kGroupTT; ++k)
+      if (k < nt) hst[k].store(hs + k * hstride, p.I, p.I, 0, 1.0f, threadIdx.x, kThreads);
+    __syncthreads();
+#pragma unroll 1
+    for (int k = 0; k < nt; ++k) {
+      XRegs<FMT, L, S> xr;
+      xr.load(hs + k * hstride, p.g.chunks, li);
+      float* out = p.dout + (int64_t)ch[2 + k] * p.H;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        pin_regs(ld[i]);
+        const float d = row_dot<FMT, L, S>(ld[i], xr);
+        const int row = r0 + (i * kWaves + wave) * RPW + rr;
+        if (li == 0 && row < p.H) out[row] = d;
+      }
+    }
+  }
+}
+
+// y[t] = (x[t] +) sum_j w[t][j] * dout[t*K + j], j in order (the last layer
+// of a grouped step; earlier layers combine inside the next route kernel).
+__global__ void __launch_bounds__(kThreads)
+moe_combine_kernel(const float* __restrict__ x_prev, int residual, const float* __restrict__ dout,
+                   const float* __restrict__ w, int H, int K, float* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int h = (blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (h >= H) return;
+  float4 v = residual ? ldg_f4(x_prev + (int64_t)t * H + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < K; ++j) {
+    const float wj = w[t * K + j];
+    const float4 d = ldg_f4(dout + ((int64_t)t * K + j) * H + h);
+    v.x = __builtin_fmaf(wj, d.x, v.x);
+    v.y = __builtin_fmaf(wj, d.y, v.y);
+    v.z = __builtin_fmaf(wj, d.z, v.z);
+    v.w = __builtin_fmaf(wj, d.w, v.w);
+  }
+  *reinterpret_cast<float4*>(y + (int64_t)t * H + h) = v;
+}
+
 // ---------------------------------------------------------------- plan
 
 struct GraphKey {
@@ -678,6 +1041,12 @@ struct bdg_plan {
   int fuse_route;           // layers >= 1 route from the previous down kernel's partial sums
   int log2T;
   const float** wr;         // host copy of each layer's router pointer
+  // grouped path (steps of M > 1 tokens)
+  int group_ok;             // the geometry fits the grouped kernels
+  int g_grid_gu, g_grid_dn; // persistent grid sizes
+  int g_bpc, g_nrb, g_dn_NR;
+  float* dout;              // [max_m * K][H] down output per pick
+  int32_t* chunks;          // chunk table
   int32_t* idx;
   float* w;
   float* h;
@@ -706,7 +1075,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Optional per-kernel timing: every launch takes the next start/stop event
 // pair (recorded by the runtime at kernel start and end) and notes its kind.
-enum KernelKind { kRoute = 0, kGateUp = 1, kDown = 2, kKinds = 3 };
+enum KernelKind { kRoute = 0, kGateUp = 1, kDown = 2, kCombine = 3, kKinds = 4 };
 
 struct Prof {
   hipEvent_t* ev;     // 2 * cap events
@@ -730,8 +1099,10 @@ struct Prof {
 
 // layer input: the caller's x at layer 0, else the residual buffer written
 // by the previous layer's down kernel.
+// combine != 0 (grouped path, layer >= 1): the layer input is formed here
+// from the previous layer's input and per-pick down outputs.
 static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype, int m,
-                        float* resid_trace, int compute_logits, hipStream_t s, Prof* prof) {
+                        float* resid_trace, int compute_logits, hipStream_t s, Prof* prof, int combine = 0) {
   RouteParams rp{};
   rp.M = m;
   rp.H = p->d.hidden;
@@ -741,6 +1112,14 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
     rp.x_in = x;
     rp.x_bf16 = x_dtype == BDG_BF16 ? 1 : 0;
     rp.x_copy = p->resid[0];
+  } else if (combine) {
+    rp.x_in = p->resid[(layer - 1) & 1];
+    rp.x_bf16 = 0;
+    rp.x_copy = p->resid[layer & 1];
+    rp.dout = p->dout;
+    rp.wts = p->w;
+    rp.K = p->d.top_k;
+    rp.combine_residual = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
   } else {
     rp.x_in = p->resid[layer & 1];
     rp.x_bf16 = 0;
@@ -867,8 +1246,117 @@ static int launch_down(const bdg_plan* p, int layer, int m, int residual, float*
   return BDG_E_UNSUPPORTED;
 }
 
+static int launch_gu_group(const bdg_plan* p, int layer, int m, int routed, const int32_t* idx_in,
+                           const float* w_in, int32_t* topk_trace, float* wts_trace, int use_norm, hipStream_t s,
+                           Prof* prof) {
+  GroupParams gp{};
+  gp.M = m;
+  gp.H = p->d.hidden;
+  gp.I = p->d.inter;
+  gp.E = p->d.n_experts;
+  gp.K = p->d.top_k;
+  gp.routed = routed;
+  gp.part = p->part;
+  gp.pstride = p->pstride;
+  gp.norm = use_norm;
+  gp.eps = p->d.norm_eps;
+  gp.idx_in = idx_in;
+  gp.w_in = w_in;
+  gp.idx_out = p->idx;
+  gp.w_out = p->w;
+  gp.topk_trace = topk_trace;
+  gp.wts_trace = wts_trace;
+  gp.x = p->resid[layer & 1];
+  gp.L = p->hl[layer];
+  gp.g = p->gu_geom;
+  gp.h_out = p->h;
+  gp.chunks_out = p->chunks;
+  gp.bpc = p->g_bpc;
+  const size_t lds = (group_lds_floats() + (size_t)kGroupTT * gp.g.chunks * kXStride) * sizeof(float);
+  const dim3 grid((unsigned)p->g_grid_gu);
+  const int fmt = p->d.fmt, V = p->topk_V;
+#define BDG_GG_CASE(F, SS, VV)                                                                            \
+  if (fmt == F && p->gu_S == SS && V == VV) {                                                             \
+    BDG_LAUNCH(prof, kGateUp, (moe_gu_group_kernel<F, SS, gu_group_np(F, SS), VV>), grid, dim3(kThreads), \
+               lds, s, gp);                                                                               \
+    return launch_status();                                                                               \
+  }
+#define BDG_GG_V(F, SS) BDG_GG_CASE(F, SS, 1) BDG_GG_CASE(F, SS, 2) BDG_GG_CASE(F, SS, 4) BDG_GG_CASE(F, SS, 16)
+  // shapes whose rows, held across a chunk's picks, fit 256 VGPRs (group_ok)
+  BDG_GG_V(kMXFP4, 1) BDG_GG_V(kMXFP4, 2) BDG_GG_V(kMXFP4, 3)
+  BDG_GG_V(kINT4G, 1) BDG_GG_V(kINT4G, 2)
+#undef BDG_GG_V
+#undef BDG_GG_CASE
+  return BDG_E_UNSUPPORTED;
+}
+
+static int launch_dn_group(const bdg_plan* p, int layer, hipStream_t s, Prof* prof) {
+  DnGroupParams dp{};
+  dp.H = p->d.hidden;
+  dp.I = p->d.inter;
+  dp.E = p->d.n_experts;
+  dp.chunks = p->chunks;
+  dp.h = p->h;
+  dp.dout = p->dout;
+  dp.L = p->hl[layer];
+  dp.g = p->dn_geom;
+  dp.nrb = p->g_nrb;
+  const size_t lds =
+      ((size_t)(1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4 + (size_t)kGroupTT * dp.g.chunks * kXStride) *
+      sizeof(float);
+  const dim3 grid((unsigned)p->g_grid_dn);
+  const int fmt = p->d.fmt;
+#define BDG_DG_CASE(F, LL, SS)                                                                            \
+  if (fmt == F && p->dn_L == LL && p->dn_S == SS) {                                                      \
+    BDG_LAUNCH(prof, kDown, (moe_dn_group_kernel<F, LL, SS, dn_group_nr(F, LL, SS)>), grid, dim3(kThreads), \
+               lds, s, dp);                                                                               \
+    return launch_status();                                                                               \
+  }
+  // the (L, S) pairs pick_lanes gives for I <= 4096
+#define BDG_DG_ALL(F)                                                                              \
+  BDG_DG_CASE(F, 8, 1) BDG_DG_CASE(F, 8, 2) BDG_DG_CASE(F, 8, 3) BDG_DG_CASE(F, 16, 2)             \
+  BDG_DG_CASE(F, 16, 3) BDG_DG_CASE(F, 32, 2) BDG_DG_CASE(F, 32, 3) BDG_DG_CASE(F, 64, 2)
+  BDG_DG_ALL(kMXFP4)
+  BDG_DG_ALL(kINT4G)
+#undef BDG_DG_ALL
+#undef BDG_DG_CASE
+  return BDG_E_UNSUPPORTED;
+}
+
+static int launch_combine(const bdg_plan* p, int m, const float* x_prev, int residual, float* y, hipStream_t s,
+                          Prof* prof) {
+  const int H = p->d.hidden;
+  const dim3 grid((unsigned)((H / 4 + kThreads - 1) / kThreads), (unsigned)m);
+  BDG_LAUNCH(prof, kCombine, moe_combine_kernel, grid, dim3(kThreads), 0, s, x_prev, residual, p->dout, p->w, H,
+             p->d.top_k, y);
+  return launch_status();
+}
+
+// A grouped step (M > 1): per layer route (forming the layer input from the
+// previous layer's per-pick outputs), grouped gate_up, grouped down; a final
+// combine writes y.
+static int enqueue_decode_grouped(const bdg_plan* p, const GraphKey& k, hipStream_t s, Prof* prof) {
+  const int L = p->d.n_layers;
+  const int K = p->d.top_k;
+  const int H = p->d.hidden;
+  const int stack = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
+  for (int l = 0; l < L; ++l) {
+    int st = launch_route(p, l, k.x, k.x_dtype, k.m, k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr,
+                          1, s, prof, /*combine=*/l > 0);
+    if (st) return st;
+    st = launch_gu_group(p, l, k.m, 0, nullptr, nullptr,
+                         k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
+                         k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof);
+    if (st) return st;
+    st = launch_dn_group(p, l, s, prof);
+    if (st) return st;
+  }
+  return launch_combine(p, k.m, p->resid[(L - 1) & 1], stack, k.y, s, prof);
+}
+
 // The whole per-token path, enqueued on s.
 static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, Prof* prof = nullptr) {
+  if (k.m > 1 && p->group_ok) return enqueue_decode_grouped(p, k, s, prof);
   const int L = p->d.n_layers;
   const int K = p->d.top_k;
   const int H = p->d.hidden;
@@ -977,6 +1465,32 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     while (lt < 6 && (d->n_experts << (lt + 1)) <= kThreads) ++lt;
     p->log2T = lt;
   }
+  {
+    // grouped path: persistent grids sized to the device, items padded so a
+    // row block's items in consecutive chunks are a multiple of 8 apart
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    const int hc32 = d->hidden / 32, ic32 = d->inter / 32;
+    const size_t lds_gu = (group_lds_floats() + (size_t)kGroupTT * hc32 * kXStride) * sizeof(float);
+    const size_t lds_dn = ((size_t)(1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4 + (size_t)kGroupTT * ic32 * kXStride) *
+                          sizeof(float);
+    const size_t lds_cu = 160 * 1024;
+    const int bg = (int)std::min<size_t>(2, lds_cu / lds_gu), bd = (int)std::min<size_t>(2, lds_cu / lds_dn);
+    p->g_grid_gu = (cus * (bg < 1 ? 1 : bg) + 7) / 8 * 8;
+    p->g_grid_dn = (cus * (bd < 1 ? 1 : bd) + 7) / 8 * 8;
+    const int np = gu_group_np(d->fmt == BDG_FMT_MXFP4 ? 0 : 1, p->gu_S);
+    p->g_bpc = ((d->inter + kWaves * np - 1) / (kWaves * np) + 7) / 8 * 8;
+    const int rpw = kWave / p->dn_L;
+    p->g_dn_NR = dn_group_nr(d->fmt == BDG_FMT_MXFP4 ? 0 : 1, p->dn_L, p->dn_S);
+    const int B = p->g_dn_NR * rpw * kWaves;
+    p->g_nrb = ((d->hidden + B - 1) / B + 7) / 8 * 8;
+    p->group_ok = d->max_m * d->top_k <= kGroupMaxPicks && d->inter <= 4096 && p->dn_L * p->dn_S <= 128 &&
+                  p->gu_S <= (d->fmt == BDG_FMT_MXFP4 ? 3 : 2) &&
+                  lds_gu <= 64 * 1024 &&
+                  lds_dn <= 64 * 1024 && env_int("BDG_GROUP", 1, 0, 1);
+  }
   auto geom = [&](int k) {
     QGeom g;
     g.k = k;
@@ -997,6 +1511,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_idx = off; off = align256(off + sizeof(int32_t) * M * K);
   const size_t o_w = off; off = align256(off + sizeof(float) * M * K);
   const size_t o_h = off; off = align256(off + sizeof(float) * (size_t)M * K * I);
+  const size_t o_dout = off; off = align256(off + sizeof(float) * (size_t)M * K * H);
+  const size_t o_chunks = off; off = align256(off + sizeof(int32_t) * (1 + kGroupMaxPicks * kChunkInts));
   if (hipMalloc(&p->dev_base, off) != hipSuccess) {
     delete p;
     return BDG_E_NOMEM;
@@ -1008,6 +1524,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->idx = reinterpret_cast<int32_t*>(base + o_idx);
   p->w = reinterpret_cast<float*>(base + o_w);
   p->h = reinterpret_cast<float*>(base + o_h);
+  p->dout = reinterpret_cast<float*>(base + o_dout);
+  p->chunks = reinterpret_cast<int32_t*>(base + o_chunks);
   LayerDev* host = new (std::nothrow) LayerDev[d->n_layers];
   p->wr = new (std::nothrow) const float*[d->n_layers];
   if (!host || !p->wr) {
@@ -1076,7 +1594,7 @@ extern "C" int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_
   if (m > p->d.max_m) return BDG_E_INVALID;
   if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
   if (!aligned16(x) || !aligned16(y)) return BDG_E_ALIGN;
-  const int need = 3 * p->d.n_layers;
+  const int need = 3 * p->d.n_layers + 1;
   if (!p->prof_ev) {
     p->prof_ev = new (std::nothrow) hipEvent_t[2 * need];
     p->prof_kind = new (std::nothrow) int[need];
@@ -1170,6 +1688,13 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   int st = launch_status();
   if (st) return st;
   // gate_up runs on the raw x (no norm), routing from the caller
+  if (m > 1 && p->group_ok) {
+    st = launch_gu_group(p, layer, m, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
+    if (st) return st;
+    st = launch_dn_group(p, layer, s, nullptr);
+    if (st) return st;
+    return launch_combine(p, m, p->resid[layer & 1], 0, y, s, nullptr);
+  }
   st = launch_gateup(p, layer, m, 1, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
   if (st) return st;
   return launch_down(p, layer, m, 0, nullptr, y, nullptr, 0, s, nullptr);
