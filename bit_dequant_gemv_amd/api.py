@@ -212,7 +212,7 @@ def moe_experts_routed(plan: MoEPlan, layer, x, idx, wts, y=None):
     return y
 
 
-KERNEL_KINDS = ("route", "gate_up", "down")
+KERNEL_KINDS = ("route", "gate_up", "down", "combine")
 
 
 def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None):

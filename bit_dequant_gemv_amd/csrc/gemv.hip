@@ -9,63 +9,64 @@ namespace bdg {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 
-// grid = (blocks per token, m).  Block b owns row groups [g0, g1); its waves
-// take them round-robin, two groups in flight per wave.
-template <int FMT, int L, int S>
+// grid = (blocks per token, m).  Wave gw of a token owns row groups
+// [gw * NP, gw * NP + NP) (a row group = 64 / L rows).  Every load a wave needs
+// is issued up front and branch-free: x first (its loads do not depend on
+// anything), then all NP row groups; x is stored to LDS only after the
+// weights are in flight, so the weight stream starts at once.
+template <int FMT, int L, int S, int NP>
 __global__ void __launch_bounds__(kGemvThreads)
 qgemv_kernel(QMat w, QGeom g, int64_t n_rows, const void* __restrict__ x, int x_bf16,
              float* __restrict__ y) {
   extern __shared__ float lds_x[];
   constexpr int RPW = kWave / L;
+  constexpr int NX = (L * S + 31) / 32;                 // float4 of x per thread (k <= 32 * L * S)
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int li = lane % L;
   const int rr = lane / L;
 
-  if (x_bf16)
-    stage_bf16<4>(lds_x, reinterpret_cast<const uint16_t*>(x) + (int64_t)t * g.k, g.k, threadIdx.x, kGemvThreads);
-  else
-    stage_f32<4>(lds_x, reinterpret_cast<const float*>(x) + (int64_t)t * g.k, g.k, g.k, 0, 1.0f, threadIdx.x,
-                 kGemvThreads);
+  StageF32<NX> xf;
+  uint2 xb[NX];
+  if (x_bf16) {
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(x) + (int64_t)t * g.k;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int idx = (i * kGemvThreads + threadIdx.x) * 4;
+      xb[i] = ldg_u64(xs + (idx < g.k ? idx : g.k - 4));
+    }
+  } else {
+    xf.load(reinterpret_cast<const float*>(x) + (int64_t)t * g.k, g.k, threadIdx.x, kGemvThreads);
+  }
+  const int64_t gw = (int64_t)blockIdx.x * kGemvWaves + wave;
+  GroupLoad<FMT, S> ld[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int64_t row = (gw * NP + i) * RPW + rr;
+    load_row<FMT, L, S>(ld[i], w, g, row < n_rows ? row : 0, row < n_rows, li);
+  }
+  if (x_bf16) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int idx = (i * kGemvThreads + threadIdx.x) * 4;
+      if (idx < g.k)
+        *reinterpret_cast<float4*>(lds_x + (idx >> 5) * kXStride + (idx & 31)) =
+            make_float4(bf16_to_f32((uint16_t)(xb[i].x & 0xFFFFu)), bf16_to_f32((uint16_t)(xb[i].x >> 16)),
+                        bf16_to_f32((uint16_t)(xb[i].y & 0xFFFFu)), bf16_to_f32((uint16_t)(xb[i].y >> 16)));
+    }
+  } else {
+    xf.store(lds_x, g.k, g.k, 0, 1.0f, threadIdx.x, kGemvThreads);
+  }
   __syncthreads();
   XRegs<FMT, L, S> xr;
   xr.load(lds_x, g.chunks, li);
-
-  const int64_t n_groups = (n_rows + RPW - 1) / RPW;
-  const int64_t g0 = n_groups * blockIdx.x / gridDim.x;
-  const int64_t g1 = n_groups * (blockIdx.x + 1) / gridDim.x;
   float* yt = y + (int64_t)t * n_rows;
-
-  GroupLoad<FMT, S> a, b;
-  int64_t ga = g0 + wave;
-  if (ga < g1) {
-    const int64_t row = ga * RPW + rr;
-    load_row<FMT, L, S>(a, w, g, row, row < n_rows, li);
-  }
-  while (ga < g1) {
-    const int64_t gb = ga + kGemvWaves;
-    if (gb < g1) {
-      const int64_t row = gb * RPW + rr;
-      load_row<FMT, L, S>(b, w, g, row, row < n_rows, li);
-    }
-    {
-      const int64_t row = ga * RPW + rr;
-      const float d = row_dot<FMT, L, S>(a, xr);
-      if (li == 0 && row < n_rows) yt[row] = d;
-    }
-    if (gb >= g1) break;
-    const int64_t gc = gb + kGemvWaves;
-    if (gc < g1) {
-      const int64_t row = gc * RPW + rr;
-      load_row<FMT, L, S>(a, w, g, row, row < n_rows, li);
-    }
-    {
-      const int64_t row = gb * RPW + rr;
-      const float d = row_dot<FMT, L, S>(b, xr);
-      if (li == 0 && row < n_rows) yt[row] = d;
-    }
-    ga = gc;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int64_t row = (gw * NP + i) * RPW + rr;
+    const float d = row_dot<FMT, L, S>(ld[i], xr);
+    if (li == 0 && row < n_rows) yt[row] = d;
   }
 }
 
@@ -76,22 +77,26 @@ static int launch_qgemv(const QMat& w, const QGeom& g, int64_t n, const void* x,
   if (!pick_lanes(g.chunks, &L, &S)) return BDG_E_UNSUPPORTED;
   const int rpw = kWave / L;
   const int64_t n_groups = (n + rpw - 1) / rpw;
-  // about two row groups per wave, at least one block per 64 row groups
-  int64_t blocks = (n_groups + 2 * kGemvWaves - 1) / (2 * kGemvWaves);
+  // one row group per wave while that keeps the grid within a few waves per
+  // CU; long matrices take four per wave (fewer, fuller waves)
+  const int np = n_groups <= 8192 ? 1 : 4;
+  int64_t blocks = (n_groups + (int64_t)np * kGemvWaves - 1) / ((int64_t)np * kGemvWaves);
   if (blocks < 1) blocks = 1;
-  if (blocks > 65535) blocks = 65535;
+  if (blocks > 2147483647LL) return BDG_E_UNSUPPORTED;
   const size_t lds = (size_t)g.chunks * kXStride * sizeof(float);
   dim3 grid((unsigned)blocks, (unsigned)m);
-#define BDG_GEMV_CASE(LL, SS)                                                                      \
-  if (L == LL && S == SS) {                                                                        \
-    hipLaunchKernelGGL((qgemv_kernel<FMT, LL, SS>), grid, dim3(kGemvThreads), lds, s, w, g, n, x, \
-                       x_bf16, y);                                                                 \
-    return launch_status();                                                                        \
+#define BDG_GEMV_CASE(LL, SS, NN)                                                                       \
+  if (L == LL && S == SS && np == NN) {                                                                 \
+    hipLaunchKernelGGL((qgemv_kernel<FMT, LL, SS, NN>), grid, dim3(kGemvThreads), lds, s, w, g, n, x,   \
+                       x_bf16, y);                                                                      \
+    return launch_status();                                                                             \
   }
-  BDG_GEMV_CASE(8, 1) BDG_GEMV_CASE(8, 2) BDG_GEMV_CASE(8, 3)
-  BDG_GEMV_CASE(16, 2) BDG_GEMV_CASE(16, 3)
-  BDG_GEMV_CASE(32, 2) BDG_GEMV_CASE(32, 3)
-  BDG_GEMV_CASE(64, 2) BDG_GEMV_CASE(64, 3) BDG_GEMV_CASE(64, 4)
+#define BDG_GEMV_NP(LL, SS) BDG_GEMV_CASE(LL, SS, 1) BDG_GEMV_CASE(LL, SS, 4)
+  BDG_GEMV_NP(8, 1) BDG_GEMV_NP(8, 2) BDG_GEMV_NP(8, 3)
+  BDG_GEMV_NP(16, 2) BDG_GEMV_NP(16, 3)
+  BDG_GEMV_NP(32, 2) BDG_GEMV_NP(32, 3)
+  BDG_GEMV_NP(64, 2) BDG_GEMV_NP(64, 3) BDG_GEMV_NP(64, 4)
+#undef BDG_GEMV_NP
 #undef BDG_GEMV_CASE
   return BDG_E_UNSUPPORTED;
 }

@@ -212,9 +212,11 @@ int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int32_t x_dtyp
  * computes it (same kernels, same grids), launched directly rather than from
  * a graph, with a start/stop event pair recorded by the runtime at each
  * kernel's start and end.  Adds each kernel's duration (ms) to
- * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route (RMSNorm +
- * router GEMV), 1 = gate_up (top-k + grouped gate_up GEMV + SwiGLU), 2 =
- * down (grouped down GEMV + combine + residual); host arrays of at least 3.
+ * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route (router
+ * GEMV + sum of squares, and for steps of m > 1 the previous layer's
+ * combine), 1 = gate_up (top-k + grouped gate_up GEMV + SwiGLU), 2 = down
+ * (grouped down GEMV; combine + residual when m = 1), 3 = the final combine
+ * of an m > 1 step; host arrays of at least 4.
  * Synchronises on the last event before returning.  Used by the benchmark
  * for per-kernel roofline figures. */
 int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
