@@ -199,7 +199,6 @@ struct RouteParams {
 __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
   extern __shared__ float lds[];
   float* xs = lds;               // [H]
-  float* red = lds + p.H;        // [kWaves]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_wave_id();
@@ -261,28 +260,36 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
       }
     }
   }
-  float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
     const int h = (i * kThreads + threadIdx.x) * 4;
     if (h < p.H) {
       const float4 v = xv4[i];
       *reinterpret_cast<float4*>(xs + h) = v;
-      ss = __builtin_fmaf(v.x, v.x, ss);
-      ss = __builtin_fmaf(v.y, v.y, ss);
-      ss = __builtin_fmaf(v.z, v.z, ss);
-      ss = __builtin_fmaf(v.w, v.w, ss);
       if (blockIdx.x == 0) {
         if (p.x_copy) *reinterpret_cast<float4*>(p.x_copy + xoff + h) = v;
         if (p.resid_trace) *reinterpret_cast<float4*>(p.resid_trace + xoff + h) = v;
       }
     }
   }
-  ss = wave_sum(ss);
-  if (lane == 0) red[wave] = ss;
   __syncthreads();
-  if (p.compute_logits && blockIdx.x == 0 && threadIdx.x == 0)
-    p.part[((int64_t)t * (p.E + 1) + p.E) * p.pstride] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (p.compute_logits && blockIdx.x == 0 && wave == 0) {
+    // sum of squares in the lane order of moe_route_direct_kernel (same value)
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRouteMaxF4; ++i) {
+      const int h = (i * kWave + lane) * 4;
+      if (h < p.H) {
+        const float4 v = *reinterpret_cast<const float4*>(xs + h);
+        ss = __builtin_fmaf(v.x, v.x, ss);
+        ss = __builtin_fmaf(v.y, v.y, ss);
+        ss = __builtin_fmaf(v.z, v.z, ss);
+        ss = __builtin_fmaf(v.w, v.w, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) p.part[((int64_t)t * (p.E + 1) + p.E) * p.pstride] = ss;
+  }
   if (!row_ok) return;
   float acc = 0.f;
 #pragma unroll
@@ -298,6 +305,75 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
   }
   acc = wave_sum(acc);
   if (lane == 0) p.part[((int64_t)t * (p.E + 1) + e) * p.pstride] = acc;
+}
+
+// The same for the plain case (no combine): one wavefront per router row,
+// one block per row (grid (E, M)), x read straight into registers in the
+// row's lane layout (float4 i of lane l covers x[4(64i + l) .. +3]), so there
+// is no LDS staging and no barrier.  The wave of row 0 also writes the sum of
+// squares and, when asked, the fp32 copy and trace of x.  NF float4 per lane
+// cover H <= 256 NF.
+template <int NF>
+__global__ void __launch_bounds__(kWave) moe_route_direct_kernel(RouteParams p) {
+  const int e = blockIdx.x;
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x;
+  const float* wr = p.L.w_r + (int64_t)e * p.H;
+  const int64_t xoff = (int64_t)t * p.H;
+  float4 wv[NF], xv[NF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int h = (i * kWave + lane) * 4;
+    wv[i] = ldg_f4(wr + (h < p.H ? h : p.H - 4));
+  }
+  if (p.x_bf16) {
+    uint2 xb[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int h = (i * kWave + lane) * 4;
+      xb[i] = ldg_u64(reinterpret_cast<const uint16_t*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+      xv[i] = make_float4(bf16_to_f32((uint16_t)(xb[i].x & 0xFFFFu)), bf16_to_f32((uint16_t)(xb[i].x >> 16)),
+                          bf16_to_f32((uint16_t)(xb[i].y & 0xFFFFu)), bf16_to_f32((uint16_t)(xb[i].y >> 16)));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int h = (i * kWave + lane) * 4;
+      xv[i] = ldg_f4(reinterpret_cast<const float*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
+    }
+  }
+  float acc = 0.f, ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int h = (i * kWave + lane) * 4;
+    if (h < p.H) {
+      acc = __builtin_fmaf(wv[i].x, xv[i].x, acc);
+      acc = __builtin_fmaf(wv[i].y, xv[i].y, acc);
+      acc = __builtin_fmaf(wv[i].z, xv[i].z, acc);
+      acc = __builtin_fmaf(wv[i].w, xv[i].w, acc);
+      ss = __builtin_fmaf(xv[i].x, xv[i].x, ss);
+      ss = __builtin_fmaf(xv[i].y, xv[i].y, ss);
+      ss = __builtin_fmaf(xv[i].z, xv[i].z, ss);
+      ss = __builtin_fmaf(xv[i].w, xv[i].w, ss);
+    }
+  }
+  acc = wave_sum(acc);
+  float* prow = p.part + (int64_t)t * (p.E + 1) * p.pstride;
+  if (lane == 0) prow[(int64_t)e * p.pstride] = acc;
+  if (e == 0) {
+    ss = wave_sum(ss);
+    if (lane == 0) prow[(int64_t)p.E * p.pstride] = ss;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int h = (i * kWave + lane) * 4;
+      if (h < p.H) {
+        if (p.x_copy) *reinterpret_cast<float4*>(p.x_copy + xoff + h) = xv[i];
+        if (p.resid_trace) *reinterpret_cast<float4*>(p.resid_trace + xoff + h) = xv[i];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- gate_up + SwiGLU
@@ -1129,6 +1205,18 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
   rp.part = p->part;
   rp.pstride = p->pstride;
   rp.L = p->hl[layer];
+  if (compute_logits && !rp.dout) {
+    // one wave per router row, no LDS
+    const int nf = (rp.H + 255) / 256;
+    const dim3 grid((unsigned)rp.E, (unsigned)m);
+#define BDG_RD_CASE(NN)                                                                          \
+    if (nf <= NN) {                                                                              \
+      BDG_LAUNCH(prof, kRoute, moe_route_direct_kernel<NN>, grid, dim3(kWave), 0, s, rp);        \
+      return launch_status();                                                                    \
+    }
+    BDG_RD_CASE(2) BDG_RD_CASE(4) BDG_RD_CASE(8) BDG_RD_CASE(12) BDG_RD_CASE(16)
+#undef BDG_RD_CASE
+  }
   const int nblk = compute_logits ? (rp.E + kWaves - 1) / kWaves : 1;
   const size_t lds = (size_t)(rp.H + kWaves) * sizeof(float);
   BDG_LAUNCH(prof, kRoute, moe_route_kernel, dim3(nblk, m), dim3(kThreads), lds, s, rp);
