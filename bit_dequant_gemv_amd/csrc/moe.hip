@@ -630,44 +630,19 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   const bool wave_on = sub < wpe;
   const LayerDev& Ld = p.L;
 
-  // loads, in the order their data is needed (vmcnt retires in order):
-  // the first group's expert id, the epilogue operands (router weights of
-  // the next layer, residual row, combine weights: all in bounds, issued
-  // unconditionally so the compiler's wait counts stay exact), then per
-  // group the h vectors and the expert weights
-  int e_next = clamp_expert(p.idx[t * p.K + (jw < p.K ? jw : p.K - 1)], p.E);
-  // epilogue row of this lane (B <= 64); idle lanes repeat the block's last
-  // row, so their loads fall in lines the block reads anyway
-  const int orow = min(r0 + min(lane, B - 1), p.H - 1);
-  float wr[kDnRouterPerWave];                               // wr[i] = w_r'[wave + 8i][orow]
-  {
-    const float* wsrc = p.route_next ? p.wr_next : p.x_prev;
-#pragma unroll
-    for (int i = 0; i < kDnRouterPerWave; ++i) {
-      const int er = wave + kDownWaves * i;
-      wr[i] = wsrc[(int64_t)(p.route_next ? (er < p.E ? er : p.E - 1) : 0) * p.H + orow];
-    }
-  }
-  const float xp = p.x_prev[(int64_t)t * p.H + orow];
-  const float wk = p.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
-
-  for (int jg = 0; jg < p.K; jg += kg) {
+  // One group of kg experts: h vectors staged through LDS, the expert rows'
+  // dot products into dpart.  hstage holds the group's h loads, issued by the
+  // caller before anything else it needs later.
+  auto group = [&](int jg, int e, StageF32<HV>& hstage) {
     const int nj = min(kg, p.K - jg);
     const bool active = wave_on && jw < nj;
-    const int e = e_next;
     const int nh = nj * p.I;
-    StageF32<HV> hstage;
-    hstage.load(p.h + ((int64_t)t * p.K + jg) * p.I, nh, threadIdx.x, blockDim.x);
     GroupLoad<FMT, S> ld[NR];
     const QMat m = expert_dn(Ld, e);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int row = r0 + (i * wpe + sub) * RPW + rr;
       load_row<FMT, L, S>(ld[i], m, p.g, row, active && row < p.H, li);
-    }
-    if (jg + kg < p.K) {   // next group's expert id (K > 8 only)
-      const int jn = jg + kg + (jw < p.K - jg - kg ? jw : p.K - jg - kg - 1);
-      e_next = clamp_expert(p.idx[t * p.K + jn], p.E);
     }
     hstage.store(lds, nh, p.I, stride, 1.0f, threadIdx.x, blockDim.x);
     __syncthreads();
@@ -682,6 +657,40 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
       }
     }
     __syncthreads();
+  };
+
+  // loads, in the order their data is needed (vmcnt retires in order): the
+  // first group's expert id and h vectors, the epilogue operands (router
+  // weights of the next layer, residual row, combine weights: all in bounds,
+  // issued unconditionally so the compiler's wait counts stay exact), then
+  // the expert weights.  The first group is outside the loop so no loop
+  // back edge makes the compiler wait for everything before the weights.
+  const int e0 = clamp_expert(p.idx[t * p.K + (jw < p.K ? jw : p.K - 1)], p.E);
+  StageF32<HV> h0;
+  h0.load(p.h + (int64_t)t * p.K * p.I, min(kg, p.K) * p.I, threadIdx.x, blockDim.x);
+  __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the scheduler would sink loads
+  // epilogue row of this lane (B <= 64); idle lanes repeat the block's last
+  // row, so their loads fall in lines the block reads anyway
+  const int orow = min(r0 + min(lane, B - 1), p.H - 1);
+  float wr[kDnRouterPerWave];                               // wr[i] = w_r'[wave + 8i][orow]
+  {
+    const float* wsrc = p.route_next ? p.wr_next : p.x_prev;
+#pragma unroll
+    for (int i = 0; i < kDnRouterPerWave; ++i) {
+      const int er = wave + kDownWaves * i;
+      wr[i] = wsrc[(int64_t)(p.route_next ? (er < p.E ? er : p.E - 1) : 0) * p.H + orow];
+    }
+  }
+  const float xp = p.x_prev[(int64_t)t * p.H + orow];
+  const float wk = p.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  group(0, e0, h0);
+  for (int jg = kg; jg < p.K; jg += kg) {   // K > 8 only
+    const int jn = jg + (jw < p.K - jg ? jw : p.K - jg - 1);
+    const int e = clamp_expert(p.idx[t * p.K + jn], p.E);
+    StageF32<HV> hs;
+    hs.load(p.h + ((int64_t)t * p.K + jg) * p.I, min(kg, p.K - jg) * p.I, threadIdx.x, blockDim.x);
+    group(jg, e, hs);
   }
 
   if (B <= kWave) {
