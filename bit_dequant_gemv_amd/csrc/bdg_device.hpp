@@ -116,6 +116,31 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// One DPP move of a float (lanes with no source get 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over aligned groups of L lanes, valid only in the LAST lane of each
+// group (lane L-1, 2L-1, ...).  All steps are DPP moves inside the VALU (row
+// shifts, then the GFX9 row broadcasts across rows), no LDS round trip:
+// after row_shr 1, 2, 4, 8 lane 15 of each 16-lane row holds its row sum;
+// row_bcast:15 adds row r-1's lane 15 into rows 1 and 3, row_bcast:31 adds
+// lane 31 into rows 2 and 3.  Lanes with no source read the old value 0.
+// Fixed order: deterministic.
+template <int L>
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "group size");
+  v += dpp_f32<0x111, 0xF>(v);                          // row_shr:1
+  v += dpp_f32<0x112, 0xF>(v);                          // row_shr:2
+  if constexpr (L > 4) v += dpp_f32<0x114, 0xF>(v);     // row_shr:4
+  if constexpr (L > 8) v += dpp_f32<0x118, 0xF>(v);     // row_shr:8
+  if constexpr (L > 16) v += dpp_f32<0x142, 0xA>(v);    // row_bcast:15 into rows 1, 3
+  if constexpr (L > 32) v += dpp_f32<0x143, 0xC>(v);    // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // ---------------------------------------------------------------- chunk dot products
 
 // MXFP4: unscaled sum_i E2M1(code_i) * x_i over one 16-byte chunk (32 codes),

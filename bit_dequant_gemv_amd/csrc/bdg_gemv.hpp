@@ -117,7 +117,8 @@ struct XRegs {
 };
 
 // Lane-partial dot of the loaded row against x, summed over the L lanes of
-// the row (every lane of the row group receives the row's dot product).
+// the row; the row's dot product is valid in the group's last lane
+// (li == L - 1, see kRowSumLane).
 template <int FMT, int L, int S>
 __device__ __forceinline__ float row_dot(const GroupLoad<FMT, S>& ld, const XRegs<FMT, L, S>& xr) {
   float acc = 0.f;
@@ -129,8 +130,12 @@ __device__ __forceinline__ float row_dot(const GroupLoad<FMT, S>& ld, const XReg
     const uint32_t z = (ld.zn[s] >> (((ld.zhi >> s) & 1u) * 4u)) & 15u;
     acc += chunk_contrib<FMT>(ld.q[s], sc, z, xr.v[s], xr.sum[s]);
   }
-  return group_sum<L>(acc);
+  return group_sum_last<L>(acc);
 }
+
+// Lane (within its L-lane group) that holds row_dot's result.
+template <int L>
+constexpr int kRowSumLane = L - 1;
 
 // Stage n fp32 values (times `mult`) from global memory into the LDS chunk
 // layout.  Values are split into `per`-long vectors placed `region` floats

@@ -66,7 +66,7 @@ qgemv_kernel(QMat w, QGeom g, int64_t n_rows, const void* __restrict__ x, int x_
   for (int i = 0; i < NP; ++i) {
     const int64_t row = (gw * NP + i) * RPW + rr;
     const float d = row_dot<FMT, L, S>(ld[i], xr);
-    if (li == 0 && row < n_rows) yt[row] = d;
+    if (li == kRowSumLane<L> && row < n_rows) yt[row] = d;
   }
 }
 

@@ -569,8 +569,8 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const float d = row_dot<FMT, L, S>(ld[i], xr);
-    const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 0));
-    const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L));
+    const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), kRowSumLane<L>));
+    const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L + kRowSumLane<L>));
     if (lane == i) {
       g_sel = gv;
       u_sel = uv;
@@ -653,7 +653,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
       for (int i = 0; i < NR; ++i) {
         const float d = row_dot<FMT, L, S>(ld[i], xr);
         const int b = (i * wpe + sub) * RPW + rr;
-        if (li == 0 && b < B) dpart[(jg + jw) * B + b] = d;
+        if (li == kRowSumLane<L> && b < B) dpart[(jg + jw) * B + b] = d;
       }
     }
     __syncthreads();
@@ -979,8 +979,8 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
       for (int i = 0; i < NP; ++i) {
         pin_regs(ld[i]);
         const float d = row_dot<FMT, L, S>(ld[i], xr);
-        const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 0));
-        const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L));
+        const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), kRowSumLane<L>));
+        const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L + kRowSumLane<L>));
         if (lane == i) {
           g_sel = gv;
           u_sel = uv;
@@ -1058,7 +1058,7 @@ __global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams
         pin_regs(ld[i]);
         const float d = row_dot<FMT, L, S>(ld[i], xr);
         const int row = r0 + (i * kWaves + wave) * RPW + rr;
-        if (li == 0 && row < p.H) out[row] = d;
+        if (li == kRowSumLane<L> && row < p.H) out[row] = d;
       }
     }
   }
