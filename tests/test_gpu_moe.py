@@ -227,6 +227,9 @@ def test_layer_routing_ties(dev, E, k, L):
 
 def _decode_with(cfg, dev, m, group, monkeypatch):
     monkeypatch.setenv("BDG_GROUP", group)
+    # the grouped path routes every layer with the route kernel; so must the
+    # per-token path here (no partial sums from the previous down kernel)
+    monkeypatch.setenv("BDG_FUSE_ROUTE", "0")
     plan, _ = sdev.build_plan(cfg, dev, max_m=m)
     x, _ = sdev.hidden_device(cfg, range(m), dev)
     y, tr = bdg.moe_expert_decode(plan, x, traces=True)
@@ -278,3 +281,19 @@ def test_small_m_120b_stack_full(dev):
     plan.close()
     del layers
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("E,k,m", [(4, 2, 16), (2, 2, 16), (8, 8, 16), (6, 1, 9)])
+def test_grouped_heavy_sharing(dev, E, k, m, monkeypatch):
+    """Few experts shared by every token (up to 16 picks of one expert, so an
+    expert spans several chunks; k = E; k = 1): the grouped path against the
+    per-token path bit for bit, and the first layer against the oracle."""
+    cfg = small_cfg("mxfp4", 1800 + 10 * E + k, E=E, k=k, H=256, I=128, L=2, stack=True, m=m)
+    banner(f"grouped heavy sharing E={E} k={k} m={m}")
+    g = _decode_with(cfg, dev, m, "1", monkeypatch)
+    t = _decode_with(cfg, dev, m, "0", monkeypatch)
+    for a, b, what in zip(g, t, ("y", "topk", "wts", "resid")):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b), what
+    y, topk, wts, resid = g
+    check_layer(cfg, 0, resid[0], resid[1], topk[0], wts[0], True, f"sharing E={E} layer 0")
