@@ -85,18 +85,22 @@ __device__ __forceinline__ uint32_t topk_key(float x) {
 }
 
 // Maximum of a per-lane unsigned value over the wavefront (uniform result):
-// quad max by DPP quad permutes, row max by DPP row rotations, then the four
-// row maxima read out.
+// a prefix maximum by DPP row shifts 1, 2, 4, 8 (lane 15 of each row then
+// holds the row's maximum), the GFX9 row broadcasts carry it across rows to
+// lane 63, one readlane.  Lanes without a DPP source read 0, the neutral value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm xor 1
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm xor 2
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(r0, r1), max(r2, r3));
+  v = max(v, dpp_u32<0x111, 0xF>(v));   // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xF>(v));   // row_shr:2
+  v = max(v, dpp_u32<0x114, 0xF>(v));   // row_shr:4
+  v = max(v, dpp_u32<0x118, 0xF>(v));   // row_shr:8
+  v = max(v, dpp_u32<0x142, 0xA>(v));   // row_bcast:15 into rows 1, 3
+  v = max(v, dpp_u32<0x143, 0xC>(v));   // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 // One wavefront: the K largest of row[0..E) in descending order, ties to the
