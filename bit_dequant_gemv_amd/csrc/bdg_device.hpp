@@ -116,10 +116,15 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
-// One DPP move of a float (lanes with no source get 0).
+// One DPP move of a 32-bit value (lanes with no source, or outside ROW_MASK,
+// get 0).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
 }
 
 // Sum over aligned groups of L lanes, valid only in the LAST lane of each

@@ -8,10 +8,11 @@
 // is named there as the untried lever (section 5), and the TinyTitan tracker
 // moves a layer's experts into one submission (entry D114).  Here a layer is
 // at most three kernels, each over ALL chosen experts of the layer:
-//   route  : the router GEMV (one router row per wavefront, the row's loads
-//            issued before the input is staged) and the input's sum of
-//            squares, as one slice of router partial sums; in a stack it
-//            runs for the first layer only (or every layer when E > 64);
+//   route  : the router GEMV (one router row per wavefront) and the input's
+//            sum of squares, as one slice of router partial sums; in an
+//            M = 1 stack it runs for the first layer only (or every layer
+//            when E > 64); for steps of M > 1 it also forms the layer input
+//            from the previous layer's per-pick down outputs;
 //   gate_up: adds the router slices, applies the RMSNorm scale and bias,
 //            and every wavefront computes the top-k + softmax itself; it
 //            issues the loads of all its (g, u) row pairs at once, then
@@ -88,11 +89,6 @@ __device__ __forceinline__ uint32_t topk_key(float x) {
 // a prefix maximum by DPP row shifts 1, 2, 4, 8 (lane 15 of each row then
 // holds the row's maximum), the GFX9 row broadcasts carry it across rows to
 // lane 63, one readlane.  Lanes without a DPP source read 0, the neutral value.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
-}
-
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0x111, 0xF>(v));   // row_shr:1
   v = max(v, dpp_u32<0x112, 0xF>(v));   // row_shr:2
@@ -190,8 +186,8 @@ struct RouteParams {
   float* resid_trace; // [M][H] or NULL, written by block 0
   float* part;        // [M][E + 1][pstride]: slice 0 written
   int pstride;
-  // combine (grouped path): the layer input is x_in (+ x_in when
-  // combine_residual) + sum_j wts[t][j] * dout[t*K + j], j in order
+  // combine (grouped path): the layer input is (x_in when combine_residual,
+  // else 0) + sum_j wts[t][j] * dout[t*K + j], j in order
   const float* dout;  // [M * K][H] previous layer's down output per pick, or NULL
   const float* wts;   // [M][K]
   int K;
@@ -200,6 +196,9 @@ struct RouteParams {
 };
 
 // One router row per wavefront; block b handles rows 4b .. 4b+3 of token t.
+// Used when the layer input has to be formed first (the combine of a grouped
+// step) or when no logits are wanted (only the fp32 copy of x): the input is
+// built once per block in LDS and shared by the block's four rows.
 __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
   extern __shared__ float lds[];
   float* xs = lds;               // [H]
@@ -810,6 +809,7 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 // picks of each in pick order, kGroupTT per chunk.  The block's threads all
 // call it; the result does not depend on thread timing (the only atomics are
 // an OR and a count).  P <= kGroupMaxPicks, blockDim >= kGroupMaxPicks.
+static_assert(BDG_MAX_EXPERTS / 32 <= kWave, "build_groups scans the used-expert words in one wave");
 __device__ void build_groups(GroupLds& g, int P, int E) {
   const int tid = threadIdx.x;
   const int nw = (E + 31) >> 5;
@@ -1124,7 +1124,7 @@ struct bdg_plan {
   void* dev_base;
   bdg::LayerDev* hl;        // host copy of each layer's weight pointers (passed by value to the kernels)
   float* resid[2];
-  float* part;              // [M][E][pstride] router partial sums
+  float* part;              // [M][E + 1][pstride] router partial sums (column E: sums of squares)
   int pstride;
   int dn_blocks;            // down row blocks per token
   int fuse_route;           // layers >= 1 route from the previous down kernel's partial sums

@@ -77,17 +77,31 @@ def test_layer_small(dev, fmt, m):
     run_and_check(cfg, dev, m)
 
 
+def route_launches(plan, x):
+    """Route-kernel launches of one decode step (per-kernel event pass)."""
+    y = torch.empty((x.shape[0], plan.hidden), dtype=torch.float32, device=x.device)
+    _, cnt = bdg.moe_expert_decode_profiled(plan, x, y)
+    torch.cuda.synchronize()
+    return int(cnt[bdg.KERNEL_KINDS.index("route")])
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4g"])
 @pytest.mark.parametrize("fuse", ["1", "0"])
-def test_stack_small_end_to_end(dev, fmt, fuse, monkeypatch):
-    """fuse=1: layers after the first route from the partial router sums of
-    the previous down kernel; fuse=0: every layer runs the route kernel."""
+@pytest.mark.parametrize("E", [16, 96])
+@pytest.mark.parametrize("m", [1, 2])
+def test_stack_small_end_to_end(dev, fmt, fuse, E, m, monkeypatch):
+    """The per-token path of a 3-layer stack.  fuse=1: for E <= 64, layers
+    after the first route from the partial router sums of the previous down
+    kernel; E = 96 (more router rows than the down epilogue covers) and
+    fuse=0: every layer runs the route kernel."""
     monkeypatch.setenv("BDG_FUSE_ROUTE", fuse)
-    cfg = small_cfg(fmt, 1100, E=16, k=4, H=512, I=256, L=3, stack=True, m=2)
-    plan, layers, x, y, tr = run_and_check(cfg, dev, 2)
+    monkeypatch.setenv("BDG_GROUP", "0")
+    cfg = small_cfg(fmt, 1100 + E, E=E, k=4, H=512, I=256, L=3, stack=True, m=m)
+    plan, layers, x, y, tr = run_and_check(cfg, dev, m)
+    assert route_launches(plan, x) == (1 if fuse == "1" and E <= 64 else cfg.n_layers)
     # end to end without teacher forcing on the residual (routing forced only in band)
     layers_o = [(synth.router(cfg, l)[0], None, oracle_expert_getter(cfg, l)) for l in range(3)]
-    xv = synth.hidden_batch(cfg, [0, 1])[0]
+    xv = synth.hidden_batch(cfg, list(range(m)))[0]
     results, out = omoe.moe_stack(xv, layers_o, cfg.top_k, forced_idx=to_np(tr["topk"]))
     assert_close(y, out, results[-1]["den"], "stack end to end")
 
@@ -195,13 +209,16 @@ def test_stack_full(dev, name, check_layers):
 
 @pytest.mark.parametrize("E,k", [(32, 4), (128, 8), (256, 8), (300, 16)])
 @pytest.mark.parametrize("L", [1, 2])
-def test_layer_routing_ties(dev, E, k, L):
+@pytest.mark.parametrize("group", ["0", "1"])
+def test_layer_routing_ties(dev, E, k, L, group, monkeypatch):
     """The expert selection inside the fused path on tie-heavy logits: zero
     router rows, so each logit is its bias, drawn from a small value set with
     -inf entries.  The selection must match the oracle's order exactly (ties
     to the lower index), and the layer output the oracle's for those picks.
-    L=2 checks the second layer of a residual stack, which (for E <= 64)
-    routes from the partial sums written by the first layer's down kernel."""
+    L=2 checks the second layer of a residual stack, which on the per-token
+    path (group=0; for E <= 64) routes from the partial sums written by the
+    first layer's down kernel; group=1 runs the grouped kernels."""
+    monkeypatch.setenv("BDG_GROUP", group)
     cfg = small_cfg("mxfp4", 1500 + E, E=E, k=k, H=128, I=64, m=2, L=L, stack=L > 1)
     rng = np.random.default_rng(E)
     b = rng.choice(np.array([1.0, 0.5, 0.5, 0.0, -np.inf], dtype=np.float32), size=E)
@@ -245,7 +262,8 @@ def test_grouped_equals_per_token(dev, fmt, m, monkeypatch):
     """Steps of M > 1 tokens read each chosen expert once (grouped kernels);
     every output row is the same arithmetic as on the per-token path (same
     row dot products, the combine in slot order), so the two agree bit for
-    bit.  E > 64 keeps both paths on the route kernel."""
+    bit.  The per-token side routes every layer with the route kernel, as the
+    grouped path does."""
     cfg = small_cfg(fmt, 1700 + m, E=80, k=4, H=384, I=192, L=3, stack=True, m=m)
     banner(f"grouped vs per-token fmt={fmt} m={m}")
     g = _decode_with(cfg, dev, m, "1", monkeypatch)
