@@ -15,7 +15,10 @@ Prints one JSON line: the expert-path HBM rate (algorithmic packed-weight
 bytes of every (layer, expert) matrix the step uses, once, plus the router
 weights, over GPU time), the per-kernel roofline figure of the dominant
 kernel (gate_up), the measured streaming-read rate, and the CPU oracle timed
-on a bounded sample.
+on a bounded sample.  After the timed run the same steps run again twice,
+untimed for the headline: with an event pair around each step (the per-step
+median / mean / spread) and with a host sync after each step (sync mode, the
+wall time when the host picks every next token).
 """
 
 import argparse
@@ -471,6 +474,29 @@ def main():
     log(f"timed {K} steps of M={m}: {gpu_ms / K * 1e3:.1f} us/step GPU, {gpu_ms / K / m * 1e3:.1f} us/token, "
         f"{wall / K * 1e6:.1f} us/step wall, {value:.1f} GB/s (unique experts/layer {mean_uniq:.2f})")
 
+    # per-step distribution: an event pair around each replay (stream mode), and
+    # sync mode: a host sync after every step, as when the host picks the next
+    # token; both on the same steps, after the timed run
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i, s in enumerate(range(W, W + K)):
+        x_buf.copy_(x_all[s])
+        ev[i][0].record()
+        bdg.moe_expert_decode(plan, x_buf, y=y_buf)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    step_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    sync_us = []
+    for s in range(W, W + K):
+        t1 = time.perf_counter()
+        x_buf.copy_(x_all[s])
+        bdg.moe_expert_decode(plan, x_buf, y=y_buf)
+        torch.cuda.synchronize()
+        sync_us.append((time.perf_counter() - t1) * 1e6)
+    per_step = {"median_us": round(statistics.median(step_us), 2), "mean_us": round(statistics.mean(step_us), 2),
+                "min_us": round(min(step_us), 2), "max_us": round(max(step_us), 2)}
+    sync_mode = {"median_us": round(statistics.median(sync_us), 2), "mean_us": round(statistics.mean(sync_us), 2)}
+    log(f"per step (events around each replay): {per_step}; sync mode wall per step: {sync_mode}")
+
     # per-kernel durations, same kernels and grids, start/stop events at each kernel
     acc = None
     for s in range(W, W + K):
@@ -530,6 +556,9 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "us_per_token": round(gpu_ms / K / m * 1e3, 2),
         "wall_us_per_token": round(wall / K / m * 1e6, 2),
+        "per_step_gpu": per_step,
+        "sync_mode_wall_per_step": sync_mode,
+        "pct_of_stream_read": round(100.0 * value / stream["best_GBps"], 2) if stream else None,
         "roofline": {
             "kernel": "moe_gateup_kernel",
             "bound": "hbm",
