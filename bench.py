@@ -282,6 +282,96 @@ def bench_gemv(torch, bdg, synth, sdev, dev, cfg, args):
     print(json.dumps(out), flush=True)
 
 
+def dense_bytes(cfg):
+    """Packed bytes of one dense matrix: codes + scales (+ int4 zero points)."""
+    if cfg.fmt == "mxfp4":
+        return cfg.n * cfg.k // 2 + cfg.n * (cfg.k // 32)
+    groups = cfg.k // cfg.group
+    return cfg.n * cfg.k // 2 + cfg.n * groups * 2 + cfg.n * ((groups + 1) // 2)
+
+
+def bench_dense(torch, bdg, synth, sdev, dev, cfg, args):
+    """One dense packed GEMV on a non-expert shape at M=1 (bf16 x): cfg.rotate
+    distinct matrices, together larger than L2 and the Infinity Cache, called
+    in turn from a captured graph, so every call reads its matrix from HBM.
+    The time per call (events around the replays) is the kernel plus the gap
+    between graph nodes, so the roofline figure from it is a lower bound."""
+    import numpy as np
+
+    R = cfg.rotate
+    nbytes = dense_bytes(cfg)
+    calls = max(R, (64 // R) * R)                      # calls per graph replay
+    K = args.steps if args.steps is not None else 8
+    W = args.warmup if args.warmup is not None else 2
+    t0 = time.time()
+    qws = []
+    for i in range(R):
+        arrs = synth.dense_matrix(cfg, i)
+        qws.append(sdev.qweight_from_arrays(cfg.fmt, arrs, cfg.group, dev))
+        del arrs
+    log(f"uploaded {R} matrices of {nbytes / 1e6:.1f} MB ({time.time() - t0:.1f} s)")
+    _, xbits = synth.hidden(cfg, 0)
+    x = torch.from_numpy(xbits.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty(cfg.n, dtype=torch.float32, device=dev)
+
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for c in range(calls):
+                bdg.qgemv(qws[c % R], x, out=y)
+    torch.cuda.current_stream().wait_stream(st)
+    for _ in range(W):
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        g.replay()
+    b.record()
+    b.synchronize()
+    call_us = a.elapsed_time(b) * 1e3 / (K * calls)
+    value = nbytes / (call_us * 1e-6) / 1e9
+    if not torch.isfinite(y).all():
+        raise SystemExit("non-finite output")
+    log(f"{cfg.name}: {call_us:.2f} us/call in the graph ({value:.1f} GB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on a bounded row sample (dequantize + float64 matvec), scaled by bytes
+        from oracle import formats, gemv as ogemv
+        arrs = synth.dense_matrix(cfg, 0)
+        xv = synth.hidden(cfg, 0)[0]
+        rows = min(cfg.n, 16384)
+        sample = tuple(a_[:rows] for a_ in arrs)
+        sbytes = nbytes * rows / cfg.n
+        t1 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t1 < 10.0 or n < 2:
+            if cfg.fmt == "mxfp4":
+                w = formats.mxfp4_dequant(*sample)
+            else:
+                w = formats.int4g_dequant(*sample, cfg.group)
+            ogemv.gemv(w, xv)
+            n += 1
+        dt = (time.perf_counter() - t1) / n
+        cpu = {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+               "cores": int(os.cpu_count() or 1),
+               "sample": f"{rows} of {cfg.n} rows, {n} passes of dequant (NumPy) + float64 matvec"}
+    out = base_record(cfg, value, K * calls, W * calls, call_us * 1e-3, {
+        "workload": cfg.name, "fmt": cfg.fmt, "n": cfg.n, "k": cfg.k, "m": 1,
+        "matrices_rotated": R, "bytes_per_call": nbytes,
+        "timing": f"graph of {calls} calls replayed; per call = kernel + node gap"})
+    out.update({"us_per_call": round(call_us, 3), "cpu_baseline": cpu,
+                "roofline": {"kernel": "qgemv_kernel", "bound": "hbm", "achieved": round(value, 1),
+                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(value / PEAK_HBM_GBPS, 4),
+                             "traffic": measured_traffic(cfg.name, "qgemv"),
+                             "traffic_algorithmic_bytes": nbytes}})
+    print(json.dumps(out), flush=True)
+
+
 def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     """One bare MoE layer (no norm, no residual) at M=1, rotating over 8
     independently seeded layers (3.4 GB, beyond every cache) with a fresh
@@ -396,6 +486,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nb, "launches": 4}), flush=True)
         return
+    if args.workload in synth.DENSE:
+        return bench_dense(torch, bdg, synth, sdev, dev, synth.DENSE[args.workload], args)
     cfg = synth.CONFIGS[args.workload]
     if cfg.name == "gemv_2880":
         return bench_gemv(torch, bdg, synth, sdev, dev, cfg, args)

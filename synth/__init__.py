@@ -88,6 +88,35 @@ CONFIGS = {
 }
 
 
+@dataclass(frozen=True)
+class DenseConfig:
+    """A single packed weight matrix [n][k] applied to one token's input."""
+    name: str
+    base: int
+    fmt: str
+    n: int                    # rows (outputs)
+    k: int                    # reduction length
+    group: int = 32
+    exp_lo: int = 118
+    exp_hi: int = 128
+    scale_lo: float = 0.005
+    scale_hi: float = 0.02
+    x_dtype: str = "bf16"
+    rotate: int = 2           # distinct matrices called in turn (their bytes exceed every cache)
+
+
+# Dense packed-weight GEMVs on the non-expert shapes around the path: the
+# gpt-oss vocabulary head (201,088 rows over the 2880-wide hidden state; the
+# pages' 201088-way argmax, "Sovereign gpt-oss-20B (MXFP4) on Apple Silicon",
+# section 1) and the packed-int4 head-width matrix the tracker's fused int4
+# kernel is timed on (32768 x 2048, tracker entry D110).
+DENSE = {
+    "lmhead_201088": DenseConfig(name="lmhead_201088", base=601, fmt=FMT_MXFP4, n=201088, k=2880, rotate=2),
+    "int4_32768x2048": DenseConfig(name="int4_32768x2048", base=701, fmt=FMT_INT4G, n=32768, k=2048,
+                                   group=64, rotate=16),
+}
+
+
 def rng_for(base, layer, expert, kind):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([base, layer, expert, kind])))
 
@@ -151,6 +180,14 @@ def gemv_matrix(cfg: MoEConfig, index=0):
                         cfg.hidden, cfg.hidden, cfg.exp_lo, cfg.exp_hi)
 
 
+def dense_matrix(cfg: DenseConfig, index=0):
+    """Packed arrays of dense matrix number ``index`` (see DENSE)."""
+    if cfg.fmt == FMT_MXFP4:
+        return mxfp4_matrix(cfg.base, index, 0, K_DN_CODES, K_DN_SCALES, cfg.n, cfg.k, cfg.exp_lo, cfg.exp_hi)
+    return int4g_matrix(cfg.base, index, 0, (K_DN_CODES, K_DN_SCALES, K_DN_ZEROS), cfg.n, cfg.k, cfg.group,
+                        cfg.scale_lo, cfg.scale_hi)
+
+
 def router(cfg: MoEConfig, layer):
     """(W_r fp32 [E][H], bias fp32 [E] or None, hot set or None) for one layer.
 
@@ -179,13 +216,15 @@ def bf16_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def hidden(cfg: MoEConfig, token, n=None):
-    """Hidden state of one token, N(0, 1).
+def hidden(cfg, token, n=None):
+    """Hidden state of one token, N(0, 1) (length hidden, or k for a dense
+    matrix).
 
     Returns (values as fp32, bits): bits is the bf16 uint16 array for bf16
     workloads (values are then exactly bf16) and None for fp32 ones.
     """
-    n = cfg.hidden if n is None else n
+    if n is None:
+        n = cfg.k if isinstance(cfg, DenseConfig) else cfg.hidden
     x = rng_for(cfg.base, HIDDEN_KEY, token, 0).standard_normal(n).astype(np.float32)
     if cfg.x_dtype == "bf16":
         bits = bf16_bits_of(x)

@@ -105,6 +105,32 @@ def test_qgemv_gemv_2880(dev, index):
     assert_close(y, y_ref, den, "qgemv")
 
 
+@pytest.mark.parametrize("name", sorted(synth.DENSE))
+@pytest.mark.parametrize("m", [1, 4])
+def test_qgemv_dense_workloads(dev, name, m):
+    """The dense non-expert shapes (201,088-row MXFP4 vocabulary head, 32768 x
+    2048 int4) at full size, in the launch configuration the benchmark times
+    (m = 1) and at m = 4: 512 sampled rows plus the first and last ones
+    against the oracle (dequantized rows, fp64 products)."""
+    cfg = synth.DENSE[name]
+    arrs = synth.dense_matrix(cfg, 0)
+    x, xbits = synth.hidden_batch(cfg, range(m))
+    banner(f"qgemv dense {name} m={m}")
+    if cfg.fmt == "mxfp4":
+        qw = mx_weight(*arrs, dev)
+    else:
+        qw = i4_weight(*arrs, cfg.group, dev)
+    y = to_np(bdg.qgemv(qw, dev_t(xbits, dev).view(torch.bfloat16)))   # bf16 input, as benchmarked
+    rows = np.unique(np.concatenate([[0, cfg.n - 1], np.random.default_rng(cfg.base).integers(0, cfg.n, 512)]))
+    if cfg.fmt == "mxfp4":
+        w = formats.mxfp4_dequant(arrs[0][rows], arrs[1][rows])
+    else:
+        w = formats.int4g_dequant(arrs[0][rows], arrs[1][rows], arrs[2][rows], cfg.group)
+    y_ref, den = ogemv.gemv(w, x)
+    assert np.all(np.isfinite(y))
+    assert_close(y[:, rows], y_ref, den, f"qgemv {name}")
+
+
 @pytest.mark.parametrize("n,k", [(1, 32), (3, 96), (7, 288), (37, 768), (130, 2048), (65, 2880),
                                  (33, 5760), (9, 8192), (5, 1056)])
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4g"])
