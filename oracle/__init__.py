@@ -15,10 +15,13 @@ Every function restates a plain definition in NumPy float64:
 * ``moe``      - RMSNorm, router logits, top-k with softmax weights, the
   SiLU-gated SwiGLU expert FFN, the router-weighted combine, and the
   residual layer stack (layer-major evaluation, optional teacher forcing).
+* ``mxq``      - MXFP8 (E4M3 + E8M0 per 32) quantization of activations and
+  the MX-scaled product of MXFP4 weights with MXFP8 activations (the
+  large-M / prefill GEMM).
 
 Where the pages leave a step open (they print no formula: the Methods
 sections of all three octopusresearch pages are empty) each module states the
 reading it takes.
 """
 
-from . import formats, gemv, moe  # noqa: F401
+from . import formats, gemv, moe, mxq  # noqa: F401

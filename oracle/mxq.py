@@ -1,0 +1,127 @@
+"""MX quantization of activations (MXFP8 E4M3) and the MX-scaled product.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__``).
+
+The pages name grouped-expert GEMM over the active experts as the lever left
+untried ("Sovereign gpt-oss-20B (MXFP4) on Apple Silicon", section 5) and fp8
+/ grouped-expert GEMM as what lies beyond the single-stream floor ("Amortizing
+the per-token host-sync setup tax in fused all-layer q4 decode", section 5).
+They print no activation format, so the reading taken is the OCP
+Microscaling Formats (MX) v1.0 one for MXFP8:
+
+* an element is FP8 E4M3 - 1 sign bit, 4 exponent bits with bias 7, 3
+  mantissa bits; exponent field 0 is subnormal (m * 2^-9); the pattern
+  S.1111.111 is NaN, so the largest finite magnitude is 448 (there is no
+  infinity);
+* a block of 32 contiguous K-elements of one row shares an E8M0 scale 2^X.
+
+Quantization of one block x[0..31] (the spec's conversion, with the open
+points read as stated):
+
+1. amax = max |x_i|.  If amax is NaN or infinite the block is not finite:
+   scale byte 255 (NaN) and every element code 0x7F (NaN).
+2. X = floor(log2(amax)) - 8, 8 being the exponent of E4M3's largest normal
+   (448 = 1.75 * 2^8); for amax = 0, X = -127.  X is clamped to [-127, 127];
+   the scale byte is X + 127.
+3. Each element v_i = x_i / 2^X is rounded to the nearest E4M3 value, ties to
+   the even code, and magnitudes at or above 448 saturate to 448 (v can reach
+   just under 512).  The sign is kept, so -0.0 and negative values that round
+   to zero give the code 0x80.
+
+Everything here is float64 and value-domain: the rounding is done by finding
+the quantum of v's binade and rounding v / quantum with ``np.rint`` (round
+half to even), not by manipulating bit patterns.
+"""
+
+import numpy as np
+
+from .formats import e8m0_value
+
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest normal
+E4M3_EMIN = -6         # exponent of the smallest normal
+E4M3_MBITS = 3
+MX_BLOCK = 32
+
+
+def e4m3_value(code):
+    """Value(s) of FP8 E4M3 code(s) 0..255 in float64; NaN for S.1111.111."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = (code >> 7) & 1
+    e = (code >> 3) & 15
+    m = code & 7
+    mag = np.where(e == 0, m * 2.0 ** (E4M3_EMIN - E4M3_MBITS),
+                   np.ldexp(1.0 + m / 8.0, e - 7)).astype(np.float64)
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def floor_log2(a):
+    """floor(log2 a) for finite a > 0, exactly (from the binary exponent)."""
+    _, p = np.frexp(np.asarray(a, dtype=np.float64))
+    return p.astype(np.int64) - 1
+
+
+# code of each non-negative finite E4M3 value (codes 0x00..0x7E are increasing)
+_POS_CODES = np.arange(0x7F)
+_POS_VALUES = e4m3_value(_POS_CODES)
+
+
+def e4m3_round(v):
+    """Round float64 values to E4M3 codes: nearest, ties to even code,
+    saturating at +-448 (step 3 of the block conversion above)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    # the quantum of a's binade: 2^(E - 3) for normals, 2^-9 below 2^-6;
+    # E = floor(log2 a) exactly, from frexp (a = f * 2^p, f in [0.5, 1))
+    e = floor_log2(np.where(a > 0, a, 1.0))
+    e = np.clip(e, E4M3_EMIN, E4M3_EMAX)
+    quantum = np.ldexp(1.0, (e - E4M3_MBITS).astype(np.int64))
+    q = np.rint(a / quantum) * quantum          # np.rint: round half to even
+    q = np.minimum(q, E4M3_MAX)                  # saturate (also catches rounding up past 448)
+    code = np.searchsorted(_POS_VALUES, q)       # exact: q is an E4M3 value
+    if not np.all(_POS_VALUES[np.minimum(code, 0x7E)] == q):
+        raise AssertionError("rounded value is not an E4M3 value")
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(x):
+    """Quantize rows of x (float [m][k], k % 32 == 0) to MXFP8 E4M3.
+
+    Returns (codes uint8 [m][k], scales uint8 [m][k/32]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim == 1:
+        x = x[None, :]
+    m, k = x.shape
+    if k % MX_BLOCK:
+        raise ValueError("MXFP8: k must be a multiple of 32")
+    blocks = x.reshape(m, k // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    finite = np.isfinite(amax)
+    xexp = np.where(amax > 0, floor_log2(np.where(finite & (amax > 0), amax, 1.0)) - E4M3_EMAX, -127)
+    xexp = np.clip(xexp, -127, 127).astype(np.int64)
+    scales = np.where(finite, xexp + 127, 255).astype(np.uint8)
+    v = blocks / np.ldexp(1.0, xexp)[:, :, None]
+    v = np.where(finite[:, :, None], v, 0.0)
+    codes = e4m3_round(v)
+    codes = np.where(finite[:, :, None], codes, 0x7F).astype(np.uint8)
+    return codes.reshape(m, k), scales
+
+
+def mxfp8_dequant64(codes, scales):
+    """float64 values of an MXFP8 tensor (codes [m][k], scales [m][k/32])."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    m, k = codes.shape
+    s = np.repeat(e8m0_value(scales), MX_BLOCK, axis=1)
+    return e4m3_value(codes) * s
+
+
+def mx_gemm(w_codes, w_scales, x_codes, x_scales):
+    """y[m][n] = sum_k W[n][k] * xq[m][k] for MXFP4 weights W and MXFP8
+    activations xq, both dequantized exactly to float64, plus the normaliser
+    den[m][n] = sum_k |W[n][k]| |xq[m][k]| (the GEMV definition with the
+    quantized activations in place of x)."""
+    from .formats import mxfp4_dequant64
+    from .gemv import gemv
+    return gemv(mxfp4_dequant64(w_codes, w_scales), mxfp8_dequant64(x_codes, x_scales))
