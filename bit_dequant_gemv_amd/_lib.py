@@ -30,7 +30,7 @@ BDG_MAX_M = 16
 EXPORTED = (
     "mxfp4_dequant", "int4g_dequant", "qgemv", "moe_router_topk",
     "moe_plan_create", "moe_plan_destroy", "moe_expert_decode", "moe_experts_routed",
-    "moe_expert_decode_profiled",
+    "moe_expert_decode_profiled", "mxfp8_quantize", "mx_gemm",
     "bdg_stream_read", "bdg_stream_copy", "bdg_strerror", "bdg_version",
 )
 
@@ -90,6 +90,8 @@ def load():
         "moe_expert_decode": [vp, vp, i32, i32, vp, vp, vp, vp, vp],
         "moe_experts_routed": [vp, i32, vp, i32, i32, vp, vp, vp, vp],
         "moe_expert_decode_profiled": [vp, vp, i32, i32, vp, vp, vp, vp],
+        "mxfp8_quantize": [vp, i32, i64, i64, vp, vp, vp],
+        "mx_gemm": [ctypes.POINTER(QMat), vp, vp, i64, vp, vp],
         "bdg_stream_read": [vp, i64, vp, i32, vp],
         "bdg_stream_copy": [vp, vp, i64, vp],
         "bdg_strerror": [i32],

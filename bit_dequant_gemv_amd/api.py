@@ -109,6 +109,35 @@ def qgemv(w: QWeight, x, out=None):
     return y[0] if squeeze and out is None else y
 
 
+def mxfp8_quantize(x, codes=None, scales=None):
+    """MXFP8 quantization of activations x [m][k] (fp32 or bf16): returns
+    (codes uint8 [m][k], scales uint8 [m][k/32])."""
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    m, k = x2.shape
+    if codes is None:
+        codes = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    check("mxfp8_quantize", _lib.load().mxfp8_quantize(
+        _dev_ptr(x2, "x"), _x_dtype(x2), m, k, _dev_ptr(codes, "codes", torch.uint8),
+        _dev_ptr(scales, "scales", torch.uint8), _stream()))
+    return codes, scales
+
+
+def mx_gemm(w: QWeight, codes, scales, out=None):
+    """y [m][n] = W xq^T for MXFP4 W [n][k] and MXFP8 activations (codes [m][k],
+    scales [m][k/32]) on the MX-scaled matrix cores."""
+    m = codes.shape[0]
+    if codes.shape[1] != w.k or scales.shape != (m, w.k // 32):
+        raise ValueError("activation shapes do not match W")
+    y = out if out is not None else torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
+    qm = w.qmat()
+    check("mx_gemm", _lib.load().mx_gemm(ctypes.byref(qm), _dev_ptr(codes, "codes", torch.uint8),
+                                         _dev_ptr(scales, "scales", torch.uint8), m,
+                                         _dev_ptr(y, "y", torch.float32), _stream()))
+    return y
+
+
 def moe_router_topk(x, w_r, b_r=None, topk=4, rmsnorm=False, eps=1e-5):
     """(idx [m][k] int32, wts [m][k] fp32, logits [m][E] fp32)."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x

@@ -206,6 +206,31 @@ int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, fl
 int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int32_t x_dtype, int32_t m,
                        const int32_t* idx, const float* wts, float* y, void* stream);
 
+/* ---- large-M product on the MX-scaled matrix cores ---- */
+
+/* mxfp8_quantize - quantize activations x [m][k] (x_dtype BDG_F32 or
+ * BDG_BF16, device, 16-byte aligned) to MXFP8: codes [m][k] FP8 E4M3 bytes
+ * (device, 4-byte aligned) and scales [m][k/32] E8M0 bytes (device), one
+ * per 32 contiguous elements of a row.  OCP MX v1.0 conversion, the reading
+ * for the fp8 / grouped-expert GEMM that the host-sync page (section 5) and
+ * the gpt-oss page (section 5) leave beyond their decode path: scale
+ * 2^X with X = floor(log2 max|x|) - 8 (clamped to >= -127; an all-zero
+ * block gives X = -127), elements x / 2^X rounded to nearest, ties to even,
+ * saturating at +-448; a block holding a NaN or infinity gets scale 255 and
+ * codes 0x7F.  k % 32 == 0. */
+int mxfp8_quantize(const void* x, int32_t x_dtype, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
+                   void* stream);
+
+/* mx_gemm - y[t][r] = sum_c W[r][c] * xq[t][c] for t < m: MXFP4 weights W
+ * (bdg_qmat, BDG_FMT_MXFP4, PLAIN layout, expert strides ignored) times
+ * MXFP8 activations (x_codes [m][k], x_scales [m][k/32] from
+ * mxfp8_quantize; x_codes 16-byte aligned), on the MX-scaled MFMA with fp32
+ * accumulation; y [m][n] fp32, device.  The instruction sums its products
+ * at reduced internal precision, so results agree with the exact product to
+ * about 1e-4 of sum |W||xq| (not bit for bit).  Any m >= 1, n >= 1. */
+int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, float* y,
+            void* stream);
+
 /* ---- measurement aids ---- */
 
 /* moe_expert_decode_profiled - one decode step exactly as moe_expert_decode
