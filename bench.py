@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published peak
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak (no sparsity)
 METRIC = "expert-path HBM GB/s (% of peak) + us/token, gpt-oss-20B-shape MoE at M=1"
 
 
@@ -372,6 +373,87 @@ def bench_dense(torch, bdg, synth, sdev, dev, cfg, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
+    """Large-M product on the MX-scaled matrix cores: cfg.m tokens (bf16) are
+    quantized to MXFP8, then multiplied by one MXFP4 matrix [n][k].  Both
+    kernels are timed from captured graphs of 16 calls each (events around
+    the replays); the product is priced against the dense FP8 MFMA peak (the
+    FP4 x FP8 instruction issues at the FP8 rate)."""
+    import numpy as np
+
+    m = args.m if args.m else cfg.m
+    K = args.steps if args.steps is not None else 8
+    W = args.warmup if args.warmup is not None else 2
+    calls = 16
+    arrs = synth.dense_matrix(cfg, 0)
+    qw = sdev.qweight_from_arrays(cfg.fmt, arrs, cfg.group, dev)
+    _, xbits = synth.hidden_batch(cfg, range(m))
+    x = torch.from_numpy(xbits.view(np.int16)).to(dev).view(torch.bfloat16)
+    codes = torch.empty((m, cfg.k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((m, cfg.k // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((m, cfg.n), dtype=torch.float32, device=dev)
+
+    def graph_time(fn):
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(calls):
+                    fn()
+        torch.cuda.current_stream().wait_stream(st)
+        for _ in range(W):
+            g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            g.replay()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / (K * calls)
+
+    q_us = graph_time(lambda: bdg.mxfp8_quantize(x, codes, scales))
+    g_us = graph_time(lambda: bdg.mx_gemm(qw, codes, scales, out=y))
+    if not torch.isfinite(y).all():
+        raise SystemExit("non-finite output")
+    flops = 2.0 * cfg.n * m * cfg.k
+    tflops = flops / (g_us * 1e-6) / 1e12
+    q_bytes = m * cfg.k * 2 + m * cfg.k + m * (cfg.k // 32)
+    log(f"{cfg.name} m={m}: quantize {q_us:.2f} us ({q_bytes / (q_us * 1e-6) / 1e9:.1f} GB/s), "
+        f"gemm {g_us:.2f} us ({tflops:.1f} TFLOP/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import mxq
+        xv = synth.hidden_batch(cfg, range(8))[0]
+        t1 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t1 < 10.0 or n < 2:
+            oc, os_ = mxq.mxfp8_quantize(xv)
+            mxq.mx_gemm(*arrs, oc, os_)
+            n += 1
+        dt = (time.perf_counter() - t1) / n
+        cpu = {"value": round(2.0 * cfg.n * 8 * cfg.k / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+               "cores": int(os.cpu_count() or 1),
+               "sample": f"8 of {m} tokens, {n} passes of quantize + dequantize + float64 product"}
+    out = {
+        "metric": "mx_gemm TFLOP/s (MXFP4 weights x MXFP8 activations)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K * calls, "warmup": W * calls,
+        "ms_per_step": round(g_us * 1e-3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4 x mxfp8 -> f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "n": cfg.n, "k": cfg.k, "m": m,
+                   "timing": f"graphs of {calls} calls replayed; per call = kernel + node gap"},
+        "quantize_us": round(q_us, 3), "quantize_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
+        "gemm_us": round(g_us, 3),
+        "roofline": {"kernel": "mx_gemm_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     """One bare MoE layer (no norm, no residual) at M=1, rotating over 8
     independently seeded layers (3.4 GB, beyond every cache) with a fresh
@@ -486,6 +568,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nb, "launches": 4}), flush=True)
         return
+    if args.workload in synth.DENSE and synth.DENSE[args.workload].m > 1:
+        return bench_mx(torch, bdg, synth, sdev, dev, synth.DENSE[args.workload], args)
     if args.workload in synth.DENSE:
         return bench_dense(torch, bdg, synth, sdev, dev, synth.DENSE[args.workload], args)
     cfg = synth.CONFIGS[args.workload]

@@ -103,6 +103,7 @@ class DenseConfig:
     scale_hi: float = 0.02
     x_dtype: str = "bf16"
     rotate: int = 2           # distinct matrices called in turn (their bytes exceed every cache)
+    m: int = 1                # tokens per call
 
 
 # Dense packed-weight GEMVs on the non-expert shapes around the path: the
@@ -114,6 +115,10 @@ DENSE = {
     "lmhead_201088": DenseConfig(name="lmhead_201088", base=601, fmt=FMT_MXFP4, n=201088, k=2880, rotate=2),
     "int4_32768x2048": DenseConfig(name="int4_32768x2048", base=701, fmt=FMT_INT4G, n=32768, k=2048,
                                    group=64, rotate=16),
+    # large-M (prefill) product of one gpt-oss expert's gate_up (5760 x 2880
+    # MXFP4) with 4096 tokens quantized to MXFP8, on the MX-scaled matrix cores
+    "mx_prefill_5760x2880": DenseConfig(name="mx_prefill_5760x2880", base=801, fmt=FMT_MXFP4, n=5760, k=2880,
+                                        rotate=1, m=4096),
 }
 
 
