@@ -60,8 +60,8 @@ def step_bytes(cfg, unique_experts_per_layer):
     return sum(router_bytes(cfg) + u * (gu + dn) for u in unique_experts_per_layer)
 
 
-KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp",
-                  "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
+KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/gemv.hip",
+                  "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp", "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
 
 
 def kernel_sources_sha():
