@@ -454,6 +454,61 @@ def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_prefill(torch, bdg, synth, sdev, dev, cfg, args):
+    """One bare MoE layer over cfg.m tokens at once (prefill): router + top-k,
+    MXFP8 quantization, grouped gate_up GEMM with SwiGLU and requantization,
+    grouped down GEMM, combine - replayed from a captured graph (the entry
+    point takes a preallocated workspace and allocates nothing)."""
+    m = args.m if args.m else cfg.m
+    K = args.steps if args.steps is not None else 8
+    W = args.warmup if args.warmup is not None else 2
+    layer = sdev.upload_layer(cfg, 0, dev, threads=16)
+    x, _ = sdev.hidden_device(cfg, range(m), dev)
+    ws = torch.empty(bdg.prefill_workspace_bytes(m, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty((m, cfg.hidden), dtype=torch.float32, device=dev)
+    bdg.moe_prefill_mx(layer, cfg.n_experts, cfg.top_k, x, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            bdg.moe_prefill_mx(layer, cfg.n_experts, cfg.top_k, x, y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(st)
+    for _ in range(W):
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        g.replay()
+    b.record()
+    b.synchronize()
+    us = a.elapsed_time(b) * 1e3 / K
+    if not torch.isfinite(y).all():
+        raise SystemExit("non-finite output")
+    flops = 2.0 * m * cfg.top_k * (2 * cfg.inter * cfg.hidden + cfg.hidden * cfg.inter)
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"{cfg.name} m={m}: {us:.1f} us per layer, {m / (us * 1e-6):.0f} tokens/s, {tflops:.1f} TFLOP/s")
+    out = {
+        "metric": "prefill MoE layer tokens/s (grouped MX GEMM)", "value": round(m / (us * 1e-6), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(us * 1e-3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4 x mxfp8 -> f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "m": m, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "timing": "graph of one layer replayed; events around the replays"},
+        "layer_TFLOPs": round(tflops, 1),
+        "roofline": {"kernel": "whole layer", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     """One bare MoE layer (no norm, no residual) at M=1, rotating over 8
     independently seeded layers (3.4 GB, beyond every cache) with a fresh
@@ -568,6 +623,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nb, "launches": 4}), flush=True)
         return
+    if args.workload in synth.PREFILL:
+        return bench_prefill(torch, bdg, synth, sdev, dev, synth.PREFILL[args.workload], args)
     if args.workload in synth.DENSE and synth.DENSE[args.workload].m > 1:
         return bench_mx(torch, bdg, synth, sdev, dev, synth.DENSE[args.workload], args)
     if args.workload in synth.DENSE:

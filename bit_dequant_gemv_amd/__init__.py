@@ -6,12 +6,14 @@ The compute lives in ``libbdg.so`` (HIP kernels for gfx950, C ABI in
 
 from .api import (KERNEL_KINDS, MoEPlan, QWeight, int4g_dequant, moe_expert_decode,
                   moe_expert_decode_profiled, moe_experts_routed,
-                  moe_router_topk, mx_gemm, mxfp4_dequant, mxfp8_quantize, qgemv, stream_copy,
-                  stream_read, version)
+                  moe_prefill_mx, moe_router_topk, mx_gemm, mxfp4_dequant, mxfp8_quantize,
+                  prefill_workspace_bytes, prefill_workspace_views, qgemv, stream_copy, stream_read,
+                  version)
 
 __all__ = [
     "KERNEL_KINDS", "MoEPlan", "QWeight", "int4g_dequant", "moe_expert_decode",
     "moe_expert_decode_profiled", "moe_experts_routed",
-    "moe_router_topk", "mx_gemm", "mxfp4_dequant", "mxfp8_quantize", "qgemv", "stream_copy",
-    "stream_read", "version",
+    "moe_prefill_mx", "moe_router_topk", "mx_gemm", "mxfp4_dequant", "mxfp8_quantize",
+    "prefill_workspace_bytes", "prefill_workspace_views", "qgemv", "stream_copy", "stream_read",
+    "version",
 ]

@@ -30,7 +30,8 @@ BDG_MAX_M = 16
 EXPORTED = (
     "mxfp4_dequant", "int4g_dequant", "qgemv", "moe_router_topk",
     "moe_plan_create", "moe_plan_destroy", "moe_expert_decode", "moe_experts_routed",
-    "moe_expert_decode_profiled", "mxfp8_quantize", "mx_gemm",
+    "moe_expert_decode_profiled", "mxfp8_quantize", "mx_gemm", "moe_prefill_mx_workspace",
+    "moe_prefill_mx",
     "bdg_stream_read", "bdg_stream_copy", "bdg_strerror", "bdg_version",
 )
 
@@ -92,6 +93,8 @@ def load():
         "moe_expert_decode_profiled": [vp, vp, i32, i32, vp, vp, vp, vp],
         "mxfp8_quantize": [vp, i32, i64, i64, vp, vp, vp],
         "mx_gemm": [ctypes.POINTER(QMat), vp, vp, i64, vp, vp],
+        "moe_prefill_mx_workspace": [i64, i32, i32, i32, i32],
+        "moe_prefill_mx": [ctypes.POINTER(LayerDesc), i32, i32, vp, i32, i64, vp, vp, vp, vp, i64, vp],
         "bdg_stream_read": [vp, i64, vp, i32, vp],
         "bdg_stream_copy": [vp, vp, i64, vp],
         "bdg_strerror": [i32],
@@ -100,7 +103,8 @@ def load():
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name in ("bdg_strerror", "bdg_version") else ctypes.c_int
+        fn.restype = (ctypes.c_char_p if name in ("bdg_strerror", "bdg_version")
+                      else ctypes.c_int64 if name == "moe_prefill_mx_workspace" else ctypes.c_int)
     _lib = lib
     return lib
 

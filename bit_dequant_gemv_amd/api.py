@@ -138,6 +138,65 @@ def mx_gemm(w: QWeight, codes, scales, out=None):
     return y
 
 
+def moe_prefill_mx(layer, n_experts, top_k, x, y=None, workspace=None):
+    """One bare MoE layer over m tokens on the MX-scaled matrix cores.
+
+    layer: dict with w_router [E][H] fp32, b_router or None, gate_up QWeight
+    [E][2I][H] and down QWeight [E][H][I] (MXFP4).  Returns (y [m][H] fp32,
+    idx [m][k] int32, w [m][k] fp32).  ``workspace`` (a uint8 device tensor of
+    at least ``prefill_workspace_bytes`` bytes) is allocated when not given.
+    """
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    m, hid = x2.shape
+    gu, dn = layer["gate_up"], layer["down"]
+    inter = dn.k
+    need = prefill_workspace_bytes(m, hid, inter, n_experts, top_k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((m, hid), dtype=torch.float32, device=x.device)
+    idx = torch.empty((m, top_k), dtype=torch.int32, device=x.device)
+    wts = torch.empty((m, top_k), dtype=torch.float32, device=x.device)
+    desc = LayerDesc()
+    desc.w_router = _dev_ptr(layer["w_router"], "w_router", torch.float32).value
+    b = layer.get("b_router")
+    desc.b_router = _dev_ptr(b, "b_router", torch.float32).value if b is not None else None
+    desc.gate_up = gu.qmat()
+    desc.down = dn.qmat()
+    check("moe_prefill_mx", _lib.load().moe_prefill_mx(
+        ctypes.byref(desc), n_experts, top_k, _dev_ptr(x2, "x"), _x_dtype(x2), m,
+        _dev_ptr(y, "y", torch.float32), _dev_ptr(idx, "idx", torch.int32), _dev_ptr(wts, "wts", torch.float32),
+        _dev_ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream()))
+    return y, idx, wts
+
+
+def prefill_workspace_views(workspace, m, hidden, inter, n_experts, top_k):
+    """Views of the parts of a moe_prefill_mx workspace (the layout include/bdg.h
+    states: 256-byte aligned parts in order).  For inspection only."""
+    P = m * top_k
+    sizes = [("xq", m * hidden, torch.uint8, (m, hidden)),
+             ("xq_scales", m * (hidden // 32), torch.uint8, (m, hidden // 32)),
+             ("row_off", 4 * (n_experts + 1), torch.int32, (n_experts + 1,)),
+             ("tile_off", 4 * (n_experts + 1), torch.int32, (n_experts + 1,)),
+             ("row_src", 4 * P, torch.int32, (P,)),
+             ("pick_row", 4 * P, torch.int32, (P,)),
+             ("hq", P * inter, torch.uint8, (P, inter)),
+             ("hq_scales", P * (inter // 32), torch.uint8, (P, inter // 32)),
+             ("d", 4 * P * hidden, torch.float32, (P, hidden))]
+    out, off = {}, 0
+    for name, nbytes, dt, shape in sizes:
+        out[name] = workspace[off:off + nbytes].view(dt).view(shape)
+        off += (nbytes + 255) // 256 * 256
+    return out
+
+
+def prefill_workspace_bytes(m, hidden, inter, n_experts, top_k):
+    n = _lib.load().moe_prefill_mx_workspace(m, hidden, inter, n_experts, top_k)
+    if n < 0:
+        raise ValueError("invalid prefill shape")
+    return int(n)
+
+
 def moe_router_topk(x, w_r, b_r=None, topk=4, rmsnorm=False, eps=1e-5):
     """(idx [m][k] int32, wts [m][k] fp32, logits [m][E] fp32)."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x

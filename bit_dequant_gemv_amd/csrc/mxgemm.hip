@@ -124,52 +124,50 @@ struct MxLds {
   uint8_t sb[2][4][kBM];            // [stage][32-block][token] E8M0
 };
 
+// Per-thread source rows, fixed for the whole K loop: the stage loads add
+// only the K offset.  A: load i of a stage reads 16 bytes (one 32-block) of
+// code row a[i]; B: load i reads 16 fp8 codes of activation row b[i]; sa /
+// sb are the scale rows of A row `tid` and of activation row `tid % 128`.
+struct MxRows {
+  const uint8_t* a[4];
+  const uint8_t* b[4];
+  const uint8_t* sa;
+  const uint8_t* sb;
+};
+
 // One stage's global loads for this thread.  All addresses are clamped in
 // bounds and nothing reads the loaded registers until the stage is stored to
 // LDS (a select on a loaded value would make the wave wait for it at once);
 // `valid` marks which pieces lie inside K, the others are stored as zeros.
 struct MxStage {
   uint4 a[4], b[4];
-  uint32_t sa[4], sb[4];            // scale bytes of the 4 32-blocks (sb: threads < kBM)
+  uint32_t sa[4], sb[4];            // scale bytes of the stage's 4 32-blocks
   uint32_t valid;                   // bit i: a[i] inside K; bit 4 + i: b[i] inside K
 };
 
-__device__ __forceinline__ void mx_stage_load(MxStage& st, const uint8_t* __restrict__ wc,
-                                              const uint8_t* __restrict__ ws, const uint8_t* __restrict__ xc,
-                                              const uint8_t* __restrict__ xs, int64_t n0, int64_t m0, int64_t N,
-                                              int64_t M, int K, int k0, int tid) {
+__device__ __forceinline__ void mx_stage_load(MxStage& st, const MxRows& rows, int K, int k0, int tid) {
   const int kblocks = K >> 5;
   const int kb0 = k0 >> 5;
   uint32_t valid = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // A: uint4 u = 256 i + tid of the stage: row u / 4, piece q = u % 4 (4 lanes per row)
     const int u = i * kGemmThreads + tid;
-    int64_t row = n0 + (u >> 2);
-    row = row < N ? row : N - 1;
-    const int kb = kb0 + (u & 3);
+    const int kb = kb0 + (u & 3);                      // A: piece u % 4 of row u / 4
     const int kbc = kb < kblocks ? kb : kblocks - 1;
-    st.a[i] = ldg_u128(wc + row * (K >> 1) + (int64_t)kbc * 16);
+    st.a[i] = ldg_u128(rows.a[i] + (int64_t)kbc * 16);
     valid |= (kb < kblocks ? 1u : 0u) << i;
-    // B: token u / 8, piece p = u % 8 (16 fp8 values, K k0 + 16 p ..)
-    int64_t tok = m0 + (u >> 3);
-    tok = tok < M ? tok : M - 1;
-    const int kp = k0 + 16 * (u & 7);
+    const int kp = k0 + 16 * (u & 7);                  // B: piece u % 8 of token u / 8
     const int kpc = kp < K ? kp : K - 16;
-    st.b[i] = ldg_u128(xc + tok * K + kpc);
+    st.b[i] = ldg_u128(rows.b[i] + kpc);
     valid |= (kp < K ? 1u : 0u) << (4 + i);
   }
   st.valid = valid;
-  int64_t row = n0 + tid;
-  row = row < N ? row : N - 1;
-  int64_t tok = m0 + (tid & (kBM - 1));
-  tok = tok < M ? tok : M - 1;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int kb = kb0 + q;
     const int kbc = kb < kblocks ? kb : kblocks - 1;
-    st.sa[q] = ldg_u8(ws + row * kblocks + kbc);
-    st.sb[q] = ldg_u8(xs + tok * kblocks + kbc);
+    st.sa[q] = ldg_u8(rows.sa + kbc);
+    st.sb[q] = ldg_u8(rows.sb + kbc);
   }
 }
 
@@ -180,10 +178,10 @@ __device__ __forceinline__ void mx_stage_store(MxLds& l, int buf, const MxStage&
     // component-wise selects (a select of whole structs can become a select
     // of their addresses, which moves the stage to scratch memory)
     const bool oka = (st.valid >> i) & 1u, okb = (st.valid >> (4 + i)) & 1u;
-    l.a[buf][u & 3][(u >> 2) ^ (4 * (u & 3))] = make_uint4(oka ? st.a[i].x : 0u, oka ? st.a[i].y : 0u, oka ? st.a[i].z : 0u,
-                                         oka ? st.a[i].w : 0u);
-    l.b[buf][u & 7][(u >> 3) ^ (2 * (u & 7))] = make_uint4(okb ? st.b[i].x : 0u, okb ? st.b[i].y : 0u, okb ? st.b[i].z : 0u,
-                                         okb ? st.b[i].w : 0u);
+    l.a[buf][u & 3][(u >> 2) ^ (4 * (u & 3))] = make_uint4(oka ? st.a[i].x : 0u, oka ? st.a[i].y : 0u,
+                                                           oka ? st.a[i].z : 0u, oka ? st.a[i].w : 0u);
+    l.b[buf][u & 7][(u >> 3) ^ (2 * (u & 7))] = make_uint4(okb ? st.b[i].x : 0u, okb ? st.b[i].y : 0u,
+                                                           okb ? st.b[i].z : 0u, okb ? st.b[i].w : 0u);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) l.sa[buf][q][tid] = (uint8_t)st.sa[q];
@@ -212,26 +210,137 @@ __device__ __forceinline__ bool mx_tile_of_block(int b, int gx, int gy, int* x, 
   return true;
 }
 
-// y[m][n] = sum_k W[n][k] * xq[m][k].  Block = 4 waves over 256 weight rows
-// x 128 tokens; wave w takes rows 128 (w & 1) + [0, 128) (four 32-row MFMA
-// tiles) and tokens 64 (w >> 1) + [0, 64) (two 32-token tiles): 8 MFMAs per
-// 64-deep step, operands read from LDS.  Global loads run two stages ahead
-// of the MFMAs (two register sets), the LDS holds two stages.
-__global__ void __launch_bounds__(kGemmThreads, 1)
-mx_gemm_kernel(const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws, const uint8_t* __restrict__ xc,
-               const uint8_t* __restrict__ xs, int64_t N, int64_t M, int K, int gx, int gy,
-               float* __restrict__ y) {
+enum MxMode { kMxDense = 0, kMxGateUp = 1, kMxDown = 2 };
+
+struct MxArgs {
+  const uint8_t* wc;                // weight codes (expert 0 in the grouped modes)
+  const uint8_t* ws;                // weight scales
+  int64_t stride_c, stride_s;       // bytes between experts
+  const uint8_t* xc;                // activation codes [rows][K]
+  const uint8_t* xs;                // activation scales [rows][K / 32]
+  int64_t N;                        // weight rows (dense, down); gate_up: 2 I
+  int64_t M;                        // dense: tokens
+  int K;
+  int gx, gy;                       // row tiles; dense: token tiles
+  // grouped modes: experts' rows in grouped order
+  int E;
+  int I;                            // gate_up: intermediate size
+  const int32_t* row_off;           // [E + 1] first grouped row of each expert
+  const int32_t* tile_off;          // [E + 1] first token tile of each expert
+  const int32_t* row_src;           // gate_up: activation row of each grouped row
+  float* y;                         // dense [M][N]; down [grouped rows][N]
+  uint8_t* hc;                      // gate_up: h codes [grouped rows][I]
+  uint8_t* hs;                      // gate_up: h scales [grouped rows][I / 32]
+};
+
+// Block tile of the 256 x 128 (weight rows x tokens) product, 4 waves:
+// wave w takes 128 weight rows (four 32-row MFMA tiles) and 64 tokens (two
+// 32-token tiles): 8 MFMAs per 64-deep step, operands read from LDS.  Global
+// loads run two stages ahead of the MFMAs (two register sets), the LDS holds
+// two stages.
+//   kMxDense : y[m][n] = sum_k W[n][k] xq[m][k].
+//   kMxGateUp: block (token tile of expert e, 128 intermediate rows): A rows
+//              0..127 are gate rows i, 128..255 the up rows I + i, and each
+//              wave holds the gate and up sums of the same 64 rows, so
+//              h = silu(g) * u is formed in registers and quantized to MXFP8
+//              along the intermediate axis (a 32-row MFMA tile is one block)
+//              straight into the down product's operand.
+//   kMxDown  : d[r][n] = sum_i Wd_e[n][i] hq[r][i] for the expert's grouped rows r.
+template <int MODE>
+__global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
   __shared__ MxLds l;
-  int tx, ty;
-  if (!mx_tile_of_block(blockIdx.x, gx, gy, &tx, &ty)) return;   // block-uniform
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
-  const int64_t n0 = (int64_t)tx * kBN;
-  const int64_t m0 = (int64_t)ty * kBM;
-  const int wr = (wave & 1) * 128;                 // the wave's first row in the block tile
-  const int wt = (wave >> 1) * 64;                 // the wave's first token in the block tile
+  const int K = p.K;
+  const int kblocks = K >> 5;
+
+  // the block's tile: weight rows from n0 (or intermediate rows from i0),
+  // token slots [0, 128) -> tokens m0 + slot, or grouped rows r0 + slot (< r_end)
+  int64_t n0 = 0, m0 = 0;
+  int e = 0, r0 = 0, r_end = 0;
+  const uint8_t* wc = p.wc;
+  const uint8_t* ws = p.ws;
+  if (MODE == kMxDense) {
+    int tx, ty;
+    if (!mx_tile_of_block(blockIdx.x, p.gx, p.gy, &tx, &ty)) return;   // block-uniform
+    n0 = (int64_t)tx * kBN;
+    m0 = (int64_t)ty * kBM;
+  } else {
+    const int T = (int)blockIdx.x / p.gx;
+    const int tx = (int)blockIdx.x - T * p.gx;
+    if (T >= p.tile_off[p.E]) return;                                  // block-uniform
+    int lo = 0, hi = p.E;                                              // tile_off[lo] <= T < tile_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_off[mid] <= T) lo = mid; else hi = mid;
+    }
+    e = lo;
+    r0 = p.row_off[e] + (T - p.tile_off[e]) * kBM;
+    r_end = p.row_off[e + 1];
+    wc += (int64_t)e * p.stride_c;
+    ws += (int64_t)e * p.stride_s;
+    n0 = (int64_t)tx * (MODE == kMxGateUp ? kBN / 2 : kBN);
+  }
+
+  MxRows rows;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = i * kGemmThreads + tid;
+    const int br = u >> 2;                                   // block row of A load i
+    int64_t row;
+    if (MODE == kMxGateUp) {
+      int64_t ir = n0 + (br & 127);
+      ir = ir < p.I ? ir : p.I - 1;
+      row = br < 128 ? ir : p.I + ir;
+    } else {
+      row = n0 + br;
+      row = row < p.N ? row : p.N - 1;
+    }
+    rows.a[i] = wc + row * (K >> 1);
+    const int slot = u >> 3;                                 // token slot of B load i
+    int64_t src;
+    if (MODE == kMxDense) {
+      src = m0 + slot;
+      src = src < p.M ? src : p.M - 1;
+    } else {
+      int gr = r0 + slot;
+      gr = gr < r_end ? gr : r_end - 1;
+      src = MODE == kMxGateUp ? p.row_src[gr] : gr;
+    }
+    rows.b[i] = p.xc + src * K;
+  }
+  {
+    int64_t row;
+    if (MODE == kMxGateUp) {
+      int64_t ir = n0 + (tid & 127);
+      ir = ir < p.I ? ir : p.I - 1;
+      row = tid < 128 ? ir : p.I + ir;
+    } else {
+      row = n0 + tid;
+      row = row < p.N ? row : p.N - 1;
+    }
+    rows.sa = ws + row * kblocks;
+    const int slot = tid & (kBM - 1);
+    int64_t src;
+    if (MODE == kMxDense) {
+      src = m0 + slot;
+      src = src < p.M ? src : p.M - 1;
+    } else {
+      int gr = r0 + slot;
+      gr = gr < r_end ? gr : r_end - 1;
+      src = MODE == kMxGateUp ? p.row_src[gr] : gr;
+    }
+    rows.sb = p.xs + src * kblocks;
+  }
+
+  // the wave's A tiles: block rows arow(a) + j; gate_up pairs tile a (gate)
+  // with tile a + 2 (up) over the same intermediate rows
+  const int wt = (wave >> 1) * 64;                 // the wave's first token slot
+  auto arow = [&](int a) {
+    return MODE == kMxGateUp ? (a >> 1) * 128 + (wave & 1) * 64 + 32 * (a & 1) : (wave & 1) * 128 + 32 * a;
+  };
   v16f acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -250,7 +359,7 @@ mx_gemm_kernel(const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws, c
       const int pa = 2 * ks + h;                  // A piece (32-block of the stage)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int r = wr + 32 * a + j;
+        const int r = arow(a) + j;
         const uint4 q = l.a[buf][pa][r ^ (4 * pa)];
         A[ks][a][0] = (int)q.x;
         A[ks][a][1] = (int)q.y;
@@ -294,44 +403,157 @@ mx_gemm_kernel(const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws, c
   const int stages = (K + kBK - 1) / kBK;
   const int padded = (stages + 1) & ~1;
   MxStage s0, s1;
-  mx_stage_load(s0, wc, ws, xc, xs, n0, m0, N, M, K, 0, tid);
-  mx_stage_load(s1, wc, ws, xc, xs, n0, m0, N, M, K, kBK, tid);
+  mx_stage_load(s0, rows, K, 0, tid);
+  mx_stage_load(s1, rows, K, kBK, tid);
   mx_stage_store(l, 0, s0, tid);
   __syncthreads();
   for (int s = 0; s < padded; s += 2) {
-    mx_stage_load(s0, wc, ws, xc, xs, n0, m0, N, M, K, (s + 2) * kBK, tid);
+    mx_stage_load(s0, rows, K, (s + 2) * kBK, tid);
     compute(0);
     mx_stage_store(l, 1, s1, tid);
     __syncthreads();
-    mx_stage_load(s1, wc, ws, xc, xs, n0, m0, N, M, K, (s + 3) * kBK, tid);
+    mx_stage_load(s1, rows, K, (s + 3) * kBK, tid);
     compute(1);
     mx_stage_store(l, 0, s0, tid);
     __syncthreads();
   }
 
+  if (MODE == kMxGateUp) {
+    // h = silu(g) * u; then MXFP8 per (grouped row, 32 intermediate rows):
+    // lane (j, h) holds 16 of a tile's 32 rows, lane (j, 1 - h) the rest
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int gr = r0 + wt + 32 * b + j;
+      const bool row_ok = gr < r_end;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int64_t i0 = n0 + (wave & 1) * 64 + 32 * a;   // first intermediate row of the tile
+        float hv[16];
+        uint32_t amax = 0, bad = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float g = acc[a][b][r], u = acc[a + 2][b][r];
+          hv[r] = g / (1.0f + expf(-g)) * u;
+          const uint32_t ab = __float_as_uint(hv[r]) & 0x7FFFFFFFu;
+          bad |= ab >= 0x7F800000u ? 1u : 0u;
+          amax = max(amax, ab);
+        }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+        bad |= (uint32_t)__shfl_xor((int)bad, 32);
+        const int eb = (int)(amax >> 23);
+        int X = amax == 0 ? -127 : eb - 127 - 8;
+        X = X < -127 ? -127 : X;
+        const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
+        if (row_ok && i0 < p.I) {
+          uint8_t* hrow = p.hc + (int64_t)gr * p.I;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              word |= (bad ? 0x7Fu : f32_to_e4m3(hv[4 * g4 + q] * inv)) << (8 * q);
+            *reinterpret_cast<uint32_t*>(hrow + i0 + 8 * g4 + 4 * h) = word;
+          }
+          if (h == 0) p.hs[(int64_t)gr * (p.I >> 5) + (i0 >> 5)] = (uint8_t)(bad ? 255 : X + 127);
+        }
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int64_t tok = m0 + wt + 32 * b + j;
-    if (tok >= M) continue;
-    float* yrow = y + tok * N;
+    int64_t orow;                                   // output row: token, or grouped row
+    if (MODE == kMxDense) {
+      orow = m0 + wt + 32 * b + j;
+      if (orow >= p.M) continue;
+    } else {
+      orow = r0 + wt + 32 * b + j;
+      if (orow >= r_end) continue;
+    }
+    float* yrow = p.y + orow * p.N;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t row = n0 + wr + 32 * a + 8 * g + 4 * h;
+        const int64_t row = n0 + arow(a) + 8 * g + 4 * h;
         const float4 v = make_float4(acc[a][b][4 * g + 0], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
                                      acc[a][b][4 * g + 3]);
-        if (row + 3 < N && (N & 3) == 0) {
+        if (row + 3 < p.N && (p.N & 3) == 0) {
           *reinterpret_cast<float4*>(yrow + row) = v;
         } else {
-          if (row + 0 < N) yrow[row + 0] = v.x;
-          if (row + 1 < N) yrow[row + 1] = v.y;
-          if (row + 2 < N) yrow[row + 2] = v.z;
-          if (row + 3 < N) yrow[row + 3] = v.w;
+          if (row + 0 < p.N) yrow[row + 0] = v.x;
+          if (row + 1 < p.N) yrow[row + 1] = v.y;
+          if (row + 2 < p.N) yrow[row + 2] = v.z;
+          if (row + 3 < p.N) yrow[row + 3] = v.w;
         }
       }
     }
   }
+}
+
+// Picks (t, j) of the M x K routing, grouped by expert: row_off / tile_off
+// (token tiles of 128 rows) per expert, row_src[r] = token of grouped row r,
+// pick_row[t K + j] = its grouped row.  One block; counts are exact, the
+// order of one expert's rows depends on atomic timing, which changes no
+// result (every grouped row is computed on its own and the combine reads
+// each pick's row in slot order).
+constexpr int kGroupThreads = 1024;
+
+__global__ void __launch_bounds__(kGroupThreads)
+moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int32_t* __restrict__ row_off,
+                       int32_t* __restrict__ tile_off, int32_t* __restrict__ row_src,
+                       int32_t* __restrict__ pick_row) {
+  __shared__ int cnt[BDG_MAX_EXPERTS];
+  __shared__ int off[BDG_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int q = tid; q < P; q += kGroupThreads) {
+    int e = idx[q];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int r = 0, t = 0;
+    for (int e = 0; e < E; ++e) {
+      row_off[e] = r;
+      tile_off[e] = t;
+      off[e] = r;
+      r += cnt[e];
+      t += (cnt[e] + kBM - 1) / kBM;
+    }
+    row_off[E] = r;
+    tile_off[E] = t;
+  }
+  __syncthreads();
+  for (int q = tid; q < P; q += kGroupThreads) {
+    int e = idx[q];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    const int r = atomicAdd(&off[e], 1);
+    row_src[r] = q / K;
+    pick_row[q] = r;
+  }
+}
+
+// y[t] = sum_j w[t][j] * d[pick_row[t K + j]], j in order.
+__global__ void __launch_bounds__(256)
+moe_prefill_combine_kernel(const float* __restrict__ d, const int32_t* __restrict__ pick_row,
+                           const float* __restrict__ w, int H, int K, float* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int jj = 0; jj < K; ++jj) {
+    const float wj = w[t * K + jj];
+    const float4 dv = ldg_f4(d + (int64_t)pick_row[t * K + jj] * H + c);
+    v.x = __builtin_fmaf(wj, dv.x, v.x);
+    v.y = __builtin_fmaf(wj, dv.y, v.y);
+    v.z = __builtin_fmaf(wj, dv.z, v.z);
+    v.w = __builtin_fmaf(wj, dv.w, v.w);
+  }
+  *reinterpret_cast<float4*>(y + (int64_t)t * H + c) = v;
 }
 
 }  // namespace bdg
@@ -363,8 +585,127 @@ extern "C" int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t*
   const int64_t gy = (m + kBM - 1) / kBM;
   if (gx * gy + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
   const int64_t blocks = (gx * gy + 7) / 8 * 8;     // whole chunks for the 8 XCDs
-  hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)blocks), dim3(kGemmThreads), 0, as_stream(stream),
-                     static_cast<const uint8_t*>(w->codes), static_cast<const uint8_t*>(w->scales), x_codes,
-                     x_scales, w->n, m, (int)w->k, (int)gx, (int)gy, y);
+  MxArgs a{};
+  a.wc = static_cast<const uint8_t*>(w->codes);
+  a.ws = static_cast<const uint8_t*>(w->scales);
+  a.xc = x_codes;
+  a.xs = x_scales;
+  a.N = w->n;
+  a.M = m;
+  a.K = (int)w->k;
+  a.gx = (int)gx;
+  a.gy = (int)gy;
+  a.y = y;
+  hipLaunchKernelGGL(mx_gemm_kernel<kMxDense>, dim3((unsigned)blocks), dim3(kGemmThreads), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+// Workspace of moe_prefill_mx, in order: activation codes [m][H] and scales
+// [m][H/32], row_off / tile_off [E + 1] each, row_src / pick_row [m K] each,
+// h codes [m K][I] and scales [m K][I/32], down outputs [m K][H] fp32; each
+// part 256-byte aligned.
+static int64_t a256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+extern "C" int64_t moe_prefill_mx_workspace(int64_t m, int32_t hidden, int32_t inter, int32_t n_experts,
+                                            int32_t top_k) {
+  if (m < 1 || hidden < 32 || inter < 32 || n_experts < 1 || top_k < 1) return -1;
+  const int64_t P = m * top_k;
+  return a256(m * hidden) + a256(m * (hidden / 32)) + 2 * a256(4 * (int64_t)(n_experts + 1)) + 2 * a256(4 * P) +
+         a256(P * inter) + a256(P * (inter / 32)) + a256(4 * P * hidden);
+}
+
+extern "C" int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r, const float* b_r, int32_t m,
+                               int32_t h, int32_t e, int32_t topk, int32_t flags, float norm_eps, int32_t* idx,
+                               float* wts, float* logits, void* stream);
+
+extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, int32_t top_k, const void* x,
+                              int32_t x_dtype, int64_t m, float* y, int32_t* topk_idx, float* topk_w,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!layer || !x || !y || !topk_idx || !topk_w || !workspace || m < 1) return BDG_E_INVALID;
+  if (n_experts < 1 || top_k < 1 || top_k > n_experts) return BDG_E_INVALID;
+  if (n_experts > BDG_MAX_EXPERTS || top_k > BDG_MAX_TOPK) return BDG_E_UNSUPPORTED;
+  const bdg_qmat& gu = layer->gate_up;
+  const bdg_qmat& dn = layer->down;
+  int st = check_qmat(&gu, true);
+  if (st) return st;
+  st = check_qmat(&dn, true);
+  if (st) return st;
+  if (gu.fmt != BDG_FMT_MXFP4 || dn.fmt != BDG_FMT_MXFP4) return BDG_E_INVALID;
+  const int64_t H = gu.k, I = dn.k;
+  if (gu.n != 2 * I || dn.n != H) return BDG_E_INVALID;
+  if (n_experts > 1 && (gu.expert_stride_codes == 0 || dn.expert_stride_codes == 0)) return BDG_E_INVALID;
+  if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace)) return BDG_E_ALIGN;
+  if (H > 16384 || I > 16384) return BDG_E_UNSUPPORTED;
+  const int64_t need = moe_prefill_mx_workspace(m, (int32_t)H, (int32_t)I, n_experts, top_k);
+  if (workspace_bytes < need) return BDG_E_INVALID;
+  const int64_t P = m * top_k;
+  if (P > (int64_t)1 << 30) return BDG_E_UNSUPPORTED;
+  char* wp = static_cast<char*>(workspace);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(wp);             wp += a256(m * H);
+  uint8_t* xqs = reinterpret_cast<uint8_t*>(wp);            wp += a256(m * (H / 32));
+  int32_t* row_off = reinterpret_cast<int32_t*>(wp);        wp += a256(4 * (int64_t)(n_experts + 1));
+  int32_t* tile_off = reinterpret_cast<int32_t*>(wp);       wp += a256(4 * (int64_t)(n_experts + 1));
+  int32_t* row_src = reinterpret_cast<int32_t*>(wp);        wp += a256(4 * P);
+  int32_t* pick_row = reinterpret_cast<int32_t*>(wp);       wp += a256(4 * P);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(wp);             wp += a256(P * I);
+  uint8_t* hqs = reinterpret_cast<uint8_t*>(wp);            wp += a256(P * (I / 32));
+  float* d = reinterpret_cast<float*>(wp);
+  hipStream_t s = as_stream(stream);
+
+  st = moe_router_topk(x, x_dtype, layer->w_router, layer->b_router, (int32_t)m, (int32_t)H, n_experts, top_k, 0,
+                       0.f, topk_idx, topk_w, nullptr, stream);
+  if (st) return st;
+  st = mxfp8_quantize(x, x_dtype, m, H, xq, xqs, stream);
+  if (st) return st;
+  hipLaunchKernelGGL(moe_group_picks_kernel, dim3(1), dim3(kGroupThreads), 0, s, topk_idx, (int)P, top_k,
+                     n_experts, row_off, tile_off, row_src, pick_row);
+  st = launch_status();
+  if (st) return st;
+  // token tiles: at most one partial tile per expert beyond P / 128
+  const int64_t tiles = (P + kBM - 1) / kBM + n_experts;
+  MxArgs a{};
+  a.E = n_experts;
+  a.row_off = row_off;
+  a.tile_off = tile_off;
+  a.row_src = row_src;
+  // gate_up: 128 intermediate rows per block (their gate and up rows)
+  a.wc = static_cast<const uint8_t*>(gu.codes);
+  a.ws = static_cast<const uint8_t*>(gu.scales);
+  a.stride_c = gu.expert_stride_codes;
+  a.stride_s = gu.expert_stride_scales;
+  a.xc = xq;
+  a.xs = xqs;
+  a.N = 2 * I;
+  a.K = (int)H;
+  a.I = (int)I;
+  a.gx = (int)((I + kBN / 2 - 1) / (kBN / 2));
+  a.hc = hq;
+  a.hs = hqs;
+  if (tiles * a.gx > 2147483647LL) return BDG_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mx_gemm_kernel<kMxGateUp>, dim3((unsigned)(tiles * a.gx)), dim3(kGemmThreads), 0, s, a);
+  st = launch_status();
+  if (st) return st;
+  // down: 256 output rows per block over the grouped h rows
+  MxArgs b{};
+  b.E = n_experts;
+  b.row_off = row_off;
+  b.tile_off = tile_off;
+  b.wc = static_cast<const uint8_t*>(dn.codes);
+  b.ws = static_cast<const uint8_t*>(dn.scales);
+  b.stride_c = dn.expert_stride_codes;
+  b.stride_s = dn.expert_stride_scales;
+  b.xc = hq;
+  b.xs = hqs;
+  b.N = H;
+  b.K = (int)I;
+  b.gx = (int)((H + kBN - 1) / kBN);
+  b.y = d;
+  if (tiles * b.gx > 2147483647LL) return BDG_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mx_gemm_kernel<kMxDown>, dim3((unsigned)(tiles * b.gx)), dim3(kGemmThreads), 0, s, b);
+  st = launch_status();
+  if (st) return st;
+  hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)m), dim3(256), 0, s,
+                     d, pick_row, topk_w, (int)H, top_k, y);
   return launch_status();
 }

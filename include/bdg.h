@@ -231,6 +231,34 @@ int mxfp8_quantize(const void* x, int32_t x_dtype, int64_t m, int64_t k, uint8_t
 int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, float* y,
             void* stream);
 
+/* moe_prefill_mx_workspace - bytes of device workspace moe_prefill_mx needs
+ * for m tokens of a layer of the given shape (-1 for invalid arguments).
+ * Layout (each part starting 256-byte aligned, in this order; P = m * top_k):
+ * activation codes [m][H] and scales [m][H/32] (MXFP8), row_off and
+ * tile_off [E+1] int32, row_src [P] int32 (token of each grouped row),
+ * pick_row [P] int32 (grouped row of pick t*k + j), h codes [P][I] and
+ * scales [P][I/32] (MXFP8), down outputs [P][H] fp32. */
+int64_t moe_prefill_mx_workspace(int64_t m, int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k);
+
+/* moe_prefill_mx - one bare MoE layer (no norm, no residual) over m tokens
+ * at once on the MX-scaled matrix cores: the grouped-expert GEMM the
+ * gpt-oss page leaves untried (section 5).  Router logits of x (fp32),
+ * top-k + softmax as moe_router_topk (written to topk_idx [m][k] int32 and
+ * topk_w [m][k] fp32); x quantized to MXFP8 (mxfp8_quantize); picks grouped
+ * by expert; per expert [g; u] = W_gu . xq on the matrix cores, h = silu(g) *
+ * u quantized to MXFP8 along the intermediate axis in the same kernel,
+ * d = W_d . hq; y[t] = sum_j topk_w[t][j] d_{t,j} in slot order.  layer:
+ * MXFP4 gate_up [E][2I][H] and down [E][H][I] at expert strides, router
+ * w_router [E][H] fp32 (+ b_router); x [m][H] (BDG_F32 / BDG_BF16), y [m][H]
+ * fp32, all device and 16-byte aligned; workspace: device memory of at least
+ * moe_prefill_mx_workspace(...) bytes, owned by the caller (the call
+ * allocates nothing).  Results agree with the exact MX arithmetic to about
+ * 1e-3 of sum |W_d| |hq| (the matrix cores' reduced-precision sums, and the
+ * rare rounding-boundary flips of hq that they cause). */
+int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, int32_t top_k, const void* x, int32_t x_dtype,
+                   int64_t m, float* y, int32_t* topk_idx, float* topk_w, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
 /* ---- measurement aids ---- */
 
 /* moe_expert_decode_profiled - one decode step exactly as moe_expert_decode

@@ -125,3 +125,55 @@ def mx_gemm(w_codes, w_scales, x_codes, x_scales):
     from .formats import mxfp4_dequant64
     from .gemv import gemv
     return gemv(mxfp4_dequant64(w_codes, w_scales), mxfp8_dequant64(x_codes, x_scales))
+
+
+def moe_layer_mx(x, w_r, get_expert_packed, k, bias=None, forced_idx=None):
+    """A bare MoE layer (no norm, no residual) evaluated the large-M way.
+
+    Routing is the oracle's own (``oracle.moe``: logits of x, top-k, softmax
+    over the chosen k; ``forced_idx`` adopts a GPU choice only inside the
+    near-tie band).  Then, per pick (t, j) of expert e:
+      xq = MXFP8(x[t])                      (the activation quantizer above)
+      [g; u] = W_gu[e] . xq,  h = silu(g) * u
+      hq = MXFP8(h)                         (h quantized along the intermediate axis)
+      d = W_d[e] . hq
+    and y[t] = sum_j w[t][j] d_{t,j}, all in float64.
+    den[t] = sum_j w[t][j] |W_d| . |hq| normalises the error of y[t].
+
+    get_expert_packed : e -> ((gu_codes, gu_scales), (dn_codes, dn_scales)).
+    """
+    from . import moe as omoe
+    from .formats import mxfp4_dequant64
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    m = x.shape[0]
+    logits, scale = omoe.router_logits(w_r, x, bias)
+    idx, w = omoe.topk_softmax(logits, k)
+    ties = 0
+    if forced_idx is not None:
+        forced_idx = np.atleast_2d(np.asarray(forced_idx))
+        for t in range(m):
+            ok, n_ties, msg = omoe.check_routing(logits[t], scale[t], forced_idx[t], k)
+            if not ok:
+                raise AssertionError(f"token {t}: {msg}")
+            if n_ties:
+                ties += n_ties
+                idx[t] = forced_idx[t]
+                w[t] = omoe.softmax_over(logits[t], idx[t])
+    xc, xs = mxfp8_quantize(x)
+    xq = mxfp8_dequant64(xc, xs)
+    y = np.zeros_like(x)
+    den = np.zeros_like(x)
+    for e in np.unique(idx):
+        (gc, gs), (dc, ds) = get_expert_packed(int(e))
+        w_gu = mxfp4_dequant64(gc, gs)
+        w_d = mxfp4_dequant64(dc, ds)
+        inter = w_d.shape[1]
+        toks, slots = np.nonzero(idx == e)          # a token picks an expert at most once
+        gu = xq[toks] @ w_gu.T
+        h = omoe.swiglu(gu, inter)
+        hc, hs = mxfp8_quantize(h)
+        hq = mxfp8_dequant64(hc, hs)
+        wt = w[toks, slots][:, None]
+        y[toks] += wt * (hq @ w_d.T)
+        den[toks] += np.abs(wt) * (np.abs(hq) @ np.abs(w_d).T)
+    return dict(y=y, den=den, idx=idx, w=w, logits=logits, scale=scale, ties=ties)

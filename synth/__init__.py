@@ -122,6 +122,15 @@ DENSE = {
 }
 
 
+# Large-M (prefill) evaluation of one bare gpt-oss-20B-shape MoE layer: all
+# tokens of a 4096-token prompt routed at once, the experts as grouped GEMMs on
+# the MX-scaled matrix cores.
+PREFILL = {
+    "gptoss20b_prefill": MoEConfig(name="gptoss20b_prefill", base=901, fmt=FMT_MXFP4, n_layers=1, hidden=2880,
+                                   inter=2880, n_experts=32, top_k=4, norm=False, n_tokens=4096, m=4096),
+}
+
+
 def rng_for(base, layer, expert, kind):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([base, layer, expert, kind])))
 

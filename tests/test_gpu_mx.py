@@ -12,6 +12,7 @@ import torch
 import bit_dequant_gemv_amd as bdg
 import synth
 from oracle import mxq
+from synth import device as sdev
 
 from bit_dequant_gemv_amd._lib import BdgError
 from helpers import banner, to_np
@@ -184,3 +185,120 @@ def test_mx_rejects_bad_args(dev):
         bdg.mx_gemm(w, c, torch.zeros((4, 1), dtype=torch.uint8, device=dev))
     with pytest.raises(BdgError):
         bdg.mxfp8_quantize(torch.zeros((2, 48), dtype=torch.float32, device=dev))
+
+
+# ---------------------------------------------------------------- grouped prefill layer
+
+# Checking the layer.  h is computed on the matrix cores (sums at reduced
+# precision) and then quantized to MXFP8, so an element of h near a rounding
+# boundary - or a block maximum near a power of two - can take the
+# neighbouring code on the GPU: the quantized h is not unique.  The test
+# therefore (1) checks every GPU code of h against the oracle's float64 h:
+# within one quantum of it, block scales within one step, and the codes
+# equal to the oracle's own rounding almost everywhere; then (2) feeds those
+# validated codes to the oracle's down product and combine (teacher forcing,
+# as the routing is forced inside its near-tie band) and holds y to the
+# matrix cores' product error, 5e-4 of den = sum_j w_j |W_d| |hq|; (3) the
+# end-to-end difference from the oracle's own quantization is reported.
+MX_LAYER_TOL = 5e-4
+
+
+def _prefill_case(dev, name, E, k, H, I, m, base):
+    from oracle import formats, moe as omoe
+    cfg = synth.MoEConfig(name=name, base=base, fmt="mxfp4", n_layers=1, hidden=H, inter=I, n_experts=E,
+                          top_k=k, norm=False, m=m)
+    layer = sdev.upload_layer(cfg, 0, dev)
+    x, xv = sdev.hidden_device(cfg, range(m), dev)
+    banner(f"moe_prefill_mx {name} E={E} k={k} H={H} I={I} m={m}")
+    ws = torch.empty(bdg.prefill_workspace_bytes(m, H, I, E, k), dtype=torch.uint8, device=dev)
+    y, idx, wts = bdg.moe_prefill_mx(layer, E, k, x, workspace=ws)
+    torch.cuda.synchronize()
+    views = {n: to_np(v) for n, v in bdg.prefill_workspace_views(ws, m, H, I, E, k).items()}
+    y, idx, wts = to_np(y), to_np(idx), to_np(wts)
+    w_r, b_r, _ = synth.router(cfg, 0)
+
+    def get_packed(e):
+        wts_e = synth.expert_weights(cfg, 0, e)
+        return wts_e["gu"], wts_e["dn"]
+    res = mxq.moe_layer_mx(xv, w_r, get_packed, k, bias=b_r, forced_idx=idx)
+    assert np.array_equal(idx, res["idx"])
+    assert np.max(np.abs(wts - res["w"])) <= 1e-5
+    # the activations and the grouping
+    oc, os_ = mxq.mxfp8_quantize(xv)
+    assert np.array_equal(views["xq"], oc) and np.array_equal(views["xq_scales"], os_)
+    pick_row = views["pick_row"]
+    assert np.array_equal(np.sort(pick_row), np.arange(m * k))
+    assert np.array_equal(views["row_src"][pick_row], np.repeat(np.arange(m), k))
+    # (1) h codes, (2) teacher-forced down product
+    xq = mxq.mxfp8_dequant64(oc, os_)
+    y_tf = np.zeros((m, H))
+    den = np.zeros((m, H))
+    n_codes = n_diff = 0
+    for e in np.unique(idx):
+        (gc, gs), (dc, ds) = get_packed(int(e))
+        w_gu = formats.mxfp4_dequant64(gc, gs)
+        w_d = formats.mxfp4_dequant64(dc, ds)
+        toks, slots = np.nonzero(idx == e)
+        gu = xq[toks] @ w_gu.T
+        h = omoe.swiglu(gu, I)
+        hc_o, hs_o = mxq.mxfp8_quantize(h)
+        # how far the GPU's own h may lie from the float64 h: the matrix
+        # cores' error (<= 1e-4 of sum |terms| per product, taken x10 here)
+        # carried through h = silu(g) u
+        gd = np.abs(xq[toks]) @ np.abs(w_gu).T
+        g, u = gu[:, :I], gu[:, I:]
+        sig = 1.0 / (1.0 + np.exp(-g))
+        herr = 1e-3 * (np.abs(g * sig) * gd[:, I:] + np.abs(u * sig * (1 + g * (1 - sig))) * gd[:, :I])
+        rows = pick_row[toks * k + slots]
+        hc_g, hs_g = views["hq"][rows], views["hq_scales"][rows]
+        assert np.all(np.abs(hs_g.astype(int) - hs_o.astype(int)) <= 1)
+        hq_g = mxq.mxfp8_dequant64(hc_g, hs_g)
+        X = np.repeat(hs_g.astype(np.int64) - 127, 32, axis=1)
+        # within one quantum of the GPU's block (and the GPU's h error) of h
+        lim = 2.0 ** -3 * (np.abs(h) + herr) + 2.0 ** (X - 9) + herr
+        bad = np.abs(hq_g - h) > lim
+        assert not bad.any(), (f"expert {e}: {int(bad.sum())} codes off, worst "
+                               f"{float(np.max((np.abs(hq_g - h) / lim)[bad])):.2f}x the limit")
+        n_codes += hc_g.size
+        n_diff += int(np.count_nonzero(hc_g != hc_o))
+        wt = res["w"][toks, slots][:, None]
+        y_tf[toks] += wt * (hq_g @ w_d.T)
+        den[toks] += np.abs(wt) * (np.abs(hq_g) @ np.abs(w_d).T)
+    frac = n_diff / n_codes
+    rel = float(np.max(np.abs(y - y_tf) / np.maximum(den, 1e-30)))
+    a, b = y.ravel().astype(np.float64), y_tf.ravel()
+    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+    e2e = float(np.max(np.abs(y - res["y"]) / np.maximum(res["den"], 1e-30)))
+    banner(f"moe_prefill_mx {name}: h codes differing from the oracle's rounding {frac:.2e}; "
+           f"y vs teacher-forced {rel:.3e} (cosine {cos:.9f}); end to end {e2e:.3e}; near ties {res['ties']}")
+    assert frac <= 0.01
+    assert np.all(np.isfinite(y))
+    assert rel <= MX_LAYER_TOL and cos >= 0.99999
+
+
+@pytest.mark.parametrize("m", [1, 37, 300])
+def test_moe_prefill_small(dev, m):
+    """Ragged token tiles, experts with no picks (m = 1) and several tiles."""
+    _prefill_case(dev, "prefill_small", 8, 2, 256, 128, m, 2100 + m)
+
+
+def test_moe_prefill_heavy_sharing(dev):
+    """Every token on both experts: 300 grouped rows per expert (3 token tiles)."""
+    _prefill_case(dev, "prefill_share", 2, 2, 384, 160, 300, 2200)
+
+
+def test_moe_prefill_gptoss_layer(dev):
+    """The gpt-oss-20B layer shape (32 experts, top-4, 2880 x 2880) over 512 tokens."""
+    _prefill_case(dev, "prefill_20b", 32, 4, 2880, 2880, 512, 2300)
+
+
+def test_moe_prefill_rejects_bad_args(dev):
+    cfg = synth.MoEConfig(name="bad", base=1, fmt="mxfp4", n_layers=1, hidden=64, inter=32, n_experts=4,
+                          top_k=2, norm=False, m=2)
+    layer = sdev.upload_layer(cfg, 0, dev)
+    x, _ = sdev.hidden_device(cfg, range(2), dev)
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(BdgError):
+        bdg.moe_prefill_mx(layer, 4, 2, x, workspace=small)
+    with pytest.raises(BdgError):
+        bdg.moe_prefill_mx(layer, 4, 5, x)

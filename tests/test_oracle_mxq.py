@@ -166,3 +166,60 @@ def test_mx_gemm_brute_force():
                 dd += abs(w * xv)
             assert y[i, j] == pytest.approx(acc, rel=1e-12, abs=1e-12)
             assert den[i, j] == pytest.approx(dd, rel=1e-12)
+
+
+def _layer_case(seed, m=6, E=4, k=2, H=64, I=32):
+    from oracle import formats
+    rng = np.random.default_rng(seed)
+    w_r = rng.standard_normal((E, H)) * 0.3
+    packed = []
+    for e in range(E):
+        gu = (rng.integers(0, 256, (2 * I, H // 2), dtype=np.uint8), rng.integers(120, 127, (2 * I, H // 32), dtype=np.uint8))
+        dn = (rng.integers(0, 256, (H, I // 2), dtype=np.uint8), rng.integers(120, 127, (H, I // 32), dtype=np.uint8))
+        packed.append((gu, dn))
+    x = rng.standard_normal((m, H))
+
+    def get_packed(e):
+        return packed[e]
+
+    def get_deq(e):
+        (gc, gs), (dc, ds) = packed[e]
+        return formats.mxfp4_dequant64(gc, gs), formats.mxfp4_dequant64(dc, ds)
+    return x, w_r, packed, get_packed, get_deq, k
+
+
+def test_moe_layer_mx_close_to_unquantized():
+    # MXFP8 keeps 3 mantissa bits: the quantized layer stays near the exact one
+    # (same routing: both route on the unquantized x)
+    from oracle import moe as omoe
+    x, w_r, _, get_packed, get_deq, k = _layer_case(21)
+    q = mxq.moe_layer_mx(x, w_r, get_packed, k)
+    ref = omoe.moe_layer(x, w_r, get_deq, k)
+    assert np.array_equal(q["idx"], ref["idx"])
+    rel = np.max(np.abs(q["y"] - ref["y"]) / ref["den"])
+    cos = np.dot(q["y"].ravel(), ref["y"].ravel()) / (np.linalg.norm(q["y"]) * np.linalg.norm(ref["y"]))
+    assert rel < 0.25 and cos > 0.99
+    assert not np.allclose(q["y"], ref["y"])          # the quantization is really applied
+
+
+def test_moe_layer_mx_linear_in_down_scale():
+    # raising every down-matrix E8M0 scale by one doubles each d exactly (the
+    # quantized h does not depend on the down weights), so y doubles exactly
+    x, w_r, packed, get_packed, _, k = _layer_case(22)
+    q1 = mxq.moe_layer_mx(x, w_r, get_packed, k)
+    packed2 = [(gu, (dc, ds + 1)) for gu, (dc, ds) in packed]
+    q2 = mxq.moe_layer_mx(x, w_r, lambda e: packed2[e], k)
+    assert np.array_equal(q2["y"], 2 * q1["y"])
+
+
+def test_moe_layer_mx_single_expert():
+    # k = E = 1: every token's output is its own expert product, weight 1
+    from oracle import formats, moe as omoe
+    x, w_r, packed, get_packed, _, _ = _layer_case(23, E=1)
+    q = mxq.moe_layer_mx(x, w_r[:1], get_packed, 1)
+    (gc, gs), (dc, ds) = packed[0]
+    xq = mxq.mxfp8_dequant64(*mxq.mxfp8_quantize(x))
+    for t in range(x.shape[0]):
+        h = omoe.swiglu(formats.mxfp4_dequant64(gc, gs) @ xq[t], dc.shape[1] * 2)
+        hq = mxq.mxfp8_dequant64(*mxq.mxfp8_quantize(h[None, :]))[0]
+        assert np.allclose(q["y"][t], formats.mxfp4_dequant64(dc, ds) @ hq, rtol=1e-12, atol=1e-12)
