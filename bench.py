@@ -110,24 +110,29 @@ def cpu_baseline(cfg, sample_layers, m):
         w_r, b_r, _ = synth.router(cfg, l)
         experts = [synth.expert_weights(cfg, l, e) for e in range(cfg.n_experts)]
         gen.append((w_r, b_r, experts))
-    x = synth.hidden_batch(cfg, range(m))[0].astype(np.float64)
     log("cpu baseline: timing the oracle")
     uniq = []
+    passes = 0
     t0 = time.perf_counter()
-    for l in range(sample_layers):
-        w_r, b_r, experts = gen[l]
+    # whole passes over the sampled layers, each on fresh tokens, until at
+    # least 10 s of CPU work
+    while passes < 1 or time.perf_counter() - t0 < 10.0:
+        x = synth.hidden_batch(cfg, range(passes * m, (passes + 1) * m))[0].astype(np.float64)
+        for l in range(sample_layers):
+            w_r, b_r, experts = gen[l]
 
-        def get(e, experts=experts):
-            w = experts[e]
-            if cfg.fmt == "mxfp4":
-                return formats.mxfp4_dequant(*w["gu"]), formats.mxfp4_dequant(*w["dn"])
-            return (formats.int4g_dequant(*w["gu"], cfg.group),
-                    formats.int4g_dequant(*w["dn"], cfg.group))
-        res = omoe.moe_layer(x, w_r, get, cfg.top_k, bias=b_r, norm=cfg.norm, residual=cfg.norm)
-        uniq.append(len(np.unique(res["idx"])))
-        x = res["y"]
+            def get(e, experts=experts):
+                w = experts[e]
+                if cfg.fmt == "mxfp4":
+                    return formats.mxfp4_dequant(*w["gu"]), formats.mxfp4_dequant(*w["dn"])
+                return (formats.int4g_dequant(*w["gu"], cfg.group),
+                        formats.int4g_dequant(*w["dn"], cfg.group))
+            res = omoe.moe_layer(x, w_r, get, cfg.top_k, bias=b_r, norm=cfg.norm, residual=cfg.norm)
+            uniq.append(len(np.unique(res["idx"])))
+            x = res["y"]
+        passes += 1
     dt = time.perf_counter() - t0
-    per_step_s = dt / sample_layers * cfg.n_layers
+    per_step_s = dt / (passes * sample_layers) * cfg.n_layers
     blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     nbytes = step_bytes(cfg, [float(np.mean(uniq))] * cfg.n_layers)
     return {
@@ -136,9 +141,9 @@ def cpu_baseline(cfg, sample_layers, m):
         "cores": int(blas_threads),
         "kind": "oracle",
         "us_per_token": round(per_step_s / m * 1e6, 1),
-        "sample": f"{sample_layers} of {cfg.n_layers} layers of one step of M={m} tokens, "
-                  f"{dt:.1f} s of CPU time, scaled to a whole step; float64 NumPy, elementwise "
-                  f"dequant on one thread, BLAS matvecs on {blas_threads}",
+        "sample": f"{sample_layers} of {cfg.n_layers} layers of a step of M={m} tokens, {passes} pass{'es' if passes != 1 else ''} "
+                  f"on fresh tokens, {dt:.1f} s of CPU time, scaled to a whole step; float64 NumPy, "
+                  f"elementwise dequant on one thread, BLAS matvecs on {blas_threads}",
     }
 
 

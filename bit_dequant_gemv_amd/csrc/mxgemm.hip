@@ -108,7 +108,8 @@ mxfp8_quant_kernel(const void* __restrict__ x, int x_bf16, int64_t n_elems, uint
 
 constexpr int kGemmThreads = 256;   // 4 waves
 constexpr int kBN = 256;            // weight rows per block (128 per wave)
-constexpr int kBM = 128;            // tokens per block (64 per wave)
+constexpr int kNB = 1;              // 32-token MFMA tiles per wave
+constexpr int kBM = 64 * kNB;       // tokens per block
 constexpr int kBK = 128;            // K per stage: two 64-deep MFMA steps, four 32-blocks
 
 // LDS of one block: two stages of the A (weight) and B (activation) tiles,
@@ -119,7 +120,7 @@ constexpr int kBK = 128;            // K per stage: two 64-deep MFMA steps, four
 // also land in 16 different slots.
 struct MxLds {
   uint4 a[2][4][kBN];               // [stage][piece: 32-block of the stage][row]       32 KB
-  uint4 b[2][8][kBM];               // [stage][piece: 16 K of the stage][token]          32 KB
+  uint4 b[2][8][kBM];               // [stage][piece: 16 K of the stage][token]
   uint8_t sa[2][4][kBN];            // [stage][32-block][row] E8M0
   uint8_t sb[2][4][kBM];            // [stage][32-block][token] E8M0
 };
@@ -127,12 +128,16 @@ struct MxLds {
 // Per-thread source rows, fixed for the whole K loop: the stage loads add
 // only the K offset.  A: load i of a stage reads 16 bytes (one 32-block) of
 // code row a[i]; B: load i reads 16 fp8 codes of activation row b[i]; sa /
-// sb are the scale rows of A row `tid` and of activation row `tid % 128`.
+// sb are the scale rows of A row `tid` and of activation row `tid % kBM`
+// (byte offsets from the block-uniform bases).
+constexpr int kBL = kBM * 8 / kGemmThreads;   // B loads per thread per stage
 struct MxRows {
-  const uint8_t* a[4];
-  const uint8_t* b[4];
-  const uint8_t* sa;
-  const uint8_t* sb;
+  const uint8_t* abase;             // block-uniform bases
+  const uint8_t* sabase;
+  const uint8_t* bbase;
+  const uint8_t* sbbase;
+  uint32_t a[4], b[kBL];            // per-thread byte offsets of the rows
+  uint32_t sa, sb;
 };
 
 // One stage's global loads for this thread.  All addresses are clamped in
@@ -140,7 +145,7 @@ struct MxRows {
 // LDS (a select on a loaded value would make the wave wait for it at once);
 // `valid` marks which pieces lie inside K, the others are stored as zeros.
 struct MxStage {
-  uint4 a[4], b[4];
+  uint4 a[4], b[kBL];
   uint32_t sa[4], sb[4];            // scale bytes of the stage's 4 32-blocks
   uint32_t valid;                   // bit i: a[i] inside K; bit 4 + i: b[i] inside K
 };
@@ -154,11 +159,15 @@ __device__ __forceinline__ void mx_stage_load(MxStage& st, const MxRows& rows, i
     const int u = i * kGemmThreads + tid;
     const int kb = kb0 + (u & 3);                      // A: piece u % 4 of row u / 4
     const int kbc = kb < kblocks ? kb : kblocks - 1;
-    st.a[i] = ldg_u128(rows.a[i] + (int64_t)kbc * 16);
+    st.a[i] = ldg_u128(rows.abase + rows.a[i] + (uint32_t)kbc * 16u);
     valid |= (kb < kblocks ? 1u : 0u) << i;
+  }
+#pragma unroll
+  for (int i = 0; i < kBL; ++i) {
+    const int u = i * kGemmThreads + tid;
     const int kp = k0 + 16 * (u & 7);                  // B: piece u % 8 of token u / 8
     const int kpc = kp < K ? kp : K - 16;
-    st.b[i] = ldg_u128(rows.b[i] + kpc);
+    st.b[i] = ldg_u128(rows.bbase + rows.b[i] + (uint32_t)kpc);
     valid |= (kp < K ? 1u : 0u) << (4 + i);
   }
   st.valid = valid;
@@ -166,8 +175,8 @@ __device__ __forceinline__ void mx_stage_load(MxStage& st, const MxRows& rows, i
   for (int q = 0; q < 4; ++q) {
     const int kb = kb0 + q;
     const int kbc = kb < kblocks ? kb : kblocks - 1;
-    st.sa[q] = ldg_u8(rows.sa + kbc);
-    st.sb[q] = ldg_u8(rows.sb + kbc);
+    st.sa[q] = ldg_u8(rows.sabase + rows.sa + (uint32_t)kbc);
+    st.sb[q] = ldg_u8(rows.sbbase + rows.sb + (uint32_t)kbc);
   }
 }
 
@@ -177,9 +186,14 @@ __device__ __forceinline__ void mx_stage_store(MxLds& l, int buf, const MxStage&
     const int u = i * kGemmThreads + tid;
     // component-wise selects (a select of whole structs can become a select
     // of their addresses, which moves the stage to scratch memory)
-    const bool oka = (st.valid >> i) & 1u, okb = (st.valid >> (4 + i)) & 1u;
+    const bool oka = (st.valid >> i) & 1u;
     l.a[buf][u & 3][(u >> 2) ^ (4 * (u & 3))] = make_uint4(oka ? st.a[i].x : 0u, oka ? st.a[i].y : 0u,
                                                            oka ? st.a[i].z : 0u, oka ? st.a[i].w : 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < kBL; ++i) {
+    const int u = i * kGemmThreads + tid;
+    const bool okb = (st.valid >> (4 + i)) & 1u;
     l.b[buf][u & 7][(u >> 3) ^ (2 * (u & 7))] = make_uint4(okb ? st.b[i].x : 0u, okb ? st.b[i].y : 0u,
                                                            okb ? st.b[i].z : 0u, okb ? st.b[i].w : 0u);
   }
@@ -233,11 +247,12 @@ struct MxArgs {
   uint8_t* hs;                      // gate_up: h scales [grouped rows][I / 32]
 };
 
-// Block tile of the 256 x 128 (weight rows x tokens) product, 4 waves:
-// wave w takes 128 weight rows (four 32-row MFMA tiles) and 64 tokens (two
-// 32-token tiles): 8 MFMAs per 64-deep step, operands read from LDS.  Global
-// loads run two stages ahead of the MFMAs (two register sets), the LDS holds
-// two stages.
+// Block tile of the 256 x 64 (weight rows x tokens) product, 4 waves: wave
+// w takes 128 weight rows (four 32-row MFMA tiles) and 32 tokens (one
+// 32-token tile): 4 MFMAs per 64-deep step, operands read from LDS.  The
+// next stage's global loads are in flight while the MFMAs run; the LDS holds
+// two stages.  About 200 VGPRs and 51 KB of LDS let two blocks share a CU,
+// so one block's MFMAs cover the other's barrier and LDS phases.
 //   kMxDense : y[m][n] = sum_k W[n][k] xq[m][k].
 //   kMxGateUp: block (token tile of expert e, 128 intermediate rows): A rows
 //              0..127 are gate rows i, 128..255 the up rows I + i, and each
@@ -247,7 +262,7 @@ struct MxArgs {
 //              straight into the down product's operand.
 //   kMxDown  : d[r][n] = sum_i Wd_e[n][i] hq[r][i] for the expert's grouped rows r.
 template <int MODE>
-__global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
+__global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   __shared__ MxLds l;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -285,6 +300,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
   }
 
   MxRows rows;
+  rows.abase = wc;
+  rows.sabase = ws;
+  rows.bbase = p.xc;
+  rows.sbbase = p.xs;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = i * kGemmThreads + tid;
@@ -298,7 +317,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
       row = n0 + br;
       row = row < p.N ? row : p.N - 1;
     }
-    rows.a[i] = wc + row * (K >> 1);
+    rows.a[i] = (uint32_t)(row * (K >> 1));
+    if (i >= kBL) continue;
     const int slot = u >> 3;                                 // token slot of B load i
     int64_t src;
     if (MODE == kMxDense) {
@@ -309,7 +329,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
       gr = gr < r_end ? gr : r_end - 1;
       src = MODE == kMxGateUp ? p.row_src[gr] : gr;
     }
-    rows.b[i] = p.xc + src * K;
+    rows.b[i] = (uint32_t)(src * K);
   }
   {
     int64_t row;
@@ -321,7 +341,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
       row = n0 + tid;
       row = row < p.N ? row : p.N - 1;
     }
-    rows.sa = ws + row * kblocks;
+    rows.sa = (uint32_t)(row * kblocks);
     const int slot = tid & (kBM - 1);
     int64_t src;
     if (MODE == kMxDense) {
@@ -332,89 +352,74 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
       gr = gr < r_end ? gr : r_end - 1;
       src = MODE == kMxGateUp ? p.row_src[gr] : gr;
     }
-    rows.sb = p.xs + src * kblocks;
+    rows.sb = (uint32_t)(src * kblocks);
   }
 
   // the wave's A tiles: block rows arow(a) + j; gate_up pairs tile a (gate)
   // with tile a + 2 (up) over the same intermediate rows
-  const int wt = (wave >> 1) * 64;                 // the wave's first token slot
+  const int wt = (wave >> 1) * 32 * kNB;           // the wave's first token slot
   auto arow = [&](int a) {
     return MODE == kMxGateUp ? (a >> 1) * 128 + (wave & 1) * 64 + 32 * (a & 1) : (wave & 1) * 128 + 32 * a;
   };
-  v16f acc[4][2];
+  v16f acc[4][kNB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kNB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // both 64-deep steps' operands are read from LDS before the first MFMA
-  // issues, so the reads of the second step overlap the first step's MFMAs
   auto compute = [&](int buf) {
-    v8i A[2][4], B[2][2];
-    int sa[2][4], sb[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int pa = 2 * ks + h;                  // A piece (32-block of the stage)
+      v8i A[4], B[kNB];
+      int sa[4], sb[kNB];
+      const int pa = 2 * ks + h;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int r = arow(a) + j;
         const uint4 q = l.a[buf][pa][r ^ (4 * pa)];
-        A[ks][a][0] = (int)q.x;
-        A[ks][a][1] = (int)q.y;
-        A[ks][a][2] = (int)q.z;
-        A[ks][a][3] = (int)q.w;
-        A[ks][a][4] = A[ks][a][5] = A[ks][a][6] = A[ks][a][7] = 0;
-        sa[ks][a] = l.sa[buf][pa][r];
+        A[a][0] = (int)q.x;
+        A[a][1] = (int)q.y;
+        A[a][2] = (int)q.z;
+        A[a][3] = (int)q.w;
+        A[a][4] = A[a][5] = A[a][6] = A[a][7] = 0;
+        sa[a] = l.sa[buf][pa][r];
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < kNB; ++b) {
         const int t = wt + 32 * b + j;
         const int plo = 4 * ks + h, phi = 4 * ks + 2 + h;
         const uint4 lo = l.b[buf][plo][t ^ (2 * plo)];
         const uint4 hi = l.b[buf][phi][t ^ (2 * phi)];
-        B[ks][b][0] = (int)lo.x;
-        B[ks][b][1] = (int)lo.y;
-        B[ks][b][2] = (int)lo.z;
-        B[ks][b][3] = (int)lo.w;
-        B[ks][b][4] = (int)hi.x;
-        B[ks][b][5] = (int)hi.y;
-        B[ks][b][6] = (int)hi.z;
-        B[ks][b][7] = (int)hi.w;
-        sb[ks][b] = l.sb[buf][2 * ks + h][t];
+        B[b][0] = (int)lo.x;
+        B[b][1] = (int)lo.y;
+        B[b][2] = (int)lo.z;
+        B[b][3] = (int)lo.w;
+        B[b][4] = (int)hi.x;
+        B[b][5] = (int)hi.y;
+        B[b][6] = (int)hi.z;
+        B[b][7] = (int)hi.w;
+        sb[b] = l.sb[buf][2 * ks + h][t];
       }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ks][a], B[ks][b], acc[a][b], 4, 0, 0,
-                                                                       sa[ks][a], 0, sb[ks][b]);
+        for (int b = 0; b < kNB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a], B[b], acc[a][b], 4, 0, 0, sa[a], 0,
+                                                                       sb[b]);
+    }
   };
 
-  // stage s: operands in LDS buffer s & 1; the register set that held it
-  // takes the loads of stage s + 2 while the MFMAs run, the other set (stage
-  // s + 1) goes to the other buffer afterwards.  The stage count is padded to
-  // even: stages past K load clamped addresses and store zeros, so every
-  // load and store is unconditional.
   const int stages = (K + kBK - 1) / kBK;
-  const int padded = (stages + 1) & ~1;
-  MxStage s0, s1;
-  mx_stage_load(s0, rows, K, 0, tid);
-  mx_stage_load(s1, rows, K, kBK, tid);
-  mx_stage_store(l, 0, s0, tid);
+  MxStage st;
+  mx_stage_load(st, rows, K, 0, tid);
+  mx_stage_store(l, 0, st, tid);
   __syncthreads();
-  for (int s = 0; s < padded; s += 2) {
-    mx_stage_load(s0, rows, K, (s + 2) * kBK, tid);
-    compute(0);
-    mx_stage_store(l, 1, s1, tid);
-    __syncthreads();
-    mx_stage_load(s1, rows, K, (s + 3) * kBK, tid);
-    compute(1);
-    mx_stage_store(l, 0, s0, tid);
+  for (int s = 0; s < stages; ++s) {
+    mx_stage_load(st, rows, K, (s + 1) * kBK, tid);   // past K: clamped, stored as zeros, unused
+    compute(s & 1);
+    mx_stage_store(l, (s + 1) & 1, st, tid);
     __syncthreads();
   }
 
@@ -422,7 +427,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
     // h = silu(g) * u; then MXFP8 per (grouped row, 32 intermediate rows):
     // lane (j, h) holds 16 of a tile's 32 rows, lane (j, 1 - h) the rest
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kNB; ++b) {
       const int gr = r0 + wt + 32 * b + j;
       const bool row_ok = gr < r_end;
 #pragma unroll
@@ -462,7 +467,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) mx_gemm_kernel(MxArgs p) {
   }
 
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < kNB; ++b) {
     int64_t orow;                                   // output row: token, or grouped row
     if (MODE == kMxDense) {
       orow = m0 + wt + 32 * b + j;
