@@ -61,7 +61,8 @@ def step_bytes(cfg, unique_experts_per_layer):
 
 
 KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/gemv.hip",
-                  "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp", "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
+                  "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp", "bit_dequant_gemv_amd/csrc/bdg_device.hpp",
+                  "bit_dequant_gemv_amd/csrc/bdg_topk.hpp")
 
 
 def kernel_sources_sha():

@@ -34,6 +34,7 @@
 
 #include "bdg_gemv.hpp"
 #include "bdg_host.hpp"
+#include "bdg_topk.hpp"
 
 namespace bdg {
 
@@ -73,97 +74,6 @@ __device__ __forceinline__ int uniform_wave_id() {
 }
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
-
-// ---------------------------------------------------------------- top-k
-
-// Order-preserving unsigned key of a float: larger float <-> larger key.
-// -0.0 is folded onto +0.0 (they compare equal as floats) and NaN onto -inf.
-__device__ __forceinline__ uint32_t topk_key(float x) {
-  if (x != x) x = -INFINITY;
-  x = x + 0.0f;
-  const uint32_t b = __float_as_uint(x);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Maximum of a per-lane unsigned value over the wavefront (uniform result):
-// a prefix maximum by DPP row shifts 1, 2, 4, 8 (lane 15 of each row then
-// holds the row's maximum), the GFX9 row broadcasts carry it across rows to
-// lane 63, one readlane.  Lanes without a DPP source read 0, the neutral value.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0x111, 0xF>(v));   // row_shr:1
-  v = max(v, dpp_u32<0x112, 0xF>(v));   // row_shr:2
-  v = max(v, dpp_u32<0x114, 0xF>(v));   // row_shr:4
-  v = max(v, dpp_u32<0x118, 0xF>(v));   // row_shr:8
-  v = max(v, dpp_u32<0x142, 0xA>(v));   // row_bcast:15 into rows 1, 3
-  v = max(v, dpp_u32<0x143, 0xC>(v));   // row_bcast:31 into rows 2, 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
-}
-
-// One wavefront: the K largest of row[0..E) in descending order, ties to the
-// lower index, and softmax weights over them.  Each of the K rounds takes the
-// wave maximum of the untaken keys, then the lowest expert index holding it
-// (a ballot per value slot, lowest slot first), and retires that one entry.
-// NaN ranks as -inf.  Lane j < K receives pick j in (out_e, out_w); other
-// lanes get (0, 0).  V = values per lane (E <= 64V); expert e sits in lane
-// e % 64, slot e / 64.
-template <int V>
-__device__ __forceinline__ void topk_load(const float* row, int E, float (&v)[V]) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int e = lane + kWave * i;
-    v[i] = row[e < E ? e : E - 1];   // in bounds; lanes past E are masked in topk_rank
-  }
-}
-
-template <int V>
-__device__ __forceinline__ void topk_rank(float (&v)[V], int E, int K, int& out_e, float& out_w) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t key[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) key[i] = (lane + kWave * i < E) ? topk_key(v[i]) : 0u;   // 0 = retired / absent
-  int my_e = 0;
-  float my_l = 0.f;
-  float l0 = 0.f;
-  for (int j = 0; j < K; ++j) {
-    uint32_t m = key[0];
-#pragma unroll
-    for (int i = 1; i < V; ++i) m = max(m, key[i]);
-    const uint32_t best = wave_max_u32(m);
-    int pick = E - 1;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(key[i] == best);
-      if (!found && hit != 0) {
-        pick = kWave * i + (int)__builtin_ctzll(hit);
-        found = true;
-      }
-    }
-    // the winner's value: floats ordered like their keys, so read it back from the key
-    const uint32_t kb = (best & 0x80000000u) ? (best & 0x7FFFFFFFu) : ~best;
-    const float val = best == 0u ? -INFINITY : __uint_as_float(kb);
-    if (j == 0) l0 = val;
-    if (lane == j) {
-      my_e = pick;
-      my_l = val;
-    }
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (lane + kWave * i == pick) key[i] = 0u;
-  }
-  const float ex = lane < K ? expf(my_l - l0) : 0.f;
-  const float sum = wave_sum(ex);
-  out_e = lane < K ? my_e : 0;
-  out_w = lane < K ? ex / sum : 0.f;
-}
-
-template <int V>
-__device__ __forceinline__ void wave_topk(const float* row, int E, int K, int& out_e, float& out_w) {
-  float v[V];
-  topk_load<V>(row, E, v);
-  topk_rank<V>(v, E, K, out_e, out_w);
-}
 
 // ---------------------------------------------------------------- route
 
@@ -1799,80 +1709,4 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   st = launch_gateup(p, layer, m, 1, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
   if (st) return st;
   return launch_down(p, layer, m, 0, nullptr, y, nullptr, 0, s, nullptr);
-}
-
-// ---------------------------------------------------------------- standalone router
-
-namespace bdg {
-
-// One block per token: (optional RMSNorm of) x into LDS, all E router rows
-// one wave at a time, then top-k + softmax by wave 0.  The decode plan uses
-// the split route / gate_up kernels instead; this entry point serves callers
-// that need only the routing.
-__global__ void __launch_bounds__(kThreads)
-router_topk_kernel(const void* __restrict__ x, int x_bf16, const float* __restrict__ w_r,
-                   const float* __restrict__ b_r, int H, int E, int K, int norm, float eps,
-                   int32_t* __restrict__ idx, float* __restrict__ wts, float* __restrict__ logits) {
-  extern __shared__ float lds[];
-  float* xs = lds;             // [H]
-  float* lg = lds + H;         // [E]
-  float* red = lg + E;         // [kWaves]
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  float ss = 0.f;
-  for (int h = threadIdx.x; h < H; h += kThreads) {
-    const float v = x_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[(int64_t)t * H + h])
-                           : reinterpret_cast<const float*>(x)[(int64_t)t * H + h];
-    xs[h] = v;
-    ss = __builtin_fmaf(v, v, ss);
-  }
-  ss = wave_sum(ss);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  float r = 1.f;
-  if (norm) r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
-  for (int e = wave; e < E; e += kWaves) {
-    const float* wr = w_r + (int64_t)e * H;
-    float acc = 0.f;
-    for (int h = lane * 4; h < H; h += kWave * 4) {
-      const float4 wv = *reinterpret_cast<const float4*>(wr + h);
-      acc = __builtin_fmaf(wv.x, xs[h] * r, acc);
-      acc = __builtin_fmaf(wv.y, xs[h + 1] * r, acc);
-      acc = __builtin_fmaf(wv.z, xs[h + 2] * r, acc);
-      acc = __builtin_fmaf(wv.w, xs[h + 3] * r, acc);
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) lg[e] = acc + (b_r ? b_r[e] : 0.f);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int my_e;
-    float my_w;
-    wave_topk<BDG_MAX_EXPERTS / kWave>(lg, E, K, my_e, my_w);
-    if (lane < K) {
-      idx[t * K + lane] = my_e;
-      wts[t * K + lane] = my_w;
-    }
-  }
-  if (logits)
-    for (int e = threadIdx.x; e < E; e += kThreads) logits[(int64_t)t * E + e] = lg[e];
-}
-
-}  // namespace bdg
-
-extern "C" int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r, const float* b_r,
-                               int32_t m, int32_t h, int32_t e, int32_t topk, int32_t flags,
-                               float norm_eps, int32_t* idx, float* wts, float* logits, void* stream) {
-  if (!x || !w_r || !idx || !wts || m < 1 || h < 1 || e < 1 || topk < 1 || topk > e) return BDG_E_INVALID;
-  if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
-  if ((flags & ~BDG_ROUTER_RMSNORM) != 0 || (h % 4) != 0) return BDG_E_INVALID;
-  if ((flags & BDG_ROUTER_RMSNORM) && !(norm_eps >= 0.f)) return BDG_E_INVALID;
-  if ((reinterpret_cast<uintptr_t>(w_r) & 15u) != 0) return BDG_E_ALIGN;
-  if (e > BDG_MAX_EXPERTS || topk > BDG_MAX_TOPK || h > 16384) return BDG_E_UNSUPPORTED;
-  const size_t lds = (size_t)(h + e + kWaves) * sizeof(float);
-  hipLaunchKernelGGL(router_topk_kernel, dim3(m), dim3(kThreads), lds, as_stream(stream), x,
-                     x_dtype == BDG_BF16 ? 1 : 0, w_r, b_r, h, e, topk,
-                     (flags & BDG_ROUTER_RMSNORM) ? 1 : 0, norm_eps, idx, wts, logits);
-  return launch_status();
 }

@@ -235,7 +235,7 @@ struct MxArgs {
   int64_t N;                        // weight rows (dense, down); gate_up: 2 I
   int64_t M;                        // dense: tokens
   int K;
-  int gx, gy;                       // row tiles; dense: token tiles
+  int gx, gy;                       // row tiles; token tiles (grouped: an upper bound)
   // grouped modes: experts' rows in grouped order
   int E;
   int I;                            // gate_up: intermediate size
@@ -283,8 +283,10 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     n0 = (int64_t)tx * kBN;
     m0 = (int64_t)ty * kBM;
   } else {
-    const int T = (int)blockIdx.x / p.gx;
-    const int tx = (int)blockIdx.x - T * p.gx;
+    // gy = the launch's upper bound on token tiles; the XCD-grouped order
+    // keeps the token tiles of one expert and row tile on one XCD's L2
+    int tx, T;
+    if (!mx_tile_of_block(blockIdx.x, p.gx, p.gy, &tx, &T)) return;    // block-uniform
     if (T >= p.tile_off[p.E]) return;                                  // block-uniform
     int lo = 0, hi = p.E;                                              // tile_off[lo] <= T < tile_off[hi]
     while (hi - lo > 1) {
@@ -687,8 +689,10 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   a.gx = (int)((I + kBN / 2 - 1) / (kBN / 2));
   a.hc = hq;
   a.hs = hqs;
-  if (tiles * a.gx > 2147483647LL) return BDG_E_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_gemm_kernel<kMxGateUp>, dim3((unsigned)(tiles * a.gx)), dim3(kGemmThreads), 0, s, a);
+  a.gy = (int)tiles;
+  if (tiles * a.gx + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mx_gemm_kernel<kMxGateUp>, dim3((unsigned)((tiles * a.gx + 7) / 8 * 8)), dim3(kGemmThreads), 0,
+                     s, a);
   st = launch_status();
   if (st) return st;
   // down: 256 output rows per block over the grouped h rows
@@ -706,8 +710,10 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   b.K = (int)I;
   b.gx = (int)((H + kBN - 1) / kBN);
   b.y = d;
-  if (tiles * b.gx > 2147483647LL) return BDG_E_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_gemm_kernel<kMxDown>, dim3((unsigned)(tiles * b.gx)), dim3(kGemmThreads), 0, s, b);
+  b.gy = (int)tiles;
+  if (tiles * b.gx + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mx_gemm_kernel<kMxDown>, dim3((unsigned)((tiles * b.gx + 7) / 8 * 8)), dim3(kGemmThreads), 0,
+                     s, b);
   st = launch_status();
   if (st) return st;
   hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)m), dim3(256), 0, s,
