@@ -127,7 +127,8 @@ int qgemv(const bdg_qmat* w, const void* x, int32_t x_dtype, int32_t m, float* y
  * xin = x, or RMSNorm(x) = x / sqrt(mean(x^2) + eps) (unit gain) when flags
  * has BDG_ROUTER_RMSNORM.  The GPU top-k of the host-sync page, section 3.
  * x [m][h] of x_dtype, w_r [e][h] fp32, b_r [e] fp32 or NULL; idx [m][k]
- * int32, wts [m][k] fp32, logits [m][e] fp32 or NULL - all device. */
+ * int32, wts [m][k] fp32, logits [m][e] fp32 or NULL - all device; x and
+ * w_r 16-byte aligned, h % 4 == 0. */
 #define BDG_ROUTER_RMSNORM 1
 int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r, const float* b_r,
                     int32_t m, int32_t h, int32_t e, int32_t topk, int32_t flags,

@@ -245,6 +245,27 @@ def test_router_topk(dev, E, k, H, norm):
         assert ok, msg
 
 
+@pytest.mark.parametrize("m,norm", [(64, False), (203, True)])
+def test_router_topk_many_tokens(dev, m, norm):
+    """Many tokens in one call (m = 64, 203): logits, picks and weights must
+    equal those of one-token calls bit for bit (the same sums in the same
+    order), and the logits the oracle's within the router tolerance."""
+    E, k, H = 32, 4, 2880
+    cfg = synth.MoEConfig(name="r", base=760, fmt="mxfp4", n_layers=1, hidden=H, inter=64, n_experts=E, top_k=k)
+    w_r, _, _ = synth.router(cfg, 0)
+    x = np.stack([synth.hidden(cfg, t)[0] for t in range(m)])
+    banner(f"moe_router_topk many tokens m={m} norm={norm}")
+    xt, wt = dev_t(x, dev), dev_t(w_r, dev)
+    idx, wts, logits = (to_np(a) for a in bdg.moe_router_topk(xt, wt, None, k, rmsnorm=norm))
+    for t in (0, 1, 63, m - 1):
+        i1, w1, l1 = (to_np(a) for a in bdg.moe_router_topk(xt[t:t + 1].contiguous(), wt, None, k, rmsnorm=norm))
+        assert np.array_equal(f32_bits(l1[0]), f32_bits(logits[t]))
+        assert np.array_equal(i1[0], idx[t]) and np.array_equal(f32_bits(w1[0]), f32_bits(wts[t]))
+    xin = omoe.rmsnorm(x) if norm else x.astype(np.float64)
+    ref, scale = omoe.router_logits(w_r, xin)
+    assert np.all(np.abs(logits - ref) <= ROUTER_REL * scale + 1e-30)
+
+
 def test_router_ties_lower_index(dev):
     E, H = 16, 64
     w_r = np.zeros((E, H), dtype=np.float32)
