@@ -587,7 +587,9 @@ extern "C" int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t*
   if (w->fmt != BDG_FMT_MXFP4) return BDG_E_INVALID;
   if (!x_codes || !x_scales || !y || m < 1) return BDG_E_INVALID;
   if (!aligned16(x_codes)) return BDG_E_ALIGN;
-  if (w->k > (int64_t)1 << 20 || w->n * (w->k / 2) >= ((int64_t)1 << 40)) return BDG_E_UNSUPPORTED;
+  // operand rows are addressed by 32-bit byte offsets from the base pointers
+  if (w->k > (int64_t)1 << 20 || w->n * (w->k / 2) >= ((int64_t)1 << 32) || m * w->k >= ((int64_t)1 << 32))
+    return BDG_E_UNSUPPORTED;
   const int64_t gx = (w->n + kBN - 1) / kBN;
   const int64_t gy = (m + kBM - 1) / kBM;
   if (gx * gy + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
@@ -647,7 +649,10 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   const int64_t need = moe_prefill_mx_workspace(m, (int32_t)H, (int32_t)I, n_experts, top_k);
   if (workspace_bytes < need) return BDG_E_INVALID;
   const int64_t P = m * top_k;
-  if (P > (int64_t)1 << 30) return BDG_E_UNSUPPORTED;
+  // 32-bit row offsets inside one expert and into the activations / h
+  if (P > (int64_t)1 << 30 || m * H >= ((int64_t)1 << 32) || P * I >= ((int64_t)1 << 32) ||
+      2 * I * (H / 2) >= ((int64_t)1 << 32))
+    return BDG_E_UNSUPPORTED;
   char* wp = static_cast<char*>(workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(wp);             wp += a256(m * H);
   uint8_t* xqs = reinterpret_cast<uint8_t*>(wp);            wp += a256(m * (H / 32));

@@ -228,7 +228,8 @@ int mxfp8_quantize(const void* x, int32_t x_dtype, int64_t m, int64_t k, uint8_t
  * mxfp8_quantize; x_codes 16-byte aligned), on the MX-scaled MFMA with fp32
  * accumulation; y [m][n] fp32, device.  The instruction sums its products
  * at reduced internal precision, so results agree with the exact product to
- * about 1e-4 of sum |W||xq| (not bit for bit).  Any m >= 1, n >= 1. */
+ * about 1e-4 of sum |W||xq| (not bit for bit).  Any m >= 1, n >= 1 with
+ * n * k / 2 and m * k below 2^32 (BDG_E_UNSUPPORTED beyond). */
 int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, float* y,
             void* stream);
 
