@@ -18,10 +18,14 @@ Every function restates a plain definition in NumPy float64:
 * ``mxq``      - MXFP8 (E4M3 + E8M0 per 32) quantization of activations and
   the MX-scaled product of MXFP4 weights with MXFP8 activations (the
   large-M / prefill GEMM).
+* ``attn``     - decode attention of a gpt-oss layer: YaRN inverse
+  frequencies and attention scaling, the rotary table and the rotation that
+  feeds the KV cache, and causal attention with learned per-head sinks over a
+  full or sliding window.
 
 Where the pages leave a step open (they print no formula: the Methods
 sections of all three octopusresearch pages are empty) each module states the
 reading it takes.
 """
 
-from . import formats, gemv, moe, mxq  # noqa: F401
+from . import attn, formats, gemv, moe, mxq  # noqa: F401
