@@ -31,7 +31,7 @@ EXPORTED = (
     "mxfp4_dequant", "int4g_dequant", "qgemv", "moe_router_topk",
     "moe_plan_create", "moe_plan_destroy", "moe_expert_decode", "moe_experts_routed",
     "moe_expert_decode_profiled", "mxfp8_quantize", "mx_gemm", "moe_prefill_mx_workspace",
-    "moe_prefill_mx",
+    "moe_prefill_mx", "attn_rope_table", "attn_decode_workspace", "attn_decode",
     "bdg_stream_read", "bdg_stream_copy", "bdg_strerror", "bdg_version",
 )
 
@@ -68,6 +68,14 @@ class MoEDesc(ctypes.Structure):
     ]
 
 
+class Rope(ctypes.Structure):
+    _fields_ = [
+        ("theta", ctypes.c_double), ("factor", ctypes.c_double),
+        ("beta_fast", ctypes.c_double), ("beta_slow", ctypes.c_double),
+        ("orig_ctx", ctypes.c_int32), ("truncate", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -95,6 +103,10 @@ def load():
         "mx_gemm": [ctypes.POINTER(QMat), vp, vp, i64, vp, vp],
         "moe_prefill_mx_workspace": [i64, i32, i32, i32, i32],
         "moe_prefill_mx": [ctypes.POINTER(LayerDesc), i32, i32, vp, i32, i64, vp, vp, vp, vp, i64, vp],
+        "attn_rope_table": [ctypes.POINTER(Rope), i32, i64, vp, vp, vp, vp],
+        "attn_decode_workspace": [i32, i32, i32, i32, i64],
+        "attn_decode": [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp, i64, f32, vp, i32, vp, vp,
+                        i64, vp],
         "bdg_stream_read": [vp, i64, vp, i32, vp],
         "bdg_stream_copy": [vp, vp, i64, vp],
         "bdg_strerror": [i32],
@@ -104,7 +116,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = (ctypes.c_char_p if name in ("bdg_strerror", "bdg_version")
-                      else ctypes.c_int64 if name == "moe_prefill_mx_workspace" else ctypes.c_int)
+                      else ctypes.c_int64 if name in ("moe_prefill_mx_workspace", "attn_decode_workspace")
+                      else ctypes.c_int)
     _lib = lib
     return lib
 

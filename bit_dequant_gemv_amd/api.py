@@ -11,7 +11,7 @@ import torch
 
 from . import _lib
 from ._lib import (BDG_BF16, BDG_F32, BDG_FMT_INT4G, BDG_FMT_MXFP4, BDG_MOE_NO_GRAPH,
-                   BDG_MOE_STACK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, check)
+                   BDG_MOE_STACK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, Rope, check)
 
 
 def _stream():
@@ -195,6 +195,79 @@ def prefill_workspace_bytes(m, hidden, inter, n_experts, top_k):
     if n < 0:
         raise ValueError("invalid prefill shape")
     return int(n)
+
+
+def _rope(rope):
+    r = Rope()
+    r.theta, r.factor = float(rope["theta"]), float(rope["factor"])
+    r.beta_fast, r.beta_slow = float(rope["beta_fast"]), float(rope["beta_slow"])
+    r.orig_ctx, r.truncate = int(rope["orig_ctx"]), int(bool(rope.get("truncate", False)))
+    return r
+
+
+def attn_rope_table(rope, head_dim, n_pos, device=None, table=None):
+    """Rotary table [n_pos][head_dim] fp32 for YaRN parameters ``rope`` (a dict
+    with theta, factor, beta_fast, beta_slow, orig_ctx, truncate).  Returns
+    (table, inv_freq [head_dim/2], attn_scale [1]), all device tensors."""
+    device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if table is None:
+        table = torch.empty((n_pos, head_dim), dtype=torch.float32, device=device)
+    inv = torch.empty(head_dim // 2, dtype=torch.float32, device=device)
+    scale = torch.empty(1, dtype=torch.float32, device=device)
+    r = _rope(rope)
+    check("attn_rope_table", _lib.load().attn_rope_table(
+        ctypes.byref(r), head_dim, n_pos, _dev_ptr(table, "table", torch.float32),
+        _dev_ptr(inv, "inv_freq", torch.float32), _dev_ptr(scale, "attn_scale", torch.float32), _stream()))
+    return table, inv, scale
+
+
+def attn_decode_workspace_bytes(n_heads, n_kv_heads, head_dim, m, max_keys):
+    n = _lib.load().attn_decode_workspace(n_heads, n_kv_heads, head_dim, m, max_keys)
+    if n < 0:
+        raise ValueError("attention shape not supported")
+    return int(n)
+
+
+def attn_workspace(n_heads, n_kv_heads, head_dim, m, max_keys, device):
+    """A zero-filled workspace for attn_decode calls up to (m, max_keys), or None."""
+    n = attn_decode_workspace_bytes(n_heads, n_kv_heads, head_dim, m, max_keys)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, window=0, o=None,
+                workspace=None):
+    """One attention step of m new tokens (positions pos0 .. pos0 + m - 1).
+
+    q [m][Hq][64], k and v [m][Hkv][64] fp32; caches [Hkv][cap][64] bf16 or
+    fp32 (updated in place with the new rotated keys and values); table from
+    attn_rope_table; sinks [Hq] fp32 or None; window 0 = full attention.
+    Returns o [m][Hq][64] fp32.  A zero-filled workspace is allocated when
+    needed and not given (reuse one across calls with attn_workspace)."""
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (m, hkv, d) or v.shape != (m, hkv, d):
+        raise ValueError("k and v must be [m][n_kv_heads][head_dim]")
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape or k_cache.shape[0] != hkv:
+        raise ValueError("caches must match and be [n_kv_heads][cap][head_dim]")
+    cdt = {torch.bfloat16: BDG_BF16, torch.float32: BDG_F32}.get(k_cache.dtype)
+    if cdt is None:
+        raise ValueError("caches must be bfloat16 or float32")
+    cap = k_cache.shape[1]
+    last = pos0 + m
+    max_keys = min(window, last) if window > 0 else last
+    need = attn_decode_workspace_bytes(hq, hkv, d, m, max_keys)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((m, hq, d), dtype=torch.float32, device=q.device)
+    check("attn_decode", _lib.load().attn_decode(
+        _dev_ptr(q, "q", torch.float32), _dev_ptr(k, "k", torch.float32), _dev_ptr(v, "v", torch.float32),
+        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), cdt, cap, hq, hkv, d, m, pos0,
+        _dev_ptr(table, "table", torch.float32), table.shape[0], float(sm_scale),
+        _dev_ptr(sinks, "sinks", torch.float32), int(window), _dev_ptr(o, "o", torch.float32),
+        _dev_ptr(workspace, "workspace", torch.uint8), 0 if workspace is None else workspace.numel(),
+        _stream()))
+    return o
 
 
 def moe_router_topk(x, w_r, b_r=None, topk=4, rmsnorm=False, eps=1e-5):

@@ -261,6 +261,78 @@ int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, int32_t top_k
                    int64_t m, float* y, int32_t* topk_idx, float* topk_w, void* workspace,
                    int64_t workspace_bytes, void* stream);
 
+/* ---- decode attention (gpt-oss layer) ---- */
+
+/* Rotary embedding parameters, YaRN form (Peng, Quesnelle, Fan, Shippole
+ * 2023) - the gpt-oss page reproduces its inverse frequencies and
+ * attention scaling ("Sovereign gpt-oss-20B (MXFP4) on Apple Silicon",
+ * section 3).  gpt-oss: theta 150000, factor 32, beta_fast 32, beta_slow 1,
+ * orig_ctx 4096, truncate 0. */
+typedef struct bdg_rope {
+  double theta;       /* rotary base */
+  double factor;      /* YaRN scale s; <= 1 gives plain rotary frequencies */
+  double beta_fast;   /* rotation count over orig_ctx above which a frequency is kept */
+  double beta_slow;   /* rotation count below which a frequency is divided by s */
+  int32_t orig_ctx;   /* original context length L */
+  int32_t truncate;   /* 1: round the two ramp ends outward to whole indices */
+} bdg_rope;
+
+/* attn_rope_table - the rotary table for positions 0 .. n_pos-1, computed
+ * once per session: table [n_pos][head_dim] fp32 (device) holds
+ * cos(p f_i) a in column i and sin(p f_i) a in column head_dim/2 + i, where
+ * f_i is the YaRN inverse frequency of pair i and a the attention scaling
+ * 0.1 ln s + 1 (1 when s <= 1), both rounded to fp32 first; the angle p f_i
+ * is exact (float64) and each entry is rounded once to fp32.  Base
+ * frequencies are theta^(-2i/d); between the indices where a pair turns
+ * beta_fast and beta_slow times over orig_ctx the weight of the base
+ * frequency falls linearly in the index from 1 to 0, the rest going to
+ * f_i / s.  Optional outputs (device, nullable): inv_freq [head_dim/2] and
+ * attn_scale [1].  head_dim even; n_pos <= 2^31. */
+int attn_rope_table(const bdg_rope* rope, int32_t head_dim, int64_t n_pos, float* table, float* inv_freq,
+                    float* attn_scale, void* stream);
+
+/* attn_decode_workspace - bytes of device workspace attn_decode needs for
+ * calls of m tokens whose longest key range (window, or pos0 + m) is at most
+ * max_keys: 0 when one block covers it, -1 for shapes attn_decode does not
+ * take. */
+int64_t attn_decode_workspace(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t m,
+                              int64_t max_keys);
+
+/* attn_decode - one attention step of m new tokens at positions pos0 ..
+ * pos0 + m - 1 (a decode token, or a short causal chunk), the attention of a
+ * gpt-oss layer with learned per-head sinks ("Sovereign gpt-oss-20B (MXFP4)
+ * on Apple Silicon", sections 1 and 4) and a sliding window (section 3).
+ *   q [m][n_heads][64], k and v [m][n_kv_heads][64]: fp32 projections of
+ *     the new tokens, before the rotation (device).
+ *   k_cache, v_cache [n_kv_heads][cache_cap][64] of cache_dtype (BDG_BF16 or
+ *     BDG_F32, device): positions < pos0 hold earlier tokens; the call
+ *     stores the new tokens' rotated keys and values at pos0 .. pos0 + m - 1
+ *     (rotation in fp32 with each product and sum rounded on its own, then
+ *     round-to-nearest-even to the cache dtype).
+ *   rope_table [table_rows][64] from attn_rope_table (device).
+ *   Query head h uses KV head h / 8 (n_heads = 8 n_kv_heads) and its rotated
+ *     query; token t (position p = pos0 + t) attends keys j with
+ *     max(0, p - window + 1) <= j <= p (window 0: 0 <= j <= p):
+ *     o = sum_j e^(s_j) v_j / (sum_j e^(s_j) + e^(sinks[h])),
+ *     s_j = sm_scale (q . k_j); sinks [n_heads] fp32 (device) or NULL for none.
+ *   o [m][n_heads][64] fp32 (device).
+ *   workspace: attn_decode_workspace(...) bytes of device memory, 256-byte
+ *     aligned, zero-filled by the caller before its first use (each call
+ *     leaves it ready for the next, and one workspace serves every call of
+ *     the same n_kv_heads within the m and key count it was sized for); NULL
+ *     when that size is 0.  Calls that share a workspace must not overlap in
+ *     time.
+ * Scores, softmax and sums are fp32 (within a stated bound of the exact
+ * result, not bit for bit); the stored cache entries are exact.  All device
+ * pointers 16-byte aligned.  head_dim 64, 8 query heads per KV head and
+ * m <= 64 only (BDG_E_UNSUPPORTED otherwise); pos0 + m <= cache_cap and
+ * <= table_rows.
+ * Inputs must be finite. */
+int attn_decode(const float* q, const float* k, const float* v, void* k_cache, void* v_cache, int32_t cache_dtype,
+                int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t m, int64_t pos0,
+                const float* rope_table, int64_t table_rows, float sm_scale, const float* sinks, int32_t window,
+                float* o, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ---- measurement aids ---- */
 
 /* moe_expert_decode_profiled - one decode step exactly as moe_expert_decode

@@ -131,6 +131,81 @@ PREFILL = {
 }
 
 
+# Decode attention of gpt-oss-20B (the model the gpt-oss page ports; its
+# attention has learned per-head sinks, a 128-token sliding window and YaRN,
+# sections 1 and 3).  The head counts, head size, rotary parameters and the
+# alternation of sliding and full layers are the public gpt-oss-20B
+# configuration, which the pages do not print: 64 query heads sharing 8 KV
+# heads of 64 dimensions, YaRN base 150000 with factor 32 over an original
+# 4096-token context (beta_fast 32, beta_slow 1), scores scaled by 1/8, even
+# layers sliding.  The decode token sits at position ctx - 1 with ctx - 1
+# earlier keys in the cache.
+GPTOSS_ROPE = dict(theta=150000.0, factor=32.0, beta_fast=32.0, beta_slow=1.0, orig_ctx=4096, truncate=False)
+
+K_ATT_KC, K_ATT_VC, K_ATT_SINK, K_ATT_TOKEN = 10, 11, 12, 13
+ATT_TOKEN_KEY = 0x10000
+
+
+@dataclass(frozen=True)
+class AttnConfig:
+    name: str
+    base: int
+    n_layers: int
+    n_heads: int = 64
+    n_kv_heads: int = 8
+    head_dim: int = 64
+    ctx: int = 8192               # keys a full layer's decode token attends (its position + 1)
+    window: int = 128             # keys a sliding layer's token attends
+    cache_dtype: str = "bf16"
+    m: int = 1                    # tokens per step
+    sm_scale: float = 0.125
+    sink_sigma: float = 1.0
+    n_tokens: int = 64            # decode steps timed
+    rope: dict = field(default_factory=lambda: dict(GPTOSS_ROPE))
+
+    def sliding(self, layer):
+        return layer % 2 == 0
+
+
+ATTN = {
+    "gptoss20b_attn_8k": AttnConfig(name="gptoss20b_attn_8k", base=1001, n_layers=24, ctx=8192),
+}
+
+
+def attn_cache(cfg: AttnConfig, layer, n_pos, cap=None):
+    """Earlier keys and values of one layer: N(0, 1) at positions < n_pos of
+    caches [n_kv_heads][cap][head_dim] (cap defaults to n_pos), rounded to
+    bf16 for a bf16 cache.  Positions >= n_pos hold NaN (never attended).
+    Returns (k values fp32, v values fp32, k bits, v bits); bits are the
+    uint16 bf16 patterns for a bf16 cache and None for fp32."""
+    cap = n_pos if cap is None else cap
+    out = []
+    for kind in (K_ATT_KC, K_ATT_VC):
+        x = np.full((cfg.n_kv_heads, cap, cfg.head_dim), np.nan, dtype=np.float32)
+        x[:, :n_pos] = rng_for(cfg.base, layer, 0, kind).standard_normal(
+            (cfg.n_kv_heads, n_pos, cfg.head_dim), dtype=np.float32)
+        out.append(x)
+    if cfg.cache_dtype == "bf16":
+        kb, vb = bf16_bits_of(out[0]), bf16_bits_of(out[1])
+        return bf16_to_f32(kb), bf16_to_f32(vb), kb, vb
+    return out[0], out[1], None, None
+
+
+def attn_sinks(cfg: AttnConfig, layer):
+    return (rng_for(cfg.base, layer, 0, K_ATT_SINK).standard_normal(cfg.n_heads) * cfg.sink_sigma).astype(
+        np.float32)
+
+
+def attn_token(cfg: AttnConfig, layer, step, m=None):
+    """q [m][n_heads][d], k and v [m][n_kv_heads][d]: fp32 N(0, 1) projections."""
+    m = cfg.m if m is None else m
+    r = rng_for(cfg.base, layer, ATT_TOKEN_KEY + step, K_ATT_TOKEN)
+    q = r.standard_normal((m, cfg.n_heads, cfg.head_dim), dtype=np.float32)
+    k = r.standard_normal((m, cfg.n_kv_heads, cfg.head_dim), dtype=np.float32)
+    v = r.standard_normal((m, cfg.n_kv_heads, cfg.head_dim), dtype=np.float32)
+    return q, k, v
+
+
 def rng_for(base, layer, expert, kind):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([base, layer, expert, kind])))
 
@@ -221,9 +296,12 @@ def router(cfg: MoEConfig, layer):
 
 def bf16_bits_of(values_f32):
     """bf16 bit patterns (uint16) of fp32 values, round-to-nearest-even."""
-    u = np.asarray(values_f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = np.ascontiguousarray(values_f32, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)          # no overflow below the all-ones NaN patterns
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_to_f32(bits):

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: libbdg.so loads, exports every function that
+include/bdg.h declares, the binding covers each of them, and the pure host
+entry points (status text, version, workspace sizes, argument rejection before
+any launch) behave as the header states.  No call here reaches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_dequant_gemv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bdg.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:const\s+char\s*\*|int64_t|int)\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_parses():
+    names = _declared()
+    assert "attn_decode" in names and "qgemv" in names and len(names) >= 20
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), f"libbdg.so does not export {name}"
+
+
+def test_binding_covers_the_header():
+    assert sorted(_lib.EXPORTED) == _declared()
+    lib = _lib.load()
+    for name in _lib.EXPORTED:
+        assert getattr(lib, name).argtypes is not None or name == "bdg_version"
+
+
+def test_status_text_and_version():
+    lib = _lib.load()
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.bdg_strerror(st)
+    assert lib.bdg_version().decode()
+
+
+def test_attention_workspace_sizes():
+    lib = _lib.load()
+    # one block of 128 keys: no workspace
+    assert lib.attn_decode_workspace(64, 8, 64, 1, 128) == 0
+    n1 = lib.attn_decode_workspace(64, 8, 64, 1, 8192)
+    n2 = lib.attn_decode_workspace(64, 8, 64, 1, 16384)
+    assert 0 < n1 < n2
+    # counters [64 tokens][8 kv heads] + 64 splits x 8 kv heads x 8 heads x 66 floats
+    assert n1 == 64 * 8 * 4 + 64 * 8 * 8 * 66 * 4
+    assert lib.attn_decode_workspace(64, 8, 64, 65, 8192) == -1
+    # shapes the kernel does not take
+    assert lib.attn_decode_workspace(64, 8, 128, 1, 8192) == -1
+    assert lib.attn_decode_workspace(32, 8, 64, 1, 8192) == -1
+    assert lib.attn_decode_workspace(64, 8, 64, 0, 8192) == -1
+
+
+def test_attention_rejects_arguments_before_launch():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)        # never dereferenced: every call below fails its checks
+    args = dict(q=fake, k=fake, v=fake, kc=fake, vc=fake, dt=1, cap=256, hq=64, hkv=8, d=64, m=1, pos0=10,
+                tab=fake, rows=256, sm=0.125, sinks=None, window=0, o=fake, ws=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.attn_decode(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["dt"], a["cap"], a["hq"], a["hkv"],
+                               a["d"], a["m"], a["pos0"], a["tab"], a["rows"], a["sm"], a["sinks"], a["window"],
+                               a["o"], a["ws"], a["wsb"], a["s"])
+    assert call(q=None) == _lib.BDG_E_INVALID
+    assert call(dt=7) == _lib.BDG_E_INVALID
+    assert call(pos0=256) == _lib.BDG_E_INVALID           # past the cache
+    assert call(rows=5) == _lib.BDG_E_INVALID             # past the rotary table
+    assert call(sm=0.0) == _lib.BDG_E_INVALID
+    assert call(window=-1) == _lib.BDG_E_INVALID
+    assert call(d=128) == _lib.BDG_E_UNSUPPORTED
+    assert call(hq=16) == _lib.BDG_E_UNSUPPORTED
+    assert call(m=65, cap=1000, rows=1000) == _lib.BDG_E_UNSUPPORTED
+    assert call(q=ctypes.c_void_p(0x1004)) == _lib.BDG_E_ALIGN
+    # more than one block of keys needs the workspace
+    assert call(pos0=200, ws=None) == _lib.BDG_E_INVALID
+
+
+def test_rope_table_rejects_arguments_before_launch():
+    lib = _lib.load()
+    good = dict(theta=150000.0, factor=32.0, beta_fast=32.0, beta_slow=1.0, orig_ctx=4096, truncate=0)
+    fake = ctypes.c_void_p(0x1000)
+    for bad in (dict(theta=1.0), dict(factor=0.0), dict(orig_ctx=0), dict(truncate=2)):
+        r = _lib.Rope(**dict(good, **bad))
+        assert lib.attn_rope_table(ctypes.byref(r), 64, 16, fake, None, None, None) == _lib.BDG_E_INVALID
+    r = _lib.Rope(**good)
+    assert lib.attn_rope_table(ctypes.byref(r), 63, 16, fake, None, None, None) == _lib.BDG_E_INVALID
+    assert lib.attn_rope_table(ctypes.byref(r), 64, 0, fake, None, None, None) == _lib.BDG_E_INVALID
+
+
+def test_prefill_workspace_size_is_host_arithmetic():
+    lib = _lib.load()
+    assert lib.moe_prefill_mx_workspace(64, 2880, 2880, 32, 4) > 0
+    assert lib.moe_prefill_mx_workspace(0, 2880, 2880, 32, 4) == -1
+
+
+@pytest.mark.parametrize("name", ["mxfp4_dequant", "qgemv", "moe_router_topk", "mx_gemm"])
+def test_null_arguments_are_rejected(name):
+    lib = _lib.load()
+    fn = getattr(lib, name)
+    nargs = len(fn.argtypes)
+    zero = [None if t is ctypes.c_void_p or issubclass(t, ctypes._Pointer) else 0 for t in fn.argtypes]
+    assert fn(*zero[:nargs]) == _lib.BDG_E_INVALID
