@@ -19,6 +19,11 @@ on a bounded sample.  After the timed run the same steps run again twice,
 untimed for the headline: with an event pair around each step (the per-step
 median / mean / spread) and with a host sync after each step (sync mode, the
 wall time when the host picks every next token).
+
+Other workloads (``--workload``): the five expert-path configurations, dense
+packed GEMVs on non-expert shapes, the large-M (prefill) path on the
+MX-scaled matrix cores, and the decode attention of a gpt-oss-shape stack
+(``gptoss20b_attn_8k``: KV-cache bytes read per token over GPU time).
 """
 
 import argparse
@@ -65,20 +70,23 @@ KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csr
                   "bit_dequant_gemv_amd/csrc/bdg_topk.hpp")
 
 
-def kernel_sources_sha():
+def kernel_sources_sha(sources=KERNEL_SOURCES):
     """Hash of the kernel sources' code (comments and blank lines dropped), so a
     counter summary stays valid across comment-only edits and no longer."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         text = open(os.path.join(ROOT, f)).read()
         lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
         h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
+ATTN_SOURCES = ("bit_dequant_gemv_amd/csrc/attn.hip", "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
+
+
+def measured_traffic(workload, kernel, sources=KERNEL_SOURCES):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
     none or the kernel sources changed since it was taken."""
@@ -86,7 +94,7 @@ def measured_traffic(workload, kernel):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if kernel_sources_sha() != rec.get("kernel_sources_sha"):
+    if kernel_sources_sha(sources) != rec.get("kernel_sources_sha"):
         return None
     t = rec["per_launch"].get(kernel)
     return None if t is None else t["fetch_bytes"] + t["write_bytes"]
@@ -587,6 +595,150 @@ def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
         pl.close()
 
 
+def attn_layer_keys(cfg, layer):
+    return min(cfg.window, cfg.ctx) if cfg.sliding(layer) else cfg.ctx
+
+
+def attn_layer_bytes(cfg, layer):
+    """KV-cache bytes one decode token reads in a layer: n_kv_heads x keys x
+    head_dim x 2 (keys and values) x element size."""
+    es = 2 if cfg.cache_dtype == "bf16" else 4
+    return cfg.n_kv_heads * attn_layer_keys(cfg, layer) * cfg.head_dim * 2 * es
+
+
+def bench_attn(torch, bdg, synth, dev, cfg, args):
+    """Decode attention of a gpt-oss-shape stack: per layer one attn_decode
+    launch (rotation, cache append, sink + window attention, split merge) at a
+    context of cfg.ctx keys (even layers: the 128-key window).  One captured
+    graph per token replays all layers; the rate is KV-cache bytes read per
+    token over GPU time.  The roofline figure times the full-attention
+    launches alone in a graph (per launch = kernel + node gap)."""
+    import numpy as np
+
+    K = args.steps if args.steps is not None else 64
+    W = args.warmup if args.warmup is not None else 8
+    L, m = cfg.n_layers, cfg.m
+    pos0, cap = cfg.ctx - m, cfg.ctx
+    t0 = time.time()
+    caches, sinks = [], []
+    for l in range(L):
+        kv, vv, kb, vb = synth.attn_cache(cfg, l, pos0, cap)
+        if cfg.cache_dtype == "bf16":
+            kc = torch.from_numpy(kb.view(np.int16)).to(dev).view(torch.bfloat16)
+            vc = torch.from_numpy(vb.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            kc, vc = torch.from_numpy(kv).to(dev), torch.from_numpy(vv).to(dev)
+        caches.append((kc, vc))
+        sinks.append(torch.from_numpy(synth.attn_sinks(cfg, l)).to(dev))
+    table, _, _ = bdg.attn_rope_table(cfg.rope, cfg.head_dim, cap, device=dev)
+    ws = bdg.attn_workspace(cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, m, cfg.ctx, dev)
+    n_sets = 8                                   # distinct token inputs, used in turn
+    inputs = [[tuple(torch.from_numpy(a).to(dev) for a in synth.attn_token(cfg, l, s)) for l in range(L)]
+              for s in range(n_sets)]
+    outs = [torch.empty((m, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev) for _ in range(L)]
+    log(f"uploaded {L} layers of KV cache ({time.time() - t0:.1f} s)")
+
+    def layer_call(s, l):
+        q, k, v = inputs[s][l]
+        window = cfg.window if cfg.sliding(l) else 0
+        bdg.attn_decode(q, k, v, caches[l][0], caches[l][1], pos0, table, cfg.sm_scale, sinks[l], window,
+                        o=outs[l], workspace=ws)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                fn()
+        torch.cuda.current_stream().wait_stream(st)
+        return g
+
+    graphs = [capture(lambda s=s: [layer_call(s, l) for l in range(L)]) for s in range(n_sets)]
+    for i in range(W):
+        graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(K):
+        graphs[i % n_sets].replay()
+    b.record()
+    b.synchronize()
+    us_tok = a.elapsed_time(b) * 1e3 / K
+    nbytes = sum(attn_layer_bytes(cfg, l) for l in range(L))
+    value = nbytes / (us_tok * 1e-6) / 1e9
+    for o in outs:
+        if not torch.isfinite(o).all():
+            raise SystemExit("non-finite attention output")
+    log(f"{cfg.name}: {us_tok:.2f} us/token, {value:.1f} GB/s of KV cache")
+
+    # dominant kernel: the full-attention launches, alone in a graph
+    full = [l for l in range(L) if not cfg.sliding(l)]
+    reps = 4
+    gf = capture(lambda: [layer_call(0, l) for _ in range(reps) for l in full])
+    gf.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(4):
+        gf.replay()
+    b.record()
+    b.synchronize()
+    launch_us = a.elapsed_time(b) * 1e3 / (4 * reps * len(full))
+    fbytes = attn_layer_bytes(cfg, full[0])
+    achieved = fbytes / (launch_us * 1e-6) / 1e9
+    slide = [l for l in range(L) if cfg.sliding(l)]
+    gs = capture(lambda: [layer_call(0, l) for _ in range(reps) for l in slide])
+    gs.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(4):
+        gs.replay()
+    b.record()
+    b.synchronize()
+    slide_us = a.elapsed_time(b) * 1e3 / (4 * reps * max(1, len(slide)))
+    log(f"full-attention launch {launch_us:.2f} us ({achieved:.1f} GB/s), sliding launch {slide_us:.2f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on one full-attention layer of one token, repeated for >= 10 s
+        from oracle import attn as oattn
+        l = full[0]
+        kv, vv, _, _ = synth.attn_cache(cfg, l, pos0, cap)
+        kv64, vv64 = np.nan_to_num(kv.astype(np.float64)), np.nan_to_num(vv.astype(np.float64))
+        inv32, a32 = oattn.rope_constants(cfg.head_dim, **{k_: cfg.rope[k_] for k_ in (
+            "theta", "factor", "orig_ctx", "beta_fast", "beta_slow", "truncate")})
+        sk = synth.attn_sinks(cfg, l)
+        t1 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t1 < 10.0 or n < 2:
+            q, k, v = synth.attn_token(cfg, l, n)
+            oattn.decode_step(q, k, v, kv64, vv64, cfg.cache_dtype, pos0, inv32, a32, 0, cfg.sm_scale, sk)
+            n += 1
+        dt = (time.perf_counter() - t1) / n
+        cpu = {"value": round(fbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
+               "cores": int(os.cpu_count() or 1),
+               "us_per_token": round(dt * 1e6 * nbytes / fbytes, 1),
+               "sample": f"one full-attention layer (ctx {cfg.ctx}) of one token, {n} passes of the float64 "
+                         f"oracle step (rotation, cache store, 64 heads of attention), per-byte rate"}
+    out = base_record(cfg, value, K, W, us_tok * 1e-3, {
+        "workload": cfg.name, "layers": L, "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads,
+        "head_dim": cfg.head_dim, "ctx": cfg.ctx, "window": cfg.window, "m": m,
+        "cache_dtype": cfg.cache_dtype, "kv_bytes_per_token": nbytes,
+        "timing": "one graph per token (all layers), replayed back to back"})
+    out.update({"metric": "decode-attention KV-cache HBM GB/s + us/token, gpt-oss-20B shape",
+                "us_per_token": round(us_tok, 2),
+                "sliding_launch_us": round(slide_us, 3),
+                "cpu_baseline": cpu,
+                "roofline": {"kernel": "attn_decode_kernel (full attention)", "bound": "hbm",
+                             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                             "launch_us": round(launch_us, 3),
+                             "traffic": measured_traffic(cfg.name, "attn", ATTN_SOURCES),
+                             "traffic_algorithmic_bytes": fbytes}})
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -629,6 +781,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nb, "launches": 4}), flush=True)
         return
+    if args.workload in synth.ATTN:
+        return bench_attn(torch, bdg, synth, dev, synth.ATTN[args.workload], args)
     if args.workload in synth.PREFILL:
         return bench_prefill(torch, bdg, synth, sdev, dev, synth.PREFILL[args.workload], args)
     if args.workload in synth.DENSE and synth.DENSE[args.workload].m > 1:

@@ -229,9 +229,9 @@ def attn_decode_workspace_bytes(n_heads, n_kv_heads, head_dim, m, max_keys):
 
 
 def attn_workspace(n_heads, n_kv_heads, head_dim, m, max_keys, device):
-    """A zero-filled workspace for attn_decode calls up to (m, max_keys), or None."""
+    """A workspace for attn_decode calls of up to m tokens."""
     n = attn_decode_workspace_bytes(n_heads, n_kv_heads, head_dim, m, max_keys)
-    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, window=0, o=None,
@@ -241,8 +241,8 @@ def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, wi
     q [m][Hq][64], k and v [m][Hkv][64] fp32; caches [Hkv][cap][64] bf16 or
     fp32 (updated in place with the new rotated keys and values); table from
     attn_rope_table; sinks [Hq] fp32 or None; window 0 = full attention.
-    Returns o [m][Hq][64] fp32.  A zero-filled workspace is allocated when
-    needed and not given (reuse one across calls with attn_workspace)."""
+    Returns o [m][Hq][64] fp32.  A workspace is allocated when not given
+    (reuse one across calls with attn_workspace)."""
     m, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != (m, hkv, d) or v.shape != (m, hkv, d):
@@ -256,8 +256,8 @@ def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, wi
     last = pos0 + m
     max_keys = min(window, last) if window > 0 else last
     need = attn_decode_workspace_bytes(hq, hkv, d, m, max_keys)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if o is None:
         o = torch.empty((m, hq, d), dtype=torch.float32, device=q.device)
     check("attn_decode", _lib.load().attn_decode(
@@ -265,7 +265,7 @@ def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, wi
         _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), cdt, cap, hq, hkv, d, m, pos0,
         _dev_ptr(table, "table", torch.float32), table.shape[0], float(sm_scale),
         _dev_ptr(sinks, "sinks", torch.float32), int(window), _dev_ptr(o, "o", torch.float32),
-        _dev_ptr(workspace, "workspace", torch.uint8), 0 if workspace is None else workspace.numel(),
+        _dev_ptr(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream()))
     return o
 

@@ -1,22 +1,25 @@
 // Decode attention of a gpt-oss layer on gfx950: YaRN rotary embedding, the
 // KV-cache append, learned per-head attention sinks and full or
-// sliding-window causal attention with grouped KV heads, in one launch per
-// layer.  The gpt-oss page ("Sovereign gpt-oss-20B (MXFP4) on Apple
-// Silicon") names the sink kernel as one of its two new kernels (section 1),
-// the 128-token window and the YaRN frequencies and attention scaling
-// (section 3); the formulas are the published YaRN method and a softmax in
-// which each query head's sink is one more logit with a zero value.
+// sliding-window causal attention with grouped KV heads.  The gpt-oss page
+// ("Sovereign gpt-oss-20B (MXFP4) on Apple Silicon") names the sink kernel as
+// one of its two new kernels (section 1), the 128-token window and the YaRN
+// frequencies and attention scaling (section 3); the formulas are the
+// published YaRN method and a softmax in which each query head's sink is one
+// more logit with a zero value.
 //
-// Work split (flash-decoding): block (split, kv head, token) takes up to
-// kKeys keys of the token's window for the kGqa query heads that share the
-// KV head.  A lane owns 8 of the 64 dimensions of one key (8 lanes per key,
-// 8 keys per wave per pass): the key loads are 1 KB contiguous per wave, the
-// rotated queries of the 8 heads stay in 64 registers, and one transposing
-// butterfly over the 8 lanes leaves lane (key, h) with head h's score.
-// Values go to LDS as fp32; the weighted sum runs with lane (head, 8 dims).
-// Each block writes (max, sum, weighted values) per head; the last block of
-// a (token, kv head) to finish - found with one atomic counter - merges the
-// splits with the sink.  No block waits on another.
+// Two launches per layer, no block waiting on or signalling another.
+// attn_split_kernel (flash-decoding) covers the keys already in the cache:
+// block (split, kv head, token) takes a run of the token's window for the
+// kGqa query heads that share the KV head, rotating their queries itself;
+// each wave walks its keys in sub-chunks with its own running maximum.  A
+// lane owns 8 of the 64 dimensions of one key (8 lanes per key, 8 keys per
+// wave per pass): key and value loads are 1 KB contiguous per wave, the 8
+// rotated queries stay in 64 registers, one transposing butterfly over the
+// 8 lanes leaves lane (key, h) with head h's score, and the weighted values
+// accumulate in the same lanes; the block writes (max, sum, weighted values)
+// per head.  attn_merge_kernel, one block per (kv head, token), adds the
+// keys of the call itself (rotated from their projections), merges the
+// splits and the sink, and appends the token's key and value to the cache.
 #include <math.h>
 
 #include "bdg_device.hpp"
@@ -28,13 +31,11 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kGqa = 8;                        // query heads per KV head
 constexpr int kHd = 64;                        // head dimension
-constexpr int kKeys = 128;                     // keys per block
-constexpr int kKeysPerWave = kKeys / kAttnWaves;
-constexpr int kPasses = kKeysPerWave / 8;      // 8 keys per wave per pass
+constexpr int kMaxSplits = 64;                 // blocks per (token, kv head) at most
+constexpr int kTargetBlocks = 256;             // split-kernel blocks a call aims for
+constexpr int kFuseKeys = 256;                 // cached keys one fused block takes
 constexpr int kPartStride = kHd + 2;           // floats per head of a split: max, sum, o[64]
 constexpr float kLog2e = 1.4426950408889634f;
-
-static_assert(kKeys % (8 * kAttnWaves) == 0, "keys per block");
 
 // ---------------------------------------------------------------- rotary table
 
@@ -164,7 +165,7 @@ struct Cache<float> {           // fp32 cache: 8 values in two 16-byte loads
   }
 };
 
-// ---------------------------------------------------------------- attention
+// ---------------------------------------------------------------- attention over the cache
 
 struct AttnArgs {
   const float* q;        // [m][hq][64] projections of the new tokens
@@ -175,12 +176,17 @@ struct AttnArgs {
   const float* tab;      // rotary table [rows][64]
   const float* sinks;    // [hq] or null
   float* o;              // [m][hq][64]
-  float* part;           // split partials [m][hkv][n_split][kGqa][kPartStride]
-  int32_t* counters;     // [m][hkv], zero between calls
+  float* part;           // split partials [m][hkv][n_split][kGqa][kPartStride] (workspace)
   int64_t cap, pos0;
-  int hkv, window;
+  int hkv, window, n_split;
+  int keys_per_block;    // a multiple of the sub-chunk
   float qscale;          // score scale times log2(e)
 };
+
+// first key position of token t's window
+__device__ __forceinline__ int64_t window_lo(const AttnArgs& g, int64_t pt) {
+  return g.window > 0 ? (pt - g.window + 1 > 0 ? pt - g.window + 1 : 0) : 0;
+}
 
 // The block's 8 per-head scores of key group `a`: lane (a, db) holds the
 // partial dot products acc[h] over its 8 dimensions; three exchange steps
@@ -220,230 +226,402 @@ __device__ __forceinline__ float groups_sum(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// value of lane (lane & ~7) | H, i.e. lane H of this lane's group of 8
+template <int H>
+__device__ __forceinline__ float bcast8(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (H << 5) | 0x18));
+}
+
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// exp2(x - m) with an empty maximum (m = -inf) giving 0 rather than NaN
+__device__ __forceinline__ float exp2_rel(float x, float m) { return m == -INFINITY ? 0.f : exp2f(x - m); }
+
+// Sum over the 8 key groups of a wave of the 64 weighted-value accumulators
+// acc[h][i] of lane (a, db): three halving exchanges (lane ^ 32, ^ 16, ^ 8)
+// keep 4, 2, then 1 head per lane, so lane (a, db) ends with head a's sums
+// of dimensions 8 db .. 8 db + 7.  Fixed order: deterministic.
+__device__ __forceinline__ void group_transpose_sum(float (&acc)[kGqa][8], int a, float (&out)[8]) {
+  const bool b2 = (a & 4) != 0, b1 = (a & 2) != 0, b0 = (a & 1) != 0;
+  float s4[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float keep = b2 ? acc[4 + c][i] : acc[c][i];
+      const float send = b2 ? acc[c][i] : acc[4 + c][i];
+      s4[c][i] = keep + __shfl_xor(send, 32);
+    }
+  float s2[2][8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float keep = b1 ? s4[2 + c][i] : s4[c][i];
+      const float send = b1 ? s4[c][i] : s4[2 + c][i];
+      s2[c][i] = keep + swz_xor<16>(send);
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float keep = b0 ? s2[1][i] : s2[0][i];
+    const float send = b0 ? s2[0][i] : s2[1][i];
+    out[i] = keep + dpp_f32<0x128, 0xF>(send);
+  }
+}
+
 template <typename T>
-__global__ void __launch_bounds__(kAttnThreads)
-attn_decode_kernel(AttnArgs g) {
+struct AttnTile {
   using C = Cache<T>;
-  constexpr int kUnitsPerKey = kHd * (int)sizeof(T) / 16;     // 16-byte units of a value row
-  constexpr int kValsPerUnit = 16 / (int)sizeof(T);
-  constexpr int kVUnits = kKeys * kUnitsPerKey / kAttnThreads; // value units per thread
-  __shared__ float vs[kKeys][kHd];
-  __shared__ float ps[kKeys][kGqa];
-  __shared__ float ow[kAttnWaves][kGqa][kHd];
-  __shared__ float red_m[kAttnWaves][kGqa], red_l[kAttnWaves][kGqa];
-  __shared__ int last_flag;
+  static constexpr int kPasses = 4 / C::kU;                  // passes per sub-chunk
+  static constexpr int kPass = kAttnWaves * 8;               // keys per block per pass (8 per wave)
+  static constexpr int kSub = kPass * kPasses;               // keys per block per sub-chunk
+};
+
+// Keys of this block's sub-chunk starting at `sub`: pass p gives wave w the
+// 8 keys sub + (4p + w) 8 + 0..7; passes wholly past the block's keys are
+// skipped, and keys past its end repeat its last key (discarded later).
+template <typename T>
+__device__ __forceinline__ void load_sub(const T* kc, const T* vc, int64_t row0, int sub, int nk, int w, int a,
+                                         int db, uint4 (&kraw)[AttnTile<T>::kPasses][Cache<T>::kU],
+                                         uint4 (&vraw)[AttnTile<T>::kPasses][Cache<T>::kU]) {
+  constexpr int kPasses = AttnTile<T>::kPasses, kU = Cache<T>::kU, kPass = AttnTile<T>::kPass;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    if (sub + p * kPass >= nk) break;
+    const int jl = sub + (p * kAttnWaves + w) * 8 + a;
+    const int jc = jl < nk ? jl : nk - 1;
+    const int64_t off = (row0 + jc) * kHd + db * 8;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      kraw[p][i] = ldg_u128(kc + off + i * (8 / kU));
+      vraw[p][i] = ldg_u128(vc + off + i * (8 / kU));
+    }
+  }
+}
+
+// Thread (head oh, dimensions e = 2 od, 2 od + 1) of a block: what it needs
+// of the query and of the call's first key in the token's window, loaded up
+// front (own pair, rotation partner pair e ^ 32, table rows).
+struct NewKeyIn {
+  float2 qx, qy, c, s;          // query own / partner pair, table row of the token
+  float2 kx, ky, v, cj, sj;     // first key of the call in the window: own / partner, value, its table row
+};
+
+__device__ __forceinline__ float2 ld2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+
+__device__ __forceinline__ NewKeyIn load_new_in(const AttnArgs& g, int kvh, int t, int oh, int od) {
+  NewKeyIn in;
+  const int e = 2 * od, ti = e & 31;
+  const int64_t pt = g.pos0 + t;
+  const int64_t lo = window_lo(g, pt);
+  const int64_t j0 = lo > g.pos0 ? lo : g.pos0;
+  const float* qh = g.q + ((int64_t)t * g.hkv * kGqa + kvh * kGqa + oh) * kHd;
+  in.qx = ld2(qh + e);
+  in.qy = ld2(qh + (e ^ 32));
+  in.c = ld2(g.tab + pt * kHd + ti);
+  in.s = ld2(g.tab + pt * kHd + 32 + ti);
+  const int64_t k0 = ((j0 - g.pos0) * g.hkv + kvh) * kHd;
+  in.kx = ld2(g.k + k0 + e);
+  in.ky = ld2(g.k + k0 + (e ^ 32));
+  in.v = ld2(g.v + k0 + e);
+  in.cj = ld2(g.tab + j0 * kHd + ti);
+  in.sj = ld2(g.tab + j0 * kHd + 32 + ti);
+  return in;
+}
+
+// rotation of an own / partner pair (dimensions below 32 are the first half)
+__device__ __forceinline__ float2 rot_pair(float2 own, float2 par, float2 c, float2 s, bool first) {
+  return first ? make_float2(rot_first(own.x, par.x, c.x, s.x), rot_first(own.y, par.y, c.y, s.y))
+               : make_float2(rot_second(par.x, own.x, c.x, s.x), rot_second(par.y, own.y, c.y, s.y));
+}
+
+template <typename T>
+__device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, int oh, int od, const NewKeyIn& in,
+                                            const float* pb, int n_split, float bm, float bl, float o0, float o1);
+
+
+template <typename T, bool kFused>
+__global__ void __launch_bounds__(kAttnThreads)
+attn_split_kernel(AttnArgs g) {
+  using C = Cache<T>;
+  constexpr int kPasses = AttnTile<T>::kPasses;
+  constexpr int kSub = AttnTile<T>::kSub;
+  constexpr int kPass = AttnTile<T>::kPass;
+  __shared__ float wo[kAttnWaves][kGqa][kHd];
+  __shared__ float wm[kAttnWaves][kGqa], wl[kAttnWaves][kGqa];
+  __shared__ float qlds[kGqa][kHd];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int a = lane >> 3, db = lane & 7;
-  const int t = blockIdx.z, kvh = blockIdx.y, split = blockIdx.x, n_split = gridDim.x;
+  const int t = blockIdx.z, kvh = blockIdx.y, split = blockIdx.x;
   const int hq = g.hkv * kGqa;
   const int64_t pt = g.pos0 + t;
-  const int64_t lo = g.window > 0 ? (pt - g.window + 1 > 0 ? pt - g.window + 1 : 0) : 0;
-  const int64_t jb = lo + (int64_t)split * kKeys;
-  const int64_t je = jb + kKeys < pt + 1 ? jb + kKeys : pt + 1;
+  const int64_t jb = window_lo(g, pt) + (int64_t)split * g.keys_per_block;
+  const int64_t je = jb + g.keys_per_block < g.pos0 ? jb + g.keys_per_block : g.pos0;   // cached keys only
   const int nk = je > jb ? (int)(je - jb) : 0;
   const T* kc = reinterpret_cast<const T*>(g.kc);
   const T* vc = reinterpret_cast<const T*>(g.vc);
   const int64_t row0 = (int64_t)kvh * g.cap + jb;             // cache row of key jb
 
-  // this thread's share of the block result: head oh, dimensions 2 od, 2 od + 1
-  const int oh = tid >> 5, od = tid & 31;
-  float blk_m = -INFINITY, blk_l = 0.f, o0 = 0.f, o1 = 0.f;
+  uint4 kraw[kPasses][C::kU], vraw[kPasses][C::kU];
+  if (nk > 0) load_sub<T>(kc, vc, row0, 0, nk, w, a, db, kraw, vraw);
+  NewKeyIn nin;
+  if constexpr (kFused) nin = load_new_in(g, kvh, t, tid >> 5, tid & 31);
 
-  if (nk > 0) {
-    // value rows and this lane's key rows, all loads issued up front (rows
-    // past the block's keys repeat its last key and are discarded)
-    uint4 vraw[kVUnits];
-#pragma unroll
-    for (int r = 0; r < kVUnits; ++r) {
-      const int u = tid + r * kAttnThreads;
-      const int jl = u / kUnitsPerKey, part = u % kUnitsPerKey;
-      const int jc = jl < nk ? jl : nk - 1;
-      vraw[r] = ldg_u128(vc + (row0 + jc) * kHd + part * kValsPerUnit);
-    }
-    uint4 kraw[kPasses][C::kU];
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int jl = w * kKeysPerWave + p * 8 + a;
-      const int jc = jl < nk ? jl : nk - 1;
-#pragma unroll
-      for (int i = 0; i < C::kU; ++i) kraw[p][i] = ldg_u128(kc + (row0 + jc) * kHd + db * 8 + i * (8 / C::kU));
-    }
-
-    // the 8 query heads of this KV head, rotated, scaled by qscale
-    float qs[kGqa][8];
+  // the 8 query heads of this KV head, rotated and scaled by qscale: thread
+  // (head, pair i) rotates dimensions i and i + 32 into LDS, then lane (a, db)
+  // keeps dimensions 8 db .. of every head in registers
+  {
+    const int h = tid >> 5, i = tid & 31;
+    const float* qh = g.q + ((int64_t)t * hq + kvh * kGqa + h) * kHd;
     const float* tr = g.tab + pt * kHd;
+    const float x1 = qh[i], x2 = qh[i + 32], c = tr[i], sn = tr[32 + i];
+    qlds[h][i] = rot_first(x1, x2, c, sn) * g.qscale;
+    qlds[h][i + 32] = rot_second(x1, x2, c, sn) * g.qscale;
+  }
+  __syncthreads();
+  float qs[kGqa][8];
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) {
-      float r8[8];
-      rotate8(g.q + ((int64_t)t * hq + kvh * kGqa + h) * kHd, tr, db, r8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qs[h][i] = r8[i] * g.qscale;
-    }
+  for (int h = 0; h < kGqa; ++h) {
+    const float4 lo4 = *reinterpret_cast<const float4*>(&qlds[h][db * 8]);
+    const float4 hi4 = *reinterpret_cast<const float4*>(&qlds[h][db * 8 + 4]);
+    qs[h][0] = lo4.x; qs[h][1] = lo4.y; qs[h][2] = lo4.z; qs[h][3] = lo4.w;
+    qs[h][4] = hi4.x; qs[h][5] = hi4.y; qs[h][6] = hi4.z; qs[h][7] = hi4.w;
+  }
 
-    // scores
-    float sc[kPasses];
+  float m_run[kGqa];        // running maximum per head (wave-uniform)
+  float acc[kGqa][8];       // weighted values: head h, dimensions 8 db ..
+  float lsum = 0.f;         // this lane's share of head db's weight sum
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) {
+    m_run[h] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+  }
+
+  for (int sub = 0; sub < nk; sub += kSub) {
+    if (sub > 0) load_sub<T>(kc, vc, row0, sub, nk, w, a, db, kraw, vraw);
+    float s[kPasses];
+    float mx = -INFINITY;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-      const int jl = w * kKeysPerWave + p * 8 + a;
-      const int64_t j = jb + jl;
+      s[p] = -INFINITY;
+      if (sub + p * kPass >= nk) break;
+      const int jl = sub + (p * kAttnWaves + w) * 8 + a;
       float kf[8];
       C::unpack(kraw[p], kf);
-      if (jl < nk && j >= g.pos0) {        // a key of this call: rotate its projection
-        float r8[8];
-        rotate8(g.k + ((j - g.pos0) * g.hkv + kvh) * kHd, g.tab + j * kHd, db, r8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kf[i] = C::round(r8[i]);
-      }
-      float acc[kGqa];
+      float d[kGqa];
 #pragma unroll
       for (int h = 0; h < kGqa; ++h) {
-        float s = 0.f;
+        float x = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s += qs[h][i] * kf[i];
-        acc[h] = s;
+        for (int i = 0; i < 8; ++i) x += qs[h][i] * kf[i];
+        d[h] = x;
       }
-      const float s = head_transpose_sum(acc, db);
-      sc[p] = jl < nk ? s : -INFINITY;
+      const float sc = head_transpose_sum(d, db);
+      s[p] = jl < nk ? sc : -INFINITY;
+      mx = fmaxf(mx, s[p]);
     }
-
-    // per-head maximum over the block
-    float mx = sc[0];
-#pragma unroll
-    for (int p = 1; p < kPasses; ++p) mx = fmaxf(mx, sc[p]);
+    // new running maximum of head db, then every head's value to every lane
     mx = groups_max(mx);
-    if (a == 0) red_m[w][db] = mx;
-    __syncthreads();
-    const float mh = fmaxf(fmaxf(red_m[0][db], red_m[1][db]), fmaxf(red_m[2][db], red_m[3][db]));
-    float ls = 0.f;
+    float m_new[kGqa], fac[kGqa];
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      m_new[h] = fmaxf(m_run[h], lane_value(mx, h));
+      fac[h] = exp2_rel(m_run[h], m_new[h]);
+      m_run[h] = m_new[h];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] *= fac[h];
+    }
+    float m_mine = m_new[0], f_mine = fac[0];
+#pragma unroll
+    for (int h = 1; h < kGqa; ++h) {
+      m_mine = db == h ? m_new[h] : m_mine;
+      f_mine = db == h ? fac[h] : f_mine;
+    }
+    lsum *= f_mine;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
-      const float e = exp2f(sc[p] - mh);
-      ps[w * kKeysPerWave + p * 8 + a][db] = e;
-      ls += e;
+      if (sub + p * kPass >= nk) break;
+      const float e = exp2_rel(s[p], m_mine);              // weight of (head db, key a)
+      lsum += e;
+      float vf[8];
+      C::unpack(vraw[p], vf);
+      const float e8[kGqa] = {bcast8<0>(e), bcast8<1>(e), bcast8<2>(e), bcast8<3>(e),
+                              bcast8<4>(e), bcast8<5>(e), bcast8<6>(e), bcast8<7>(e)};
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] += e8[h] * vf[i];
     }
-    ls = groups_sum(ls);
-    if (a == 0) red_l[w][db] = ls;
+  }
 
-    // values to LDS as fp32 (keys of this call from their projections)
+  // wave results: weight sums per head, weighted values of head a
+  lsum = groups_sum(lsum);
+  float o8[8];
+  group_transpose_sum(acc, a, o8);
+  if (a == 0) {
+    float mm = m_run[0];
 #pragma unroll
-    for (int r = 0; r < kVUnits; ++r) {
-      const int u = tid + r * kAttnThreads;
-      const int jl = u / kUnitsPerKey, part = u % kUnitsPerKey;
-      const int64_t j = jb + jl;
-      float vals[kValsPerUnit];
-      if constexpr (kValsPerUnit == 8) {
-        float v8[8];
-        C::unpack(&vraw[r], v8);
+    for (int h = 1; h < kGqa; ++h) mm = db == h ? m_run[h] : mm;
+    wm[w][db] = mm;
+    wl[w][db] = lsum;
+  }
+  *reinterpret_cast<float4*>(&wo[w][a][db * 8]) = make_float4(o8[0], o8[1], o8[2], o8[3]);
+  *reinterpret_cast<float4*>(&wo[w][a][db * 8 + 4]) = make_float4(o8[4], o8[5], o8[6], o8[7]);
+  __syncthreads();
+
+  // block partial: thread (head oh, dimensions 2 od, 2 od + 1)
+  const int oh = tid >> 5, od = tid & 31;
+  const float bm = fmaxf(fmaxf(wm[0][oh], wm[1][oh]), fmaxf(wm[2][oh], wm[3][oh]));
+  float bl = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vals[i] = v8[i];
+  for (int ww = 0; ww < kAttnWaves; ++ww) {
+    const float f = exp2_rel(wm[ww][oh], bm);
+    bl += f * wl[ww][oh];
+    o0 += f * wo[ww][oh][2 * od];
+    o1 += f * wo[ww][oh][2 * od + 1];
+  }
+  if constexpr (kFused) {                    // one block holds every cached key: merge here
+    merge_heads<T>(g, kvh, t, oh, od, nin, nullptr, 0, bm, bl, o0, o1);
+  } else {
+    float* pp = g.part + ((((int64_t)t * g.hkv + kvh) * g.n_split + split) * kGqa + oh) * kPartStride;
+    if (od == 0) *reinterpret_cast<float2*>(pp) = make_float2(bm, bl);
+    *reinterpret_cast<float2*>(pp + 2 + 2 * od) = make_float2(o0, o1);
+  }
+}
+
+// ---------------------------------------------------------------- merge, new keys, append
+
+// The softmax of one (token, query head) over the cached-key splits, the
+// keys of this call and the sink, by thread (oh, od) for dimensions 2 od and
+// 2 od + 1.  Splits come from `pb` ([n_split][kGqa][kPartStride], global) or,
+// with pb null, as the single partial (bm, bl, o0, o1) in registers.  The
+// call's keys are rotated from their projections in the cache's rounding and
+// scored with a sum over the head's 32 threads; threads of head 0 append the
+// token's own key and value to the cache.
+template <typename T>
+__device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, int oh, int od, const NewKeyIn& in,
+                                            const float* pb, int n_split, float bm, float bl, float o0, float o1) {
+  using C = Cache<T>;
+  const int e = 2 * od, ti = e & 31;
+  const bool first = e < 32;
+  const int hq = g.hkv * kGqa;
+  const int64_t pt = g.pos0 + t;
+  const int64_t lo = window_lo(g, pt);
+  const int64_t j0 = lo > g.pos0 ? lo : g.pos0;
+
+  // running softmax state: max, weight sum, weighted values
+  float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+  if (pb == nullptr) {
+    M = bm; L = bl; A0 = o0; A1 = o1;
+  } else {
+    constexpr int kChunk = 16;
+    for (int c0 = 0; c0 < n_split; c0 += kChunk) {
+      // splits past the end read the chunk's first split and weigh nothing
+      float2 ml[kChunk], ov[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int sp = c0 + u < n_split ? c0 + u : c0;
+        const float* ph = pb + ((int64_t)sp * kGqa + oh) * kPartStride;
+        ml[u] = ld2(ph);
+        ov[u] = ld2(ph + 2 + e);
+      }
+      float cm = M;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) cm = fmaxf(cm, ml[u].x);
+      const float f = exp2_rel(M, cm);
+      L *= f; A0 *= f; A1 *= f;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const float wgt = c0 + u < n_split ? exp2_rel(ml[u].x, cm) : 0.f;
+        L += wgt * ml[u].y;
+        A0 += wgt * ov[u].x;
+        A1 += wgt * ov[u].y;
+      }
+      M = cm;
+    }
+  }
+
+  // the call's keys in the window
+  const float2 qr = rot_pair(in.qx, in.qy, in.c, in.s, first);
+  const float q0 = qr.x * g.qscale, q1 = qr.y * g.qscale;
+  for (int64_t j = j0; j <= pt; ++j) {
+    float2 kx = in.kx, ky = in.ky, vv = in.v, cj = in.cj, sj = in.sj;
+    if (j > j0) {
+      const int64_t ki = ((j - g.pos0) * g.hkv + kvh) * kHd;
+      kx = ld2(g.k + ki + e);
+      ky = ld2(g.k + ki + (e ^ 32));
+      vv = ld2(g.v + ki + e);
+      cj = ld2(g.tab + j * kHd + ti);
+      sj = ld2(g.tab + j * kHd + 32 + ti);
+    }
+    const float2 kr = rot_pair(kx, ky, cj, sj, first);
+    const float k0 = C::round(kr.x), k1 = C::round(kr.y);
+    const float v0 = C::round(vv.x), v1 = C::round(vv.y);
+    if (j == pt && oh == 0) {                // the token's own key and value into the cache
+      const int64_t ci = ((int64_t)kvh * g.cap + pt) * kHd + e;
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t kb = (uint32_t)f32_to_bf16_rne(k0) | ((uint32_t)f32_to_bf16_rne(k1) << 16);
+        const uint32_t vb = (uint32_t)f32_to_bf16_rne(v0) | ((uint32_t)f32_to_bf16_rne(v1) << 16);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(g.kc) + ci) = kb;
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(g.vc) + ci) = vb;
       } else {
-        vals[0] = __uint_as_float(vraw[r].x);
-        vals[1] = __uint_as_float(vraw[r].y);
-        vals[2] = __uint_as_float(vraw[r].z);
-        vals[3] = __uint_as_float(vraw[r].w);
+        *reinterpret_cast<float2*>(reinterpret_cast<float*>(g.kc) + ci) = make_float2(k0, k1);
+        *reinterpret_cast<float2*>(reinterpret_cast<float*>(g.vc) + ci) = make_float2(v0, v1);
       }
-      if (jl < nk && j >= g.pos0) {
-        const float* src = g.v + ((j - g.pos0) * g.hkv + kvh) * kHd + part * kValsPerUnit;
-#pragma unroll
-        for (int i = 0; i < kValsPerUnit; ++i) vals[i] = C::round(src[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < kValsPerUnit; ++i) vs[jl][part * kValsPerUnit + i] = jl < nk ? vals[i] : 0.f;
     }
-
-    // the block that holds the token's own position appends its key and value
-    if (pt < je && w == 0 && a == 0) {
-      float r8[8], v8[8];
-      rotate8(g.k + ((int64_t)t * g.hkv + kvh) * kHd, tr, db, r8);
-      ld8(g.v + ((int64_t)t * g.hkv + kvh) * kHd + db * 8, v8);
-      C::store8(reinterpret_cast<T*>(g.kc) + ((int64_t)kvh * g.cap + pt) * kHd + db * 8, r8);
-      C::store8(reinterpret_cast<T*>(g.vc) + ((int64_t)kvh * g.cap + pt) * kHd + db * 8, v8);
-    }
-    __syncthreads();
-
-    // weighted values: lane (head a, dimensions 8 db ..), this wave's keys
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int kk = 0; kk < kKeysPerWave; ++kk) {
-      const int jl = w * kKeysPerWave + kk;
-      const float pw = ps[jl][a];
-      const float4 va = *reinterpret_cast<const float4*>(&vs[jl][db * 8]);
-      const float4 vb = *reinterpret_cast<const float4*>(&vs[jl][db * 8 + 4]);
-      acc[0] += pw * va.x; acc[1] += pw * va.y; acc[2] += pw * va.z; acc[3] += pw * va.w;
-      acc[4] += pw * vb.x; acc[5] += pw * vb.y; acc[6] += pw * vb.z; acc[7] += pw * vb.w;
-    }
-    *reinterpret_cast<float4*>(&ow[w][a][db * 8]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4*>(&ow[w][a][db * 8 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    __syncthreads();
-    blk_m = fmaxf(fmaxf(red_m[0][oh], red_m[1][oh]), fmaxf(red_m[2][oh], red_m[3][oh]));
-    blk_l = (red_l[0][oh] + red_l[1][oh]) + (red_l[2][oh] + red_l[3][oh]);
-    o0 = (ow[0][oh][2 * od] + ow[1][oh][2 * od]) + (ow[2][oh][2 * od] + ow[3][oh][2 * od]);
-    o1 = (ow[0][oh][2 * od + 1] + ow[1][oh][2 * od + 1]) + (ow[2][oh][2 * od + 1] + ow[3][oh][2 * od + 1]);
+    const float sc = group_sum<32>(q0 * k0 + q1 * k1);
+    const float m2 = fmaxf(M, sc);
+    const float f = exp2_rel(M, m2), ew = exp2f(sc - m2);
+    L = L * f + ew;
+    A0 = A0 * f + ew * v0;
+    A1 = A1 * f + ew * v1;
+    M = m2;
   }
 
+  // the sink: one more logit with a zero value
   const int qh = kvh * kGqa + oh;
-  const float sink = g.sinks ? g.sinks[qh] * kLog2e : -INFINITY;
-  float* out = g.o + ((int64_t)t * hq + qh) * kHd + 2 * od;
-  if (n_split == 1) {
-    const float mx = fmaxf(blk_m, sink);
-    const float f = exp2f(blk_m - mx);
-    const float den = blk_l * f + exp2f(sink - mx);
-    out[0] = o0 * f / den;
-    out[1] = o1 * f / den;
-    return;
+  if (g.sinks) {
+    const float sk = g.sinks[qh] * kLog2e;
+    const float m2 = fmaxf(M, sk);
+    const float f = exp2_rel(M, m2);
+    L = L * f + exp2f(sk - m2);
+    A0 *= f;
+    A1 *= f;
   }
+  const float inv = 1.f / L;
+  *reinterpret_cast<float2*>(g.o + ((int64_t)t * hq + qh) * kHd + e) = make_float2(A0 * inv, A1 * inv);
+}
 
-  // split partial, then the last block of this (token, kv head) merges
-  const int64_t grp = (int64_t)t * g.hkv + kvh;
-  float* pp = g.part + ((grp * n_split + split) * kGqa + oh) * kPartStride;
-  if (od == 0) {
-    pp[0] = blk_m;
-    pp[1] = blk_l;
-  }
-  pp[2 + 2 * od] = o0;
-  pp[3 + 2 * od] = o1;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_flag = atomicAdd(&g.counters[grp], 1) == n_split - 1;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const float* pb = g.part + (grp * n_split * kGqa + oh) * kPartStride;
-  constexpr int64_t kSplitStride = (int64_t)kGqa * kPartStride;
-  float mx = sink;
-  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, pb[s * kSplitStride]);
-  float den = exp2f(sink - mx), n0 = 0.f, n1 = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float* ps_ = pb + s * kSplitStride;
-    const float f = exp2f(ps_[0] - mx);
-    den += f * ps_[1];
-    n0 += f * ps_[2 + 2 * od];
-    n1 += f * ps_[3 + 2 * od];
-  }
-  out[0] = n0 / den;
-  out[1] = n1 / den;
-  if (tid == 0) g.counters[grp] = 0;
+template <typename T>
+__global__ void __launch_bounds__(kAttnThreads)
+attn_merge_kernel(AttnArgs g) {
+  const int kvh = blockIdx.x, t = blockIdx.y;
+  const int oh = threadIdx.x >> 5, od = threadIdx.x & 31;
+  const NewKeyIn in = load_new_in(g, kvh, t, oh, od);
+  merge_heads<T>(g, kvh, t, oh, od, in, g.part + ((int64_t)t * g.hkv + kvh) * g.n_split * kGqa * kPartStride,
+                 g.n_split, 0.f, 0.f, 0.f, 0.f);
 }
 
 // ---------------------------------------------------------------- host side
 
-inline int64_t attn_splits(int64_t max_keys) { return (max_keys + kKeys - 1) / kKeys; }
-
-inline int64_t round256(int64_t b) { return (b + 255) & ~(int64_t)255; }
-
-// Workspace: counters [kAttnMaxM][hkv] int32 at a fixed place (so one
-// workspace serves calls of any m and key count up to its size, every call
-// leaving the counters it used at zero), then the split partials.
-constexpr int kAttnMaxM = 64;
-
-inline int64_t attn_counter_bytes(int hkv) { return round256((int64_t)kAttnMaxM * hkv * 4); }
+// Keys per block: whole passes of 32 keys.  Up to kFuseKeys cached keys go
+// to one block (the fused single launch); longer ranges are split to fill
+// the chip (about kTargetBlocks blocks over all tokens and KV heads), at most
+// kMaxSplits per token and KV head.
+inline int64_t attn_keys_per_block(int64_t keys, int hkv, int m) {
+  if (keys <= kFuseKeys) return (keys + kAttnWaves * 8 - 1) / (kAttnWaves * 8) * (kAttnWaves * 8);
+  int64_t splits = kTargetBlocks / ((int64_t)hkv * m);
+  splits = splits < 1 ? 1 : splits > kMaxSplits ? kMaxSplits : splits;
+  const int64_t per = (keys + splits - 1) / splits;
+  return (per + kAttnWaves * 8 - 1) / (kAttnWaves * 8) * (kAttnWaves * 8);
+}
 
 inline int64_t attn_ws_bytes(int hkv, int m, int64_t max_keys) {
-  const int64_t n_split = attn_splits(max_keys);
-  if (n_split <= 1) return 0;
-  return attn_counter_bytes(hkv) + (int64_t)m * hkv * n_split * kGqa * kPartStride * 4;
+  return (int64_t)m * hkv * kMaxSplits * kGqa * kPartStride * 4;
 }
 
 }  // namespace bdg
@@ -464,6 +642,8 @@ extern "C" int attn_rope_table(const bdg_rope* rope, int32_t head_dim, int64_t n
   return launch_status();
 }
 
+constexpr int kAttnMaxM = 64;
+
 extern "C" int64_t attn_decode_workspace(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t m,
                                          int64_t max_keys) {
   if (n_kv_heads < 1 || n_kv_heads > 65535 || n_heads != n_kv_heads * kGqa || head_dim != kHd || m < 1 ||
@@ -477,34 +657,47 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
                            int32_t head_dim, int32_t m, int64_t pos0, const float* rope_table, int64_t table_rows,
                            float sm_scale, const float* sinks, int32_t window, float* o, void* workspace,
                            int64_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !k_cache || !v_cache || !rope_table || !o) return BDG_E_INVALID;
+  if (!q || !k || !v || !k_cache || !v_cache || !rope_table || !o || !workspace) return BDG_E_INVALID;
   if (cache_dtype != BDG_F32 && cache_dtype != BDG_BF16) return BDG_E_INVALID;
   if (m < 1 || n_kv_heads < 1 || n_heads < 1 || pos0 < 0 || window < 0 || !(sm_scale > 0.f)) return BDG_E_INVALID;
   if (pos0 + m > cache_cap || pos0 + m > table_rows) return BDG_E_INVALID;
   if (n_heads != n_kv_heads * kGqa || head_dim != kHd) return BDG_E_UNSUPPORTED;
   if (m > kAttnMaxM || n_kv_heads > 65535) return BDG_E_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(rope_table) || !aligned16(o))
+      !aligned16(rope_table) || !aligned16(o) || !aligned16(workspace))
     return BDG_E_ALIGN;
-  const int64_t last = pos0 + m;                                   // keys of the last token
-  const int64_t max_keys = window > 0 && window < last ? window : last;
-  const int64_t n_split = attn_splits(max_keys);
-  if (n_split > 65535) return BDG_E_UNSUPPORTED;
+  if (workspace_bytes < attn_ws_bytes(n_kv_heads, m, pos0 + m)) return BDG_E_INVALID;
+  // cached keys the first token attends: the longest run over the tokens
+  const int64_t lo0 = window > 0 && pos0 - window + 1 > 0 ? pos0 - window + 1 : 0;
+  const int64_t old_keys = pos0 - lo0;
+  const int64_t kpb = old_keys > 0 ? attn_keys_per_block(old_keys, n_kv_heads, m) : kAttnWaves * 8;
+  const int64_t n_split = old_keys > 0 ? (old_keys + kpb - 1) / kpb : 0;
+  if (kpb > ((int64_t)1 << 30)) return BDG_E_UNSUPPORTED;
   AttnArgs g{};
   g.q = q; g.k = k; g.v = v; g.kc = k_cache; g.vc = v_cache; g.tab = rope_table; g.sinks = sinks; g.o = o;
-  g.cap = cache_cap; g.pos0 = pos0; g.hkv = n_kv_heads; g.window = window;
+  g.part = reinterpret_cast<float*>(workspace);
+  g.cap = cache_cap; g.pos0 = pos0; g.hkv = n_kv_heads; g.window = window; g.n_split = (int)n_split;
+  g.keys_per_block = (int)kpb;
   g.qscale = sm_scale * kLog2e;
-  if (n_split > 1) {
-    const int64_t need = attn_ws_bytes(n_kv_heads, m, max_keys);
-    if (!workspace || workspace_bytes < need) return BDG_E_INVALID;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return BDG_E_ALIGN;
-    g.counters = reinterpret_cast<int32_t*>(workspace);
-    g.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + attn_counter_bytes(n_kv_heads));
-  }
   const dim3 grid((unsigned)n_split, (unsigned)n_kv_heads, (unsigned)m);
-  if (cache_dtype == BDG_BF16)
-    hipLaunchKernelGGL(attn_decode_kernel<uint16_t>, grid, dim3(kAttnThreads), 0, as_stream(stream), g);
-  else
-    hipLaunchKernelGGL(attn_decode_kernel<float>, grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+  const dim3 grid_m((unsigned)n_kv_heads, (unsigned)m);
+  // one block per (token, kv head) covers the cached keys: a single fused launch
+  if (cache_dtype == BDG_BF16) {
+    if (n_split == 1) {
+      hipLaunchKernelGGL((attn_split_kernel<uint16_t, true>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+    } else {
+      if (n_split > 0)
+        hipLaunchKernelGGL((attn_split_kernel<uint16_t, false>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+      hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, grid_m, dim3(kAttnThreads), 0, as_stream(stream), g);
+    }
+  } else {
+    if (n_split == 1) {
+      hipLaunchKernelGGL((attn_split_kernel<float, true>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+    } else {
+      if (n_split > 0)
+        hipLaunchKernelGGL((attn_split_kernel<float, false>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+      hipLaunchKernelGGL(attn_merge_kernel<float>, grid_m, dim3(kAttnThreads), 0, as_stream(stream), g);
+    }
+  }
   return launch_status();
 }

@@ -293,8 +293,9 @@ int attn_rope_table(const bdg_rope* rope, int32_t head_dim, int64_t n_pos, float
 
 /* attn_decode_workspace - bytes of device workspace attn_decode needs for
  * calls of m tokens whose longest key range (window, or pos0 + m) is at most
- * max_keys: 0 when one block covers it, -1 for shapes attn_decode does not
- * take. */
+ * max_keys (-1 for shapes attn_decode does not take): the split partials
+ * [m][n_kv_heads][splits <= 64][8][66] fp32 (max, sum, 64 weighted values)
+ * of the attention over the cached keys. */
 int64_t attn_decode_workspace(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t m,
                               int64_t max_keys);
 
@@ -316,12 +317,12 @@ int64_t attn_decode_workspace(int32_t n_heads, int32_t n_kv_heads, int32_t head_
  *     o = sum_j e^(s_j) v_j / (sum_j e^(s_j) + e^(sinks[h])),
  *     s_j = sm_scale (q . k_j); sinks [n_heads] fp32 (device) or NULL for none.
  *   o [m][n_heads][64] fp32 (device).
- *   workspace: attn_decode_workspace(...) bytes of device memory, 256-byte
- *     aligned, zero-filled by the caller before its first use (each call
- *     leaves it ready for the next, and one workspace serves every call of
- *     the same n_kv_heads within the m and key count it was sized for); NULL
- *     when that size is 0.  Calls that share a workspace must not overlap in
- *     time.
+ *   workspace: attn_decode_workspace(...) bytes of device memory, 16-byte
+ *     aligned, owned by the caller (no initial contents needed).  Calls that
+ *     share a workspace must not overlap in time.
+ * Two kernels: the attention over the cached keys, split across blocks;
+ * then per (token, KV head) the keys of the call itself, the merge of the
+ * splits and the sink, and the append of the token's key and value.
  * Scores, softmax and sums are fp32 (within a stated bound of the exact
  * result, not bit for bit); the stored cache entries are exact.  All device
  * pointers 16-byte aligned.  head_dim 64, 8 query heads per KV head and

@@ -49,14 +49,11 @@ def test_status_text_and_version():
 
 def test_attention_workspace_sizes():
     lib = _lib.load()
-    # one block of 128 keys: no workspace
-    assert lib.attn_decode_workspace(64, 8, 64, 1, 128) == 0
-    n1 = lib.attn_decode_workspace(64, 8, 64, 1, 8192)
-    n2 = lib.attn_decode_workspace(64, 8, 64, 1, 16384)
-    assert 0 < n1 < n2
-    # counters [64 tokens][8 kv heads] + 64 splits x 8 kv heads x 8 heads x 66 floats
-    assert n1 == 64 * 8 * 4 + 64 * 8 * 8 * 66 * 4
-    assert lib.attn_decode_workspace(64, 8, 64, 65, 8192) == -1
+    part = 64 * 8 * 8 * 66 * 4            # up to 64 splits x 8 kv heads x 8 heads x (max, sum, 64 values)
+    assert lib.attn_decode_workspace(64, 8, 64, 1, 128) == part
+    assert lib.attn_decode_workspace(64, 8, 64, 1, 1 << 20) == part
+    assert lib.attn_decode_workspace(64, 8, 64, 3, 8192) == 3 * part
+    assert lib.attn_decode_workspace(16, 2, 64, 1, 8192) == part // 4
     # shapes the kernel does not take
     assert lib.attn_decode_workspace(64, 8, 128, 1, 8192) == -1
     assert lib.attn_decode_workspace(32, 8, 64, 1, 8192) == -1
@@ -67,7 +64,7 @@ def test_attention_rejects_arguments_before_launch():
     lib = _lib.load()
     fake = ctypes.c_void_p(0x1000)        # never dereferenced: every call below fails its checks
     args = dict(q=fake, k=fake, v=fake, kc=fake, vc=fake, dt=1, cap=256, hq=64, hkv=8, d=64, m=1, pos0=10,
-                tab=fake, rows=256, sm=0.125, sinks=None, window=0, o=fake, ws=None, wsb=0, s=None)
+                tab=fake, rows=256, sm=0.125, sinks=None, window=0, o=fake, ws=fake, wsb=1 << 30, s=None)
 
     def call(**kw):
         a = dict(args, **kw)
@@ -84,8 +81,8 @@ def test_attention_rejects_arguments_before_launch():
     assert call(hq=16) == _lib.BDG_E_UNSUPPORTED
     assert call(m=65, cap=1000, rows=1000) == _lib.BDG_E_UNSUPPORTED
     assert call(q=ctypes.c_void_p(0x1004)) == _lib.BDG_E_ALIGN
-    # more than one block of keys needs the workspace
-    assert call(pos0=200, ws=None) == _lib.BDG_E_INVALID
+    assert call(ws=None) == _lib.BDG_E_INVALID             # the workspace is required
+    assert call(ws=fake, wsb=100) == _lib.BDG_E_INVALID    # and must be large enough
 
 
 def test_rope_table_rejects_arguments_before_launch():
