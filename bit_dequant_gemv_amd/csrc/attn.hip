@@ -518,7 +518,7 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
   if (pb == nullptr) {
     M = bm; L = bl; A0 = o0; A1 = o1;
   } else {
-    constexpr int kChunk = 16;
+    constexpr int kChunk = 32;
     for (int c0 = 0; c0 < n_split; c0 += kChunk) {
       // splits past the end read the chunk's first split and weigh nothing
       float2 ml[kChunk], ov[kChunk];
@@ -597,7 +597,7 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kAttnThreads)
+__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_merge_kernel(AttnArgs g) {
   const int kvh = blockIdx.x, t = blockIdx.y;
   const int oh = threadIdx.x >> 5, od = threadIdx.x & 31;
