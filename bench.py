@@ -606,6 +606,13 @@ def attn_layer_bytes(cfg, layer):
     return cfg.n_kv_heads * attn_layer_keys(cfg, layer) * cfg.head_dim * 2 * es
 
 
+def attn_traffic(workload):
+    """HBM bytes of one full-attention call (split + merge kernels) from the
+    committed counter summary, or None."""
+    parts = [measured_traffic(workload, k, ATTN_SOURCES) for k in ("attn_split", "attn_merge")]
+    return None if None in parts else sum(parts)
+
+
 def bench_attn(torch, bdg, synth, dev, cfg, args):
     """Decode attention of a gpt-oss-shape stack: per layer one attn_decode
     launch (rotation, cache append, sink + window attention, split merge) at a
@@ -730,11 +737,12 @@ def bench_attn(torch, bdg, synth, dev, cfg, args):
                 "us_per_token": round(us_tok, 2),
                 "sliding_launch_us": round(slide_us, 3),
                 "cpu_baseline": cpu,
-                "roofline": {"kernel": "attn_decode_kernel (full attention)", "bound": "hbm",
+                "roofline": {"kernel": "attn_decode on a full-attention layer: attn_split_kernel + "
+                                       "attn_merge_kernel", "bound": "hbm",
                              "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                              "frac": round(achieved / PEAK_HBM_GBPS, 4),
                              "launch_us": round(launch_us, 3),
-                             "traffic": measured_traffic(cfg.name, "attn", ATTN_SOURCES),
+                             "traffic": attn_traffic(cfg.name),
                              "traffic_algorithmic_bytes": fbytes}})
     print(json.dumps(out), flush=True)
 
