@@ -36,10 +36,9 @@ def test_yarn_factor_one_is_plain_rope():
         assert scale == 1.0
 
 
-@pytest.mark.parametrize("p", [GPTOSS, OTHER], ids=["gptoss", "other"])
-def test_yarn_regions_follow_rotation_counts(p):
+def pin_yarn_regions(p, A=attn):
     d, base, s, L = p["head_dim"], p["theta"], p["factor"], p["orig_ctx"]
-    inv, _ = attn.yarn_inv_freq(**p)
+    inv, _ = A.yarn_inv_freq(**p)
     theta_i = base ** (-2.0 * np.arange(d // 2) / d)
     turns = L * theta_i / (2 * math.pi)           # rotations over the original context
     fast = turns >= p["beta_fast"]
@@ -52,13 +51,12 @@ def test_yarn_regions_follow_rotation_counts(p):
     assert np.all(np.diff(inv) < 0)
 
 
-@pytest.mark.parametrize("p", [GPTOSS, OTHER], ids=["gptoss", "other"])
-def test_yarn_ramp_is_linear_between_the_correction_dims(p):
+def pin_yarn_ramp(p, A=attn):
     # the weight of the original frequency falls linearly in the index; the
     # two ends of the ramp sit where the rotation count equals beta_fast and
     # beta_slow
     d, base, s, L = p["head_dim"], p["theta"], p["factor"], p["orig_ctx"]
-    inv, _ = attn.yarn_inv_freq(**p)
+    inv, _ = A.yarn_inv_freq(**p)
     theta_i = base ** (-2.0 * np.arange(d // 2) / d)
     w = (inv - theta_i / s) / (theta_i - theta_i / s)
     inner = np.nonzero((w > 0) & (w < 1))[0]
@@ -83,27 +81,27 @@ def test_yarn_truncate_rounds_the_ramp_ends_outward():
     np.testing.assert_allclose(np.diff(w[8:19]), -0.1, atol=1e-12)
 
 
-def test_attention_scaling():
+def pin_attention_scaling(A=attn):
     for s, want in ((1.0, 1.0), (0.5, 1.0), (math.exp(10.0), 2.0), (math.exp(5.0), 1.5)):
-        _, scale = attn.yarn_inv_freq(64, 10000.0, s, 4096, 32.0, 1.0)
+        _, scale = A.yarn_inv_freq(64, 10000.0, s, 4096, 32.0, 1.0)
         assert scale == pytest.approx(want, rel=1e-15)
 
 
 # ---- rotation ----
 
-def test_rotation_is_a_complex_multiplication():
+def pin_rotation_complex(A=attn):
     r = _rng(1)
     d = 64
-    inv32, a32 = attn.rope_constants(**GPTOSS)
+    inv32, a32 = A.rope_constants(**GPTOSS)
     x = r.standard_normal((5, 3, d)).astype(np.float32)
     pos = r.integers(0, 200000, size=(5, 3))
-    got = attn.rotate64(x, pos, inv32, a32)
+    got = A.rotate64(x, pos, inv32, a32)
     z = (x[..., :32] + 1j * x[..., 32:].astype(np.float64)) * \
         np.exp(1j * pos[..., None] * inv32.astype(np.float64)) * float(a32)
     np.testing.assert_allclose(got[..., :32], z.real, rtol=0, atol=1e-12)
     np.testing.assert_allclose(got[..., 32:], z.imag, rtol=0, atol=1e-12)
     # the table's columns are the same phasor
-    tab = attn.rope_table(inv32, a32, pos[:, 0])
+    tab = A.rope_table(inv32, a32, pos[:, 0])
     ph = np.exp(1j * pos[:, 0, None] * inv32.astype(np.float64)) * float(a32)
     np.testing.assert_allclose(tab[:, :32], ph.real, rtol=0, atol=2e-7)
     np.testing.assert_allclose(tab[:, 32:], ph.imag, rtol=0, atol=2e-7)
@@ -134,7 +132,7 @@ def test_rotation_in_fp32_is_within_two_ulps():
     assert np.all(np.abs(got - want) <= tol)
 
 
-def test_round_bf16_matches_torch():
+def pin_round_bf16(A=attn):
     r = _rng(4)
     x = np.concatenate([
         r.standard_normal(20000).astype(np.float32),
@@ -145,7 +143,7 @@ def test_round_bf16_matches_torch():
         np.array([0.0, -0.0], dtype=np.float32),
     ])
     want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
-    got = attn.round_bf16(x)
+    got = A.round_bf16(x)
     assert np.array_equal(got, want)
     assert got[-6] == 1.0 and got[-5] == 1 + 2 ** -6
 
@@ -185,12 +183,10 @@ def _case(seed, m=3, hq=8, hkv=2, d=16, n=37):
     return q, kc, vc, pos, sinks
 
 
-@pytest.mark.parametrize("window", [0, 5, 36, 200])
-@pytest.mark.parametrize("with_sinks", [False, True])
-def test_attention_matches_sdpa(window, with_sinks):
+def pin_attention_sdpa(window, with_sinks, A=attn):
     q, kc, vc, pos, sinks = _case(10 + window)
     s = sinks if with_sinks else None
-    got = attn.attention(q, kc, vc, pos, window, 0.25, s)
+    got = A.attention(q, kc, vc, pos, window, 0.25, s)
     want = _sdpa(q, kc, vc, pos, window, 0.25, s)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
@@ -294,3 +290,153 @@ def test_output_bound_covers_a_float32_evaluation():
     # the bound is a worst case; a float32 evaluation lands far inside it
     vmax = np.abs(vc).max()
     assert err.max() <= 2e-5 * vmax
+
+
+# ---- the pins as tests ----
+
+@pytest.mark.parametrize("p", [GPTOSS, OTHER], ids=["gptoss", "other"])
+def test_yarn_regions_follow_rotation_counts(p):
+    pin_yarn_regions(p)
+
+
+@pytest.mark.parametrize("p", [GPTOSS, OTHER], ids=["gptoss", "other"])
+def test_yarn_ramp_is_linear_between_the_correction_dims(p):
+    pin_yarn_ramp(p)
+
+
+def test_attention_scaling():
+    pin_attention_scaling()
+
+
+def test_rotation_is_a_complex_multiplication():
+    pin_rotation_complex()
+
+
+def test_round_bf16_matches_torch():
+    pin_round_bf16()
+
+
+@pytest.mark.parametrize("window", [0, 5, 36, 200])
+@pytest.mark.parametrize("with_sinks", [False, True])
+def test_attention_matches_sdpa(window, with_sinks):
+    pin_attention_sdpa(window, with_sinks)
+
+
+# ---- planted mistakes: each plausible slip in the oracle fails a pin ----
+
+class NS:
+    def __init__(self, base, **over):
+        for name in dir(base):
+            if not name.startswith("__"):
+                setattr(self, name, getattr(base, name))
+        for k, v in over.items():
+            setattr(self, k, v)
+
+
+def _rotate_interleaved(x, pos, inv_freq32, scale32):
+    x = np.asarray(x, dtype=np.float64)
+    f = np.asarray(inv_freq32, dtype=np.float32).astype(np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * f
+    a = float(np.float32(scale32))
+    c, s = np.cos(ang) * a, np.sin(ang) * a
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * c - x2 * s
+    out[..., 1::2] = x2 * c + x1 * s
+    return out
+
+
+def _rotate_sign(x, pos, inv_freq32, scale32):
+    return attn.rotate64(x, -np.asarray(pos), inv_freq32, scale32)
+
+
+def _table_swapped(inv_freq32, scale32, positions):
+    t = attn.rope_table(inv_freq32, scale32, positions)
+    half = t.shape[1] // 2
+    return np.concatenate([t[:, half:], t[:, :half]], axis=1)
+
+
+def _yarn_reversed(head_dim, theta, factor, orig_ctx, beta_fast, beta_slow, truncate=False):
+    inv, sc = attn.yarn_inv_freq(head_dim, theta, factor, orig_ctx, beta_fast, beta_slow, truncate)
+    base = np.power(float(theta), -2.0 * np.arange(head_dim // 2) / head_dim)
+    keep = (inv - base / factor) / (base - base / factor)
+    return base / factor * keep + base * (1.0 - keep), sc
+
+
+def _yarn_log2(head_dim, theta, factor, orig_ctx, beta_fast, beta_slow, truncate=False):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    base = np.power(float(theta), -2.0 * i / head_dim)
+    lo = head_dim * math.log2(orig_ctx / (beta_fast * 2 * math.pi)) / (2 * math.log(theta))
+    hi = head_dim * math.log2(orig_ctx / (beta_slow * 2 * math.pi)) / (2 * math.log(theta))
+    lo, hi = max(lo, 0.0), min(hi, head_dim - 1.0)
+    keep = 1.0 - np.clip((i - lo) / (hi - lo), 0.0, 1.0)
+    return base / factor * (1.0 - keep) + base * keep, 0.1 * math.log(factor) + 1.0
+
+
+def _yarn_scale_log10(head_dim, theta, factor, orig_ctx, beta_fast, beta_slow, truncate=False):
+    inv, _ = attn.yarn_inv_freq(head_dim, theta, factor, orig_ctx, beta_fast, beta_slow, truncate)
+    return inv, (0.1 * math.log10(factor) + 1.0 if factor > 1 else 1.0)
+
+
+def _bf16_truncate(x32):
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _attention_variant(kind):
+    def f(q_rot, k_cache, v_cache, pos_q, window, sm_scale, sinks=None):
+        q_rot = np.asarray(q_rot, dtype=np.float64)
+        m, hq, d = q_rot.shape
+        hkv = k_cache.shape[0]
+        o = np.zeros((m, hq, d))
+        for t in range(m):
+            p = int(pos_q[t])
+            lo = (max(0, p - window) if kind == "window" else max(0, p - window + 1)) if window else 0
+            for h in range(hq):
+                g = h % hkv if kind == "gqa" else h // (hq // hkv)
+                kk, vv = k_cache[g, lo:p + 1], v_cache[g, lo:p + 1]
+                sc = (1.0 if kind == "scale" else sm_scale) * (kk @ q_rot[t, h])
+                top = sc.max() if sinks is None else max(sc.max(), float(sinks[h]))
+                e = np.exp(sc - top)
+                if sinks is None or kind == "nosink":
+                    den = e.sum()
+                else:
+                    den = e.sum() + math.exp(float(sinks[h]) - top)
+                num = e @ vv
+                if kind == "sinkvalue" and sinks is not None:
+                    num = num + math.exp(float(sinks[h]) - top) * vv.mean(axis=0)
+                o[t, h] = num / den
+        return o
+    return f
+
+
+@pytest.mark.parametrize("which", [
+    "interleaved", "sin_sign", "table_swapped", "yarn_reversed", "yarn_log2", "scale_log10", "bf16_truncate",
+    "window_off_by_one", "gqa_modulo", "no_score_scale", "sink_dropped", "sink_has_value",
+])
+def test_planted_mistake_is_caught(which):
+    with pytest.raises(AssertionError):
+        if which == "interleaved":
+            pin_rotation_complex(NS(attn, rotate64=_rotate_interleaved))
+        elif which == "sin_sign":
+            pin_rotation_complex(NS(attn, rotate64=_rotate_sign))
+        elif which == "table_swapped":
+            pin_rotation_complex(NS(attn, rope_table=_table_swapped))
+        elif which == "yarn_reversed":
+            pin_yarn_regions(GPTOSS, NS(attn, yarn_inv_freq=_yarn_reversed))
+        elif which == "yarn_log2":
+            pin_yarn_ramp(GPTOSS, NS(attn, yarn_inv_freq=_yarn_log2))
+        elif which == "scale_log10":
+            pin_attention_scaling(NS(attn, yarn_inv_freq=_yarn_scale_log10))
+        elif which == "bf16_truncate":
+            pin_round_bf16(NS(attn, round_bf16=_bf16_truncate))
+        elif which == "window_off_by_one":
+            pin_attention_sdpa(5, True, NS(attn, attention=_attention_variant("window")))
+        elif which == "gqa_modulo":
+            pin_attention_sdpa(0, False, NS(attn, attention=_attention_variant("gqa")))
+        elif which == "no_score_scale":
+            pin_attention_sdpa(0, False, NS(attn, attention=_attention_variant("scale")))
+        elif which == "sink_dropped":
+            pin_attention_sdpa(0, True, NS(attn, attention=_attention_variant("nosink")))
+        elif which == "sink_has_value":
+            pin_attention_sdpa(36, True, NS(attn, attention=_attention_variant("sinkvalue")))
