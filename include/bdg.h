@@ -19,6 +19,9 @@
  *   - the TinyTitan project-tracker history, entries D108/D110 (fused int4
  *     dequant-inside-matmul, 16-byte row loads) and D114 (a layer's experts
  *     in one submission).
+ * Beside it: a dense packed GEMV (qgemv), the large-M expert products on the
+ * MX-scaled matrix cores, and the decode attention of a gpt-oss layer
+ * (attn_rope_table, attn_decode).
  *
  * Conventions for every entry point:
  *   - Pointers named as device pointers must be device memory (hipMalloc /
