@@ -214,16 +214,46 @@ __device__ __forceinline__ float head_transpose_sum(const float (&acc)[kGqa], in
   return keep + dpp_quad_xor1(send);
 }
 
+// a value and its partner's at lane ^ 16 / lane ^ 32 (gfx950 permlane swaps
+// of a register with itself: the two results hold the pair in either order)
+__device__ __forceinline__ void pair16(float x, float& u, float& v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  v = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float& u, float& v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  v = __uint_as_float(r[1]);
+}
+
 // max / sum over the 8 key groups of a wave (lanes with equal lane & 7)
 __device__ __forceinline__ float groups_max(float x) {
+  float u, v;
   x = fmaxf(x, dpp_f32<0x128, 0xF>(x));                 // row_ror:8 = lane ^ 8
-  x = fmaxf(x, swz_xor<16>(x));
-  return fmaxf(x, __shfl_xor(x, 32));
+  pair16(x, u, v);
+  x = fmaxf(u, v);
+  pair32(x, u, v);
+  return fmaxf(u, v);
 }
 __device__ __forceinline__ float groups_sum(float x) {
+  float u, v;
   x += dpp_f32<0x128, 0xF>(x);
-  x += swz_xor<16>(x);
-  return x + __shfl_xor(x, 32);
+  pair16(x, u, v);
+  x = u + v;
+  pair32(x, u, v);
+  return u + v;
+}
+
+// sum over each half-wave (32 lanes), every lane receiving its half's sum
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_quad_xor1(x);
+  x += dpp_quad_xor2(x);
+  x += dpp_f32<0x141, 0xF>(x);                          // row_half_mirror: the other quad of 8
+  x += dpp_f32<0x140, 0xF>(x);                          // row_mirror: the other 8 of 16
+  float u, v;
+  pair16(x, u, v);
+  return u + v;
 }
 
 // value of lane (lane & ~7) | H, i.e. lane H of this lane's group of 8
@@ -240,29 +270,35 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 __device__ __forceinline__ float exp2_rel(float x, float m) { return m == -INFINITY ? 0.f : exp2f(x - m); }
 
 // Sum over the 8 key groups of a wave of the 64 weighted-value accumulators
-// acc[h][i] of lane (a, db): three halving exchanges (lane ^ 32, ^ 16, ^ 8)
-// keep 4, 2, then 1 head per lane, so lane (a, db) ends with head a's sums
-// of dimensions 8 db .. 8 db + 7.  Fixed order: deterministic.
+// acc[h][i] of lane (a, db), transposing as it halves: lane ^ 32, then ^ 16
+// (gfx950's permlane32 / permlane16 swaps: each exchanges the half of one
+// register that the partner keeps with the half of the other it sends, so
+// the two results add to the kept sum), then ^ 8 (DPP).  Lanes keep 4, 2,
+// then 1 head: lane (a, db) ends with head a's sums of dimensions 8 db ..
+// 8 db + 7.  Fixed order: deterministic.
+__device__ __forceinline__ float swap_sum32(float keep_lo, float keep_hi) {
+  // lanes 0..31 keep keep_lo's head, lanes 32..63 keep_hi's
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(keep_lo), __float_as_uint(keep_hi), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float keep_even, float keep_odd) {
+  // even 16-lane rows keep keep_even's head, odd rows keep_odd's
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(keep_even), __float_as_uint(keep_odd), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void group_transpose_sum(float (&acc)[kGqa][8], int a, float (&out)[8]) {
-  const bool b2 = (a & 4) != 0, b1 = (a & 2) != 0, b0 = (a & 1) != 0;
+  const bool b0 = (a & 1) != 0;
   float s4[4][8];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float keep = b2 ? acc[4 + c][i] : acc[c][i];
-      const float send = b2 ? acc[c][i] : acc[4 + c][i];
-      s4[c][i] = keep + __shfl_xor(send, 32);
-    }
+    for (int i = 0; i < 8; ++i) s4[c][i] = swap_sum32(acc[c][i], acc[4 + c][i]);
   float s2[2][8];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float keep = b1 ? s4[2 + c][i] : s4[c][i];
-      const float send = b1 ? s4[c][i] : s4[2 + c][i];
-      s2[c][i] = keep + swz_xor<16>(send);
-    }
+    for (int i = 0; i < 8; ++i) s2[c][i] = swap_sum16(s4[c][i], s4[2 + c][i]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float keep = b0 ? s2[1][i] : s2[0][i];
@@ -282,7 +318,7 @@ struct AttnTile {
 // Keys of this block's sub-chunk starting at `sub`: pass p gives wave w the
 // 8 keys sub + (4p + w) 8 + 0..7; passes wholly past the block's keys are
 // skipped, and keys past its end repeat its last key (discarded later).
-template <typename T>
+template <typename T, bool kKeys = true, bool kVals = true>
 __device__ __forceinline__ void load_sub(const T* kc, const T* vc, int64_t row0, int sub, int nk, int w, int a,
                                          int db, uint4 (&kraw)[AttnTile<T>::kPasses][Cache<T>::kU],
                                          uint4 (&vraw)[AttnTile<T>::kPasses][Cache<T>::kU]) {
@@ -295,8 +331,8 @@ __device__ __forceinline__ void load_sub(const T* kc, const T* vc, int64_t row0,
     const int64_t off = (row0 + jc) * kHd + db * 8;
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
-      kraw[p][i] = ldg_u128(kc + off + i * (8 / kU));
-      vraw[p][i] = ldg_u128(vc + off + i * (8 / kU));
+      if constexpr (kKeys) kraw[p][i] = ldg_u128(kc + off + i * (8 / kU));
+      if constexpr (kVals) vraw[p][i] = ldg_u128(vc + off + i * (8 / kU));
     }
   }
 }
@@ -402,7 +438,6 @@ attn_split_kernel(AttnArgs g) {
   }
 
   for (int sub = 0; sub < nk; sub += kSub) {
-    if (sub > 0) load_sub<T>(kc, vc, row0, sub, nk, w, a, db, kraw, vraw);
     float s[kPasses];
     float mx = -INFINITY;
 #pragma unroll
@@ -424,6 +459,9 @@ attn_split_kernel(AttnArgs g) {
       s[p] = jl < nk ? sc : -INFINITY;
       mx = fmaxf(mx, s[p]);
     }
+    // the next sub-chunk's keys load during this one's softmax and value sums
+    const bool more = sub + kSub < nk;
+    if (more) load_sub<T, true, false>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
     // new running maximum of head db, then every head's value to every lane
     mx = groups_max(mx);
     float m_new[kGqa], fac[kGqa];
@@ -456,6 +494,8 @@ attn_split_kernel(AttnArgs g) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] += e8[h] * vf[i];
     }
+    // and its values during the next one's scores
+    if (more) load_sub<T, false, true>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
   }
 
   // wave results: weight sums per head, weighted values of head a
@@ -573,7 +613,7 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
         *reinterpret_cast<float2*>(reinterpret_cast<float*>(g.vc) + ci) = make_float2(v0, v1);
       }
     }
-    const float sc = group_sum<32>(q0 * k0 + q1 * k1);
+    const float sc = half_sum(q0 * k0 + q1 * k1);
     const float m2 = fmaxf(M, sc);
     const float f = exp2_rel(M, m2), ew = exp2f(sc - m2);
     L = L * f + ew;
