@@ -101,25 +101,6 @@ __device__ __forceinline__ float rot_second(float x1, float x2, float c, float s
   return x2 * c + x1 * s;
 }
 
-__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
-  const float4 a = ldg_f4(p), b = ldg_f4(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// Dimensions 8 db .. 8 db + 7 of a head vector x [64] rotated at the table
-// row `tr` [64]: pair i of the first half is (i, i + 32).
-__device__ __forceinline__ void rotate8(const float* x, const float* tr, int db, float (&out)[8]) {
-  float own[8], par[8], c[8], s[8];
-  ld8(x + db * 8, own);
-  ld8(x + (db ^ 4) * 8, par);
-  ld8(tr + (db & 3) * 8, c);
-  ld8(tr + 32 + (db & 3) * 8, s);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    out[i] = db < 4 ? rot_first(own[i], par[i], c[i], s[i]) : rot_second(par[i], own[i], c[i], s[i]);
-}
-
 // ---------------------------------------------------------------- cache values
 
 template <typename T>
@@ -137,13 +118,6 @@ struct Cache<uint16_t> {        // bf16 cache: 8 values in one 16-byte load
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
-  __device__ static void store8(uint16_t* p, const float (&v)[8]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16_rne(v[2 * i]) | ((uint32_t)f32_to_bf16_rne(v[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
 };
 
 template <>
@@ -158,10 +132,6 @@ struct Cache<float> {           // fp32 cache: 8 values in two 16-byte loads
       v[4 * j + 2] = __uint_as_float(u[j].z);
       v[4 * j + 3] = __uint_as_float(u[j].w);
     }
-  }
-  __device__ static void store8(float* p, const float (&v)[8]) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
   }
 };
 
