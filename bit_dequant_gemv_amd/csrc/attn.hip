@@ -606,11 +606,13 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
   *reinterpret_cast<float2*>(g.o + ((int64_t)t * hq + qh) * kHd + e) = make_float2(A0 * inv, A1 * inv);
 }
 
+// One wave per (kv head, pair of query heads, token): 32 threads per head,
+// so the partials of a KV head are read by four CUs rather than one.
 template <typename T>
-__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_merge_kernel(AttnArgs g) {
-  const int kvh = blockIdx.x, t = blockIdx.y;
-  const int oh = threadIdx.x >> 5, od = threadIdx.x & 31;
+  const int kvh = blockIdx.x >> 2, t = blockIdx.y;
+  const int oh = (blockIdx.x & 3) * 2 + (threadIdx.x >> 5), od = threadIdx.x & 31;
   const NewKeyIn in = load_new_in(g, kvh, t, oh, od);
   merge_heads<T>(g, kvh, t, oh, od, in, g.part + ((int64_t)t * g.hkv + kvh) * g.n_split * kGqa * kPartStride,
                  g.n_split, 0.f, 0.f, 0.f, 0.f);
@@ -690,7 +692,7 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
   g.keys_per_block = (int)kpb;
   g.qscale = sm_scale * kLog2e;
   const dim3 grid((unsigned)n_split, (unsigned)n_kv_heads, (unsigned)m);
-  const dim3 grid_m((unsigned)n_kv_heads, (unsigned)m);
+  const dim3 grid_m((unsigned)n_kv_heads * (kGqa / 2), (unsigned)m);
   // one block per (token, kv head) covers the cached keys: a single fused launch
   if (cache_dtype == BDG_BF16) {
     if (n_split == 1) {
@@ -698,7 +700,7 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
     } else {
       if (n_split > 0)
         hipLaunchKernelGGL((attn_split_kernel<uint16_t, false>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
-      hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, grid_m, dim3(kAttnThreads), 0, as_stream(stream), g);
+      hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, grid_m, dim3(kWave), 0, as_stream(stream), g);
     }
   } else {
     if (n_split == 1) {
@@ -706,7 +708,7 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
     } else {
       if (n_split > 0)
         hipLaunchKernelGGL((attn_split_kernel<float, false>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
-      hipLaunchKernelGGL(attn_merge_kernel<float>, grid_m, dim3(kAttnThreads), 0, as_stream(stream), g);
+      hipLaunchKernelGGL(attn_merge_kernel<float>, grid_m, dim3(kWave), 0, as_stream(stream), g);
     }
   }
   return launch_status();
