@@ -27,9 +27,10 @@
 
 namespace bdg {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kGqa = 8;                        // query heads per KV head
+constexpr int kHeadThreads = kGqa * 32;        // threads of the (head, 2 dimensions) phases
 constexpr int kHd = 64;                        // head dimension
 constexpr int kMaxSplits = 64;                 // blocks per (token, kv head) at most
 constexpr int kTargetBlocks = 256;             // split-kernel blocks a call aims for
@@ -374,12 +375,12 @@ attn_split_kernel(AttnArgs g) {
   uint4 kraw[kPasses][C::kU], vraw[kPasses][C::kU];
   if (nk > 0) load_sub<T>(kc, vc, row0, 0, nk, w, a, db, kraw, vraw);
   NewKeyIn nin;
-  if constexpr (kFused) nin = load_new_in(g, kvh, t, tid >> 5, tid & 31);
+  if constexpr (kFused) nin = load_new_in(g, kvh, t, (tid >> 5) & (kGqa - 1), tid & 31);
 
   // the 8 query heads of this KV head, rotated and scaled by qscale: thread
   // (head, pair i) rotates dimensions i and i + 32 into LDS, then lane (a, db)
   // keeps dimensions 8 db .. of every head in registers
-  {
+  if (tid < kHeadThreads) {
     const int h = tid >> 5, i = tid & 31;
     const float* qh = g.q + ((int64_t)t * hq + kvh * kGqa + h) * kHd;
     const float* tr = g.tab + pt * kHd;
@@ -484,8 +485,11 @@ attn_split_kernel(AttnArgs g) {
   __syncthreads();
 
   // block partial: thread (head oh, dimensions 2 od, 2 od + 1)
+  if (tid >= kHeadThreads) return;
   const int oh = tid >> 5, od = tid & 31;
-  const float bm = fmaxf(fmaxf(wm[0][oh], wm[1][oh]), fmaxf(wm[2][oh], wm[3][oh]));
+  float bm = wm[0][oh];
+#pragma unroll
+  for (int ww = 1; ww < kAttnWaves; ++ww) bm = fmaxf(bm, wm[ww][oh]);
   float bl = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int ww = 0; ww < kAttnWaves; ++ww) {
