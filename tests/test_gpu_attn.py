@@ -143,6 +143,8 @@ CASES = [
     ("f32", 5000, 2, 0, True, 2),        # two sub-chunks per block (running maximum rescaled)
     ("bf16", 10000, 1, 0, True, 1),      # two sub-chunks per block
     ("bf16", 20000, 3, 300, True, 2),    # long cache, window of 300
+    ("bf16", 65536, 1, 0, True, 1),      # 64K keys: eight sub-chunks per block
+    ("f32", 30000, 2, 0, True, 1),       # fp32 cache, several sub-chunks per block
 ]
 
 
