@@ -100,17 +100,30 @@ __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
 }
 
+// A value plus its partner's at lane ^ 16 / lane ^ 32, by gfx950's permlane
+// swaps of a register with itself (the two results hold the pair in either
+// order, so every lane gets the same sum).
+__device__ __forceinline__ float add_pair16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over aligned groups of L lanes (L in {4, 8, 16, 32, 64}); every lane of
-// a group receives the group's sum.  Fixed butterfly order: deterministic.
+// a group receives the group's sum.  All steps stay in the VALU (quad DPP,
+// row half-mirror and mirror, permlane swaps).  Fixed order: deterministic.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "group size");
   v += dpp_quad_xor1(v);
   v += dpp_quad_xor2(v);
-  if constexpr (L > 4) v += swz_xor<4>(v);
-  if constexpr (L > 8) v += swz_xor<8>(v);
-  if constexpr (L > 16) v += swz_xor<16>(v);
-  if constexpr (L > 32) v += __shfl_xor(v, 32);
+  if constexpr (L > 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  if constexpr (L > 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  if constexpr (L > 16) v = add_pair16(v);
+  if constexpr (L > 32) v = add_pair32(v);
   return v;
 }
 

@@ -635,13 +635,13 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
 #pragma unroll
     for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor2(a[i]);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += swz_xor<4>(a[i]);
+    for (int i = 0; i < NA; ++i) a[i] += dpp_f32<0x141, 0xF>(a[i]);   // row_half_mirror
 #pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += swz_xor<8>(a[i]);
+    for (int i = 0; i < NA; ++i) a[i] += dpp_f32<0x140, 0xF>(a[i]);   // row_mirror
 #pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += swz_xor<16>(a[i]);
+    for (int i = 0; i < NA; ++i) a[i] = add_pair16(a[i]);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += __shfl_xor(a[i], 32);
+    for (int i = 0; i < NA; ++i) a[i] = add_pair32(a[i]);
     if (lane == 0) {
       float* out = p.part_out + (int64_t)t * (p.E + 1) * p.pstride + blockIdx.x;
 #pragma unroll
