@@ -145,6 +145,8 @@ CASES = [
     ("bf16", 20000, 3, 300, True, 2),    # long cache, window of 300
     ("bf16", 65536, 1, 0, True, 1),      # 64K keys: eight sub-chunks per block
     ("f32", 30000, 2, 0, True, 1),       # fp32 cache, several sub-chunks per block
+    ("bf16", 3000, 64, 0, True, 1),      # the largest chunk: 64 tokens, up to 64 own keys each
+    ("bf16", 200, 64, 40, True, 2),      # 64 tokens, windows mostly inside the chunk itself
 ]
 
 
