@@ -100,6 +100,12 @@ def measured_traffic(workload, kernel, sources=KERNEL_SOURCES):
     return None if t is None else t["fetch_bytes"] + t["write_bytes"]
 
 
+def blas_threads():
+    """Threads the oracle's NumPy BLAS uses (its matrix products run on them)."""
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+
+
 def cpu_baseline(cfg, sample_layers, m):
     """The oracle as it stands on `sample_layers` layers of one step (M tokens).
 
@@ -282,7 +288,7 @@ def bench_gemv(torch, bdg, synth, sdev, dev, cfg, args):
             n += 1
         dt = (time.perf_counter() - t1) / n
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
-               "cores": int(os.cpu_count() or 1),
+               "cores": blas_threads(),
                "sample": f"{n} calls, dequant (NumPy, one thread) + float64 matvec each"}
         del w
     out = base_record(cfg, value, K * R, W * R, cold_us * 1e-3, {
@@ -373,7 +379,7 @@ def bench_dense(torch, bdg, synth, sdev, dev, cfg, args):
             n += 1
         dt = (time.perf_counter() - t1) / n
         cpu = {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
-               "cores": int(os.cpu_count() or 1),
+               "cores": blas_threads(),
                "sample": f"{rows} of {cfg.n} rows, {n} passes of dequant (NumPy) + float64 matvec"}
     out = base_record(cfg, value, K * calls, W * calls, call_us * 1e-3, {
         "workload": cfg.name, "fmt": cfg.fmt, "n": cfg.n, "k": cfg.k, "m": 1,
@@ -449,7 +455,7 @@ def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
             n += 1
         dt = (time.perf_counter() - t1) / n
         cpu = {"value": round(2.0 * cfg.n * 8 * cfg.k / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
-               "cores": int(os.cpu_count() or 1),
+               "cores": blas_threads(),
                "sample": f"8 of {m} tokens, {n} passes of quantize + dequantize + float64 product"}
     out = {
         "metric": "mx_gemm TFLOP/s (MXFP4 weights x MXFP8 activations)",
@@ -724,7 +730,7 @@ def bench_attn(torch, bdg, synth, dev, cfg, args):
             n += 1
         dt = (time.perf_counter() - t1) / n
         cpu = {"value": round(fbytes / dt / 1e9, 4), "unit": "GB/s", "kind": "oracle",
-               "cores": int(os.cpu_count() or 1),
+               "cores": blas_threads(),
                "us_per_token": round(dt * 1e6 * nbytes / fbytes, 1),
                "sample": f"one full-attention layer (ctx {cfg.ctx}) of one token, {n} passes of the float64 "
                          f"oracle step (rotation, cache store, 64 heads of attention), per-byte rate"}
