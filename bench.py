@@ -114,7 +114,6 @@ def cpu_baseline(cfg, sample_layers, m):
     layer; the per-layer time is scaled to a whole step of every layer.
     """
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     import synth
     from oracle import formats, moe as omoe
@@ -148,17 +147,17 @@ def cpu_baseline(cfg, sample_layers, m):
         passes += 1
     dt = time.perf_counter() - t0
     per_step_s = dt / (passes * sample_layers) * cfg.n_layers
-    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    n_threads = blas_threads()
     nbytes = step_bytes(cfg, [float(np.mean(uniq))] * cfg.n_layers)
     return {
         "value": round(nbytes / per_step_s / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(blas_threads),
+        "cores": n_threads,
         "kind": "oracle",
         "us_per_token": round(per_step_s / m * 1e6, 1),
         "sample": f"{sample_layers} of {cfg.n_layers} layers of a step of M={m} tokens, {passes} pass{'es' if passes != 1 else ''} "
                   f"on fresh tokens, {dt:.1f} s of CPU time, scaled to a whole step; float64 NumPy, "
-                  f"elementwise dequant on one thread, BLAS matvecs on {blas_threads}",
+                  f"elementwise dequant on one thread, BLAS matvecs on {n_threads}",
     }
 
 
