@@ -27,8 +27,8 @@
 
 namespace bdg {
 
-constexpr int kAttnThreads = 512;
-constexpr int kAttnWaves = kAttnThreads / kWave;
+constexpr int kSplitWaves = 8;                 // waves of a split block (one of several per KV head)
+constexpr int kFusedWaves = 4;                 // waves of a block that takes every cached key
 constexpr int kGqa = 8;                        // query heads per KV head
 constexpr int kHeadThreads = kGqa * 32;        // threads of the (head, 2 dimensions) phases
 constexpr int kHd = 64;                        // head dimension
@@ -278,26 +278,26 @@ __device__ __forceinline__ void group_transpose_sum(float (&acc)[kGqa][8], int a
   }
 }
 
-template <typename T>
+template <typename T, int NW>
 struct AttnTile {
   using C = Cache<T>;
   static constexpr int kPasses = 4 / C::kU;                  // passes per sub-chunk
-  static constexpr int kPass = kAttnWaves * 8;               // keys per block per pass (8 per wave)
+  static constexpr int kPass = NW * 8;                       // keys per block per pass (8 per wave)
   static constexpr int kSub = kPass * kPasses;               // keys per block per sub-chunk
 };
 
 // Keys of this block's sub-chunk starting at `sub`: pass p gives wave w the
 // 8 keys sub + (4p + w) 8 + 0..7; passes wholly past the block's keys are
 // skipped, and keys past its end repeat its last key (discarded later).
-template <typename T, bool kKeys = true, bool kVals = true>
+template <typename T, int NW, bool kKeys = true, bool kVals = true>
 __device__ __forceinline__ void load_sub(const T* kc, const T* vc, int64_t row0, int sub, int nk, int w, int a,
-                                         int db, uint4 (&kraw)[AttnTile<T>::kPasses][Cache<T>::kU],
-                                         uint4 (&vraw)[AttnTile<T>::kPasses][Cache<T>::kU]) {
-  constexpr int kPasses = AttnTile<T>::kPasses, kU = Cache<T>::kU, kPass = AttnTile<T>::kPass;
+                                         int db, uint4 (&kraw)[AttnTile<T, NW>::kPasses][Cache<T>::kU],
+                                         uint4 (&vraw)[AttnTile<T, NW>::kPasses][Cache<T>::kU]) {
+  constexpr int kPasses = AttnTile<T, NW>::kPasses, kU = Cache<T>::kU, kPass = AttnTile<T, NW>::kPass;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     if (sub + p * kPass >= nk) break;
-    const int jl = sub + (p * kAttnWaves + w) * 8 + a;
+    const int jl = sub + (p * NW + w) * 8 + a;
     const int jc = jl < nk ? jl : nk - 1;
     const int64_t off = (row0 + jc) * kHd + db * 8;
 #pragma unroll
@@ -350,14 +350,15 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
 
 
 template <typename T, bool kFused>
-__global__ void __launch_bounds__(kAttnThreads)
+__global__ void __launch_bounds__(kFused ? kFusedWaves * kWave : kSplitWaves * kWave)
 attn_split_kernel(AttnArgs g) {
+  constexpr int NW = kFused ? kFusedWaves : kSplitWaves;
   using C = Cache<T>;
-  constexpr int kPasses = AttnTile<T>::kPasses;
-  constexpr int kSub = AttnTile<T>::kSub;
-  constexpr int kPass = AttnTile<T>::kPass;
-  __shared__ float wo[kAttnWaves][kGqa][kHd];
-  __shared__ float wm[kAttnWaves][kGqa], wl[kAttnWaves][kGqa];
+  constexpr int kPasses = AttnTile<T, NW>::kPasses;
+  constexpr int kSub = AttnTile<T, NW>::kSub;
+  constexpr int kPass = AttnTile<T, NW>::kPass;
+  __shared__ float wo[NW][kGqa][kHd];
+  __shared__ float wm[NW][kGqa], wl[NW][kGqa];
   __shared__ float qlds[kGqa][kHd];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -373,7 +374,7 @@ attn_split_kernel(AttnArgs g) {
   const int64_t row0 = (int64_t)kvh * g.cap + jb;             // cache row of key jb
 
   uint4 kraw[kPasses][C::kU], vraw[kPasses][C::kU];
-  if (nk > 0) load_sub<T>(kc, vc, row0, 0, nk, w, a, db, kraw, vraw);
+  if (nk > 0) load_sub<T, NW>(kc, vc, row0, 0, nk, w, a, db, kraw, vraw);
   NewKeyIn nin;
   if constexpr (kFused) nin = load_new_in(g, kvh, t, (tid >> 5) & (kGqa - 1), tid & 31);
 
@@ -415,7 +416,7 @@ attn_split_kernel(AttnArgs g) {
     for (int p = 0; p < kPasses; ++p) {
       s[p] = -INFINITY;
       if (sub + p * kPass >= nk) break;
-      const int jl = sub + (p * kAttnWaves + w) * 8 + a;
+      const int jl = sub + (p * NW + w) * 8 + a;
       float kf[8];
       C::unpack(kraw[p], kf);
       float d[kGqa];
@@ -432,7 +433,7 @@ attn_split_kernel(AttnArgs g) {
     }
     // the next sub-chunk's keys load during this one's softmax and value sums
     const bool more = sub + kSub < nk;
-    if (more) load_sub<T, true, false>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
+    if (more) load_sub<T, NW, true, false>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
     // new running maximum of head db, then every head's value to every lane
     mx = groups_max(mx);
     float m_new[kGqa], fac[kGqa];
@@ -466,7 +467,7 @@ attn_split_kernel(AttnArgs g) {
         for (int i = 0; i < 8; ++i) acc[h][i] += e8[h] * vf[i];
     }
     // and its values during the next one's scores
-    if (more) load_sub<T, false, true>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
+    if (more) load_sub<T, NW, false, true>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
   }
 
   // wave results: weight sums per head, weighted values of head a
@@ -489,10 +490,10 @@ attn_split_kernel(AttnArgs g) {
   const int oh = tid >> 5, od = tid & 31;
   float bm = wm[0][oh];
 #pragma unroll
-  for (int ww = 1; ww < kAttnWaves; ++ww) bm = fmaxf(bm, wm[ww][oh]);
+  for (int ww = 1; ww < NW; ++ww) bm = fmaxf(bm, wm[ww][oh]);
   float bl = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < kAttnWaves; ++ww) {
+  for (int ww = 0; ww < NW; ++ww) {
     const float f = exp2_rel(wm[ww][oh], bm);
     bl += f * wl[ww][oh];
     o0 += f * wo[ww][oh][2 * od];
@@ -629,11 +630,11 @@ attn_merge_kernel(AttnArgs g) {
 // the chip (about kTargetBlocks blocks over all tokens and KV heads), at most
 // kMaxSplits per token and KV head.
 inline int64_t attn_keys_per_block(int64_t keys, int hkv, int m) {
-  if (keys <= kFuseKeys) return (keys + kAttnWaves * 8 - 1) / (kAttnWaves * 8) * (kAttnWaves * 8);
+  if (keys <= kFuseKeys) return (keys + kFusedWaves * 8 - 1) / (kFusedWaves * 8) * (kFusedWaves * 8);
   int64_t splits = kTargetBlocks / ((int64_t)hkv * m);
   splits = splits < 1 ? 1 : splits > kMaxSplits ? kMaxSplits : splits;
   const int64_t per = (keys + splits - 1) / splits;
-  return (per + kAttnWaves * 8 - 1) / (kAttnWaves * 8) * (kAttnWaves * 8);
+  return (per + kSplitWaves * 8 - 1) / (kSplitWaves * 8) * (kSplitWaves * 8);
 }
 
 inline int64_t attn_ws_bytes(int hkv, int m, int64_t max_keys) {
@@ -686,7 +687,7 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
   // cached keys the first token attends: the longest run over the tokens
   const int64_t lo0 = window > 0 && pos0 - window + 1 > 0 ? pos0 - window + 1 : 0;
   const int64_t old_keys = pos0 - lo0;
-  const int64_t kpb = old_keys > 0 ? attn_keys_per_block(old_keys, n_kv_heads, m) : kAttnWaves * 8;
+  const int64_t kpb = old_keys > 0 ? attn_keys_per_block(old_keys, n_kv_heads, m) : kFusedWaves * 8;
   const int64_t n_split = old_keys > 0 ? (old_keys + kpb - 1) / kpb : 0;
   if (kpb > ((int64_t)1 << 30)) return BDG_E_UNSUPPORTED;
   AttnArgs g{};
@@ -700,18 +701,18 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
   // one block per (token, kv head) covers the cached keys: a single fused launch
   if (cache_dtype == BDG_BF16) {
     if (n_split == 1) {
-      hipLaunchKernelGGL((attn_split_kernel<uint16_t, true>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+      hipLaunchKernelGGL((attn_split_kernel<uint16_t, true>), grid, dim3(kFusedWaves * kWave), 0, as_stream(stream), g);
     } else {
       if (n_split > 0)
-        hipLaunchKernelGGL((attn_split_kernel<uint16_t, false>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+        hipLaunchKernelGGL((attn_split_kernel<uint16_t, false>), grid, dim3(kSplitWaves * kWave), 0, as_stream(stream), g);
       hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, grid_m, dim3(kWave), 0, as_stream(stream), g);
     }
   } else {
     if (n_split == 1) {
-      hipLaunchKernelGGL((attn_split_kernel<float, true>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+      hipLaunchKernelGGL((attn_split_kernel<float, true>), grid, dim3(kFusedWaves * kWave), 0, as_stream(stream), g);
     } else {
       if (n_split > 0)
-        hipLaunchKernelGGL((attn_split_kernel<float, false>), grid, dim3(kAttnThreads), 0, as_stream(stream), g);
+        hipLaunchKernelGGL((attn_split_kernel<float, false>), grid, dim3(kSplitWaves * kWave), 0, as_stream(stream), g);
       hipLaunchKernelGGL(attn_merge_kernel<float>, grid_m, dim3(kWave), 0, as_stream(stream), g);
     }
   }
