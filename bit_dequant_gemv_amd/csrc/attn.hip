@@ -7,7 +7,8 @@
 // published YaRN method and a softmax in which each query head's sink is one
 // more logit with a zero value.
 //
-// Two launches per layer, no block waiting on or signalling another.
+// Two launches per layer (one when a single block holds every cached key of
+// a token), no block waiting on or signalling another.
 // attn_split_kernel (flash-decoding) covers the keys already in the cache:
 // block (split, kv head, token) takes a run of the token's window for the
 // kGqa query heads that share the KV head, rotating their queries itself;
@@ -17,9 +18,12 @@
 // rotated queries stay in 64 registers, one transposing butterfly over the
 // 8 lanes leaves lane (key, h) with head h's score, and the weighted values
 // accumulate in the same lanes; the block writes (max, sum, weighted values)
-// per head.  attn_merge_kernel, one block per (kv head, token), adds the
-// keys of the call itself (rotated from their projections), merges the
-// splits and the sink, and appends the token's key and value to the cache.
+// per head.  attn_merge_kernel, one wave per (kv head, pair of query heads,
+// token), adds the keys of the call itself (rotated from their projections),
+// merges the splits and the sink, and appends the token's key and value to
+// the cache; with a single block the split kernel does this itself.
+// Cross-half exchanges use gfx950's permlane swaps and DPP, not the LDS
+// crossbar.
 #include <math.h>
 
 #include "bdg_device.hpp"
