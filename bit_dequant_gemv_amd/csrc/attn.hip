@@ -377,21 +377,25 @@ attn_split_kernel(AttnArgs g) {
   const T* vc = reinterpret_cast<const T*>(g.vc);
   const int64_t row0 = (int64_t)kvh * g.cap + jb;             // cache row of key jb
 
+  // the query's rotation inputs first, so rotating them (below) waits only
+  // for these and overlaps the cache loads: thread (head, pair i) takes
+  // dimensions i and i + 32 of one of the 8 query heads of this KV head
+  const int qh_i = (tid >> 5) & (kGqa - 1), q_i = tid & 31;
+  const float* qh = g.q + ((int64_t)t * hq + kvh * kGqa + qh_i) * kHd;
+  const float* tr = g.tab + pt * kHd;
+  const float qx1 = qh[q_i], qx2 = qh[q_i + 32], qc = tr[q_i], qsn = tr[32 + q_i];
+  __builtin_amdgcn_sched_barrier(0);
   uint4 kraw[kPasses][C::kU], vraw[kPasses][C::kU];
   if (nk > 0) load_sub<T, NW>(kc, vc, row0, 0, nk, w, a, db, kraw, vraw);
   NewKeyIn nin;
   if constexpr (kFused) nin = load_new_in(g, kvh, t, (tid >> 5) & (kGqa - 1), tid & 31);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // the 8 query heads of this KV head, rotated and scaled by qscale: thread
-  // (head, pair i) rotates dimensions i and i + 32 into LDS, then lane (a, db)
-  // keeps dimensions 8 db .. of every head in registers
+  // rotated and scaled by qscale into LDS; lane (a, db) then keeps dimensions
+  // 8 db .. of every head in registers
   if (tid < kHeadThreads) {
-    const int h = tid >> 5, i = tid & 31;
-    const float* qh = g.q + ((int64_t)t * hq + kvh * kGqa + h) * kHd;
-    const float* tr = g.tab + pt * kHd;
-    const float x1 = qh[i], x2 = qh[i + 32], c = tr[i], sn = tr[32 + i];
-    qlds[h][i] = rot_first(x1, x2, c, sn) * g.qscale;
-    qlds[h][i + 32] = rot_second(x1, x2, c, sn) * g.qscale;
+    qlds[qh_i][q_i] = rot_first(qx1, qx2, qc, qsn) * g.qscale;
+    qlds[qh_i][q_i + 32] = rot_second(qx1, qx2, qc, qsn) * g.qscale;
   }
   __syncthreads();
   float qs[kGqa][8];
