@@ -163,30 +163,26 @@ __device__ __forceinline__ int64_t window_lo(const AttnArgs& g, int64_t pt) {
   return g.window > 0 ? (pt - g.window + 1 > 0 ? pt - g.window + 1 : 0) : 0;
 }
 
+// Query head that lane db of a key group holds at position j of its score
+// accumulators.  head_transpose_sum exchanges with lanes db ^ 7, db ^ 2 and
+// db ^ 1 in turn; in this order each step's kept heads are the first half of
+// the lane's positions and its partner sends the same heads from the second
+// half, so the exchange needs no per-lane selects.
+__device__ __forceinline__ int head_at(int db, int j) { return db ^ (j & 3) ^ ((j & 4) ? 7 : 0); }
+
 // The block's 8 per-head scores of key group `a`: lane (a, db) holds the
-// partial dot products acc[h] over its 8 dimensions; three exchange steps
-// (mirror within 8 lanes, then xor 2, xor 1 within 4) halve the heads a
-// lane keeps and add the partner's share, ending with lane db holding head
-// db's full sum.  Fixed order: deterministic.
-__device__ __forceinline__ float head_transpose_sum(const float (&acc)[kGqa], int db) {
-  const bool up4 = db >= 4, b1 = (db & 2) != 0, b0 = (db & 1) != 0;
+// partial dot products d[j] of head head_at(db, j) over its 8 dimensions;
+// three exchange steps (mirror within 8 lanes, then xor 2, xor 1 within 4)
+// halve the heads a lane keeps and add the partner's share, ending with lane
+// db holding head db's full sum.  Fixed order: deterministic.
+__device__ __forceinline__ float head_transpose_sum(const float (&d)[kGqa]) {
   float k4[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float keep = up4 ? acc[4 + c] : acc[c];
-    const float send = up4 ? acc[c] : acc[4 + c];
-    k4[c] = keep + dpp_f32<0x141, 0xF>(send);          // row_half_mirror: lane i <-> 7 - i
-  }
+  for (int c = 0; c < 4; ++c) k4[c] = d[c] + dpp_f32<0x141, 0xF>(d[4 + c]);   // row_half_mirror: lane i <-> 7 - i
   float k2[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float keep = b1 ? k4[2 + c] : k4[c];
-    const float send = b1 ? k4[c] : k4[2 + c];
-    k2[c] = keep + dpp_quad_xor2(send);
-  }
-  const float keep = b0 ? k2[1] : k2[0];
-  const float send = b0 ? k2[0] : k2[1];
-  return keep + dpp_quad_xor1(send);
+  for (int c = 0; c < 2; ++c) k2[c] = k4[c] + dpp_quad_xor2(k4[2 + c]);
+  return k2[0] + dpp_quad_xor1(k2[1]);
 }
 
 // a value and its partner's at lane ^ 16 / lane ^ 32 (gfx950 permlane swaps
@@ -350,7 +346,8 @@ __device__ __forceinline__ float2 rot_pair(float2 own, float2 par, float2 c, flo
 
 template <typename T>
 __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, int oh, int od, const NewKeyIn& in,
-                                            const float* pb, int n_split, float bm, float bl, float o0, float o1);
+                                            const float* pb, int n_split, float2* mls, float bm, float bl, float o0,
+                                            float o1);
 
 
 template <typename T, bool kFused>
@@ -392,7 +389,7 @@ attn_split_kernel(AttnArgs g) {
   __builtin_amdgcn_sched_barrier(0);
 
   // rotated and scaled by qscale into LDS; lane (a, db) then keeps dimensions
-  // 8 db .. of every head in registers
+  // 8 db .. of every head in registers, head head_at(db, j) at position j
   if (tid < kHeadThreads) {
     qlds[qh_i][q_i] = rot_first(qx1, qx2, qc, qsn) * g.qscale;
     qlds[qh_i][q_i + 32] = rot_second(qx1, qx2, qc, qsn) * g.qscale;
@@ -400,11 +397,12 @@ attn_split_kernel(AttnArgs g) {
   __syncthreads();
   float qs[kGqa][8];
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h) {
+  for (int j = 0; j < kGqa; ++j) {
+    const int h = head_at(db, j);
     const float4 lo4 = *reinterpret_cast<const float4*>(&qlds[h][db * 8]);
     const float4 hi4 = *reinterpret_cast<const float4*>(&qlds[h][db * 8 + 4]);
-    qs[h][0] = lo4.x; qs[h][1] = lo4.y; qs[h][2] = lo4.z; qs[h][3] = lo4.w;
-    qs[h][4] = hi4.x; qs[h][5] = hi4.y; qs[h][6] = hi4.z; qs[h][7] = hi4.w;
+    qs[j][0] = lo4.x; qs[j][1] = lo4.y; qs[j][2] = lo4.z; qs[j][3] = lo4.w;
+    qs[j][4] = hi4.x; qs[j][5] = hi4.y; qs[j][6] = hi4.z; qs[j][7] = hi4.w;
   }
 
   float m_run[kGqa];        // running maximum per head (wave-uniform)
@@ -429,13 +427,13 @@ attn_split_kernel(AttnArgs g) {
       C::unpack(kraw[p], kf);
       float d[kGqa];
 #pragma unroll
-      for (int h = 0; h < kGqa; ++h) {
+      for (int j = 0; j < kGqa; ++j) {
         float x = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x += qs[h][i] * kf[i];
-        d[h] = x;
+        for (int i = 0; i < 8; ++i) x += qs[j][i] * kf[i];
+        d[j] = x;
       }
-      const float sc = head_transpose_sum(d, db);
+      const float sc = head_transpose_sum(d);
       s[p] = jl < nk ? sc : -INFINITY;
       mx = fmaxf(mx, s[p]);
     }
@@ -444,22 +442,30 @@ attn_split_kernel(AttnArgs g) {
     if (more) load_sub<T, NW, true, false>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
     // new running maximum of head db, then every head's value to every lane
     mx = groups_max(mx);
-    float m_new[kGqa], fac[kGqa];
+    float m_new[kGqa];
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) m_new[h] = fmaxf(m_run[h], lane_value(mx, h));
+    if (sub > 0) {
+      // rescale what earlier sub-chunks gathered (before the first there is
+      // nothing: the factor would be 0 on zero sums)
+      float fac[kGqa];
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) {
+        fac[h] = exp2_rel(m_run[h], m_new[h]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] *= fac[h];
+      }
+      float f_mine = fac[0];
+#pragma unroll
+      for (int h = 1; h < kGqa; ++h) f_mine = db == h ? fac[h] : f_mine;
+      lsum *= f_mine;
+    }
+    float m_mine = m_new[0];
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) {
-      m_new[h] = fmaxf(m_run[h], lane_value(mx, h));
-      fac[h] = exp2_rel(m_run[h], m_new[h]);
       m_run[h] = m_new[h];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] *= fac[h];
-    }
-    float m_mine = m_new[0], f_mine = fac[0];
-#pragma unroll
-    for (int h = 1; h < kGqa; ++h) {
       m_mine = db == h ? m_new[h] : m_mine;
-      f_mine = db == h ? fac[h] : f_mine;
     }
-    lsum *= f_mine;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       if (sub + p * kPass >= nk) break;
@@ -508,7 +514,7 @@ attn_split_kernel(AttnArgs g) {
     o1 += f * wo[ww][oh][2 * od + 1];
   }
   if constexpr (kFused) {                    // one block holds every cached key: merge here
-    merge_heads<T>(g, kvh, t, oh, od, nin, nullptr, 0, bm, bl, o0, o1);
+    merge_heads<T>(g, kvh, t, oh, od, nin, nullptr, 0, nullptr, bm, bl, o0, o1);
   } else {
     float* pp = g.part + ((((int64_t)t * g.hkv + kvh) * g.n_split + split) * kGqa + oh) * kPartStride;
     if (od == 0) *reinterpret_cast<float2*>(pp) = make_float2(bm, bl);
@@ -521,13 +527,18 @@ attn_split_kernel(AttnArgs g) {
 // The softmax of one (token, query head) over the cached-key splits, the
 // keys of this call and the sink, by thread (oh, od) for dimensions 2 od and
 // 2 od + 1.  Splits come from `pb` ([n_split][kGqa][kPartStride], global) or,
-// with pb null, as the single partial (bm, bl, o0, o1) in registers.  The
+// with pb null, as the single partial (bm, bl, o0, o1) in registers.  With
+// pb, the caller is one wave holding two heads (lanes 0-31, 32-63) and `mls`
+// is its LDS row of 64 float2: lane od loads the (max, sum) of split od of a
+// chunk once and its half-wave reads all 32 from LDS, so a chunk costs 33
+// global loads per lane instead of 64 (a wave can have 63 in flight).  The
 // call's keys are rotated from their projections in the cache's rounding and
 // scored with a sum over the head's 32 threads; threads of head 0 append the
 // token's own key and value to the cache.
 template <typename T>
 __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, int oh, int od, const NewKeyIn& in,
-                                            const float* pb, int n_split, float bm, float bl, float o0, float o1) {
+                                            const float* pb, int n_split, float2* mls, float bm, float bl, float o0,
+                                            float o1) {
   using C = Cache<T>;
   const int e = 2 * od, ti = e & 31;
   const bool first = e < 32;
@@ -542,16 +553,22 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
     M = bm; L = bl; A0 = o0; A1 = o1;
   } else {
     constexpr int kChunk = 32;
+    const int half = threadIdx.x & 32;
     for (int c0 = 0; c0 < n_split; c0 += kChunk) {
       // splits past the end read the chunk's first split and weigh nothing
+      const int so = c0 + od < n_split ? c0 + od : c0;
+      const float2 ml_own = ld2(pb + ((int64_t)so * kGqa + oh) * kPartStride);
       float2 ml[kChunk], ov[kChunk];
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const int sp = c0 + u < n_split ? c0 + u : c0;
-        const float* ph = pb + ((int64_t)sp * kGqa + oh) * kPartStride;
-        ml[u] = ld2(ph);
-        ov[u] = ld2(ph + 2 + e);
+        ov[u] = ld2(pb + ((int64_t)sp * kGqa + oh) * kPartStride + 2 + e);
       }
+      mls[threadIdx.x] = ml_own;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) ml[u] = mls[half + u];
+      __syncthreads();                         // the next chunk rewrites mls
       float cm = M;
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) cm = fmaxf(cm, ml[u].x);
@@ -626,9 +643,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 attn_merge_kernel(AttnArgs g) {
   const int kvh = blockIdx.x >> 2, t = blockIdx.y;
   const int oh = (blockIdx.x & 3) * 2 + (threadIdx.x >> 5), od = threadIdx.x & 31;
+  __shared__ float2 mls[kWave];
   const NewKeyIn in = load_new_in(g, kvh, t, oh, od);
   merge_heads<T>(g, kvh, t, oh, od, in, g.part + ((int64_t)t * g.hkv + kvh) * g.n_split * kGqa * kPartStride,
-                 g.n_split, 0.f, 0.f, 0.f, 0.f);
+                 g.n_split, mls, 0.f, 0.f, 0.f, 0.f);
 }
 
 // ---------------------------------------------------------------- host side
