@@ -227,6 +227,17 @@ __device__ __forceinline__ float half_sum(float x) {
   return u + v;
 }
 
+// maximum over each half-wave (32 lanes), every lane receiving its half's
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_quad_xor1(x));
+  x = fmaxf(x, dpp_quad_xor2(x));
+  x = fmaxf(x, dpp_f32<0x141, 0xF>(x));
+  x = fmaxf(x, dpp_f32<0x140, 0xF>(x));
+  float u, v;
+  pair16(x, u, v);
+  return fmaxf(u, v);
+}
+
 // value of lane (lane & ~7) | H, i.e. lane H of this lane's group of 8
 template <int H>
 __device__ __forceinline__ float bcast8(float v) {
@@ -346,7 +357,7 @@ __device__ __forceinline__ float2 rot_pair(float2 own, float2 par, float2 c, flo
 
 template <typename T>
 __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, int oh, int od, const NewKeyIn& in,
-                                            const float* pb, int n_split, float2* mls, float bm, float bl, float o0,
+                                            const float* pb, int n_split, float* wls, float bm, float bl, float o0,
                                             float o1);
 
 
@@ -528,16 +539,17 @@ attn_split_kernel(AttnArgs g) {
 // keys of this call and the sink, by thread (oh, od) for dimensions 2 od and
 // 2 od + 1.  Splits come from `pb` ([n_split][kGqa][kPartStride], global) or,
 // with pb null, as the single partial (bm, bl, o0, o1) in registers.  With
-// pb, the caller is one wave holding two heads (lanes 0-31, 32-63) and `mls`
-// is its LDS row of 64 float2: lane od loads the (max, sum) of split od of a
-// chunk once and its half-wave reads all 32 from LDS, so a chunk costs 33
-// global loads per lane instead of 64 (a wave can have 63 in flight).  The
+// pb, the caller is one wave holding two heads (lanes 0-31, 32-63) and `wls`
+// is its LDS row of 64 floats: lane od loads the (max, sum) of split od of a
+// chunk, weighs that split against the half-wave's maximum, and the
+// half-wave reads the 32 weights back from LDS; a chunk costs 33 global
+// loads per lane (a wave keeps at most 63 in flight) and one exponential.  The
 // call's keys are rotated from their projections in the cache's rounding and
 // scored with a sum over the head's 32 threads; threads of head 0 append the
 // token's own key and value to the cache.
 template <typename T>
 __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, int oh, int od, const NewKeyIn& in,
-                                            const float* pb, int n_split, float2* mls, float bm, float bl, float o0,
+                                            const float* pb, int n_split, float* wls, float bm, float bl, float o0,
                                             float o1) {
   using C = Cache<T>;
   const int e = 2 * od, ti = e & 31;
@@ -558,28 +570,29 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
       // splits past the end read the chunk's first split and weigh nothing
       const int so = c0 + od < n_split ? c0 + od : c0;
       const float2 ml_own = ld2(pb + ((int64_t)so * kGqa + oh) * kPartStride);
-      float2 ml[kChunk], ov[kChunk];
+      float2 ov[kChunk];
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const int sp = c0 + u < n_split ? c0 + u : c0;
         ov[u] = ld2(pb + ((int64_t)sp * kGqa + oh) * kPartStride + 2 + e);
       }
-      mls[threadIdx.x] = ml_own;
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) ml[u] = mls[half + u];
-      __syncthreads();                         // the next chunk rewrites mls
-      float cm = M;
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) cm = fmaxf(cm, ml[u].x);
+      // the chunk's maximum over the half-wave (repeated splits change no
+      // maximum), then lane od weighs split od alone
+      const float cm = fmaxf(M, half_max(ml_own.x));
       const float f = exp2_rel(M, cm);
-      L *= f; A0 *= f; A1 *= f;
+      const float w_own = c0 + od < n_split ? exp2_rel(ml_own.x, cm) : 0.f;
+      L = L * f + half_sum(w_own * ml_own.y);
+      wls[threadIdx.x] = w_own;
+      __syncthreads();
+      float wgt[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) wgt[u] = wls[half + u];
+      __syncthreads();                         // the next chunk rewrites wls
+      A0 *= f; A1 *= f;
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
-        const float wgt = c0 + u < n_split ? exp2_rel(ml[u].x, cm) : 0.f;
-        L += wgt * ml[u].y;
-        A0 += wgt * ov[u].x;
-        A1 += wgt * ov[u].y;
+        A0 += wgt[u] * ov[u].x;
+        A1 += wgt[u] * ov[u].y;
       }
       M = cm;
     }
@@ -643,10 +656,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1
 attn_merge_kernel(AttnArgs g) {
   const int kvh = blockIdx.x >> 2, t = blockIdx.y;
   const int oh = (blockIdx.x & 3) * 2 + (threadIdx.x >> 5), od = threadIdx.x & 31;
-  __shared__ float2 mls[kWave];
+  __shared__ float wls[kWave];
   const NewKeyIn in = load_new_in(g, kvh, t, oh, od);
   merge_heads<T>(g, kvh, t, oh, od, in, g.part + ((int64_t)t * g.hkv + kvh) * g.n_split * kGqa * kPartStride,
-                 g.n_split, mls, 0.f, 0.f, 0.f, 0.f);
+                 g.n_split, wls, 0.f, 0.f, 0.f, 0.f);
 }
 
 // ---------------------------------------------------------------- host side
