@@ -248,8 +248,14 @@ __device__ __forceinline__ float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
+// 2^x by the hardware exponential alone (v_exp_f32, 1 ulp).  The library
+// exp2f adds a rescaling for results below 2^-126; every exponential here is
+// a softmax weight relative to a running maximum (at most 1, and the maximum
+// itself weighs 1), so such results are far below the sum's resolution.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // exp2(x - m) with an empty maximum (m = -inf) giving 0 rather than NaN
-__device__ __forceinline__ float exp2_rel(float x, float m) { return m == -INFINITY ? 0.f : exp2f(x - m); }
+__device__ __forceinline__ float exp2_rel(float x, float m) { return m == -INFINITY ? 0.f : exp2_hw(x - m); }
 
 // Sum over the 8 key groups of a wave of the 64 weighted-value accumulators
 // acc[h][i] of lane (a, db), transposing as it halves: lane ^ 32, then ^ 16
@@ -628,7 +634,7 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
     }
     const float sc = half_sum(q0 * k0 + q1 * k1);
     const float m2 = fmaxf(M, sc);
-    const float f = exp2_rel(M, m2), ew = exp2f(sc - m2);
+    const float f = exp2_rel(M, m2), ew = exp2_hw(sc - m2);
     L = L * f + ew;
     A0 = A0 * f + ew * v0;
     A1 = A1 * f + ew * v1;
@@ -641,7 +647,7 @@ __device__ __forceinline__ void merge_heads(const AttnArgs& g, int kvh, int t, i
     const float sk = g.sinks[qh] * kLog2e;
     const float m2 = fmaxf(M, sk);
     const float f = exp2_rel(M, m2);
-    L = L * f + exp2f(sk - m2);
+    L = L * f + exp2_hw(sk - m2);
     A0 *= f;
     A1 *= f;
   }
