@@ -244,6 +244,12 @@ __device__ __forceinline__ float bcast8(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (H << 5) | 0x18));
 }
 
+// value of lane W of this lane's group of 32
+template <int W>
+__device__ __forceinline__ float bcast32(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), W << 5));
+}
+
 __device__ __forceinline__ float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
@@ -422,15 +428,13 @@ attn_split_kernel(AttnArgs g) {
     qs[j][4] = hi4.x; qs[j][5] = hi4.y; qs[j][6] = hi4.z; qs[j][7] = hi4.w;
   }
 
-  float m_run[kGqa];        // running maximum per head (wave-uniform)
+  float m_mine = -INFINITY; // running maximum of head db (equal in the lanes of equal db)
   float acc[kGqa][8];       // weighted values: head h, dimensions 8 db ..
   float lsum = 0.f;         // this lane's share of head db's weight sum
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h) {
-    m_run[h] = -INFINITY;
+  for (int h = 0; h < kGqa; ++h)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-  }
 
   for (int sub = 0; sub < nk; sub += kSub) {
     float s[kPasses];
@@ -457,32 +461,24 @@ attn_split_kernel(AttnArgs g) {
     // the next sub-chunk's keys load during this one's softmax and value sums
     const bool more = sub + kSub < nk;
     if (more) load_sub<T, NW, true, false>(kc, vc, row0, sub + kSub, nk, w, a, db, kraw, vraw);
-    // new running maximum of head db, then every head's value to every lane
+    // new running maximum of head db (the group maximum is head db's in
+    // every lane of equal db)
     mx = groups_max(mx);
-    float m_new[kGqa];
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) m_new[h] = fmaxf(m_run[h], lane_value(mx, h));
+    const float m_new = fmaxf(m_mine, mx);
     if (sub > 0) {
       // rescale what earlier sub-chunks gathered (before the first there is
-      // nothing: the factor would be 0 on zero sums)
-      float fac[kGqa];
+      // nothing: the factor would be 0 on zero sums); lane h holds head h's
+      // factor
+      const float f_mine = exp2_rel(m_mine, m_new);
+      lsum *= f_mine;
 #pragma unroll
       for (int h = 0; h < kGqa; ++h) {
-        fac[h] = exp2_rel(m_run[h], m_new[h]);
+        const float fac = lane_value(f_mine, h);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] *= fac[h];
+        for (int i = 0; i < 8; ++i) acc[h][i] *= fac;
       }
-      float f_mine = fac[0];
-#pragma unroll
-      for (int h = 1; h < kGqa; ++h) f_mine = db == h ? fac[h] : f_mine;
-      lsum *= f_mine;
     }
-    float m_mine = m_new[0];
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) {
-      m_run[h] = m_new[h];
-      m_mine = db == h ? m_new[h] : m_mine;
-    }
+    m_mine = m_new;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       if (sub + p * kPass >= nk) break;
@@ -506,10 +502,7 @@ attn_split_kernel(AttnArgs g) {
   float o8[8];
   group_transpose_sum(acc, a, o8);
   if (a == 0) {
-    float mm = m_run[0];
-#pragma unroll
-    for (int h = 1; h < kGqa; ++h) mm = db == h ? m_run[h] : mm;
-    wm[w][db] = mm;
+    wm[w][db] = m_mine;
     wl[w][db] = lsum;
   }
   *reinterpret_cast<float4*>(&wo[w][a][db * 8]) = make_float4(o8[0], o8[1], o8[2], o8[3]);
@@ -522,10 +515,15 @@ attn_split_kernel(AttnArgs g) {
   float bm = wm[0][oh];
 #pragma unroll
   for (int ww = 1; ww < NW; ++ww) bm = fmaxf(bm, wm[ww][oh]);
+  // thread od < NW weighs wave od; the head's 32 threads share the factors
+  const float f_own = exp2_rel(wm[od < NW ? od : 0][oh], bm);
+  const float fw[8] = {bcast32<0>(f_own), bcast32<1>(f_own), bcast32<2>(f_own), bcast32<3>(f_own),
+                       bcast32<4 % NW>(f_own), bcast32<5 % NW>(f_own), bcast32<6 % NW>(f_own),
+                       bcast32<7 % NW>(f_own)};
   float bl = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) {
-    const float f = exp2_rel(wm[ww][oh], bm);
+    const float f = fw[ww];
     bl += f * wl[ww][oh];
     o0 += f * wo[ww][oh][2 * od];
     o1 += f * wo[ww][oh][2 * od + 1];
