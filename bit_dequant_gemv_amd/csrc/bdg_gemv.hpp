@@ -114,6 +114,33 @@ struct XRegs {
       }
     }
   }
+
+  // The same where the LDS region holds one more chunk, all zeros, at index
+  // `chunks`: a slot past the row end reads that chunk, so no value needs a
+  // select (one index clamp per slot instead of 32 selects).
+  __device__ __forceinline__ void load_zpad(const float* __restrict__ lds_x, int chunks, int li) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = li + L * s;
+      const float4* src = reinterpret_cast<const float4*>(lds_x + (c < chunks ? c : chunks) * kXStride);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 t = src[q];
+        v[s][4 * q + 0] = t.x;
+        v[s][4 * q + 1] = t.y;
+        v[s][4 * q + 2] = t.z;
+        v[s][4 * q + 3] = t.w;
+      }
+      if constexpr (FMT == kINT4G) {
+        float a = 0.f;
+#pragma unroll
+        for (int q = 0; q < kChunkElems; ++q) a += v[s][q];
+        sum[s] = a;
+      } else {
+        sum[s] = 0.f;
+      }
+    }
+  }
 };
 
 // Lane-partial dot of the loaded row against x, summed over the L lanes of
@@ -125,8 +152,11 @@ __device__ __forceinline__ float row_dot(const GroupLoad<FMT, S>& ld, const XReg
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const bool ok = (ld.ok >> s) & 1u;
-    // neutral scale for padding slots: E8M0 127 = 1.0, fp16 0x3C00 = 1.0
-    const uint32_t sc = ok ? ld.sc[s] : (FMT == kMXFP4 ? 127u : 0x3C00u);
+    // neutral scale for padding slots (fp16 0x3C00 = 1.0: an infinite scale
+    // times their zero sum would be NaN).  MXFP4 needs none: a padding slot
+    // repeats the row's last chunk against zero x, so it adds 0, or NaN only
+    // where that chunk's own scale (E8M0 255) already makes the row NaN.
+    const uint32_t sc = FMT == kMXFP4 ? ld.sc[s] : (ok ? ld.sc[s] : 0x3C00u);
     const uint32_t z = (ld.zn[s] >> (((ld.zhi >> s) & 1u) * 4u)) & 15u;
     acc += chunk_contrib<FMT>(ld.q[s], sc, z, xr.v[s], xr.sum[s]);
   }

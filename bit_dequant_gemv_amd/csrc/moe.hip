@@ -320,8 +320,8 @@ template <int FMT, int S, int NP, int V>
 __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   constexpr int L = 32;
   extern __shared__ float lds[];
-  float* xs = lds;                                          // [chunks * kXStride]
-  float* red = xs + p.g.chunks * kXStride;                  // [kWaves]
+  float* xs = lds;                                          // [(chunks + 1) * kXStride], chunk `chunks` zero
+  float* red = xs + (p.g.chunks + 1) * kXStride;            // [kWaves]
   float* psum = red + kWaves;                               // [E << log2T]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -472,9 +472,10 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   }
 
   xstage.store(xs, p.H, p.H, 0, mult, threadIdx.x, kThreads);
+  xs[p.g.chunks * kXStride + (threadIdx.x & (kChunkElems - 1))] = 0.f;   // the zero chunk (no branch)
   __syncthreads();
   XRegs<FMT, L, S> xr;
-  xr.load(xs, p.g.chunks, li);
+  xr.load_zpad(xs, p.g.chunks, li);
 
   // pair i: lanes 0..31 hold the gate row's dot g_i, lanes 32..63 the up
   // row's u_i; lane i gathers (g_i, u_i) and SwiGLU runs once per wave
@@ -530,7 +531,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   const int kg = p.K < kDownWaves ? p.K : kDownWaves;      // experts per group
   const int wpe = kDownWaves / kg;                          // waves per expert
   const int B = NR * RPW * wpe;
-  const int stride = p.g.chunks * kXStride;
+  const int stride = (p.g.chunks + 1) * kXStride;          // per expert: chunks of h, then a zero chunk
   float* dpart = lds + kg * stride;                         // [K][B]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -561,7 +562,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
     __syncthreads();
     if (active) {
       XRegs<FMT, L, S> xr;
-      xr.load(lds + jw * stride, p.g.chunks, li);
+      xr.load_zpad(lds + jw * stride, p.g.chunks, li);
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         const float d = row_dot<FMT, L, S>(ld[i], xr);
@@ -597,6 +598,12 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   const float xp = p.x_prev[(int64_t)t * p.H + orow];
   const float wk = p.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
   __builtin_amdgcn_sched_barrier(0);
+  // the zero chunk after each expert's h (h staging never writes it); no
+  // branch: threads past the kg chunks repeat the last one's stores
+  {
+    const int zr = min((int)(threadIdx.x / kChunkElems), kg - 1);
+    lds[zr * stride + p.g.chunks * kXStride + (threadIdx.x & (kChunkElems - 1))] = 0.f;
+  }
   group(0, e0, h0);
   for (int jg = kg; jg < p.K; jg += kg) {   // K > 8 only
     const int jn = jg + (jw < p.K - jg ? jw : p.K - jg - 1);
@@ -1178,7 +1185,7 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int np
   if (blocks > 65535) return BDG_E_UNSUPPORTED;
   const int E = gp.E;
   const size_t psum = (size_t)E << p->log2T;
-  const size_t lds = ((size_t)gp.g.chunks * kXStride + kWaves + psum) * sizeof(float);
+  const size_t lds = ((size_t)(gp.g.chunks + 1) * kXStride + kWaves + psum) * sizeof(float);
   dim3 grid((unsigned)blocks, m);
   const int fmt = p->d.fmt, V = p->topk_V;
 #define BDG_GU_CASE(F, SS, VV)                                                                            \
@@ -1228,7 +1235,7 @@ static int launch_down(const bdg_plan* p, int layer, int m, int residual, float*
   const int kg = dp.K < kDownWaves ? dp.K : kDownWaves;
   const int wpe = kDownWaves / kg;
   const int B = p->dn_NR * rpw * wpe;
-  const size_t lds = ((size_t)kg * dp.g.chunks * kXStride + (size_t)dp.K * B) * sizeof(float);
+  const size_t lds = ((size_t)kg * (dp.g.chunks + 1) * kXStride + (size_t)dp.K * B) * sizeof(float);
   dim3 grid((unsigned)((dp.H + B - 1) / B), m);
   const int fmt = p->d.fmt, NR = p->dn_NR;
   const int hv = down_stage_f4(dp.K, dp.I);
