@@ -355,11 +355,10 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
     if (slices) {
       const int c = threadIdx.x >> lt;
       const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
+      // rows are zero past the nparts slices up to pstride >= 4 * T * kPartF4
+      // (the plan zeroes the buffer once; no kernel writes there)
 #pragma unroll
-      for (int i = 0; i < kPartF4; ++i) {
-        const int k4 = sub + (i << lt);
-        pv[i] = k4 < n4 ? ldg_f4(row + 4 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int i = 0; i < kPartF4; ++i) pv[i] = ldg_f4(row + 4 * (sub + (i << lt)));
       // sum-of-squares slices (column E): one float4 per thread, n4 <= kThreads
       const int k4 = threadIdx.x;
       const float4 q = k4 < n4 ? ldg_f4(p.part + pbase + (int64_t)p.E * p.pstride + 4 * k4)
@@ -383,6 +382,18 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   StageF32<NX> xstage;
   xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
 
+  // this wave's pair range (independent of the routing: computed while the
+  // routing inputs are in flight)
+  const int P = p.K * p.I;
+  const int GW = gridDim.x * kWaves;
+  const int gw = blockIdx.x * kWaves + wave;
+  const int q0 = (int)((int64_t)P * gw / GW);
+  const int q1 = (int)((int64_t)P * (gw + 1) / GW);
+  const int nq = q1 - q0;                 // <= NP pairs for this wave
+  // (slot, row) of q0; later pairs step the row and wrap to the next slot
+  const int j0 = q0 / p.I;
+  const int row0 = q0 - j0 * p.I;
+
   float r = 1.0f;
   if (slices) {
     // slices of expert c: thread sub adds slices 4*(sub + i*T) .. +3, in order
@@ -394,11 +405,10 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
       if (c0 == 0) {
 #pragma unroll
         for (int i = 0; i < kPartF4; ++i, k4 += T) {
-          const int k = 4 * k4;
-          a += k < p.nparts ? pv[i].x : 0.f;
-          a += k + 1 < p.nparts ? pv[i].y : 0.f;
-          a += k + 2 < p.nparts ? pv[i].z : 0.f;
-          a += k + 3 < p.nparts ? pv[i].w : 0.f;
+          a += pv[i].x;
+          a += pv[i].y;
+          a += pv[i].z;
+          a += pv[i].w;
         }
       }
       for (; k4 < n4; k4 += T) {   // beyond the slices loaded up front
@@ -444,15 +454,6 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
     if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
   }
 
-  const int P = p.K * p.I;
-  const int GW = gridDim.x * kWaves;
-  const int gw = blockIdx.x * kWaves + wave;
-  const int q0 = (int)((int64_t)P * gw / GW);
-  const int q1 = (int)((int64_t)P * (gw + 1) / GW);
-  const int nq = q1 - q0;                 // <= NP pairs for this wave
-  // (slot, row) of q0; later pairs step the row and wrap to the next slot
-  const int j0 = q0 / p.I;
-  const int row0 = q0 - j0 * p.I;
 
   // every slot loads (a wave short of NP pairs repeats its last pair and
   // stores nothing for the repeats): no branch around the loads
@@ -1478,10 +1479,13 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     p->fuse_route = (d->flags & BDG_MOE_STACK) && d->n_layers > 1 && B <= kWave &&
                     p->dn_blocks <= 4 * kThreads && d->n_experts <= kDownWaves * kDnRouterPerWave &&
                     env_int("BDG_FUSE_ROUTE", 1, 0, 1);
-    p->pstride = ((p->fuse_route ? p->dn_blocks : 1) + 3) & ~3;
     int lt = 0;
     while (lt < 6 && (d->n_experts << (lt + 1)) <= kThreads) ++lt;
     p->log2T = lt;
+    // gate_up loads 4 * T * kPartF4 slices per expert row up front, without
+    // bounds checks: rows are at least that long, zero past the slices
+    p->pstride = ((p->fuse_route ? p->dn_blocks : 1) + 3) & ~3;
+    if (p->fuse_route) p->pstride = std::max(p->pstride, 4 * (1 << lt) * kPartF4);
   }
   {
     // grouped path: persistent grids sized to the device, items padded so a
@@ -1544,6 +1548,13 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->h = reinterpret_cast<float*>(base + o_h);
   p->dout = reinterpret_cast<float*>(base + o_dout);
   p->chunks = reinterpret_cast<int32_t*>(base + o_chunks);
+  // router partial sums: zero once, so slots past the slices read as 0
+  if (hipMemset(p->part, 0, sizeof(float) * (size_t)M * (E + 1) * p->pstride) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(p->dev_base);
+    delete p;
+    return BDG_E_HIP;
+  }
   LayerDev* host = new (std::nothrow) LayerDev[d->n_layers];
   p->wr = new (std::nothrow) const float*[d->n_layers];
   if (!host || !p->wr) {
