@@ -56,12 +56,12 @@ __device__ __forceinline__ void load_row(GroupLoad<FMT, S>& ld, const QMat& m, c
     ld.ok |= (ok ? 1u : 0u) << s;
     ld.q[s] = ldg_u128(m.codes + (r * (uint32_t)g.chunks + cc) * 16u);
     if constexpr (FMT == kMXFP4) {
-      ld.sc[s] = ldg_u8(m.scales + r * (uint32_t)g.chunks + cc);
+      ld.sc[s] = ldg_u8(m.scales + (r * (uint32_t)g.chunks + cc));   // one 32-bit offset: scalar-base load
       ld.zn[s] = 0;
     } else {
       const uint32_t gi = (cc * kChunkElems) / (uint32_t)g.group;
       ld.sc[s] = ldg_u16(m.scales + (r * (uint32_t)g.groups + gi) * 2u);
-      ld.zn[s] = ldg_u8(m.zeros + r * (uint32_t)g.zrow + (gi >> 1));
+      ld.zn[s] = ldg_u8(m.zeros + (r * (uint32_t)g.zrow + (gi >> 1)));
       ld.zhi |= (gi & 1u) << s;
     }
   }
