@@ -170,9 +170,11 @@ __device__ __forceinline__ f32x2 fp4_pair(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
 
+// Two interleaved partial sums (even and odd elements): enough independent
+// chains for back-to-back wave64 issue, one add to combine them.
 __device__ __forceinline__ float fp4_chunk_dot(const uint4 q, const float* __restrict__ x) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     f32x2 p0 = fp4_pair<0>(w[d]);
@@ -181,14 +183,14 @@ __device__ __forceinline__ float fp4_chunk_dot(const uint4 q, const float* __res
     f32x2 p3 = fp4_pair<3>(w[d]);
     a0 = __builtin_fmaf(p0.x, x[8 * d + 0], a0);
     a1 = __builtin_fmaf(p0.y, x[8 * d + 1], a1);
-    a2 = __builtin_fmaf(p1.x, x[8 * d + 2], a2);
-    a3 = __builtin_fmaf(p1.y, x[8 * d + 3], a3);
+    a0 = __builtin_fmaf(p1.x, x[8 * d + 2], a0);
+    a1 = __builtin_fmaf(p1.y, x[8 * d + 3], a1);
     a0 = __builtin_fmaf(p2.x, x[8 * d + 4], a0);
     a1 = __builtin_fmaf(p2.y, x[8 * d + 5], a1);
-    a2 = __builtin_fmaf(p3.x, x[8 * d + 6], a2);
-    a3 = __builtin_fmaf(p3.y, x[8 * d + 7], a3);
+    a0 = __builtin_fmaf(p3.x, x[8 * d + 6], a0);
+    a1 = __builtin_fmaf(p3.y, x[8 * d + 7], a1);
   }
-  return (a0 + a1) + (a2 + a3);
+  return a0 + a1;
 }
 
 // int4: sum_i q_i * x_i over one 16-byte chunk (32 unsigned nibbles).
@@ -205,7 +207,7 @@ __device__ __forceinline__ f32x2 u4_pair(uint32_t plane) {
 
 __device__ __forceinline__ float u4_chunk_dot(const uint4 q, const float* __restrict__ x) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t lo = w[d] & 0x0F0F0F0Fu;          // elements 8d + 0, 2, 4, 6
@@ -216,14 +218,14 @@ __device__ __forceinline__ float u4_chunk_dot(const uint4 q, const float* __rest
     const f32x2 e57 = u4_pair<true>(hi);
     a0 = __builtin_fmaf(e02.x, x[8 * d + 0], a0);
     a1 = __builtin_fmaf(e13.x, x[8 * d + 1], a1);
-    a2 = __builtin_fmaf(e02.y, x[8 * d + 2], a2);
-    a3 = __builtin_fmaf(e13.y, x[8 * d + 3], a3);
+    a0 = __builtin_fmaf(e02.y, x[8 * d + 2], a0);
+    a1 = __builtin_fmaf(e13.y, x[8 * d + 3], a1);
     a0 = __builtin_fmaf(e46.x, x[8 * d + 4], a0);
     a1 = __builtin_fmaf(e57.x, x[8 * d + 5], a1);
-    a2 = __builtin_fmaf(e46.y, x[8 * d + 6], a2);
-    a3 = __builtin_fmaf(e57.y, x[8 * d + 7], a3);
+    a0 = __builtin_fmaf(e46.y, x[8 * d + 6], a0);
+    a1 = __builtin_fmaf(e57.y, x[8 * d + 7], a1);
   }
-  return (a0 + a1) + (a2 + a3);
+  return a0 + a1;
 }
 
 // ---------------------------------------------------------------- packed-matrix view
