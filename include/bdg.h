@@ -178,7 +178,10 @@ typedef struct bdg_plan bdg_plan;
  * and a cache of captured per-token HIP graphs.  The session-keyed setup
  * cache of the host-sync page (section 3): nothing of this is rebuilt per
  * token; a change of any weight pointer, shape or flag needs a new plan.
- * Allocates device memory; synchronous.  *out receives the plan. */
+ * Allocates device memory, zero-fills the routing partial sums (padding
+ * past the slices the kernels write must read as 0) and waits for the
+ * device; synchronous.  *out receives the plan; BDG_E_HIP if the fill
+ * fails. */
 int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out);
 
 /* moe_plan_destroy - free a plan and everything it allocated; waits for
