@@ -58,9 +58,10 @@ qgemv_kernel(QMat w, QGeom g, int64_t n_rows, const void* __restrict__ x, int x_
   } else {
     xf.store(lds_x, g.k, g.k, 0, 1.0f, threadIdx.x, kGemvThreads);
   }
+  lds_x[g.chunks * kXStride + (threadIdx.x & (kChunkElems - 1))] = 0.f;   // the zero chunk after x (no branch)
   __syncthreads();
   XRegs<FMT, L, S> xr;
-  xr.load(lds_x, g.chunks, li);
+  xr.load_zpad(lds_x, g.chunks, li);
   float* yt = y + (int64_t)t * n_rows;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -83,7 +84,7 @@ static int launch_qgemv(const QMat& w, const QGeom& g, int64_t n, const void* x,
   int64_t blocks = (n_groups + (int64_t)np * kGemvWaves - 1) / ((int64_t)np * kGemvWaves);
   if (blocks < 1) blocks = 1;
   if (blocks > 2147483647LL) return BDG_E_UNSUPPORTED;
-  const size_t lds = (size_t)g.chunks * kXStride * sizeof(float);
+  const size_t lds = (size_t)(g.chunks + 1) * kXStride * sizeof(float);   // x chunks and one zero chunk
   dim3 grid((unsigned)blocks, (unsigned)m);
 #define BDG_GEMV_CASE(LL, SS, NN)                                                                       \
   if (L == LL && S == SS && np == NN) {                                                                 \
