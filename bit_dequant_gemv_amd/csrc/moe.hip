@@ -808,8 +808,12 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
   constexpr int NX = S;                                 // H <= 32 * L * S: float4 of x per thread
   extern __shared__ float lds[];
   GroupLds& gl = *reinterpret_cast<GroupLds*>(lds);
-  float* xs = lds + group_lds_floats();                 // [kGroupTT][chunks * kXStride]
-  const int xstride = p.g.chunks * kXStride;
+  float* xs = lds + group_lds_floats();                 // [kGroupTT][(chunks + 1) * kXStride]
+  const int xstride = (p.g.chunks + 1) * kXStride;      // each input: chunks, then a zero chunk
+  // the zero chunks (staging never writes them; the first item's barrier
+  // orders these stores before any read); no branch
+  xs[min((int)(threadIdx.x / kChunkElems), kGroupTT - 1) * xstride + p.g.chunks * kXStride +
+     (threadIdx.x & (kChunkElems - 1))] = 0.f;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_wave_id();
   const int li = lane % L;
@@ -895,7 +899,7 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
 #pragma unroll 1
     for (int k = 0; k < nt; ++k) {
       XRegs<FMT, L, S> xr;
-      xr.load(xs + k * xstride, p.g.chunks, li);
+      xr.load_zpad(xs + k * xstride, p.g.chunks, li);
       float g_sel = 0.f, u_sel = 0.f;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
@@ -933,8 +937,10 @@ __global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams
   constexpr int NH = (L * S + 31) / 32;                // I <= 32 * L * S: float4 of h per thread
   extern __shared__ float lds[];
   int* tab = reinterpret_cast<int*>(lds);               // [1 + kGroupMaxPicks * kChunkInts]
-  float* hs = lds + (1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4;   // [kGroupTT][chunks * kXStride]
-  const int hstride = p.g.chunks * kXStride;
+  float* hs = lds + (1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4;   // [kGroupTT][(chunks + 1) * kXStride]
+  const int hstride = (p.g.chunks + 1) * kXStride;      // each input: chunks, then a zero chunk
+  hs[min((int)(threadIdx.x / kChunkElems), kGroupTT - 1) * hstride + p.g.chunks * kXStride +
+     (threadIdx.x & (kChunkElems - 1))] = 0.f;           // the zero chunks (no branch)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_wave_id();
   const int li = lane % L;
@@ -973,7 +979,7 @@ __global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams
 #pragma unroll 1
     for (int k = 0; k < nt; ++k) {
       XRegs<FMT, L, S> xr;
-      xr.load(hs + k * hstride, p.g.chunks, li);
+      xr.load_zpad(hs + k * hstride, p.g.chunks, li);
       float* out = p.dout + (int64_t)ch[2 + k] * p.H;
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -1291,7 +1297,7 @@ static int launch_gu_group(const bdg_plan* p, int layer, int m, int routed, cons
   gp.h_out = p->h;
   gp.chunks_out = p->chunks;
   gp.bpc = p->g_bpc;
-  const size_t lds = (group_lds_floats() + (size_t)kGroupTT * gp.g.chunks * kXStride) * sizeof(float);
+  const size_t lds = (group_lds_floats() + (size_t)kGroupTT * (gp.g.chunks + 1) * kXStride) * sizeof(float);
   const dim3 grid((unsigned)p->g_grid_gu);
   const int fmt = p->d.fmt, V = p->topk_V;
 #define BDG_GG_CASE(F, SS, VV)                                                                            \
@@ -1321,7 +1327,7 @@ static int launch_dn_group(const bdg_plan* p, int layer, hipStream_t s, Prof* pr
   dp.g = p->dn_geom;
   dp.nrb = p->g_nrb;
   const size_t lds =
-      ((size_t)(1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4 + (size_t)kGroupTT * dp.g.chunks * kXStride) *
+      ((size_t)(1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4 + (size_t)kGroupTT * (dp.g.chunks + 1) * kXStride) *
       sizeof(float);
   const dim3 grid((unsigned)p->g_grid_dn);
   const int fmt = p->d.fmt;
@@ -1495,8 +1501,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
     const int hc32 = d->hidden / 32, ic32 = d->inter / 32;
-    const size_t lds_gu = (group_lds_floats() + (size_t)kGroupTT * hc32 * kXStride) * sizeof(float);
-    const size_t lds_dn = ((size_t)(1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4 + (size_t)kGroupTT * ic32 * kXStride) *
+    const size_t lds_gu = (group_lds_floats() + (size_t)kGroupTT * (hc32 + 1) * kXStride) * sizeof(float);
+    const size_t lds_dn = ((size_t)(1 + kGroupMaxPicks * kChunkInts + 3) / 4 * 4 + (size_t)kGroupTT * (ic32 + 1) * kXStride) *
                           sizeof(float);
     const size_t lds_cu = 160 * 1024;
     const int bg = (int)std::min<size_t>(2, lds_cu / lds_gu), bd = (int)std::min<size_t>(2, lds_cu / lds_dn);
