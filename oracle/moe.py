@@ -130,24 +130,38 @@ def near_tie(logits_row, scale_row, a, b, rel=NEAR_TIE_REL):
 def check_routing(logits_row, scale_row, idx_gpu, k, rel=NEAR_TIE_REL):
     """Validate a GPU top-k list against float64 logits.
 
-    Outside the near-tie band the choice and order are unique and must match;
-    inside it either choice is correct.  Returns (ok, n_ties, msg).
+    A list is a correct top-k when it names k distinct experts in [0, E),
+    no expert it leaves out beats an expert it keeps, and it runs in
+    descending order -- each comparison exact outside the near-tie band and
+    free inside it (fp32 rounding may decide a near tie either way).
+    Returns (ok, n_ties, msg); n_ties counts the decisions taken inside the
+    band (picks that differ from the oracle's own, and swapped neighbours).
     """
-    own = topk_order(logits_row[None, :], k)[0]
-    idx_gpu = [int(e) for e in idx_gpu]
-    if list(own) == idx_gpu:
-        return True, 0, ""
+    logits_row = np.asarray(logits_row, dtype=np.float64)
+    n_exp = logits_row.shape[0]
+    try:
+        idx_gpu = [int(e) for e in idx_gpu]
+    except (TypeError, ValueError):
+        return False, 0, "GPU top-k holds a non-integer"
+    if len(idx_gpu) != k:
+        return False, 0, f"GPU top-k holds {len(idx_gpu)} entries, expected {k}"
+    for e in idx_gpu:
+        if not 0 <= e < n_exp:
+            return False, 0, f"expert {e} outside [0, {n_exp})"
     if len(set(idx_gpu)) != k:
         return False, 0, "duplicate expert in GPU top-k"
-    ties = 0
-    # every GPU pick must be at least as large as the oracle's k-th pick, up to the band
-    kth = own[-1]
-    for e in idx_gpu:
-        if e in own:
+    own = [int(e) for e in topk_order(logits_row[None, :], k)[0]]
+    if own == idx_gpu:
+        return True, 0, ""
+    kept = set(idx_gpu)
+    # every expert left out must not beat any expert kept, up to the band
+    for u in range(n_exp):
+        if u in kept:
             continue
-        if not near_tie(logits_row, scale_row, e, kth, rel):
-            return False, ties, f"expert {e} chosen outside the near-tie band"
-        ties += 1
+        for c in idx_gpu:
+            if logits_row[u] > logits_row[c] and not near_tie(logits_row, scale_row, u, c, rel):
+                return False, 0, f"expert {u} left out although it beats chosen expert {c}"
+    ties = sum(1 for e in idx_gpu if e not in own)
     # the order must be descending up to the band
     for a, b in zip(idx_gpu[:-1], idx_gpu[1:]):
         inverted = logits_row[a] < logits_row[b] or (logits_row[a] == logits_row[b] and a > b)

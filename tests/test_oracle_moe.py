@@ -138,14 +138,53 @@ def test_router_logits_loops():
     pin_router_logits(moe)
 
 
-def test_check_routing_band():
+def pin_check_routing(mm):
     row = np.array([0.0, 5.0, 4.0, 4.0 - 1e-9, 1.0])
     scale = np.full(5, 10.0)
-    assert moe.check_routing(row, scale, [1, 2], 2)[0]
-    ok, ties, _ = moe.check_routing(row, scale, [1, 3], 2)      # in band: accepted
+    assert mm.check_routing(row, scale, [1, 2], 2)[0]
+    ok, ties, _ = mm.check_routing(row, scale, [1, 3], 2)       # in band: accepted
     assert ok and ties == 1
-    assert not moe.check_routing(row, scale, [1, 4], 2)[0]       # outside band
-    assert not moe.check_routing(row, scale, [2, 1], 2)[0]       # wrong order
+    assert not mm.check_routing(row, scale, [1, 4], 2)[0]        # outside band
+    assert not mm.check_routing(row, scale, [2, 1], 2)[0]        # wrong order
+    # a list that drops a clear winner for two near-tied losers is wrong:
+    # expert 2 (logit 4) is left out although it beats the kept expert 4 by 1
+    row = np.array([0.0, 5.0, 4.0, 3.0, 3.0 - 1e-9])
+    scale = np.full(5, 10.0)
+    assert mm.check_routing(row, scale, [1, 2, 3], 3)[0]
+    assert mm.check_routing(row, scale, [1, 2, 4], 3) == (True, 1, "")
+    assert not mm.check_routing(row, scale, [1, 3, 4], 3)[0]
+    # dropping the largest logit, with the rest in band, is wrong too
+    row = np.array([10.0, 5.0, 4.0, 3.0, 3.0 + 1e-9])
+    assert not mm.check_routing(row, scale, [1, 2, 4, 3], 4)[0]
+    assert mm.check_routing(row, scale, [0, 1, 2, 4], 4)[0]
+    # indices must name experts: negative (Python would wrap) and >= E fail
+    assert not mm.check_routing(row, scale, [0, 1, 2, -1], 4)[0]
+    assert not mm.check_routing(row, scale, [0, 1, 2, 5], 4)[0]
+    # wrong length and duplicates fail
+    assert not mm.check_routing(row, scale, [0, 1, 2], 4)[0]
+    assert not mm.check_routing(row, scale, [0, 1, 1, 2], 4)[0]
+    # brute force: on random logits with planted near ties, the checker agrees
+    # with the definition "no left-out expert beats a kept one beyond the band,
+    # order descending up to the band" taken over every k-subset and order
+    import itertools
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        n_exp, k = 6, 3
+        lg = np.round(rng.standard_normal(n_exp), 1)
+        if trial % 2:
+            lg[rng.integers(n_exp)] = lg[rng.integers(n_exp)] + 1e-9
+        sc = np.full(n_exp, 10.0)
+        band = 1e-6 * 10.0
+        for cand in itertools.permutations(range(n_exp), k):
+            beats = any(lg[u] - lg[c] > band for u in range(n_exp) if u not in cand
+                        for c in cand)
+            inv = any(lg[b] - lg[a] > band for a, b in zip(cand[:-1], cand[1:]))
+            assert mm.check_routing(lg, sc, list(cand), k)[0] == (not beats and not inv), \
+                (lg, cand)
+
+
+def test_check_routing_band():
+    pin_check_routing(moe)
 
 
 # ---------------------------------------------------------------- SwiGLU / expert
@@ -373,9 +412,33 @@ def _router_dropped_term(w_r, xin, bias=None):
     return lg, sc
 
 
+def _check_routing_kth_only(logits_row, scale_row, idx_gpu, k, rel=moe.NEAR_TIE_REL):
+    # compares each pick the oracle did not make with the oracle's k-th pick
+    # only, so a list that drops a larger logit passes
+    own = list(moe.topk_order(np.asarray(logits_row)[None, :], k)[0])
+    idx_gpu = [int(e) for e in idx_gpu]
+    if own == idx_gpu:
+        return True, 0, ""
+    if len(set(idx_gpu)) != k:
+        return False, 0, "dup"
+    for e in idx_gpu:
+        if e not in own and not moe.near_tie(logits_row, scale_row, e, own[-1], rel):
+            return False, 0, "band"
+    for a, b in zip(idx_gpu[:-1], idx_gpu[1:]):
+        if logits_row[a] < logits_row[b] and not moe.near_tie(logits_row, scale_row, a, b, rel):
+            return False, 0, "order"
+    return True, 1, ""
+
+
+def _check_routing_no_range(logits_row, scale_row, idx_gpu, k, rel=moe.NEAR_TIE_REL):
+    # negative indices wrap in Python indexing and pass unnoticed
+    idx = [int(e) % len(logits_row) for e in idx_gpu]
+    return moe.check_routing(logits_row, scale_row, idx, k, rel)
+
+
 @pytest.mark.parametrize("which", [
     "gemv_T", "gemv_den", "ties_high", "full_softmax", "gu_swap", "silu_sign",
-    "norm_eps", "router_bias",
+    "norm_eps", "router_bias", "routing_kth_only", "routing_no_range",
 ])
 def test_planted_mistake_is_caught(which):
     with pytest.raises(AssertionError):
@@ -395,3 +458,7 @@ def test_planted_mistake_is_caught(which):
             pin_rmsnorm(NS(moe, rmsnorm=_rmsnorm_no_eps))
         elif which == "router_bias":
             pin_router_logits(NS(moe, router_logits=_router_dropped_term))
+        elif which == "routing_kth_only":
+            pin_check_routing(NS(moe, check_routing=_check_routing_kth_only))
+        elif which == "routing_no_range":
+            pin_check_routing(NS(moe, check_routing=_check_routing_no_range))
