@@ -24,6 +24,8 @@ BDG_FMT_INT4G = 1
 BDG_ROUTER_RMSNORM = 1
 BDG_MOE_STACK = 1
 BDG_MOE_NO_GRAPH = 2
+BDG_MOE_ROUTE_EVERY_LAYER = 4
+BDG_MOE_PER_TOKEN = 8
 BDG_MAX_M = 16
 
 # every symbol include/bdg.h declares

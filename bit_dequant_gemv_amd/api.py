@@ -11,7 +11,8 @@ import torch
 
 from . import _lib
 from ._lib import (BDG_BF16, BDG_F32, BDG_FMT_INT4G, BDG_FMT_MXFP4, BDG_MOE_NO_GRAPH,
-                   BDG_MOE_STACK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, Rope, check)
+                   BDG_MOE_PER_TOKEN, BDG_MOE_ROUTE_EVERY_LAYER, BDG_MOE_STACK, BDG_ROUTER_RMSNORM,
+                   LayerDesc, MoEDesc, QMat, Rope, check)
 
 
 def _stream():
@@ -28,6 +29,14 @@ def _dev_ptr(t, name, dtype=None):
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor t has exactly this shape."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def _x_dtype(x):
@@ -56,6 +65,14 @@ class QWeight:
         self.k = 2 * codes.shape[-1]
         self.batched = codes.dim() == 3
         self.n_experts = codes.shape[0] if self.batched else 1
+        if codes.dim() not in (2, 3):
+            raise ValueError("codes must be [n][k/2] or [E][n][k/2]")
+        lead = tuple(codes.shape[:-1])
+        if self.k % 32 or self.k % self.group:
+            raise ValueError("k must be a multiple of 32 and of the group size")
+        _shape(scales, lead + (self.k // self.group,), "scales")
+        if fmt == "int4g":
+            _shape(zeros, lead + ((self.k // self.group + 1) // 2,), "zeros")
         _dev_ptr(codes, "codes", torch.uint8)
         _dev_ptr(scales, "scales", torch.uint8 if fmt == "mxfp4" else torch.int16)
         if fmt == "int4g":
@@ -75,6 +92,7 @@ class QWeight:
 
 def mxfp4_dequant(codes, scales, out_dtype=torch.float32):
     n, half_k = codes.shape
+    _shape(scales, (n, 2 * half_k // 32), "scales")
     out = torch.empty((n, 2 * half_k), dtype=out_dtype, device=codes.device)
     odt = BDG_F32 if out_dtype == torch.float32 else BDG_BF16
     if out_dtype not in (torch.float32, torch.bfloat16):
@@ -87,6 +105,11 @@ def mxfp4_dequant(codes, scales, out_dtype=torch.float32):
 
 def int4g_dequant(codes, scales, zeros, group):
     n, half_k = codes.shape
+    group = int(group)
+    if group <= 0 or (2 * half_k) % group:
+        raise ValueError("k must be a multiple of the group size")
+    _shape(scales, (n, 2 * half_k // group), "scales")
+    _shape(zeros, (n, (2 * half_k // group + 1) // 2), "zeros")
     out = torch.empty((n, 2 * half_k), dtype=torch.float32, device=codes.device)
     check("int4g_dequant", _lib.load().int4g_dequant(
         _dev_ptr(codes, "codes", torch.uint8), _dev_ptr(scales, "scales", torch.int16),
@@ -102,6 +125,8 @@ def qgemv(w: QWeight, x, out=None):
     m = x2.shape[0]
     if x2.shape[1] != w.k:
         raise ValueError("x and W disagree on K")
+    if out is not None:
+        _shape(out, (m, w.n), "out")
     y = out if out is not None else torch.empty((m, w.n), dtype=torch.float32, device=x.device)
     qm = w.qmat()
     check("qgemv", _lib.load().qgemv(ctypes.byref(qm), _dev_ptr(x2, "x"), _x_dtype(x2), m,
@@ -114,10 +139,14 @@ def mxfp8_quantize(x, codes=None, scales=None):
     (codes uint8 [m][k], scales uint8 [m][k/32])."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     m, k = x2.shape
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
     if codes is None:
         codes = torch.empty((m, k), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _shape(codes, (m, k), "codes")
+    _shape(scales, (m, k // 32), "scales")
     check("mxfp8_quantize", _lib.load().mxfp8_quantize(
         _dev_ptr(x2, "x"), _x_dtype(x2), m, k, _dev_ptr(codes, "codes", torch.uint8),
         _dev_ptr(scales, "scales", torch.uint8), _stream()))
@@ -128,8 +157,10 @@ def mx_gemm(w: QWeight, codes, scales, out=None):
     """y [m][n] = W xq^T for MXFP4 W [n][k] and MXFP8 activations (codes [m][k],
     scales [m][k/32]) on the MX-scaled matrix cores."""
     m = codes.shape[0]
-    if codes.shape[1] != w.k or scales.shape != (m, w.k // 32):
+    if codes.dim() != 2 or codes.shape[1] != w.k or tuple(scales.shape) != (m, w.k // 32):
         raise ValueError("activation shapes do not match W")
+    if out is not None:
+        _shape(out, (m, w.n), "out")
     y = out if out is not None else torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
     qm = w.qmat()
     check("mx_gemm", _lib.load().mx_gemm(ctypes.byref(qm), _dev_ptr(codes, "codes", torch.uint8),
@@ -150,9 +181,19 @@ def moe_prefill_mx(layer, n_experts, top_k, x, y=None, workspace=None):
     m, hid = x2.shape
     gu, dn = layer["gate_up"], layer["down"]
     inter = dn.k
+    if gu.k != hid or gu.n != 2 * inter or dn.n != hid:
+        raise ValueError("gate_up must be [E][2I][H] and down [E][H][I] for x [m][H]")
+    if gu.n_experts != n_experts or dn.n_experts != n_experts:
+        raise ValueError("expert batches must hold n_experts matrices")
+    _shape(layer["w_router"], (n_experts, hid), "w_router")
+    _shape(layer.get("b_router"), (n_experts,), "b_router")
+    if y is not None:
+        _shape(y, (m, hid), "y")
     need = prefill_workspace_bytes(m, hid, inter, n_experts, top_k)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
     if y is None:
         y = torch.empty((m, hid), dtype=torch.float32, device=x.device)
     idx = torch.empty((m, top_k), dtype=torch.int32, device=x.device)
@@ -252,12 +293,20 @@ def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, wi
     cdt = {torch.bfloat16: BDG_BF16, torch.float32: BDG_F32}.get(k_cache.dtype)
     if cdt is None:
         raise ValueError("caches must be bfloat16 or float32")
+    if q.dim() != 3 or k_cache.dim() != 3 or k_cache.shape[2] != d:
+        raise ValueError("q must be [m][n_heads][head_dim] and caches [n_kv_heads][cap][head_dim]")
+    if table.dim() != 2 or table.shape[1] != d:
+        raise ValueError("table must be [positions][head_dim]")
+    _shape(sinks, (hq,), "sinks")
+    _shape(o, (m, hq, d), "o")
     cap = k_cache.shape[1]
     last = pos0 + m
     max_keys = min(window, last) if window > 0 else last
     need = attn_decode_workspace_bytes(hq, hkv, d, m, max_keys)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
     if o is None:
         o = torch.empty((m, hq, d), dtype=torch.float32, device=q.device)
     check("attn_decode", _lib.load().attn_decode(
@@ -275,6 +324,10 @@ def moe_router_topk(x, w_r, b_r=None, topk=4, rmsnorm=False, eps=1e-5):
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     m, h = x2.shape
     e = w_r.shape[0]
+    _shape(w_r, (e, h), "w_r")
+    _shape(b_r, (e,), "b_r")
+    if not 1 <= topk <= e:
+        raise ValueError("need 1 <= topk <= number of experts")
     idx = torch.empty((m, topk), dtype=torch.int32, device=x.device)
     wts = torch.empty((m, topk), dtype=torch.float32, device=x.device)
     logits = torch.empty((m, e), dtype=torch.float32, device=x.device)
@@ -295,7 +348,8 @@ class MoEPlan:
     """
 
     def __init__(self, layers, hidden, inter, n_experts, top_k, fmt="mxfp4", group=32,
-                 stack=True, norm_eps=1e-5, max_m=1, use_graph=True):
+                 stack=True, norm_eps=1e-5, max_m=1, use_graph=True, route_every_layer=False,
+                 per_token=False):
         self._layers = layers
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.n_layers = len(layers)
@@ -303,12 +357,21 @@ class MoEPlan:
         self.max_m = max_m
         arr = (LayerDesc * len(layers))()
         for i, L in enumerate(layers):
+            gu, dn = L["gate_up"], L["down"]
+            if gu.n != 2 * inter or gu.k != hidden or dn.n != hidden or dn.k != inter:
+                raise ValueError(f"layer {i}: gate_up must be [E][2I][H] and down [E][H][I]")
+            if gu.n_experts != n_experts or dn.n_experts != n_experts:
+                raise ValueError(f"layer {i}: expert batches must hold n_experts matrices")
+            _shape(L["w_router"], (n_experts, hidden), f"layer {i} w_router")
+            _shape(L.get("b_router"), (n_experts,), f"layer {i} b_router")
             arr[i].w_router = _dev_ptr(L["w_router"], "w_router", torch.float32).value
             b = L.get("b_router")
             arr[i].b_router = _dev_ptr(b, "b_router", torch.float32).value if b is not None else None
             arr[i].gate_up = L["gate_up"].qmat()
             arr[i].down = L["down"].qmat()
-        flags = (BDG_MOE_STACK if stack else 0) | (0 if use_graph else BDG_MOE_NO_GRAPH)
+        flags = ((BDG_MOE_STACK if stack else 0) | (0 if use_graph else BDG_MOE_NO_GRAPH)
+                 | (BDG_MOE_ROUTE_EVERY_LAYER if route_every_layer else 0)
+                 | (BDG_MOE_PER_TOKEN if per_token else 0))
         desc = MoEDesc(n_layers=len(layers), hidden=hidden, inter=inter, n_experts=n_experts,
                        top_k=top_k, fmt=BDG_FMT_MXFP4 if fmt == "mxfp4" else BDG_FMT_INT4G,
                        group=32 if fmt == "mxfp4" else group, flags=flags,
@@ -344,8 +407,12 @@ def moe_expert_decode(plan: MoEPlan, x, y=None, traces=False):
     """
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     m = x2.shape[0]
+    _shape(x2, (m, plan.hidden), "x")
+    if not 1 <= m <= plan.max_m:
+        raise ValueError(f"m must be in [1, {plan.max_m}] (the plan's max_m)")
     if y is None:
         y = torch.empty((m, plan.hidden), dtype=torch.float32, device=x.device)
+    _shape(y, (m, plan.hidden), "y")
     tr = None
     if traces:
         L, k, H = plan.n_layers, plan.top_k, plan.hidden
@@ -364,8 +431,16 @@ def moe_experts_routed(plan: MoEPlan, layer, x, idx, wts, y=None):
     """Experts of one layer with fixed routing: y[t] = sum_j wts[t][j] FFN_{idx[t][j]}(x[t])."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     m = x2.shape[0]
+    _shape(x2, (m, plan.hidden), "x")
+    if not 1 <= m <= plan.max_m:
+        raise ValueError(f"m must be in [1, {plan.max_m}] (the plan's max_m)")
+    _shape(idx, (m, plan.top_k), "idx")
+    _shape(wts, (m, plan.top_k), "wts")
+    if not 0 <= int(layer) < plan.n_layers:
+        raise ValueError("layer out of range")
     if y is None:
         y = torch.empty((m, plan.hidden), dtype=torch.float32, device=x.device)
+    _shape(y, (m, plan.hidden), "y")
     check("moe_experts_routed", _lib.load().moe_experts_routed(
         plan.handle, int(layer), _dev_ptr(x2, "x"), _x_dtype(x2), m,
         _dev_ptr(idx, "idx", torch.int32), _dev_ptr(wts, "wts", torch.float32),
@@ -380,6 +455,10 @@ def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None)
     """One decode step with per-kernel start/stop events; accumulates into
     acc_ms / acc_count (ctypes double[4] / int64[4]) and returns them."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    _shape(x2, (x2.shape[0], plan.hidden), "x")
+    _shape(y, (x2.shape[0], plan.hidden), "y")
+    if not 1 <= x2.shape[0] <= plan.max_m:
+        raise ValueError(f"m must be in [1, {plan.max_m}] (the plan's max_m)")
     if acc_ms is None:
         acc_ms = (ctypes.c_double * 4)()
         acc_count = (ctypes.c_int64 * 4)()

@@ -31,6 +31,8 @@ inline int check_qmat(const bdg_qmat* w, bool need_expert_strides) {
     return BDG_E_INVALID;
   }
   if (!aligned16(w->codes)) return BDG_E_ALIGN;
+  // the kernels address one matrix (one expert) with 32-bit byte offsets
+  if (w->n > (int64_t)0xFFFFFFFF / (w->k / 2)) return BDG_E_UNSUPPORTED;
   if (need_expert_strides) {
     if (w->expert_stride_codes < 0 || (w->expert_stride_codes & 15) != 0) return BDG_E_ALIGN;
     if (w->expert_stride_scales < 0 || w->expert_stride_zeros < 0) return BDG_E_INVALID;

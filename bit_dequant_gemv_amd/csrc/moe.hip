@@ -1036,6 +1036,7 @@ struct GraphEntry {
   GraphKey key{};
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;   // recorded after each launch of exec, on the launching stream
 };
 
 }  // namespace bdg
@@ -1072,15 +1073,6 @@ struct bdg_plan {
 };
 
 namespace bdg {
-
-static int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  int x = atoi(v);
-  if (x < lo) x = lo;
-  if (x > hi) x = hi;
-  return x;
-}
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1408,7 +1400,13 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
   return BDG_OK;
 }
 
+// Destroy a cached graph once its last launch has finished, on whichever
+// stream that launch was queued.
 static void drop_graph(GraphEntry& g) {
+  if (g.done) {
+    (void)hipEventSynchronize(g.done);
+    (void)hipEventDestroy(g.done);
+  }
   if (g.exec) (void)hipGraphExecDestroy(g.exec);
   if (g.graph) (void)hipGraphDestroy(g.graph);
   g = GraphEntry{};
@@ -1425,8 +1423,12 @@ static int check_layer(const bdg_moe_desc* d, const bdg_layer_desc& L) {
   }
   if (L.gate_up.n != 2LL * d->inter || L.gate_up.k != d->hidden) return BDG_E_INVALID;
   if (L.down.n != d->hidden || L.down.k != d->inter) return BDG_E_INVALID;
-  if (d->n_experts > 1 && (L.gate_up.expert_stride_codes == 0 || L.down.expert_stride_codes == 0))
-    return BDG_E_INVALID;
+  if (d->n_experts > 1) {
+    for (int i = 0; i < 2; ++i) {
+      if (mats[i]->expert_stride_codes == 0 || mats[i]->expert_stride_scales == 0) return BDG_E_INVALID;
+      if (mats[i]->fmt == BDG_FMT_INT4G && mats[i]->expert_stride_zeros == 0) return BDG_E_INVALID;
+    }
+  }
   return BDG_OK;
 }
 
@@ -1442,7 +1444,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     return BDG_E_INVALID;
   if (d->fmt != BDG_FMT_MXFP4 && d->fmt != BDG_FMT_INT4G) return BDG_E_INVALID;
   if ((d->hidden % 32) || (d->inter % 32)) return BDG_E_INVALID;
-  if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH)) != 0) return BDG_E_INVALID;
+  if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH | BDG_MOE_ROUTE_EVERY_LAYER | BDG_MOE_PER_TOKEN)) != 0)
+    return BDG_E_INVALID;
   if ((d->flags & BDG_MOE_STACK) && !(d->norm_eps >= 0.f)) return BDG_E_INVALID;
   if (d->top_k > BDG_MAX_TOPK || d->n_experts > BDG_MAX_EXPERTS || d->max_m > BDG_MAX_M)
     return BDG_E_UNSUPPORTED;
@@ -1477,14 +1480,14 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     int nr = (d->hidden + 256 * rpw * wpe - 1) / (256 * rpw * wpe);
     if (nr < 1) nr = 1;
     if (nr > 4) nr = 4;
-    p->dn_NR = env_int("BDG_DN_NR", nr, 1, 4);
+    p->dn_NR = nr;
     const int B = p->dn_NR * rpw * wpe;
     p->dn_blocks = (d->hidden + B - 1) / B;
     // a layer routes from the previous down kernel's partial sums when the
     // sums are small enough for every gate_up block to add them up
     p->fuse_route = (d->flags & BDG_MOE_STACK) && d->n_layers > 1 && B <= kWave &&
                     p->dn_blocks <= 4 * kThreads && d->n_experts <= kDownWaves * kDnRouterPerWave &&
-                    env_int("BDG_FUSE_ROUTE", 1, 0, 1);
+                    !(d->flags & BDG_MOE_ROUTE_EVERY_LAYER);
     int lt = 0;
     while (lt < 6 && (d->n_experts << (lt + 1)) <= kThreads) ++lt;
     p->log2T = lt;
@@ -1517,7 +1520,7 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     p->group_ok = d->max_m * d->top_k <= kGroupMaxPicks && d->inter <= 4096 && p->dn_L * p->dn_S <= 128 &&
                   p->gu_S <= (d->fmt == BDG_FMT_MXFP4 ? 3 : 2) &&
                   lds_gu <= 64 * 1024 &&
-                  lds_dn <= 64 * 1024 && env_int("BDG_GROUP", 1, 0, 1);
+                  lds_dn <= 64 * 1024 && !(d->flags & BDG_MOE_PER_TOKEN);
   }
   auto geom = [&](int k) {
     QGeom g;
@@ -1671,11 +1674,7 @@ extern "C" int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, in
       if (!p->graphs[i].used) { slot = &p->graphs[i]; break; }
       if (p->graphs[i].stamp < slot->stamp) slot = &p->graphs[i];
     }
-    if (slot->used) {
-      // the evicted graph may still be queued: let it finish before destroying
-      (void)hipStreamSynchronize(s);
-      drop_graph(*slot);
-    }
+    if (slot->used) drop_graph(*slot);   // waits for that graph's last launch only
     if (hipStreamBeginCapture(p->cap_stream, hipStreamCaptureModeRelaxed) != hipSuccess) return BDG_E_HIP;
     int st = enqueue_decode(p, key, p->cap_stream);
     hipGraph_t graph = nullptr;
@@ -1689,14 +1688,22 @@ extern "C" int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, in
       (void)hipGraphDestroy(graph);
       return BDG_E_HIP;
     }
+    hipEvent_t done = nullptr;
+    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGraphExecDestroy(exec);
+      (void)hipGraphDestroy(graph);
+      return BDG_E_HIP;
+    }
     slot->used = true;
     slot->key = key;
     slot->graph = graph;
     slot->exec = exec;
+    slot->done = done;
     hit = slot;
   }
   hit->stamp = ++p->clock;
-  return hip_status(hipGraphLaunch(hit->exec, s));
+  if (hipGraphLaunch(hit->exec, s) != hipSuccess) return BDG_E_HIP;
+  return hip_status(hipEventRecord(hit->done, s));
 }
 
 extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int32_t x_dtype, int32_t m,

@@ -31,7 +31,9 @@
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Calls only enqueue work on it and never synchronise, except
  *     moe_plan_create / moe_plan_destroy, which may allocate, free and
- *     synchronise.
+ *     synchronise, moe_expert_decode_profiled (it reads its timing events),
+ *     and moe_expert_decode when a new key evicts a cached graph (it waits
+ *     for that graph's last launch).
  *   - Return value: BDG_OK (0) or a negative BDG_E_* status.  Argument
  *     errors are found on the host before anything is enqueued, and leave
  *     outputs untouched.  Faults inside kernels surface at the caller's next
@@ -82,7 +84,8 @@ extern "C" {
 #define BDG_MAX_TOPK 32
 
 /* A packed low-bit matrix [n][k] in the PLAIN layout, optionally one of a
- * batch of experts laid out at fixed byte strides. */
+ * batch of experts laid out at fixed byte strides.  One matrix (one expert)
+ * holds at most 2^32 code bytes (n * k / 2; BDG_E_UNSUPPORTED beyond). */
 typedef struct bdg_qmat {
   int32_t fmt;     /* BDG_FMT_MXFP4 or BDG_FMT_INT4G */
   int32_t group;   /* MXFP4: 32; INT4G: group size, a multiple of 32 */
@@ -150,10 +153,20 @@ typedef struct bdg_layer_desc {
   bdg_qmat down;
 } bdg_layer_desc;
 
-/* flags for bdg_moe_desc.flags */
+/* flags for bdg_moe_desc.flags.  Every choice of the plan is made here, at
+ * create time, from the descriptor alone (no environment variables): the
+ * per-session setup of the host-sync page (section 3) is keyed on the
+ * geometry, and a change needs a new plan. */
 #define BDG_MOE_STACK 1      /* x <- x + MoE(RMSNorm(x)) per layer; else bare layers: x <- MoE(x) */
 #define BDG_MOE_NO_GRAPH 2   /* launch the per-token kernels directly instead of replaying a graph
                                 (same kernels, same results; for A/B checks) */
+#define BDG_MOE_ROUTE_EVERY_LAYER 4  /* route every layer of an m = 1 stack with its own router
+                                        kernel instead of from partial sums written by the
+                                        previous layer's down kernel (same selection rule;
+                                        logits differ only in fp32 summation order) */
+#define BDG_MOE_PER_TOKEN 8  /* steps of m > 1 tokens run the per-token kernels (each pick reads
+                                its expert) instead of the grouped kernels (each distinct
+                                expert read once per step); same results bit for bit */
 
 typedef struct bdg_moe_desc {
   int32_t n_layers;
@@ -184,12 +197,19 @@ typedef struct bdg_plan bdg_plan;
  * fails. */
 int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out);
 
-/* moe_plan_destroy - free a plan and everything it allocated; waits for
- * work queued on its internal stream.  NULL is accepted. */
+/* moe_plan_destroy - free a plan and everything it allocated (the end of
+ * the session whose setup moe_plan_create built; host-sync page, section 3).
+ * Waits for the device to finish queued work first, since captured graphs
+ * and the workspace may still be in use.  NULL is accepted.  Returns BDG_OK. */
 int moe_plan_destroy(bdg_plan* p);
 
 /* moe_expert_decode - one decode step of m tokens through every layer of
- * the plan.  x [m][H] of x_dtype (device) is the input hidden state; y [m][H]
+ * the plan: per layer the router, top-k + softmax, the chosen experts'
+ * gate_up dequant-GEMV + SwiGLU and down dequant-GEMV, and the weighted
+ * combine (the per-token expert path of the gpt-oss page, section 3, with
+ * the k experts of a layer run together as its section 5 proposes and the
+ * tracker's entry D114 does; the all-layer decode of one submission per
+ * token of the host-sync page, section 3).  x [m][H] of x_dtype (device) is the input hidden state; y [m][H]
  * fp32 (device) receives the output: for a stack, the residual stream after
  * the last layer; for a bare layer, the combine sum_j w_j * down_j(h_j).
  * Optional device traces (NULL to skip): topk_trace [L][m][k] int32 with
@@ -197,15 +217,22 @@ int moe_plan_destroy(bdg_plan* p);
  * resid_trace [L][m][H] fp32 with each layer's input residual (stack) or
  * input (bare layer).  The per-token path is replayed from a captured HIP
  * graph keyed on (x, y, traces, m, x_dtype), captured at the first call with
- * that key (a cache of 8 graphs, least recently used evicted).  x, y and
- * resid_trace must be 16-byte aligned.  A plan is not re-entrant: calls on
- * one plan must be ordered on one stream. */
+ * that key (a cache of 8 graphs, least recently used evicted).  The first
+ * call with a new key captures and instantiates (host work, no device
+ * synchronisation); when that evicts a cached graph, the call first waits
+ * on the host for the evicted graph's last launch to finish (an event
+ * recorded on whichever stream launched it), then destroys it.  Other calls
+ * only enqueue.  x, y and resid_trace must be 16-byte aligned.  m > max_m is
+ * BDG_E_INVALID.  A plan is not re-entrant: calls on one plan must not run
+ * concurrently (they share its workspace). */
 int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
                       int32_t* topk_trace, float* wts_trace, float* resid_trace, void* stream);
 
 /* moe_experts_routed - the expert part of one layer with caller-fixed
  * routing: y[t] = sum_j wts[t][j] * FFN_{idx[t][j]}(x[t]) (no router, no
- * norm, no residual).  Runs the same grouped gate_up/SwiGLU and down kernels
+ * norm, no residual): the "4 sequential experts x 2 GEMVs" of the gpt-oss
+ * page (section 3) for routing the caller fixes, e.g. duplicate or skewed
+ * picks.  Runs the same grouped gate_up/SwiGLU and down kernels
  * as moe_expert_decode.  x [m][H] of x_dtype, idx [m][k] int32 in [0, E),
  * wts [m][k] fp32, y [m][H] fp32, all device.  Expert ids are not range
  * checked on the host (they live on the device): out-of-range ids are
@@ -366,7 +393,9 @@ int bdg_stream_read(const void* buf, int64_t bytes, float* sink, int32_t n_block
  * 16-byte loads/stores; a kernel of known traffic for calibrating counters. */
 int bdg_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
-/* bdg_strerror - static text for a status code. */
+/* bdg_strerror - static text for a status code (any int; unknown codes get
+ * a generic text).  Host only, never fails; the text is owned by the
+ * library. */
 const char* bdg_strerror(int32_t status);
 
 /* bdg_version - library version string. */

@@ -177,3 +177,45 @@ def moe_layer_mx(x, w_r, get_expert_packed, k, bias=None, forced_idx=None):
         y[toks] += wt * (hq @ w_d.T)
         den[toks] += np.abs(wt) * (np.abs(hq) @ np.abs(w_d).T)
     return dict(y=y, den=den, idx=idx, w=w, logits=logits, scale=scale, ties=ties)
+
+
+def mxfp8_requant_spread(h, herr):
+    """Largest change of the MXFP8 quantization of h (rows along the last axis)
+    over all h' with |h' - h| <= herr elementwise: spread[i] = max |MXFP8(h')_i
+    - MXFP8(h)_i| (dequantized, float64).
+
+    Used where h is computed with a bounded error (here by matrix cores that
+    sum at reduced precision) before it is quantized: the quantization of the
+    computed h may then differ from the exact h's.  Worst case taken from the
+    conversion steps above:
+    * a block's amax' lies in [max_i (|h_i| - herr_i)+, max_i (|h_i| + herr_i)],
+      so its exponent X' takes every value floor_log2 gives on that range;
+    * at a fixed X', rounding to nearest (any tie rule) with saturation is
+      monotone, so an element's code lies between the codes of
+      (h_i - herr_i) / 2^X' and (h_i + herr_i) / 2^X'.
+    Finite inputs only.
+    """
+    h = np.atleast_2d(np.asarray(h, dtype=np.float64))
+    herr = np.broadcast_to(np.asarray(herr, dtype=np.float64), h.shape)
+    m, k = h.shape
+    if k % MX_BLOCK:
+        raise ValueError("MXFP8: k must be a multiple of 32")
+    hc, hs = mxfp8_quantize(h)
+    hq = mxfp8_dequant64(hc, hs).reshape(m, k // MX_BLOCK, MX_BLOCK)
+    hb = h.reshape(m, k // MX_BLOCK, MX_BLOCK)
+    eb = herr.reshape(m, k // MX_BLOCK, MX_BLOCK)
+    lo_v, hi_v = hb - eb, hb + eb
+    amax_lo = np.max(np.maximum(np.abs(hb) - eb, 0.0), axis=2)
+    amax_hi = np.max(np.abs(hb) + eb, axis=2)
+
+    def xexp(a):
+        return np.where(a > 0, np.clip(floor_log2(np.where(a > 0, a, 1.0)) - E4M3_EMAX, -127, 127), -127)
+    x_lo, x_hi = xexp(amax_lo), xexp(amax_hi)
+    spread = np.zeros_like(hb)
+    for d in range(int(np.max(x_hi - x_lo)) + 1):
+        X = np.minimum(x_lo + d, x_hi)                   # every exponent in [x_lo, x_hi]
+        sc = np.ldexp(1.0, X.astype(np.int64))[:, :, None]
+        q_lo = e4m3_value(e4m3_round(lo_v / sc)) * sc
+        q_hi = e4m3_value(e4m3_round(hi_v / sc)) * sc
+        spread = np.maximum(spread, np.maximum(np.abs(q_lo - hq), np.abs(q_hi - hq)))
+    return spread.reshape(m, k)

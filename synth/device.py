@@ -49,14 +49,15 @@ def upload_layer(cfg, layer, device, threads=8, experts=None):
     )
 
 
-def build_plan(cfg, device, n_layers=None, max_m=None, use_graph=True, threads=8, layers=None):
-    """(plan, layer tensors) for the first n_layers layers of cfg."""
+def build_plan(cfg, device, n_layers=None, max_m=None, use_graph=True, threads=8, layers=None, **plan_opts):
+    """(plan, layer tensors) for the first n_layers layers of cfg; plan_opts
+    go to MoEPlan (route_every_layer, per_token)."""
     n_layers = cfg.n_layers if n_layers is None else n_layers
     if layers is None:
         layers = [upload_layer(cfg, l, device, threads) for l in range(n_layers)]
     plan = MoEPlan(layers, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, fmt=cfg.fmt,
                    group=cfg.group, stack=cfg.norm, norm_eps=1e-5,
-                   max_m=max_m if max_m is not None else cfg.m, use_graph=use_graph)
+                   max_m=max_m if max_m is not None else cfg.m, use_graph=use_graph, **plan_opts)
     return plan, layers
 
 

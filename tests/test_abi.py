@@ -110,3 +110,98 @@ def test_null_arguments_are_rejected(name):
     nargs = len(fn.argtypes)
     zero = [None if t is ctypes.c_void_p or issubclass(t, ctypes._Pointer) else 0 for t in fn.argtypes]
     assert fn(*zero[:nargs]) == _lib.BDG_E_INVALID
+
+
+def _plan_desc(k=4, E=32, H=2880, I=2880, L=1, max_m=1, flags=0, mutate=None):
+    """A plan descriptor over fake device addresses (never dereferenced: every
+    case below fails its host checks before any HIP call)."""
+    layers = (_lib.LayerDesc * L)()
+    for l in range(L):
+        base = 0x100000000 * (l + 1)
+
+        def qmat(n, kk, off):
+            return _lib.QMat(fmt=_lib.BDG_FMT_MXFP4, group=32, n=n, k=kk, codes=base + off,
+                             scales=base + off + 0x40000000, zeros=None,
+                             expert_stride_codes=n * kk // 2, expert_stride_scales=n * kk // 32,
+                             expert_stride_zeros=0)
+        layers[l].w_router = base
+        layers[l].b_router = None
+        layers[l].gate_up = qmat(2 * I, H, 0x1000000)
+        layers[l].down = qmat(H, I, 0x8000000)
+    if mutate:
+        mutate(layers)
+    return _lib.MoEDesc(n_layers=L, hidden=H, inter=I, n_experts=E, top_k=k, fmt=_lib.BDG_FMT_MXFP4,
+                        group=32, flags=flags, norm_eps=1e-5, max_m=max_m, layers=layers), layers
+
+
+def _create(desc):
+    lib = _lib.load()
+    handle = ctypes.c_void_p()
+    st = lib.moe_plan_create(ctypes.byref(desc), ctypes.byref(handle))
+    assert handle.value is None, "a rejected plan must not be returned"
+    return st
+
+
+def test_plan_create_rejects_arguments_before_any_allocation():
+    lib = _lib.load()
+    assert lib.moe_plan_create(None, None) == _lib.BDG_E_INVALID
+    d, _ = _plan_desc(k=33, E=32)
+    assert _create(d) == _lib.BDG_E_INVALID                 # k > E
+    d, _ = _plan_desc(k=0)
+    assert _create(d) == _lib.BDG_E_INVALID                 # k < 1
+    d, _ = _plan_desc(max_m=0)
+    assert _create(d) == _lib.BDG_E_INVALID
+    d, _ = _plan_desc(max_m=17)
+    assert _create(d) == _lib.BDG_E_UNSUPPORTED             # past BDG_MAX_M
+    d, _ = _plan_desc(H=2890)
+    assert _create(d) == _lib.BDG_E_INVALID                 # H % 32
+    d, _ = _plan_desc(flags=64)
+    assert _create(d) == _lib.BDG_E_INVALID                 # unknown flag
+
+    def zero_stride_codes(ls):
+        ls[0].gate_up.expert_stride_codes = 0
+    d, _ = _plan_desc(mutate=zero_stride_codes)
+    assert _create(d) == _lib.BDG_E_INVALID                 # experts would alias
+
+    def zero_stride_scales(ls):
+        ls[0].down.expert_stride_scales = 0
+    d, _ = _plan_desc(mutate=zero_stride_scales)
+    assert _create(d) == _lib.BDG_E_INVALID
+
+    def misaligned_codes(ls):
+        ls[0].down.codes += 8
+    d, _ = _plan_desc(mutate=misaligned_codes)
+    assert _create(d) == _lib.BDG_E_ALIGN
+
+    def misaligned_stride(ls):
+        ls[0].gate_up.expert_stride_codes += 4
+    d, _ = _plan_desc(mutate=misaligned_stride)
+    assert _create(d) == _lib.BDG_E_ALIGN
+
+    def wrong_shape(ls):
+        ls[0].down.n = 2848
+    d, _ = _plan_desc(mutate=wrong_shape)
+    assert _create(d) == _lib.BDG_E_INVALID
+
+    def no_router(ls):
+        ls[0].w_router = None
+    d, _ = _plan_desc(mutate=no_router)
+    assert _create(d) == _lib.BDG_E_INVALID
+
+
+def test_decode_calls_reject_a_null_plan():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_expert_decode(None, fake, 0, 1, fake, None, None, None, None) == _lib.BDG_E_INVALID
+    assert lib.moe_experts_routed(None, 0, fake, 0, 1, fake, fake, fake, None) == _lib.BDG_E_INVALID
+    assert lib.moe_plan_destroy(None) == _lib.BDG_OK
+
+
+def test_qgemv_rejects_matrices_past_32_bit_offsets():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    # 2^21 rows x 4096 columns: 2^32 code bytes, one past what 32-bit offsets reach
+    big = _lib.QMat(fmt=_lib.BDG_FMT_MXFP4, group=32, n=1 << 21, k=4096, codes=0x100000000,
+                    scales=0x200000000, zeros=None, expert_stride_codes=0, expert_stride_scales=0,
+                    expert_stride_zeros=0)
+    assert lib.qgemv(ctypes.byref(big), fake, 0, 1, fake, None) == _lib.BDG_E_UNSUPPORTED

@@ -53,8 +53,8 @@ def small_cfg(fmt, base, E=8, k=2, H=320, I=96, L=1, stack=False, m=3, group=64)
                            inter=I, n_experts=E, top_k=k, group=group, norm=stack, m=m)
 
 
-def run_and_check(cfg, dev, m, use_graph=True, tokens=None):
-    plan, layers = sdev.build_plan(cfg, dev, max_m=m, use_graph=use_graph)
+def run_and_check(cfg, dev, m, use_graph=True, tokens=None, **plan_opts):
+    plan, layers = sdev.build_plan(cfg, dev, max_m=m, use_graph=use_graph, **plan_opts)
     tokens = list(range(m)) if tokens is None else tokens
     x, xv = sdev.hidden_device(cfg, tokens, dev)
     banner(f"moe_expert_decode {cfg.name} fmt={cfg.fmt} L={cfg.n_layers} E={cfg.n_experts} "
@@ -89,15 +89,13 @@ def route_launches(plan, x):
 @pytest.mark.parametrize("fuse", ["1", "0"])
 @pytest.mark.parametrize("E", [16, 96])
 @pytest.mark.parametrize("m", [1, 2])
-def test_stack_small_end_to_end(dev, fmt, fuse, E, m, monkeypatch):
+def test_stack_small_end_to_end(dev, fmt, fuse, E, m):
     """The per-token path of a 3-layer stack.  fuse=1: for E <= 64, layers
     after the first route from the partial router sums of the previous down
     kernel; E = 96 (more router rows than the down epilogue covers) and
     fuse=0: every layer runs the route kernel."""
-    monkeypatch.setenv("BDG_FUSE_ROUTE", fuse)
-    monkeypatch.setenv("BDG_GROUP", "0")
     cfg = small_cfg(fmt, 1100 + E, E=E, k=4, H=512, I=256, L=3, stack=True, m=m)
-    plan, layers, x, y, tr = run_and_check(cfg, dev, m)
+    plan, layers, x, y, tr = run_and_check(cfg, dev, m, route_every_layer=fuse == "0", per_token=True)
     assert route_launches(plan, x) == (1 if fuse == "1" and E <= 64 else cfg.n_layers)
     # end to end without teacher forcing on the residual (routing forced only in band)
     layers_o = [(synth.router(cfg, l)[0], None, oracle_expert_getter(cfg, l)) for l in range(3)]
@@ -210,7 +208,7 @@ def test_stack_full(dev, name, check_layers):
 @pytest.mark.parametrize("E,k", [(32, 4), (128, 8), (256, 8), (300, 16)])
 @pytest.mark.parametrize("L", [1, 2])
 @pytest.mark.parametrize("group", ["0", "1"])
-def test_layer_routing_ties(dev, E, k, L, group, monkeypatch):
+def test_layer_routing_ties(dev, E, k, L, group):
     """The expert selection inside the fused path on tie-heavy logits: zero
     router rows, so each logit is its bias, drawn from a small value set with
     -inf entries.  The selection must match the oracle's order exactly (ties
@@ -218,7 +216,6 @@ def test_layer_routing_ties(dev, E, k, L, group, monkeypatch):
     L=2 checks the second layer of a residual stack, which on the per-token
     path (group=0; for E <= 64) routes from the partial sums written by the
     first layer's down kernel; group=1 runs the grouped kernels."""
-    monkeypatch.setenv("BDG_GROUP", group)
     cfg = small_cfg("mxfp4", 1500 + E, E=E, k=k, H=128, I=64, m=2, L=L, stack=L > 1)
     rng = np.random.default_rng(E)
     b = rng.choice(np.array([1.0, 0.5, 0.5, 0.0, -np.inf], dtype=np.float32), size=E)
@@ -227,7 +224,7 @@ def test_layer_routing_ties(dev, E, k, L, group, monkeypatch):
     layers = [sdev.upload_layer(cfg, l, dev) for l in range(L)]
     layers[-1]["w_router"] = torch.from_numpy(w_r).to(dev)
     layers[-1]["b_router"] = torch.from_numpy(b).to(dev)
-    plan, _ = sdev.build_plan(cfg, dev, max_m=2, layers=layers)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=2, layers=layers, per_token=group == "0")
     x, xv = sdev.hidden_device(cfg, [0, 1], dev)
     banner(f"moe_expert_decode routing ties E={E} k={k} L={L}")
     y, tr = bdg.moe_expert_decode(plan, x, traces=True)
@@ -242,12 +239,10 @@ def test_layer_routing_ties(dev, E, k, L, group, monkeypatch):
     assert_close(y, res["y"], res["den"], f"ties E={E} L={L}")
 
 
-def _decode_with(cfg, dev, m, group, monkeypatch):
-    monkeypatch.setenv("BDG_GROUP", group)
+def _decode_with(cfg, dev, m, group):
     # the grouped path routes every layer with the route kernel; so must the
     # per-token path here (no partial sums from the previous down kernel)
-    monkeypatch.setenv("BDG_FUSE_ROUTE", "0")
-    plan, _ = sdev.build_plan(cfg, dev, max_m=m)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=m, per_token=group == "0", route_every_layer=True)
     x, _ = sdev.hidden_device(cfg, range(m), dev)
     y, tr = bdg.moe_expert_decode(plan, x, traces=True)
     torch.cuda.synchronize()
@@ -258,7 +253,7 @@ def _decode_with(cfg, dev, m, group, monkeypatch):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4g"])
 @pytest.mark.parametrize("m", [3, 16])
-def test_grouped_equals_per_token(dev, fmt, m, monkeypatch):
+def test_grouped_equals_per_token(dev, fmt, m):
     """Steps of M > 1 tokens read each chosen expert once (grouped kernels);
     every output row is the same arithmetic as on the per-token path (same
     row dot products, the combine in slot order), so the two agree bit for
@@ -266,8 +261,8 @@ def test_grouped_equals_per_token(dev, fmt, m, monkeypatch):
     grouped path does."""
     cfg = small_cfg(fmt, 1700 + m, E=80, k=4, H=384, I=192, L=3, stack=True, m=m)
     banner(f"grouped vs per-token fmt={fmt} m={m}")
-    g = _decode_with(cfg, dev, m, "1", monkeypatch)
-    t = _decode_with(cfg, dev, m, "0", monkeypatch)
+    g = _decode_with(cfg, dev, m, "1")
+    t = _decode_with(cfg, dev, m, "0")
     for a, b, what in zip(g, t, ("y", "topk", "wts", "resid")):
         assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                               b.view(np.uint32) if b.dtype == np.float32 else b), what
@@ -275,41 +270,43 @@ def test_grouped_equals_per_token(dev, fmt, m, monkeypatch):
 
 def test_small_m_120b_stack_full(dev):
     """The 36-layer 120B-shape stack (128 experts, top-4, biased hot set) at
-    M = 4 through the grouped path: routing of every token checked on every
-    layer, outputs teacher-forced on sampled layers."""
+    M = 4 and M = 16 through the grouped path, in the launch configuration
+    the benchmark times (one plan of max_m 16, graph replay): routing of
+    every token checked on every layer, outputs teacher-forced on sampled
+    layers (first, two inner, last) for every token."""
     cfg = synth.CONFIGS["gptoss120b_smallm"]
-    m = 4
-    plan, layers = sdev.build_plan(cfg, dev, max_m=m)
-    x, xv = sdev.hidden_device(cfg, range(m), dev)
-    banner(f"moe_expert_decode gptoss120b_smallm M={m}")
-    y, tr = bdg.moe_expert_decode(plan, x, traces=True)
-    torch.cuda.synchronize()
-    y, topk, wts, resid = to_np(y), to_np(tr["topk"]), to_np(tr["wts"]), to_np(tr["resid"])
-    assert np.array_equal(resid[0], xv)
-    assert np.all(np.isfinite(y))
-    for l in range(cfg.n_layers):
-        w_r, b_r, _ = synth.router(cfg, l)
-        lg, sc = omoe.router_logits(w_r, omoe.rmsnorm(resid[l]), b_r)
-        for t in range(m):
-            ok, _, msg = omoe.check_routing(lg[t], sc[t], topk[l, t], cfg.top_k)
-            assert ok, f"layer {l} token {t}: {msg}"
-    for l in (0, cfg.n_layers - 1):
-        out = resid[l + 1] if l + 1 < cfg.n_layers else y
-        check_layer(cfg, l, resid[l], out, topk[l], wts[l], True, f"120B layer {l}")
+    plan, layers = sdev.build_plan(cfg, dev, max_m=16)
+    for m in (4, 16):
+        x, xv = sdev.hidden_device(cfg, range(m), dev)
+        banner(f"moe_expert_decode gptoss120b_smallm M={m}")
+        y, tr = bdg.moe_expert_decode(plan, x, traces=True)
+        torch.cuda.synchronize()
+        y, topk, wts, resid = to_np(y), to_np(tr["topk"]), to_np(tr["wts"]), to_np(tr["resid"])
+        assert np.array_equal(resid[0], xv)
+        assert np.all(np.isfinite(y))
+        for l in range(cfg.n_layers):
+            w_r, b_r, _ = synth.router(cfg, l)
+            lg, sc = omoe.router_logits(w_r, omoe.rmsnorm(resid[l]), b_r)
+            for t in range(m):
+                ok, _, msg = omoe.check_routing(lg[t], sc[t], topk[l, t], cfg.top_k)
+                assert ok, f"M={m} layer {l} token {t}: {msg}"
+        for l in (0, 11, 23, cfg.n_layers - 1):
+            out = resid[l + 1] if l + 1 < cfg.n_layers else y
+            check_layer(cfg, l, resid[l], out, topk[l], wts[l], True, f"120B M={m} layer {l}")
     plan.close()
     del layers
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("E,k,m", [(4, 2, 16), (2, 2, 16), (8, 8, 16), (6, 1, 9)])
-def test_grouped_heavy_sharing(dev, E, k, m, monkeypatch):
+def test_grouped_heavy_sharing(dev, E, k, m):
     """Few experts shared by every token (up to 16 picks of one expert, so an
     expert spans several chunks; k = E; k = 1): the grouped path against the
     per-token path bit for bit, and the first layer against the oracle."""
     cfg = small_cfg("mxfp4", 1800 + 10 * E + k, E=E, k=k, H=256, I=128, L=2, stack=True, m=m)
     banner(f"grouped heavy sharing E={E} k={k} m={m}")
-    g = _decode_with(cfg, dev, m, "1", monkeypatch)
-    t = _decode_with(cfg, dev, m, "0", monkeypatch)
+    g = _decode_with(cfg, dev, m, "1")
+    t = _decode_with(cfg, dev, m, "0")
     for a, b, what in zip(g, t, ("y", "topk", "wts", "resid")):
         assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                               b.view(np.uint32) if b.dtype == np.float32 else b), what

@@ -223,3 +223,66 @@ def test_moe_layer_mx_single_expert():
         h = omoe.swiglu(formats.mxfp4_dequant64(gc, gs) @ xq[t], dc.shape[1] * 2)
         hq = mxq.mxfp8_dequant64(*mxq.mxfp8_quantize(h[None, :]))[0]
         assert np.allclose(q["y"][t], formats.mxfp4_dequant64(dc, ds) @ hq, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- requantization spread
+
+def _spread_cases():
+    rng = np.random.default_rng(23)
+    cases = []
+    h = rng.standard_normal((3, 64))
+    cases.append((h, np.abs(h) * 1e-3 + 1e-4))
+    # block maxima just under and just over a power of two: the scale can flip
+    h = rng.uniform(-1, 1, (2, 64))
+    h[0, 5] = 2.0 - 1e-6
+    h[0, 40] = -(4.0 + 1e-6)
+    h[1, 0] = 0.5
+    cases.append((h, np.full(h.shape, 1e-5)))
+    # elements on rounding midpoints of their block's scale (448 fixes X = 0)
+    mids = (mxq.e4m3_value(np.arange(0x7E)) + mxq.e4m3_value(np.arange(1, 0x7F))) / 2
+    h = np.zeros((1, 32))
+    h[0, 0] = 448.0
+    h[0, 1:] = mids[::4][:31]
+    cases.append((h, np.full(h.shape, 1e-9)))
+    return cases
+
+
+def pin_requant_spread(mq):
+    rng = np.random.default_rng(29)
+    attained = False
+    for h, herr in _spread_cases():
+        sp = mq.mxfp8_requant_spread(h, herr)
+        hq = mxq.mxfp8_dequant64(*mxq.mxfp8_quantize(h))
+        assert np.array_equal(mq.mxfp8_requant_spread(h, 0.0), np.zeros_like(h))
+        for i in range(600):
+            u = rng.choice([-1.0, 1.0], h.shape) if i % 2 else rng.uniform(-1, 1, h.shape)
+            hp = h + herr * u
+            d = np.abs(mxq.mxfp8_dequant64(*mxq.mxfp8_quantize(hp)) - hq)
+            assert np.all(d <= sp), f"requantization moved {np.max(d - sp):.3e} past the spread"
+            attained |= bool(np.any((d == sp) & (sp > 0)))
+    assert attained, "the spread is never reached (not a worst case)"
+
+
+def test_requant_spread_brute_force():
+    """The spread bounds every quantization of a perturbed h in the box, and
+    some perturbation reaches it."""
+    pin_requant_spread(mxq)
+
+
+def _spread_fixed_scale(h, herr):
+    # takes the scale of h itself only: misses codes re-quantized at a flipped scale
+    h = np.atleast_2d(np.asarray(h, np.float64))
+    herr = np.broadcast_to(np.asarray(herr, np.float64), h.shape)
+    hc, hs = mxq.mxfp8_quantize(h)
+    sc = np.repeat(np.ldexp(1.0, hs.astype(np.int64) - 127), 32, axis=1)
+    hq = mxq.mxfp8_dequant64(hc, hs)
+    lo = mxq.e4m3_value(mxq.e4m3_round((h - herr) / sc)) * sc
+    hi = mxq.e4m3_value(mxq.e4m3_round((h + herr) / sc)) * sc
+    return np.maximum(np.abs(lo - hq), np.abs(hi - hq))
+
+
+def test_requant_spread_planted_fixed_scale_is_caught():
+    class Planted:
+        mxfp8_requant_spread = staticmethod(_spread_fixed_scale)
+    with pytest.raises(AssertionError):
+        pin_requant_spread(Planted)
