@@ -183,8 +183,15 @@ def test_mx_rejects_bad_args(dev):
     c = torch.zeros((4, 64), dtype=torch.uint8, device=dev)
     with pytest.raises(ValueError):
         bdg.mx_gemm(w, c, torch.zeros((4, 1), dtype=torch.uint8, device=dev))
-    with pytest.raises(BdgError):
-        bdg.mxfp8_quantize(torch.zeros((2, 48), dtype=torch.float32, device=dev))
+    xb = torch.zeros((2, 48), dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        bdg.mxfp8_quantize(xb)                    # the binding refuses k % 32 != 0
+    from bit_dequant_gemv_amd import _lib
+    import ctypes
+    cb = torch.zeros((2, 48), dtype=torch.uint8, device=dev)
+    assert _lib.load().mxfp8_quantize(ctypes.c_void_p(xb.data_ptr()), _lib.BDG_F32, 2, 48,
+                                      ctypes.c_void_p(cb.data_ptr()), ctypes.c_void_p(cb.data_ptr()),
+                                      None) == _lib.BDG_E_INVALID   # and so does the library
 
 
 # ---------------------------------------------------------------- grouped prefill layer
@@ -340,7 +347,20 @@ def test_moe_prefill_rejects_bad_args(dev):
     layer = sdev.upload_layer(cfg, 0, dev)
     x, _ = sdev.hidden_device(cfg, range(2), dev)
     small = torch.empty(16, dtype=torch.uint8, device=dev)
-    with pytest.raises(BdgError):
+    with pytest.raises(ValueError):                # the binding checks the size first
         bdg.moe_prefill_mx(layer, 4, 2, x, workspace=small)
-    with pytest.raises(BdgError):
-        bdg.moe_prefill_mx(layer, 4, 5, x)
+    with pytest.raises((ValueError, BdgError)):
+        bdg.moe_prefill_mx(layer, 4, 5, x)         # k > E
+    # the library itself rejects a short workspace before any launch
+    import ctypes
+    from bit_dequant_gemv_amd import _lib
+    desc = _lib.LayerDesc()
+    desc.w_router = layer["w_router"].data_ptr()
+    desc.b_router = None
+    desc.gate_up = layer["gate_up"].qmat()
+    desc.down = layer["down"].qmat()
+    y = torch.empty((2, 64), dtype=torch.float32, device=dev)
+    idx = torch.empty((2, 2), dtype=torch.int32, device=dev)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    assert _lib.load().moe_prefill_mx(ctypes.byref(desc), 4, 2, p(x), _lib.BDG_BF16, 2, p(y), p(idx), p(y),
+                                      p(small), 16, None) == _lib.BDG_E_INVALID
