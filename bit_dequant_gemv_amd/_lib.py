@@ -16,6 +16,8 @@ BDG_E_ALIGN = -2
 BDG_E_UNSUPPORTED = -3
 BDG_E_HIP = -4
 BDG_E_NOMEM = -5
+BDG_E_TOO_LARGE = -6
+BDG_ATTN_SCRATCH_BYTES = 8 * 1024 * 1024
 
 BDG_F32 = 0
 BDG_BF16 = 1
@@ -33,7 +35,7 @@ EXPORTED = (
     "mxfp4_dequant", "int4g_dequant", "qgemv", "moe_router_topk",
     "moe_plan_create", "moe_plan_destroy", "moe_expert_decode", "moe_experts_routed",
     "moe_expert_decode_profiled", "mxfp8_quantize", "mx_gemm", "moe_prefill_mx_workspace",
-    "moe_prefill_mx", "attn_rope_table", "attn_decode_workspace", "attn_decode",
+    "moe_prefill_mx", "attn_rope_table", "attn_decode_workspace", "attn_decode", "attn_decode_noalloc",
     "bdg_stream_read", "bdg_stream_copy", "bdg_strerror", "bdg_version",
 )
 
@@ -109,6 +111,8 @@ def load():
         "attn_decode_workspace": [i32, i32, i32, i32, i64],
         "attn_decode": [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp, i64, f32, vp, i32, vp, vp,
                         i64, vp],
+        "attn_decode_noalloc": [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i64, vp, i64, f32, vp, i32, vp,
+                                vp],
         "bdg_stream_read": [vp, i64, vp, i32, vp],
         "bdg_stream_copy": [vp, vp, i64, vp],
         "bdg_strerror": [i32],

@@ -319,6 +319,34 @@ def attn_decode(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, wi
     return o
 
 
+def attn_decode_noalloc(q, k, v, k_cache, v_cache, pos0, table, sm_scale, sinks=None, window=0, o=None):
+    """attn_decode without a workspace: the library's static scratch holds the
+    split partials (for callers that cannot allocate device memory; calls
+    that overlap in time on one GPU race).  Returns o [m][Hq][64] fp32 (pass
+    o to keep the call allocation-free on the torch side too)."""
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (m, hkv, d) or v.shape != (m, hkv, d):
+        raise ValueError("k and v must be [m][n_kv_heads][head_dim]")
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape or k_cache.shape[0] != hkv:
+        raise ValueError("caches must match and be [n_kv_heads][cap][head_dim]")
+    if k_cache.dim() != 3 or k_cache.shape[2] != d or table.dim() != 2 or table.shape[1] != d:
+        raise ValueError("caches must be [n_kv_heads][cap][head_dim] and table [positions][head_dim]")
+    cdt = {torch.bfloat16: BDG_BF16, torch.float32: BDG_F32}.get(k_cache.dtype)
+    if cdt is None:
+        raise ValueError("caches must be bfloat16 or float32")
+    _shape(sinks, (hq,), "sinks")
+    if o is None:
+        o = torch.empty((m, hq, d), dtype=torch.float32, device=q.device)
+    _shape(o, (m, hq, d), "o")
+    check("attn_decode_noalloc", _lib.load().attn_decode_noalloc(
+        _dev_ptr(q, "q", torch.float32), _dev_ptr(k, "k", torch.float32), _dev_ptr(v, "v", torch.float32),
+        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), cdt, k_cache.shape[1], hq, hkv, d, m, pos0,
+        _dev_ptr(table, "table", torch.float32), table.shape[0], float(sm_scale),
+        _dev_ptr(sinks, "sinks", torch.float32), int(window), _dev_ptr(o, "o", torch.float32), _stream()))
+    return o
+
+
 def moe_router_topk(x, w_r, b_r=None, topk=4, rmsnorm=False, eps=1e-5):
     """(idx [m][k] int32, wts [m][k] fp32, logits [m][E] fp32)."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x

@@ -26,6 +26,8 @@
 // crossbar.
 #include <math.h>
 
+#include <mutex>
+
 #include "bdg_device.hpp"
 #include "bdg_host.hpp"
 
@@ -712,11 +714,13 @@ extern "C" int64_t attn_decode_workspace(int32_t n_heads, int32_t n_kv_heads, in
   return attn_ws_bytes(n_kv_heads, m, max_keys);
 }
 
-extern "C" int attn_decode(const float* q, const float* k, const float* v, void* k_cache, void* v_cache,
-                           int32_t cache_dtype, int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads,
-                           int32_t head_dim, int32_t m, int64_t pos0, const float* rope_table, int64_t table_rows,
-                           float sm_scale, const float* sinks, int32_t window, float* o, void* workspace,
-                           int64_t workspace_bytes, void* stream) {
+// The attention step over a workspace the caller (attn_decode) or the
+// library's static scratch (attn_decode_noalloc) provides.
+static int attn_decode_impl(const float* q, const float* k, const float* v, void* k_cache, void* v_cache,
+                            int32_t cache_dtype, int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t m, int64_t pos0, const float* rope_table, int64_t table_rows,
+                            float sm_scale, const float* sinks, int32_t window, float* o, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !k_cache || !v_cache || !rope_table || !o || !workspace) return BDG_E_INVALID;
   if (cache_dtype != BDG_F32 && cache_dtype != BDG_BF16) return BDG_E_INVALID;
   if (m < 1 || n_kv_heads < 1 || n_heads < 1 || pos0 < 0 || window < 0 || !(sm_scale > 0.f)) return BDG_E_INVALID;
@@ -760,4 +764,57 @@ extern "C" int attn_decode(const float* q, const float* k, const float* v, void*
     }
   }
   return launch_status();
+}
+
+extern "C" int attn_decode(const float* q, const float* k, const float* v, void* k_cache, void* v_cache,
+                           int32_t cache_dtype, int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads,
+                           int32_t head_dim, int32_t m, int64_t pos0, const float* rope_table, int64_t table_rows,
+                           float sm_scale, const float* sinks, int32_t window, float* o, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  return attn_decode_impl(q, k, v, k_cache, v_cache, cache_dtype, cache_cap, n_heads, n_kv_heads, head_dim, m,
+                          pos0, rope_table, table_rows, sm_scale, sinks, window, o, workspace, workspace_bytes,
+                          stream);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+
+// The split partials of attn_decode_noalloc live in this device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): it uses the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device at that device's first call.
+static __device__ __align__(256) unsigned char scratch[BDG_ATTN_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, or null
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BDG_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BDG_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return BDG_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BDG_OK;
+}
+}  // namespace
+
+extern "C" int attn_decode_noalloc(const float* q, const float* k, const float* v, void* k_cache, void* v_cache,
+                                   int32_t cache_dtype, int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int32_t m, int64_t pos0, const float* rope_table,
+                                   int64_t table_rows, float sm_scale, const float* sinks, int32_t window, float* o,
+                                   void* stream) {
+  const int64_t need = attn_decode_workspace(n_heads, n_kv_heads, head_dim, m, pos0 + m);
+  if (need > (int64_t)BDG_ATTN_SCRATCH_BYTES) return BDG_E_TOO_LARGE;   // (need < 0: impl reports it)
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != BDG_OK) return st;
+  return attn_decode_impl(q, k, v, k_cache, v_cache, cache_dtype, cache_cap, n_heads, n_kv_heads, head_dim, m, pos0,
+                          rope_table, table_rows, sm_scale, sinks, window, o, ws, BDG_ATTN_SCRATCH_BYTES, stream);
 }

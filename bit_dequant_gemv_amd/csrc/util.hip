@@ -68,6 +68,7 @@ extern "C" const char* bdg_strerror(int32_t status) {
     case BDG_E_UNSUPPORTED: return "outside the shapes the kernels cover";
     case BDG_E_HIP: return "HIP runtime or kernel launch error";
     case BDG_E_NOMEM: return "device allocation failed";
+    case BDG_E_TOO_LARGE: return "request needs more than the static scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

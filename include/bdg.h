@@ -68,6 +68,7 @@ extern "C" {
 #define BDG_E_UNSUPPORTED -3 /* valid request outside what the kernels cover */
 #define BDG_E_HIP -4         /* a HIP runtime call or kernel launch failed */
 #define BDG_E_NOMEM -5       /* device allocation failed */
+#define BDG_E_TOO_LARGE -6   /* request exceeds the static scratch of an allocation-free entry point */
 
 /* ---- activation dtypes ---- */
 #define BDG_F32 0
@@ -366,6 +367,25 @@ int attn_decode(const float* q, const float* k, const float* v, void* k_cache, v
                 int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t m, int64_t pos0,
                 const float* rope_table, int64_t table_rows, float sm_scale, const float* sinks, int32_t window,
                 float* o, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* attn_decode_noalloc - attn_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results
+ * (bit for bit) as attn_decode, without the workspace: the split partials
+ * live in a static device array of BDG_ATTN_SCRATCH_BYTES per GPU, owned by
+ * the library and held until the process ends (its device address is looked
+ * up once per device, at that device's first call).  The call itself
+ * allocates and frees nothing.  A call whose attn_decode_workspace(...)
+ * exceeds BDG_ATTN_SCRATCH_BYTES returns BDG_E_TOO_LARGE before any launch
+ * (with 8 KV heads: m <= 7 tokens).  Nothing in the array needs initial
+ * contents; every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (other streams, other threads) race: order
+ * them. */
+#define BDG_ATTN_SCRATCH_BYTES (8 * 1024 * 1024)
+int attn_decode_noalloc(const float* q, const float* k, const float* v, void* k_cache, void* v_cache,
+                        int32_t cache_dtype, int64_t cache_cap, int32_t n_heads, int32_t n_kv_heads,
+                        int32_t head_dim, int32_t m, int64_t pos0, const float* rope_table, int64_t table_rows,
+                        float sm_scale, const float* sinks, int32_t window, float* o, void* stream);
 
 /* ---- measurement aids ---- */
 

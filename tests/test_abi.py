@@ -42,7 +42,7 @@ def test_binding_covers_the_header():
 
 def test_status_text_and_version():
     lib = _lib.load()
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.bdg_strerror(st)
     assert lib.bdg_version().decode()
 
