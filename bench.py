@@ -65,9 +65,10 @@ def step_bytes(cfg, unique_experts_per_layer):
     return sum(router_bytes(cfg) + u * (gu + dn) for u in unique_experts_per_layer)
 
 
-KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/gemv.hip",
-                  "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp", "bit_dequant_gemv_amd/csrc/bdg_device.hpp",
-                  "bit_dequant_gemv_amd/csrc/bdg_topk.hpp")
+KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/moe_layer.hip",
+                  "bit_dequant_gemv_amd/csrc/gemv.hip", "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp",
+                  "bit_dequant_gemv_amd/csrc/bdg_device.hpp", "bit_dequant_gemv_amd/csrc/bdg_topk.hpp",
+                  "bit_dequant_gemv_amd/csrc/bdg_moe.hpp", "bit_dequant_gemv_amd/csrc/bdg_moe_layer.hpp")
 
 
 def kernel_sources_sha(sources=KERNEL_SOURCES):
@@ -752,6 +753,45 @@ def bench_attn(torch, bdg, synth, dev, cfg, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_timeline(bdg, plan, cfg, x_all, x_buf, y_buf, W, K):
+    """Where a fused layer kernel's time goes: per-block 100 MHz clock stamps
+    at its phase boundaries (moe_expert_decode_timeline, direct launches).
+    Per phase, the median and the latest block's time after the kernel's
+    first block started, over the timed tokens and layers 1..L-1, and the
+    gap from a layer's last block to the next layer's first."""
+    import numpy as np
+    names = bdg.api.LAYER_STAMPS
+    rows, gaps = [], []
+    for s in range(W, W + K):
+        x_buf.copy_(x_all[s])
+        st = bdg.moe_expert_decode_timeline(plan, x_buf, y_buf).astype(np.int64)   # [L][blocks][16]
+        for l in range(1, st.shape[0]):
+            blk = st[l][:, :len(names)]
+            t0 = blk[:, 0][blk[:, 0] > 0].min()
+            rec = {}
+            for i, nm in enumerate(names):
+                v = blk[:, i][blk[:, i] > 0]
+                if v.size:
+                    rec[nm] = ((np.median(v) - t0) * 0.01, (v.max() - t0) * 0.01)
+            rows.append(rec)
+            if l + 1 < st.shape[0]:
+                nxt = st[l + 1][:, 0]
+                end = blk[:, names.index("end")]
+                gaps.append((nxt[nxt > 0].min() - max(end.max(), blk[:, names.index("barrier")].max())) * 0.01)
+    out = {}
+    for nm in names:
+        vals = [r[nm] for r in rows if nm in r]
+        if vals:
+            out[nm] = {"median_block_us": round(float(np.mean([v[0] for v in vals])), 2),
+                       "last_block_us": round(float(np.mean([v[1] for v in vals])), 2)}
+    res = {"workload": cfg.name, "kernel": "moe_layer_kernel", "tokens": K, "layers_averaged": cfg.n_layers - 1,
+           "clock": "s_memrealtime, 100 MHz", "phases_after_first_block_start": out,
+           "gap_to_next_layer_us": round(float(np.mean(gaps)), 2) if gaps else None}
+    log(f"timeline: {res}")
+    print(json.dumps(res), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -762,6 +802,16 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
+    ap.add_argument("--fused-layer", action="store_true",
+                    help="one-token steps run each layer as the fused per-layer kernel instead of two "
+                         "kernels (gate_up, down): the A/B of the fused design")
+    ap.add_argument("--timeline", action="store_true",
+                    help="one-token stacks: phase timeline of the fused per-layer kernel (per-block clock "
+                         "stamps of moe_expert_decode_timeline), summarized per phase, then exit")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="only the warmup and the timed graph replays (no per-step events, sync mode, "
+                         "per-kernel event pass, stream read or CPU baseline): the run a kernel trace "
+                         "of graph replays alone is taken from")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the 16-byte copy kernel 4 times over BYTES (for scaling "
                          "HBM counters against a kernel of known traffic), then exit")
@@ -819,7 +869,7 @@ def main():
         layers.append(sdev.upload_layer(cfg, l, dev, threads=16))
         if l % 6 == 5 or l == cfg.n_layers - 1:
             log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.1f} s)")
-    plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers, fused_layer=args.fused_layer or args.timeline)
     x_all, _ = sdev.hidden_device(cfg, range((W + K) * m), dev)
     x_all = x_all.reshape(W + K, m, cfg.hidden)
     x_buf = torch.empty_like(x_all[0])
@@ -830,6 +880,8 @@ def main():
         bdg.moe_expert_decode(plan, x_buf, y=y_buf)
     torch.cuda.synchronize()
     log(f"warmup done ({W} steps of M={m})")
+    if args.timeline:
+        return bench_timeline(bdg, plan, cfg, x_all, x_buf, y_buf, W, K)
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -843,8 +895,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     gpu_ms = start.elapsed_time(end)
-    if not torch.isfinite(y_buf).all():
-        raise SystemExit("non-finite output")
+    if not torch.isfinite(y_buf).all() or not plan.check():
+        raise SystemExit("non-finite output or a failed in-kernel wait")
+    if args.graph_only:
+        log(f"graph-only run: {K} steps of M={m}, {gpu_ms / K * 1e3:.1f} us/step")
+        print(json.dumps({"workload": cfg.name, "m": m, "steps": K, "us_per_step": round(gpu_ms / K * 1e3, 2),
+                          "fused_layer": bool(args.fused_layer)}), flush=True)
+        plan.close()
+        return
 
     # unique (layer, expert) matrices per step: M=1 reads k experts per layer;
     # for M > 1 the same steps are replayed untimed with routing traces
@@ -914,19 +972,32 @@ def main():
         if kcnt[i]:
             kernels[name] = {"avg_us": round(kms[i] / kcnt[i] * 1e3, 3), "launches": int(kcnt[i])}
     gu_launch_bytes = int(round(mean_uniq * gu_bytes))
-    gu_avg_s = kms[1] / kcnt[1] * 1e-3
-    achieved = gu_launch_bytes / gu_avg_s / 1e9
-    kernels["gate_up"]["GBps"] = round(achieved, 1)
-    kernels["down"]["GBps"] = round(mean_uniq * dn_bytes / (kms[2] / kcnt[2] * 1e-3) / 1e9, 1)
-    kernels["route"]["GBps"] = round(router_bytes(cfg) / (kms[0] / kcnt[0] * 1e-3) / 1e9, 1)
-    sum_kernel_us = sum(kms[i] for i in range(4)) / K * 1e3
+    layer_launch_bytes = int(round(mean_uniq * (gu_bytes + dn_bytes)))
+
+    def rate(kind, nbytes):
+        i = bdg.KERNEL_KINDS.index(kind)
+        if kcnt[i]:
+            kernels[kind]["GBps"] = round(nbytes / (kms[i] / kcnt[i] * 1e-3) / 1e9, 1)
+            return kernels[kind]["GBps"]
+        return None
+    rate("gate_up", gu_launch_bytes)
+    rate("down", int(round(mean_uniq * dn_bytes)))
+    rate("route", router_bytes(cfg))
+    fused = kcnt[bdg.KERNEL_KINDS.index("layer")] > 0
+    if fused:
+        # the fused per-layer kernel: the chosen experts' gate_up and down bytes per launch
+        dom_kernel, dom_kind, dom_bytes = "moe_layer_kernel", "layer", layer_launch_bytes
+    else:
+        dom_kernel, dom_kind, dom_bytes = "moe_gateup_kernel", "gate_up", gu_launch_bytes
+    achieved = rate(dom_kind, dom_bytes)
+    sum_kernel_us = sum(kms[i] for i in range(len(bdg.KERNEL_KINDS))) / K * 1e3
     log(f"per-kernel: {kernels}; kernel time {sum_kernel_us:.1f} us/step of {gpu_ms / K * 1e3:.1f}")
 
     stream = None
     if not args.no_stream_read:
         best, med, phases = stream_read_rate(
             torch, bdg, dev, {"gate_up": gu_launch_bytes, "down": int(round(mean_uniq * dn_bytes)),
-                              "router": router_bytes(cfg)})
+                              "layer": layer_launch_bytes, "router": router_bytes(cfg)})
         stream = {"best_GBps": round(best, 1), "median_GBps": round(med, 1), "bytes": "4 GiB",
                   "phase_sized_reads": phases}
         log(f"stream read: best {best:.1f} GB/s, median {med:.1f} GB/s; phase-sized: {phases}")
@@ -942,6 +1013,7 @@ def main():
         "experts": cfg.n_experts, "top_k": cfg.top_k, "m": m,
         "bytes_per_step": int(round(nbytes / K)),
         "timing": "HIP graph per step (M tokens), stream-ordered",
+        "layer_kernels": "fused per-layer kernel" if fused else "two kernels per layer (gate_up, down)",
     }
     if routing:
         config["routing"] = routing
@@ -966,14 +1038,14 @@ def main():
         "sync_mode_wall_per_step": sync_mode,
         "pct_of_stream_read": round(100.0 * value / stream["best_GBps"], 2) if stream else None,
         "roofline": {
-            "kernel": "moe_gateup_kernel",
+            "kernel": dom_kernel,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(cfg.name, "gate_up") if m == 1 else None,
-            "traffic_algorithmic_bytes": gu_launch_bytes,
+            "traffic": measured_traffic(cfg.name, dom_kind) if m == 1 else None,
+            "traffic_algorithmic_bytes": dom_bytes,
         },
         "kernels": kernels,
         "kernel_us_per_step": round(sum_kernel_us, 2),

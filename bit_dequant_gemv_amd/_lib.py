@@ -17,6 +17,7 @@ BDG_E_UNSUPPORTED = -3
 BDG_E_HIP = -4
 BDG_E_NOMEM = -5
 BDG_E_TOO_LARGE = -6
+BDG_E_WAIT = -7
 BDG_ATTN_SCRATCH_BYTES = 8 * 1024 * 1024
 
 BDG_F32 = 0
@@ -28,13 +29,14 @@ BDG_MOE_STACK = 1
 BDG_MOE_NO_GRAPH = 2
 BDG_MOE_ROUTE_EVERY_LAYER = 4
 BDG_MOE_PER_TOKEN = 8
+BDG_MOE_FUSED_LAYER = 16
 BDG_MAX_M = 16
 
 # every symbol include/bdg.h declares
 EXPORTED = (
     "mxfp4_dequant", "int4g_dequant", "qgemv", "moe_router_topk",
-    "moe_plan_create", "moe_plan_destroy", "moe_expert_decode", "moe_experts_routed",
-    "moe_expert_decode_profiled", "mxfp8_quantize", "mx_gemm", "moe_prefill_mx_workspace",
+    "moe_plan_create", "moe_plan_destroy", "moe_plan_check", "moe_expert_decode", "moe_experts_routed",
+    "moe_expert_decode_profiled", "moe_expert_decode_timeline", "mxfp8_quantize", "mx_gemm", "moe_prefill_mx_workspace",
     "moe_prefill_mx", "attn_rope_table", "attn_decode_workspace", "attn_decode", "attn_decode_noalloc",
     "bdg_stream_read", "bdg_stream_copy", "bdg_strerror", "bdg_version",
 )
@@ -69,6 +71,7 @@ class MoEDesc(ctypes.Structure):
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("fmt", ctypes.c_int32),
         ("group", ctypes.c_int32), ("flags", ctypes.c_int32), ("norm_eps", ctypes.c_float),
         ("max_m", ctypes.c_int32), ("layers", ctypes.POINTER(LayerDesc)),
+        ("wait_polls", ctypes.c_int32),
     ]
 
 
@@ -100,9 +103,11 @@ def load():
         "moe_router_topk": [vp, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp],
         "moe_plan_create": [ctypes.POINTER(MoEDesc), ctypes.POINTER(vp)],
         "moe_plan_destroy": [vp],
+        "moe_plan_check": [vp, vp],
         "moe_expert_decode": [vp, vp, i32, i32, vp, vp, vp, vp, vp],
         "moe_experts_routed": [vp, i32, vp, i32, i32, vp, vp, vp, vp],
         "moe_expert_decode_profiled": [vp, vp, i32, i32, vp, vp, vp, vp],
+        "moe_expert_decode_timeline": [vp, vp, i32, vp, vp, i64, vp],
         "mxfp8_quantize": [vp, i32, i64, i64, vp, vp, vp],
         "mx_gemm": [ctypes.POINTER(QMat), vp, vp, i64, vp, vp],
         "moe_prefill_mx_workspace": [i64, i32, i32, i32, i32],
@@ -122,7 +127,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = (ctypes.c_char_p if name in ("bdg_strerror", "bdg_version")
-                      else ctypes.c_int64 if name in ("moe_prefill_mx_workspace", "attn_decode_workspace")
+                      else ctypes.c_int64 if name in ("moe_prefill_mx_workspace", "attn_decode_workspace",
+                                                      "moe_expert_decode_timeline")
                       else ctypes.c_int)
     _lib = lib
     return lib

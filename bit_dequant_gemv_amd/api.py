@@ -10,9 +10,9 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (BDG_BF16, BDG_F32, BDG_FMT_INT4G, BDG_FMT_MXFP4, BDG_MOE_NO_GRAPH,
-                   BDG_MOE_PER_TOKEN, BDG_MOE_ROUTE_EVERY_LAYER, BDG_MOE_STACK, BDG_ROUTER_RMSNORM,
-                   LayerDesc, MoEDesc, QMat, Rope, check)
+from ._lib import (BDG_BF16, BDG_E_WAIT, BDG_F32, BDG_FMT_INT4G, BDG_FMT_MXFP4, BDG_MOE_NO_GRAPH,
+                   BDG_MOE_PER_TOKEN, BDG_MOE_ROUTE_EVERY_LAYER, BDG_MOE_STACK, BDG_MOE_FUSED_LAYER,
+                   BDG_OK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, Rope, check)
 
 
 def _stream():
@@ -126,7 +126,7 @@ def qgemv(w: QWeight, x, out=None):
     if x2.shape[1] != w.k:
         raise ValueError("x and W disagree on K")
     if out is not None:
-        _shape(out, (m, w.n), "out")
+        _shape(out, (w.n,) if squeeze else (m, w.n), "out")
     y = out if out is not None else torch.empty((m, w.n), dtype=torch.float32, device=x.device)
     qm = w.qmat()
     check("qgemv", _lib.load().qgemv(ctypes.byref(qm), _dev_ptr(x2, "x"), _x_dtype(x2), m,
@@ -377,7 +377,7 @@ class MoEPlan:
 
     def __init__(self, layers, hidden, inter, n_experts, top_k, fmt="mxfp4", group=32,
                  stack=True, norm_eps=1e-5, max_m=1, use_graph=True, route_every_layer=False,
-                 per_token=False):
+                 per_token=False, fused_layer=False, wait_polls=0):
         self._layers = layers
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.n_layers = len(layers)
@@ -399,11 +399,12 @@ class MoEPlan:
             arr[i].down = L["down"].qmat()
         flags = ((BDG_MOE_STACK if stack else 0) | (0 if use_graph else BDG_MOE_NO_GRAPH)
                  | (BDG_MOE_ROUTE_EVERY_LAYER if route_every_layer else 0)
-                 | (BDG_MOE_PER_TOKEN if per_token else 0))
+                 | (BDG_MOE_PER_TOKEN if per_token else 0)
+                 | (BDG_MOE_FUSED_LAYER if fused_layer else 0))
         desc = MoEDesc(n_layers=len(layers), hidden=hidden, inter=inter, n_experts=n_experts,
                        top_k=top_k, fmt=BDG_FMT_MXFP4 if fmt == "mxfp4" else BDG_FMT_INT4G,
                        group=32 if fmt == "mxfp4" else group, flags=flags,
-                       norm_eps=norm_eps, max_m=max_m, layers=arr)
+                       norm_eps=norm_eps, max_m=max_m, layers=arr, wait_polls=int(wait_polls))
         handle = ctypes.c_void_p()
         check("moe_plan_create", _lib.load().moe_plan_create(ctypes.byref(desc), ctypes.byref(handle)))
         self._handle = handle
@@ -414,6 +415,15 @@ class MoEPlan:
         if self._handle is None:
             raise RuntimeError("plan is closed")
         return self._handle
+
+    def check(self):
+        """moe_plan_check: True if no in-kernel wait gave up since the last
+        check (False: some step's outputs were made NaN).  Synchronous."""
+        st = _lib.load().moe_plan_check(self.handle, _stream())
+        if st == BDG_E_WAIT:
+            return False
+        check("moe_plan_check", st)
+        return True
 
     def close(self):
         if getattr(self, "_handle", None) is not None:
@@ -476,24 +486,46 @@ def moe_experts_routed(plan: MoEPlan, layer, x, idx, wts, y=None):
     return y
 
 
-KERNEL_KINDS = ("route", "gate_up", "down", "combine")
+KERNEL_KINDS = ("route", "gate_up", "down", "combine", "layer")
 
 
 def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None):
     """One decode step with per-kernel start/stop events; accumulates into
-    acc_ms / acc_count (ctypes double[4] / int64[4]) and returns them."""
+    acc_ms / acc_count (ctypes double[5] / int64[5], indexed like
+    KERNEL_KINDS) and returns them."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     _shape(x2, (x2.shape[0], plan.hidden), "x")
     _shape(y, (x2.shape[0], plan.hidden), "y")
     if not 1 <= x2.shape[0] <= plan.max_m:
         raise ValueError(f"m must be in [1, {plan.max_m}] (the plan's max_m)")
     if acc_ms is None:
-        acc_ms = (ctypes.c_double * 4)()
-        acc_count = (ctypes.c_int64 * 4)()
+        acc_ms = (ctypes.c_double * len(KERNEL_KINDS))()
+        acc_count = (ctypes.c_int64 * len(KERNEL_KINDS))()
     check("moe_expert_decode_profiled", _lib.load().moe_expert_decode_profiled(
         plan.handle, _dev_ptr(x2, "x"), _x_dtype(x2), x2.shape[0], _dev_ptr(y, "y", torch.float32),
         acc_ms, acc_count, _stream()))
     return acc_ms, acc_count
+
+
+LAYER_STAMPS = ("start", "routed", "gu_issued", "dn_issued", "gu_done", "h_stored", "barrier", "h_staged",
+                "dn_done", "end")
+
+
+def moe_expert_decode_timeline(plan: MoEPlan, x, y, n_blocks=4096):
+    """One single-token step on the fused per-layer path with per-block phase
+    stamps: returns a numpy uint64 array [L][blocks][16] of 100 MHz clock
+    values (0 = phase not reached by that block), indexed by LAYER_STAMPS."""
+    import numpy as np
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    _shape(x2, (1, plan.hidden), "x")
+    _shape(y, (1, plan.hidden), "y")
+    buf = np.zeros(plan.n_layers * n_blocks * 16, dtype=np.uint64)
+    n = _lib.load().moe_expert_decode_timeline(
+        plan.handle, _dev_ptr(x2, "x"), _x_dtype(x2), _dev_ptr(y, "y", torch.float32),
+        buf.ctypes.data_as(ctypes.c_void_p), buf.size, _stream())
+    if n < 0:
+        check("moe_expert_decode_timeline", int(n))
+    return buf[:n].reshape(plan.n_layers, -1, 16)
 
 
 def stream_read(buf, n_blocks=0, sink=None):

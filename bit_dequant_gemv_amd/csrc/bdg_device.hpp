@@ -52,6 +52,24 @@ __device__ __forceinline__ uint2 ldg_u64(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
+// ---------------------------------------------------------------- block barrier
+
+// A barrier for LDS hand-offs between the waves of a block, issued while
+// global loads are still in flight: each wave waits for its own LDS
+// accesses only (lgkmcnt 0), then meets the others at s_barrier.
+// __syncthreads() would also wait for every outstanding global load of the
+// wave (its workgroup-scope release fence waits for vmcnt 0), so a block
+// that stages x or h after issuing its weight loads could not start on the
+// first rows before the last rows had arrived.  The wavefront-scope fences
+// only keep the compiler from moving memory accesses across the barrier.
+// Not for hand-offs through global memory.
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // gfx9 encoding: lgkmcnt(0), vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------- scalars
 
 // E8M0 byte -> fp32 2^(e-127).  e = 0 is the fp32 subnormal 2^-127,

@@ -1,0 +1,300 @@
+// Pieces shared by the MoE decode kernels (moe.hip: the router, gate_up and
+// down kernels and the grouped kernels; moe_layer.hip: the fused per-layer
+// kernel): per-layer weight addresses, expert views, and the routing
+// prologue in which a kernel selects its own experts from router sums.
+#pragma once
+
+#include "bdg_gemv.hpp"
+#include "bdg_topk.hpp"
+
+namespace bdg {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kDownWaves = 8;        // waves per down block
+constexpr int kGuPairsPerWave = 6;   // gate_up: (g, u) row pairs in flight per wave
+constexpr int kRouteMaxF4 = 16;      // router row float4 per lane (H <= 4096)
+constexpr int kPartF4 = 8;           // float4 of router partial sums per thread issued up front
+constexpr int kDnRouterPerWave = 8;  // next-layer router rows per down wave
+
+// Weight addresses of one layer.  The plan keeps one per layer on the host
+// and passes it by value to each kernel launch (a kernel argument, so the
+// first weight load does not wait for a dependent table load).
+struct LayerDev {
+  const float* w_r;
+  const float* b_r;
+  const uint8_t* gu_codes;
+  const uint8_t* gu_scales;
+  const uint8_t* gu_zeros;
+  int64_t gu_sc, gu_ss, gu_sz;
+  const uint8_t* dn_codes;
+  const uint8_t* dn_scales;
+  const uint8_t* dn_zeros;
+  int64_t dn_sc, dn_ss, dn_sz;
+};
+
+__device__ __forceinline__ QMat expert_gu(const LayerDev& L, int e) {
+  return QMat{L.gu_codes + (int64_t)e * L.gu_sc, L.gu_scales + (int64_t)e * L.gu_ss,
+              L.gu_zeros ? L.gu_zeros + (int64_t)e * L.gu_sz : nullptr};
+}
+__device__ __forceinline__ QMat expert_dn(const LayerDev& L, int e) {
+  return QMat{L.dn_codes + (int64_t)e * L.dn_sc, L.dn_scales + (int64_t)e * L.dn_ss,
+              L.dn_zeros ? L.dn_zeros + (int64_t)e * L.dn_sz : nullptr};
+}
+
+__device__ __forceinline__ int uniform_wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// ---------------------------------------------------------------- routing prologue
+//
+// Router dot products travel between kernels as partial sums:
+// part[t][e][k], k < nparts (row stride pstride), holds the sum over one
+// slice of the hidden dimension of w_r[e][h] * x[h] for the layer input x,
+// before the RMSNorm scale and the bias.  The route kernel writes one slice
+// (the whole of x); a down kernel that feeds the next layer writes one slice
+// per row block.  Column E holds the matching slices of the sum of squares
+// of x.  A kernel that selects its own experts adds the slices in a fixed
+// order, scales by the RMSNorm factor, adds the bias and takes the top-k.
+// (RMSNorm is a per-token scale, so w_r . (x * r) = r * (w_r . x).)
+
+struct RouteSrc {
+  int routed;                 // 1: routing given in idx_in / w_in
+  const int32_t* idx_in;      // [M][K]
+  const float* w_in;
+  const float* part;          // [M][E + 1][pstride] router partial sums
+  int nparts, pstride;
+  int log2T;                  // 2^log2T threads add up one expert's slices
+  int norm;                   // RMSNorm scale on x (and on the router input)
+  float eps;
+  int E, K, H;
+  const float* b_r;           // [E] or NULL
+};
+
+template <int V>
+struct RouteState {
+  float4 pv[kPartF4];
+  float lg[V], bias[V];
+  float ssq;
+  int my_e;                   // lane j < K: pick j (expert, weight)
+  float my_w;
+  float r;                    // RMSNorm factor of the layer input (1 without norm)
+};
+
+// Issue the loads of token t's routing inputs (call first: vmcnt retires in
+// order, so anything issued later does not delay their wait).  NT threads.
+template <int V, int NT>
+__device__ __forceinline__ void route_issue(RouteState<V>& rs, const RouteSrc& p, int t, int lane) {
+  const int lt = p.log2T;
+  const int T = 1 << lt;
+  const int sub = threadIdx.x & (T - 1);
+  const int n4 = (p.nparts + 3) >> 2;                      // float4 per expert row of slices
+  const int64_t pbase = (int64_t)t * (p.E + 1) * p.pstride;
+  const bool slices = !p.routed && p.nparts > 1;
+  rs.ssq = 0.f;
+  rs.my_e = 0;
+  rs.my_w = 0.f;
+  rs.r = 1.f;
+  if (p.routed) {
+    rs.my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
+    rs.my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = lane + kWave * i;
+    rs.bias[i] = p.b_r ? p.b_r[e < p.E ? e : p.E - 1] : 0.f;
+  }
+  if (slices) {
+    const int c = threadIdx.x >> lt;
+    const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
+    // rows are zero past the nparts slices up to pstride >= 4 * T * kPartF4
+    // (the plan zeroes the buffer once; no kernel writes there)
+#pragma unroll
+    for (int i = 0; i < kPartF4; ++i) rs.pv[i] = ldg_f4(row + 4 * (sub + (i << lt)));
+    // sum-of-squares slices (column E): one float4 per thread, n4 <= kThreads
+    const int k4 = threadIdx.x;
+    const float4 q = k4 < n4 ? ldg_f4(p.part + pbase + (int64_t)p.E * p.pstride + 4 * k4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int k = 4 * k4;
+    rs.ssq = k < p.nparts ? q.x : 0.f;
+    rs.ssq += k + 1 < p.nparts ? q.y : 0.f;
+    rs.ssq += k + 2 < p.nparts ? q.z : 0.f;
+    rs.ssq += k + 3 < p.nparts ? q.w : 0.f;
+  } else {
+    // one slice (the route kernel's): each wave reads its values directly
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      rs.lg[i] = p.part[pbase + (int64_t)(e < p.E ? e : p.E - 1) * p.pstride];
+    }
+    rs.ssq = p.part[pbase + (int64_t)p.E * p.pstride];
+  }
+}
+
+// Add the slices in a fixed order, apply the RMSNorm factor and bias, and
+// select: every wave ends with the token's top-k in its lanes 0..K-1.  All
+// NT threads of the block call it (a barrier inside when slices are summed).
+// red: NT / 64 floats of LDS; psum: E << log2T floats of LDS.
+template <int V, int NT>
+__device__ __forceinline__ void route_finish(RouteState<V>& rs, const RouteSrc& p, int t, int lane, int wave,
+                                             float* red, float* psum) {
+  if (p.routed) {
+    if (lane >= p.K) {
+      rs.my_e = 0;
+      rs.my_w = 0.f;
+    }
+    return;
+  }
+  const int lt = p.log2T;
+  const int T = 1 << lt;
+  const int sub = threadIdx.x & (T - 1);
+  const int n4 = (p.nparts + 3) >> 2;
+  const int64_t pbase = (int64_t)t * (p.E + 1) * p.pstride;
+  float ssq = rs.ssq;
+  if (p.nparts > 1) {
+    // slices of expert c: thread sub adds slices 4*(sub + i*T) .. +3, in order
+    for (int c0 = 0; c0 < p.E; c0 += NT >> lt) {
+      const int c = c0 + (threadIdx.x >> lt);
+      const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
+      float a = 0.f;
+      int k4 = sub;
+      if (c0 == 0) {
+#pragma unroll
+        for (int i = 0; i < kPartF4; ++i, k4 += T) {
+          a += rs.pv[i].x;
+          a += rs.pv[i].y;
+          a += rs.pv[i].z;
+          a += rs.pv[i].w;
+        }
+      }
+      for (; k4 < n4; k4 += T) {   // beyond the slices loaded up front
+        const float4 v = ldg_f4(row + 4 * k4);
+        const int k = 4 * k4;
+        a += v.x;
+        a += k + 1 < p.nparts ? v.y : 0.f;
+        a += k + 2 < p.nparts ? v.z : 0.f;
+        a += k + 3 < p.nparts ? v.w : 0.f;
+      }
+      if (c < p.E) psum[(c << lt) + sub] = a;
+    }
+    {
+      const float ss = wave_sum(ssq);
+      if (lane == 0) red[wave] = ss;
+    }
+    __syncthreads();
+    // the sum-of-squares slices sit in threads 0..255 (waves 0..3)
+    if (p.norm) ssq = (red[0] + red[1]) + (red[2] + red[3]);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      const float* ps = psum + ((e < p.E ? e : p.E - 1) << lt);
+      float a = 0.f;
+      for (int q = 0; q < T; ++q) a += ps[q];
+      rs.lg[i] = a;
+    }
+  }
+  float r = 1.0f;
+  if (p.norm) r = 1.0f / sqrtf(ssq / (float)p.H + p.eps);
+#pragma unroll
+  for (int i = 0; i < V; ++i) rs.lg[i] = r * rs.lg[i] + rs.bias[i];
+  topk_rank<V>(rs.lg, p.E, p.K, rs.my_e, rs.my_w);
+  rs.r = r;
+  if (lane >= p.K) {
+    rs.my_e = 0;
+    rs.my_w = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- down epilogue
+//
+// A block of 8 waves that owns output rows [r0, r0 + B), B <= 64, with the
+// expert rows' dot products in dpart[j][b] (LDS): every wave forms row
+// r0 + lane = (x_prev +) sum_j w_j dpart[j][lane], j in slot order, and wave
+// 0 stores it; with route_next, wave w also reduces the rows against router
+// rows w, w + 8, ... of the next layer and writes slice `slice` of its
+// router partial sums (and of the sum of squares, column E).
+
+struct DownOut {
+  int H, E, K;
+  int residual;               // add x_prev
+  const float* x_prev;        // [M][H] layer input (residual)
+  const float* w;             // [M][K] routing weights
+  float* x_out;               // [M][H] next layer's input, or NULL
+  float* y_out;               // [M][H] caller output, or NULL
+  float* trace_out;           // [M][H] copy of x_out (next layer's input trace), or NULL
+  int route_next;             // then E <= kDownWaves * kDnRouterPerWave
+  const float* wr_next;       // [E][H]
+  float* part_out;            // [M][E + 1][pstride]
+  int pstride;
+};
+
+// The epilogue's router and residual operands for this lane (all in
+// bounds and unconditional, so the compiler's wait counts stay exact): idle
+// lanes past the block's rows repeat its last row.
+struct DownEpiIn {
+  float wr[kDnRouterPerWave];   // wr[i] = w_r'[wave + 8i][orow]
+  float xp;                     // x_prev[orow]
+  float wk;                     // routing weight of slot `lane` (lane < K), set by the caller
+};
+
+__device__ __forceinline__ void down_epilogue_load(DownEpiIn& in, const DownOut& o, int t, int r0, int B, int lane,
+                                                   int wave) {
+  const int orow = min(r0 + min(lane, B - 1), o.H - 1);
+  const float* wsrc = o.route_next ? o.wr_next : o.x_prev;
+#pragma unroll
+  for (int i = 0; i < kDnRouterPerWave; ++i) {
+    const int er = wave + kDownWaves * i;
+    in.wr[i] = wsrc[(int64_t)(o.route_next ? (er < o.E ? er : o.E - 1) : 0) * o.H + orow];
+  }
+  in.xp = o.x_prev[(int64_t)t * o.H + orow];
+}
+
+__device__ __forceinline__ void down_epilogue(const DownOut& o, const DownEpiIn& in, const float* dpart, int t,
+                                              int slice, int r0, int B, int lane, int wave) {
+  const int row = r0 + lane;
+  const bool ok = lane < B && row < o.H;
+  float v = o.residual ? in.xp : 0.f;
+  for (int j = 0; j < o.K; ++j)
+    v = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(in.wk), j)),
+                       dpart[j * B + (ok ? lane : 0)], v);
+  v = ok ? v : 0.f;
+  if (wave == 0 && ok) {
+    if (o.x_out) o.x_out[(int64_t)t * o.H + row] = v;
+    if (o.y_out) o.y_out[(int64_t)t * o.H + row] = v;
+    if (o.trace_out) o.trace_out[(int64_t)t * o.H + row] = v;
+  }
+  if (!o.route_next) return;
+  // all router rows of the wave (and the rows' sum of squares, column E)
+  // reduced together, one butterfly step at a time
+  constexpr int NA = kDnRouterPerWave + 1;
+  float a[NA];
+#pragma unroll
+  for (int i = 0; i < kDnRouterPerWave; ++i) a[i] = ok ? in.wr[i] * v : 0.f;
+  a[kDnRouterPerWave] = v * v;
+#pragma unroll
+  for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor1(a[i]);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor2(a[i]);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) a[i] += dpp_f32<0x141, 0xF>(a[i]);   // row_half_mirror
+#pragma unroll
+  for (int i = 0; i < NA; ++i) a[i] += dpp_f32<0x140, 0xF>(a[i]);   // row_mirror
+#pragma unroll
+  for (int i = 0; i < NA; ++i) a[i] = add_pair16(a[i]);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) a[i] = add_pair32(a[i]);
+  if (lane == 0) {
+    float* out = o.part_out + (int64_t)t * (o.E + 1) * o.pstride + slice;
+#pragma unroll
+    for (int i = 0; i < kDnRouterPerWave; ++i) {
+      const int er = wave + kDownWaves * i;
+      if (er < o.E) out[(int64_t)er * o.pstride] = a[i];
+    }
+    if (wave == 0) out[(int64_t)o.E * o.pstride] = a[kDnRouterPerWave];
+  }
+}
+
+}  // namespace bdg

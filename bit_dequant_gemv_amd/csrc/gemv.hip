@@ -59,7 +59,7 @@ qgemv_kernel(QMat w, QGeom g, int64_t n_rows, const void* __restrict__ x, int x_
     xf.store(lds_x, g.k, g.k, 0, 1.0f, threadIdx.x, kGemvThreads);
   }
   lds_x[g.chunks * kXStride + (threadIdx.x & (kChunkElems - 1))] = 0.f;   // the zero chunk after x (no branch)
-  __syncthreads();
+  block_sync_lds();   // weights still in flight: each row group waits for its own rows only
   XRegs<FMT, L, S> xr;
   xr.load_zpad(lds_x, g.chunks, li);
   float* yt = y + (int64_t)t * n_rows;

@@ -32,60 +32,16 @@
 #include <algorithm>
 #include <new>
 
-#include "bdg_gemv.hpp"
 #include "bdg_host.hpp"
-#include "bdg_topk.hpp"
+#include "bdg_moe.hpp"
+#include "bdg_moe_layer.hpp"
 
 namespace bdg {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kDownWaves = 8;        // waves per down block
-constexpr int kGuPairsPerWave = 6;   // gate_up: (g, u) row pairs in flight per wave
-constexpr int kRouteMaxF4 = 16;      // router row float4 per lane (H <= 4096)
-
-// Weight addresses of one layer.  The plan keeps one per layer on the host
-// and passes it by value to each kernel launch (a kernel argument, so the
-// first weight load does not wait for a dependent table load).
-struct LayerDev {
-  const float* w_r;
-  const float* b_r;
-  const uint8_t* gu_codes;
-  const uint8_t* gu_scales;
-  const uint8_t* gu_zeros;
-  int64_t gu_sc, gu_ss, gu_sz;
-  const uint8_t* dn_codes;
-  const uint8_t* dn_scales;
-  const uint8_t* dn_zeros;
-  int64_t dn_sc, dn_ss, dn_sz;
-};
-
-__device__ __forceinline__ QMat expert_gu(const LayerDev& L, int e) {
-  return QMat{L.gu_codes + (int64_t)e * L.gu_sc, L.gu_scales + (int64_t)e * L.gu_ss,
-              L.gu_zeros ? L.gu_zeros + (int64_t)e * L.gu_sz : nullptr};
-}
-__device__ __forceinline__ QMat expert_dn(const LayerDev& L, int e) {
-  return QMat{L.dn_codes + (int64_t)e * L.dn_sc, L.dn_scales + (int64_t)e * L.dn_ss,
-              L.dn_zeros ? L.dn_zeros + (int64_t)e * L.dn_sz : nullptr};
-}
-
-__device__ __forceinline__ int uniform_wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-}
-
-__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
-
 // ---------------------------------------------------------------- route
 
-// Router dot products travel between kernels as partial sums:
-// part[t][e][k], k < nparts (row stride pstride), holds the sum over one
-// slice of the hidden dimension of w_r[e][h] * x[h] for the layer input x,
-// before the RMSNorm scale and the bias.  The route kernel writes one slice
-// (the whole of x); a down kernel that feeds the next layer writes one slice
-// per row block.  Column E holds the matching slices of the sum of squares
-// of x.  gate_up adds the slices in a fixed order, scales by the RMSNorm
-// factor, adds the bias and selects.  (RMSNorm is a per-token scale, so
-// w_r . (x * r) = r * (w_r . x).)
+// The route kernel writes slice 0 of the router partial sums (see
+// bdg_moe.hpp) for the layer input, and for grouped steps forms that input.
 
 struct RouteParams {
   int M, H, E;
@@ -293,14 +249,7 @@ __global__ void __launch_bounds__(kWave) moe_route_direct_kernel(RouteParams p) 
 
 struct GateUpParams {
   int M, H, I, E, K;
-  int routed;                 // 1: routing given in idx_in / w_in
-  const float* part;          // [M][E + 1][pstride] router partial sums (see the route section)
-  int nparts, pstride;
-  int log2T;                  // 2^log2T threads add up one expert's slices
-  int norm;                   // RMSNorm scale on x (and on the router input)
-  float eps;
-  const int32_t* idx_in;
-  const float* w_in;
+  RouteSrc rt;                // routing inputs (partial router sums, or the caller's routing)
   int32_t* idx_out;           // [M][K] routing buffer, written by block 0
   float* w_out;
   int32_t* topk_trace;        // [M][K] or NULL
@@ -310,8 +259,6 @@ struct GateUpParams {
   QGeom g;                    // reduction over H
   float* h_out;               // [M][K][I]
 };
-
-constexpr int kPartF4 = 8;    // float4 of router partial sums per thread issued up front
 
 // Wave gw of token t owns the (expert slot, row pair) range
 // [P*gw/GW, P*(gw+1)/GW) of the P = K*I pairs; the grid makes it <= NP.
@@ -332,52 +279,8 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
 
   // load order: routing inputs, then x (independent of the routing), then
   // the expert weights - the in-order wait for each stays short
-  const int lt = p.log2T;
-  const int T = 1 << lt;
-  const int sub = threadIdx.x & (T - 1);
-  const int n4 = (p.nparts + 3) >> 2;                      // float4 per expert row of slices
-  const int64_t pbase = (int64_t)t * (p.E + 1) * p.pstride;
-  const bool slices = !p.routed && p.nparts > 1;
-  float4 pv[kPartF4];
-  float lg[V], bias[V];
-  float ssq = 0.f;
-  int my_e = 0;
-  float my_w = 0.f;
-  if (p.routed) {
-    my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
-    my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
-  } else {
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int e = lane + kWave * i;
-      bias[i] = Ld.b_r ? Ld.b_r[e < p.E ? e : p.E - 1] : 0.f;
-    }
-    if (slices) {
-      const int c = threadIdx.x >> lt;
-      const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
-      // rows are zero past the nparts slices up to pstride >= 4 * T * kPartF4
-      // (the plan zeroes the buffer once; no kernel writes there)
-#pragma unroll
-      for (int i = 0; i < kPartF4; ++i) pv[i] = ldg_f4(row + 4 * (sub + (i << lt)));
-      // sum-of-squares slices (column E): one float4 per thread, n4 <= kThreads
-      const int k4 = threadIdx.x;
-      const float4 q = k4 < n4 ? ldg_f4(p.part + pbase + (int64_t)p.E * p.pstride + 4 * k4)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-      const int k = 4 * k4;
-      ssq = k < p.nparts ? q.x : 0.f;
-      ssq += k + 1 < p.nparts ? q.y : 0.f;
-      ssq += k + 2 < p.nparts ? q.z : 0.f;
-      ssq += k + 3 < p.nparts ? q.w : 0.f;
-    } else {
-      // one slice (the route kernel's): each wave reads its values directly
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int e = lane + kWave * i;
-        lg[i] = p.part[pbase + (int64_t)(e < p.E ? e : p.E - 1) * p.pstride];
-      }
-      ssq = p.part[pbase + (int64_t)p.E * p.pstride];
-    }
-  }
+  RouteState<V> rs;
+  route_issue<V, kThreads>(rs, p.rt, t, lane);
   constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // H <= 4096
   StageF32<NX> xstage;
   xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
@@ -394,66 +297,16 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   const int j0 = q0 / p.I;
   const int row0 = q0 - j0 * p.I;
 
-  float r = 1.0f;
-  if (slices) {
-    // slices of expert c: thread sub adds slices 4*(sub + i*T) .. +3, in order
-    for (int c0 = 0; c0 < p.E; c0 += kThreads >> lt) {
-      const int c = c0 + (threadIdx.x >> lt);
-      const float* row = p.part + pbase + (int64_t)(c < p.E ? c : p.E - 1) * p.pstride;
-      float a = 0.f;
-      int k4 = sub;
-      if (c0 == 0) {
-#pragma unroll
-        for (int i = 0; i < kPartF4; ++i, k4 += T) {
-          a += pv[i].x;
-          a += pv[i].y;
-          a += pv[i].z;
-          a += pv[i].w;
-        }
-      }
-      for (; k4 < n4; k4 += T) {   // beyond the slices loaded up front
-        const float4 v = ldg_f4(row + 4 * k4);
-        const int k = 4 * k4;
-        a += v.x;
-        a += k + 1 < p.nparts ? v.y : 0.f;
-        a += k + 2 < p.nparts ? v.z : 0.f;
-        a += k + 3 < p.nparts ? v.w : 0.f;
-      }
-      if (c < p.E) psum[(c << lt) + sub] = a;
-    }
-    {
-      const float ss = wave_sum(ssq);
-      if (lane == 0) red[wave] = ss;
-    }
-    __syncthreads();
-    if (p.norm) ssq = (red[0] + red[1]) + (red[2] + red[3]);
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int e = lane + kWave * i;
-      const float* ps = psum + ((e < p.E ? e : p.E - 1) << lt);
-      float a = 0.f;
-      for (int q = 0; q < T; ++q) a += ps[q];
-      lg[i] = a;
-    }
-  }
-  if (!p.routed) {
-    if (p.norm) r = 1.0f / sqrtf(ssq / (float)p.H + p.eps);
-#pragma unroll
-    for (int i = 0; i < V; ++i) lg[i] = r * lg[i] + bias[i];
-    topk_rank<V>(lg, p.E, p.K, my_e, my_w);
-  }
-  const float mult = r;
-  if (lane >= p.K) {
-    my_e = 0;
-    my_w = 0.f;
-  }
+  route_finish<V, kThreads>(rs, p.rt, t, lane, wave, red, psum);
+  const int my_e = rs.my_e;
+  const float my_w = rs.my_w;
+  const float mult = rs.r;
   if (blockIdx.x == 0 && wave == 0 && lane < p.K) {
     p.idx_out[t * p.K + lane] = my_e;
     p.w_out[t * p.K + lane] = my_w;
     if (p.topk_trace) p.topk_trace[t * p.K + lane] = my_e;
     if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
   }
-
 
   // every slot loads (a wave short of NP pairs repeats its last pair and
   // stores nothing for the repeats): no branch around the loads
@@ -474,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
 
   xstage.store(xs, p.H, p.H, 0, mult, threadIdx.x, kThreads);
   xs[p.g.chunks * kXStride + (threadIdx.x & (kChunkElems - 1))] = 0.f;   // the zero chunk (no branch)
-  __syncthreads();
+  block_sync_lds();   // weights still in flight: each pair's dot waits for its own rows only
   XRegs<FMT, L, S> xr;
   xr.load_zpad(xs, p.g.chunks, li);
 
@@ -498,26 +351,12 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
 
 struct DownParams {
   int M, H, I, E, K;
-  int residual;               // add x_prev
   const int32_t* idx;         // [M][K] routing buffer
-  const float* w;             // [M][K]
   const float* h;             // [M][K][I]
-  const float* x_prev;        // [M][H] layer input (residual)
-  float* x_out;               // [M][H] next layer's input, or NULL
-  float* y_out;               // [M][H] caller output, or NULL
-  float* trace_out;           // [M][H] copy of x_out (next layer's input trace), or NULL
-  // next layer's router partial sums over this block's rows (slice
-  // blockIdx.x of part_out) when route_next; then B <= 64 and
-  // E <= kDownWaves * kDnRouterPerWave
-  int route_next;
-  const float* wr_next;       // [E][H]
-  float* part_out;            // [M][E + 1][pstride]
-  int pstride;
+  DownOut o;                  // combine, residual, outputs, next layer's router slice
   LayerDev L;                 // this layer's weights
   QGeom g;                    // reduction over I
 };
-
-constexpr int kDnRouterPerWave = 8;   // next-layer router rows per down wave
 
 // Block (rb, t) of 8 waves: WPE = 8 / K waves per chosen expert (1 when
 // K >= 8; experts then go in groups of 8).  Wave w works on expert slot
@@ -560,7 +399,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
       load_row<FMT, L, S>(ld[i], m, p.g, row, active && row < p.H, li);
     }
     hstage.store(lds, nh, p.I, stride, 1.0f, threadIdx.x, blockDim.x);
-    __syncthreads();
+    block_sync_lds();   // weights still in flight
     if (active) {
       XRegs<FMT, L, S> xr;
       xr.load_zpad(lds + jw * stride, p.g.chunks, li);
@@ -571,7 +410,7 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
         if (li == kRowSumLane<L> && b < B) dpart[(jg + jw) * B + b] = d;
       }
     }
-    __syncthreads();
+    block_sync_lds();
   };
 
   // loads, in the order their data is needed (vmcnt retires in order): the
@@ -584,20 +423,9 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   StageF32<HV> h0;
   h0.load(p.h + (int64_t)t * p.K * p.I, min(kg, p.K) * p.I, threadIdx.x, blockDim.x);
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the scheduler would sink loads
-  // epilogue row of this lane (B <= 64); idle lanes repeat the block's last
-  // row, so their loads fall in lines the block reads anyway
-  const int orow = min(r0 + min(lane, B - 1), p.H - 1);
-  float wr[kDnRouterPerWave];                               // wr[i] = w_r'[wave + 8i][orow]
-  {
-    const float* wsrc = p.route_next ? p.wr_next : p.x_prev;
-#pragma unroll
-    for (int i = 0; i < kDnRouterPerWave; ++i) {
-      const int er = wave + kDownWaves * i;
-      wr[i] = wsrc[(int64_t)(p.route_next ? (er < p.E ? er : p.E - 1) : 0) * p.H + orow];
-    }
-  }
-  const float xp = p.x_prev[(int64_t)t * p.H + orow];
-  const float wk = p.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
+  DownEpiIn epi;
+  down_epilogue_load(epi, p.o, t, r0, B, lane, wave);
+  epi.wk = p.o.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
   __builtin_amdgcn_sched_barrier(0);
   // the zero chunk after each expert's h (h staging never writes it); no
   // branch: threads past the kg chunks repeat the last one's stores
@@ -615,60 +443,17 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
   }
 
   if (B <= kWave) {
-    // every wave forms the block's rows (row r0 + lane) and wave 0 stores
-    // them; with route_next, wave w reduces them against router rows
-    // w, w + 8, ... of the next layer
-    const int row = r0 + lane;
-    const bool ok = lane < B && row < p.H;
-    float v = p.residual ? xp : 0.f;
-    for (int j = 0; j < p.K; ++j)
-      v = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j)),
-                         dpart[j * B + (ok ? lane : 0)], v);
-    v = ok ? v : 0.f;
-    if (wave == 0 && ok) {
-      if (p.x_out) p.x_out[(int64_t)t * p.H + row] = v;
-      if (p.y_out) p.y_out[(int64_t)t * p.H + row] = v;
-      if (p.trace_out) p.trace_out[(int64_t)t * p.H + row] = v;
-    }
-    if (!p.route_next) return;
-    // all router rows of the wave (and the rows' sum of squares, column E)
-    // reduced together, one butterfly step at a time
-    constexpr int NA = kDnRouterPerWave + 1;
-    float a[NA];
-#pragma unroll
-    for (int i = 0; i < kDnRouterPerWave; ++i) a[i] = ok ? wr[i] * v : 0.f;
-    a[kDnRouterPerWave] = v * v;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor1(a[i]);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor2(a[i]);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += dpp_f32<0x141, 0xF>(a[i]);   // row_half_mirror
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] += dpp_f32<0x140, 0xF>(a[i]);   // row_mirror
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] = add_pair16(a[i]);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] = add_pair32(a[i]);
-    if (lane == 0) {
-      float* out = p.part_out + (int64_t)t * (p.E + 1) * p.pstride + blockIdx.x;
-#pragma unroll
-      for (int i = 0; i < kDnRouterPerWave; ++i) {
-        const int er = wave + kDownWaves * i;
-        if (er < p.E) out[(int64_t)er * p.pstride] = a[i];
-      }
-      if (wave == 0) out[(int64_t)p.E * p.pstride] = a[kDnRouterPerWave];
-    }
+    down_epilogue(p.o, epi, dpart, t, blockIdx.x, r0, B, lane, wave);
     return;
   }
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
     const int row = r0 + b;
     if (row >= p.H) continue;
-    float v = p.residual ? p.x_prev[(int64_t)t * p.H + row] : 0.f;
-    for (int j = 0; j < p.K; ++j) v = __builtin_fmaf(p.w[t * p.K + j], dpart[j * B + b], v);
-    if (p.x_out) p.x_out[(int64_t)t * p.H + row] = v;
-    if (p.y_out) p.y_out[(int64_t)t * p.H + row] = v;
-    if (p.trace_out) p.trace_out[(int64_t)t * p.H + row] = v;
+    float v = p.o.residual ? p.o.x_prev[(int64_t)t * p.H + row] : 0.f;
+    for (int j = 0; j < p.K; ++j) v = __builtin_fmaf(p.o.w[t * p.K + j], dpart[j * B + b], v);
+    if (p.o.x_out) p.o.x_out[(int64_t)t * p.H + row] = v;
+    if (p.o.y_out) p.o.y_out[(int64_t)t * p.H + row] = v;
+    if (p.o.trace_out) p.o.trace_out[(int64_t)t * p.H + row] = v;
   }
 }
 
@@ -890,11 +675,11 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
       const bool ok = row < p.I;
       load_row<FMT, L, S>(ld[i], expert_gu(Ld, e), p.g, is_up ? p.I + row : row, ok, li);
     }
-    __syncthreads();                                      // the previous item's x reads are done
+    block_sync_lds();                                     // the previous item's x reads are done
 #pragma unroll
     for (int k = 0; k < kGroupTT; ++k)
       if (k < nt) xst[k].store(xs + k * xstride, p.H, p.H, 0, gl.rt[gl.cpk[c][k] / p.K], threadIdx.x, kThreads);
-    __syncthreads();
+    block_sync_lds();                                     // weights still in flight
     const int nq = min(max(p.I - rw, 0), NP);
 #pragma unroll 1
     for (int k = 0; k < nt; ++k) {
@@ -971,11 +756,11 @@ __global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams
       const int row = r0 + (i * kWaves + wave) * RPW + rr;
       load_row<FMT, L, S>(ld[i], m, p.g, row, row < p.H, li);
     }
-    __syncthreads();
+    block_sync_lds();                                     // the previous item's h reads are done
 #pragma unroll
     for (int k = 0; k < kGroupTT; ++k)
       if (k < nt) hst[k].store(hs + k * hstride, p.I, p.I, 0, 1.0f, threadIdx.x, kThreads);
-    __syncthreads();
+    block_sync_lds();                                     // weights still in flight
 #pragma unroll 1
     for (int k = 0; k < nt; ++k) {
       XRegs<FMT, L, S> xr;
@@ -1061,6 +846,17 @@ struct bdg_plan {
   int g_bpc, g_nrb, g_dn_NR;
   float* dout;              // [max_m * K][H] down output per pick
   int32_t* chunks;          // chunk table
+  // fused per-layer kernel (steps of one token)
+  int fused_ok;
+  bdg::LayerConfig fused_cfg;
+  int fused_nblk, fused_B, fused_dn_blocks;
+  size_t fused_lds;
+  float* hbuf;              // [K * I] h exchanged between the fused kernel's blocks
+  unsigned* bar;            // grid barrier words (arrivals, generation), zero at create
+  unsigned* fault;          // fault word (moe_plan_check)
+  int wait_polls;
+  uint64_t* tl_stamps;      // timeline mode: [L][nblk][kLayerStamps] (lazily allocated)
+  int tl_active;            // set only inside moe_expert_decode_timeline
   int32_t* idx;
   float* w;
   float* h;
@@ -1080,7 +876,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Optional per-kernel timing: every launch takes the next start/stop event
 // pair (recorded by the runtime at kernel start and end) and notes its kind.
-enum KernelKind { kRoute = 0, kGateUp = 1, kDown = 2, kCombine = 3, kKinds = 4 };
+enum KernelKind { kRoute = 0, kGateUp = 1, kDown = 2, kCombine = 3, kLayer = 4, kKinds = 5 };
 
 struct Prof {
   hipEvent_t* ev;     // 2 * cap events
@@ -1152,6 +948,26 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
   return launch_status();
 }
 
+// Where a kernel that selects its own experts finds the routing of `layer`.
+static RouteSrc route_src(const bdg_plan* p, int layer, int routed, int nparts, const int32_t* idx_in,
+                          const float* w_in, int use_norm) {
+  RouteSrc r{};
+  r.routed = routed;
+  r.idx_in = idx_in;
+  r.w_in = w_in;
+  r.part = p->part;
+  r.nparts = nparts;
+  r.pstride = p->pstride;
+  r.log2T = p->log2T;
+  r.norm = use_norm;
+  r.eps = p->d.norm_eps;
+  r.E = p->d.n_experts;
+  r.K = p->d.top_k;
+  r.H = p->d.hidden;
+  r.b_r = p->hl[layer].b_r;
+  return r;
+}
+
 static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int nparts, const int32_t* idx_in,
                          const float* w_in, int32_t* topk_trace, float* wts_trace, int use_norm,
                          hipStream_t s, Prof* prof) {
@@ -1161,15 +977,7 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int np
   gp.I = p->d.inter;
   gp.E = p->d.n_experts;
   gp.K = p->d.top_k;
-  gp.routed = routed;
-  gp.part = p->part;
-  gp.nparts = nparts;
-  gp.pstride = p->pstride;
-  gp.log2T = p->log2T;
-  gp.norm = use_norm;
-  gp.eps = p->d.norm_eps;
-  gp.idx_in = idx_in;
-  gp.w_in = w_in;
+  gp.rt = route_src(p, layer, routed, nparts, idx_in, w_in, use_norm);
   gp.idx_out = p->idx;
   gp.w_out = p->w;
   gp.topk_trace = topk_trace;
@@ -1208,6 +1016,26 @@ static int down_stage_f4(int K, int I) {
   return (kg * I + kDownWaves * kWave * 4 - 1) / (kDownWaves * kWave * 4);
 }
 
+// The combine / residual / next-layer router outputs of `layer`'s down product.
+static DownOut down_out(const bdg_plan* p, int layer, int residual, float* x_out, float* y_out, float* trace_out,
+                        int route_next) {
+  DownOut o{};
+  o.H = p->d.hidden;
+  o.E = p->d.n_experts;
+  o.K = p->d.top_k;
+  o.residual = residual;
+  o.x_prev = p->resid[layer & 1];
+  o.w = p->w;
+  o.x_out = x_out;
+  o.y_out = y_out;
+  o.trace_out = trace_out;
+  o.route_next = route_next;
+  o.wr_next = route_next ? p->wr[layer + 1] : nullptr;
+  o.part_out = p->part;
+  o.pstride = p->pstride;
+  return o;
+}
+
 static int launch_down(const bdg_plan* p, int layer, int m, int residual, float* x_out, float* y_out,
                        float* trace_out, int route_next, hipStream_t s, Prof* prof) {
   DownParams dp{};
@@ -1216,18 +1044,9 @@ static int launch_down(const bdg_plan* p, int layer, int m, int residual, float*
   dp.I = p->d.inter;
   dp.E = p->d.n_experts;
   dp.K = p->d.top_k;
-  dp.residual = residual;
   dp.idx = p->idx;
-  dp.w = p->w;
   dp.h = p->h;
-  dp.x_prev = p->resid[layer & 1];
-  dp.x_out = x_out;
-  dp.y_out = y_out;
-  dp.trace_out = trace_out;
-  dp.route_next = route_next;
-  dp.wr_next = route_next ? p->wr[layer + 1] : nullptr;
-  dp.part_out = p->part;
-  dp.pstride = p->pstride;
+  dp.o = down_out(p, layer, residual, x_out, y_out, trace_out, route_next);
   dp.L = p->hl[layer];
   dp.g = p->dn_geom;
   const int rpw = kWave / p->dn_L;
@@ -1349,6 +1168,47 @@ static int launch_combine(const bdg_plan* p, int m, const float* x_prev, int res
   return launch_status();
 }
 
+// The fused per-layer kernel of a one-token step: routing from `nparts`
+// router slices, gate_up + SwiGLU, down + combine, and the outputs of
+// launch_down.
+static int launch_layer(const bdg_plan* p, int layer, int nparts, int32_t* topk_trace, float* wts_trace, int use_norm,
+                        int residual, float* x_out, float* y_out, float* trace_out, int route_next, hipStream_t s,
+                        Prof* prof) {
+  LayerParams lp{};
+  lp.H = p->d.hidden;
+  lp.I = p->d.inter;
+  lp.E = p->d.n_experts;
+  lp.K = p->d.top_k;
+  lp.rt = route_src(p, layer, 0, nparts, nullptr, nullptr, use_norm);
+  lp.idx_out = p->idx;
+  lp.w_out = p->w;
+  lp.topk_trace = topk_trace;
+  lp.wts_trace = wts_trace;
+  lp.x = p->resid[layer & 1];
+  lp.L = p->hl[layer];
+  lp.g_gu = p->gu_geom;
+  lp.g_dn = p->dn_geom;
+  lp.hbuf = p->hbuf;
+  lp.bar = p->bar;
+  lp.fault = p->fault;
+  lp.wait_polls = p->wait_polls;
+  lp.dn_blocks = p->fused_dn_blocks;
+  lp.B = p->fused_B;
+  lp.o = down_out(p, layer, residual, x_out, y_out, trace_out, route_next);
+  lp.stamps = p->tl_active ? p->tl_stamps + (size_t)layer * p->fused_nblk * kLayerStamps : nullptr;
+  if (prof) {
+    // start/stop events recorded by the runtime at the kernel's start and end
+    if (prof->used >= prof->cap) return BDG_E_UNSUPPORTED;
+    const int slot = prof->used++;
+    prof->kind[slot] = kLayer;
+    void* args[] = {&lp};
+    return hip_status(hipExtLaunchKernel(layer_fused_kernel(p->fused_cfg), dim3(p->fused_nblk),
+                                         dim3(layer_threads()), args, p->fused_lds, s, prof->ev[2 * slot],
+                                         prof->ev[2 * slot + 1], 0));
+  }
+  return launch_layer_fused(p->fused_cfg, lp, p->fused_nblk, p->fused_lds, s);
+}
+
 // A grouped step (M > 1): per layer route (forming the layer input from the
 // previous layer's per-pick outputs), grouped gate_up, grouped down; a final
 // combine writes y.
@@ -1386,6 +1246,16 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
     if (!fused) {
       st = launch_route(p, l, k.x, k.x_dtype, k.m, trace(l), 1, s, prof);
       if (st) return st;
+    }
+    if (k.m == 1 && p->fused_ok) {
+      const bool last = l + 1 == L;
+      const bool feed = !last && p->fuse_route;
+      st = launch_layer(p, l, fused ? p->dn_blocks : 1, k.topk_trace ? k.topk_trace + (int64_t)l * K : nullptr,
+                        k.wts_trace ? k.wts_trace + (int64_t)l * K : nullptr, stack, stack,
+                        last ? nullptr : p->resid[(l + 1) & 1], last ? k.y : nullptr, feed ? trace(l + 1) : nullptr,
+                        feed ? 1 : 0, s, prof);
+      if (st) return st;
+      continue;
     }
     st = launch_gateup(p, l, k.m, 0, fused ? p->dn_blocks : 1, nullptr, nullptr,
                        k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
@@ -1444,7 +1314,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     return BDG_E_INVALID;
   if (d->fmt != BDG_FMT_MXFP4 && d->fmt != BDG_FMT_INT4G) return BDG_E_INVALID;
   if ((d->hidden % 32) || (d->inter % 32)) return BDG_E_INVALID;
-  if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH | BDG_MOE_ROUTE_EVERY_LAYER | BDG_MOE_PER_TOKEN)) != 0)
+  if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH | BDG_MOE_ROUTE_EVERY_LAYER | BDG_MOE_PER_TOKEN |
+                    BDG_MOE_FUSED_LAYER)) != 0)
     return BDG_E_INVALID;
   if ((d->flags & BDG_MOE_STACK) && !(d->norm_eps >= 0.f)) return BDG_E_INVALID;
   if (d->top_k > BDG_MAX_TOPK || d->n_experts > BDG_MAX_EXPERTS || d->max_m > BDG_MAX_M)
@@ -1533,6 +1404,53 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   };
   p->gu_geom = geom(d->hidden);
   p->dn_geom = geom(d->inter);
+  p->wait_polls = d->wait_polls == 0 ? (1 << 20) : (d->wait_polls < 0 ? 0 : d->wait_polls);
+  {
+    // fused per-layer kernel for one-token steps (BDG_MOE_FUSED_LAYER): one
+    // block of 8 waves per CU, all blocks resident (the grid waits on
+    // itself); block b < dn_blocks owns B down rows of every chosen expert.
+    // Shapes without a compiled variant, or whose grid would not be
+    // resident, keep two kernels.
+    int dev = 0, cus = 0;
+    p->fused_ok = 0;
+    const int K = d->top_k;
+    const int rpw = kWave / p->dn_L;
+    if ((d->flags & BDG_MOE_FUSED_LAYER) && K <= 8 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+      const int nblk = cus;
+      int B = rpw;
+      while ((d->hidden + B - 1) / B > nblk) B += rpw;
+      const int groups = K * (B / rpw);
+      const int ng = (groups + layer_dn_load_waves() - 1) / layer_dn_load_waves();
+      const int64_t pairs = (int64_t)K * d->inter;
+      const int np = (int)((pairs + (int64_t)nblk * 8 - 1) / ((int64_t)nblk * 8));
+      const int64_t nh = (pairs + layer_threads() - 1) / layer_threads();
+      const int nhl = nh <= 12 ? 12 : nh <= 24 ? 24 : 0;
+      LayerConfig c{d->fmt == BDG_FMT_MXFP4 ? (int)kMXFP4 : (int)kINT4G, p->gu_S, np, p->topk_V, p->dn_L, p->dn_S,
+                    ng, nhl};
+      LayerShape sh{p->gu_geom, p->dn_geom, K, d->n_experts, p->log2T, B};
+      const int lds = layer_fused_lds_bytes(sh, np, ng, p->dn_S);
+      const void* fn = layer_fused_kernel(c);
+      const int dn_blocks = (d->hidden + B - 1) / B;
+      // the epilogue's router slices must match what the next layer adds up
+      const bool slices_match = !p->fuse_route || dn_blocks == p->dn_blocks;
+      int per_cu = 0;
+      if (fn && B <= kWave && nhl > 0 && slices_match && lds <= 160 * 1024) {
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, layer_threads(), (size_t)lds) != hipSuccess)
+          per_cu = 0;
+        (void)hipGetLastError();
+      }
+      if (per_cu >= 1) {
+        p->fused_ok = 1;
+        p->fused_cfg = c;
+        p->fused_nblk = nblk;
+        p->fused_B = B;
+        p->fused_dn_blocks = dn_blocks;
+        p->fused_lds = (size_t)lds;
+      }
+    }
+  }
   // device memory: layer table + workspace
   const int M = d->max_m, H = d->hidden, I = d->inter, E = d->n_experts, K = d->top_k;
   size_t off = 0;
@@ -1544,6 +1462,9 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_h = off; off = align256(off + sizeof(float) * (size_t)M * K * I);
   const size_t o_dout = off; off = align256(off + sizeof(float) * (size_t)M * K * H);
   const size_t o_chunks = off; off = align256(off + sizeof(int32_t) * (1 + kGroupMaxPicks * kChunkInts));
+  const size_t o_hbuf = off; off = align256(off + sizeof(float) * (size_t)K * I);
+  const size_t o_bar = off; off = align256(off + sizeof(unsigned) * 64);
+  const size_t o_fault = off; off = align256(off + sizeof(unsigned) * 64);
   if (hipMalloc(&p->dev_base, off) != hipSuccess) {
     delete p;
     return BDG_E_NOMEM;
@@ -1557,6 +1478,9 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->h = reinterpret_cast<float*>(base + o_h);
   p->dout = reinterpret_cast<float*>(base + o_dout);
   p->chunks = reinterpret_cast<int32_t*>(base + o_chunks);
+  p->hbuf = reinterpret_cast<float*>(base + o_hbuf);
+  p->bar = reinterpret_cast<unsigned*>(base + o_bar);
+  p->fault = reinterpret_cast<unsigned*>(base + o_fault);
   // router partial sums: zero once, so slots past the slices read as 0
   if (hipMemset(p->part, 0, sizeof(float) * (size_t)M * (E + 1) * p->pstride) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
@@ -1594,6 +1518,7 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   }
   p->hl = host;
   hipError_t e2 = hipMemset(base + o_res0, 0, off - o_res0);
+  if (e2 == hipSuccess) e2 = hipDeviceSynchronize();   // zeroed before any stream uses it
   hipError_t e3 = hipStreamCreateWithFlags(&p->cap_stream, hipStreamNonBlocking);
   if (e2 != hipSuccess || e3 != hipSuccess) {
     if (e3 == hipSuccess) (void)hipStreamDestroy(p->cap_stream);
@@ -1619,11 +1544,37 @@ extern "C" int moe_plan_destroy(bdg_plan* p) {
     delete[] p->prof_ev;
     delete[] p->prof_kind;
   }
+  if (p->tl_stamps) (void)hipFree(p->tl_stamps);
   (void)hipFree(p->dev_base);
   delete[] p->wr;
   delete[] p->hl;
   delete p;
   return BDG_OK;
+}
+
+extern "C" int64_t moe_expert_decode_timeline(bdg_plan* p, const void* x, int32_t x_dtype, float* y,
+                                              uint64_t* stamps, int64_t max_stamps, void* stream) {
+  if (!p || !x || !y || !stamps) return BDG_E_INVALID;
+  if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return BDG_E_ALIGN;
+  if (!p->fused_ok) return BDG_E_UNSUPPORTED;
+  const int64_t n = (int64_t)p->d.n_layers * p->fused_nblk * kLayerStamps;
+  if (max_stamps < n) return BDG_E_INVALID;
+  if (!p->tl_stamps && hipMalloc(&p->tl_stamps, n * sizeof(uint64_t)) != hipSuccess) {
+    p->tl_stamps = nullptr;
+    return BDG_E_NOMEM;
+  }
+  hipStream_t s = as_stream(stream);
+  if (hipMemsetAsync(p->tl_stamps, 0, n * sizeof(uint64_t), s) != hipSuccess) return BDG_E_HIP;
+  GraphKey key{x, x_dtype, 1, y, nullptr, nullptr, nullptr};
+  p->tl_active = 1;
+  const int st = enqueue_decode(p, key, s);
+  p->tl_active = 0;
+  if (st) return st;
+  if (hipMemcpyAsync(stamps, p->tl_stamps, n * sizeof(uint64_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return BDG_E_HIP;
+  return n;
 }
 
 extern "C" int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
@@ -1632,7 +1583,7 @@ extern "C" int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_
   if (m > p->d.max_m) return BDG_E_INVALID;
   if (x_dtype != BDG_F32 && x_dtype != BDG_BF16) return BDG_E_INVALID;
   if (!aligned16(x) || !aligned16(y)) return BDG_E_ALIGN;
-  const int need = 3 * p->d.n_layers + 1;
+  const int need = 3 * p->d.n_layers + 1;   // at most route + gate_up + down per layer, + combine
   if (!p->prof_ev) {
     p->prof_ev = new (std::nothrow) hipEvent_t[2 * need];
     p->prof_kind = new (std::nothrow) int[need];
@@ -1654,6 +1605,20 @@ extern "C" int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_
     kernel_count[p->prof_kind[i]] += 1;
   }
   return BDG_OK;
+}
+
+extern "C" int moe_plan_check(bdg_plan* p, void* stream) {
+  if (!p) return BDG_E_INVALID;
+  hipStream_t s = as_stream(stream);
+  unsigned v = 0;
+  if (hipMemcpyAsync(&v, p->fault, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return BDG_E_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return BDG_E_HIP;
+  if (v == 0) return BDG_OK;
+  const unsigned zero = 0;
+  if (hipMemcpyAsync(p->fault, &zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return BDG_E_HIP;
+  return BDG_E_WAIT;
 }
 
 extern "C" int moe_expert_decode(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,

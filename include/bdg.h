@@ -69,6 +69,7 @@ extern "C" {
 #define BDG_E_HIP -4         /* a HIP runtime call or kernel launch failed */
 #define BDG_E_NOMEM -5       /* device allocation failed */
 #define BDG_E_TOO_LARGE -6   /* request exceeds the static scratch of an allocation-free entry point */
+#define BDG_E_WAIT -7        /* a bounded wait inside a kernel gave up (its outputs were made NaN) */
 
 /* ---- activation dtypes ---- */
 #define BDG_F32 0
@@ -168,6 +169,11 @@ typedef struct bdg_layer_desc {
 #define BDG_MOE_PER_TOKEN 8  /* steps of m > 1 tokens run the per-token kernels (each pick reads
                                 its expert) instead of the grouped kernels (each distinct
                                 expert read once per step); same results bit for bit */
+#define BDG_MOE_FUSED_LAYER 16  /* m = 1 steps run each layer as one kernel that streams the down
+                                   weights into LDS behind the gate_up weights and exchanges h
+                                   through a grid barrier, instead of two kernels (gate_up +
+                                   SwiGLU, then down + combine); same results bit for bit.
+                                   Slower on MI355X (measured); kept for A/B measurement */
 
 typedef struct bdg_moe_desc {
   int32_t n_layers;
@@ -181,6 +187,9 @@ typedef struct bdg_moe_desc {
   float norm_eps;      /* RMSNorm eps (stack only), e.g. 1e-5 */
   int32_t max_m;       /* largest m a decode call will pass, <= BDG_MAX_M */
   const bdg_layer_desc* layers;   /* n_layers entries; copied at create */
+  int32_t wait_polls;  /* bound of the fused kernel's in-kernel wait, in polls of about a
+                          microsecond: 0 = the default (2^20, about a second); a negative value
+                          makes every wait give up at once (exercises the failure path) */
 } bdg_moe_desc;
 
 typedef struct bdg_plan bdg_plan;
@@ -203,6 +212,16 @@ int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out);
  * Waits for the device to finish queued work first, since captured graphs
  * and the workspace may still be in use.  NULL is accepted.  Returns BDG_OK. */
 int moe_plan_destroy(bdg_plan* p);
+
+/* moe_plan_check - report and clear the plan's fault word: BDG_E_WAIT if,
+ * since the last check, a bounded wait inside the fused per-layer kernel
+ * gave up (the blocks that gave up wrote NaN outputs, so the step's y holds
+ * NaN), else BDG_OK.  Such a wait holds a block until every block of the
+ * layer has published its h; it gives up only when blocks of the grid could
+ * not run (the device shared with other work for about a second) or when
+ * wait_polls is negative.  Waits for the plan's work queued on `stream`
+ * (synchronous). */
+int moe_plan_check(bdg_plan* p, void* stream);
 
 /* moe_expert_decode - one decode step of m tokens through every layer of
  * the plan: per layer the router, top-k + softmax, the chosen experts'
@@ -397,11 +416,26 @@ int attn_decode_noalloc(const float* q, const float* k, const float* v, void* k_
  * GEMV + sum of squares, and for steps of m > 1 the previous layer's
  * combine), 1 = gate_up (top-k + grouped gate_up GEMV + SwiGLU), 2 = down
  * (grouped down GEMV; combine + residual when m = 1), 3 = the final combine
- * of an m > 1 step; host arrays of at least 4.
+ * of an m > 1 step, 4 = the fused per-layer kernel; host arrays of at
+ * least 5.
  * Synchronises on the last event before returning.  Used by the benchmark
  * for per-kernel roofline figures. */
 int moe_expert_decode_profiled(bdg_plan* p, const void* x, int32_t x_dtype, int32_t m, float* y,
                                double* kernel_ms, int64_t* kernel_count, void* stream);
+
+/* moe_expert_decode_timeline - one single-token decode step exactly as
+ * moe_expert_decode computes it on the fused per-layer path (launched
+ * directly, not from a graph), with each block of each layer kernel
+ * stamping the GPU's 100 MHz clock at its phase boundaries: routing done,
+ * gate_up loads issued, down codes issued, h computed, h stored, barrier
+ * passed, h staged, down rows done, end (see LayerStamp in the sources).
+ * stamps (host) receives [n_layers][blocks][16] uint64 (0 = not reached);
+ * returns the count written, or a negative status (BDG_E_UNSUPPORTED when
+ * the plan does not use the fused kernel).  Synchronous; allocates a stamp
+ * buffer in the plan on first use.  For measuring where a layer's time
+ * goes. */
+int64_t moe_expert_decode_timeline(bdg_plan* p, const void* x, int32_t x_dtype, float* y, uint64_t* stamps,
+                                   int64_t max_stamps, void* stream);
 
 /* bdg_stream_read - read `bytes` (a multiple of 16) of device memory with
  * 16-byte coalesced loads and write one fp32 checksum per workgroup into
