@@ -101,6 +101,160 @@ def measured_traffic(workload, kernel, sources=KERNEL_SOURCES):
     return None if t is None else t["fetch_bytes"] + t["write_bytes"]
 
 
+# ---------------------------------------------------------------- rocprofv3 summaries
+#
+# `python bench.py summarize ...` turns rocprofv3 CSV output (kernel-trace
+# statistics, FETCH_SIZE / WRITE_SIZE passes, SQ counter passes) into the
+# text summaries kept under profiles/.  Host-only; reads the CSV files given.
+
+KERNEL_KIND_PATTERNS = (          # kernel name fragment -> kind (per-launch traffic keys)
+    ("moe_layer_kernel", "layer"), ("moe_gateup_kernel", "gate_up"), ("moe_gu_group_kernel", "gate_up"),
+    ("moe_down_kernel", "down"), ("moe_dn_group_kernel", "down"), ("moe_route", "route"),
+    ("moe_combine_kernel", "combine"), ("qgemv_kernel", "qgemv"), ("attn_split_kernel", "attn_split"),
+    ("attn_merge_kernel", "attn_merge"), ("mx_gemm_kernel", "mx_gemm"), ("stream_copy_kernel", "copy"),
+)
+
+
+def kernel_kind(name):
+    for frag, kind in KERNEL_KIND_PATTERNS:
+        if frag in name:
+            return kind
+    return None
+
+
+def short_kernel(name):
+    name = name.split("(")[0]
+    return name.replace("void ", "").replace("bdg::", "")
+
+
+def _find(src, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(src, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {src}")
+    return hits[0]
+
+
+def _counter_rows(src):
+    import csv
+    return list(csv.DictReader(open(_find(src, "counter_collection.csv"))))
+
+
+def _per_kernel_counter(src, counter):
+    """{kernel name: [value per dispatch]} for one counter of a pass."""
+    out = {}
+    for r in _counter_rows(src):
+        if r["Counter_Name"] == counter:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize(argv):
+    import csv
+    import statistics as st
+    ap = argparse.ArgumentParser(prog="bench.py summarize")
+    ap.add_argument("what", choices=["trace", "traffic", "sq"])
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--src", help="rocprofv3 output directory (trace or SQ pass)")
+    ap.add_argument("--fetch", help="FETCH_SIZE pass of the workload")
+    ap.add_argument("--write", help="WRITE_SIZE pass of the workload")
+    ap.add_argument("--cal-fetch", help="FETCH_SIZE pass of bench.py --copy-calibration BYTES")
+    ap.add_argument("--cal-write", help="WRITE_SIZE pass of the same")
+    ap.add_argument("--cal-bytes", type=int, default=268435456)
+    ap.add_argument("--command", action="append", default=[], help="the rocprofv3 command(s), for the record")
+    ap.add_argument("--note", default="", help="a paragraph of reading under the table")
+    ap.add_argument("--name", default=None, help="output file stem (default: kind_workload)")
+    ap.add_argument("--sources", default="moe", choices=["moe", "attn"])
+    a = ap.parse_args(argv)
+    srcs = KERNEL_SOURCES if a.sources == "moe" else ATTN_SOURCES
+    sha = kernel_sources_sha(srcs)
+    cmds = "\n".join(f"    {c}" for c in a.command)
+    if a.what == "trace":
+        rows = list(csv.DictReader(open(_find(a.src, "kernel_stats.csv"))))
+        total = sum(float(r["TotalDurationNs"]) for r in rows)
+        lines = [f"# Kernel trace: {a.workload}", "", "Command (from the repository root, on one MI355X):", "",
+                 cmds, "",
+                 "rocprofv3 kernel statistics.  In a run of back-to-back launches (graph replays) a",
+                 "kernel's recorded start is the previous kernel's end, so each duration covers the",
+                 "kernel and the launch gap before it, and the durations tile the replayed steps.", "",
+                 "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| `{short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{100.0 * float(r['TotalDurationNs']) / total:.1f}% |")
+        stem = a.name or f"kernel_trace_{a.workload}"
+    elif a.what == "traffic":
+        calf = _per_kernel_counter(a.cal_fetch, "FETCH_SIZE")
+        calw = _per_kernel_counter(a.cal_write, "WRITE_SIZE")
+        kib = a.cal_bytes / 1024.0
+        cf = st.mean(next(v for k, v in calf.items() if "bdg_stream_copy" in k or "copy_kernel" in k))
+        cw = st.mean(next(v for k, v in calw.items() if "bdg_stream_copy" in k or "copy_kernel" in k))
+        fs, ws = kib / cf, kib / cw
+        fetch = _per_kernel_counter(a.fetch, "FETCH_SIZE")
+        write = _per_kernel_counter(a.write, "WRITE_SIZE")
+        per, table = {}, []
+        for name, vals in sorted(fetch.items()):
+            kind = kernel_kind(name)
+            if kind is None or kind == "copy":
+                continue
+            f = st.mean(vals)
+            w = st.mean(write.get(name, [0.0]))
+            fb, wb = int(round(f * fs * 1024)), int(round(w * ws * 1024))
+            prev = per.get(kind)
+            n = len(vals)
+            if prev:      # several template instances of one kind: launch-weighted mean
+                tot = prev["launches"] + n
+                fb = int(round((prev["fetch_bytes"] * prev["launches"] + fb * n) / tot))
+                wb = int(round((prev["write_bytes"] * prev["launches"] + wb * n) / tot))
+                n = tot
+            per[kind] = {"fetch_bytes": fb, "write_bytes": wb, "launches": n}
+            table.append(f"| `{short_kernel(name)}` | {len(vals)} | {f:.1f} | {w:.1f} | {int(round(f * fs * 1024)):,} "
+                         f"| {int(round(w * ws * 1024)):,} |")
+        lines = [f"# HBM traffic per launch: {a.workload}", "",
+                 "Commands (one counter pass each; FETCH_SIZE and WRITE_SIZE cannot share a pass):", "",
+                 cmds, "",
+                 f"Calibration: the 16-byte copy kernel over {a.cal_bytes} B reads and writes {kib:.0f} KiB;",
+                 f"the counters read FETCH_SIZE {cf:.1f} KiB (scale x{fs:.3f}) and WRITE_SIZE {cw:.1f} KiB "
+                 f"(scale x{ws:.3f}) per launch.", "",
+                 "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) |",
+                 "|---|---|---|---|---|---|"] + table
+        rec = {"workload": a.workload, "kernel_sources_sha": sha, "fetch_scale": fs, "write_scale": ws,
+               "per_launch": {k: {"fetch_bytes": v["fetch_bytes"], "write_bytes": v["write_bytes"]}
+                              for k, v in per.items()}}
+        stem = a.name or f"hbm_traffic_{a.workload}"
+        json.dump(rec, open(os.path.join(ROOT, "profiles", stem + ".json"), "w"), indent=1)
+    else:
+        ctr = {}
+        for r in _counter_rows(a.src):
+            ctr.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        lines = [f"# SQ counters: {a.workload}", "",
+                 "Command (from the repository root, on one MI355X; a counter pass of its own, no trace options):",
+                 "", cmds, "",
+                 "Counters averaged over the dispatches of the run.  The ratio columns divide counters that",
+                 "share a unit (wave-cycles summed over all waves): SQ_ACTIVE_INST_VALU, SQ_WAIT_ANY and",
+                 "SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.", "",
+                 "| kernel | dispatches | waves / dispatch | VALU instr / wave | VMEM read instr / wave | "
+                 "VALU active / wave-cycles | waiting (any) / wave-cycles | waiting for issue / wave-cycles |",
+                 "|---|---:|---:|---:|---:|---:|---:|---:|"]
+        for name, c in sorted(ctr.items()):
+            if kernel_kind(name) is None or "SQ_WAVES" not in c:
+                continue
+            m = {k: st.mean(v) for k, v in c.items()}
+            wv = max(m["SQ_WAVES"], 1.0)
+            wc = max(m.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+            lines.append(f"| `{short_kernel(name)}` | {len(c['SQ_WAVES'])} | {wv:.0f} | "
+                         f"{m.get('SQ_INSTS_VALU', 0) / wv:.0f} | {m.get('SQ_INSTS_VMEM_RD', 0) / wv:.1f} | "
+                         f"{m.get('SQ_ACTIVE_INST_VALU', 0) / wc:.2f} | {m.get('SQ_WAIT_ANY', 0) / wc:.2f} | "
+                         f"{m.get('SQ_WAIT_INST_ANY', 0) / wc:.2f} |")
+        stem = a.name or f"sq_counters_{a.workload}"
+    if a.note:
+        lines += ["", a.note]
+    lines += ["", f"Kernel sources sha256[:16]: `{sha}`", ""]
+    path = os.path.join(ROOT, "profiles", stem + ".md")
+    open(path, "w").write("\n".join(lines))
+    print(path)
+
+
 def blas_threads():
     """Threads the oracle's NumPy BLAS uses (its matrix products run on them)."""
     from threadpoolctl import threadpool_info
@@ -577,6 +731,12 @@ def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     nbytes = step_bytes(cfg, [cfg.top_k])
     value = nbytes * K / (gpu_ms * 1e-3) / 1e9
     log(f"timed {K} tokens: {gpu_ms / K * 1e3:.2f} us/token, {value:.1f} GB/s")
+    if args.graph_only:
+        print(json.dumps({"workload": cfg.name, "steps": K, "us_per_token": round(gpu_ms / K * 1e3, 2)}),
+              flush=True)
+        for pl in plans:
+            pl.close()
+        return
     acc = None
     for t in range(W, W + K):
         x_buf.copy_(x_all[t])
@@ -802,6 +962,9 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")
+    ap.add_argument("--mfma", action="store_true",
+                    help="steps of M > 1: the grouped expert products on the matrix cores (BDG_MOE_MFMA) "
+                         "instead of the VALU kernels (A/B)")
     ap.add_argument("--fused-layer", action="store_true",
                     help="one-token steps run each layer as the fused per-layer kernel instead of two "
                          "kernels (gate_up, down): the A/B of the fused design")
@@ -869,7 +1032,8 @@ def main():
         layers.append(sdev.upload_layer(cfg, l, dev, threads=16))
         if l % 6 == 5 or l == cfg.n_layers - 1:
             log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.1f} s)")
-    plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers, fused_layer=args.fused_layer or args.timeline)
+    plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers, fused_layer=args.fused_layer or args.timeline,
+                              mfma=args.mfma)
     x_all, _ = sdev.hidden_device(cfg, range((W + K) * m), dev)
     x_all = x_all.reshape(W + K, m, cfg.hidden)
     x_buf = torch.empty_like(x_all[0])
@@ -1013,7 +1177,9 @@ def main():
         "experts": cfg.n_experts, "top_k": cfg.top_k, "m": m,
         "bytes_per_step": int(round(nbytes / K)),
         "timing": "HIP graph per step (M tokens), stream-ordered",
-        "layer_kernels": "fused per-layer kernel" if fused else "two kernels per layer (gate_up, down)",
+        "layer_kernels": ("fused per-layer kernel" if fused else
+                          "grouped gate_up and down on the matrix cores" if (m > 1 and args.mfma) else
+                          "two kernels per layer (gate_up, down)"),
     }
     if routing:
         config["routing"] = routing
@@ -1057,4 +1223,7 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize":
+        summarize(sys.argv[2:])
+    else:
+        main()

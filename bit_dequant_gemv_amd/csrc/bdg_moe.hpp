@@ -297,4 +297,148 @@ __device__ __forceinline__ void down_epilogue(const DownOut& o, const DownEpiIn&
   }
 }
 
+// ---------------------------------------------------------------- expert grouping (steps of M > 1)
+//
+// Every block of a grouped kernel routes all M tokens of the step and builds
+// the same deterministic table of "chunks": the distinct chosen experts in
+// ascending order, each with its picks (p = t*K + j) in pick order, TT picks
+// per chunk (an expert with more picks spans several chunks).
+
+constexpr int kGroupMaxPicks = 128;   // M * K bound of the grouped path
+
+template <int TT>
+struct GroupLdsT {
+  int sel_e[kGroupMaxPicks];          // pick p = t*K + j -> expert
+  float rt[BDG_MAX_M];                // RMSNorm scale per token
+  unsigned used[BDG_MAX_EXPERTS / 32];
+  int ppc[BDG_MAX_EXPERTS / 32 + 1];  // prefix popcounts of used[]
+  int cnt[kGroupMaxPicks];            // picks per distinct expert (by rank)
+  int cbase[kGroupMaxPicks + 1];      // first chunk of each distinct expert
+  int n;                              // chunks
+  int ce[kGroupMaxPicks];             // expert of chunk c
+  int cn[kGroupMaxPicks];             // picks in chunk c
+  int cpk[kGroupMaxPicks][TT];        // the picks of chunk c
+};
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Chunks of the P picks in g.sel_e.  The block's threads all call it; the
+// result does not depend on thread timing (the only atomics are an OR and a
+// count).  P <= kGroupMaxPicks, blockDim >= kGroupMaxPicks.
+static_assert(BDG_MAX_EXPERTS / 32 <= kWave, "build_groups scans the used-expert words in one wave");
+template <int TT>
+__device__ void build_groups(GroupLdsT<TT>& g, int P, int E) {
+  const int tid = threadIdx.x;
+  const int nw = (E + 31) >> 5;
+  if (tid < nw) g.used[tid] = 0u;
+  if (tid < P) g.cnt[tid] = 0;
+  __syncthreads();
+  if (tid < P) atomicOr(&g.used[g.sel_e[tid] >> 5], 1u << (g.sel_e[tid] & 31));
+  __syncthreads();
+  if (tid < kWave) {
+    const int pc = wave_scan_incl(tid < nw ? __popc(g.used[tid]) : 0);
+    if (tid < nw) g.ppc[tid + 1] = pc;
+    if (tid == 0) g.ppc[0] = 0;
+  }
+  __syncthreads();
+  int my_u = 0, my_pos = 0;
+  if (tid < P) {
+    const int e = g.sel_e[tid];
+    my_u = g.ppc[e >> 5] + __popc(g.used[e >> 5] & ((1u << (e & 31)) - 1u));
+    for (int q = 0; q < tid; ++q) my_pos += g.sel_e[q] == e ? 1 : 0;
+    atomicAdd(&g.cnt[my_u], 1);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int U = g.ppc[nw];
+    const int a = tid < U ? (g.cnt[tid] + TT - 1) / TT : 0;
+    const int b = tid + kWave < U ? (g.cnt[tid + kWave] + TT - 1) / TT : 0;
+    const int sa = wave_scan_incl(a);
+    const int sb = wave_scan_incl(b);
+    const int tot_a = __shfl(sa, kWave - 1);
+    g.cbase[tid] = sa - a;
+    g.cbase[tid + kWave] = tot_a + sb - b;
+    if (tid == kWave - 1) g.n = tot_a + sb;
+  }
+  __syncthreads();
+  if (tid < P) {
+    const int c = g.cbase[my_u] + my_pos / TT;
+    const int k = my_pos % TT;
+    g.cpk[c][k] = tid;
+    if (k == 0) {
+      g.ce[c] = g.sel_e[tid];
+      g.cn[c] = min(TT, g.cnt[my_u] - my_pos);
+    }
+  }
+  __syncthreads();
+}
+
+// Routing of every token of the step (a share of the tokens per wave, NW
+// waves), then the chunk table; block 0 also writes the routing outputs.
+// GP: a parameter block with M, H, E, K, routed, idx_in, w_in, part, pstride,
+// norm, eps, idx_out, w_out, topk_trace, wts_trace and L (LayerDev).
+template <int V, int TT, class GP>
+__device__ void group_route(GroupLdsT<TT>& gl, const GP& p, int lane, int wave, int NW) {
+  for (int t = wave; t < p.M; t += NW) {
+    int my_e = 0;
+    float my_w = 0.f, r = 1.f;
+    if (p.routed) {
+      my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
+      my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
+    } else {
+      const int64_t pb = (int64_t)t * (p.E + 1) * p.pstride;
+      float lg[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = lane + kWave * i;
+        const int ec = e < p.E ? e : p.E - 1;
+        lg[i] = p.part[pb + (int64_t)ec * p.pstride];
+      }
+      const float ssq = p.part[pb + (int64_t)p.E * p.pstride];
+      if (p.norm) r = 1.0f / sqrtf(ssq / (float)p.H + p.eps);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = lane + kWave * i;
+        lg[i] = r * lg[i] + (p.L.b_r ? p.L.b_r[e < p.E ? e : p.E - 1] : 0.f);
+      }
+      topk_rank<V>(lg, p.E, p.K, my_e, my_w);
+    }
+    if (lane < p.K) {
+      gl.sel_e[t * p.K + lane] = my_e;
+      if (blockIdx.x == 0) {
+        p.idx_out[t * p.K + lane] = my_e;
+        p.w_out[t * p.K + lane] = my_w;
+        if (p.topk_trace) p.topk_trace[t * p.K + lane] = my_e;
+        if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
+      }
+    }
+    if (lane == 0) gl.rt[t] = r;
+  }
+  __syncthreads();
+  build_groups<TT>(gl, p.M * p.K, p.E);
+}
+
+// The chunk table as the down kernels read it: [0] = chunks, then per chunk
+// (expert, picks, pick 0 .. pick TT-1).
+template <int TT>
+__device__ void write_chunk_table(const GroupLdsT<TT>& gl, int32_t* out, int nthreads) {
+  if (threadIdx.x == 0) out[0] = gl.n;
+  for (int c = threadIdx.x; c < gl.n; c += nthreads) {
+    int32_t* o = out + 1 + c * (2 + TT);
+    o[0] = gl.ce[c];
+    o[1] = gl.cn[c];
+#pragma unroll
+    for (int k = 0; k < TT; ++k) o[2 + k] = k < gl.cn[c] ? gl.cpk[c][k] : 0;
+  }
+}
+
 }  // namespace bdg

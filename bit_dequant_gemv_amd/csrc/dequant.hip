@@ -27,14 +27,18 @@ mxfp4_dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restric
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
   } else {
+    // bf16 through gfx950's scaled FP4 -> bf16 conversion, the instruction
+    // the matrix-core decode path uses: E2M1 times 2^(e-127) is exact in
+    // bf16 (subnormals included), so this is the fp32 value above rounded
+    // to nearest even (+-inf where that overflows, NaN for e = 255)
     uint4* o = reinterpret_cast<uint4*>(out) + t * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t p[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        p[j] = (uint32_t)f32_to_bf16_rne(v[8 * i + 2 * j]) | ((uint32_t)f32_to_bf16_rne(v[8 * i + 2 * j + 1]) << 16);
-      o[i] = make_uint4(p[0], p[1], p[2], p[3]);
+      const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], s, 0));
+      const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], s, 1));
+      const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], s, 2));
+      const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], s, 3));
+      o[i] = make_uint4(p0, p1, p2, p3);
     }
   }
   (void)chunks_per_row;

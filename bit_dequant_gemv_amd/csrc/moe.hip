@@ -25,7 +25,6 @@
 //            rows, which saves that layer's route kernel.
 // A whole token is one captured HIP graph (the per-token setup amortised as
 // in the host-sync page, section 3).
-#include <hip/hip_ext.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -35,6 +34,7 @@
 #include "bdg_host.hpp"
 #include "bdg_moe.hpp"
 #include "bdg_moe_layer.hpp"
+#include "bdg_moe_mfma.hpp"
 
 namespace bdg {
 
@@ -59,6 +59,12 @@ struct RouteParams {
   int K;
   int combine_residual;
   LayerDev L;         // this layer's weights (a kernel argument: no dependent table load)
+  // the matrix-core path's operands (written by block 0, or NULL): the layer
+  // input times its RMSNorm factor (1 without norm or logits) as bf16 parts
+  uint16_t* xh;       // [M][H] hi = bf16(v)
+  uint16_t* xl;       // [M][H] lo = bf16(v - hi)
+  int norm;
+  float eps;
 };
 
 // One router row per wavefront; block b handles rows 4b .. 4b+3 of token t.
@@ -158,6 +164,24 @@ __global__ void __launch_bounds__(kThreads) moe_route_kernel(RouteParams p) {
     }
     ss = wave_sum(ss);
     if (lane == 0) p.part[((int64_t)t * (p.E + 1) + p.E) * p.pstride] = ss;
+    // the RMSNorm factor as the gate_up kernels compute it from this sum
+    if (lane == 0) xs[p.H] = (p.norm ? 1.0f / sqrtf(ss / (float)p.H + p.eps) : 1.0f);
+  }
+  if (p.xh && blockIdx.x == 0) {   // block-uniform
+    __syncthreads();
+    const float r = p.compute_logits ? xs[p.H] : 1.0f;
+    for (int h = threadIdx.x * 4; h < p.H; h += kThreads * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xs + h);
+      const float vv[4] = {v.x * r, v.y * r, v.z * r, v.w * r};
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = f32_to_bf16_rne(vv[i]);
+        lo[i] = f32_to_bf16_rne(vv[i] - bf16_to_f32(hi[i]));
+      }
+      *reinterpret_cast<uint2*>(p.xh + xoff + h) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2*>(p.xl + xoff + h) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    }
   }
   if (!row_ok) return;
   float acc = 0.f;
@@ -481,83 +505,8 @@ __host__ __device__ constexpr int gu_group_np(int fmt, int S) {
 __host__ __device__ constexpr int dn_group_nr(int fmt, int L, int S) {
   return (kWave / L <= 2 && (fmt == 0 || L * S < 96)) ? 4 : 2;
 }
-constexpr int kGroupMaxPicks = 128;   // M * K bound of the grouped path
 constexpr int kChunkInts = 2 + kGroupTT;
-
-struct GroupLds {
-  int sel_e[kGroupMaxPicks];          // pick p = t*K + j -> expert
-  float rt[BDG_MAX_M];                // RMSNorm scale per token
-  unsigned used[BDG_MAX_EXPERTS / 32];
-  int ppc[BDG_MAX_EXPERTS / 32 + 1];  // prefix popcounts of used[]
-  int cnt[kGroupMaxPicks];            // picks per distinct expert (by rank)
-  int cbase[kGroupMaxPicks + 1];      // first chunk of each distinct expert
-  int n;                              // chunks
-  int ce[kGroupMaxPicks];             // expert of chunk c
-  int cn[kGroupMaxPicks];             // picks in chunk c
-  int cpk[kGroupMaxPicks][kGroupTT];  // the picks of chunk c
-};
-
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-__device__ __forceinline__ int wave_scan_incl(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-// Chunks of the P picks in g.sel_e: distinct experts in ascending order, the
-// picks of each in pick order, kGroupTT per chunk.  The block's threads all
-// call it; the result does not depend on thread timing (the only atomics are
-// an OR and a count).  P <= kGroupMaxPicks, blockDim >= kGroupMaxPicks.
-static_assert(BDG_MAX_EXPERTS / 32 <= kWave, "build_groups scans the used-expert words in one wave");
-__device__ void build_groups(GroupLds& g, int P, int E) {
-  const int tid = threadIdx.x;
-  const int nw = (E + 31) >> 5;
-  if (tid < nw) g.used[tid] = 0u;
-  if (tid < P) g.cnt[tid] = 0;
-  __syncthreads();
-  if (tid < P) atomicOr(&g.used[g.sel_e[tid] >> 5], 1u << (g.sel_e[tid] & 31));
-  __syncthreads();
-  if (tid < kWave) {
-    const int pc = wave_scan_incl(tid < nw ? __popc(g.used[tid]) : 0);
-    if (tid < nw) g.ppc[tid + 1] = pc;
-    if (tid == 0) g.ppc[0] = 0;
-  }
-  __syncthreads();
-  int my_u = 0, my_pos = 0;
-  if (tid < P) {
-    const int e = g.sel_e[tid];
-    my_u = g.ppc[e >> 5] + __popc(g.used[e >> 5] & ((1u << (e & 31)) - 1u));
-    for (int q = 0; q < tid; ++q) my_pos += g.sel_e[q] == e ? 1 : 0;
-    atomicAdd(&g.cnt[my_u], 1);
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    const int U = g.ppc[nw];
-    const int a = tid < U ? (g.cnt[tid] + kGroupTT - 1) / kGroupTT : 0;
-    const int b = tid + kWave < U ? (g.cnt[tid + kWave] + kGroupTT - 1) / kGroupTT : 0;
-    const int sa = wave_scan_incl(a);
-    const int sb = wave_scan_incl(b);
-    const int tot_a = __shfl(sa, kWave - 1);
-    g.cbase[tid] = sa - a;
-    g.cbase[tid + kWave] = tot_a + sb - b;
-    if (tid == kWave - 1) g.n = tot_a + sb;
-  }
-  __syncthreads();
-  if (tid < P) {
-    const int c = g.cbase[my_u] + my_pos / kGroupTT;
-    const int k = my_pos % kGroupTT;
-    g.cpk[c][k] = tid;
-    if (k == 0) {
-      g.ce[c] = g.sel_e[tid];
-      g.cn[c] = min(kGroupTT, g.cnt[my_u] - my_pos);
-    }
-  }
-  __syncthreads();
-}
+using GroupLds = GroupLdsT<kGroupTT>;
 
 struct GroupParams {
   int M, H, I, E, K;
@@ -606,54 +555,10 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
   const LayerDev& Ld = p.L;
   const int P = p.M * p.K;
 
-  // routing of every token of the step, a share of the tokens per wave
-  for (int t = wave; t < p.M; t += kWaves) {
-    int my_e = 0;
-    float my_w = 0.f, r = 1.f;
-    if (p.routed) {
-      my_e = clamp_expert(p.idx_in[t * p.K + (lane < p.K ? lane : 0)], p.E);
-      my_w = p.w_in[t * p.K + (lane < p.K ? lane : 0)];
-    } else {
-      const int64_t pb = (int64_t)t * (p.E + 1) * p.pstride;
-      float lg[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int e = lane + kWave * i;
-        const int ec = e < p.E ? e : p.E - 1;
-        lg[i] = p.part[pb + (int64_t)ec * p.pstride];
-      }
-      const float ssq = p.part[pb + (int64_t)p.E * p.pstride];
-      if (p.norm) r = 1.0f / sqrtf(ssq / (float)p.H + p.eps);
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const int e = lane + kWave * i;
-        lg[i] = r * lg[i] + (Ld.b_r ? Ld.b_r[e < p.E ? e : p.E - 1] : 0.f);
-      }
-      topk_rank<V>(lg, p.E, p.K, my_e, my_w);
-    }
-    if (lane < p.K) {
-      gl.sel_e[t * p.K + lane] = my_e;
-      if (blockIdx.x == 0) {
-        p.idx_out[t * p.K + lane] = my_e;
-        p.w_out[t * p.K + lane] = my_w;
-        if (p.topk_trace) p.topk_trace[t * p.K + lane] = my_e;
-        if (p.wts_trace) p.wts_trace[t * p.K + lane] = my_w;
-      }
-    }
-    if (lane == 0) gl.rt[t] = r;
-  }
-  __syncthreads();
-  build_groups(gl, P, p.E);
-  if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) p.chunks_out[0] = gl.n;
-    for (int c = threadIdx.x; c < gl.n; c += kThreads) {
-      int32_t* o = p.chunks_out + 1 + c * kChunkInts;
-      o[0] = gl.ce[c];
-      o[1] = gl.cn[c];
-#pragma unroll
-      for (int k = 0; k < kGroupTT; ++k) o[2 + k] = k < gl.cn[c] ? gl.cpk[c][k] : 0;
-    }
-  }
+  // routing of every token of the step and the chunk table (block 0 writes
+  // it for the down kernel)
+  group_route<V, kGroupTT>(gl, p, lane, wave, kWaves);
+  if (blockIdx.x == 0) write_chunk_table(gl, p.chunks_out, kThreads);
 
   const int nitems = gl.n * p.bpc;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -855,6 +760,15 @@ struct bdg_plan {
   unsigned* bar;            // grid barrier words (arrivals, generation), zero at create
   unsigned* fault;          // fault word (moe_plan_check)
   int wait_polls;
+  // grouped products on the matrix cores (BDG_MOE_MFMA, steps of m > 1)
+  int mfma;
+  int mfma_grid_gu, mfma_grid_dn;
+  uint16_t* xh;             // [max_m][H] bf16 hi/lo parts of the normalized layer input
+  uint16_t* xl;
+  uint16_t* h_hi;           // [max_m * K][I] bf16 hi/lo parts of h
+  uint16_t* h_lo;
+  uint16_t* zeros;          // [max(H, I)] zero bf16
+  int32_t* mfma_table;      // chunk table (all picks of an expert per chunk)
   uint64_t* tl_stamps;      // timeline mode: [L][nblk][kLayerStamps] (lazily allocated)
   int tl_active;            // set only inside moe_expert_decode_timeline
   int32_t* idx;
@@ -885,14 +799,19 @@ struct Prof {
   int used;
 };
 
+// Each timed kernel is bracketed by event records on its stream: the start
+// event completes when the stream reaches it (the previous kernel done), so a
+// duration covers the launch gap and the kernel, as a kernel trace of
+// back-to-back launches (a graph replay) counts each kernel.
 #define BDG_LAUNCH(PROF, KIND, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                          \
   do {                                                                                         \
     if (PROF) {                                                                                \
       if ((PROF)->used >= (PROF)->cap) return BDG_E_UNSUPPORTED;                               \
       const int slot_ = (PROF)->used++;                                                        \
       (PROF)->kind[slot_] = (KIND);                                                            \
-      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, (PROF)->ev[2 * slot_],            \
-                            (PROF)->ev[2 * slot_ + 1], 0, __VA_ARGS__);                         \
+      if (hipEventRecord((PROF)->ev[2 * slot_], STREAM) != hipSuccess) return BDG_E_HIP;       \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                       \
+      if (hipEventRecord((PROF)->ev[2 * slot_ + 1], STREAM) != hipSuccess) return BDG_E_HIP;   \
     } else {                                                                                   \
       hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                       \
     }                                                                                          \
@@ -903,7 +822,8 @@ struct Prof {
 // combine != 0 (grouped path, layer >= 1): the layer input is formed here
 // from the previous layer's input and per-pick down outputs.
 static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype, int m,
-                        float* resid_trace, int compute_logits, hipStream_t s, Prof* prof, int combine = 0) {
+                        float* resid_trace, int compute_logits, hipStream_t s, Prof* prof, int combine = 0,
+                        int mfma_ops = 0) {
   RouteParams rp{};
   rp.M = m;
   rp.H = p->d.hidden;
@@ -930,7 +850,14 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
   rp.part = p->part;
   rp.pstride = p->pstride;
   rp.L = p->hl[layer];
-  if (compute_logits && !rp.dout) {
+  if (mfma_ops) {
+    // the matrix-core path's bf16 hi/lo operands of the (normalized) input
+    rp.xh = p->xh;
+    rp.xl = p->xl;
+    rp.norm = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
+    rp.eps = p->d.norm_eps;
+  }
+  if (compute_logits && !rp.dout && !rp.xh) {
     // one wave per router row, no LDS
     const int nf = (rp.H + 255) / 256;
     const dim3 grid((unsigned)rp.E, (unsigned)m);
@@ -1197,16 +1124,64 @@ static int launch_layer(const bdg_plan* p, int layer, int nparts, int32_t* topk_
   lp.o = down_out(p, layer, residual, x_out, y_out, trace_out, route_next);
   lp.stamps = p->tl_active ? p->tl_stamps + (size_t)layer * p->fused_nblk * kLayerStamps : nullptr;
   if (prof) {
-    // start/stop events recorded by the runtime at the kernel's start and end
+    // bracketed by event records, as BDG_LAUNCH does
     if (prof->used >= prof->cap) return BDG_E_UNSUPPORTED;
     const int slot = prof->used++;
     prof->kind[slot] = kLayer;
-    void* args[] = {&lp};
-    return hip_status(hipExtLaunchKernel(layer_fused_kernel(p->fused_cfg), dim3(p->fused_nblk),
-                                         dim3(layer_threads()), args, p->fused_lds, s, prof->ev[2 * slot],
-                                         prof->ev[2 * slot + 1], 0));
+    if (hipEventRecord(prof->ev[2 * slot], s) != hipSuccess) return BDG_E_HIP;
+    const int st = launch_layer_fused(p->fused_cfg, lp, p->fused_nblk, p->fused_lds, s);
+    if (st) return st;
+    return hip_status(hipEventRecord(prof->ev[2 * slot + 1], s));
   }
   return launch_layer_fused(p->fused_cfg, lp, p->fused_nblk, p->fused_lds, s);
+}
+
+static MfmaParams mfma_params(const bdg_plan* p, int layer, int m, int routed, const int32_t* idx_in,
+                               const float* w_in, int32_t* topk_trace, float* wts_trace, int use_norm) {
+  MfmaParams mp{};
+  mp.M = m;
+  mp.H = p->d.hidden;
+  mp.I = p->d.inter;
+  mp.E = p->d.n_experts;
+  mp.K = p->d.top_k;
+  mp.routed = routed;
+  mp.idx_in = idx_in;
+  mp.w_in = w_in;
+  mp.part = p->part;
+  mp.pstride = p->pstride;
+  mp.norm = use_norm;
+  mp.eps = p->d.norm_eps;
+  mp.idx_out = p->idx;
+  mp.w_out = p->w;
+  mp.topk_trace = topk_trace;
+  mp.wts_trace = wts_trace;
+  mp.L = p->hl[layer];
+  mp.xh = p->xh;
+  mp.xl = p->xl;
+  mp.hh = p->h_hi;
+  mp.hl = p->h_lo;
+  mp.zeros = p->zeros;
+  mp.table = p->mfma_table;
+  mp.dout = p->dout;
+  return mp;
+}
+
+// The matrix-core grouped gate_up and down of one layer, timed like BDG_LAUNCH.
+static int launch_mfma_pair(const bdg_plan* p, const MfmaParams& mp, hipStream_t s, Prof* prof) {
+  for (int which = 0; which < 2; ++which) {
+    int slot = -1;
+    if (prof) {
+      if (prof->used >= prof->cap) return BDG_E_UNSUPPORTED;
+      slot = prof->used++;
+      prof->kind[slot] = which == 0 ? kGateUp : kDown;
+      if (hipEventRecord(prof->ev[2 * slot], s) != hipSuccess) return BDG_E_HIP;
+    }
+    const int st = which == 0 ? launch_gu_mfma(mp, p->topk_V, p->mfma_grid_gu, s)
+                              : launch_dn_mfma(mp, p->mfma_grid_dn, s);
+    if (st) return st;
+    if (prof && hipEventRecord(prof->ev[2 * slot + 1], s) != hipSuccess) return BDG_E_HIP;
+  }
+  return BDG_OK;
 }
 
 // A grouped step (M > 1): per layer route (forming the layer input from the
@@ -1219,8 +1194,16 @@ static int enqueue_decode_grouped(const bdg_plan* p, const GraphKey& k, hipStrea
   const int stack = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
   for (int l = 0; l < L; ++l) {
     int st = launch_route(p, l, k.x, k.x_dtype, k.m, k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr,
-                          1, s, prof, /*combine=*/l > 0);
+                          1, s, prof, /*combine=*/l > 0, /*mfma_ops=*/p->mfma);
     if (st) return st;
+    if (p->mfma) {
+      st = launch_mfma_pair(p, mfma_params(p, l, k.m, 0, nullptr, nullptr,
+                                           k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
+                                           k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack),
+                            s, prof);
+      if (st) return st;
+      continue;
+    }
     st = launch_gu_group(p, l, k.m, 0, nullptr, nullptr,
                          k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
                          k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof);
@@ -1315,7 +1298,7 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   if (d->fmt != BDG_FMT_MXFP4 && d->fmt != BDG_FMT_INT4G) return BDG_E_INVALID;
   if ((d->hidden % 32) || (d->inter % 32)) return BDG_E_INVALID;
   if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH | BDG_MOE_ROUTE_EVERY_LAYER | BDG_MOE_PER_TOKEN |
-                    BDG_MOE_FUSED_LAYER)) != 0)
+                    BDG_MOE_FUSED_LAYER | BDG_MOE_MFMA)) != 0)
     return BDG_E_INVALID;
   if ((d->flags & BDG_MOE_STACK) && !(d->norm_eps >= 0.f)) return BDG_E_INVALID;
   if (d->top_k > BDG_MAX_TOPK || d->n_experts > BDG_MAX_EXPERTS || d->max_m > BDG_MAX_M)
@@ -1392,6 +1375,22 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
                   p->gu_S <= (d->fmt == BDG_FMT_MXFP4 ? 3 : 2) &&
                   lds_gu <= 64 * 1024 &&
                   lds_dn <= 64 * 1024 && !(d->flags & BDG_MOE_PER_TOKEN);
+    // grouped products on the matrix cores: MXFP4, K multiples of 64 (whole
+    // 2-block super-steps), grids of every block the kernels keep resident
+    p->mfma = 0;
+    if ((d->flags & BDG_MOE_MFMA) && p->group_ok && d->fmt == BDG_FMT_MXFP4 && d->hidden % 64 == 0 &&
+        d->inter % 64 == 0 && d->max_m <= 16) {
+      int bg = 0, bd = 0;
+      const void* fg = mfma_gu_kernel(p->topk_V);
+      if (fg && hipOccupancyMaxActiveBlocksPerMultiprocessor(&bg, fg, 256, 0) == hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&bd, mfma_dn_kernel(), 256, 0) == hipSuccess && bg > 0 &&
+          bd > 0) {
+        p->mfma = 1;
+        p->mfma_grid_gu = cus * bg;
+        p->mfma_grid_dn = cus * bd;
+      }
+      (void)hipGetLastError();
+    }
   }
   auto geom = [&](int k) {
     QGeom g;
@@ -1465,6 +1464,12 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_hbuf = off; off = align256(off + sizeof(float) * (size_t)K * I);
   const size_t o_bar = off; off = align256(off + sizeof(unsigned) * 64);
   const size_t o_fault = off; off = align256(off + sizeof(unsigned) * 64);
+  const size_t o_xh = off; off = align256(off + sizeof(uint16_t) * (size_t)M * H);
+  const size_t o_xl = off; off = align256(off + sizeof(uint16_t) * (size_t)M * H);
+  const size_t o_hh = off; off = align256(off + sizeof(uint16_t) * (size_t)M * K * I);
+  const size_t o_hlo = off; off = align256(off + sizeof(uint16_t) * (size_t)M * K * I);
+  const size_t o_zero = off; off = align256(off + sizeof(uint16_t) * (size_t)std::max(H, I));
+  const size_t o_mtab = off; off = align256(off + sizeof(int32_t) * (1 + kGroupMaxPicks * kMfmaChunkInts));
   if (hipMalloc(&p->dev_base, off) != hipSuccess) {
     delete p;
     return BDG_E_NOMEM;
@@ -1481,6 +1486,12 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->hbuf = reinterpret_cast<float*>(base + o_hbuf);
   p->bar = reinterpret_cast<unsigned*>(base + o_bar);
   p->fault = reinterpret_cast<unsigned*>(base + o_fault);
+  p->xh = reinterpret_cast<uint16_t*>(base + o_xh);
+  p->xl = reinterpret_cast<uint16_t*>(base + o_xl);
+  p->h_hi = reinterpret_cast<uint16_t*>(base + o_hh);
+  p->h_lo = reinterpret_cast<uint16_t*>(base + o_hlo);
+  p->zeros = reinterpret_cast<uint16_t*>(base + o_zero);
+  p->mfma_table = reinterpret_cast<int32_t*>(base + o_mtab);
   // router partial sums: zero once, so slots past the slices read as 0
   if (hipMemset(p->part, 0, sizeof(float) * (size_t)M * (E + 1) * p->pstride) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
@@ -1690,11 +1701,21 @@ extern "C" int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int
   rp.part = p->part;
   rp.pstride = p->pstride;
   rp.L = p->hl[layer];
+  const bool mfma = m > 1 && p->mfma;
+  if (mfma) {   // also the bf16 operand parts of x (factor 1) for the matrix cores
+    rp.xh = p->xh;
+    rp.xl = p->xl;
+  }
   hipLaunchKernelGGL(moe_route_kernel, dim3(1, m), dim3(kThreads), (size_t)(rp.H + kWaves) * sizeof(float), s,
                      rp);
   int st = launch_status();
   if (st) return st;
   // gate_up runs on the raw x (no norm), routing from the caller
+  if (mfma) {
+    st = launch_mfma_pair(p, mfma_params(p, layer, m, 1, idx, wts, nullptr, nullptr, 0), s, nullptr);
+    if (st) return st;
+    return launch_combine(p, m, p->resid[layer & 1], 0, y, s, nullptr);
+  }
   if (m > 1 && p->group_ok) {
     st = launch_gu_group(p, layer, m, 1, idx, wts, nullptr, nullptr, 0, s, nullptr);
     if (st) return st;

@@ -107,7 +107,9 @@ typedef struct bdg_qmat {
  * the MXFP4 reader of the gpt-oss page, section 3, is bit-exact).
  * codes [n][k/2], scales [n][k/32] as in the PLAIN layout; out [n][k] of
  * out_dtype (BDG_F32: bit-exact IEEE product, subnormals kept, +-inf on
- * overflow; BDG_BF16: that value rounded to nearest even).  k % 32 == 0. */
+ * overflow; BDG_BF16: that value rounded to nearest even, produced by
+ * gfx950's scaled FP4 -> bf16 conversion, the one the matrix-core decode
+ * path (BDG_MOE_MFMA) uses).  k % 32 == 0. */
 int mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                   void* out, int32_t out_dtype, void* stream);
 
@@ -174,6 +176,12 @@ typedef struct bdg_layer_desc {
                                    through a grid barrier, instead of two kernels (gate_up +
                                    SwiGLU, then down + combine); same results bit for bit.
                                    Slower on MI355X (measured); kept for A/B measurement */
+#define BDG_MOE_MFMA 32  /* MXFP4 steps of m > 1 run each layer's grouped gate_up and down on the
+                            matrix cores (v_mfma_f32_32x32x16_bf16): weights decoded once to
+                            bf16 with the block scale, activations as bf16 hi + lo parts, fp32
+                            accumulation; within the fp32 tolerance of the exact result, not
+                            bit for bit with the VALU kernels.  Needs hidden and inter
+                            multiples of 64 (else ignored) */
 
 typedef struct bdg_moe_desc {
   int32_t n_layers;
@@ -410,8 +418,9 @@ int attn_decode_noalloc(const float* q, const float* k, const float* v, void* k_
 
 /* moe_expert_decode_profiled - one decode step exactly as moe_expert_decode
  * computes it (same kernels, same grids), launched directly rather than from
- * a graph, with a start/stop event pair recorded by the runtime at each
- * kernel's start and end.  Adds each kernel's duration (ms) to
+ * a graph, each kernel between a start and a stop event recorded on the
+ * stream (so a duration covers the kernel and the launch gap before it, the
+ * way a kernel trace of back-to-back graph replays counts it).  Adds each kernel's duration (ms) to
  * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route (router
  * GEMV + sum of squares, and for steps of m > 1 the previous layer's
  * combine), 1 = gate_up (top-k + grouped gate_up GEMV + SwiGLU), 2 = down

@@ -36,6 +36,9 @@ def test_mxfp4_dequant_exhaustive(dev):
 
 
 def test_mxfp4_dequant_bf16_output(dev):
+    """bf16 output over all 16 codes x 256 E8M0: produced by the scaled FP4 ->
+    bf16 conversion the matrix-core decode path uses, so this pins that
+    instruction to the exact values (subnormals, -0, overflow to inf)."""
     codes, scales = mxfp4_exhaustive_inputs()
     got = bdg.mxfp4_dequant(dev_t(codes, dev), dev_t(scales, dev), out_dtype=torch.bfloat16)
     got_bits = to_np(got.view(torch.int16)).view(np.uint16)
