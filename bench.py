@@ -39,6 +39,11 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published peak
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak (no sparsity)
 METRIC = "expert-path HBM GB/s (% of peak) + us/token, gpt-oss-20B-shape MoE at M=1"
+SHARE_NOTE = ("duration_us = the dispatch's own time (start/stop events of the directly launched "
+              "per-kernel pass) plus gap_share_us, an equal share of the replayed step's launch gaps "
+              "(replayed step time minus the step's dispatch times, over its launches): the duration a "
+              "kernel trace of graph replays gives each launch; achieved_kernel_only divides by the "
+              "dispatch time alone")
 
 
 def log(msg):
@@ -65,10 +70,10 @@ def step_bytes(cfg, unique_experts_per_layer):
     return sum(router_bytes(cfg) + u * (gu + dn) for u in unique_experts_per_layer)
 
 
-KERNEL_SOURCES = ("bit_dequant_gemv_amd/csrc/moe.hip", "bit_dequant_gemv_amd/csrc/moe_layer.hip",
-                  "bit_dequant_gemv_amd/csrc/gemv.hip", "bit_dequant_gemv_amd/csrc/bdg_gemv.hpp",
-                  "bit_dequant_gemv_amd/csrc/bdg_device.hpp", "bit_dequant_gemv_amd/csrc/bdg_topk.hpp",
-                  "bit_dequant_gemv_amd/csrc/bdg_moe.hpp", "bit_dequant_gemv_amd/csrc/bdg_moe_layer.hpp")
+KERNEL_SOURCES = tuple("bit_dequant_gemv_amd/csrc/" + f for f in (
+    "moe.hip", "moe_down.hip", "moe_layer.hip", "moe_mfma.hip", "gemv.hip",
+    "bdg_gemv.hpp", "bdg_device.hpp", "bdg_topk.hpp", "bdg_moe.hpp", "bdg_moe_down.hpp", "bdg_moe_layer.hpp",
+    "bdg_moe_mfma.hpp"))
 
 
 def kernel_sources_sha(sources=KERNEL_SOURCES):
@@ -110,7 +115,8 @@ def measured_traffic(workload, kernel, sources=KERNEL_SOURCES):
 KERNEL_KIND_PATTERNS = (          # kernel name fragment -> kind (per-launch traffic keys)
     ("moe_layer_kernel", "layer"), ("moe_gateup_kernel", "gate_up"), ("moe_gu_group_kernel", "gate_up"),
     ("moe_down_kernel", "down"), ("moe_dn_group_kernel", "down"), ("moe_route", "route"),
-    ("moe_combine_kernel", "combine"), ("qgemv_kernel", "qgemv"), ("attn_split_kernel", "attn_split"),
+    ("moe_combine_kernel", "combine"), ("moe_gu_mfma_kernel", "gate_up"), ("moe_dn_mfma_kernel", "down"),
+    ("qgemv_kernel", "qgemv"), ("attn_split_kernel", "attn_split"),
     ("attn_merge_kernel", "attn_merge"), ("mx_gemm_kernel", "mx_gemm"), ("stream_copy_kernel", "copy"),
 )
 
@@ -155,7 +161,8 @@ def summarize(argv):
     ap = argparse.ArgumentParser(prog="bench.py summarize")
     ap.add_argument("what", choices=["trace", "traffic", "sq"])
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--src", help="rocprofv3 output directory (trace or SQ pass)")
+    ap.add_argument("--src", action="append", default=[],
+                    help="rocprofv3 output directory (the trace; for sq, one per counter pass, merged)")
     ap.add_argument("--fetch", help="FETCH_SIZE pass of the workload")
     ap.add_argument("--write", help="WRITE_SIZE pass of the workload")
     ap.add_argument("--cal-fetch", help="FETCH_SIZE pass of bench.py --copy-calibration BYTES")
@@ -170,7 +177,7 @@ def summarize(argv):
     sha = kernel_sources_sha(srcs)
     cmds = "\n".join(f"    {c}" for c in a.command)
     if a.what == "trace":
-        rows = list(csv.DictReader(open(_find(a.src, "kernel_stats.csv"))))
+        rows = list(csv.DictReader(open(_find(a.src[0], "kernel_stats.csv"))))
         total = sum(float(r["TotalDurationNs"]) for r in rows)
         lines = [f"# Kernel trace: {a.workload}", "", "Command (from the repository root, on one MI355X):", "",
                  cmds, "",
@@ -225,27 +232,49 @@ def summarize(argv):
         json.dump(rec, open(os.path.join(ROOT, "profiles", stem + ".json"), "w"), indent=1)
     else:
         ctr = {}
-        for r in _counter_rows(a.src):
-            ctr.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for src in a.src:
+            for r in _counter_rows(src):
+                ctr.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+        have = set(k for c in ctr.values() for k in c)
+        cols = [("dispatches", None), ("waves / dispatch", None)]
+        if "SQ_INSTS_VALU" in have:
+            cols += [("VALU instr / wave", lambda m, wv, wc: f"{m.get('SQ_INSTS_VALU', 0) / wv:.0f}")]
+        if "SQ_INSTS_MFMA" in have:
+            cols += [("MFMA instr / wave", lambda m, wv, wc: f"{m.get('SQ_INSTS_MFMA', 0) / wv:.0f}")]
+        if "SQ_INSTS_VMEM_RD" in have:
+            cols += [("VMEM read instr / wave", lambda m, wv, wc: f"{m.get('SQ_INSTS_VMEM_RD', 0) / wv:.1f}")]
+        if "SQ_WAVE_CYCLES" in have:
+            cols += [("VALU active / wave-cycles", lambda m, wv, wc: f"{m.get('SQ_ACTIVE_INST_VALU', 0) / wc:.2f}"),
+                     ("waiting (any) / wave-cycles", lambda m, wv, wc: f"{m.get('SQ_WAIT_ANY', 0) / wc:.2f}"),
+                     ("waiting for issue / wave-cycles",
+                      lambda m, wv, wc: f"{m.get('SQ_WAIT_INST_ANY', 0) / wc:.2f}")]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in have and "GRBM_GUI_ACTIVE" in have:
+            cols += [("MFMA busy / (GUI-active cycles x 1024 SIMDs)",
+                      lambda m, wv, wc: f"{m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / max(m['GRBM_GUI_ACTIVE'] * 1024, 1):.3f}")]
+        if "TA_BUSY_avr" in have and "GRBM_GUI_ACTIVE" in have:
+            cols += [("TA busy / GUI-active cycles (mean TA)",
+                      lambda m, wv, wc: f"{m.get('TA_BUSY_avr', 0) / max(m['GRBM_GUI_ACTIVE'], 1):.2f}")]
+        if "GRBM_GUI_ACTIVE" in have:
+            cols += [("GUI-active cycles / dispatch", lambda m, wv, wc: f"{m.get('GRBM_GUI_ACTIVE', 0):.0f}")]
         lines = [f"# SQ counters: {a.workload}", "",
-                 "Command (from the repository root, on one MI355X; a counter pass of its own, no trace options):",
-                 "", cmds, "",
-                 "Counters averaged over the dispatches of the run.  The ratio columns divide counters that",
-                 "share a unit (wave-cycles summed over all waves): SQ_ACTIVE_INST_VALU, SQ_WAIT_ANY and",
-                 "SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.", "",
-                 "| kernel | dispatches | waves / dispatch | VALU instr / wave | VMEM read instr / wave | "
-                 "VALU active / wave-cycles | waiting (any) / wave-cycles | waiting for issue / wave-cycles |",
-                 "|---|---:|---:|---:|---:|---:|---:|---:|"]
+                 "Commands (from the repository root, on one MI355X; counter passes of their own, no trace "
+                 "options, merged per kernel):", "", cmds, "",
+                 "Counters averaged over the dispatches of the run (a counter pass serialises dispatches, so no",
+                 "timing is taken from it).  The wave-cycle ratios divide counters that share a unit (summed over",
+                 "all waves): SQ_ACTIVE_INST_VALU, SQ_WAIT_ANY and SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.  MFMA busy",
+                 "is SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the 1024 SIMDs; TA busy is the mean",
+                 "texture-address unit's busy cycles (TA_BUSY_avr) over GRBM_GUI_ACTIVE.", "",
+                 "| kernel | " + " | ".join(c for c, _ in cols) + " |",
+                 "|---|" + "---:|" * len(cols)]
         for name, c in sorted(ctr.items()):
             if kernel_kind(name) is None or "SQ_WAVES" not in c:
                 continue
             m = {k: st.mean(v) for k, v in c.items()}
             wv = max(m["SQ_WAVES"], 1.0)
             wc = max(m.get("SQ_WAVE_CYCLES", 0.0), 1.0)
-            lines.append(f"| `{short_kernel(name)}` | {len(c['SQ_WAVES'])} | {wv:.0f} | "
-                         f"{m.get('SQ_INSTS_VALU', 0) / wv:.0f} | {m.get('SQ_INSTS_VMEM_RD', 0) / wv:.1f} | "
-                         f"{m.get('SQ_ACTIVE_INST_VALU', 0) / wc:.2f} | {m.get('SQ_WAIT_ANY', 0) / wc:.2f} | "
-                         f"{m.get('SQ_WAIT_INST_ANY', 0) / wc:.2f} |")
+            vals = [str(len(c["SQ_WAVES"])), f"{wv:.0f}"] + [f(m, wv, wc) for _, f in cols[2:]]
+            lines.append(f"| `{short_kernel(name)}` | " + " | ".join(vals) + " |")
         stem = a.name or f"sq_counters_{a.workload}"
     if a.note:
         lines += ["", a.note]
@@ -740,12 +769,11 @@ def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     acc = None
     for t in range(W, W + K):
         x_buf.copy_(x_all[t])
-        acc = bdg.moe_expert_decode_profiled(plans[t % NL], x_buf, y_buf, *(acc if acc else (None, None)))
-    kms, kcnt = acc
-    kernels = {name: {"avg_us": round(kms[i] / kcnt[i] * 1e3, 3), "launches": int(kcnt[i])}
-               for i, name in enumerate(bdg.KERNEL_KINDS) if kcnt[i]}
+        acc = bdg.moe_expert_decode_profiled(plans[t % NL], x_buf, y_buf, acc)
     gu_bytes, dn_bytes = expert_bytes(cfg)
-    achieved = cfg.top_k * gu_bytes / (kms[1] / kcnt[1] * 1e-3) / 1e9
+    kernels, gap_us, _ = kernel_figures(bdg, acc, {"gate_up": cfg.top_k * gu_bytes, "down": cfg.top_k * dn_bytes,
+                                                   "route": router_bytes(cfg)}, gpu_ms / K * 1e3, K)
+    achieved = kernels["gate_up"]["GBps"]
     log(f"per-kernel: {kernels}")
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, 1, 1)
     out = base_record(cfg, value, K, W, gpu_ms / K, {
@@ -755,7 +783,10 @@ def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     out.update({"us_per_token": round(gpu_ms / K * 1e3, 2), "kernels": kernels, "cpu_baseline": cpu,
                 "roofline": {"kernel": "moe_gateup_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                              "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                             "traffic": None, "traffic_algorithmic_bytes": cfg.top_k * gu_bytes}})
+                             "traffic": None, "traffic_algorithmic_bytes": cfg.top_k * gu_bytes,
+                             "duration_us": kernels["gate_up"]["share_us"], "gap_share_us": round(gap_us, 3),
+                             "duration": SHARE_NOTE,
+                             "achieved_kernel_only": kernels["gate_up"]["GBps_kernel_only"]}})
     print(json.dumps(out), flush=True)
     for pl in plans:
         pl.close()
@@ -952,6 +983,91 @@ def bench_timeline(bdg, plan, cfg, x_all, x_buf, y_buf, W, K):
     plan.close()
 
 
+def routing_stats(bdg, np, synth, plan, cfg, m, x_all, x_buf, y_buf, W, K):
+    """Unique (layer, expert) matrices per step of the K steps after W: M=1
+    reads k experts per layer; for M > 1 the steps are replayed untimed with
+    routing traces.  Returns (uniq [K][L], routing summary or None)."""
+    routing = None
+    if m == 1:
+        return [[cfg.top_k] * cfg.n_layers for _ in range(K)], None
+    uniq, hot_frac, tpe = [], [], []
+    hot_sets = [synth.router(cfg, l)[2] for l in range(cfg.n_layers)]
+    for s in range(W, W + K):
+        x_buf.copy_(x_all[s])
+        _, tr = bdg.moe_expert_decode(plan, x_buf, y=y_buf, traces=True)
+        topk = tr["topk"].cpu().numpy()                       # [L][m][k]
+        uniq.append([len(set(topk[l].ravel().tolist())) for l in range(cfg.n_layers)])
+        if hot_sets[0] is not None:
+            hot_frac.append([float(np.isin(topk[l], hot_sets[l]).mean()) for l in range(cfg.n_layers)])
+        for l in range(cfg.n_layers):
+            tpe.extend(np.bincount(topk[l].ravel(), minlength=cfg.n_experts)[
+                np.unique(topk[l].ravel())].tolist())
+    hist = np.bincount(np.array(tpe), minlength=m + 1)[1:].tolist()
+    routing = {
+        "unique_experts_per_layer_mean": round(float(np.mean(uniq)), 3),
+        "picks_per_layer": m * cfg.top_k,
+        "tokens_per_active_expert_hist": {str(i + 1): c for i, c in enumerate(hist) if c},
+    }
+    if hot_frac:
+        routing["hot_pick_fraction_per_layer"] = [round(v, 3) for v in np.mean(hot_frac, axis=0)]
+        routing["hot_pick_fraction_mean"] = round(float(np.mean(hot_frac)), 3)
+    return uniq, routing
+
+
+def kernel_figures(bdg, acc, launch_bytes, replay_us_per_step, steps):
+    """Per-kind figures of a KernelTimes over `steps` steps: avg_us (the
+    dispatch's own start-to-end time), share_us = avg_us plus an equal share
+    of the replayed step's launch gaps ((replayed step time - the step's
+    dispatch times) / launches per step: in a graph replay each launch
+    waits one gap behind the previous kernel, and a kernel trace of the
+    replay starts each launch at the previous kernel's end), launches, and
+    for kinds with algorithmic bytes per launch GBps = bytes / share_us (the
+    roofline figure) and GBps_kernel_only = bytes / avg_us."""
+    kinds = range(len(bdg.KERNEL_KINDS))
+    launches = sum(acc.count[i] for i in kinds) / steps
+    dispatch_us = sum(acc.ms[i] for i in kinds) / steps * 1e3
+    gap_us = max(0.0, (replay_us_per_step - dispatch_us) / launches) if launches else 0.0
+    kernels = {}
+    for i, name in enumerate(bdg.KERNEL_KINDS):
+        if acc.count[i]:
+            avg = acc.ms[i] / acc.count[i] * 1e3
+            k = {"avg_us": round(avg, 3), "share_us": round(avg + gap_us, 3), "launches": int(acc.count[i])}
+            if name in launch_bytes:
+                k["GBps"] = round(launch_bytes[name] / ((avg + gap_us) * 1e-6) / 1e9, 1)
+                k["GBps_kernel_only"] = round(launch_bytes[name] / (avg * 1e-6) / 1e9, 1)
+            kernels[name] = k
+    return kernels, gap_us, dispatch_us
+
+
+def kernel_pass(bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, replay_us_per_step):
+    """Per-kernel figures over the K steps after W: the same kernels and
+    grids launched directly, each dispatch with start/stop events (see
+    kernel_figures; replay_us_per_step is the graph replay's step time, or
+    None for no gap share).  Returns (per-kind figures, dominant kernel
+    name, its algorithmic bytes per launch, its GB/s, gap share us,
+    dispatch us per step, fused-layer flag)."""
+    gu_bytes, dn_bytes = expert_bytes(cfg)
+    acc = None
+    for s in range(W, W + K):
+        x_buf.copy_(x_all[s])
+        acc = bdg.moe_expert_decode_profiled(plan, x_buf, y_buf, acc)
+    gu_launch_bytes = int(round(mean_uniq * gu_bytes))
+    layer_launch_bytes = int(round(mean_uniq * (gu_bytes + dn_bytes)))
+    dispatch_only = sum(acc.ms[i] for i in range(len(bdg.KERNEL_KINDS))) / K * 1e3
+    kernels, gap_us, dispatch_us = kernel_figures(
+        bdg, acc, {"gate_up": gu_launch_bytes, "down": int(round(mean_uniq * dn_bytes)),
+                   "route": router_bytes(cfg), "layer": layer_launch_bytes},
+        replay_us_per_step if replay_us_per_step else dispatch_only, K)
+    fused = "layer" in kernels
+    if fused:
+        # the fused per-layer kernel: the chosen experts' gate_up and down bytes per launch
+        dom_kernel, dom_kind, dom_bytes = "moe_layer_kernel", "layer", layer_launch_bytes
+    else:
+        dom_kernel, dom_kind, dom_bytes = "moe_gateup_kernel", "gate_up", gu_launch_bytes
+    achieved = kernels[dom_kind]["GBps"]
+    return kernels, dom_kernel, dom_bytes, achieved, gap_us, dispatch_us, fused
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -968,6 +1084,9 @@ def main():
     ap.add_argument("--fused-layer", action="store_true",
                     help="one-token steps run each layer as the fused per-layer kernel instead of two "
                          "kernels (gate_up, down): the A/B of the fused design")
+    ap.add_argument("--route-every-layer", action="store_true",
+                    help="stacks: a route kernel before every layer instead of the router partial sums "
+                         "from the previous down kernel (BDG_MOE_ROUTE_EVERY_LAYER): the A/B of fused routing")
     ap.add_argument("--timeline", action="store_true",
                     help="one-token stacks: phase timeline of the fused per-layer kernel (per-block clock "
                          "stamps of moe_expert_decode_timeline), summarized per phase, then exit")
@@ -975,6 +1094,10 @@ def main():
                     help="only the warmup and the timed graph replays (no per-step events, sync mode, "
                          "per-kernel event pass, stream read or CPU baseline): the run a kernel trace "
                          "of graph replays alone is taken from")
+    ap.add_argument("--kernel-pass-only", action="store_true",
+                    help="only the per-kernel pass: every step launched directly (no graph), each kernel "
+                         "timed by its dispatch's start/stop events; prints the per-kernel figures.  A "
+                         "kernel trace of this command holds exactly the dispatches the events time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the 16-byte copy kernel 4 times over BYTES (for scaling "
                          "HBM counters against a kernel of known traffic), then exit")
@@ -1033,7 +1156,8 @@ def main():
         if l % 6 == 5 or l == cfg.n_layers - 1:
             log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.1f} s)")
     plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers, fused_layer=args.fused_layer or args.timeline,
-                              mfma=args.mfma)
+                              mfma=args.mfma, route_every_layer=args.route_every_layer,
+                              use_graph=not args.kernel_pass_only)
     x_all, _ = sdev.hidden_device(cfg, range((W + K) * m), dev)
     x_all = x_all.reshape(W + K, m, cfg.hidden)
     x_buf = torch.empty_like(x_all[0])
@@ -1046,6 +1170,18 @@ def main():
     log(f"warmup done ({W} steps of M={m})")
     if args.timeline:
         return bench_timeline(bdg, plan, cfg, x_all, x_buf, y_buf, W, K)
+    if args.kernel_pass_only:
+        uniq, _ = routing_stats(bdg, np, synth, plan, cfg, m, x_all, x_buf, y_buf, W, K)
+        kernels, dom_kernel, dom_bytes, achieved, _, dispatch_us, _ = kernel_pass(
+            bdg, plan, cfg, x_all, x_buf, y_buf, W, K, float(np.mean(uniq)), None)
+        if not torch.isfinite(y_buf).all() or not plan.check():
+            raise SystemExit("non-finite output or a failed in-kernel wait")
+        log(f"kernel pass ({K} steps of M={m}, direct launches): {kernels}")
+        print(json.dumps({"workload": cfg.name, "m": m, "steps": K, "kernels": kernels,
+                          "roofline_kernel": dom_kernel, "algorithmic_bytes_per_launch": dom_bytes,
+                          "achieved_GBps": achieved, "dispatch_us_per_step": round(dispatch_us, 2)}), flush=True)
+        plan.close()
+        return
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -1068,34 +1204,8 @@ def main():
         plan.close()
         return
 
-    # unique (layer, expert) matrices per step: M=1 reads k experts per layer;
-    # for M > 1 the same steps are replayed untimed with routing traces
     gu_bytes, dn_bytes = expert_bytes(cfg)
-    routing = None
-    if m == 1:
-        uniq = [[cfg.top_k] * cfg.n_layers for _ in range(K)]
-    else:
-        uniq, hot_frac, tpe = [], [], []
-        hot_sets = [synth.router(cfg, l)[2] for l in range(cfg.n_layers)]
-        for s in range(W, W + K):
-            x_buf.copy_(x_all[s])
-            _, tr = bdg.moe_expert_decode(plan, x_buf, y=y_buf, traces=True)
-            topk = tr["topk"].cpu().numpy()                       # [L][m][k]
-            uniq.append([len(set(topk[l].ravel().tolist())) for l in range(cfg.n_layers)])
-            if hot_sets[0] is not None:
-                hot_frac.append([float(np.isin(topk[l], hot_sets[l]).mean()) for l in range(cfg.n_layers)])
-            for l in range(cfg.n_layers):
-                tpe.extend(np.bincount(topk[l].ravel(), minlength=cfg.n_experts)[
-                    np.unique(topk[l].ravel())].tolist())
-        hist = np.bincount(np.array(tpe), minlength=m + 1)[1:].tolist()
-        routing = {
-            "unique_experts_per_layer_mean": round(float(np.mean(uniq)), 3),
-            "picks_per_layer": m * cfg.top_k,
-            "tokens_per_active_expert_hist": {str(i + 1): c for i, c in enumerate(hist) if c},
-        }
-        if hot_frac:
-            routing["hot_pick_fraction_per_layer"] = [round(v, 3) for v in np.mean(hot_frac, axis=0)]
-            routing["hot_pick_fraction_mean"] = round(float(np.mean(hot_frac)), 3)
+    uniq, routing = routing_stats(bdg, np, synth, plan, cfg, m, x_all, x_buf, y_buf, W, K)
     nbytes = sum(step_bytes(cfg, u) for u in uniq)
     value = nbytes / (gpu_ms * 1e-3) / 1e9
     mean_uniq = float(np.mean(uniq))
@@ -1125,37 +1235,12 @@ def main():
     sync_mode = {"median_us": round(statistics.median(sync_us), 2), "mean_us": round(statistics.mean(sync_us), 2)}
     log(f"per step (events around each replay): {per_step}; sync mode wall per step: {sync_mode}")
 
-    # per-kernel durations, same kernels and grids, start/stop events at each kernel
-    acc = None
-    for s in range(W, W + K):
-        x_buf.copy_(x_all[s])
-        acc = bdg.moe_expert_decode_profiled(plan, x_buf, y_buf, *(acc if acc else (None, None)))
-    kms, kcnt = acc
-    kernels = {}
-    for i, name in enumerate(bdg.KERNEL_KINDS):
-        if kcnt[i]:
-            kernels[name] = {"avg_us": round(kms[i] / kcnt[i] * 1e3, 3), "launches": int(kcnt[i])}
+    kernels, dom_kernel, dom_bytes, achieved, gap_us, dispatch_us, fused = kernel_pass(
+        bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, gpu_ms / K * 1e3)
     gu_launch_bytes = int(round(mean_uniq * gu_bytes))
     layer_launch_bytes = int(round(mean_uniq * (gu_bytes + dn_bytes)))
-
-    def rate(kind, nbytes):
-        i = bdg.KERNEL_KINDS.index(kind)
-        if kcnt[i]:
-            kernels[kind]["GBps"] = round(nbytes / (kms[i] / kcnt[i] * 1e-3) / 1e9, 1)
-            return kernels[kind]["GBps"]
-        return None
-    rate("gate_up", gu_launch_bytes)
-    rate("down", int(round(mean_uniq * dn_bytes)))
-    rate("route", router_bytes(cfg))
-    fused = kcnt[bdg.KERNEL_KINDS.index("layer")] > 0
-    if fused:
-        # the fused per-layer kernel: the chosen experts' gate_up and down bytes per launch
-        dom_kernel, dom_kind, dom_bytes = "moe_layer_kernel", "layer", layer_launch_bytes
-    else:
-        dom_kernel, dom_kind, dom_bytes = "moe_gateup_kernel", "gate_up", gu_launch_bytes
-    achieved = rate(dom_kind, dom_bytes)
-    sum_kernel_us = sum(kms[i] for i in range(len(bdg.KERNEL_KINDS))) / K * 1e3
-    log(f"per-kernel: {kernels}; kernel time {sum_kernel_us:.1f} us/step of {gpu_ms / K * 1e3:.1f}")
+    log(f"per-kernel: {kernels}; dispatch time {dispatch_us:.1f} us/step of {gpu_ms / K * 1e3:.1f} replayed "
+        f"(gap share {gap_us:.2f} us per launch)")
 
     stream = None
     if not args.no_stream_read:
@@ -1183,6 +1268,8 @@ def main():
     }
     if routing:
         config["routing"] = routing
+    if args.route_every_layer:
+        config["router"] = "route kernel before every layer"
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -1210,11 +1297,15 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(cfg.name, dom_kind) if m == 1 else None,
+            "traffic": measured_traffic(cfg.name, "layer" if fused else "gate_up") if m == cfg.m else None,
             "traffic_algorithmic_bytes": dom_bytes,
+            "duration_us": kernels["layer" if fused else "gate_up"]["share_us"],
+            "gap_share_us": round(gap_us, 3),
+            "duration": SHARE_NOTE,
+            "achieved_kernel_only": kernels["layer" if fused else "gate_up"]["GBps_kernel_only"],
         },
         "kernels": kernels,
-        "kernel_us_per_step": round(sum_kernel_us, 2),
+        "kernel_us_per_step": round(dispatch_us, 2),
         "stream_read": stream,
         "cpu_baseline": cpu,
     }

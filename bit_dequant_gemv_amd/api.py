@@ -490,22 +490,30 @@ def moe_experts_routed(plan: MoEPlan, layer, x, idx, wts, y=None):
 KERNEL_KINDS = ("route", "gate_up", "down", "combine", "layer")
 
 
-def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc_ms=None, acc_count=None):
-    """One decode step with per-kernel start/stop events; accumulates into
-    acc_ms / acc_count (ctypes double[5] / int64[5], indexed like
-    KERNEL_KINDS) and returns them."""
+class KernelTimes:
+    """Per-kernel-kind accumulators of moe_expert_decode_profiled, indexed like
+    KERNEL_KINDS: ms (sum of the dispatches' start-to-end times) and count."""
+
+    def __init__(self):
+        n = len(KERNEL_KINDS)
+        self.ms = (ctypes.c_double * n)()
+        self.count = (ctypes.c_int64 * n)()
+
+
+def moe_expert_decode_profiled(plan: MoEPlan, x, y, acc: KernelTimes = None) -> KernelTimes:
+    """One decode step with per-kernel start/stop events; accumulates into acc
+    (a new KernelTimes when None) and returns it."""
     x2 = x.reshape(1, -1) if x.dim() == 1 else x
     _shape(x2, (x2.shape[0], plan.hidden), "x")
     _shape(y, (x2.shape[0], plan.hidden), "y")
     if not 1 <= x2.shape[0] <= plan.max_m:
         raise ValueError(f"m must be in [1, {plan.max_m}] (the plan's max_m)")
-    if acc_ms is None:
-        acc_ms = (ctypes.c_double * len(KERNEL_KINDS))()
-        acc_count = (ctypes.c_int64 * len(KERNEL_KINDS))()
+    if acc is None:
+        acc = KernelTimes()
     check("moe_expert_decode_profiled", _lib.load().moe_expert_decode_profiled(
         plan.handle, _dev_ptr(x2, "x"), _x_dtype(x2), x2.shape[0], _dev_ptr(y, "y", torch.float32),
-        acc_ms, acc_count, _stream()))
-    return acc_ms, acc_count
+        acc.ms, acc.count, _stream()))
+    return acc
 
 
 LAYER_STAMPS = ("start", "routed", "gu_issued", "dn_issued", "gu_done", "h_stored", "barrier", "h_staged",

@@ -1,6 +1,7 @@
 // Host-side helpers of libbdg: argument checks and launch error mapping.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

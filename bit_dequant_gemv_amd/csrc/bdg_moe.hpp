@@ -15,7 +15,7 @@ constexpr int kDownWaves = 8;        // waves per down block
 constexpr int kGuPairsPerWave = 6;   // gate_up: (g, u) row pairs in flight per wave
 constexpr int kRouteMaxF4 = 16;      // router row float4 per lane (H <= 4096)
 constexpr int kPartF4 = 8;           // float4 of router partial sums per thread issued up front
-constexpr int kDnRouterPerWave = 8;  // next-layer router rows per down wave
+constexpr int kDnRouterPerWave = 8;  // next-layer router rows per down wave (E <= 64)
 
 // Weight addresses of one layer.  The plan keeps one per layer on the host
 // and passes it by value to each kernel launch (a kernel argument, so the
@@ -225,7 +225,7 @@ struct DownOut {
   float* x_out;               // [M][H] next layer's input, or NULL
   float* y_out;               // [M][H] caller output, or NULL
   float* trace_out;           // [M][H] copy of x_out (next layer's input trace), or NULL
-  int route_next;             // then E <= kDownWaves * kDnRouterPerWave
+  int route_next;             // then E <= kDownWaves * RW (the epilogue's router rows per wave)
   const float* wr_next;       // [E][H]
   float* part_out;            // [M][E + 1][pstride]
   int pstride;
@@ -234,25 +234,28 @@ struct DownOut {
 // The epilogue's router and residual operands for this lane (all in
 // bounds and unconditional, so the compiler's wait counts stay exact): idle
 // lanes past the block's rows repeat its last row.
+template <int RW>
 struct DownEpiIn {
-  float wr[kDnRouterPerWave];   // wr[i] = w_r'[wave + 8i][orow]
+  float wr[RW];                 // wr[i] = w_r'[wave + 8i][orow]
   float xp;                     // x_prev[orow]
   float wk;                     // routing weight of slot `lane` (lane < K), set by the caller
 };
 
-__device__ __forceinline__ void down_epilogue_load(DownEpiIn& in, const DownOut& o, int t, int r0, int B, int lane,
+template <int RW>
+__device__ __forceinline__ void down_epilogue_load(DownEpiIn<RW>& in, const DownOut& o, int t, int r0, int B, int lane,
                                                    int wave) {
   const int orow = min(r0 + min(lane, B - 1), o.H - 1);
   const float* wsrc = o.route_next ? o.wr_next : o.x_prev;
 #pragma unroll
-  for (int i = 0; i < kDnRouterPerWave; ++i) {
+  for (int i = 0; i < RW; ++i) {
     const int er = wave + kDownWaves * i;
     in.wr[i] = wsrc[(int64_t)(o.route_next ? (er < o.E ? er : o.E - 1) : 0) * o.H + orow];
   }
   in.xp = o.x_prev[(int64_t)t * o.H + orow];
 }
 
-__device__ __forceinline__ void down_epilogue(const DownOut& o, const DownEpiIn& in, const float* dpart, int t,
+template <int RW>
+__device__ __forceinline__ void down_epilogue(const DownOut& o, const DownEpiIn<RW>& in, const float* dpart, int t,
                                               int slice, int r0, int B, int lane, int wave) {
   const int row = r0 + lane;
   const bool ok = lane < B && row < o.H;
@@ -269,11 +272,11 @@ __device__ __forceinline__ void down_epilogue(const DownOut& o, const DownEpiIn&
   if (!o.route_next) return;
   // all router rows of the wave (and the rows' sum of squares, column E)
   // reduced together, one butterfly step at a time
-  constexpr int NA = kDnRouterPerWave + 1;
+  constexpr int NA = RW + 1;
   float a[NA];
 #pragma unroll
-  for (int i = 0; i < kDnRouterPerWave; ++i) a[i] = ok ? in.wr[i] * v : 0.f;
-  a[kDnRouterPerWave] = v * v;
+  for (int i = 0; i < RW; ++i) a[i] = ok ? in.wr[i] * v : 0.f;
+  a[RW] = v * v;
 #pragma unroll
   for (int i = 0; i < NA; ++i) a[i] += dpp_quad_xor1(a[i]);
 #pragma unroll
@@ -289,11 +292,11 @@ __device__ __forceinline__ void down_epilogue(const DownOut& o, const DownEpiIn&
   if (lane == 0) {
     float* out = o.part_out + (int64_t)t * (o.E + 1) * o.pstride + slice;
 #pragma unroll
-    for (int i = 0; i < kDnRouterPerWave; ++i) {
+    for (int i = 0; i < RW; ++i) {
       const int er = wave + kDownWaves * i;
       if (er < o.E) out[(int64_t)er * o.pstride] = a[i];
     }
-    if (wave == 0) out[(int64_t)o.E * o.pstride] = a[kDnRouterPerWave];
+    if (wave == 0) out[(int64_t)o.E * o.pstride] = a[RW];
   }
 }
 

@@ -59,7 +59,10 @@ struct LayerConfig {
 
 int layer_fused_lds_bytes(const LayerShape& s, int np, int ng, int sd);
 const void* layer_fused_kernel(const LayerConfig& c);   // NULL: no such variant
-int launch_layer_fused(const LayerConfig& c, const LayerParams& lp, int nblk, size_t lds, hipStream_t s);
+// ev_start / ev_stop (or null): events that take the dispatch's own start and
+// end times.
+int launch_layer_fused(const LayerConfig& c, const LayerParams& lp, int nblk, size_t lds, hipStream_t s,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 int layer_threads();
 int layer_dn_load_waves();
 

@@ -8,9 +8,9 @@
 
 namespace bdg {
 
-constexpr int kMfmaTT = 16;                 // picks per chunk: every pick of an expert (M <= 16)
+constexpr int kMfmaTT = 8;                  // picks per chunk (16 token rows: hi and lo part of each)
 constexpr int kMfmaChunkInts = 2 + kMfmaTT;
-constexpr int kMfmaRows = 32;               // weight rows per matrix-core tile
+constexpr int kMfmaRows = 16;               // weight rows per matrix-core tile
 
 struct MfmaParams {
   // routing (gate_up kernel), as group_route reads it
@@ -37,8 +37,12 @@ struct MfmaParams {
   float* dout;                // [M * K][H] down output per pick
 };
 
-int launch_gu_mfma(const MfmaParams& p, int V, int nblk, hipStream_t s);
-int launch_dn_mfma(const MfmaParams& p, int nblk, hipStream_t s);
+// ev_start / ev_stop (or null): events that take the dispatch's own start and
+// end times.
+int launch_gu_mfma(const MfmaParams& p, int V, int nblk, hipStream_t s, hipEvent_t ev_start = nullptr,
+                   hipEvent_t ev_stop = nullptr);
+int launch_dn_mfma(const MfmaParams& p, int nblk, hipStream_t s, hipEvent_t ev_start = nullptr,
+                   hipEvent_t ev_stop = nullptr);
 size_t mfma_gu_lds_bytes();
 size_t mfma_dn_lds_bytes();
 const void* mfma_gu_kernel(int V);

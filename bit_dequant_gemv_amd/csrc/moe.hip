@@ -33,6 +33,7 @@
 
 #include "bdg_host.hpp"
 #include "bdg_moe.hpp"
+#include "bdg_moe_down.hpp"
 #include "bdg_moe_layer.hpp"
 #include "bdg_moe_mfma.hpp"
 
@@ -371,116 +372,6 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   if (lane < nq) p.h_out[(int64_t)t * P + q0 + lane] = g_sel / (1.0f + expf(-g_sel)) * u_sel;
 }
 
-// ---------------------------------------------------------------- down + combine
-
-struct DownParams {
-  int M, H, I, E, K;
-  const int32_t* idx;         // [M][K] routing buffer
-  const float* h;             // [M][K][I]
-  DownOut o;                  // combine, residual, outputs, next layer's router slice
-  LayerDev L;                 // this layer's weights
-  QGeom g;                    // reduction over I
-};
-
-// Block (rb, t) of 8 waves: WPE = 8 / K waves per chosen expert (1 when
-// K >= 8; experts then go in groups of 8).  Wave w works on expert slot
-// j = jg + w % K' and row groups (w / K'), (w / K') + WPE, ... of the block's
-// B = NR * RPW * WPE rows.  The h_j of a group are staged into LDS by the whole
-// block (loads issued before the expert weights' loads), the partial rows
-// meet in LDS and are combined in slot order with the residual.
-template <int FMT, int L, int S, int NR, int HV>
-__global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams p) {
-  constexpr int RPW = kWave / L;
-  extern __shared__ float lds[];
-  const int kg = p.K < kDownWaves ? p.K : kDownWaves;      // experts per group
-  const int wpe = kDownWaves / kg;                          // waves per expert
-  const int B = NR * RPW * wpe;
-  const int stride = (p.g.chunks + 1) * kXStride;          // per expert: chunks of h, then a zero chunk
-  float* dpart = lds + kg * stride;                         // [K][B]
-  const int t = blockIdx.y;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = uniform_wave_id();
-  const int li = lane % L;
-  const int rr = lane / L;
-  const int r0 = blockIdx.x * B;
-  const int jw = wave % kg;                                 // expert within the group
-  const int sub = wave / kg;                                // row-group phase (sub < wpe, or idle)
-  const bool wave_on = sub < wpe;
-  const LayerDev& Ld = p.L;
-
-  // One group of kg experts: h vectors staged through LDS, the expert rows'
-  // dot products into dpart.  hstage holds the group's h loads, issued by the
-  // caller before anything else it needs later.
-  auto group = [&](int jg, int e, StageF32<HV>& hstage) {
-    const int nj = min(kg, p.K - jg);
-    const bool active = wave_on && jw < nj;
-    const int nh = nj * p.I;
-    GroupLoad<FMT, S> ld[NR];
-    const QMat m = expert_dn(Ld, e);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int row = r0 + (i * wpe + sub) * RPW + rr;
-      load_row<FMT, L, S>(ld[i], m, p.g, row, active && row < p.H, li);
-    }
-    hstage.store(lds, nh, p.I, stride, 1.0f, threadIdx.x, blockDim.x);
-    block_sync_lds();   // weights still in flight
-    if (active) {
-      XRegs<FMT, L, S> xr;
-      xr.load_zpad(lds + jw * stride, p.g.chunks, li);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const float d = row_dot<FMT, L, S>(ld[i], xr);
-        const int b = (i * wpe + sub) * RPW + rr;
-        if (li == kRowSumLane<L> && b < B) dpart[(jg + jw) * B + b] = d;
-      }
-    }
-    block_sync_lds();
-  };
-
-  // loads, in the order their data is needed (vmcnt retires in order): the
-  // first group's expert id and h vectors, the epilogue operands (router
-  // weights of the next layer, residual row, combine weights: all in bounds,
-  // issued unconditionally so the compiler's wait counts stay exact), then
-  // the expert weights.  The first group is outside the loop so no loop
-  // back edge makes the compiler wait for everything before the weights.
-  const int e0 = clamp_expert(p.idx[t * p.K + (jw < p.K ? jw : p.K - 1)], p.E);
-  StageF32<HV> h0;
-  h0.load(p.h + (int64_t)t * p.K * p.I, min(kg, p.K) * p.I, threadIdx.x, blockDim.x);
-  __builtin_amdgcn_sched_barrier(0);   // keep the issue order: the scheduler would sink loads
-  DownEpiIn epi;
-  down_epilogue_load(epi, p.o, t, r0, B, lane, wave);
-  epi.wk = p.o.w[t * p.K + (lane < p.K ? lane : p.K - 1)];
-  __builtin_amdgcn_sched_barrier(0);
-  // the zero chunk after each expert's h (h staging never writes it); no
-  // branch: threads past the kg chunks repeat the last one's stores
-  {
-    const int zr = min((int)(threadIdx.x / kChunkElems), kg - 1);
-    lds[zr * stride + p.g.chunks * kXStride + (threadIdx.x & (kChunkElems - 1))] = 0.f;
-  }
-  group(0, e0, h0);
-  for (int jg = kg; jg < p.K; jg += kg) {   // K > 8 only
-    const int jn = jg + (jw < p.K - jg ? jw : p.K - jg - 1);
-    const int e = clamp_expert(p.idx[t * p.K + jn], p.E);
-    StageF32<HV> hs;
-    hs.load(p.h + ((int64_t)t * p.K + jg) * p.I, min(kg, p.K - jg) * p.I, threadIdx.x, blockDim.x);
-    group(jg, e, hs);
-  }
-
-  if (B <= kWave) {
-    down_epilogue(p.o, epi, dpart, t, blockIdx.x, r0, B, lane, wave);
-    return;
-  }
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int row = r0 + b;
-    if (row >= p.H) continue;
-    float v = p.o.residual ? p.o.x_prev[(int64_t)t * p.H + row] : 0.f;
-    for (int j = 0; j < p.K; ++j) v = __builtin_fmaf(p.o.w[t * p.K + j], dpart[j * B + b], v);
-    if (p.o.x_out) p.o.x_out[(int64_t)t * p.H + row] = v;
-    if (p.o.y_out) p.o.y_out[(int64_t)t * p.H + row] = v;
-    if (p.o.trace_out) p.o.trace_out[(int64_t)t * p.H + row] = v;
-  }
-}
-
 // ---------------------------------------------------------------- grouped path (M > 1)
 //
 // With several tokens per step, tokens share experts (the 120B small-M
@@ -799,22 +690,21 @@ struct Prof {
   int used;
 };
 
-// Each timed kernel is bracketed by event records on its stream: the start
-// event completes when the stream reaches it (the previous kernel done), so a
-// duration covers the launch gap and the kernel, as a kernel trace of
-// back-to-back launches (a graph replay) counts each kernel.
-#define BDG_LAUNCH(PROF, KIND, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                          \
-  do {                                                                                         \
-    if (PROF) {                                                                                \
-      if ((PROF)->used >= (PROF)->cap) return BDG_E_UNSUPPORTED;                               \
-      const int slot_ = (PROF)->used++;                                                        \
-      (PROF)->kind[slot_] = (KIND);                                                            \
-      if (hipEventRecord((PROF)->ev[2 * slot_], STREAM) != hipSuccess) return BDG_E_HIP;       \
-      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                       \
-      if (hipEventRecord((PROF)->ev[2 * slot_ + 1], STREAM) != hipSuccess) return BDG_E_HIP;   \
-    } else {                                                                                   \
-      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                       \
-    }                                                                                          \
+// A timed kernel is launched with a start and a stop event that take the
+// dispatch's own start and end times (the times a kernel trace records for
+// the same dispatch); separate event records on the stream would add their
+// own gaps to every duration.
+#define BDG_LAUNCH(PROF, KIND, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                               \
+  do {                                                                                              \
+    if (PROF) {                                                                                     \
+      if ((PROF)->used >= (PROF)->cap) return BDG_E_UNSUPPORTED;                                    \
+      const int slot_ = (PROF)->used++;                                                             \
+      (PROF)->kind[slot_] = (KIND);                                                                 \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, (PROF)->ev[2 * slot_],                 \
+                            (PROF)->ev[2 * slot_ + 1], 0, __VA_ARGS__);                             \
+    } else {                                                                                        \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                            \
+    }                                                                                               \
   } while (0)
 
 // layer input: the caller's x at layer 0, else the residual buffer written
@@ -982,31 +872,17 @@ static int launch_down(const bdg_plan* p, int layer, int m, int residual, float*
   const int B = p->dn_NR * rpw * wpe;
   const size_t lds = ((size_t)kg * (dp.g.chunks + 1) * kXStride + (size_t)dp.K * B) * sizeof(float);
   dim3 grid((unsigned)((dp.H + B - 1) / B), m);
-  const int fmt = p->d.fmt, NR = p->dn_NR;
   const int hv = down_stage_f4(dp.K, dp.I);
   const int HV = hv <= 2 ? 2 : hv <= 4 ? 4 : hv <= 6 ? 6 : hv <= 8 ? 8 : 12;
-#define BDG_DN_CASE(F, LL, SS, NN, HH)                                                                  \
-  if (fmt == F && p->dn_L == LL && p->dn_S == SS && NR == NN && HV == HH) {                            \
-    BDG_LAUNCH(prof, kDown, (moe_down_kernel<F, LL, SS, NN, HH>), grid, dim3(kDownWaves * kWave), lds, \
-               s, dp);                                                                                  \
-    return launch_status();                                                                             \
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (prof) {
+    if (prof->used >= prof->cap) return BDG_E_UNSUPPORTED;
+    const int slot = prof->used++;
+    prof->kind[slot] = kDown;
+    e0 = prof->ev[2 * slot];
+    e1 = prof->ev[2 * slot + 1];
   }
-#define BDG_DN_HV(F, LL, SS, NN) \
-  BDG_DN_CASE(F, LL, SS, NN, 2) BDG_DN_CASE(F, LL, SS, NN, 4) BDG_DN_CASE(F, LL, SS, NN, 6) \
-  BDG_DN_CASE(F, LL, SS, NN, 8) BDG_DN_CASE(F, LL, SS, NN, 12)
-#define BDG_DN_NR(F, LL, SS) \
-  BDG_DN_HV(F, LL, SS, 1) BDG_DN_HV(F, LL, SS, 2) BDG_DN_HV(F, LL, SS, 3) BDG_DN_HV(F, LL, SS, 4)
-#define BDG_DN_ALL(F)                                                             \
-  BDG_DN_NR(F, 8, 1) BDG_DN_NR(F, 8, 2) BDG_DN_NR(F, 8, 3) BDG_DN_NR(F, 16, 2)   \
-  BDG_DN_NR(F, 16, 3) BDG_DN_NR(F, 32, 2) BDG_DN_NR(F, 32, 3) BDG_DN_NR(F, 64, 2) \
-  BDG_DN_NR(F, 64, 3) BDG_DN_NR(F, 64, 4)
-  BDG_DN_ALL(kMXFP4)
-  BDG_DN_ALL(kINT4G)
-#undef BDG_DN_ALL
-#undef BDG_DN_NR
-#undef BDG_DN_HV
-#undef BDG_DN_CASE
-  return BDG_E_UNSUPPORTED;
+  return launch_down_kernel(dp, p->d.fmt, p->dn_L, p->dn_S, p->dn_NR, HV, grid, lds, s, e0, e1);
 }
 
 static int launch_gu_group(const bdg_plan* p, int layer, int m, int routed, const int32_t* idx_in,
@@ -1124,14 +1000,12 @@ static int launch_layer(const bdg_plan* p, int layer, int nparts, int32_t* topk_
   lp.o = down_out(p, layer, residual, x_out, y_out, trace_out, route_next);
   lp.stamps = p->tl_active ? p->tl_stamps + (size_t)layer * p->fused_nblk * kLayerStamps : nullptr;
   if (prof) {
-    // bracketed by event records, as BDG_LAUNCH does
+    // dispatch events, as BDG_LAUNCH takes them
     if (prof->used >= prof->cap) return BDG_E_UNSUPPORTED;
     const int slot = prof->used++;
     prof->kind[slot] = kLayer;
-    if (hipEventRecord(prof->ev[2 * slot], s) != hipSuccess) return BDG_E_HIP;
-    const int st = launch_layer_fused(p->fused_cfg, lp, p->fused_nblk, p->fused_lds, s);
-    if (st) return st;
-    return hip_status(hipEventRecord(prof->ev[2 * slot + 1], s));
+    return launch_layer_fused(p->fused_cfg, lp, p->fused_nblk, p->fused_lds, s, prof->ev[2 * slot],
+                              prof->ev[2 * slot + 1]);
   }
   return launch_layer_fused(p->fused_cfg, lp, p->fused_nblk, p->fused_lds, s);
 }
@@ -1166,20 +1040,20 @@ static MfmaParams mfma_params(const bdg_plan* p, int layer, int m, int routed, c
   return mp;
 }
 
-// The matrix-core grouped gate_up and down of one layer, timed like BDG_LAUNCH.
+// The matrix-core grouped gate_up and down of one layer, timed as BDG_LAUNCH times.
 static int launch_mfma_pair(const bdg_plan* p, const MfmaParams& mp, hipStream_t s, Prof* prof) {
   for (int which = 0; which < 2; ++which) {
-    int slot = -1;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
     if (prof) {
       if (prof->used >= prof->cap) return BDG_E_UNSUPPORTED;
-      slot = prof->used++;
+      const int slot = prof->used++;
       prof->kind[slot] = which == 0 ? kGateUp : kDown;
-      if (hipEventRecord(prof->ev[2 * slot], s) != hipSuccess) return BDG_E_HIP;
+      e0 = prof->ev[2 * slot];
+      e1 = prof->ev[2 * slot + 1];
     }
-    const int st = which == 0 ? launch_gu_mfma(mp, p->topk_V, p->mfma_grid_gu, s)
-                              : launch_dn_mfma(mp, p->mfma_grid_dn, s);
+    const int st = which == 0 ? launch_gu_mfma(mp, p->topk_V, p->mfma_grid_gu, s, e0, e1)
+                              : launch_dn_mfma(mp, p->mfma_grid_dn, s, e0, e1);
     if (st) return st;
-    if (prof && hipEventRecord(prof->ev[2 * slot + 1], s) != hipSuccess) return BDG_E_HIP;
   }
   return BDG_OK;
 }
@@ -1338,7 +1212,9 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     const int B = p->dn_NR * rpw * wpe;
     p->dn_blocks = (d->hidden + B - 1) / B;
     // a layer routes from the previous down kernel's partial sums when the
-    // sums are small enough for every gate_up block to add them up
+    // sums are small enough for every gate_up block to add them up (more
+    // than 64 experts keep the route kernel: fusing them needed fewer, taller
+    // down blocks and measured slower on the 128-expert int4 stack)
     p->fuse_route = (d->flags & BDG_MOE_STACK) && d->n_layers > 1 && B <= kWave &&
                     p->dn_blocks <= 4 * kThreads && d->n_experts <= kDownWaves * kDnRouterPerWave &&
                     !(d->flags & BDG_MOE_ROUTE_EVERY_LAYER);
@@ -1375,11 +1251,11 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
                   p->gu_S <= (d->fmt == BDG_FMT_MXFP4 ? 3 : 2) &&
                   lds_gu <= 64 * 1024 &&
                   lds_dn <= 64 * 1024 && !(d->flags & BDG_MOE_PER_TOKEN);
-    // grouped products on the matrix cores: MXFP4, K multiples of 64 (whole
-    // 2-block super-steps), grids of every block the kernels keep resident
+    // grouped products on the matrix cores: MXFP4 (hidden and inter are
+    // multiples of 32: whole 16-row tile pairs and MX blocks), grids of
+    // every block the kernels keep resident
     p->mfma = 0;
-    if ((d->flags & BDG_MOE_MFMA) && p->group_ok && d->fmt == BDG_FMT_MXFP4 && d->hidden % 64 == 0 &&
-        d->inter % 64 == 0 && d->max_m <= 16) {
+    if ((d->flags & BDG_MOE_MFMA) && p->group_ok && d->fmt == BDG_FMT_MXFP4 && d->max_m <= 16) {
       int bg = 0, bd = 0;
       const void* fg = mfma_gu_kernel(p->topk_V);
       if (fg && hipOccupancyMaxActiveBlocksPerMultiprocessor(&bg, fg, 256, 0) == hipSuccess &&

@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(kLayerThreads) moe_layer_kernel(LayerParams p)
     const int idx = min((int)threadIdx.x + kLayerThreads * n, KI - 1);
     hv[n] = __hip_atomic_load(p.hbuf + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  DownEpiIn epi;
+  DownEpiIn<kDnRouterPerWave> epi;
   down_epilogue_load(epi, p.o, 0, r0, p.B, lane, wave);
   epi.wk = my_w;
   const float poison = flag[0] ? __uint_as_float(0x7FC00000u) : 0.f;   // NaN after a failed wait
@@ -369,12 +369,13 @@ const void* layer_fused_kernel(const LayerConfig& c) {
   return nullptr;
 }
 
-int launch_layer_fused(const LayerConfig& c, const LayerParams& lp, int nblk, size_t lds, hipStream_t s) {
+int launch_layer_fused(const LayerConfig& c, const LayerParams& lp, int nblk, size_t lds, hipStream_t s,
+                       hipEvent_t ev_start, hipEvent_t ev_stop) {
 #define BDG_LAUNCH_ONE(F, SG_, NP_, V_, LD_, SD_, NG_, NHL_)                                                \
   if (c.fmt == F && c.sg == SG_ && c.np == NP_ && c.v == V_ && c.ld == LD_ && c.sd == SD_ && c.ng == NG_ && \
       c.nhl == NHL_) {                                                                                       \
-    hipLaunchKernelGGL((moe_layer_kernel<F, SG_, NP_, V_, LD_, SD_, NG_, NHL_>), dim3(nblk),                \
-                       dim3(kLayerThreads), lds, s, lp);                                                     \
+    hipExtLaunchKernelGGL((moe_layer_kernel<F, SG_, NP_, V_, LD_, SD_, NG_, NHL_>), dim3(nblk),             \
+                          dim3(kLayerThreads), lds, s, ev_start, ev_stop, 0, lp);                            \
     return launch_status();                                                                                  \
   }
   BDG_LAYER_VARIANTS(BDG_LAUNCH_ONE)

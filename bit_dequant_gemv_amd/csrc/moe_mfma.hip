@@ -5,8 +5,8 @@
 // small M of a decode step most chosen experts serve one or two tokens, and
 // the grouped VALU kernels (moe.hip) decode every weight once per pick; at
 // M = 16 their waves keep the vector unit about 80% busy.  Here each
-// distinct expert of a layer is one chunk holding all its picks (t <= 16),
-// and its products run on v_mfma_f32_32x32x16_bf16 with:
+// distinct expert of a layer is one or more chunks of up to 8 picks, and its
+// products run on v_mfma_f32_16x16x32_bf16 with:
 //   * weights decoded once per element to bf16 with the E8M0 block scale
 //     applied in the conversion (v_cvt_scalef32_pk_bf16_fp4: E2M1 times
 //     2^(e-127) is exact in bf16, subnormals included, +-inf exactly where
@@ -14,19 +14,25 @@
 //   * activations as two bf16 parts, hi = bf16(v) and lo = bf16(v - hi), so
 //     hi + lo carries v to about 2^-17 relative and every product is exact
 //     in the fp32 accumulator (the decode path's fp32 accuracy, not bf16's);
-//   * the weight rows as the instruction's columns: D[token row][weight row],
-//     token rows 0..15 = the picks' hi parts, 16..31 = their lo parts, so a
-//     lane's 16 results all belong to one weight row and y = D[r] + D[r + 8].
-// MFMA operand layout (measured on the device with one-hot operands): lane l
-// supplies row (A) / column (B) l % 32 and K positions 8 (l / 32) + i; D
-// register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column
-// l % 32.  Lanes 0..31 take MX block 2s of a super-step s, lanes 32..63
-// block 2s + 1, so one 16-byte code chunk feeds a lane for 4 instructions.
+//   * the weight rows as the instruction's 16 columns and the picks' parts
+//     as its 16 rows: token row 2s is pick slot s's hi part, 2s + 1 its lo
+//     part, so lane (n, q) ends with rows 4q .. 4q+3 of weight row n, i.e.
+//     slots 2q and 2q + 1, and y = D[2s] + D[2s + 1] lane-locally.
+// Operand layout: lane l supplies row (A) / column (B) l % 16 and one group
+// of 8 K positions per lane quarter q = l / 16 (A and B alike, so any
+// assignment of K to (q, element) that both sides share is correct); D
+// register r of lane l holds row 4 (l / 16) + r, column l % 16.  Quarter q
+// of a K group takes MX block 4g + q whole: its 16 code bytes are one load
+// and feed the 4 instructions of the group (bytes 4j .. 4j+3 in
+// instruction j), so one load instruction reads 64 contiguous bytes of each
+// of 16 weight rows and the next group the rest of the 128-byte line.
 //
-// A wave takes (chunk, 32-row tile) items: gate_up tiles pair gate rows
-// i0..i0+31 with up rows I+i0..I+i0+31 so h = silu(g) u forms lane-locally
-// and is written as its bf16 hi/lo parts; down tiles write one fp32 output
-// row block per pick, combined later in slot order as on the VALU path.
+// A block (4 waves) takes (chunk, tile pair) items: gate_up pairs gate rows
+// i0..i0+15 with up rows I+i0.. so h = silu(g) u forms lane-locally and is
+// written as its bf16 hi/lo parts; down pairs two 16-row tiles of the
+// output.  The 4 waves split the K groups of an item, keep 3 groups in
+// flight each, and add their partial tiles in LDS in wave order (a fixed
+// order: results do not depend on timing).
 #include "bdg_host.hpp"
 #include "bdg_moe.hpp"
 #include "bdg_moe_mfma.hpp"
@@ -35,14 +41,16 @@ namespace bdg {
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
-typedef float f32x16_v __attribute__((ext_vector_type(16)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaThreads = 256;
 constexpr int kMfmaWaves = kMfmaThreads / kWave;
+constexpr int kMfmaDepth = 3;               // K groups in flight per wave
 using MfmaGroupLds = GroupLdsT<kMfmaTT>;
 
 // 16 bytes of E2M1 codes (32 elements, one MX block) to 4 MFMA B operands of
-// 8 bf16, the block scale applied in the conversion.
+// 8 bf16 (elements 8j .. 8j+7 in operand j), the block scale applied in the
+// conversion.
 __device__ __forceinline__ void fp4_chunk_to_bf16(const uint4 q, float scale, bf16x8_v (&b)[4]) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -57,65 +65,140 @@ __device__ __forceinline__ void fp4_chunk_to_bf16(const uint4 q, float scale, bf
 
 __device__ __forceinline__ bf16x8_v as_bf16x8(const uint4 v) { return __builtin_bit_cast(bf16x8_v, v); }
 
-// E8M0 byte -> fp32 scale 2^(e-127) (e = 0: the subnormal 2^-127; 255: NaN).
-__device__ __forceinline__ float e8m0_scale(uint32_t e) { return e8m0_to_f32(e); }
-
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return f32_to_bf16_rne(v); }
-
-// The operand row of token row `ar` of an item: the hi or lo part of the
-// pick's activation (or the zero row when the chunk has fewer picks).
+// The operand row of token row `ar` (0..15) of an item: the hi (even rows)
+// or lo (odd rows) part of pick slot ar / 2's activation, or the zero row
+// when the chunk has fewer picks.
 __device__ __forceinline__ const uint16_t* operand_row(const int* picks, int nt, int ar, const uint16_t* hi,
                                                        const uint16_t* lo, const uint16_t* zeros, int64_t stride,
                                                        int pick_div) {
-  const int slot = ar & 15;
+  const int slot = ar >> 1;
   if (slot >= nt) return zeros;
   const int src = picks[slot] / pick_div;
-  return (ar >= 16 ? lo : hi) + (int64_t)src * stride;
+  return ((ar & 1) ? lo : hi) + (int64_t)src * stride;
 }
 
-// Token row of D register r (r < 8) for lane half h.
-__device__ __forceinline__ int d_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+// One K group of one lane: the codes and scale of block b of its two weight
+// rows, and elements 32b .. 32b+31 of its token row.
+struct MfmaStage {
+  uint4 q[2];
+  uint32_t sc[2];
+  uint4 a[4];
+};
 
-// One tile: acc[T] += D over a K of `kblocks` MX blocks, for T weight tiles
-// sharing the activation operand.  Row r of tile T reads codes/scales at
-// crow[T] / srow[T] (the lane's weight row); the activation row is arow.
-template <int T>
-__device__ __forceinline__ void mfma_tile(f32x16_v (&acc)[T], const uint8_t* const (&crow)[T],
-                                          const uint8_t* const (&srow)[T], const uint16_t* arow, int kblocks,
-                                          int h) {
-  const int nsuper = kblocks >> 1;
-  // loads of super-step s: this lane's block 2s + h
-  uint4 q[T], qn[T];
-  uint32_t sc[T], scn[T];
-  uint4 a[4], an[4];
-  auto load = [&](int s, uint4 (&qq)[T], uint32_t (&ss)[T], uint4 (&aa)[4]) {
-    const int bk = 2 * s + h;
+__device__ __forceinline__ void stage_load(MfmaStage& st, const uint8_t* const (&crow)[2],
+                                           const uint8_t* const (&srow)[2], const uint16_t* arow, int b) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      qq[t] = ldg_u128(crow[t] + (uint32_t)bk * 16u);
-      ss[t] = ldg_u8(srow[t] + bk);
+  for (int t = 0; t < 2; ++t) {
+    st.q[t] = ldg_u128(crow[t] + (uint32_t)b * 16u);
+    st.sc[t] = ldg_u8(srow[t] + b);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st.a[j] = ldg_u128(arow + b * 32 + 8 * j);
+}
+
+// acc[t] += the group's products; an invalid group (past the row's blocks,
+// or past this wave's share) adds exact zeros (zero codes, unit scale).
+__device__ __forceinline__ void stage_mma(f32x4_v (&acc)[2], const MfmaStage& st, bool valid) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x8_v b[4];
+    const uint4 q = valid ? st.q[t] : make_uint4(0u, 0u, 0u, 0u);
+    fp4_chunk_to_bf16(q, valid ? e8m0_to_f32(st.sc[t]) : 1.0f, b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[j]), b[j], acc[t], 0, 0, 0);
+  }
+}
+
+// The 4 waves' partial tiles of an item meet here; wave 0 adds them in wave
+// order.  Double-buffered by item parity, so one barrier per item suffices.
+struct MfmaRed {
+  float v[2][kMfmaWaves][8][kWave];
+};
+
+// Operand addresses of one item for one lane: its two weight rows' codes and
+// scales, and its token row.
+struct MfmaRows {
+  const uint8_t* crow[2];
+  const uint8_t* srow[2];
+  const uint16_t* arow;
+};
+
+// A block's items (first, first + stride, ... < nitems) streamed by its 4
+// waves: wave w takes K groups [g0, g1) of every item (4 MX blocks each, kb
+// per row; lane quarter q takes block 4g + q), one step per group, and its
+// loads run kMfmaDepth steps ahead across item boundaries, so the next
+// item's first groups are in flight while an item finishes.  rows(item)
+// gives an item's operand addresses; finish(item, j, y) runs in wave 0 with
+// the item's summed tile (y[0..3]: first weight row, token rows 4q..4q+3;
+// y[4..7]: second weight row), j the block-local item index.
+template <class RowsF, class FinishF>
+__device__ __forceinline__ void mfma_stream(MfmaRed& red, int first, int stride, int nitems, int kb, int wave,
+                                            int lane, RowsF rows, FinishF finish) {
+  const int q = lane >> 4;
+  const int ngr = (kb + 3) >> 2;
+  const int g0 = ngr * wave / kMfmaWaves, g1 = ngr * (wave + 1) / kMfmaWaves;
+  const int n = g1 - g0;
+  const int ns = n > 0 ? n : 1;              // steps per item (a wave without groups still meets each barrier)
+  const int nj = first < nitems ? (nitems - first + stride - 1) / stride : 0;
+  const int total = nj * ns;
+
+  // load side: (item, step) of the next stage to fill, and its item's rows;
+  // stages past the last step (the prologue of a block with few steps)
+  // reload the last item's rows, in bounds and never used
+  int ld_j = 0, ld_i = 0;
+  MfmaRows lr = rows(first < nitems ? first : 0);
+  auto load_next = [&](MfmaStage& st) {
+    if (ld_i == 0 && ld_j > 0 && ld_j < nj) lr = rows(first + ld_j * stride);   // LDS reads only
+    const int b = min(4 * (g0 + min(ld_i, ns - 1)) + q, kb - 1);
+    stage_load(st, lr.crow, lr.srow, lr.arow, b);
+    if (++ld_i == ns) {
+      ld_i = 0;
+      ++ld_j;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aa[i] = ldg_u128(arow + bk * 32 + 8 * i);
   };
-  load(0, q, sc, a);
-  for (int s = 0; s < nsuper; ++s) {
-    const int sn = s + 1 < nsuper ? s + 1 : s;   // the last step reloads itself (in bounds, unused)
-    load(sn, qn, scn, an);
+  MfmaStage st[kMfmaDepth];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      bf16x8_v b[4];
-      fp4_chunk_to_bf16(q[t], e8m0_scale(sc[t]), b);
+  for (int d = 0; d < kMfmaDepth; ++d) load_next(st[d]);
+
+  // Every stage is reloaded unconditionally (the last kMfmaDepth loads of a
+  // wave fetch in-bounds rows nobody uses): with a load skipped on some path
+  // the compiler could not count the loads still in flight at the loop's
+  // join and would wait for all of them before the first product.
+  f32x4_v acc[2] = {f32x4_v{0.f, 0.f, 0.f, 0.f}, f32x4_v{0.f, 0.f, 0.f, 0.f}};
+  int cp_j = 0, cp_i = 0;
+  for (int t0 = 0; t0 < total; t0 += kMfmaDepth) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), b[i], acc[t], 0, 0, 0);
+    for (int d = 0; d < kMfmaDepth; ++d) {
+      const bool live = t0 + d < total;
+      stage_mma(acc, st[d], live && cp_i < n && 4 * (g0 + cp_i) + q < kb);
+      load_next(st[d]);
+      if (live) {
+        if (++cp_i == ns) {
+          const int buf = cp_j & 1;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) red.v[buf][wave][4 * t + k][lane] = acc[t][k];
+          acc[0] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+          acc[1] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+          block_sync_lds();
+          if (wave == 0) {
+            float y[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              float sum = red.v[buf][0][k][lane];
+#pragma unroll
+              for (int w = 1; w < kMfmaWaves; ++w) sum += red.v[buf][w][k][lane];
+              y[k] = sum;
+            }
+            finish(first + cp_j * stride, cp_j, y);
+          }
+          cp_i = 0;
+          ++cp_j;
+        }
+      }
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      q[t] = qn[t];
-      sc[t] = scn[t];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = an[i];
   }
 }
 
@@ -124,88 +207,103 @@ __device__ __forceinline__ void mfma_tile(f32x16_v (&acc)[T], const uint8_t* con
 template <int V>
 __global__ void __launch_bounds__(kMfmaThreads) moe_gu_mfma_kernel(MfmaParams p) {
   __shared__ MfmaGroupLds gl;
+  __shared__ MfmaRed red;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_wave_id();
   group_route<V, kMfmaTT>(gl, p, lane, wave, kMfmaWaves);
   if (blockIdx.x == 0) write_chunk_table(gl, p.table, kMfmaThreads);
 
-  const int h = lane >> 5;
-  const int wr = lane & 31;
+  const int n = lane & 15;
+  const int q = lane >> 4;
   const int kb = p.H / 32;
   const int tiles = p.I / kMfmaRows;
-  const int nitems = gl.n * tiles;
-  const int GW = gridDim.x * kMfmaWaves;
-  for (int item = blockIdx.x * kMfmaWaves + wave; item < nitems; item += GW) {
+  auto rows = [&](int item) {
     const int c = item / tiles;
     const int i0 = (item - c * tiles) * kMfmaRows;
-    const int e = gl.ce[c];
+    const QMat m = expert_gu(p.L, gl.ce[c]);
+    const uint32_t grow = (uint32_t)(i0 + n), urow = (uint32_t)(p.I + i0 + n);
+    MfmaRows r;
+    r.crow[0] = m.codes + grow * (uint32_t)kb * 16u;
+    r.crow[1] = m.codes + urow * (uint32_t)kb * 16u;
+    r.srow[0] = m.scales + grow * (uint32_t)kb;
+    r.srow[1] = m.scales + urow * (uint32_t)kb;
+    r.arow = operand_row(gl.cpk[c], gl.cn[c], n, p.xh, p.xl, p.zeros, p.H, p.K);
+    return r;
+  };
+  // lane (n, q): slots 2q and 2q + 1 of gate row i0 + n (y[0..3]) and of up row I + i0 + n (y[4..7])
+  auto finish = [&](int item, int, const float (&y)[8]) {
+    const int c = item / tiles;
+    const int i0 = (item - c * tiles) * kMfmaRows;
     const int nt = gl.cn[c];
-    const QMat m = expert_gu(p.L, e);
-    const uint32_t grow = (uint32_t)(i0 + wr), urow = (uint32_t)(p.I + i0 + wr);
-    const uint8_t* const crow[2] = {m.codes + grow * (uint32_t)kb * 16u, m.codes + urow * (uint32_t)kb * 16u};
-    const uint8_t* const srow[2] = {m.scales + grow * (uint32_t)kb, m.scales + urow * (uint32_t)kb};
-    const uint16_t* arow = operand_row(gl.cpk[c], nt, lane & 31, p.xh, p.xl, p.zeros, p.H, p.K);
-    f32x16_v acc[2] = {};
-    mfma_tile<2>(acc, crow, srow, arow, kb, h);
-    // h = silu(g) u for each pick of the chunk, as bf16 hi/lo parts
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int slot = d_row(r, h);
+    for (int h = 0; h < 2; ++h) {
+      const int slot = 2 * q + h;
       if (slot < nt) {
-        const float g = acc[0][r] + acc[0][r + 8];
-        const float u = acc[1][r] + acc[1][r + 8];
+        const float g = y[2 * h] + y[2 * h + 1];
+        const float u = y[4 + 2 * h] + y[4 + 2 * h + 1];
         const float hv = g / (1.0f + expf(-g)) * u;
-        const uint16_t hi = bf16_bits(hv);
-        const uint16_t lo = bf16_bits(hv - bf16_to_f32(hi));
-        const int64_t o = (int64_t)gl.cpk[c][slot] * p.I + i0 + wr;
+        const uint16_t hi = f32_to_bf16_rne(hv);
+        const uint16_t lo = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+        const int64_t o = (int64_t)gl.cpk[c][slot] * p.I + i0 + n;
         p.hh[o] = hi;
         p.hl[o] = lo;
       }
     }
-  }
+  };
+  mfma_stream(red, blockIdx.x, gridDim.x, gl.n * tiles, kb, wave, lane, rows, finish);
 }
 
 // ---------------------------------------------------------------- down
 
 __global__ void __launch_bounds__(kMfmaThreads) moe_dn_mfma_kernel(MfmaParams p) {
   __shared__ int tab[1 + kGroupMaxPicks * kMfmaChunkInts];
+  __shared__ MfmaRed red;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform_wave_id();
-  const int n = p.table[0];
-  for (int i = threadIdx.x; i < n * kMfmaChunkInts; i += kMfmaThreads) tab[1 + i] = p.table[1 + i];
+  const int nch = p.table[0];
+  for (int i = threadIdx.x; i < nch * kMfmaChunkInts; i += kMfmaThreads) tab[1 + i] = p.table[1 + i];
   __syncthreads();
 
-  const int h = lane >> 5;
-  const int wr = lane & 31;
+  const int n = lane & 15;
+  const int q = lane >> 4;
   const int kb = p.I / 32;
-  const int tiles = p.H / kMfmaRows;
-  const int nitems = n * tiles;
-  const int GW = gridDim.x * kMfmaWaves;
-  for (int item = blockIdx.x * kMfmaWaves + wave; item < nitems; item += GW) {
+  const int tiles = p.H / (2 * kMfmaRows);
+  auto rows = [&](int item) {
     const int c = item / tiles;
-    const int r0 = (item - c * tiles) * kMfmaRows;
+    const int r0 = (item - c * tiles) * 2 * kMfmaRows;
     const int* ch = tab + 1 + c * kMfmaChunkInts;
-    const int e = clamp_expert(ch[0], p.E);
+    const QMat m = expert_dn(p.L, clamp_expert(ch[0], p.E));
+    const uint32_t ra = (uint32_t)(r0 + n), rb = (uint32_t)(r0 + kMfmaRows + n);
+    MfmaRows r;
+    r.crow[0] = m.codes + ra * (uint32_t)kb * 16u;
+    r.crow[1] = m.codes + rb * (uint32_t)kb * 16u;
+    r.srow[0] = m.scales + ra * (uint32_t)kb;
+    r.srow[1] = m.scales + rb * (uint32_t)kb;
+    r.arow = operand_row(ch + 2, ch[1], n, p.hh, p.hl, p.zeros, p.I, 1);
+    return r;
+  };
+  auto finish = [&](int item, int, const float (&y)[8]) {
+    const int c = item / tiles;
+    const int r0 = (item - c * tiles) * 2 * kMfmaRows;
+    const int* ch = tab + 1 + c * kMfmaChunkInts;
     const int nt = ch[1];
-    const QMat m = expert_dn(p.L, e);
-    const uint32_t row = (uint32_t)(r0 + wr);
-    const uint8_t* const crow[1] = {m.codes + row * (uint32_t)kb * 16u};
-    const uint8_t* const srow[1] = {m.scales + row * (uint32_t)kb};
-    const uint16_t* arow = operand_row(ch + 2, nt, lane & 31, p.hh, p.hl, p.zeros, p.I, 1);
-    f32x16_v acc[1] = {};
-    mfma_tile<1>(acc, crow, srow, arow, kb, h);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int slot = d_row(r, h);
-      if (slot < nt) p.dout[(int64_t)ch[2 + slot] * p.H + r0 + wr] = acc[0][r] + acc[0][r + 8];
+    for (int h = 0; h < 2; ++h) {
+      const int slot = 2 * q + h;
+      if (slot < nt) {
+        float* out = p.dout + (int64_t)ch[2 + slot] * p.H;
+        out[r0 + n] = y[2 * h] + y[2 * h + 1];
+        out[r0 + kMfmaRows + n] = y[4 + 2 * h] + y[4 + 2 * h + 1];
+      }
     }
-  }
+  };
+  mfma_stream(red, blockIdx.x, gridDim.x, nch * tiles, kb, wave, lane, rows, finish);
 }
 
 // ---------------------------------------------------------------- host side
 
-size_t mfma_gu_lds_bytes() { return sizeof(MfmaGroupLds); }
-size_t mfma_dn_lds_bytes() { return sizeof(int) * (1 + kGroupMaxPicks * kMfmaChunkInts); }
+size_t mfma_gu_lds_bytes() { return sizeof(MfmaGroupLds) + sizeof(MfmaRed); }
+size_t mfma_dn_lds_bytes() { return sizeof(int) * (1 + kGroupMaxPicks * kMfmaChunkInts) + sizeof(MfmaRed); }
 
 const void* mfma_gu_kernel(int V) {
   switch (V) {
@@ -218,19 +316,21 @@ const void* mfma_gu_kernel(int V) {
 }
 const void* mfma_dn_kernel() { return reinterpret_cast<const void*>(&moe_dn_mfma_kernel); }
 
-int launch_gu_mfma(const MfmaParams& p, int V, int nblk, hipStream_t s) {
+int launch_gu_mfma(const MfmaParams& p, int V, int nblk, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+#define BDG_GU_MFMA(VV)                                                                                         \
+  case VV:                                                                                                       \
+    hipExtLaunchKernelGGL(moe_gu_mfma_kernel<VV>, dim3(nblk), dim3(kMfmaThreads), 0, s, ev_start, ev_stop, 0, p); \
+    break;
   switch (V) {
-    case 1: hipLaunchKernelGGL(moe_gu_mfma_kernel<1>, dim3(nblk), dim3(kMfmaThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(moe_gu_mfma_kernel<2>, dim3(nblk), dim3(kMfmaThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(moe_gu_mfma_kernel<4>, dim3(nblk), dim3(kMfmaThreads), 0, s, p); break;
-    case 16: hipLaunchKernelGGL(moe_gu_mfma_kernel<16>, dim3(nblk), dim3(kMfmaThreads), 0, s, p); break;
+    BDG_GU_MFMA(1) BDG_GU_MFMA(2) BDG_GU_MFMA(4) BDG_GU_MFMA(16)
     default: return BDG_E_UNSUPPORTED;
   }
+#undef BDG_GU_MFMA
   return launch_status();
 }
 
-int launch_dn_mfma(const MfmaParams& p, int nblk, hipStream_t s) {
-  hipLaunchKernelGGL(moe_dn_mfma_kernel, dim3(nblk), dim3(kMfmaThreads), 0, s, p);
+int launch_dn_mfma(const MfmaParams& p, int nblk, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  hipExtLaunchKernelGGL(moe_dn_mfma_kernel, dim3(nblk), dim3(kMfmaThreads), 0, s, ev_start, ev_stop, 0, p);
   return launch_status();
 }
 

@@ -418,9 +418,8 @@ int attn_decode_noalloc(const float* q, const float* k, const float* v, void* k_
 
 /* moe_expert_decode_profiled - one decode step exactly as moe_expert_decode
  * computes it (same kernels, same grids), launched directly rather than from
- * a graph, each kernel between a start and a stop event recorded on the
- * stream (so a duration covers the kernel and the launch gap before it, the
- * way a kernel trace of back-to-back graph replays counts it).  Adds each kernel's duration (ms) to
+ * a graph, each kernel with a start and a stop event that take the
+ * dispatch's own start and end times.  Adds each kernel's duration (ms) to
  * kernel_ms[kind] and 1 to kernel_count[kind]; kind 0 = route (router
  * GEMV + sum of squares, and for steps of m > 1 the previous layer's
  * combine), 1 = gate_up (top-k + grouped gate_up GEMV + SwiGLU), 2 = down

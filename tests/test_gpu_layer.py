@@ -39,7 +39,7 @@ def shape_cfg(name, base):
 
 def kernel_counts(plan, x):
     y = torch.empty((1, plan.hidden), dtype=torch.float32, device=x.device)
-    _, cnt = bdg.moe_expert_decode_profiled(plan, x, y)
+    cnt = bdg.moe_expert_decode_profiled(plan, x, y).count
     torch.cuda.synchronize()
     return {k: int(cnt[i]) for i, k in enumerate(bdg.KERNEL_KINDS)}
 

@@ -1,6 +1,8 @@
 """GPU parity of the grouped expert products on the matrix cores
-(BDG_MOE_MFMA, moe_mfma.hip): steps of M > 1 tokens with every distinct
-expert's picks in one chunk, weights decoded to bf16 with their block scale
+(BDG_MOE_MFMA, moe_mfma.hip): steps of M > 1 tokens with up to 8 of a
+distinct expert's picks per chunk (an expert with more spans several
+chunks), K split over a block's 4 waves (a wave may get no K group at all
+when the rows are short), weights decoded to bf16 with their block scale
 (the conversion pinned by the exhaustive bf16 dequant test), activations as
 bf16 hi + lo parts, fp32 accumulation.  Held to the same oracle tolerance as
 the VALU path: max |y - y_ref| / (|W| . |x|) <= 1e-4, cosine >= 0.99999, per
@@ -23,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 def kernel_counts(plan, x):
     y = torch.empty((x.shape[0], plan.hidden), dtype=torch.float32, device=x.device)
-    _, cnt = bdg.moe_expert_decode_profiled(plan, x, y)
+    cnt = bdg.moe_expert_decode_profiled(plan, x, y).count
     torch.cuda.synchronize()
     return {k: int(cnt[i]) for i, k in enumerate(bdg.KERNEL_KINDS)}
 
@@ -50,8 +52,10 @@ def test_mfma_stack_small(dev, m):
 @pytest.mark.parametrize("case", ["all_on_two", "spread", "k_equals_e"])
 def test_mfma_routed(dev, case):
     """Fixed routing through the matrix-core pair: 16 tokens on the same two
-    experts (t = 16 per chunk), picks spread over many experts (t = 1), and
-    k = E (every token on every expert)."""
+    experts (16 picks per expert: two chunks of 8), picks spread over many
+    experts (one pick per chunk; H = 320 gives 10 MX blocks, so one wave of
+    the block gets no K group and the last group is half empty), and k = E
+    (every token on every expert)."""
     if case == "k_equals_e":
         cfg = small_cfg("mxfp4", 4100, E=4, k=4, H=256, I=128, m=7)
     else:

@@ -80,7 +80,7 @@ def test_layer_small(dev, fmt, m):
 def route_launches(plan, x):
     """Route-kernel launches of one decode step (per-kernel event pass)."""
     y = torch.empty((x.shape[0], plan.hidden), dtype=torch.float32, device=x.device)
-    _, cnt = bdg.moe_expert_decode_profiled(plan, x, y)
+    cnt = bdg.moe_expert_decode_profiled(plan, x, y).count
     torch.cuda.synchronize()
     return int(cnt[bdg.KERNEL_KINDS.index("route")])
 
