@@ -179,16 +179,35 @@ def summarize(argv):
     if a.what == "trace":
         rows = list(csv.DictReader(open(_find(a.src[0], "kernel_stats.csv"))))
         total = sum(float(r["TotalDurationNs"]) for r in rows)
+        # per dispatch: back to back (its start is the previous dispatch's end on
+        # the queue: a graph replay) or not (a direct launch the host issued late)
+        disp = sorted(csv.DictReader(open(_find(a.src[0], "kernel_trace.csv"))),
+                      key=lambda r: (r["Queue_Id"], int(r["Start_Timestamp"])))
+        split = {}
+        prev_q, prev_end = None, None
+        for r in disp:
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            b2b = prev_q == r["Queue_Id"] and prev_end is not None and t0 <= prev_end
+            d = split.setdefault(r["Kernel_Name"], {True: [], False: []})
+            d[b2b].append((t1 - t0) / 1e3)
+            prev_q, prev_end = r["Queue_Id"], t1
         lines = [f"# Kernel trace: {a.workload}", "", "Command (from the repository root, on one MI355X):", "",
                  cmds, "",
                  "rocprofv3 kernel statistics.  In a run of back-to-back launches (graph replays) a",
                  "kernel's recorded start is the previous kernel's end, so each duration covers the",
-                 "kernel and the launch gap before it, and the durations tile the replayed steps.", "",
-                 "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+                 "kernel and the launch gap before it, and the durations tile the replayed steps.  The",
+                 "last two columns split the dispatches by that test: back to back (start = the previous",
+                 "dispatch's end on the queue) and the rest (launched directly, e.g. the per-kernel pass).", "",
+                 "| kernel | calls | avg us | min us | max us | share | avg us back to back (n) | avg us other (n) |",
+                 "|---|---|---|---|---|---|---|---|"]
+
+        def avg(v):
+            return f"{st.mean(v):.2f} ({len(v)})" if v else "-"
         for r in rows:
+            sp = split.get(r["Name"], {True: [], False: []})
             lines.append(f"| `{short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                         f"{100.0 * float(r['TotalDurationNs']) / total:.1f}% |")
+                         f"{100.0 * float(r['TotalDurationNs']) / total:.1f}% | {avg(sp[True])} | {avg(sp[False])} |")
         stem = a.name or f"kernel_trace_{a.workload}"
     elif a.what == "traffic":
         calf = _per_kernel_counter(a.cal_fetch, "FETCH_SIZE")

@@ -27,6 +27,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# extra flags of single sources: the matrix-core grouped kernels keep their
+# accumulators in VGPRs (the MFMA's VGPR form); with the default register
+# heuristics the compiler holds them in VGPRs across the item loop and copies
+# them to and from AGPRs around every K group, each copy waiting for the last
+# product to retire
+FILE_FLAGS = {"moe_mfma.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -45,7 +53,7 @@ def build(verbose=False, jobs=8):
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

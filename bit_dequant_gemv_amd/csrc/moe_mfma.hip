@@ -97,17 +97,21 @@ __device__ __forceinline__ void stage_load(MfmaStage& st, const uint8_t* const (
 }
 
 // acc[t] += the group's products; an invalid group (past the row's blocks,
-// or past this wave's share) adds exact zeros (zero codes, unit scale).
+// or past this wave's share) adds exact zeros (zero codes, unit scale).  Both
+// tiles are converted first and their products alternate, so no product
+// waits on the one issued just before it.
 __device__ __forceinline__ void stage_mma(f32x4_v (&acc)[2], const MfmaStage& st, bool valid) {
+  bf16x8_v b[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    bf16x8_v b[4];
     const uint4 q = valid ? st.q[t] : make_uint4(0u, 0u, 0u, 0u);
-    fp4_chunk_to_bf16(q, valid ? e8m0_to_f32(st.sc[t]) : 1.0f, b);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[j]), b[j], acc[t], 0, 0, 0);
+    fp4_chunk_to_bf16(q, valid ? e8m0_to_f32(st.sc[t]) : 1.0f, b[t]);
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.a[j]), b[t][j], acc[t], 0, 0, 0);
 }
 
 // The 4 waves' partial tiles of an item meet here; wave 0 adds them in wave
