@@ -117,7 +117,8 @@ KERNEL_KIND_PATTERNS = (          # kernel name fragment -> kind (per-launch tra
     ("moe_down_kernel", "down"), ("moe_dn_group_kernel", "down"), ("moe_route", "route"),
     ("moe_combine_kernel", "combine"), ("moe_gu_mfma_kernel", "gate_up"), ("moe_dn_mfma_kernel", "down"),
     ("qgemv_kernel", "qgemv"), ("attn_split_kernel", "attn_split"),
-    ("attn_merge_kernel", "attn_merge"), ("mx_gemm_kernel", "mx_gemm"), ("stream_copy_kernel", "copy"),
+    ("attn_merge_kernel", "attn_merge"), ("mx_gemm_kernel", "mx_gemm"), ("mxfp8_quant_kernel", "mx_quant"),
+    ("stream_copy_kernel", "copy"),
 )
 
 
@@ -268,9 +269,9 @@ def summarize(argv):
                      ("waiting (any) / wave-cycles", lambda m, wv, wc: f"{m.get('SQ_WAIT_ANY', 0) / wc:.2f}"),
                      ("waiting for issue / wave-cycles",
                       lambda m, wv, wc: f"{m.get('SQ_WAIT_INST_ANY', 0) / wc:.2f}")]
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in have and "GRBM_GUI_ACTIVE" in have:
-            cols += [("MFMA busy / (GUI-active cycles x 1024 SIMDs)",
-                      lambda m, wv, wc: f"{m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / max(m['GRBM_GUI_ACTIVE'] * 1024, 1):.3f}")]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in have:
+            cols += [("MFMA busy, M SIMD-cycles / dispatch",
+                      lambda m, wv, wc: f"{m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / 1e6:.2f}")]
         if "TA_BUSY_avr" in have and "GRBM_GUI_ACTIVE" in have:
             cols += [("TA busy / GUI-active cycles (mean TA)",
                       lambda m, wv, wc: f"{m.get('TA_BUSY_avr', 0) / max(m['GRBM_GUI_ACTIVE'], 1):.2f}")]
@@ -282,7 +283,9 @@ def summarize(argv):
                  "Counters averaged over the dispatches of the run (a counter pass serialises dispatches, so no",
                  "timing is taken from it).  The wave-cycle ratios divide counters that share a unit (summed over",
                  "all waves): SQ_ACTIVE_INST_VALU, SQ_WAIT_ANY and SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.  MFMA busy",
-                 "is SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE times the 1024 SIMDs; TA busy is the mean",
+                 "is SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs; divided by a launch's traced duration times",
+                 "2.4 GHz times the 1024 SIMDs it gives the matrix cores' share of the launch (a counter pass",
+                 "stretches the launches, so GRBM_GUI_ACTIVE is no clock for it).  TA busy is the mean",
                  "texture-address unit's busy cycles (TA_BUSY_avr) over GRBM_GUI_ACTIVE.", "",
                  "| kernel | " + " | ".join(c for c, _ in cols) + " |",
                  "|---|" + "---:|" * len(cols)]
