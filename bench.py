@@ -1319,7 +1319,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic(cfg.name, "layer" if fused else "gate_up") if m == cfg.m else None,
+            "traffic": (measured_traffic(cfg.name + ("_mfma" if args.mfma and m > 1 else ""),
+                                         "layer" if fused else "gate_up") if m == cfg.m else None),
             "traffic_algorithmic_bytes": dom_bytes,
             "duration_us": kernels["layer" if fused else "gate_up"]["share_us"],
             "gap_share_us": round(gap_us, 3),
