@@ -173,6 +173,7 @@ def summarize(argv):
     ap.add_argument("--note", default="", help="a paragraph of reading under the table")
     ap.add_argument("--name", default=None, help="output file stem (default: kind_workload)")
     ap.add_argument("--sources", default="moe", choices=["moe", "attn"])
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"), help="where the summary goes")
     a = ap.parse_args(argv)
     srcs = KERNEL_SOURCES if a.sources == "moe" else ATTN_SOURCES
     sha = kernel_sources_sha(srcs)
@@ -249,7 +250,7 @@ def summarize(argv):
                "per_launch": {k: {"fetch_bytes": v["fetch_bytes"], "write_bytes": v["write_bytes"]}
                               for k, v in per.items()}}
         stem = a.name or f"hbm_traffic_{a.workload}"
-        json.dump(rec, open(os.path.join(ROOT, "profiles", stem + ".json"), "w"), indent=1)
+        json.dump(rec, open(os.path.join(a.out_dir, stem + ".json"), "w"), indent=1)
     else:
         ctr = {}
         for src in a.src:
@@ -301,7 +302,7 @@ def summarize(argv):
     if a.note:
         lines += ["", a.note]
     lines += ["", f"Kernel sources sha256[:16]: `{sha}`", ""]
-    path = os.path.join(ROOT, "profiles", stem + ".md")
+    path = os.path.join(a.out_dir, stem + ".md")
     open(path, "w").write("\n".join(lines))
     print(path)
 
