@@ -90,6 +90,9 @@ def kernel_sources_sha(sources=KERNEL_SOURCES):
 
 
 ATTN_SOURCES = ("bit_dequant_gemv_amd/csrc/attn.hip", "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
+MX_SOURCES = ("bit_dequant_gemv_amd/csrc/mxgemm.hip", "bit_dequant_gemv_amd/csrc/router.hip",
+              "bit_dequant_gemv_amd/csrc/bdg_device.hpp")
+SOURCE_SETS = {"moe": KERNEL_SOURCES, "attn": ATTN_SOURCES, "mx": MX_SOURCES}
 
 
 def measured_traffic(workload, kernel, sources=KERNEL_SOURCES):
@@ -172,11 +175,10 @@ def summarize(argv):
     ap.add_argument("--command", action="append", default=[], help="the rocprofv3 command(s), for the record")
     ap.add_argument("--note", default="", help="a paragraph of reading under the table")
     ap.add_argument("--name", default=None, help="output file stem (default: kind_workload)")
-    ap.add_argument("--sources", default="moe", choices=["moe", "attn"])
+    ap.add_argument("--sources", default="moe", choices=sorted(SOURCE_SETS))
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"), help="where the summary goes")
     a = ap.parse_args(argv)
-    srcs = KERNEL_SOURCES if a.sources == "moe" else ATTN_SOURCES
-    sha = kernel_sources_sha(srcs)
+    sha = kernel_sources_sha(SOURCE_SETS[a.sources])
     cmds = "\n".join(f"    {c}" for c in a.command)
     if a.what == "trace":
         rows = list(csv.DictReader(open(_find(a.src[0], "kernel_stats.csv"))))
@@ -276,6 +278,11 @@ def summarize(argv):
         if "TA_BUSY_avr" in have and "GRBM_GUI_ACTIVE" in have:
             cols += [("TA busy / GUI-active cycles (mean TA)",
                       lambda m, wv, wc: f"{m.get('TA_BUSY_avr', 0) / max(m['GRBM_GUI_ACTIVE'], 1):.2f}")]
+        if "SQ_LDS_BANK_CONFLICT" in have and "SQ_ACTIVE_INST_LDS" in have:
+            cols += [("LDS bank-conflict cycles / LDS instr",
+                      lambda m, wv, wc: f"{m.get('SQ_LDS_BANK_CONFLICT', 0) / max(m['SQ_ACTIVE_INST_LDS'], 1):.2f}")]
+        if "SQ_WAIT_INST_LDS" in have and "SQ_WAVE_CYCLES" in have:
+            cols += [("waiting for LDS / wave-cycles", lambda m, wv, wc: f"{m.get('SQ_WAIT_INST_LDS', 0) / wc:.3f}")]
         if "GRBM_GUI_ACTIVE" in have:
             cols += [("GUI-active cycles / dispatch", lambda m, wv, wc: f"{m.get('GRBM_GUI_ACTIVE', 0):.0f}")]
         lines = [f"# SQ counters: {a.workload}", "",
@@ -674,7 +681,7 @@ def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
         "gemm_us": round(g_us, 3),
         "roofline": {"kernel": "mx_gemm_kernel", "bound": "mfma", "achieved": round(tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(cfg.name, "mx_gemm", MX_SOURCES) if m == cfg.m else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -729,7 +736,7 @@ def bench_prefill(torch, bdg, synth, sdev, dev, cfg, args):
         "layer_TFLOPs": round(tflops, 1),
         "roofline": {"kernel": "whole layer", "bound": "mfma", "achieved": round(tflops, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(cfg.name, "mx_gemm", MX_SOURCES) if m == cfg.m else None},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

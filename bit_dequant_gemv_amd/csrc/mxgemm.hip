@@ -112,97 +112,104 @@ constexpr int kNB = 1;              // 32-token MFMA tiles per wave
 constexpr int kBM = 64 * kNB;       // tokens per block
 constexpr int kBK = 128;            // K per stage: two 64-deep MFMA steps, four 32-blocks
 
-// LDS of one block: two stages of the A (weight) and B (activation) tiles,
-// each stored piece-major - piece q = 16 bytes of a row - so that a half-wave
-// reads 32 consecutive 16-byte slots.  Slots are XOR-swizzled (row ^ 4q for
-// A, token ^ 2q for B, both inside aligned groups of 16) so that the 16
-// lanes of a store pass - 4 pieces x 4 rows of A, 8 pieces x 2 tokens of B -
-// also land in 16 different slots.
-struct MxLds {
-  uint4 a[2][4][kBN];               // [stage][piece: 32-block of the stage][row]       32 KB
-  uint4 b[2][8][kBM];               // [stage][piece: 16 K of the stage][token]
-  uint8_t sa[2][4][kBN];            // [stage][32-block][row] E8M0
-  uint8_t sb[2][4][kBM];            // [stage][32-block][token] E8M0
+// The operands of one K stage are copied from global memory straight into
+// LDS (global_load_lds: each lane of a wave sends its 16 - or 4 - bytes to
+// the next slot of an LDS chunk, so nothing passes through VGPRs).  Three
+// stages form a ring: the copies run two stages ahead of the MFMAs.  Each
+// operand row is kept whole - A row r: its 4 pieces (32-blocks of the stage)
+// in 16-byte slots 4r .. 4r+3; B token t: its 8 pieces (16 K each) in slots
+// 8t .. 8t+7 - with the pieces XOR-permuted by the row, so that the 8 and
+// the 16 lanes of one LDS pass of the MFMA operand reads (one piece of 8 or
+// 16 consecutive rows) fall in distinct bank groups; the copy lanes fetch
+// the matching global pieces, so the permutation costs nothing.
+//
+// Scale bytes: a row's 4 E8M0 bytes of a stage sit at any byte offset, so
+// each row gets an 8-byte window of two aligned dwords, the first holding
+// its first byte of the stage and the second its last (the same dword when
+// all four share one): every dword read holds a needed byte, so no read
+// leaves the pages the scales are on.  The MFMA step picks its byte at
+// offset mis(row) + block from the window, mis = the row's misalignment.
+constexpr int kSlotsA = kBN * 4;                 // 16-byte slots of A per stage (16 KB)
+constexpr int kSlotsB = kBM * 8;                 // of B (8 KB)
+constexpr int kDmaA = kSlotsA / 64 / 4;          // A chunks per wave and stage
+constexpr int kDmaB = kSlotsB / 64 / 4;          // B chunks per wave and stage
+constexpr int kDmaSa = kBN * 2 / 64 / 4;         // A scale-window chunks (64 dwords) per wave
+constexpr int kDmaPerStage = kDmaA + kDmaB + kDmaSa + 1;   // + one B scale-window chunk
+
+__device__ __forceinline__ int a_slot(int r, int q) { return 4 * r + (q ^ (((r >> 1) ^ (r >> 3)) & 3)); }
+__device__ __forceinline__ int b_slot(int t, int p) { return 8 * t + (p ^ ((t ^ (t >> 3)) & 7)); }
+
+struct MxStageLds {                // one stage of the ring: one LDS object per stage
+  uint4 a[kSlotsA];
+  uint4 b[kSlotsB];
+  uint32_t saw[2 * kBN];           // A scale windows [block row][2]
+  uint32_t sbw[2 * kBM];           // B scale windows [token slot][2]
 };
 
-// Per-thread source rows, fixed for the whole K loop: the stage loads add
-// only the K offset.  A: load i of a stage reads 16 bytes (one 32-block) of
-// code row a[i]; B: load i reads 16 fp8 codes of activation row b[i]; sa /
-// sb are the scale rows of A row `tid` and of activation row `tid % kBM`
-// (byte offsets from the block-uniform bases).
-constexpr int kBL = kBM * 8 / kGemmThreads;   // B loads per thread per stage
+// Per-thread copy sources, fixed for the whole K loop (byte offsets from the
+// block-uniform bases): A copy i of a stage moves chunk kDmaA wave + i (rows
+// 16 c .. 16 c + 15), the lane taking piece qa[i] of row a[i]; B copy i
+// moves chunk kDmaB wave + i (tokens 8 c .. 8 c + 7), the lane taking piece
+// pb[i] of the token row at b[i].  Scale windows: A copy i fills dwords
+// 64 c .. 64 c + 63 (c = kDmaSa wave + i), the lane taking dword wa[i] & 1
+// of row wa[i] >> 1's window, whose scales start at sa[i]; the B copy fills
+// the 128 dwords of the 64 tokens (waves 2 and 3 copying what 0 and 1 do).
 struct MxRows {
-  const uint8_t* abase;             // block-uniform bases
+  const uint8_t* abase;
   const uint8_t* sabase;
   const uint8_t* bbase;
   const uint8_t* sbbase;
-  uint32_t a[4], b[kBL];            // per-thread byte offsets of the rows
-  uint32_t sa, sb;
+  uint32_t a[kDmaA], b[kDmaB];
+  uint32_t qa[kDmaA], pb[kDmaB];
+  uint32_t sa[kDmaSa], wa[kDmaSa];
+  uint32_t sb, wb;
 };
 
-// One stage's global loads for this thread.  All addresses are clamped in
-// bounds and nothing reads the loaded registers until the stage is stored to
-// LDS (a select on a loaded value would make the wave wait for it at once);
-// `valid` marks which pieces lie inside K, the others are stored as zeros.
-struct MxStage {
-  uint4 a[4], b[kBL];
-  uint32_t sa[4], sb[4];            // scale bytes of the stage's 4 32-blocks
-  uint32_t valid;                   // bit i: a[i] inside K; bit 4 + i: b[i] inside K
-};
+typedef __attribute__((address_space(3))) void mx_lds_void;
+typedef __attribute__((address_space(1))) const void mx_gbl_void;
 
-__device__ __forceinline__ void mx_stage_load(MxStage& st, const MxRows& rows, int K, int k0, int tid) {
-  const int kblocks = K >> 5;
-  const int kb0 = k0 >> 5;
-  uint32_t valid = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = i * kGemmThreads + tid;
-    const int kb = kb0 + (u & 3);                      // A: piece u % 4 of row u / 4
-    const int kbc = kb < kblocks ? kb : kblocks - 1;
-    st.a[i] = ldg_u128(rows.abase + rows.a[i] + (uint32_t)kbc * 16u);
-    valid |= (kb < kblocks ? 1u : 0u) << i;
-  }
-#pragma unroll
-  for (int i = 0; i < kBL; ++i) {
-    const int u = i * kGemmThreads + tid;
-    const int kp = k0 + 16 * (u & 7);                  // B: piece u % 8 of token u / 8
-    const int kpc = kp < K ? kp : K - 16;
-    st.b[i] = ldg_u128(rows.bbase + rows.b[i] + (uint32_t)kpc);
-    valid |= (kp < K ? 1u : 0u) << (4 + i);
-  }
-  st.valid = valid;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int kb = kb0 + q;
-    const int kbc = kb < kblocks ? kb : kblocks - 1;
-    st.sa[q] = ldg_u8(rows.sabase + rows.sa + (uint32_t)kbc);
-    st.sb[q] = ldg_u8(rows.sbbase + rows.sb + (uint32_t)kbc);
-  }
+// 16 (or 4) bytes per lane into the LDS chunk at `dst` (wave-uniform; lane
+// L's bytes land at dst + 16 L, or dst + 4 L)
+__device__ __forceinline__ void dma16_to_lds(const uint8_t* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((mx_gbl_void*)src, (mx_lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const uint8_t* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((mx_gbl_void*)src, (mx_lds_void*)dst, 4, 0, 0);
 }
 
-__device__ __forceinline__ void mx_stage_store(MxLds& l, int buf, const MxStage& st, int tid) {
+// the dword of a scale window: the row's scales start at `row` (from base);
+// the stage's needed bytes are kb0 .. min(kb0 + 3, kblocks - 1)
+__device__ __forceinline__ const uint8_t* scale_dword(const uint8_t* base, uint32_t row, int kb0, int kblocks,
+                                                      uint32_t half) {
+  const int first = min(kb0, kblocks - 1);
+  const int last = min(kb0 + 3, kblocks - 1);
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(base + row + (uint32_t)first) & ~(uintptr_t)3;
+  const uintptr_t w1 = reinterpret_cast<uintptr_t>(base + row + (uint32_t)last) & ~(uintptr_t)3;
+  return reinterpret_cast<const uint8_t*>(half ? w1 : w0);
+}
+
+// Stage s's copies into LDS: exactly kDmaPerStage copy instructions per
+// wave.  Pieces past K are clamped in bounds: their weight operands are
+// zeroed at the MFMA (the activation bytes there are copies of real ones, so
+// every such product is an exact zero).
+__device__ __forceinline__ void mx_stage_dma(MxStageLds& d, const MxRows& rows, int K, int s, int wave) {
+  const int kblocks = K >> 5;
+  const int kb0 = 4 * s;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = i * kGemmThreads + tid;
-    // component-wise selects (a select of whole structs can become a select
-    // of their addresses, which moves the stage to scratch memory)
-    const bool oka = (st.valid >> i) & 1u;
-    l.a[buf][u & 3][(u >> 2) ^ (4 * (u & 3))] = make_uint4(oka ? st.a[i].x : 0u, oka ? st.a[i].y : 0u,
-                                                           oka ? st.a[i].z : 0u, oka ? st.a[i].w : 0u);
+  for (int i = 0; i < kDmaA; ++i) {
+    const int kb = min(kb0 + (int)rows.qa[i], kblocks - 1);
+    dma16_to_lds(rows.abase + rows.a[i] + (uint32_t)kb * 16u, d.a + 64 * (kDmaA * wave + i));
   }
 #pragma unroll
-  for (int i = 0; i < kBL; ++i) {
-    const int u = i * kGemmThreads + tid;
-    const bool okb = (st.valid >> (4 + i)) & 1u;
-    l.b[buf][u & 7][(u >> 3) ^ (2 * (u & 7))] = make_uint4(okb ? st.b[i].x : 0u, okb ? st.b[i].y : 0u,
-                                                           okb ? st.b[i].z : 0u, okb ? st.b[i].w : 0u);
+  for (int i = 0; i < kDmaB; ++i) {
+    const int kp = min(kBK * s + 16 * (int)rows.pb[i], K - 16);
+    dma16_to_lds(rows.bbase + rows.b[i] + (uint32_t)kp, d.b + 64 * (kDmaB * wave + i));
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) l.sa[buf][q][tid] = (uint8_t)st.sa[q];
-  if (tid < kBM) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) l.sb[buf][q][tid] = (uint8_t)st.sb[q];
-  }
+  for (int i = 0; i < kDmaSa; ++i)
+    dma4_to_lds(scale_dword(rows.sabase, rows.sa[i], kb0, kblocks, rows.wa[i] & 1u),
+                  d.saw + 64 * (kDmaSa * wave + i));
+  dma4_to_lds(scale_dword(rows.sbbase, rows.sb, kb0, kblocks, rows.wb & 1u), d.sbw + 64 * (wave & 1));
 }
 
 // Tile t of the gx x gy block tiles (gx over weight rows, gy over tokens):
@@ -250,9 +257,9 @@ struct MxArgs {
 // Block tile of the 256 x 64 (weight rows x tokens) product, 4 waves: wave
 // w takes 128 weight rows (four 32-row MFMA tiles) and 32 tokens (one
 // 32-token tile): 4 MFMAs per 64-deep step, operands read from LDS.  The
-// next stage's global loads are in flight while the MFMAs run; the LDS holds
-// two stages.  About 200 VGPRs and 51 KB of LDS let two blocks share a CU,
-// so one block's MFMAs cover the other's barrier and LDS phases.
+// copies of the next two K stages are in flight while the MFMAs run (a ring
+// of three LDS stages, 76 KB); under 256 VGPRs and that LDS let two blocks
+// share a CU, so one block's MFMAs cover the other's barrier and LDS phases.
 //   kMxDense : y[m][n] = sum_k W[n][k] xq[m][k].
 //   kMxGateUp: block (token tile of expert e, 128 intermediate rows): A rows
 //              0..127 are gate rows i, 128..255 the up rows I + i, and each
@@ -263,7 +270,10 @@ struct MxArgs {
 //   kMxDown  : d[r][n] = sum_i Wd_e[n][i] hq[r][i] for the expert's grouped rows r.
 template <int MODE>
 __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
-  __shared__ MxLds l;
+  // three separate LDS objects, so that the compiler's wait tracking for
+  // the copies tells them apart: an access to one ring stage waits only for
+  // the copies into that stage
+  __shared__ MxStageLds R0, R1, R2;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -301,60 +311,53 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     n0 = (int64_t)tx * (MODE == kMxGateUp ? kBN / 2 : kBN);
   }
 
+  // operand rows of the block: A block row br (0..255) -> weight row;
+  // token slot t (0..63) -> activation row
+  auto a_row = [&](int br) -> int64_t {
+    if (MODE == kMxGateUp) {
+      int64_t ir = n0 + (br & 127);
+      ir = ir < p.I ? ir : p.I - 1;
+      return br < 128 ? ir : p.I + ir;
+    }
+    const int64_t row = n0 + br;
+    return row < p.N ? row : p.N - 1;
+  };
+  auto b_row = [&](int t) -> int64_t {
+    if (MODE == kMxDense) {
+      const int64_t src = m0 + t;
+      return src < p.M ? src : p.M - 1;
+    }
+    int gr = r0 + t;
+    gr = gr < r_end ? gr : r_end - 1;
+    return MODE == kMxGateUp ? p.row_src[gr] : gr;
+  };
   MxRows rows;
   rows.abase = wc;
   rows.sabase = ws;
   rows.bbase = p.xc;
   rows.sbbase = p.xs;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = i * kGemmThreads + tid;
-    const int br = u >> 2;                                   // block row of A load i
-    int64_t row;
-    if (MODE == kMxGateUp) {
-      int64_t ir = n0 + (br & 127);
-      ir = ir < p.I ? ir : p.I - 1;
-      row = br < 128 ? ir : p.I + ir;
-    } else {
-      row = n0 + br;
-      row = row < p.N ? row : p.N - 1;
-    }
-    rows.a[i] = (uint32_t)(row * (K >> 1));
-    if (i >= kBL) continue;
-    const int slot = u >> 3;                                 // token slot of B load i
-    int64_t src;
-    if (MODE == kMxDense) {
-      src = m0 + slot;
-      src = src < p.M ? src : p.M - 1;
-    } else {
-      int gr = r0 + slot;
-      gr = gr < r_end ? gr : r_end - 1;
-      src = MODE == kMxGateUp ? p.row_src[gr] : gr;
-    }
-    rows.b[i] = (uint32_t)(src * K);
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = 16 * (kDmaA * wave + i) + (lane >> 2);     // slot 64 c + lane = 4 r + (lane & 3)
+    rows.a[i] = (uint32_t)(a_row(r) * (K >> 1));
+    rows.qa[i] = (uint32_t)((lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3));
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int t = 8 * (kDmaB * wave + i) + (lane >> 3);      // slot 64 c + lane = 8 t + (lane & 7)
+    rows.b[i] = (uint32_t)(b_row(t) * K);
+    rows.pb[i] = (uint32_t)((lane & 7) ^ ((t ^ (t >> 3)) & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaSa; ++i) {
+    const int u = 64 * (kDmaSa * wave + i) + lane;           // window dword u: row u >> 1, dword u & 1
+    rows.wa[i] = (uint32_t)u;
+    rows.sa[i] = (uint32_t)(a_row(u >> 1) * kblocks);
   }
   {
-    int64_t row;
-    if (MODE == kMxGateUp) {
-      int64_t ir = n0 + (tid & 127);
-      ir = ir < p.I ? ir : p.I - 1;
-      row = tid < 128 ? ir : p.I + ir;
-    } else {
-      row = n0 + tid;
-      row = row < p.N ? row : p.N - 1;
-    }
-    rows.sa = (uint32_t)(row * kblocks);
-    const int slot = tid & (kBM - 1);
-    int64_t src;
-    if (MODE == kMxDense) {
-      src = m0 + slot;
-      src = src < p.M ? src : p.M - 1;
-    } else {
-      int gr = r0 + slot;
-      gr = gr < r_end ? gr : r_end - 1;
-      src = MODE == kMxGateUp ? p.row_src[gr] : gr;
-    }
-    rows.sb = (uint32_t)(src * kblocks);
+    const int u = (64 * wave + lane) & (2 * kBM - 1);
+    rows.wb = (uint32_t)u;
+    rows.sb = (uint32_t)(b_row(u >> 1) * kblocks);
   }
 
   // the wave's A tiles: block rows arow(a) + j; gate_up pairs tile a (gate)
@@ -363,6 +366,21 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   auto arow = [&](int a) {
     return MODE == kMxGateUp ? (a >> 1) * 128 + (wave & 1) * 64 + 32 * (a & 1) : (wave & 1) * 128 + 32 * a;
   };
+  // misalignment of the scale rows this lane reads at the MFMA (A tile a's
+  // row arow(a) + j, token wt + 32 b + j): where the stage's first byte sits
+  // in the window
+  uint32_t mis_a[4], mis_b[kNB];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    mis_a[a] = (uint32_t)(reinterpret_cast<uintptr_t>(ws) + (uintptr_t)(a_row(arow(a) + j) * kblocks)) & 3u;
+#pragma unroll
+  for (int b = 0; b < kNB; ++b)
+    mis_b[b] = (uint32_t)(reinterpret_cast<uintptr_t>(p.xs) + (uintptr_t)(b_row(wt + 32 * b + j) * kblocks)) & 3u;
+  // byte o of the window of row r
+  auto window_byte = [](const uint32_t* w, int r, uint32_t o) -> int {
+    return (int)((w[2 * r + (int)(o >> 2)] >> (8u * (o & 3u))) & 0xFFu);
+  };
+
   v16f acc[4][kNB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -371,29 +389,36 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  auto compute = [&](int buf) {
+  // stage s's MFMAs from LDS stage d.  TAIL: a last stage with kval < 4 of
+  // its 32-blocks inside K; the weights of the others are masked to zero
+  // (bitwise, so that no select turns into a branch around the LDS read).
+  auto compute = [&](const MxStageLds& d, int s, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;   // std::bool_constant
+    const int kval = kblocks - 4 * s;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      if (TAIL && ks == 1 && kval <= 2) break;         // block-uniform
       v8i A[4], B[kNB];
       int sa[4], sb[kNB];
       const int pa = 2 * ks + h;
+      const uint32_t keep = TAIL ? 0u - (uint32_t)(pa < kval) : ~0u;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int r = arow(a) + j;
-        const uint4 q = l.a[buf][pa][r ^ (4 * pa)];
-        A[a][0] = (int)q.x;
-        A[a][1] = (int)q.y;
-        A[a][2] = (int)q.z;
-        A[a][3] = (int)q.w;
+        const uint4 q = d.a[a_slot(r, pa)];
+        A[a][0] = (int)(q.x & keep);
+        A[a][1] = (int)(q.y & keep);
+        A[a][2] = (int)(q.z & keep);
+        A[a][3] = (int)(q.w & keep);
         A[a][4] = A[a][5] = A[a][6] = A[a][7] = 0;
-        sa[a] = l.sa[buf][pa][r];
+        sa[a] = window_byte(d.saw, r, mis_a[a] + (uint32_t)pa);
+        if (TAIL && pa >= kval) sa[a] = 127;            // past K: any finite scale (window byte unrelated)
       }
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
         const int t = wt + 32 * b + j;
-        const int plo = 4 * ks + h, phi = 4 * ks + 2 + h;
-        const uint4 lo = l.b[buf][plo][t ^ (2 * plo)];
-        const uint4 hi = l.b[buf][phi][t ^ (2 * phi)];
+        const uint4 lo = d.b[b_slot(t, 4 * ks + h)];
+        const uint4 hi = d.b[b_slot(t, 4 * ks + 2 + h)];
         B[b][0] = (int)lo.x;
         B[b][1] = (int)lo.y;
         B[b][2] = (int)lo.z;
@@ -402,7 +427,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
         B[b][5] = (int)hi.y;
         B[b][6] = (int)hi.z;
         B[b][7] = (int)hi.w;
-        sb[b] = l.sb[buf][2 * ks + h][t];
+        sb[b] = window_byte(d.sbw, t, mis_b[b] + (uint32_t)(2 * ks + h));
+        if (TAIL && 2 * ks + h >= kval) sb[b] = 127;
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -413,16 +439,52 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     }
   };
 
-  const int stages = (K + kBK - 1) / kBK;
-  MxStage st;
-  mx_stage_load(st, rows, K, 0, tid);
-  mx_stage_store(l, 0, st, tid);
-  __syncthreads();
-  for (int s = 0; s < stages; ++s) {
-    mx_stage_load(st, rows, K, (s + 1) * kBK, tid);   // past K: clamped, stored as zeros, unused
-    compute(s & 1);
-    mx_stage_store(l, (s + 1) & 1, st, tid);
-    __syncthreads();
+  // The ring: stage s lives in LDS stage s % 3.  Step s issues stage s + 2's
+  // copies, runs stage s's MFMAs, waits until all of this wave's copies but
+  // the last kDmaPerStage (stage s + 2's) have landed - the loop issues no
+  // other global loads, and copies complete in issue order, so stage s + 1
+  // has - and meets the block at an LDS-only barrier, which publishes every
+  // wave's stage s + 1.  Stage s + 2's copies stay in flight through the
+  // next step's MFMAs.  The loop runs the full stages; a last, partial
+  // stage is computed after it.  Stages past K are loaded clamped and never
+  // used; the exit waits for all copies.
+  constexpr int kWaitLastStage = 0x0F70 | (kDmaPerStage & 15) | ((kDmaPerStage >> 4) << 14);   // gfx9 vmcnt(n)
+  static_assert(kDmaPerStage < 64, "vmcnt holds 6 bits");
+  const int full = kblocks / 4;
+  auto issue = [&](MxStageLds& d, int s) {
+    __builtin_amdgcn_sched_barrier(0);
+    mx_stage_dma(d, rows, K, s, wave);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_for_all_but_last_stage = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLastStage);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto step = [&](int s, const MxStageLds& cur, MxStageLds& load) {
+    issue(load, s + 2);
+    compute(cur, s, std::false_type{});
+    wait_for_all_but_last_stage();
+    block_sync_lds();
+  };
+  issue(R0, 0);
+  issue(R1, 1);
+  wait_for_all_but_last_stage();
+  block_sync_lds();
+  // one exit from the loop: every path into its head then has the same
+  // copies in flight (those of stage s + 1), so the compiler adds no wait
+  int s0 = 0;
+  for (; s0 + 3 <= full; s0 += 3) {
+    step(s0 + 0, R0, R2);
+    step(s0 + 1, R1, R0);
+    step(s0 + 2, R2, R1);
+  }
+  if (s0 < full) step(s0, R0, R2);
+  if (s0 + 1 < full) step(s0 + 1, R1, R0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // gfx9 encoding: vmcnt(0)
+  if (4 * full < kblocks) {               // block-uniform: the partial last stage, published by the last barrier
+    const int r = full % 3;
+    compute(r == 0 ? R0 : (r == 1 ? R1 : R2), full, std::true_type{});
   }
 
   if (MODE == kMxGateUp) {
