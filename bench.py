@@ -121,6 +121,7 @@ KERNEL_KIND_PATTERNS = (          # kernel name fragment -> kind (per-launch tra
     ("moe_combine_kernel", "combine"), ("moe_gu_mfma_kernel", "gate_up"), ("moe_dn_mfma_kernel", "down"),
     ("qgemv_kernel", "qgemv"), ("attn_split_kernel", "attn_split"),
     ("attn_merge_kernel", "attn_merge"), ("mx_gemm_kernel", "mx_gemm"), ("mxfp8_quant_kernel", "mx_quant"),
+    ("mx_stage_scales_kernel", "mx_stage"),
     ("stream_copy_kernel", "copy"),
 )
 
@@ -620,11 +621,14 @@ def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
     calls = 16
     arrs = synth.dense_matrix(cfg, 0)
     qw = sdev.qweight_from_arrays(cfg.fmt, arrs, cfg.group, dev)
+    if not args.mx_scales_per_call:
+        qw.stage_mx_scales()          # weight layout, once per matrix (untimed, like the upload)
     _, xbits = synth.hidden_batch(cfg, range(m))
     x = torch.from_numpy(xbits.view(np.int16)).to(dev).view(torch.bfloat16)
     codes = torch.empty((m, cfg.k), dtype=torch.uint8, device=dev)
     scales = torch.empty((m, cfg.k // 32), dtype=torch.uint8, device=dev)
     y = torch.empty((m, cfg.n), dtype=torch.float32, device=dev)
+    ws = torch.empty(bdg.mx_gemm_workspace_bytes(cfg.n, cfg.k, m), dtype=torch.uint8, device=dev)
 
     def graph_time(fn):
         g = torch.cuda.CUDAGraph()
@@ -648,7 +652,7 @@ def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
         return a.elapsed_time(b) * 1e3 / (K * calls)
 
     q_us = graph_time(lambda: bdg.mxfp8_quantize(x, codes, scales))
-    g_us = graph_time(lambda: bdg.mx_gemm(qw, codes, scales, out=y))
+    g_us = graph_time(lambda: bdg.mx_gemm(qw, codes, scales, out=y, workspace=ws))
     if not torch.isfinite(y).all():
         raise SystemExit("non-finite output")
     flops = 2.0 * cfg.n * m * cfg.k
@@ -676,6 +680,7 @@ def bench_mx(torch, bdg, synth, sdev, dev, cfg, args):
         "ms_per_step": round(g_us * 1e-3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4 x mxfp8 -> f32", "data": "synthetic",
         "config": {"workload": cfg.name, "n": cfg.n, "k": cfg.k, "m": m,
+                   "weight_scale_words": "per call" if args.mx_scales_per_call else "staged once",
                    "timing": f"graphs of {calls} calls replayed; per call = kernel + node gap"},
         "quantize_us": round(q_us, 3), "quantize_GBps": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
         "gemm_us": round(g_us, 3),
@@ -696,6 +701,9 @@ def bench_prefill(torch, bdg, synth, sdev, dev, cfg, args):
     K = args.steps if args.steps is not None else 8
     W = args.warmup if args.warmup is not None else 2
     layer = sdev.upload_layer(cfg, 0, dev, threads=16)
+    if not args.mx_scales_per_call:   # weight layout, once per matrix (untimed, like the upload)
+        layer["gate_up"].stage_mx_scales()
+        layer["down"].stage_mx_scales()
     x, _ = sdev.hidden_device(cfg, range(m), dev)
     ws = torch.empty(bdg.prefill_workspace_bytes(m, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k),
                      dtype=torch.uint8, device=dev)
@@ -732,6 +740,7 @@ def bench_prefill(torch, bdg, synth, sdev, dev, cfg, args):
         "data": "synthetic",
         "config": {"workload": cfg.name, "m": m, "hidden": cfg.hidden, "inter": cfg.inter,
                    "experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "weight_scale_words": "per call" if args.mx_scales_per_call else "staged once",
                    "timing": "graph of one layer replayed; events around the replays"},
         "layer_TFLOPs": round(tflops, 1),
         "roofline": {"kernel": "whole layer", "bound": "mfma", "achieved": round(tflops, 1),
@@ -1105,6 +1114,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 8 at M=1, 4 at M>1)")
     ap.add_argument("--workload", default="gptoss20b_stack")
     ap.add_argument("--m", type=int, default=0, help="tokens per step (default: the workload's own)")
+    ap.add_argument("--mx-scales-per-call", action="store_true",
+                    help="MX workloads: let each call stage the weights' scale words (default: staged once)")
     ap.add_argument("--cpu-sample-layers", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true")

@@ -37,7 +37,9 @@ BDG_MAX_M = 16
 EXPORTED = (
     "mxfp4_dequant", "int4g_dequant", "qgemv", "moe_router_topk",
     "moe_plan_create", "moe_plan_destroy", "moe_plan_check", "moe_expert_decode", "moe_experts_routed",
-    "moe_expert_decode_profiled", "moe_expert_decode_timeline", "mxfp8_quantize", "mx_gemm", "moe_prefill_mx_workspace",
+    "moe_expert_decode_profiled", "moe_expert_decode_timeline", "mxfp8_quantize", "mx_scale_words_bytes",
+    "mx_stage_scales", "mx_gemm_workspace", "mx_gemm",
+    "moe_prefill_mx_workspace",
     "moe_prefill_mx", "attn_rope_table", "attn_decode_workspace", "attn_decode", "attn_decode_noalloc",
     "bdg_stream_read", "bdg_stream_copy", "bdg_strerror", "bdg_version",
 )
@@ -55,7 +57,7 @@ class QMat(ctypes.Structure):
         ("n", ctypes.c_int64), ("k", ctypes.c_int64),
         ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
         ("expert_stride_codes", ctypes.c_int64), ("expert_stride_scales", ctypes.c_int64),
-        ("expert_stride_zeros", ctypes.c_int64),
+        ("expert_stride_zeros", ctypes.c_int64), ("mx_scale_words", ctypes.c_void_p),
     ]
 
 
@@ -110,7 +112,10 @@ def load():
         "moe_expert_decode_profiled": [vp, vp, i32, i32, vp, vp, vp, vp],
         "moe_expert_decode_timeline": [vp, vp, i32, vp, vp, i64, vp],
         "mxfp8_quantize": [vp, i32, i64, i64, vp, vp, vp],
-        "mx_gemm": [ctypes.POINTER(QMat), vp, vp, i64, vp, vp],
+        "mx_scale_words_bytes": [ctypes.POINTER(QMat), i32],
+        "mx_stage_scales": [ctypes.POINTER(QMat), i32, vp, i64, vp],
+        "mx_gemm_workspace": [i64, i64, i64],
+        "mx_gemm": [ctypes.POINTER(QMat), vp, vp, i64, vp, vp, i64, vp],
         "moe_prefill_mx_workspace": [i64, i32, i32, i32, i32],
         "moe_prefill_mx": [ctypes.POINTER(LayerDesc), i32, i32, vp, i32, i64, vp, vp, vp, vp, i64, vp],
         "attn_rope_table": [ctypes.POINTER(Rope), i32, i64, vp, vp, vp, vp],
@@ -128,7 +133,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = (ctypes.c_char_p if name in ("bdg_strerror", "bdg_version")
-                      else ctypes.c_int64 if name in ("moe_prefill_mx_workspace", "attn_decode_workspace",
+                      else ctypes.c_int64 if name in ("moe_prefill_mx_workspace", "mx_gemm_workspace",
+                                                      "mx_scale_words_bytes", "attn_decode_workspace",
                                                       "moe_expert_decode_timeline")
                       else ctypes.c_int)
     _lib = lib

@@ -77,6 +77,25 @@ class QWeight:
         _dev_ptr(scales, "scales", torch.uint8 if fmt == "mxfp4" else torch.int16)
         if fmt == "int4g":
             _dev_ptr(zeros, "zeros", torch.uint8)
+        self.scale_words = None
+
+    def stage_mx_scales(self):
+        """Write the stage-major copy of the MXFP4 scales that the MX
+        matrix-core products read (mx_stage_scales; once per matrix, again
+        after the scales change); later qmat() views carry it."""
+        if self.fmt != "mxfp4":
+            raise ValueError("stage_mx_scales is for MXFP4 matrices")
+        self.scale_words = None
+        qm = self.qmat()
+        lib = _lib.load()
+        nbytes = lib.mx_scale_words_bytes(ctypes.byref(qm), self.n_experts)
+        if nbytes < 0:
+            raise ValueError("invalid matrix for mx_stage_scales")
+        words = torch.empty(nbytes // 4, dtype=torch.int32, device=self.codes.device)
+        check("mx_stage_scales", lib.mx_stage_scales(ctypes.byref(qm), self.n_experts,
+                                                     _dev_ptr(words, "scale_words", torch.int32), nbytes, _stream()))
+        self.scale_words = words
+        return self
 
     def qmat(self):
         def stride(t):
@@ -87,7 +106,8 @@ class QWeight:
             codes=self.codes.data_ptr(), scales=self.scales.data_ptr(),
             zeros=self.zeros.data_ptr() if self.zeros is not None else None,
             expert_stride_codes=stride(self.codes), expert_stride_scales=stride(self.scales),
-            expert_stride_zeros=stride(self.zeros))
+            expert_stride_zeros=stride(self.zeros),
+            mx_scale_words=self.scale_words.data_ptr() if self.scale_words is not None else None)
 
 
 def mxfp4_dequant(codes, scales, out_dtype=torch.float32):
@@ -153,19 +173,32 @@ def mxfp8_quantize(x, codes=None, scales=None):
     return codes, scales
 
 
-def mx_gemm(w: QWeight, codes, scales, out=None):
+def mx_gemm_workspace_bytes(n, k, m):
+    nb = _lib.load().mx_gemm_workspace(n, k, m)
+    if nb < 0:
+        raise ValueError("invalid mx_gemm shape")
+    return int(nb)
+
+
+def mx_gemm(w: QWeight, codes, scales, out=None, workspace=None):
     """y [m][n] = W xq^T for MXFP4 W [n][k] and MXFP8 activations (codes [m][k],
-    scales [m][k/32]) on the MX-scaled matrix cores."""
+    scales [m][k/32]) on the MX-scaled matrix cores.  workspace: a uint8
+    device tensor of mx_gemm_workspace_bytes(n, k, m) bytes or more (made
+    here when not given)."""
     m = codes.shape[0]
     if codes.dim() != 2 or codes.shape[1] != w.k or tuple(scales.shape) != (m, w.k // 32):
         raise ValueError("activation shapes do not match W")
     if out is not None:
         _shape(out, (m, w.n), "out")
     y = out if out is not None else torch.empty((m, w.n), dtype=torch.float32, device=codes.device)
+    if workspace is None:
+        workspace = torch.empty(mx_gemm_workspace_bytes(w.n, w.k, m), dtype=torch.uint8, device=codes.device)
     qm = w.qmat()
     check("mx_gemm", _lib.load().mx_gemm(ctypes.byref(qm), _dev_ptr(codes, "codes", torch.uint8),
                                          _dev_ptr(scales, "scales", torch.uint8), m,
-                                         _dev_ptr(y, "y", torch.float32), _stream()))
+                                         _dev_ptr(y, "y", torch.float32),
+                                         _dev_ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+                                         _stream()))
     return y
 
 
@@ -213,8 +246,11 @@ def moe_prefill_mx(layer, n_experts, top_k, x, y=None, workspace=None):
 
 def prefill_workspace_views(workspace, m, hidden, inter, n_experts, top_k):
     """Views of the parts of a moe_prefill_mx workspace (the layout include/bdg.h
-    states: 256-byte aligned parts in order).  For inspection only."""
+    states: 256-byte aligned parts in order), plus "hq_scales": h's scale
+    bytes as [P][I/32], arranged (a copy) from its stage-major words.  For
+    inspection only."""
     P = m * top_k
+    sh, si = (hidden // 32 + 3) // 4, (inter // 32 + 3) // 4
     sizes = [("xq", m * hidden, torch.uint8, (m, hidden)),
              ("xq_scales", m * (hidden // 32), torch.uint8, (m, hidden // 32)),
              ("row_off", 4 * (n_experts + 1), torch.int32, (n_experts + 1,)),
@@ -222,12 +258,16 @@ def prefill_workspace_views(workspace, m, hidden, inter, n_experts, top_k):
              ("row_src", 4 * P, torch.int32, (P,)),
              ("pick_row", 4 * P, torch.int32, (P,)),
              ("hq", P * inter, torch.uint8, (P, inter)),
-             ("hq_scales", P * (inter // 32), torch.uint8, (P, inter // 32)),
+             ("xq_scale_words", 4 * sh * P, torch.uint8, (sh, P, 4)),
+             ("hq_scale_words", 4 * si * P, torch.uint8, (si, P, 4)),
+             ("gate_up_scale_words", 4 * sh * 2 * inter * n_experts, torch.uint8, (n_experts, sh, 2 * inter, 4)),
+             ("down_scale_words", 4 * si * hidden * n_experts, torch.uint8, (n_experts, si, hidden, 4)),
              ("d", 4 * P * hidden, torch.float32, (P, hidden))]
     out, off = {}, 0
     for name, nbytes, dt, shape in sizes:
         out[name] = workspace[off:off + nbytes].view(dt).view(shape)
         off += (nbytes + 255) // 256 * 256
+    out["hq_scales"] = out["hq_scale_words"].permute(1, 0, 2).reshape(P, 4 * si)[:, :inter // 32]
     return out
 
 

@@ -121,20 +121,17 @@ constexpr int kBK = 128;            // K per stage: two 64-deep MFMA steps, four
 // 8t .. 8t+7 - with the pieces XOR-permuted by the row, so that the 8 and
 // the 16 lanes of one LDS pass of the MFMA operand reads (one piece of 8 or
 // 16 consecutive rows) fall in distinct bank groups; the copy lanes fetch
-// the matching global pieces, so the permutation costs nothing.
+// the matching global piece, so the permutation costs nothing.
 //
-// Scale bytes: a row's 4 E8M0 bytes of a stage sit at any byte offset, so
-// each row gets an 8-byte window of two aligned dwords, the first holding
-// its first byte of the stage and the second its last (the same dword when
-// all four share one): every dword read holds a needed byte, so no read
-// leaves the pages the scales are on.  The MFMA step picks its byte at
-// offset mis(row) + block from the window, mis = the row's misalignment.
+// Scale bytes come stage-major (mx_stage_scales_kernel): word [s][row]
+// holds the row's 4 E8M0 bytes of stage s (byte q = K block 4 s + q), so
+// one stage's scales of a block's 256 weight rows are 1 KB in a row - 8
+// cache lines - where the [row][K / 32] layout scatters them over ~180.
 constexpr int kSlotsA = kBN * 4;                 // 16-byte slots of A per stage (16 KB)
 constexpr int kSlotsB = kBM * 8;                 // of B (8 KB)
 constexpr int kDmaA = kSlotsA / 64 / 4;          // A chunks per wave and stage
 constexpr int kDmaB = kSlotsB / 64 / 4;          // B chunks per wave and stage
-constexpr int kDmaSa = kBN * 2 / 64 / 4;         // A scale-window chunks (64 dwords) per wave
-constexpr int kDmaPerStage = kDmaA + kDmaB + kDmaSa + 1;   // + one B scale-window chunk
+constexpr int kDmaPerStage = kDmaA + kDmaB + 2;  // + the A scale words (64 rows) and the B ones (64 tokens)
 
 __device__ __forceinline__ int a_slot(int r, int q) { return 4 * r + (q ^ (((r >> 1) ^ (r >> 3)) & 3)); }
 __device__ __forceinline__ int b_slot(int t, int p) { return 8 * t + (p ^ ((t ^ (t >> 3)) & 7)); }
@@ -142,27 +139,29 @@ __device__ __forceinline__ int b_slot(int t, int p) { return 8 * t + (p ^ ((t ^ 
 struct MxStageLds {                // one stage of the ring: one LDS object per stage
   uint4 a[kSlotsA];
   uint4 b[kSlotsB];
-  uint32_t saw[2 * kBN];           // A scale windows [block row][2]
-  uint32_t sbw[2 * kBM];           // B scale windows [token slot][2]
+  uint32_t saw[kBN];               // A scale words of the stage [block row]
+  uint32_t sbw[kBM];               // B scale words of the stage [token slot]
 };
 
 // Per-thread copy sources, fixed for the whole K loop (byte offsets from the
 // block-uniform bases): A copy i of a stage moves chunk kDmaA wave + i (rows
 // 16 c .. 16 c + 15), the lane taking piece qa[i] of row a[i]; B copy i
 // moves chunk kDmaB wave + i (tokens 8 c .. 8 c + 7), the lane taking piece
-// pb[i] of the token row at b[i].  Scale windows: A copy i fills dwords
-// 64 c .. 64 c + 63 (c = kDmaSa wave + i), the lane taking dword wa[i] & 1
-// of row wa[i] >> 1's window, whose scales start at sa[i]; the B copy fills
-// the 128 dwords of the 64 tokens (waves 2 and 3 copying what 0 and 1 do).
+// pb[i] of the token row at b[i].  Scale words: the A copy of wave w moves
+// block rows 64 w .. 64 w + 63, the lane's weight row being sa; every wave
+// copies the 64 tokens' words (the same bytes to the same slots), the
+// lane's scale row being sb.  wsm / xsm: stage 0 of the stage-major scale
+// words (the block's expert), wrows / xrows: rows per stage.
 struct MxRows {
   const uint8_t* abase;
-  const uint8_t* sabase;
   const uint8_t* bbase;
-  const uint8_t* sbbase;
+  const uint32_t* wsm;
+  const uint32_t* xsm;
   uint32_t a[kDmaA], b[kDmaB];
   uint32_t qa[kDmaA], pb[kDmaB];
-  uint32_t sa[kDmaSa], wa[kDmaSa];
-  uint32_t sb, wb;
+  uint32_t sa, sb;
+  uint32_t wrows, xrows;
+  int stages;
 };
 
 typedef __attribute__((address_space(3))) void mx_lds_void;
@@ -175,17 +174,6 @@ __device__ __forceinline__ void dma16_to_lds(const uint8_t* src, void* dst) {
 }
 __device__ __forceinline__ void dma4_to_lds(const uint8_t* src, void* dst) {
   __builtin_amdgcn_global_load_lds((mx_gbl_void*)src, (mx_lds_void*)dst, 4, 0, 0);
-}
-
-// the dword of a scale window: the row's scales start at `row` (from base);
-// the stage's needed bytes are kb0 .. min(kb0 + 3, kblocks - 1)
-__device__ __forceinline__ const uint8_t* scale_dword(const uint8_t* base, uint32_t row, int kb0, int kblocks,
-                                                      uint32_t half) {
-  const int first = min(kb0, kblocks - 1);
-  const int last = min(kb0 + 3, kblocks - 1);
-  const uintptr_t w0 = reinterpret_cast<uintptr_t>(base + row + (uint32_t)first) & ~(uintptr_t)3;
-  const uintptr_t w1 = reinterpret_cast<uintptr_t>(base + row + (uint32_t)last) & ~(uintptr_t)3;
-  return reinterpret_cast<const uint8_t*>(half ? w1 : w0);
 }
 
 // Stage s's copies into LDS: exactly kDmaPerStage copy instructions per
@@ -205,11 +193,9 @@ __device__ __forceinline__ void mx_stage_dma(MxStageLds& d, const MxRows& rows, 
     const int kp = min(kBK * s + 16 * (int)rows.pb[i], K - 16);
     dma16_to_lds(rows.bbase + rows.b[i] + (uint32_t)kp, d.b + 64 * (kDmaB * wave + i));
   }
-#pragma unroll
-  for (int i = 0; i < kDmaSa; ++i)
-    dma4_to_lds(scale_dword(rows.sabase, rows.sa[i], kb0, kblocks, rows.wa[i] & 1u),
-                  d.saw + 64 * (kDmaSa * wave + i));
-  dma4_to_lds(scale_dword(rows.sbbase, rows.sb, kb0, kblocks, rows.wb & 1u), d.sbw + 64 * (wave & 1));
+  const uint32_t sc = (uint32_t)min(s, rows.stages - 1);
+  dma4_to_lds(reinterpret_cast<const uint8_t*>(rows.wsm + sc * rows.wrows + rows.sa), d.saw + 64 * wave);
+  dma4_to_lds(reinterpret_cast<const uint8_t*>(rows.xsm + sc * rows.xrows + rows.sb), d.sbw);
 }
 
 // Tile t of the gx x gy block tiles (gx over weight rows, gy over tokens):
@@ -235,10 +221,11 @@ enum MxMode { kMxDense = 0, kMxGateUp = 1, kMxDown = 2 };
 
 struct MxArgs {
   const uint8_t* wc;                // weight codes (expert 0 in the grouped modes)
-  const uint8_t* ws;                // weight scales
-  int64_t stride_c, stride_s;       // bytes between experts
+  int64_t stride_c;                 // bytes between experts
+  const uint32_t* wsm;              // weight scale words, stage-major [E][stages][N]
   const uint8_t* xc;                // activation codes [rows][K]
-  const uint8_t* xs;                // activation scales [rows][K / 32]
+  const uint32_t* xsm;              // activation scale words [stages][xrows]
+  int64_t xrows;                    // rows of xsm per stage: dense M, grouped: the grouped rows
   int64_t N;                        // weight rows (dense, down); gate_up: 2 I
   int64_t M;                        // dense: tokens
   int K;
@@ -251,7 +238,7 @@ struct MxArgs {
   const int32_t* row_src;           // gate_up: activation row of each grouped row
   float* y;                         // dense [M][N]; down [grouped rows][N]
   uint8_t* hc;                      // gate_up: h codes [grouped rows][I]
-  uint8_t* hs;                      // gate_up: h scales [grouped rows][I / 32]
+  uint8_t* hs;                      // gate_up: h scale words, stage-major [I / 128][xrows], as bytes
 };
 
 // Block tile of the 256 x 64 (weight rows x tokens) product, 4 waves: wave
@@ -286,7 +273,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   int64_t n0 = 0, m0 = 0;
   int e = 0, r0 = 0, r_end = 0;
   const uint8_t* wc = p.wc;
-  const uint8_t* ws = p.ws;
+  const int stages_k = (kblocks + 3) / 4;
+  const uint32_t* wsm = p.wsm;
   if (MODE == kMxDense) {
     int tx, ty;
     if (!mx_tile_of_block(blockIdx.x, p.gx, p.gy, &tx, &ty)) return;   // block-uniform
@@ -307,12 +295,14 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     r0 = p.row_off[e] + (T - p.tile_off[e]) * kBM;
     r_end = p.row_off[e + 1];
     wc += (int64_t)e * p.stride_c;
-    ws += (int64_t)e * p.stride_s;
+    wsm += (int64_t)e * stages_k * p.N;
     n0 = (int64_t)tx * (MODE == kMxGateUp ? kBN / 2 : kBN);
   }
 
   // operand rows of the block: A block row br (0..255) -> weight row;
-  // token slot t (0..63) -> activation row
+  // token slot t (0..63) -> activation row (b_row), and the row of its scale
+  // words (b_srow: the grouped row in the grouped modes, whose scale words
+  // are gathered into grouped order beforehand)
   auto a_row = [&](int br) -> int64_t {
     if (MODE == kMxGateUp) {
       int64_t ir = n0 + (br & 127);
@@ -331,11 +321,19 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     gr = gr < r_end ? gr : r_end - 1;
     return MODE == kMxGateUp ? p.row_src[gr] : gr;
   };
+  auto b_srow = [&](int t) -> int64_t {
+    if (MODE == kMxDense) return b_row(t);
+    const int gr = r0 + t;
+    return gr < r_end ? gr : r_end - 1;
+  };
   MxRows rows;
   rows.abase = wc;
-  rows.sabase = ws;
   rows.bbase = p.xc;
-  rows.sbbase = p.xs;
+  rows.wsm = wsm;
+  rows.xsm = p.xsm;
+  rows.wrows = (uint32_t)p.N;
+  rows.xrows = (uint32_t)p.xrows;
+  rows.stages = stages_k;
 #pragma unroll
   for (int i = 0; i < kDmaA; ++i) {
     const int r = 16 * (kDmaA * wave + i) + (lane >> 2);     // slot 64 c + lane = 4 r + (lane & 3)
@@ -348,17 +346,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     rows.b[i] = (uint32_t)(b_row(t) * K);
     rows.pb[i] = (uint32_t)((lane & 7) ^ ((t ^ (t >> 3)) & 7));
   }
-#pragma unroll
-  for (int i = 0; i < kDmaSa; ++i) {
-    const int u = 64 * (kDmaSa * wave + i) + lane;           // window dword u: row u >> 1, dword u & 1
-    rows.wa[i] = (uint32_t)u;
-    rows.sa[i] = (uint32_t)(a_row(u >> 1) * kblocks);
-  }
-  {
-    const int u = (64 * wave + lane) & (2 * kBM - 1);
-    rows.wb = (uint32_t)u;
-    rows.sb = (uint32_t)(b_row(u >> 1) * kblocks);
-  }
+  rows.sa = (uint32_t)a_row(64 * wave + lane);
+  rows.sb = (uint32_t)b_srow(lane);
 
   // the wave's A tiles: block rows arow(a) + j; gate_up pairs tile a (gate)
   // with tile a + 2 (up) over the same intermediate rows
@@ -366,20 +355,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   auto arow = [&](int a) {
     return MODE == kMxGateUp ? (a >> 1) * 128 + (wave & 1) * 64 + 32 * (a & 1) : (wave & 1) * 128 + 32 * a;
   };
-  // misalignment of the scale rows this lane reads at the MFMA (A tile a's
-  // row arow(a) + j, token wt + 32 b + j): where the stage's first byte sits
-  // in the window
-  uint32_t mis_a[4], mis_b[kNB];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-    mis_a[a] = (uint32_t)(reinterpret_cast<uintptr_t>(ws) + (uintptr_t)(a_row(arow(a) + j) * kblocks)) & 3u;
-#pragma unroll
-  for (int b = 0; b < kNB; ++b)
-    mis_b[b] = (uint32_t)(reinterpret_cast<uintptr_t>(p.xs) + (uintptr_t)(b_row(wt + 32 * b + j) * kblocks)) & 3u;
-  // byte o of the window of row r
-  auto window_byte = [](const uint32_t* w, int r, uint32_t o) -> int {
-    return (int)((w[2 * r + (int)(o >> 2)] >> (8u * (o & 3u))) & 0xFFu);
-  };
+  // byte q of a scale word
+  auto word_byte = [](uint32_t w, int q) -> int { return (int)((w >> (8 * q)) & 0xFFu); };
 
   v16f acc[4][kNB];
 #pragma unroll
@@ -411,8 +388,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
         A[a][2] = (int)(q.z & keep);
         A[a][3] = (int)(q.w & keep);
         A[a][4] = A[a][5] = A[a][6] = A[a][7] = 0;
-        sa[a] = window_byte(d.saw, r, mis_a[a] + (uint32_t)pa);
-        if (TAIL && pa >= kval) sa[a] = 127;            // past K: any finite scale (window byte unrelated)
+        sa[a] = word_byte(d.saw[r], pa);
+        if (TAIL && pa >= kval) sa[a] = 127;            // past K: any finite scale (the byte is padding)
       }
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
@@ -427,7 +404,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
         B[b][5] = (int)hi.y;
         B[b][6] = (int)hi.z;
         B[b][7] = (int)hi.w;
-        sb[b] = window_byte(d.sbw, t, mis_b[b] + (uint32_t)(2 * ks + h));
+        sb[b] = word_byte(d.sbw[t], 2 * ks + h);
         if (TAIL && 2 * ks + h >= kval) sb[b] = 127;
       }
 #pragma unroll
@@ -523,7 +500,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
               word |= (bad ? 0x7Fu : f32_to_e4m3(hv[4 * g4 + q] * inv)) << (8 * q);
             *reinterpret_cast<uint32_t*>(hrow + i0 + 8 * g4 + 4 * h) = word;
           }
-          if (h == 0) p.hs[(int64_t)gr * (p.I >> 5) + (i0 >> 5)] = (uint8_t)(bad ? 255 : X + 127);
+          if (h == 0)   // byte (i0 / 32) % 4 of word [i0 / 128][gr]
+            p.hs[((i0 >> 7) * p.xrows + gr) * 4 + ((i0 >> 5) & 3)] = (uint8_t)(bad ? 255 : X + 127);
         }
       }
     }
@@ -559,6 +537,44 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
       }
     }
   }
+}
+
+// Stage-major scale words: dst[e][s][r] = the E8M0 bytes of K blocks
+// 4 s .. 4 s + 3 of source row src_row(r) of expert e, byte q = block 4 s + q
+// (blocks past K read 127); src_row(r) = gather[r] if given, else r.  One
+// thread per word; gridDim = (row blocks, stages, experts).
+constexpr int kStageThreads = 256;
+
+__global__ void __launch_bounds__(kStageThreads)
+mx_stage_scales_kernel(const uint8_t* __restrict__ src, int64_t src_stride_e, int kblocks, int64_t rows,
+                       const int32_t* __restrict__ gather, uint32_t* __restrict__ dst) {
+  const int64_t r = (int64_t)blockIdx.x * kStageThreads + threadIdx.x;
+  if (r >= rows) return;
+  const int s = blockIdx.y, e = blockIdx.z;
+  const int64_t sr = gather ? (int64_t)gather[r] : r;
+  const uint8_t* row = src + (int64_t)e * src_stride_e + sr * kblocks;
+  uint32_t w = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kb = 4 * s + q;
+    w |= (kb < kblocks ? (uint32_t)row[kb] : 127u) << (8 * q);
+  }
+  dst[((int64_t)e * gridDim.y + s) * rows + r] = w;
+}
+
+static int64_t a256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+static int64_t mx_stages(int64_t k) { return (k / 32 + 3) / 4; }
+
+// the stage-major copy of E experts' [rows][k / 32] scale bytes (gather: the
+// source row of each of the `rows` output rows, all < the source's rows)
+static int launch_stage_scales(const uint8_t* src, int64_t src_stride_e, int64_t k, int64_t rows,
+                               const int32_t* gather, int E, uint32_t* dst, hipStream_t s) {
+  const int64_t S = mx_stages(k);
+  const int64_t bx = (rows + kStageThreads - 1) / kStageThreads;
+  if (bx > 2147483647LL || S > 65535 || E > 65535) return BDG_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mx_stage_scales_kernel, dim3((unsigned)bx, (unsigned)S, (unsigned)E), dim3(kStageThreads), 0,
+                     s, src, src_stride_e, (int)(k / 32), rows, gather, dst);
+  return launch_status();
 }
 
 // Picks (t, j) of the M x K routing, grouped by expert: row_off / tile_off
@@ -642,13 +658,50 @@ extern "C" int mxfp8_quantize(const void* x, int32_t x_dtype, int64_t m, int64_t
   return launch_status();
 }
 
+extern "C" int64_t mx_scale_words_bytes(const bdg_qmat* w, int32_t n_experts) {
+  if (!w || w->fmt != BDG_FMT_MXFP4 || n_experts < 1 || w->n < 1 || w->k < 32 || (w->k % 32) != 0) return -1;
+  return 4 * (int64_t)n_experts * mx_stages(w->k) * w->n;
+}
+
+extern "C" int mx_stage_scales(const bdg_qmat* w, int32_t n_experts, void* out, int64_t out_bytes, void* stream) {
+  int st = check_qmat(w, n_experts > 1);
+  if (st != BDG_OK) return st;
+  if (w->fmt != BDG_FMT_MXFP4 || !out || n_experts < 1) return BDG_E_INVALID;
+  if (n_experts > 1 && w->expert_stride_scales == 0) return BDG_E_INVALID;
+  if (!aligned16(out)) return BDG_E_ALIGN;
+  if (out_bytes < mx_scale_words_bytes(w, n_experts)) return BDG_E_INVALID;
+  return launch_stage_scales(static_cast<const uint8_t*>(w->scales), w->expert_stride_scales, w->k, w->n, nullptr,
+                             n_experts, static_cast<uint32_t*>(out), as_stream(stream));
+}
+
+// the scale words of w for the MX products: its staged copy, else a fresh
+// one written into `dst`
+static int weight_scale_words(const bdg_qmat& w, int n_experts, uint32_t* dst, hipStream_t s,
+                              const uint32_t** words) {
+  if (w.mx_scale_words) {
+    if (!aligned16(w.mx_scale_words)) return BDG_E_ALIGN;
+    *words = static_cast<const uint32_t*>(w.mx_scale_words);
+    return BDG_OK;
+  }
+  *words = dst;
+  return launch_stage_scales(static_cast<const uint8_t*>(w.scales), w.expert_stride_scales, w.k, w.n, nullptr,
+                             n_experts, dst, s);
+}
+
+extern "C" int64_t mx_gemm_workspace(int64_t n, int64_t k, int64_t m) {
+  if (n < 1 || m < 1 || k < 32 || (k % 32) != 0) return -1;
+  const int64_t S = mx_stages(k);
+  return a256(4 * S * n) + a256(4 * S * m);
+}
+
 extern "C" int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, float* y,
-                       void* stream) {
+                       void* workspace, int64_t workspace_bytes, void* stream) {
   int st = check_qmat(w, false);
   if (st != BDG_OK) return st;
   if (w->fmt != BDG_FMT_MXFP4) return BDG_E_INVALID;
-  if (!x_codes || !x_scales || !y || m < 1) return BDG_E_INVALID;
-  if (!aligned16(x_codes)) return BDG_E_ALIGN;
+  if (!x_codes || !x_scales || !y || !workspace || m < 1) return BDG_E_INVALID;
+  if (!aligned16(x_codes) || !aligned16(workspace)) return BDG_E_ALIGN;
+  if (workspace_bytes < mx_gemm_workspace(w->n, w->k, m)) return BDG_E_INVALID;
   // operand rows are addressed by 32-bit byte offsets from the base pointers
   if (w->k > (int64_t)1 << 20 || w->n * (w->k / 2) >= ((int64_t)1 << 32) || m * w->k >= ((int64_t)1 << 32))
     return BDG_E_UNSUPPORTED;
@@ -656,33 +709,44 @@ extern "C" int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t*
   const int64_t gy = (m + kBM - 1) / kBM;
   if (gx * gy + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
   const int64_t blocks = (gx * gy + 7) / 8 * 8;     // whole chunks for the 8 XCDs
+  const int64_t S = mx_stages(w->k);
+  uint32_t* xsm = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + a256(4 * S * w->n));
+  hipStream_t s = as_stream(stream);
+  const uint32_t* wsm = nullptr;
+  st = weight_scale_words(*w, 1, static_cast<uint32_t*>(workspace), s, &wsm);
+  if (st) return st;
+  st = launch_stage_scales(x_scales, 0, w->k, m, nullptr, 1, xsm, s);
+  if (st) return st;
   MxArgs a{};
   a.wc = static_cast<const uint8_t*>(w->codes);
-  a.ws = static_cast<const uint8_t*>(w->scales);
+  a.wsm = wsm;
   a.xc = x_codes;
-  a.xs = x_scales;
+  a.xsm = xsm;
+  a.xrows = m;
   a.N = w->n;
   a.M = m;
   a.K = (int)w->k;
   a.gx = (int)gx;
   a.gy = (int)gy;
   a.y = y;
-  hipLaunchKernelGGL(mx_gemm_kernel<kMxDense>, dim3((unsigned)blocks), dim3(kGemmThreads), 0, as_stream(stream), a);
+  hipLaunchKernelGGL(mx_gemm_kernel<kMxDense>, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s, a);
   return launch_status();
 }
 
-// Workspace of moe_prefill_mx, in order: activation codes [m][H] and scales
-// [m][H/32], row_off / tile_off [E + 1] each, row_src / pick_row [m K] each,
-// h codes [m K][I] and scales [m K][I/32], down outputs [m K][H] fp32; each
-// part 256-byte aligned.
-static int64_t a256(int64_t x) { return (x + 255) & ~(int64_t)255; }
-
+// Workspace of moe_prefill_mx: x codes [m][H] and scales [m][H/32],
+// row_off / tile_off [E + 1] each, row_src / pick_row [m K] each, h codes
+// [m K][I], stage-major scale words of the grouped x [H/128][m K] and of h
+// [I/128][m K], of the gate_up weights [E][H/128][2 I] and of the down
+// weights [E][I/128][H], down outputs [m K][H] fp32; each region 256-byte
+// aligned.
 extern "C" int64_t moe_prefill_mx_workspace(int64_t m, int32_t hidden, int32_t inter, int32_t n_experts,
                                             int32_t top_k) {
   if (m < 1 || hidden < 32 || inter < 32 || n_experts < 1 || top_k < 1) return -1;
   const int64_t P = m * top_k;
+  const int64_t SH = mx_stages(hidden), SI = mx_stages(inter);
   return a256(m * hidden) + a256(m * (hidden / 32)) + 2 * a256(4 * (int64_t)(n_experts + 1)) + 2 * a256(4 * P) +
-         a256(P * inter) + a256(P * (inter / 32)) + a256(4 * P * hidden);
+         a256(P * inter) + a256(4 * SH * P) + a256(4 * SI * P) + a256(4 * SH * 2 * (int64_t)inter * n_experts) +
+         a256(4 * SI * (int64_t)hidden * n_experts) + a256(4 * P * hidden);
 }
 
 extern "C" int moe_router_topk(const void* x, int32_t x_dtype, const float* w_r, const float* b_r, int32_t m,
@@ -722,8 +786,12 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   int32_t* tile_off = reinterpret_cast<int32_t*>(wp);       wp += a256(4 * (int64_t)(n_experts + 1));
   int32_t* row_src = reinterpret_cast<int32_t*>(wp);        wp += a256(4 * P);
   int32_t* pick_row = reinterpret_cast<int32_t*>(wp);       wp += a256(4 * P);
+  const int64_t SH = mx_stages(H), SI = mx_stages(I);
   uint8_t* hq = reinterpret_cast<uint8_t*>(wp);             wp += a256(P * I);
-  uint8_t* hqs = reinterpret_cast<uint8_t*>(wp);            wp += a256(P * (I / 32));
+  uint32_t* xsm = reinterpret_cast<uint32_t*>(wp);          wp += a256(4 * SH * P);
+  uint32_t* hsm = reinterpret_cast<uint32_t*>(wp);          wp += a256(4 * SI * P);
+  uint32_t* gusm = reinterpret_cast<uint32_t*>(wp);         wp += a256(4 * SH * 2 * I * n_experts);
+  uint32_t* dnsm = reinterpret_cast<uint32_t*>(wp);         wp += a256(4 * SI * H * n_experts);
   float* d = reinterpret_cast<float*>(wp);
   hipStream_t s = as_stream(stream);
 
@@ -736,6 +804,15 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
                      n_experts, row_off, tile_off, row_src, pick_row);
   st = launch_status();
   if (st) return st;
+  // stage-major scale words: both weight matrices (unless staged already),
+  // and x's in grouped order
+  const uint32_t *gu_words = nullptr, *dn_words = nullptr;
+  st = weight_scale_words(gu, n_experts, gusm, s, &gu_words);
+  if (st) return st;
+  st = weight_scale_words(dn, n_experts, dnsm, s, &dn_words);
+  if (st) return st;
+  st = launch_stage_scales(xqs, 0, H, P, row_src, 1, xsm, s);
+  if (st) return st;
   // token tiles: at most one partial tile per expert beyond P / 128
   const int64_t tiles = (P + kBM - 1) / kBM + n_experts;
   MxArgs a{};
@@ -745,17 +822,17 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   a.row_src = row_src;
   // gate_up: 128 intermediate rows per block (their gate and up rows)
   a.wc = static_cast<const uint8_t*>(gu.codes);
-  a.ws = static_cast<const uint8_t*>(gu.scales);
+  a.wsm = gu_words;
   a.stride_c = gu.expert_stride_codes;
-  a.stride_s = gu.expert_stride_scales;
   a.xc = xq;
-  a.xs = xqs;
+  a.xsm = xsm;
+  a.xrows = P;
   a.N = 2 * I;
   a.K = (int)H;
   a.I = (int)I;
   a.gx = (int)((I + kBN / 2 - 1) / (kBN / 2));
   a.hc = hq;
-  a.hs = hqs;
+  a.hs = reinterpret_cast<uint8_t*>(hsm);
   a.gy = (int)tiles;
   if (tiles * a.gx + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
   hipLaunchKernelGGL(mx_gemm_kernel<kMxGateUp>, dim3((unsigned)((tiles * a.gx + 7) / 8 * 8)), dim3(kGemmThreads), 0,
@@ -768,11 +845,11 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   b.row_off = row_off;
   b.tile_off = tile_off;
   b.wc = static_cast<const uint8_t*>(dn.codes);
-  b.ws = static_cast<const uint8_t*>(dn.scales);
+  b.wsm = dn_words;
   b.stride_c = dn.expert_stride_codes;
-  b.stride_s = dn.expert_stride_scales;
   b.xc = hq;
-  b.xs = hqs;
+  b.xsm = hsm;
+  b.xrows = P;
   b.N = H;
   b.K = (int)I;
   b.gx = (int)((H + kBN - 1) / kBN);

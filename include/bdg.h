@@ -99,6 +99,12 @@ typedef struct bdg_qmat {
   int64_t expert_stride_codes;   /* bytes from expert e to e+1 (0 if single) */
   int64_t expert_stride_scales;
   int64_t expert_stride_zeros;
+  /* optional, MXFP4 only, for the MX matrix-core products (mx_gemm,
+   * moe_prefill_mx): device, 16-byte aligned, the stage-major copy of
+   * `scales` that mx_stage_scales writes ([E][k/128][n] 32-bit words).
+   * NULL: those calls stage a copy into their workspace on every call.
+   * The decode paths ignore it. */
+  const void* mx_scale_words;
 } bdg_qmat;
 
 /* mxfp4_dequant - decode an MXFP4 matrix to fp32 (or bf16).
@@ -283,24 +289,56 @@ int moe_experts_routed(bdg_plan* p, int32_t layer, const void* x, int32_t x_dtyp
 int mxfp8_quantize(const void* x, int32_t x_dtype, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
                    void* stream);
 
+/* mx_scale_words_bytes - bytes of the stage-major scale copy of n_experts
+ * MXFP4 matrices like w (n_experts * ceil(k/128) * n 32-bit words), -1 for
+ * invalid arguments. */
+int64_t mx_scale_words_bytes(const bdg_qmat* w, int32_t n_experts);
+
+/* mx_stage_scales - write the stage-major copy of the E8M0 scales of
+ * n_experts MXFP4 matrices (w->scales at w->expert_stride_scales) into out
+ * (device, 16-byte aligned, at least mx_scale_words_bytes(w, n_experts)
+ * bytes): word [e][s][r] = row r's bytes of K blocks 4s .. 4s+3 (byte q =
+ * block 4s + q, 127 past k).  One stage's scales of consecutive rows then
+ * sit in consecutive words - a block row range's scales of a K stage are
+ * one contiguous run for the MX products' copies to LDS, where the [n][k/32]
+ * layout spreads them over a cache line per row.  A weight-layout step,
+ * done once per matrix: point w->mx_scale_words at out afterwards (and
+ * stage again if the scales change). */
+int mx_stage_scales(const bdg_qmat* w, int32_t n_experts, void* out, int64_t out_bytes, void* stream);
+
+/* mx_gemm_workspace - bytes of device workspace mx_gemm needs for an n x k
+ * weight matrix and m tokens (-1 for invalid arguments): the stage-major
+ * copies of both operands' scale bytes, [k/128][n] and [k/128][m] 32-bit
+ * words (word [s][r] = row r's E8M0 bytes of K blocks 4s .. 4s+3), each
+ * part 256-byte aligned. */
+int64_t mx_gemm_workspace(int64_t n, int64_t k, int64_t m);
+
 /* mx_gemm - y[t][r] = sum_c W[r][c] * xq[t][c] for t < m: MXFP4 weights W
  * (bdg_qmat, BDG_FMT_MXFP4, PLAIN layout, expert strides ignored) times
  * MXFP8 activations (x_codes [m][k], x_scales [m][k/32] from
  * mxfp8_quantize; x_codes 16-byte aligned), on the MX-scaled MFMA with fp32
- * accumulation; y [m][n] fp32, device.  The instruction sums its products
- * at reduced internal precision, so results agree with the exact product to
- * about 1e-4 of sum |W||xq| (not bit for bit).  Any m >= 1, n >= 1 with
- * n * k / 2 and m * k below 2^32 (BDG_E_UNSUPPORTED beyond). */
+ * accumulation; y [m][n] fp32, device.  workspace: device, 16-byte
+ * aligned, at least mx_gemm_workspace(n, k, m) bytes, owned by the caller
+ * (the call allocates nothing; it rewrites the workspace, and stages w's
+ * scale words into it unless w->mx_scale_words is set).  The instruction
+ * sums its products at reduced internal precision, so results agree with
+ * the exact product to about 1e-4 of sum |W||xq| (not bit for bit).  Any
+ * m >= 1, n >= 1 with n * k / 2 and m * k below 2^32 (BDG_E_UNSUPPORTED
+ * beyond). */
 int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t* x_scales, int64_t m, float* y,
-            void* stream);
+            void* workspace, int64_t workspace_bytes, void* stream);
 
 /* moe_prefill_mx_workspace - bytes of device workspace moe_prefill_mx needs
  * for m tokens of a layer of the given shape (-1 for invalid arguments).
  * Layout (each part starting 256-byte aligned, in this order; P = m * top_k):
  * activation codes [m][H] and scales [m][H/32] (MXFP8), row_off and
  * tile_off [E+1] int32, row_src [P] int32 (token of each grouped row),
- * pick_row [P] int32 (grouped row of pick t*k + j), h codes [P][I] and
- * scales [P][I/32] (MXFP8), down outputs [P][H] fp32. */
+ * pick_row [P] int32 (grouped row of pick t*k + j), h codes [P][I] (MXFP8),
+ * then stage-major scale words (32-bit word [s][r] = row r's E8M0 bytes of
+ * K blocks 4s .. 4s+3, 127 past K): the grouped activations' [H/128][P],
+ * h's [I/128][P], the gate_up weights' [E][H/128][2I] and the down
+ * weights' [E][I/128][H] (divisions rounded up), then down outputs [P][H]
+ * fp32. */
 int64_t moe_prefill_mx_workspace(int64_t m, int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k);
 
 /* moe_prefill_mx - one bare MoE layer (no norm, no residual) over m tokens
@@ -315,7 +353,8 @@ int64_t moe_prefill_mx_workspace(int64_t m, int32_t hidden, int32_t inter, int32
  * w_router [E][H] fp32 (+ b_router); x [m][H] (BDG_F32 / BDG_BF16), y [m][H]
  * fp32, all device and 16-byte aligned; workspace: device memory of at least
  * moe_prefill_mx_workspace(...) bytes, owned by the caller (the call
- * allocates nothing).  Results agree with the exact MX arithmetic to about
+ * allocates nothing; a weight matrix whose mx_scale_words is set is not
+ * staged again).  Results agree with the exact MX arithmetic to about
  * 1e-3 of sum |W_d| |hq| (the matrix cores' reduced-precision sums, and the
  * rare rounding-boundary flips of hq that they cause). */
 int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, int32_t top_k, const void* x, int32_t x_dtype,

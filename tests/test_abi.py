@@ -103,6 +103,67 @@ def test_prefill_workspace_size_is_host_arithmetic():
     assert lib.moe_prefill_mx_workspace(0, 2880, 2880, 32, 4) == -1
 
 
+def test_mx_gemm_workspace_size():
+    """Two 256-byte aligned parts of stage-major scale words: [k/128][n] and
+    [k/128][m] (k/128 rounded up: K = 2880 is 90 blocks, 23 stages)."""
+    lib = _lib.load()
+    a256 = lambda b: (b + 255) // 256 * 256
+    assert lib.mx_gemm_workspace(5760, 2880, 4096) == a256(4 * 23 * 5760) + a256(4 * 23 * 4096)
+    assert lib.mx_gemm_workspace(1, 32, 1) == 2 * 256
+    assert lib.mx_gemm_workspace(5760, 2880, 0) == -1
+    assert lib.mx_gemm_workspace(5760, 48, 8) == -1
+
+
+def _fake_mx(n=256, k=256, **kw):
+    return _lib.QMat(fmt=_lib.BDG_FMT_MXFP4, group=32, n=n, k=k, codes=0x100000000, scales=0x200000000,
+                     zeros=None, expert_stride_codes=kw.get("sc", 0), expert_stride_scales=kw.get("ss", 0),
+                     expert_stride_zeros=0)
+
+
+def test_mx_scale_words_size_and_rejections():
+    """Stage-major scale words: E * ceil(k/128) * n 32-bit words; the staging
+    call rejects bad arguments before any launch (fake device addresses)."""
+    lib = _lib.load()
+    qm = _fake_mx(5760, 2880)
+    assert lib.mx_scale_words_bytes(ctypes.byref(qm), 32) == 4 * 32 * 23 * 5760
+    assert lib.mx_scale_words_bytes(ctypes.byref(_fake_mx(3, 32)), 1) == 4 * 3
+    assert lib.mx_scale_words_bytes(ctypes.byref(qm), 0) == -1
+    i4 = _lib.QMat(fmt=_lib.BDG_FMT_INT4G, group=64, n=256, k=256, codes=0x100000000, scales=0x200000000,
+                   zeros=0x300000000)
+    assert lib.mx_scale_words_bytes(ctypes.byref(i4), 1) == -1
+    need = lib.mx_scale_words_bytes(ctypes.byref(_fake_mx()), 1)
+    out = 0x700000000
+    assert lib.mx_stage_scales(ctypes.byref(i4), 1, out, 1 << 20, None) == _lib.BDG_E_INVALID
+    assert lib.mx_stage_scales(ctypes.byref(_fake_mx()), 1, None, need, None) == _lib.BDG_E_INVALID
+    assert lib.mx_stage_scales(ctypes.byref(_fake_mx()), 1, out, need - 1, None) == _lib.BDG_E_INVALID
+    assert lib.mx_stage_scales(ctypes.byref(_fake_mx()), 1, out + 4, need, None) == _lib.BDG_E_ALIGN
+    # several experts need their strides
+    assert lib.mx_stage_scales(ctypes.byref(_fake_mx()), 2, out, 2 * need, None) == _lib.BDG_E_INVALID
+
+
+def test_mx_gemm_rejects_misaligned_scale_words():
+    lib = _lib.load()
+    qm = _fake_mx()
+    qm.mx_scale_words = 0x800000004
+    need = lib.mx_gemm_workspace(256, 256, 64)
+    assert lib.mx_gemm(ctypes.byref(qm), 0x300000000, 0x400000000, 64, 0x500000000, 0x600000000, need,
+                       None) == _lib.BDG_E_ALIGN
+
+
+def test_mx_gemm_rejects_a_short_workspace():
+    """Fake device addresses, never dereferenced: the size check fails first."""
+    lib = _lib.load()
+    qm = _lib.QMat(fmt=_lib.BDG_FMT_MXFP4, group=32, n=256, k=256, codes=0x100000000, scales=0x200000000,
+                   zeros=None, expert_stride_codes=0, expert_stride_scales=0, expert_stride_zeros=0)
+    need = lib.mx_gemm_workspace(256, 256, 64)
+    args = (ctypes.byref(qm), 0x300000000, 0x400000000, 64, 0x500000000, 0x600000000)
+    assert lib.mx_gemm(*args, need - 1, None) == _lib.BDG_E_INVALID
+    assert lib.mx_gemm(ctypes.byref(qm), 0x300000000, 0x400000000, 64, 0x500000000, None, need, None) == \
+        _lib.BDG_E_INVALID
+    assert lib.mx_gemm(ctypes.byref(qm), 0x300000000, 0x400000000, 64, 0x500000000, 0x600000008, need, None) == \
+        _lib.BDG_E_ALIGN
+
+
 @pytest.mark.parametrize("name", ["mxfp4_dequant", "qgemv", "moe_router_topk", "mx_gemm"])
 def test_null_arguments_are_rejected(name):
     lib = _lib.load()

@@ -194,6 +194,48 @@ def test_mx_rejects_bad_args(dev):
                                       None) == _lib.BDG_E_INVALID   # and so does the library
 
 
+@pytest.mark.parametrize("E,n,k", [(1, 37, 96), (3, 70, 2880), (2, 256, 4096)])
+def test_mx_stage_scales_layout(dev, E, n, k):
+    """mx_stage_scales against its layout written out: word [e][s][r] holds
+    row r's scale bytes of K blocks 4s .. 4s+3 (byte q = block 4s + q), 127
+    past K (K = 96: 3 blocks, one padded byte; 2880: 90 blocks, two)."""
+    rng = np.random.default_rng(E * 1000 + n + k)
+    kb, S = k // 32, (k // 32 + 3) // 4
+    sc = rng.integers(0, 256, (E, n, kb), dtype=np.uint8)
+    codes = np.zeros((E, n, k // 2), dtype=np.uint8)
+    if E == 1:
+        w = bdg.QWeight("mxfp4", dev_t(codes[0], dev), dev_t(sc[0], dev))
+    else:
+        w = bdg.QWeight("mxfp4", dev_t(codes, dev), dev_t(sc, dev))
+    w.stage_mx_scales()
+    got = to_np(w.scale_words).view(np.uint8).reshape(E, S, n, 4)
+    want = np.full((E, S, n, 4), 127, dtype=np.uint8)
+    for s_ in range(S):
+        for q in range(4):
+            if 4 * s_ + q < kb:
+                want[:, s_, :, q] = sc[:, :, 4 * s_ + q]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("n,m,k", [(33, 5, 96), (100, 37, 2880), (257, 70, 4096)])
+def test_mx_gemm_staged_scale_words(dev, n, m, k):
+    """Weights with their stage-major scale copy staged once give the same
+    product, bit for bit, as the per-call staging (and the oracle's)."""
+    rng = np.random.default_rng(n * 13 + m * 5 + k)
+    wc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    ws = rng.integers(118, 129, (n, k // 32), dtype=np.uint8)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    c, s = quantize_dev(x, dev)
+    w = mx_weight(wc, ws, dev)
+    y0 = bdg.mx_gemm(w, dev_t(c, dev), dev_t(s, dev)).clone()
+    w.stage_mx_scales()
+    banner(f"mx_gemm with staged scale words n={n} m={m} k={k}")
+    y1 = bdg.mx_gemm(w, dev_t(c, dev), dev_t(s, dev))
+    assert torch.equal(y0, y1)
+    yref, den = mxq.mx_gemm(wc, ws, c, s)
+    check_gemm(to_np(y1), yref, den, f"mx_gemm staged {n}x{k} m={m}")
+
+
 # ---------------------------------------------------------------- grouped prefill layer
 
 # Checking the layer.  h is computed on the matrix cores (sums at reduced
@@ -228,15 +270,20 @@ def _h_error_bound(gu, gd, inter):
     return d1 * np.abs(u) * dg + np.abs(g * sig) * du + 0.5 * np.abs(u) * dg * dg + 1.1 * dg * du
 
 
-def _prefill_case(dev, name, E, k, H, I, m, base, sample=None):
+def _prefill_case(dev, name, E, k, H, I, m, base, sample=None, staged=False):
     """sample: check the h codes and outputs of this many seeded tokens
-    (routing, weights and grouping of every token are always checked)."""
+    (routing, weights and grouping of every token are always checked).
+    staged: the weights' stage-major scale words made once beforehand (as
+    the benchmark does) instead of by the call."""
     from oracle import formats, moe as omoe
     cfg = synth.MoEConfig(name=name, base=base, fmt="mxfp4", n_layers=1, hidden=H, inter=I, n_experts=E,
                           top_k=k, norm=False, m=m)
     layer = sdev.upload_layer(cfg, 0, dev)
+    if staged:
+        layer["gate_up"].stage_mx_scales()
+        layer["down"].stage_mx_scales()
     x, xv = sdev.hidden_device(cfg, range(m), dev)
-    banner(f"moe_prefill_mx {name} E={E} k={k} H={H} I={I} m={m}")
+    banner(f"moe_prefill_mx {name} E={E} k={k} H={H} I={I} m={m}{' staged scale words' if staged else ''}")
     ws = torch.empty(bdg.prefill_workspace_bytes(m, H, I, E, k), dtype=torch.uint8, device=dev)
     y, idx, wts = bdg.moe_prefill_mx(layer, E, k, x, workspace=ws)
     torch.cuda.synchronize()
@@ -328,17 +375,38 @@ def test_moe_prefill_heavy_sharing(dev):
 
 
 def test_moe_prefill_gptoss_layer(dev):
-    """The gpt-oss-20B layer shape (32 experts, top-4, 2880 x 2880) over 512 tokens."""
-    _prefill_case(dev, "prefill_20b", 32, 4, 2880, 2880, 512, 2300)
+    """The gpt-oss-20B layer shape (32 experts, top-4, 2880 x 2880) over 512
+    tokens, the weights' scale words staged once."""
+    _prefill_case(dev, "prefill_20b", 32, 4, 2880, 2880, 512, 2300, staged=True)
 
 
 def test_moe_prefill_benchmark_size(dev):
     """The benchmarked prefill workload at full size: the bare gpt-oss-20B
-    layer over 4096 tokens, in the launch configuration the benchmark times.
-    Routing, weights and grouping of all 4096 tokens; h codes and outputs of
-    384 sampled tokens."""
+    layer over 4096 tokens, in the launch configuration the benchmark times
+    (the weights' scale words staged once).  Routing, weights and grouping of
+    all 4096 tokens; h codes and outputs of 384 sampled tokens."""
     pc = synth.PREFILL["gptoss20b_prefill"]
-    _prefill_case(dev, "prefill_20b_4096", 32, 4, 2880, 2880, pc.m, pc.base, sample=384)
+    _prefill_case(dev, "prefill_20b_4096", 32, 4, 2880, 2880, pc.m, pc.base, sample=384, staged=True)
+
+
+def test_moe_prefill_staged_scale_words_bit_identical(dev):
+    """The same layer with its weights' scale words staged once and staged by
+    the call: identical outputs, routing weights and picks (H = 320 and
+    I = 224 leave the last K stage of both products partial)."""
+    cfg = synth.MoEConfig(name="pf_staged", base=2400, fmt="mxfp4", n_layers=1, hidden=320, inter=224,
+                          n_experts=8, top_k=2, norm=False, m=150)
+    layer = sdev.upload_layer(cfg, 0, dev)
+    x, _ = sdev.hidden_device(cfg, range(cfg.m), dev)
+    ws = torch.empty(bdg.prefill_workspace_bytes(cfg.m, 320, 224, 8, 2), dtype=torch.uint8, device=dev)
+    banner("moe_prefill_mx staged vs per-call scale words")
+    out0 = [t.clone() for t in bdg.moe_prefill_mx(layer, 8, 2, x, workspace=ws)]
+    layer["gate_up"].stage_mx_scales()
+    layer["down"].stage_mx_scales()
+    out1 = bdg.moe_prefill_mx(layer, 8, 2, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out1[0]).all()
+    for a, b in zip(out0, out1):
+        assert torch.equal(a, b)
 
 
 def test_moe_prefill_rejects_bad_args(dev):
