@@ -106,11 +106,11 @@ mxfp8_quant_kernel(const void* __restrict__ x, int x_bf16, int64_t n_elems, uint
   }
 }
 
-constexpr int kGemmThreads = 256;   // 4 waves
-constexpr int kBN = 256;            // weight rows per block (128 per wave)
-constexpr int kNB = 1;              // 32-token MFMA tiles per wave
-constexpr int kBM = 64 * kNB;       // tokens per block
+constexpr int kBN = 256;            // weight rows per block
 constexpr int kBK = 128;            // K per stage: two 64-deep MFMA steps, four 32-blocks
+constexpr int kTA = 2;              // 32-row MFMA tiles per wave
+constexpr int kRowGroups = kBN / (32 * kTA);   // 4 waves along the rows
+constexpr int kNB = 1;              // 32-token MFMA tiles per wave
 
 // The operands of one K stage are copied from global memory straight into
 // LDS (global_load_lds: each lane of a wave sends its 16 - or 4 - bytes to
@@ -127,38 +127,53 @@ constexpr int kBK = 128;            // K per stage: two 64-deep MFMA steps, four
 // holds the row's 4 E8M0 bytes of stage s (byte q = K block 4 s + q), so
 // one stage's scales of a block's 256 weight rows are 1 KB in a row - 8
 // cache lines - where the [row][K / 32] layout scatters them over ~180.
-constexpr int kSlotsA = kBN * 4;                 // 16-byte slots of A per stage (16 KB)
-constexpr int kSlotsB = kBM * 8;                 // of B (8 KB)
-constexpr int kDmaA = kSlotsA / 64 / 4;          // A chunks per wave and stage
-constexpr int kDmaB = kSlotsB / 64 / 4;          // B chunks per wave and stage
-constexpr int kDmaPerStage = kDmaA + kDmaB + 2;  // + the A scale words (64 rows) and the B ones (64 tokens)
+//
+// Block shapes, by TM = tokens per block: 64 (8 waves, 4 row groups x 2
+// token groups, a 76 KB ring: two blocks share a CU) or 128 (16 waves, a
+// 100 KB ring: one block per CU, half the weight bytes per product).  A
+// wave holds kTA = 2 row tiles and one token tile, so either shape runs 4
+// waves per SIMD in under 128 VGPRs.
+template <int TM>
+struct MxShape {
+  static_assert(TM == 64 || TM == 128, "64 or 128 tokens per block");
+  static constexpr int kBM = TM;
+  static constexpr int kWaves = kRowGroups * TM / 32;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kSlotsA = kBN * 4;              // 16-byte slots of A per stage (16 KB)
+  static constexpr int kSlotsB = TM * 8;               // of B (8 or 16 KB)
+  static constexpr int kDmaA = kSlotsA / 64 / kWaves;  // A chunks per wave and stage (2 or 1)
+  static constexpr int kDmaB = kSlotsB / 64 / kWaves;  // B chunks per wave and stage (1)
+  static constexpr int kDmaPerStage = kDmaA + kDmaB + 1;   // + one chunk of scale words
+};
 
 __device__ __forceinline__ int a_slot(int r, int q) { return 4 * r + (q ^ (((r >> 1) ^ (r >> 3)) & 3)); }
 __device__ __forceinline__ int b_slot(int t, int p) { return 8 * t + (p ^ ((t ^ (t >> 3)) & 7)); }
 
+template <int TM>
 struct MxStageLds {                // one stage of the ring: one LDS object per stage
-  uint4 a[kSlotsA];
-  uint4 b[kSlotsB];
+  uint4 a[MxShape<TM>::kSlotsA];
+  uint4 b[MxShape<TM>::kSlotsB];
   uint32_t saw[kBN];               // A scale words of the stage [block row]
-  uint32_t sbw[kBM];               // B scale words of the stage [token slot]
+  uint32_t sbw[TM];                // B scale words of the stage [token slot]
 };
 
 // Per-thread copy sources, fixed for the whole K loop (byte offsets from the
 // block-uniform bases): A copy i of a stage moves chunk kDmaA wave + i (rows
 // 16 c .. 16 c + 15), the lane taking piece qa[i] of row a[i]; B copy i
 // moves chunk kDmaB wave + i (tokens 8 c .. 8 c + 7), the lane taking piece
-// pb[i] of the token row at b[i].  Scale words: the A copy of wave w moves
-// block rows 64 w .. 64 w + 63, the lane's weight row being sa; every wave
-// copies the 64 tokens' words (the same bytes to the same slots), the
-// lane's scale row being sb.  wsm / xsm: stage 0 of the stage-major scale
-// words (the block's expert), wrows / xrows: rows per stage.
+// pb[i] of the token row at b[i].  Scale words: waves 0-3 copy the words of
+// block rows 64 w .. 64 w + 63 (the lane's weight row: sa), the other waves
+// those of 64 tokens each (the lane's scale row: sb), several waves copying
+// the same bytes to the same slots.  wsm / xsm: stage 0 of the stage-major
+// scale words (the block's expert), wrows / xrows: rows per stage.
+template <int TM>
 struct MxRows {
   const uint8_t* abase;
   const uint8_t* bbase;
   const uint32_t* wsm;
   const uint32_t* xsm;
-  uint32_t a[kDmaA], b[kDmaB];
-  uint32_t qa[kDmaA], pb[kDmaB];
+  uint32_t a[MxShape<TM>::kDmaA], b[MxShape<TM>::kDmaB];
+  uint32_t qa[MxShape<TM>::kDmaA], pb[MxShape<TM>::kDmaB];
   uint32_t sa, sb;
   uint32_t wrows, xrows;
   int stages;
@@ -180,22 +195,29 @@ __device__ __forceinline__ void dma4_to_lds(const uint8_t* src, void* dst) {
 // wave.  Pieces past K are clamped in bounds: their weight operands are
 // zeroed at the MFMA (the activation bytes there are copies of real ones, so
 // every such product is an exact zero).
-__device__ __forceinline__ void mx_stage_dma(MxStageLds& d, const MxRows& rows, int K, int s, int wave) {
+template <int TM>
+__device__ __forceinline__ void mx_stage_dma(MxStageLds<TM>& d, const MxRows<TM>& rows, int K, int s, int wave) {
+  using S = MxShape<TM>;
   const int kblocks = K >> 5;
   const int kb0 = 4 * s;
 #pragma unroll
-  for (int i = 0; i < kDmaA; ++i) {
+  for (int i = 0; i < S::kDmaA; ++i) {
     const int kb = min(kb0 + (int)rows.qa[i], kblocks - 1);
-    dma16_to_lds(rows.abase + rows.a[i] + (uint32_t)kb * 16u, d.a + 64 * (kDmaA * wave + i));
+    dma16_to_lds(rows.abase + rows.a[i] + (uint32_t)kb * 16u, d.a + 64 * (S::kDmaA * wave + i));
   }
 #pragma unroll
-  for (int i = 0; i < kDmaB; ++i) {
+  for (int i = 0; i < S::kDmaB; ++i) {
     const int kp = min(kBK * s + 16 * (int)rows.pb[i], K - 16);
-    dma16_to_lds(rows.bbase + rows.b[i] + (uint32_t)kp, d.b + 64 * (kDmaB * wave + i));
+    dma16_to_lds(rows.bbase + rows.b[i] + (uint32_t)kp, d.b + 64 * (S::kDmaB * wave + i));
   }
+  // scale words: waves 0-3 one chunk of 64 weight rows each, the others one
+  // chunk of 64 tokens (chunk (wave + 4) % (TM / 64))
   const uint32_t sc = (uint32_t)min(s, rows.stages - 1);
-  dma4_to_lds(reinterpret_cast<const uint8_t*>(rows.wsm + sc * rows.wrows + rows.sa), d.saw + 64 * wave);
-  dma4_to_lds(reinterpret_cast<const uint8_t*>(rows.xsm + sc * rows.xrows + rows.sb), d.sbw);
+  const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(rows.wsm + sc * rows.wrows + rows.sa);
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(rows.xsm + sc * rows.xrows + rows.sb);
+  const bool rows_chunk = wave < 4;                    // wave-uniform
+  dma4_to_lds(rows_chunk ? wsrc : xsrc,
+              rows_chunk ? d.saw + 64 * wave : d.sbw + 64 * ((wave + 4) % (TM / 64)));
 }
 
 // Tile t of the gx x gy block tiles (gx over weight rows, gy over tokens):
@@ -241,26 +263,27 @@ struct MxArgs {
   uint8_t* hs;                      // gate_up: h scale words, stage-major [I / 128][xrows], as bytes
 };
 
-// Block tile of the 256 x 64 (weight rows x tokens) product, 4 waves: wave
-// w takes 128 weight rows (four 32-row MFMA tiles) and 32 tokens (one
-// 32-token tile): 4 MFMAs per 64-deep step, operands read from LDS.  The
-// copies of the next two K stages are in flight while the MFMAs run (a ring
-// of three LDS stages, 76 KB); under 256 VGPRs and that LDS let two blocks
-// share a CU, so one block's MFMAs cover the other's barrier and LDS phases.
+// Block tile of the 256 x TM (weight rows x tokens) product (MxShape): wave
+// (row group rg, token group) takes 64 weight rows (two 32-row MFMA tiles)
+// and 32 tokens (one 32-token tile): 2 MFMAs per 64-deep step, operands
+// read from LDS.  The copies of the next two K stages are in flight while
+// the MFMAs run (a ring of three LDS stages).  Four waves per SIMD, from one
+// or two blocks, cover each other's LDS reads and barrier waits.
 //   kMxDense : y[m][n] = sum_k W[n][k] xq[m][k].
 //   kMxGateUp: block (token tile of expert e, 128 intermediate rows): A rows
 //              0..127 are gate rows i, 128..255 the up rows I + i, and each
-//              wave holds the gate and up sums of the same 64 rows, so
+//              wave holds the gate and up sums of the same 32 rows, so
 //              h = silu(g) * u is formed in registers and quantized to MXFP8
 //              along the intermediate axis (a 32-row MFMA tile is one block)
 //              straight into the down product's operand.
 //   kMxDown  : d[r][n] = sum_i Wd_e[n][i] hq[r][i] for the expert's grouped rows r.
-template <int MODE>
-__global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
+template <int MODE, int TM>
+__global__ void __launch_bounds__(MxShape<TM>::kThreads, 4) mx_gemm_kernel(MxArgs p) {
+  using S = MxShape<TM>;
   // three separate LDS objects, so that the compiler's wait tracking for
   // the copies tells them apart: an access to one ring stage waits only for
   // the copies into that stage
-  __shared__ MxStageLds R0, R1, R2;
+  __shared__ MxStageLds<TM> R0, R1, R2;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,7 +302,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     int tx, ty;
     if (!mx_tile_of_block(blockIdx.x, p.gx, p.gy, &tx, &ty)) return;   // block-uniform
     n0 = (int64_t)tx * kBN;
-    m0 = (int64_t)ty * kBM;
+    m0 = (int64_t)ty * TM;
   } else {
     // gy = the launch's upper bound on token tiles; the XCD-grouped order
     // keeps the token tiles of one expert and row tile on one XCD's L2
@@ -292,7 +315,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
       if (p.tile_off[mid] <= T) lo = mid; else hi = mid;
     }
     e = lo;
-    r0 = p.row_off[e] + (T - p.tile_off[e]) * kBM;
+    r0 = p.row_off[e] + (T - p.tile_off[e]) * TM;
     r_end = p.row_off[e + 1];
     wc += (int64_t)e * p.stride_c;
     wsm += (int64_t)e * stages_k * p.N;
@@ -326,7 +349,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     const int gr = r0 + t;
     return gr < r_end ? gr : r_end - 1;
   };
-  MxRows rows;
+  MxRows<TM> rows;
   rows.abase = wc;
   rows.bbase = p.xc;
   rows.wsm = wsm;
@@ -335,32 +358,36 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   rows.xrows = (uint32_t)p.xrows;
   rows.stages = stages_k;
 #pragma unroll
-  for (int i = 0; i < kDmaA; ++i) {
-    const int r = 16 * (kDmaA * wave + i) + (lane >> 2);     // slot 64 c + lane = 4 r + (lane & 3)
+  for (int i = 0; i < S::kDmaA; ++i) {
+    const int r = 16 * (S::kDmaA * wave + i) + (lane >> 2);  // slot 64 c + lane = 4 r + (lane & 3)
     rows.a[i] = (uint32_t)(a_row(r) * (K >> 1));
     rows.qa[i] = (uint32_t)((lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3));
   }
 #pragma unroll
-  for (int i = 0; i < kDmaB; ++i) {
-    const int t = 8 * (kDmaB * wave + i) + (lane >> 3);      // slot 64 c + lane = 8 t + (lane & 7)
+  for (int i = 0; i < S::kDmaB; ++i) {
+    const int t = 8 * (S::kDmaB * wave + i) + (lane >> 3);   // slot 64 c + lane = 8 t + (lane & 7)
     rows.b[i] = (uint32_t)(b_row(t) * K);
     rows.pb[i] = (uint32_t)((lane & 7) ^ ((t ^ (t >> 3)) & 7));
   }
-  rows.sa = (uint32_t)a_row(64 * wave + lane);
-  rows.sb = (uint32_t)b_srow(lane);
+  rows.sa = (uint32_t)a_row(64 * (wave & 3) + lane);
+  rows.sb = (uint32_t)b_srow(64 * ((wave + 4) % (TM / 64)) + lane);
 
   // the wave's A tiles: block rows arow(a) + j; gate_up pairs tile a (gate)
   // with tile a + 2 (up) over the same intermediate rows
-  const int wt = (wave >> 1) * 32 * kNB;           // the wave's first token slot
+  // wave = (row group rg, token group): kTA tiles of 32 rows, 32 tokens;
+  // gate_up: tiles a < kTA / 2 are gate rows, a + kTA / 2 the matching up rows
+  const int rg = wave % kRowGroups;
+  const int wt = (wave / kRowGroups) * 32 * kNB;   // the wave's first token slot
   auto arow = [&](int a) {
-    return MODE == kMxGateUp ? (a >> 1) * 128 + (wave & 1) * 64 + 32 * (a & 1) : (wave & 1) * 128 + 32 * a;
+    return MODE == kMxGateUp ? (a >= kTA / 2 ? 128 : 0) + rg * 16 * kTA + 32 * (a % (kTA / 2))
+                             : rg * 32 * kTA + 32 * a;
   };
   // byte q of a scale word
   auto word_byte = [](uint32_t w, int q) -> int { return (int)((w >> (8 * q)) & 0xFFu); };
 
-  v16f acc[4][kNB];
+  v16f acc[kTA][kNB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kTA; ++a)
 #pragma unroll
     for (int b = 0; b < kNB; ++b)
 #pragma unroll
@@ -369,18 +396,18 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   // stage s's MFMAs from LDS stage d.  TAIL: a last stage with kval < 4 of
   // its 32-blocks inside K; the weights of the others are masked to zero
   // (bitwise, so that no select turns into a branch around the LDS read).
-  auto compute = [&](const MxStageLds& d, int s, auto tail) {
+  auto compute = [&](const MxStageLds<TM>& d, int s, auto tail) {
     constexpr bool TAIL = decltype(tail)::value;   // std::bool_constant
     const int kval = kblocks - 4 * s;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (TAIL && ks == 1 && kval <= 2) break;         // block-uniform
-      v8i A[4], B[kNB];
-      int sa[4], sb[kNB];
+      v8i A[kTA], B[kNB];
+      int sa[kTA], sb[kNB];
       const int pa = 2 * ks + h;
       const uint32_t keep = TAIL ? 0u - (uint32_t)(pa < kval) : ~0u;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < kTA; ++a) {
         const int r = arow(a) + j;
         const uint4 q = d.a[a_slot(r, pa)];
         A[a][0] = (int)(q.x & keep);
@@ -408,7 +435,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
         if (TAIL && 2 * ks + h >= kval) sb[b] = 127;
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < kTA; ++a)
 #pragma unroll
         for (int b = 0; b < kNB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[a], B[b], acc[a][b], 4, 0, 0, sa[a], 0,
@@ -425,12 +452,13 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
   // next step's MFMAs.  The loop runs the full stages; a last, partial
   // stage is computed after it.  Stages past K are loaded clamped and never
   // used; the exit waits for all copies.
+  constexpr int kDmaPerStage = S::kDmaPerStage;
   constexpr int kWaitLastStage = 0x0F70 | (kDmaPerStage & 15) | ((kDmaPerStage >> 4) << 14);   // gfx9 vmcnt(n)
   static_assert(kDmaPerStage < 64, "vmcnt holds 6 bits");
   const int full = kblocks / 4;
-  auto issue = [&](MxStageLds& d, int s) {
+  auto issue = [&](MxStageLds<TM>& d, int s) {
     __builtin_amdgcn_sched_barrier(0);
-    mx_stage_dma(d, rows, K, s, wave);
+    mx_stage_dma<TM>(d, rows, K, s, wave);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto wait_for_all_but_last_stage = [&]() {
@@ -438,7 +466,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     __builtin_amdgcn_s_waitcnt(kWaitLastStage);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto step = [&](int s, const MxStageLds& cur, MxStageLds& load) {
+  auto step = [&](int s, const MxStageLds<TM>& cur, MxStageLds<TM>& load) {
     issue(load, s + 2);
     compute(cur, s, std::false_type{});
     wait_for_all_but_last_stage();
@@ -472,13 +500,13 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
       const int gr = r0 + wt + 32 * b + j;
       const bool row_ok = gr < r_end;
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int64_t i0 = n0 + (wave & 1) * 64 + 32 * a;   // first intermediate row of the tile
+      for (int a = 0; a < kTA / 2; ++a) {
+        const int64_t i0 = n0 + rg * 16 * kTA + 32 * a;      // first intermediate row of the tile
         float hv[16];
         uint32_t amax = 0, bad = 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float g = acc[a][b][r], u = acc[a + 2][b][r];
+          const float g = acc[a][b][r], u = acc[a + kTA / 2][b][r];
           hv[r] = g / (1.0f + expf(-g)) * u;
           const uint32_t ab = __float_as_uint(hv[r]) & 0x7FFFFFFFu;
           bad |= ab >= 0x7F800000u ? 1u : 0u;
@@ -520,7 +548,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
     }
     float* yrow = p.y + orow * p.N;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < kTA; ++a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t row = n0 + arow(a) + 8 * g + 4 * h;
@@ -541,25 +569,43 @@ __global__ void __launch_bounds__(kGemmThreads, 2) mx_gemm_kernel(MxArgs p) {
 
 // Stage-major scale words: dst[e][s][r] = the E8M0 bytes of K blocks
 // 4 s .. 4 s + 3 of source row src_row(r) of expert e, byte q = block 4 s + q
-// (blocks past K read 127); src_row(r) = gather[r] if given, else r.  One
-// thread per word; gridDim = (row blocks, stages, experts).
+// (blocks past K read 127); src_row(r) = gather[r] if given, else r.  A
+// block transposes 16 rows x 32 stages through LDS: it reads each row's 128
+// scale bytes with consecutive lanes on consecutive bytes, then writes the
+// words with consecutive lanes on consecutive rows.  gridDim = (row blocks
+// of 16, stage blocks of 32, experts).
 constexpr int kStageThreads = 256;
+constexpr int kStageRows = 16;
+constexpr int kStageChunk = 32;                       // stages per block: 128 scale bytes per row
+constexpr int kStagePitch = 4 * kStageChunk + 4;      // LDS bytes per row (a word of padding)
 
 __global__ void __launch_bounds__(kStageThreads)
 mx_stage_scales_kernel(const uint8_t* __restrict__ src, int64_t src_stride_e, int kblocks, int64_t rows,
-                       const int32_t* __restrict__ gather, uint32_t* __restrict__ dst) {
-  const int64_t r = (int64_t)blockIdx.x * kStageThreads + threadIdx.x;
-  if (r >= rows) return;
-  const int s = blockIdx.y, e = blockIdx.z;
-  const int64_t sr = gather ? (int64_t)gather[r] : r;
-  const uint8_t* row = src + (int64_t)e * src_stride_e + sr * kblocks;
-  uint32_t w = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int kb = 4 * s + q;
-    w |= (kb < kblocks ? (uint32_t)row[kb] : 127u) << (8 * q);
+                       const int32_t* __restrict__ gather, int stages, uint32_t* __restrict__ dst) {
+  __shared__ __align__(16) uint8_t tile[kStageRows * kStagePitch];
+  const int64_t r0 = (int64_t)blockIdx.x * kStageRows;
+  const int s0 = blockIdx.y * kStageChunk, e = blockIdx.z;
+  const uint8_t* base = src + (int64_t)e * src_stride_e;
+  for (int i = threadIdx.x; i < kStageRows * 4 * kStageChunk; i += kStageThreads) {
+    const int r = i / (4 * kStageChunk), c = i % (4 * kStageChunk);
+    const int64_t row = r0 + r;
+    const int kb = 4 * s0 + c;
+    uint32_t v = 127u;
+    if (row < rows && kb < kblocks) {
+      const int64_t sr = gather ? (int64_t)gather[row] : row;
+      v = base[sr * kblocks + kb];
+    }
+    tile[r * kStagePitch + c] = (uint8_t)v;
   }
-  dst[((int64_t)e * gridDim.y + s) * rows + r] = w;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kStageChunk * kStageRows; i += kStageThreads) {
+    const int sl = i / kStageRows, r = i % kStageRows;
+    const int s = s0 + sl;
+    const int64_t row = r0 + r;
+    if (s < stages && row < rows)
+      dst[((int64_t)e * stages + s) * rows + row] =
+          *reinterpret_cast<const uint32_t*>(tile + r * kStagePitch + 4 * sl);
+  }
 }
 
 static int64_t a256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -570,15 +616,16 @@ static int64_t mx_stages(int64_t k) { return (k / 32 + 3) / 4; }
 static int launch_stage_scales(const uint8_t* src, int64_t src_stride_e, int64_t k, int64_t rows,
                                const int32_t* gather, int E, uint32_t* dst, hipStream_t s) {
   const int64_t S = mx_stages(k);
-  const int64_t bx = (rows + kStageThreads - 1) / kStageThreads;
-  if (bx > 2147483647LL || S > 65535 || E > 65535) return BDG_E_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_stage_scales_kernel, dim3((unsigned)bx, (unsigned)S, (unsigned)E), dim3(kStageThreads), 0,
-                     s, src, src_stride_e, (int)(k / 32), rows, gather, dst);
+  const int64_t bx = (rows + kStageRows - 1) / kStageRows;
+  const int64_t by = (S + kStageChunk - 1) / kStageChunk;
+  if (bx > 2147483647LL || by > 65535 || E > 65535) return BDG_E_UNSUPPORTED;
+  hipLaunchKernelGGL(mx_stage_scales_kernel, dim3((unsigned)bx, (unsigned)by, (unsigned)E), dim3(kStageThreads), 0,
+                     s, src, src_stride_e, (int)(k / 32), rows, gather, (int)S, dst);
   return launch_status();
 }
 
 // Picks (t, j) of the M x K routing, grouped by expert: row_off / tile_off
-// (token tiles of 128 rows) per expert, row_src[r] = token of grouped row r,
+// (token tiles of tm rows) per expert, row_src[r] = token of grouped row r,
 // pick_row[t K + j] = its grouped row.  One block; counts are exact, the
 // order of one expert's rows depends on atomic timing, which changes no
 // result (every grouped row is computed on its own and the combine reads
@@ -586,7 +633,7 @@ static int launch_stage_scales(const uint8_t* src, int64_t src_stride_e, int64_t
 constexpr int kGroupThreads = 1024;
 
 __global__ void __launch_bounds__(kGroupThreads)
-moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int32_t* __restrict__ row_off,
+moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int tm, int32_t* __restrict__ row_off,
                        int32_t* __restrict__ tile_off, int32_t* __restrict__ row_src,
                        int32_t* __restrict__ pick_row) {
   __shared__ int cnt[BDG_MAX_EXPERTS];
@@ -607,7 +654,7 @@ moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int
       tile_off[e] = t;
       off[e] = r;
       r += cnt[e];
-      t += (cnt[e] + kBM - 1) / kBM;
+      t += (cnt[e] + tm - 1) / tm;
     }
     row_off[E] = r;
     tile_off[E] = t;
@@ -705,8 +752,16 @@ extern "C" int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t*
   // operand rows are addressed by 32-bit byte offsets from the base pointers
   if (w->k > (int64_t)1 << 20 || w->n * (w->k / 2) >= ((int64_t)1 << 32) || m * w->k >= ((int64_t)1 << 32))
     return BDG_E_UNSUPPORTED;
+  if (w->mx_scale_words && !aligned16(w->mx_scale_words)) return BDG_E_ALIGN;
+  // 128-token blocks (one per CU, half the weight bytes per product) when
+  // they still give every CU two rounds of blocks, else 64-token blocks
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return BDG_E_HIP;
   const int64_t gx = (w->n + kBN - 1) / kBN;
-  const int64_t gy = (m + kBM - 1) / kBM;
+  const int tm = gx * ((m + 127) / 128) >= 2 * (int64_t)cus ? 128 : 64;
+  const int64_t gy = (m + tm - 1) / tm;
   if (gx * gy + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
   const int64_t blocks = (gx * gy + 7) / 8 * 8;     // whole chunks for the 8 XCDs
   const int64_t S = mx_stages(w->k);
@@ -729,7 +784,11 @@ extern "C" int mx_gemm(const bdg_qmat* w, const uint8_t* x_codes, const uint8_t*
   a.gx = (int)gx;
   a.gy = (int)gy;
   a.y = y;
-  hipLaunchKernelGGL(mx_gemm_kernel<kMxDense>, dim3((unsigned)blocks), dim3(kGemmThreads), 0, s, a);
+  if (tm == 128)
+    hipLaunchKernelGGL((mx_gemm_kernel<kMxDense, 128>), dim3((unsigned)blocks), dim3(MxShape<128>::kThreads), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<kMxDense, 64>), dim3((unsigned)blocks), dim3(MxShape<64>::kThreads), 0, s, a);
   return launch_status();
 }
 
@@ -800,8 +859,12 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   if (st) return st;
   st = mxfp8_quantize(x, x_dtype, m, H, xq, xqs, stream);
   if (st) return st;
+  // token tiles of 128 grouped rows when the experts average 256 or more
+  // (half the weight bytes per product), else of 64 (fewer idle rows in
+  // each expert's last tile)
+  const int tm = P >= 256 * (int64_t)n_experts ? 128 : 64;
   hipLaunchKernelGGL(moe_group_picks_kernel, dim3(1), dim3(kGroupThreads), 0, s, topk_idx, (int)P, top_k,
-                     n_experts, row_off, tile_off, row_src, pick_row);
+                     n_experts, tm, row_off, tile_off, row_src, pick_row);
   st = launch_status();
   if (st) return st;
   // stage-major scale words: both weight matrices (unless staged already),
@@ -813,8 +876,8 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   if (st) return st;
   st = launch_stage_scales(xqs, 0, H, P, row_src, 1, xsm, s);
   if (st) return st;
-  // token tiles: at most one partial tile per expert beyond P / 128
-  const int64_t tiles = (P + kBM - 1) / kBM + n_experts;
+  // token tiles: at most one partial tile per expert beyond P / tm
+  const int64_t tiles = (P + tm - 1) / tm + n_experts;
   MxArgs a{};
   a.E = n_experts;
   a.row_off = row_off;
@@ -835,8 +898,11 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   a.hs = reinterpret_cast<uint8_t*>(hsm);
   a.gy = (int)tiles;
   if (tiles * a.gx + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_gemm_kernel<kMxGateUp>, dim3((unsigned)((tiles * a.gx + 7) / 8 * 8)), dim3(kGemmThreads), 0,
-                     s, a);
+  const dim3 grid_a((unsigned)((tiles * a.gx + 7) / 8 * 8));
+  if (tm == 128)
+    hipLaunchKernelGGL((mx_gemm_kernel<kMxGateUp, 128>), grid_a, dim3(MxShape<128>::kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<kMxGateUp, 64>), grid_a, dim3(MxShape<64>::kThreads), 0, s, a);
   st = launch_status();
   if (st) return st;
   // down: 256 output rows per block over the grouped h rows
@@ -856,8 +922,11 @@ extern "C" int moe_prefill_mx(const bdg_layer_desc* layer, int32_t n_experts, in
   b.y = d;
   b.gy = (int)tiles;
   if (tiles * b.gx + 8 > 2147483647LL) return BDG_E_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_gemm_kernel<kMxDown>, dim3((unsigned)((tiles * b.gx + 7) / 8 * 8)), dim3(kGemmThreads), 0,
-                     s, b);
+  const dim3 grid_b((unsigned)((tiles * b.gx + 7) / 8 * 8));
+  if (tm == 128)
+    hipLaunchKernelGGL((mx_gemm_kernel<kMxDown, 128>), grid_b, dim3(MxShape<128>::kThreads), 0, s, b);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<kMxDown, 64>), grid_b, dim3(MxShape<64>::kThreads), 0, s, b);
   st = launch_status();
   if (st) return st;
   hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)m), dim3(256), 0, s,

@@ -178,6 +178,47 @@ def test_mx_gemm_expert_shape_full(dev):
     check_gemm(y[toks], yref, den, "mx_gemm expert shape")
 
 
+def test_mx_gemm_wide_blocks_ragged(dev):
+    """Enough tiles for the 128-token blocks (17 row tiles x 32 token tiles on
+    256 CUs): ragged rows and tokens and a partial last K stage (K = 160,
+    five 32-blocks), every output against the oracle."""
+    n, m, k = 4100, 3970, 160
+    rng = np.random.default_rng(77)
+    wc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    ws = rng.integers(118, 129, (n, k // 32), dtype=np.uint8)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    c, s = quantize_dev(x, dev)
+    w = mx_weight(wc, ws, dev)
+    w.stage_mx_scales()
+    banner(f"mx_gemm wide blocks n={n} m={m} k={k}")
+    y = to_np(bdg.mx_gemm(w, dev_t(c, dev), dev_t(s, dev)))
+    yref, den = mxq.mx_gemm(wc, ws, c, s)
+    check_gemm(y, yref, den, "mx_gemm wide blocks")
+
+
+def test_mx_gemm_benchmark_size(dev):
+    """The benchmarked dense product at full size: a gpt-oss expert's gate_up
+    (5760 x 2880 MXFP4, scale words staged once) over 4096 tokens, in the
+    launch configuration the benchmark times (128-token blocks); 64 sampled
+    tokens x all rows against the oracle."""
+    cfg = synth.CONFIGS["gptoss20b_layer"]
+    w = synth.expert_weights(cfg, 0, 0)["gu"]
+    m = 4096
+    x = synth.hidden_batch(cfg, range(m))[0]
+    banner("mx_gemm 5760x2880 m=4096")
+    xt = dev_t(synth.bf16_bits_of(x), dev).view(torch.bfloat16)
+    c, s = bdg.mxfp8_quantize(xt)
+    qw = mx_weight(*w, dev)
+    qw.stage_mx_scales()
+    y = to_np(bdg.mx_gemm(qw, c, s))
+    c, s = to_np(c), to_np(s)
+    toks = np.random.default_rng(3).choice(m, 64, replace=False)
+    oc, os_ = mxq.mxfp8_quantize(x[toks])
+    assert np.array_equal(c[toks], oc) and np.array_equal(s[toks], os_)
+    yref, den = mxq.mx_gemm(*w, oc, os_)
+    check_gemm(y[toks], yref, den, "mx_gemm benchmark size")
+
+
 def test_mx_rejects_bad_args(dev):
     w = mx_weight(np.zeros((32, 32), dtype=np.uint8), np.full((32, 2), 127, dtype=np.uint8), dev)
     c = torch.zeros((4, 64), dtype=torch.uint8, device=dev)
