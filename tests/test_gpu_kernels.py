@@ -248,9 +248,10 @@ def test_router_topk(dev, E, k, H, norm):
         assert ok, msg
 
 
-@pytest.mark.parametrize("m,norm", [(64, False), (203, True)])
+@pytest.mark.parametrize("m,norm", [(64, False), (203, True), (1500, True), (4100, False), (4100, True)])
 def test_router_topk_many_tokens(dev, m, norm):
-    """Many tokens in one call (m = 64, 203): logits, picks and weights must
+    """Many tokens in one call (m = 64 and 203: blocks of one token; 1500:
+    of 4; 4100: of 16, the last one ragged): logits, picks and weights must
     equal those of one-token calls bit for bit (the same sums in the same
     order), and the logits the oracle's within the router tolerance."""
     E, k, H = 32, 4, 2880
@@ -260,7 +261,7 @@ def test_router_topk_many_tokens(dev, m, norm):
     banner(f"moe_router_topk many tokens m={m} norm={norm}")
     xt, wt = dev_t(x, dev), dev_t(w_r, dev)
     idx, wts, logits = (to_np(a) for a in bdg.moe_router_topk(xt, wt, None, k, rmsnorm=norm))
-    for t in (0, 1, 63, m - 1):
+    for t in sorted({0, 1, 5, 15, 16, 63, m // 2 + 7, m - 2, m - 1}):
         i1, w1, l1 = (to_np(a) for a in bdg.moe_router_topk(xt[t:t + 1].contiguous(), wt, None, k, rmsnorm=norm))
         assert np.array_equal(f32_bits(l1[0]), f32_bits(logits[t]))
         assert np.array_equal(i1[0], idx[t]) and np.array_equal(f32_bits(w1[0]), f32_bits(wts[t]))
