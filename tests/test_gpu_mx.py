@@ -235,11 +235,13 @@ def test_mx_rejects_bad_args(dev):
                                       None) == _lib.BDG_E_INVALID   # and so does the library
 
 
-@pytest.mark.parametrize("E,n,k", [(1, 37, 96), (3, 70, 2880), (2, 256, 4096)])
+@pytest.mark.parametrize("E,n,k", [(1, 37, 96), (3, 70, 2880), (2, 256, 4096), (2, 21, 4224), (1, 40, 8192)])
 def test_mx_stage_scales_layout(dev, E, n, k):
     """mx_stage_scales against its layout written out: word [e][s][r] holds
     row r's scale bytes of K blocks 4s .. 4s+3 (byte q = block 4s + q), 127
-    past K (K = 96: 3 blocks, one padded byte; 2880: 90 blocks, two)."""
+    past K (K = 96: 3 blocks, one padded byte; 2880: 90 blocks, two; 4224:
+    33 stages, two chunks of the staging kernel's 32, the last of one; 8192:
+    the largest K, 64 stages)."""
     rng = np.random.default_rng(E * 1000 + n + k)
     kb, S = k // 32, (k // 32 + 3) // 4
     sc = rng.integers(0, 256, (E, n, kb), dtype=np.uint8)
@@ -258,7 +260,7 @@ def test_mx_stage_scales_layout(dev, E, n, k):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("n,m,k", [(33, 5, 96), (100, 37, 2880), (257, 70, 4096)])
+@pytest.mark.parametrize("n,m,k", [(33, 5, 96), (100, 37, 2880), (257, 70, 4096), (70, 40, 4224), (70, 40, 8192)])
 def test_mx_gemm_staged_scale_words(dev, n, m, k):
     """Weights with their stage-major scale copy staged once give the same
     product, bit for bit, as the per-call staging (and the oracle's)."""
