@@ -119,7 +119,10 @@ KERNEL_KIND_PATTERNS = (          # kernel name fragment -> kind (per-launch tra
     ("moe_layer_kernel", "layer"), ("moe_gateup_kernel", "gate_up"), ("moe_gu_group_kernel", "gate_up"),
     ("moe_down_kernel", "down"), ("moe_dn_group_kernel", "down"), ("moe_route", "route"),
     ("moe_combine_kernel", "combine"), ("moe_gu_mfma_kernel", "gate_up"), ("moe_dn_mfma_kernel", "down"),
-    ("qgemv_kernel", "qgemv"), ("attn_split_kernel", "attn_split"),
+    ("qgemv_kernel", "qgemv"),
+    # the split kernel's one-block form (every cached key in one block, merged in place)
+    ("attn_split_kernel<unsigned short, true>", "attn_fused"), ("attn_split_kernel<float, true>", "attn_fused"),
+    ("attn_split_kernel", "attn_split"),
     ("attn_merge_kernel", "attn_merge"), ("mx_gemm_kernel", "mx_gemm"), ("mxfp8_quant_kernel", "mx_quant"),
     ("mx_stage_scales_kernel", "mx_stage"),
     ("stream_copy_kernel", "copy"),
@@ -1078,7 +1081,17 @@ def kernel_figures(bdg, acc, launch_bytes, replay_us_per_step, steps):
     return kernels, gap_us, dispatch_us
 
 
-def kernel_pass(bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, replay_us_per_step):
+def self_routed_launches(cfg, route_every_layer, gate_up_per_step, route_per_step):
+    """gate_up launches per step that compute their layer's router inside the
+    launch (and read its router weights): layers after the first that would
+    otherwise launch the route kernel - more than 64 experts, or every layer
+    routed on its own - unless a down kernel hands the next layer its router
+    sums (a stack of <= 64 experts)."""
+    down_routes = cfg.norm and cfg.n_layers > 1 and cfg.n_experts <= 64 and not route_every_layer
+    return 0.0 if down_routes else max(0.0, gate_up_per_step - route_per_step)
+
+
+def kernel_pass(bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, replay_us_per_step, route_every_layer=False):
     """Per-kernel figures over the K steps after W: the same kernels and
     grids launched directly, each dispatch with start/stop events (see
     kernel_figures; replay_us_per_step is the graph replay's step time, or
@@ -1090,7 +1103,11 @@ def kernel_pass(bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, replay_us_
     for s in range(W, W + K):
         x_buf.copy_(x_all[s])
         acc = bdg.moe_expert_decode_profiled(plan, x_buf, y_buf, acc)
-    gu_launch_bytes = int(round(mean_uniq * gu_bytes))
+    # a self-routing gate_up launch also reads its layer's router weights
+    per_step = {k: acc.count[i] / K for i, k in enumerate(bdg.KERNEL_KINDS)}
+    sr = self_routed_launches(cfg, route_every_layer, per_step["gate_up"], per_step["route"])
+    sr_share = sr / per_step["gate_up"] if per_step["gate_up"] else 0.0
+    gu_launch_bytes = int(round(mean_uniq * gu_bytes + sr_share * router_bytes(cfg)))
     layer_launch_bytes = int(round(mean_uniq * (gu_bytes + dn_bytes)))
     dispatch_only = sum(acc.ms[i] for i in range(len(bdg.KERNEL_KINDS))) / K * 1e3
     kernels, gap_us, dispatch_us = kernel_figures(
@@ -1128,6 +1145,10 @@ def main():
     ap.add_argument("--route-every-layer", action="store_true",
                     help="stacks: a route kernel before every layer instead of the router partial sums "
                          "from the previous down kernel (BDG_MOE_ROUTE_EVERY_LAYER): the A/B of fused routing")
+    ap.add_argument("--route-kernel", action="store_true",
+                    help="layers after the first that need their own router launch the route kernel "
+                         "instead of routing inside their gate_up launch (BDG_MOE_ROUTE_KERNEL): the "
+                         "A/B of self-routing")
     ap.add_argument("--timeline", action="store_true",
                     help="one-token stacks: phase timeline of the fused per-layer kernel (per-block clock "
                          "stamps of moe_expert_decode_timeline), summarized per phase, then exit")
@@ -1198,7 +1219,7 @@ def main():
             log(f"uploaded {l + 1}/{cfg.n_layers} layers ({time.time() - t0:.1f} s)")
     plan, _ = sdev.build_plan(cfg, dev, max_m=m, layers=layers, fused_layer=args.fused_layer or args.timeline,
                               mfma=args.mfma, route_every_layer=args.route_every_layer,
-                              use_graph=not args.kernel_pass_only)
+                              route_kernel=args.route_kernel, use_graph=not args.kernel_pass_only)
     x_all, _ = sdev.hidden_device(cfg, range((W + K) * m), dev)
     x_all = x_all.reshape(W + K, m, cfg.hidden)
     x_buf = torch.empty_like(x_all[0])
@@ -1214,7 +1235,7 @@ def main():
     if args.kernel_pass_only:
         uniq, _ = routing_stats(bdg, np, synth, plan, cfg, m, x_all, x_buf, y_buf, W, K)
         kernels, dom_kernel, dom_bytes, achieved, _, dispatch_us, _ = kernel_pass(
-            bdg, plan, cfg, x_all, x_buf, y_buf, W, K, float(np.mean(uniq)), None)
+            bdg, plan, cfg, x_all, x_buf, y_buf, W, K, float(np.mean(uniq)), None, args.route_every_layer)
         if not torch.isfinite(y_buf).all() or not plan.check():
             raise SystemExit("non-finite output or a failed in-kernel wait")
         log(f"kernel pass ({K} steps of M={m}, direct launches): {kernels}")
@@ -1241,7 +1262,8 @@ def main():
     if args.graph_only:
         log(f"graph-only run: {K} steps of M={m}, {gpu_ms / K * 1e3:.1f} us/step")
         print(json.dumps({"workload": cfg.name, "m": m, "steps": K, "us_per_step": round(gpu_ms / K * 1e3, 2),
-                          "fused_layer": bool(args.fused_layer)}), flush=True)
+                          "fused_layer": bool(args.fused_layer), "route_kernel": bool(args.route_kernel)}),
+              flush=True)
         plan.close()
         return
 
@@ -1277,7 +1299,7 @@ def main():
     log(f"per step (events around each replay): {per_step}; sync mode wall per step: {sync_mode}")
 
     kernels, dom_kernel, dom_bytes, achieved, gap_us, dispatch_us, fused = kernel_pass(
-        bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, gpu_ms / K * 1e3)
+        bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, gpu_ms / K * 1e3, args.route_every_layer)
     gu_launch_bytes = int(round(mean_uniq * gu_bytes))
     layer_launch_bytes = int(round(mean_uniq * (gu_bytes + dn_bytes)))
     log(f"per-kernel: {kernels}; dispatch time {dispatch_us:.1f} us/step of {gpu_ms / K * 1e3:.1f} replayed "
@@ -1311,6 +1333,8 @@ def main():
         config["routing"] = routing
     if args.route_every_layer:
         config["router"] = "route kernel before every layer"
+    if args.route_kernel:
+        config["router"] = "route kernel before every layer that needs its own router"
     out = {
         "metric": METRIC,
         "value": round(value, 2),

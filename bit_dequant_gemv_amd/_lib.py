@@ -31,6 +31,7 @@ BDG_MOE_ROUTE_EVERY_LAYER = 4
 BDG_MOE_PER_TOKEN = 8
 BDG_MOE_FUSED_LAYER = 16
 BDG_MOE_MFMA = 32
+BDG_MOE_ROUTE_KERNEL = 64
 BDG_MAX_M = 16
 
 # every symbol include/bdg.h declares

@@ -12,7 +12,7 @@ import torch
 from . import _lib
 from ._lib import (BDG_BF16, BDG_E_WAIT, BDG_F32, BDG_FMT_INT4G, BDG_FMT_MXFP4, BDG_MOE_NO_GRAPH,
                    BDG_MOE_PER_TOKEN, BDG_MOE_ROUTE_EVERY_LAYER, BDG_MOE_STACK, BDG_MOE_FUSED_LAYER, BDG_MOE_MFMA,
-                   BDG_OK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, Rope, check)
+                   BDG_MOE_ROUTE_KERNEL, BDG_OK, BDG_ROUTER_RMSNORM, LayerDesc, MoEDesc, QMat, Rope, check)
 
 
 def _stream():
@@ -417,7 +417,7 @@ class MoEPlan:
 
     def __init__(self, layers, hidden, inter, n_experts, top_k, fmt="mxfp4", group=32,
                  stack=True, norm_eps=1e-5, max_m=1, use_graph=True, route_every_layer=False,
-                 per_token=False, fused_layer=False, mfma=False, wait_polls=0):
+                 per_token=False, fused_layer=False, mfma=False, route_kernel=False, wait_polls=0):
         self._layers = layers
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.n_layers = len(layers)
@@ -441,7 +441,8 @@ class MoEPlan:
                  | (BDG_MOE_ROUTE_EVERY_LAYER if route_every_layer else 0)
                  | (BDG_MOE_PER_TOKEN if per_token else 0)
                  | (BDG_MOE_FUSED_LAYER if fused_layer else 0)
-                 | (BDG_MOE_MFMA if mfma else 0))
+                 | (BDG_MOE_MFMA if mfma else 0)
+                 | (BDG_MOE_ROUTE_KERNEL if route_kernel else 0))
         desc = MoEDesc(n_layers=len(layers), hidden=hidden, inter=inter, n_experts=n_experts,
                        top_k=top_k, fmt=BDG_FMT_MXFP4 if fmt == "mxfp4" else BDG_FMT_INT4G,
                        group=32 if fmt == "mxfp4" else group, flags=flags,

@@ -208,6 +208,115 @@ __device__ __forceinline__ void route_finish(RouteState<V>& rs, const RouteSrc& 
   }
 }
 
+// ---------------------------------------------------------------- router rows
+//
+// One router row against the layer input: lane l holds float4 i = elements
+// 4 (64 i + l) .. +3 of the row and of x (elements past H are skipped), and
+// adds w . x and x . x in that order.  The route kernel and a gate_up launch
+// that routes itself both call this, so their logits agree bit for bit.
+template <int NF>
+__device__ __forceinline__ void router_lane_sums(const float4 (&wv)[NF], const float4 (&xv)[NF], int H, int lane,
+                                                 float& acc, float& ss) {
+  acc = 0.f;
+  ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int h = (i * kWave + lane) * 4;
+    if (h < H) {
+      acc = __builtin_fmaf(wv[i].x, xv[i].x, acc);
+      acc = __builtin_fmaf(wv[i].y, xv[i].y, acc);
+      acc = __builtin_fmaf(wv[i].z, xv[i].z, acc);
+      acc = __builtin_fmaf(wv[i].w, xv[i].w, acc);
+      ss = __builtin_fmaf(xv[i].x, xv[i].x, ss);
+      ss = __builtin_fmaf(xv[i].y, xv[i].y, ss);
+      ss = __builtin_fmaf(xv[i].z, xv[i].z, ss);
+      ss = __builtin_fmaf(xv[i].w, xv[i].w, ss);
+    }
+  }
+}
+
+// Self-routing gate_up (layers >= 1 of a stack whose router has its own
+// kernel otherwise): the launch's first blocks compute the router rows, one
+// per wave, and publish each sum as one 64-bit word (tag << 32 | float bits)
+// with a device-coherent store; every block then waits until all E logits
+// and the sum of squares carry this token's tag.  The tag is the token's
+// sequence number, advanced by the layer-0 route kernel, so words left by an
+// earlier token never match.  No counter and no block waits on a block
+// dispatched after it (router blocks have the lowest indices of their
+// token), and the wait is bounded.
+constexpr int kSelfRouteNF = 12;     // router row float4 per lane (H <= 3072)
+
+struct SelfRoute {
+  unsigned long long* log;   // [M][E + 1]: tagged logits, slot E the sum of squares
+  const unsigned* seq;       // the token's sequence number
+  int blocks;                // blocks (per token) that compute router rows
+  int polls;                 // bound of the wait, in polls (0: give up at once)
+  unsigned* fault;           // set when a wait gives up
+  float* resid_trace;        // [M][H] or NULL: the layer input, written by router row 0
+};
+
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
+  return ((unsigned long long)tag << 32) | __float_as_uint(v);
+}
+
+// Wave 0 of a block: wait for token t's E tagged logits and sum of squares,
+// then leave them in lds_lg[0 .. E) and lds_misc[0] (lds_misc[1] = 1 when the
+// wait gave up: logits 0, the caller poisons its outputs).
+template <int V>
+__device__ __forceinline__ void self_route_wait(const SelfRoute& sr, int t, int E, unsigned tag, int lane,
+                                                float* lds_lg, float* lds_misc) {
+  const unsigned long long* row = sr.log + (int64_t)t * (E + 1);
+  float lg[V];
+  float ss = 0.f;
+  bool ok = false;
+#pragma unroll
+  for (int i = 0; i < V; ++i) lg[i] = 0.f;
+  int it = 0;
+  // first the sum of squares alone: one line per poll (reading every
+  // logit's line on each poll from every block crowded those lines and
+  // slowed the launch by about a microsecond); the router rows finish
+  // together, so this mostly waits for all of them
+  for (; it < sr.polls; ++it) {
+    const unsigned long long s = __hip_atomic_load(row + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((unsigned)(s >> 32) == tag) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  for (; it < sr.polls; ++it) {
+    bool mine = true;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      const unsigned long long v =
+          __hip_atomic_load(row + (e < E ? e : E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lg[i] = __uint_as_float((unsigned)v);
+      mine = mine && (unsigned)(v >> 32) == tag;
+    }
+    const unsigned long long s = __hip_atomic_load(row + E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ss = __uint_as_float((unsigned)s);
+    mine = mine && (unsigned)(s >> 32) == tag;
+    if (__builtin_amdgcn_ballot_w64(!mine) == 0) {
+      ok = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) lg[i] = 0.f;
+    ss = 0.f;
+    if (lane == 0) __hip_atomic_store(sr.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) lds_lg[e] = lg[i];
+  }
+  if (lane == 0) {
+    lds_misc[0] = ss;
+    lds_misc[1] = ok ? 0.f : 1.f;
+  }
+}
+
 // ---------------------------------------------------------------- down epilogue
 //
 // A block of 8 waves that owns output rows [r0, r0 + B), B <= 64, with the

@@ -66,6 +66,7 @@ struct RouteParams {
   uint16_t* xl;       // [M][H] lo = bf16(v - hi)
   int norm;
   float eps;
+  unsigned* seq;      // or NULL: the token sequence number, advanced by block (0, 0)
 };
 
 // One router row per wavefront; block b handles rows 4b .. 4b+3 of token t.
@@ -238,24 +239,15 @@ __global__ void __launch_bounds__(kWave) moe_route_direct_kernel(RouteParams p) 
       xv[i] = ldg_f4(reinterpret_cast<const float*>(p.x_in) + xoff + (h < p.H ? h : p.H - 4));
     }
   }
-  float acc = 0.f, ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    const int h = (i * kWave + lane) * 4;
-    if (h < p.H) {
-      acc = __builtin_fmaf(wv[i].x, xv[i].x, acc);
-      acc = __builtin_fmaf(wv[i].y, xv[i].y, acc);
-      acc = __builtin_fmaf(wv[i].z, xv[i].z, acc);
-      acc = __builtin_fmaf(wv[i].w, xv[i].w, acc);
-      ss = __builtin_fmaf(xv[i].x, xv[i].x, ss);
-      ss = __builtin_fmaf(xv[i].y, xv[i].y, ss);
-      ss = __builtin_fmaf(xv[i].z, xv[i].z, ss);
-      ss = __builtin_fmaf(xv[i].w, xv[i].w, ss);
-    }
-  }
+  float acc, ss;
+  router_lane_sums<NF>(wv, xv, p.H, lane, acc, ss);
   acc = wave_sum(acc);
   float* prow = p.part + (int64_t)t * (p.E + 1) * p.pstride;
   if (lane == 0) prow[(int64_t)e * p.pstride] = acc;
+  // a stack whose later layers route themselves: this launch starts a new
+  // token (its sequence number tags those layers' router sums)
+  if (p.seq && e == 0 && t == 0 && lane == 0)
+    __hip_atomic_fetch_add(p.seq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (e == 0) {
     ss = wave_sum(ss);
     if (lane == 0) prow[(int64_t)p.E * p.pstride] = ss;
@@ -283,12 +275,17 @@ struct GateUpParams {
   LayerDev L;                 // this layer's weights
   QGeom g;                    // reduction over H
   float* h_out;               // [M][K][I]
+  SelfRoute sr;               // self-routing launches (SR): router rows, tags, the wait
 };
 
 // Wave gw of token t owns the (expert slot, row pair) range
 // [P*gw/GW, P*(gw+1)/GW) of the P = K*I pairs; the grid makes it <= NP.
 // Lanes 0..31 compute the gate row i, lanes 32..63 the up row I+i.
-template <int FMT, int S, int NP, int V>
+// SR: the launch computes the layer's router itself (see SelfRoute): wave w
+// of block b < sr.blocks takes router row 4b + w of token t, and wave 0 of
+// every block waits for the token's tagged logits; the routing rule and its
+// arithmetic are the route kernel's, so the selection is bit for bit the same.
+template <int FMT, int S, int NP, int V, bool SR>
 __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   constexpr int L = 32;
   extern __shared__ float lds[];
@@ -305,7 +302,43 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   // load order: routing inputs, then x (independent of the routing), then
   // the expert weights - the in-order wait for each stays short
   RouteState<V> rs;
-  route_issue<V, kThreads>(rs, p.rt, t, lane);
+  constexpr int RNF = SR ? kSelfRouteNF : 1;
+  float4 rw[RNF], rx[RNF];
+  unsigned tag = 0;
+  int re = 0;
+  bool router_wave = false;
+  if constexpr (SR) {
+    // the router rows this wave computes come first: the wait below
+    // depends on them
+    tag = __hip_atomic_load(p.sr.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    re = blockIdx.x * kWaves + wave;
+    router_wave = (int)blockIdx.x < p.sr.blocks && re < p.E;
+    if (router_wave) {
+      const float* wr = Ld.w_r + (int64_t)re * p.H;
+      const float* xr = p.x + (int64_t)t * p.H;
+#pragma unroll
+      for (int i = 0; i < RNF; ++i) {
+        const int h = (i * kWave + lane) * 4;
+        rw[i] = ldg_f4(wr + (h < p.H ? h : p.H - 4));
+      }
+#pragma unroll
+      for (int i = 0; i < RNF; ++i) {
+        const int h = (i * kWave + lane) * 4;
+        rx[i] = ldg_f4(xr + (h < p.H ? h : p.H - 4));
+      }
+    }
+    rs.ssq = 0.f;
+    rs.my_e = 0;
+    rs.my_w = 0.f;
+    rs.r = 1.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      rs.bias[i] = p.rt.b_r ? p.rt.b_r[e < p.E ? e : p.E - 1] : 0.f;
+    }
+  } else {
+    route_issue<V, kThreads>(rs, p.rt, t, lane);
+  }
   constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // H <= 4096
   StageF32<NX> xstage;
   xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
@@ -322,6 +355,36 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   const int j0 = q0 / p.I;
   const int row0 = q0 - j0 * p.I;
 
+  float poison = 0.f;   // 1 after a self-routing wait gave up: h is NaN
+  if constexpr (SR) {
+    if (router_wave) {
+      float acc, ss;
+      router_lane_sums<RNF>(rw, rx, p.H, lane, acc, ss);
+      acc = wave_sum(acc);
+      unsigned long long* lrow = p.sr.log + (int64_t)t * (p.E + 1);
+      if (lane == 0) __hip_atomic_store(lrow + re, tagged(tag, acc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (re == 0) {
+        ss = wave_sum(ss);
+        if (lane == 0) __hip_atomic_store(lrow + p.E, tagged(tag, ss), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.sr.resid_trace) {
+#pragma unroll
+          for (int i = 0; i < RNF; ++i) {
+            const int h = (i * kWave + lane) * 4;
+            if (h < p.H) *reinterpret_cast<float4*>(p.sr.resid_trace + (int64_t)t * p.H + h) = rx[i];
+          }
+        }
+      }
+    }
+    if (wave == 0) self_route_wait<V>(p.sr, t, p.E, tag, lane, psum, red);
+    block_sync_lds();
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane + kWave * i;
+      rs.lg[i] = psum[e < p.E ? e : p.E - 1];
+    }
+    rs.ssq = red[0];
+    poison = red[1];
+  }
   route_finish<V, kThreads>(rs, p.rt, t, lane, wave, red, psum);
   const int my_e = rs.my_e;
   const float my_w = rs.my_w;
@@ -369,7 +432,11 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
       u_sel = uv;
     }
   }
-  if (lane < nq) p.h_out[(int64_t)t * P + q0 + lane] = g_sel / (1.0f + expf(-g_sel)) * u_sel;
+  if (lane < nq) {
+    float hv = g_sel / (1.0f + expf(-g_sel)) * u_sel;
+    if constexpr (SR) hv = poison != 0.f ? __uint_as_float(0x7FC00000u) : hv;
+    p.h_out[(int64_t)t * P + q0 + lane] = hv;
+  }
 }
 
 // ---------------------------------------------------------------- grouped path (M > 1)
@@ -651,6 +718,11 @@ struct bdg_plan {
   unsigned* bar;            // grid barrier words (arrivals, generation), zero at create
   unsigned* fault;          // fault word (moe_plan_check)
   int wait_polls;
+  // self-routing gate_up for layers >= 1 that need their own router (per-token kernels)
+  int self_route;
+  int sr_blocks;            // gate_up blocks per token that compute router rows
+  unsigned* seq;            // token sequence number (advanced by the layer-0 route kernel)
+  unsigned long long* sr_log;   // [L][max_m][E + 1] tagged router sums
   // grouped products on the matrix cores (BDG_MOE_MFMA, steps of m > 1)
   int mfma;
   int mfma_grid_gu, mfma_grid_dn;
@@ -740,6 +812,7 @@ static int launch_route(const bdg_plan* p, int layer, const void* x, int x_dtype
   rp.part = p->part;
   rp.pstride = p->pstride;
   rp.L = p->hl[layer];
+  if (layer == 0 && p->self_route) rp.seq = p->seq;   // a new token for the self-routing layers
   if (mfma_ops) {
     // the matrix-core path's bf16 hi/lo operands of the (normalized) input
     rp.xh = p->xh;
@@ -785,9 +858,10 @@ static RouteSrc route_src(const bdg_plan* p, int layer, int routed, int nparts, 
   return r;
 }
 
+// sr: a self-routing launch (the layer's router computed inside it), or NULL
 static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int nparts, const int32_t* idx_in,
                          const float* w_in, int32_t* topk_trace, float* wts_trace, int use_norm,
-                         hipStream_t s, Prof* prof) {
+                         hipStream_t s, Prof* prof, const SelfRoute* sr = nullptr) {
   GateUpParams gp{};
   gp.M = m;
   gp.H = p->d.hidden;
@@ -812,13 +886,24 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int np
   const size_t lds = ((size_t)(gp.g.chunks + 1) * kXStride + kWaves + psum) * sizeof(float);
   dim3 grid((unsigned)blocks, m);
   const int fmt = p->d.fmt, V = p->topk_V;
-#define BDG_GU_CASE(F, SS, VV)                                                                            \
-  if (fmt == F && p->gu_S == SS && V == VV) {                                                             \
-    BDG_LAUNCH(prof, kGateUp, (moe_gateup_kernel<F, SS, kGuPairsPerWave, VV>), grid, dim3(kThreads), lds, \
-               s, gp);                                                                                    \
-    return launch_status();                                                                               \
+  const bool self = sr != nullptr;
+  if (self) {
+    // every router row needs a wave of the launch's first blocks
+    if (routed || nparts != 1 || p->d.hidden > kSelfRouteNF * 256 || V > 4 ||
+        (int64_t)sr->blocks * kWaves < E || sr->blocks > blocks)
+      return BDG_E_UNSUPPORTED;
+    gp.sr = *sr;
   }
-#define BDG_GU_V(F, SS) BDG_GU_CASE(F, SS, 1) BDG_GU_CASE(F, SS, 2) BDG_GU_CASE(F, SS, 4) BDG_GU_CASE(F, SS, 16)
+#define BDG_GU_CASE(F, SS, VV, SR)                                                                            \
+  if (fmt == F && p->gu_S == SS && V == VV && self == SR) {                                                   \
+    BDG_LAUNCH(prof, kGateUp, (moe_gateup_kernel<F, SS, kGuPairsPerWave, VV, SR>), grid, dim3(kThreads), lds, \
+               s, gp);                                                                                        \
+    return launch_status();                                                                                   \
+  }
+#define BDG_GU_V(F, SS)                                                                                  \
+  BDG_GU_CASE(F, SS, 1, false) BDG_GU_CASE(F, SS, 2, false) BDG_GU_CASE(F, SS, 4, false)                 \
+  BDG_GU_CASE(F, SS, 16, false) BDG_GU_CASE(F, SS, 1, true) BDG_GU_CASE(F, SS, 2, true)                  \
+  BDG_GU_CASE(F, SS, 4, true)
   BDG_GU_V(kMXFP4, 1) BDG_GU_V(kMXFP4, 2) BDG_GU_V(kMXFP4, 3) BDG_GU_V(kMXFP4, 4)
   BDG_GU_V(kINT4G, 1) BDG_GU_V(kINT4G, 2) BDG_GU_V(kINT4G, 3) BDG_GU_V(kINT4G, 4)
 #undef BDG_GU_V
@@ -1097,14 +1182,17 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
   const int stack = (p->d.flags & BDG_MOE_STACK) ? 1 : 0;
   auto trace = [&](int l) { return k.resid_trace ? k.resid_trace + (int64_t)l * k.m * H : nullptr; };
   for (int l = 0; l < L; ++l) {
-    // layer l's router sums: the route kernel, or the previous down kernel
+    // layer l's router sums: the route kernel, the previous down kernel, or
+    // (self-routing) the gate_up launch itself
     const bool fused = p->fuse_route && l > 0;
+    const bool one_kernel = k.m == 1 && p->fused_ok;
+    const bool self = p->self_route && l > 0 && !fused && !one_kernel;
     int st = BDG_OK;
-    if (!fused) {
+    if (!fused && !self) {
       st = launch_route(p, l, k.x, k.x_dtype, k.m, trace(l), 1, s, prof);
       if (st) return st;
     }
-    if (k.m == 1 && p->fused_ok) {
+    if (one_kernel) {
       const bool last = l + 1 == L;
       const bool feed = !last && p->fuse_route;
       st = launch_layer(p, l, fused ? p->dn_blocks : 1, k.topk_trace ? k.topk_trace + (int64_t)l * K : nullptr,
@@ -1114,9 +1202,19 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
       if (st) return st;
       continue;
     }
+    SelfRoute sr{};
+    if (self) {
+      sr.log = p->sr_log + (size_t)l * p->d.max_m * (p->d.n_experts + 1);
+      sr.seq = p->seq;
+      sr.blocks = p->sr_blocks;
+      sr.polls = p->wait_polls;
+      sr.fault = p->fault;
+      sr.resid_trace = trace(l);
+    }
     st = launch_gateup(p, l, k.m, 0, fused ? p->dn_blocks : 1, nullptr, nullptr,
                        k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
-                       k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof);
+                       k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof,
+                       self ? &sr : nullptr);
     if (st) return st;
     const bool last = l + 1 == L;
     const bool feed = !last && p->fuse_route;
@@ -1172,7 +1270,7 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   if (d->fmt != BDG_FMT_MXFP4 && d->fmt != BDG_FMT_INT4G) return BDG_E_INVALID;
   if ((d->hidden % 32) || (d->inter % 32)) return BDG_E_INVALID;
   if ((d->flags & ~(BDG_MOE_STACK | BDG_MOE_NO_GRAPH | BDG_MOE_ROUTE_EVERY_LAYER | BDG_MOE_PER_TOKEN |
-                    BDG_MOE_FUSED_LAYER | BDG_MOE_MFMA)) != 0)
+                    BDG_MOE_FUSED_LAYER | BDG_MOE_MFMA | BDG_MOE_ROUTE_KERNEL)) != 0)
     return BDG_E_INVALID;
   if ((d->flags & BDG_MOE_STACK) && !(d->norm_eps >= 0.f)) return BDG_E_INVALID;
   if (d->top_k > BDG_MAX_TOPK || d->n_experts > BDG_MAX_EXPERTS || d->max_m > BDG_MAX_M)
@@ -1281,6 +1379,18 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->dn_geom = geom(d->inter);
   p->wait_polls = d->wait_polls == 0 ? (1 << 20) : (d->wait_polls < 0 ? 0 : d->wait_polls);
   {
+    // self-routing gate_up (layers >= 1 that would otherwise launch the
+    // route kernel): every router row needs one wave of the launch's first
+    // blocks, and a row of x fits kSelfRouteNF float4 per lane
+    p->self_route = 0;
+    p->sr_blocks = (d->n_experts + kWaves - 1) / kWaves;
+    const int64_t gu_blocks =
+        ((int64_t)d->top_k * d->inter + kWaves * kGuPairsPerWave - 1) / (kWaves * kGuPairsPerWave);
+    if (!(d->flags & BDG_MOE_ROUTE_KERNEL) && d->n_layers > 1 && !p->fuse_route &&
+        d->hidden <= kSelfRouteNF * 256 && p->topk_V <= 4 && p->sr_blocks <= gu_blocks)
+      p->self_route = 1;
+  }
+  {
     // fused per-layer kernel for one-token steps (BDG_MOE_FUSED_LAYER): one
     // block of 8 waves per CU, all blocks resident (the grid waits on
     // itself); block b < dn_blocks owns B down rows of every chosen expert.
@@ -1340,6 +1450,9 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_hbuf = off; off = align256(off + sizeof(float) * (size_t)K * I);
   const size_t o_bar = off; off = align256(off + sizeof(unsigned) * 64);
   const size_t o_fault = off; off = align256(off + sizeof(unsigned) * 64);
+  const size_t o_seq = off; off = align256(off + sizeof(unsigned) * 64);
+  const size_t o_srlog = off;
+  off = align256(off + sizeof(unsigned long long) * (p->self_route ? (size_t)d->n_layers * M * (E + 1) : 1));
   const size_t o_xh = off; off = align256(off + sizeof(uint16_t) * (size_t)M * H);
   const size_t o_xl = off; off = align256(off + sizeof(uint16_t) * (size_t)M * H);
   const size_t o_hh = off; off = align256(off + sizeof(uint16_t) * (size_t)M * K * I);
@@ -1362,6 +1475,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   p->hbuf = reinterpret_cast<float*>(base + o_hbuf);
   p->bar = reinterpret_cast<unsigned*>(base + o_bar);
   p->fault = reinterpret_cast<unsigned*>(base + o_fault);
+  p->seq = reinterpret_cast<unsigned*>(base + o_seq);
+  p->sr_log = reinterpret_cast<unsigned long long*>(base + o_srlog);
   p->xh = reinterpret_cast<uint16_t*>(base + o_xh);
   p->xl = reinterpret_cast<uint16_t*>(base + o_xl);
   p->h_hi = reinterpret_cast<uint16_t*>(base + o_hh);

@@ -188,6 +188,17 @@ typedef struct bdg_layer_desc {
                             accumulation; within the fp32 tolerance of the exact result, not
                             bit for bit with the VALU kernels.  Needs hidden and inter
                             multiples of 64 (else ignored) */
+#define BDG_MOE_ROUTE_KERNEL 64  /* steps that run per-token kernels: layers >= 1 that need their
+                                    own router (more than 64 experts, or
+                                    BDG_MOE_ROUTE_EVERY_LAYER) launch the router kernel before
+                                    gate_up.  By default such a layer routes inside its gate_up
+                                    launch instead: the launch's first blocks take one router row
+                                    per wave and publish the sums, every block waits for them (a
+                                    bounded wait, see wait_polls); same routing and results bit for
+                                    bit, one launch per layer fewer.  Self-routing needs hidden <=
+                                    3072, n_experts <= 256 and 4 * ceil(n_experts / 4) <= 24 *
+                                    ceil(top_k * inter / 24); other shapes launch the router
+                                    kernel */
 
 typedef struct bdg_moe_desc {
   int32_t n_layers;
@@ -201,9 +212,10 @@ typedef struct bdg_moe_desc {
   float norm_eps;      /* RMSNorm eps (stack only), e.g. 1e-5 */
   int32_t max_m;       /* largest m a decode call will pass, <= BDG_MAX_M */
   const bdg_layer_desc* layers;   /* n_layers entries; copied at create */
-  int32_t wait_polls;  /* bound of the fused kernel's in-kernel wait, in polls of about a
-                          microsecond: 0 = the default (2^20, about a second); a negative value
-                          makes every wait give up at once (exercises the failure path) */
+  int32_t wait_polls;  /* bound of the in-kernel waits (the fused kernel's grid barrier, a
+                          self-routing gate_up's wait for the router sums), in polls of about
+                          a microsecond: 0 = the default (2^20, about a second); a negative
+                          value makes every wait give up at once (exercises the failure path) */
 } bdg_moe_desc;
 
 typedef struct bdg_plan bdg_plan;
@@ -228,13 +240,14 @@ int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out);
 int moe_plan_destroy(bdg_plan* p);
 
 /* moe_plan_check - report and clear the plan's fault word: BDG_E_WAIT if,
- * since the last check, a bounded wait inside the fused per-layer kernel
- * gave up (the blocks that gave up wrote NaN outputs, so the step's y holds
- * NaN), else BDG_OK.  Such a wait holds a block until every block of the
- * layer has published its h; it gives up only when blocks of the grid could
- * not run (the device shared with other work for about a second) or when
- * wait_polls is negative.  Waits for the plan's work queued on `stream`
- * (synchronous). */
+ * since the last check, a bounded wait inside the fused per-layer kernel or
+ * a self-routing gate_up gave up (the blocks that gave up wrote NaN outputs,
+ * so the step's y holds NaN), else BDG_OK.  Such a wait holds a block until
+ * every block of the layer has published its h (fused kernel) or until the
+ * launch's router rows are published (self-routing); it gives up only when
+ * blocks of the grid could not run (the device shared with other work for
+ * about a second) or when wait_polls is negative.  Waits for the plan's work
+ * queued on `stream` (synchronous). */
 int moe_plan_check(bdg_plan* p, void* stream);
 
 /* moe_expert_decode - one decode step of m tokens through every layer of

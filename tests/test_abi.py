@@ -216,7 +216,7 @@ def test_plan_create_rejects_arguments_before_any_allocation():
     assert _create(d) == _lib.BDG_E_UNSUPPORTED             # past BDG_MAX_M
     d, _ = _plan_desc(H=2890)
     assert _create(d) == _lib.BDG_E_INVALID                 # H % 32
-    d, _ = _plan_desc(flags=64)
+    d, _ = _plan_desc(flags=128)
     assert _create(d) == _lib.BDG_E_INVALID                 # unknown flag
 
     def zero_stride_codes(ls):

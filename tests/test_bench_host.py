@@ -134,3 +134,35 @@ def test_summarize_sq_merges_passes(tmp_path):
     assert vals["waiting (any) / wave-cycles"] == "0.30"
     assert vals["MFMA busy, M SIMD-cycles / dispatch"] == "3.00"
     assert vals["TA busy / GUI-active cycles (mean TA)"] == "0.25"
+
+
+def test_kernel_kinds_of_rocprof_names():
+    """Trace and counter names map to the per-launch traffic keys the bench
+    reads: the attention split kernel's one-block form (merging in place) is
+    a kind of its own, and both gate_up instances (self-routing or not) are
+    gate_up."""
+    kk = bench.kernel_kind
+    assert kk("void bdg::attn_split_kernel<unsigned short, false>(bdg::AttnArgs)") == "attn_split"
+    assert kk("void bdg::attn_split_kernel<unsigned short, true>(bdg::AttnArgs)") == "attn_fused"
+    assert kk("void bdg::attn_split_kernel<float, true>(bdg::AttnArgs)") == "attn_fused"
+    assert kk("void bdg::attn_merge_kernel<float>(bdg::AttnArgs)") == "attn_merge"
+    assert kk("void bdg::moe_gateup_kernel<1, 2, 6, 2, true>(bdg::GateUpParams)") == "gate_up"
+    assert kk("void bdg::moe_gateup_kernel<0, 3, 6, 1, false>(bdg::GateUpParams)") == "gate_up"
+    assert kk("void bdg::moe_route_direct_kernel<8>(bdg::RouteParams)") == "route"
+    assert kk("void bdg::stream_copy_kernel(uint4 const*, uint4*, long)") == "copy"
+    assert kk("__amd_rocclr_copyBuffer") is None
+
+
+def test_self_routed_launches():
+    """gate_up launches per step that read their layer's router weights: none
+    when the down kernels hand on the router sums (a stack of <= 64 experts),
+    every layer after the first otherwise, none when every layer launches the
+    route kernel."""
+    cfg = types.SimpleNamespace(norm=True, n_layers=48, n_experts=128)
+    assert bench.self_routed_launches(cfg, False, 48.0, 1.0) == 47.0
+    assert bench.self_routed_launches(cfg, False, 48.0, 48.0) == 0.0       # route kernel flag
+    cfg = types.SimpleNamespace(norm=True, n_layers=24, n_experts=32)
+    assert bench.self_routed_launches(cfg, False, 24.0, 1.0) == 0.0        # router sums from the down kernel
+    assert bench.self_routed_launches(cfg, True, 24.0, 1.0) == 23.0        # every layer routed on its own
+    cfg = types.SimpleNamespace(norm=False, n_layers=1, n_experts=32)
+    assert bench.self_routed_launches(cfg, False, 1.0, 1.0) == 0.0

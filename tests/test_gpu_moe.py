@@ -86,17 +86,20 @@ def route_launches(plan, x):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4g"])
-@pytest.mark.parametrize("fuse", ["1", "0"])
+@pytest.mark.parametrize("fuse", ["1", "0", "kernel"])
 @pytest.mark.parametrize("E", [16, 96])
 @pytest.mark.parametrize("m", [1, 2])
 def test_stack_small_end_to_end(dev, fmt, fuse, E, m):
     """The per-token path of a 3-layer stack.  fuse=1: for E <= 64, layers
     after the first route from the partial router sums of the previous down
     kernel; E = 96 (more router rows than the down epilogue covers) and
-    fuse=0: every layer runs the route kernel."""
+    fuse=0: every layer after the first routes inside its gate_up launch;
+    fuse=kernel (BDG_MOE_ROUTE_KERNEL with every layer routed on its own):
+    every layer runs the route kernel."""
     cfg = small_cfg(fmt, 1100 + E, E=E, k=4, H=512, I=256, L=3, stack=True, m=m)
-    plan, layers, x, y, tr = run_and_check(cfg, dev, m, route_every_layer=fuse == "0", per_token=True)
-    assert route_launches(plan, x) == (1 if fuse == "1" and E <= 64 else cfg.n_layers)
+    plan, layers, x, y, tr = run_and_check(cfg, dev, m, route_every_layer=fuse != "1", per_token=True,
+                                           route_kernel=fuse == "kernel")
+    assert route_launches(plan, x) == (cfg.n_layers if fuse == "kernel" else 1)
     # end to end without teacher forcing on the residual (routing forced only in band)
     layers_o = [(synth.router(cfg, l)[0], None, oracle_expert_getter(cfg, l)) for l in range(3)]
     xv = synth.hidden_batch(cfg, list(range(m)))[0]
