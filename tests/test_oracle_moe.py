@@ -462,3 +462,25 @@ def test_planted_mistake_is_caught(which):
             pin_check_routing(NS(moe, check_routing=_check_routing_kth_only))
         elif which == "routing_no_range":
             pin_check_routing(NS(moe, check_routing=_check_routing_no_range))
+
+
+def test_comparison_helpers_pinned():
+    """The helpers every parity check ends in, against hand-worked values:
+    max_rel_err is max |y - ref| / den with den = 0 demanding an exact match
+    (inf otherwise) and NaN never passing a tolerance; cosine is the angle's
+    cosine (1 for two zero vectors)."""
+    y_ref = np.array([1.0, -2.0, 4.0])
+    assert moe.max_rel_err(y_ref, y_ref, np.ones(3)) == 0.0
+    # |0.5| / 2 = 0.25 beats |0.1| / 1 and |0| / 4
+    assert moe.max_rel_err([1.1, -2.0, 4.5], y_ref, [1.0, 4.0, 2.0]) == pytest.approx(0.25)
+    assert moe.max_rel_err([1.1, -2.0, 4.0], y_ref, [1.0, 0.0, 1.0]) == pytest.approx(0.1)
+    assert moe.max_rel_err([1.0, -2.5, 4.0], y_ref, [1.0, 0.0, 1.0]) == np.inf
+    r = moe.max_rel_err([1.0, np.nan, 4.0], y_ref, np.ones(3))
+    assert not (r <= 1e30)
+    assert moe.max_rel_err([], [], []) == 0.0
+    assert moe.cosine([1.0, 0.0], [3.0, 0.0]) == pytest.approx(1.0)
+    assert moe.cosine([1.0, 0.0], [-2.0, 0.0]) == pytest.approx(-1.0)
+    assert moe.cosine([1.0, 0.0], [0.0, 5.0]) == pytest.approx(0.0)
+    assert moe.cosine([1.0, 0.0], [1.0, 1.0]) == pytest.approx(1.0 / np.sqrt(2.0))
+    assert moe.cosine([[1.0, 2.0], [3.0, 4.0]], [1.0, 2.0, 3.0, 4.0]) == pytest.approx(1.0)
+    assert moe.cosine([0.0, 0.0], [0.0, 0.0]) == 1.0
