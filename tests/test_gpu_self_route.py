@@ -157,3 +157,51 @@ def test_self_route_wait_failure_is_reported(dev):
     torch.cuda.synchronize()
     assert torch.isfinite(y).all() and plan_ok.check()
     plan_ok.close()
+
+
+# (fmt, H, I, E, k): the self-routing edges.  65 experts leave 63 idle lanes
+# in the second logit half; H = 32 is one float4 of a router row on half a
+# wave; H = 3072 is the largest hidden size a router row covers.
+# (I is wide enough for the gate_up grid to hold a wave per router row.)
+EDGE_SHAPES = [("int4g", 128, 128, 65, 4), ("mxfp4", 32, 320, 100, 2), ("mxfp4", 3072, 128, 72, 4)]
+
+
+@pytest.mark.parametrize("fmt,H,I,E,k", EDGE_SHAPES)
+def test_self_route_edges(dev, fmt, H, I, E, k):
+    cfg = synth.MoEConfig(name=f"sr_edge_{fmt}_{H}_{E}", base=3900 + E, fmt=fmt, n_layers=3, hidden=H, inter=I,
+                          n_experts=E, top_k=k, group=64 if fmt == "int4g" else 32, norm=True, m=1)
+    plan_s, layers = sdev.build_plan(cfg, dev, max_m=1)
+    plan_r, _ = sdev.build_plan(cfg, dev, max_m=1, layers=layers, route_kernel=True)
+    x0, _ = sdev.hidden_device(cfg, [0], dev)
+    assert kernel_counts(plan_s, x0)["route"] == 1
+    for tok in range(3):
+        x, _ = sdev.hidden_device(cfg, [tok], dev)
+        banner(f"self-routing gate_up edge {cfg.name} token {tok}")
+        s = decode(plan_s, x)
+        r = decode(plan_r, x)
+        for a, b, what in zip(s, r, ("y", "topk", "wts", "resid")):
+            assert same_bits(a, b), f"token {tok}: {what}"
+        if tok == 0:
+            y, topk, wts, resid = s
+            for l in range(cfg.n_layers):
+                out = resid[l + 1] if l + 1 < cfg.n_layers else y
+                check_layer(cfg, l, resid[l], out, topk[l], wts[l], cfg.norm, f"{cfg.name} layer {l}")
+    assert plan_s.check()
+    plan_s.close()
+    plan_r.close()
+
+
+def test_self_route_falls_back_when_the_grid_is_too_small(dev):
+    """A gate_up grid with fewer waves than router rows (200 experts, k * I =
+    64 pairs: 3 blocks of 4 waves) keeps the route kernel before every layer."""
+    cfg = synth.MoEConfig(name="sr_fallback", base=3990, fmt="mxfp4", n_layers=3, hidden=256, inter=64,
+                          n_experts=200, top_k=1, group=32, norm=True, m=1)
+    plan, layers = sdev.build_plan(cfg, dev, max_m=1)
+    x, _ = sdev.hidden_device(cfg, [0], dev)
+    assert kernel_counts(plan, x)["route"] == cfg.n_layers
+    y, topk, wts, resid = decode(plan, x)
+    for l in range(cfg.n_layers):
+        out = resid[l + 1] if l + 1 < cfg.n_layers else y
+        check_layer(cfg, l, resid[l], out, topk[l], wts[l], cfg.norm, f"fallback layer {l}")
+    assert plan.check()
+    plan.close()
