@@ -1083,12 +1083,12 @@ def kernel_figures(bdg, acc, launch_bytes, replay_us_per_step, steps):
 
 def self_routed_launches(cfg, route_every_layer, gate_up_per_step, route_per_step):
     """gate_up launches per step that compute their layer's router inside the
-    launch (and read its router weights): layers after the first that would
-    otherwise launch the route kernel - more than 64 experts, or every layer
-    routed on its own - unless a down kernel hands the next layer its router
-    sums (a stack of <= 64 experts)."""
+    launch (and read its router weights): the layers that need a router of
+    their own - the first, and every later one unless a down kernel hands it
+    router sums (a stack of <= 64 experts) - less the route kernels launched."""
     down_routes = cfg.norm and cfg.n_layers > 1 and cfg.n_experts <= 64 and not route_every_layer
-    return 0.0 if down_routes else max(0.0, gate_up_per_step - route_per_step)
+    own = min(1.0, gate_up_per_step) if down_routes else gate_up_per_step
+    return max(0.0, own - route_per_step)
 
 
 def kernel_pass(bdg, plan, cfg, x_all, x_buf, y_buf, W, K, mean_uniq, replay_us_per_step, route_every_layer=False):

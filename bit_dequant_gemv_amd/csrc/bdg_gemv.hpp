@@ -234,6 +234,40 @@ struct StageF32 {
   }
 };
 
+// StageF32 for a bf16 source: the loads keep the raw 8-byte words, store()
+// widens them (exactly) to fp32 and writes them as StageF32::store does.
+template <int NV>
+struct StageBF16 {
+  uint2 v[NV];
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int n, int tid, int nthreads) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (i * nthreads + tid) * 4;
+      v[i] = ldg_u64(src + (idx < n ? idx : n - 4));   // in bounds; unused past n
+    }
+  }
+
+  __device__ __forceinline__ void store(float* __restrict__ lds_x, int n, int per, int region, float mult, int tid,
+                                        int nthreads) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (i * nthreads + tid) * 4;
+      if (idx < n) {
+        const int rgn = idx / per;
+        const int w = idx - rgn * per;
+        float4 o = make_float4(bf16_to_f32((uint16_t)(v[i].x & 0xFFFFu)), bf16_to_f32((uint16_t)(v[i].x >> 16)),
+                               bf16_to_f32((uint16_t)(v[i].y & 0xFFFFu)), bf16_to_f32((uint16_t)(v[i].y >> 16)));
+        o.x *= mult;
+        o.y *= mult;
+        o.z *= mult;
+        o.w *= mult;
+        *reinterpret_cast<float4*>(lds_x + rgn * region + (w >> 5) * kXStride + (w & 31)) = o;
+      }
+    }
+  }
+};
+
 // The same for a bf16 source (4 values per 8-byte load), one region.
 template <int NV>
 __device__ __forceinline__ void stage_bf16(float* __restrict__ lds_x, const uint16_t* __restrict__ src, int n,

@@ -235,12 +235,15 @@ __device__ __forceinline__ void router_lane_sums(const float4 (&wv)[NF], const f
   }
 }
 
-// Self-routing gate_up (layers >= 1 of a stack whose router has its own
-// kernel otherwise): the launch's first blocks compute the router rows, one
-// per wave, and publish each sum as one 64-bit word (tag << 32 | float bits)
-// with a device-coherent store; every block then waits until all E logits
-// and the sum of squares carry this token's tag.  The tag is the token's
-// sequence number, advanced by the layer-0 route kernel, so words left by an
+// Self-routing gate_up (a layer whose router would otherwise have a kernel
+// of its own: the first layer, and later layers the previous down kernel
+// cannot hand router sums to): the launch's first blocks compute the router
+// rows, one per wave, and publish each sum as one 64-bit word (tag << 32 |
+// float bits) with a device-coherent store; every block then waits until all
+// E logits and the sum of squares carry this token's tag.  The tag is the
+// token's sequence number, advanced once per token (by the first layer's
+// route kernel, or, when the first layer routes itself, by its down kernel,
+// the first layer tagging with the number plus one), so words left by an
 // earlier token never match.  No counter and no block waits on a block
 // dispatched after it (router blocks have the lowest indices of their
 // token), and the wait is bounded.
@@ -248,11 +251,13 @@ constexpr int kSelfRouteNF = 12;     // router row float4 per lane (H <= 3072)
 
 struct SelfRoute {
   unsigned long long* log;   // [M][E + 1]: tagged logits, slot E the sum of squares
-  const unsigned* seq;       // the token's sequence number
+  const unsigned* seq;       // the token's sequence number (tag = *seq + tag_add)
+  unsigned tag_add;          // 1 in the first layer (the number is advanced after it), else 0
   int blocks;                // blocks (per token) that compute router rows
   int polls;                 // bound of the wait, in polls (0: give up at once)
   unsigned* fault;           // set when a wait gives up
   float* resid_trace;        // [M][H] or NULL: the layer input, written by router row 0
+  float* x_copy;             // [M][H] or NULL: its fp32 copy (the first layer), written by router row 0
 };
 
 __device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {

@@ -20,6 +20,7 @@ struct DownParams {
   DownOut o;                  // combine, residual, outputs, next layer's router slice
   LayerDev L;                 // this layer's weights
   QGeom g;                    // reduction over I
+  unsigned* seq_bump;         // or NULL: the token sequence number, advanced by block (0, 0)
 };
 
 // Block (rb, t) of 8 waves: WPE = 8 / K waves per chosen expert (1 when
@@ -106,6 +107,10 @@ __global__ void __launch_bounds__(kDownWaves * kWave) moe_down_kernel(DownParams
     group(jg, e, hs);
   }
 
+  // after a self-routing first layer: the next token's tags differ from
+  // this one's (issued after every load of the block, so no wait covers it)
+  if (p.seq_bump && blockIdx.x == 0 && t == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(p.seq_bump, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (B <= kWave) {
     down_epilogue(p.o, epi, dpart, t, blockIdx.x, r0, B, lane, wave);
     return;

@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <new>
+#include <type_traits>
 
 #include "bdg_host.hpp"
 #include "bdg_moe.hpp"
@@ -271,22 +272,26 @@ struct GateUpParams {
   float* w_out;
   int32_t* topk_trace;        // [M][K] or NULL
   float* wts_trace;
-  const float* x;             // [M][H] layer input (fp32)
+  const float* x;             // [M][H] layer input: fp32, or the caller's bf16 bits (SR == 2)
   LayerDev L;                 // this layer's weights
   QGeom g;                    // reduction over H
   float* h_out;               // [M][K][I]
-  SelfRoute sr;               // self-routing launches (SR): router rows, tags, the wait
+  SelfRoute sr;               // self-routing launches (SR != 0): router rows, tags, the wait
 };
 
 // Wave gw of token t owns the (expert slot, row pair) range
 // [P*gw/GW, P*(gw+1)/GW) of the P = K*I pairs; the grid makes it <= NP.
 // Lanes 0..31 compute the gate row i, lanes 32..63 the up row I+i.
-// SR: the launch computes the layer's router itself (see SelfRoute): wave w
-// of block b < sr.blocks takes router row 4b + w of token t, and wave 0 of
-// every block waits for the token's tagged logits; the routing rule and its
-// arithmetic are the route kernel's, so the selection is bit for bit the same.
-template <int FMT, int S, int NP, int V, bool SR>
+// SR != 0: the launch computes the layer's router itself (see SelfRoute):
+// wave w of block b < sr.blocks takes router row 4b + w of token t, and wave
+// 0 of every block waits for the token's tagged logits; the routing rule and
+// its arithmetic are the route kernel's, so the selection is bit for bit the
+// same.  SR == 2: the input is the caller's bf16 x (the first layer), widened
+// exactly to fp32 as the route kernel's copy of it would be.
+template <int FMT, int S, int NP, int V, int SR>
 __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
+  constexpr bool kSR = SR != 0;
+  constexpr bool kXBF = SR == 2;
   constexpr int L = 32;
   extern __shared__ float lds[];
   float* xs = lds;                                          // [(chunks + 1) * kXStride], chunk `chunks` zero
@@ -302,29 +307,39 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   // load order: routing inputs, then x (independent of the routing), then
   // the expert weights - the in-order wait for each stays short
   RouteState<V> rs;
-  constexpr int RNF = SR ? kSelfRouteNF : 1;
+  constexpr int RNF = kSR ? kSelfRouteNF : 1;
   float4 rw[RNF], rx[RNF];
+  uint2 rxb[kXBF ? RNF : 1];   // bf16 input: the raw words, widened where they are used
   unsigned tag = 0;
   int re = 0;
   bool router_wave = false;
-  if constexpr (SR) {
+  if constexpr (kSR) {
     // the router rows this wave computes come first: the wait below
     // depends on them
-    tag = __hip_atomic_load(p.sr.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tag = __hip_atomic_load(p.sr.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + p.sr.tag_add;
     re = blockIdx.x * kWaves + wave;
     router_wave = (int)blockIdx.x < p.sr.blocks && re < p.E;
     if (router_wave) {
       const float* wr = Ld.w_r + (int64_t)re * p.H;
-      const float* xr = p.x + (int64_t)t * p.H;
 #pragma unroll
       for (int i = 0; i < RNF; ++i) {
         const int h = (i * kWave + lane) * 4;
         rw[i] = ldg_f4(wr + (h < p.H ? h : p.H - 4));
       }
+      if constexpr (kXBF) {
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(p.x) + (int64_t)t * p.H;
 #pragma unroll
-      for (int i = 0; i < RNF; ++i) {
-        const int h = (i * kWave + lane) * 4;
-        rx[i] = ldg_f4(xr + (h < p.H ? h : p.H - 4));
+        for (int i = 0; i < RNF; ++i) {
+          const int h = (i * kWave + lane) * 4;
+          rxb[i] = ldg_u64(xb + (h < p.H ? h : p.H - 4));
+        }
+      } else {
+        const float* xr = p.x + (int64_t)t * p.H;
+#pragma unroll
+        for (int i = 0; i < RNF; ++i) {
+          const int h = (i * kWave + lane) * 4;
+          rx[i] = ldg_f4(xr + (h < p.H ? h : p.H - 4));
+        }
       }
     }
     rs.ssq = 0.f;
@@ -340,8 +355,11 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
     route_issue<V, kThreads>(rs, p.rt, t, lane);
   }
   constexpr int NX = kRouteMaxF4 * kWave / kThreads;   // H <= 4096
-  StageF32<NX> xstage;
-  xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
+  std::conditional_t<kXBF, StageBF16<NX>, StageF32<NX>> xstage;
+  if constexpr (kXBF)
+    xstage.load(reinterpret_cast<const uint16_t*>(p.x) + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
+  else
+    xstage.load(p.x + (int64_t)t * p.H, p.H, threadIdx.x, kThreads);
 
   // this wave's pair range (independent of the routing: computed while the
   // routing inputs are in flight)
@@ -356,8 +374,14 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   const int row0 = q0 - j0 * p.I;
 
   float poison = 0.f;   // 1 after a self-routing wait gave up: h is NaN
-  if constexpr (SR) {
+  if constexpr (kSR) {
     if (router_wave) {
+      if constexpr (kXBF) {
+#pragma unroll
+        for (int i = 0; i < RNF; ++i)
+          rx[i] = make_float4(bf16_to_f32((uint16_t)(rxb[i].x & 0xFFFFu)), bf16_to_f32((uint16_t)(rxb[i].x >> 16)),
+                              bf16_to_f32((uint16_t)(rxb[i].y & 0xFFFFu)), bf16_to_f32((uint16_t)(rxb[i].y >> 16)));
+      }
       float acc, ss;
       router_lane_sums<RNF>(rw, rx, p.H, lane, acc, ss);
       acc = wave_sum(acc);
@@ -366,11 +390,13 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
       if (re == 0) {
         ss = wave_sum(ss);
         if (lane == 0) __hip_atomic_store(lrow + p.E, tagged(tag, ss), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.sr.resid_trace) {
+        // the layer input's trace and (first layer) its fp32 copy
 #pragma unroll
-          for (int i = 0; i < RNF; ++i) {
-            const int h = (i * kWave + lane) * 4;
-            if (h < p.H) *reinterpret_cast<float4*>(p.sr.resid_trace + (int64_t)t * p.H + h) = rx[i];
+        for (int i = 0; i < RNF; ++i) {
+          const int h = (i * kWave + lane) * 4;
+          if (h < p.H) {
+            if (p.sr.resid_trace) *reinterpret_cast<float4*>(p.sr.resid_trace + (int64_t)t * p.H + h) = rx[i];
+            if (p.sr.x_copy) *reinterpret_cast<float4*>(p.sr.x_copy + (int64_t)t * p.H + h) = rx[i];
           }
         }
       }
@@ -434,7 +460,7 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
   }
   if (lane < nq) {
     float hv = g_sel / (1.0f + expf(-g_sel)) * u_sel;
-    if constexpr (SR) hv = poison != 0.f ? __uint_as_float(0x7FC00000u) : hv;
+    if constexpr (kSR) hv = poison != 0.f ? __uint_as_float(0x7FC00000u) : hv;
     p.h_out[(int64_t)t * P + q0 + lane] = hv;
   }
 }
@@ -718,8 +744,9 @@ struct bdg_plan {
   unsigned* bar;            // grid barrier words (arrivals, generation), zero at create
   unsigned* fault;          // fault word (moe_plan_check)
   int wait_polls;
-  // self-routing gate_up for layers >= 1 that need their own router (per-token kernels)
-  int self_route;
+  // self-routing gate_up for layers that need their own router (per-token kernels):
+  // the first layer (self_route0), later layers without router sums from a down kernel
+  int self_route, self_route0;
   int sr_blocks;            // gate_up blocks per token that compute router rows
   unsigned* seq;            // token sequence number (advanced by the layer-0 route kernel)
   unsigned long long* sr_log;   // [L][max_m][E + 1] tagged router sums
@@ -858,10 +885,13 @@ static RouteSrc route_src(const bdg_plan* p, int layer, int routed, int nparts, 
   return r;
 }
 
-// sr: a self-routing launch (the layer's router computed inside it), or NULL
+// sr: a self-routing launch (the layer's router computed inside it), or NULL;
+// x_in: the caller's input (the first layer of a self-routing launch, fp32 or
+// bf16 bits), else the plan's residual buffer
 static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int nparts, const int32_t* idx_in,
                          const float* w_in, int32_t* topk_trace, float* wts_trace, int use_norm,
-                         hipStream_t s, Prof* prof, const SelfRoute* sr = nullptr) {
+                         hipStream_t s, Prof* prof, const SelfRoute* sr = nullptr, const void* x_in = nullptr,
+                         int x_bf16 = 0) {
   GateUpParams gp{};
   gp.M = m;
   gp.H = p->d.hidden;
@@ -886,24 +916,29 @@ static int launch_gateup(const bdg_plan* p, int layer, int m, int routed, int np
   const size_t lds = ((size_t)(gp.g.chunks + 1) * kXStride + kWaves + psum) * sizeof(float);
   dim3 grid((unsigned)blocks, m);
   const int fmt = p->d.fmt, V = p->topk_V;
-  const bool self = sr != nullptr;
-  if (self) {
+  // 0: routing from router sums; 1: self-routing; 2: self-routing on the caller's bf16 input
+  int srk = 0;
+  if (sr) {
     // every router row needs a wave of the launch's first blocks
     if (routed || nparts != 1 || p->d.hidden > kSelfRouteNF * 256 || V > 4 ||
         (int64_t)sr->blocks * kWaves < E || sr->blocks > blocks)
       return BDG_E_UNSUPPORTED;
     gp.sr = *sr;
+    srk = x_in && x_bf16 ? 2 : 1;
+  } else if (x_in) {
+    return BDG_E_INVALID;
   }
+  if (x_in) gp.x = static_cast<const float*>(x_in);   // bf16 bits when srk == 2
 #define BDG_GU_CASE(F, SS, VV, SR)                                                                            \
-  if (fmt == F && p->gu_S == SS && V == VV && self == SR) {                                                   \
+  if (fmt == F && p->gu_S == SS && V == VV && srk == SR) {                                                    \
     BDG_LAUNCH(prof, kGateUp, (moe_gateup_kernel<F, SS, kGuPairsPerWave, VV, SR>), grid, dim3(kThreads), lds, \
                s, gp);                                                                                        \
     return launch_status();                                                                                   \
   }
-#define BDG_GU_V(F, SS)                                                                                  \
-  BDG_GU_CASE(F, SS, 1, false) BDG_GU_CASE(F, SS, 2, false) BDG_GU_CASE(F, SS, 4, false)                 \
-  BDG_GU_CASE(F, SS, 16, false) BDG_GU_CASE(F, SS, 1, true) BDG_GU_CASE(F, SS, 2, true)                  \
-  BDG_GU_CASE(F, SS, 4, true)
+#define BDG_GU_V(F, SS)                                                                                        \
+  BDG_GU_CASE(F, SS, 1, 0) BDG_GU_CASE(F, SS, 2, 0) BDG_GU_CASE(F, SS, 4, 0) BDG_GU_CASE(F, SS, 16, 0)        \
+  BDG_GU_CASE(F, SS, 1, 1) BDG_GU_CASE(F, SS, 2, 1) BDG_GU_CASE(F, SS, 4, 1)                                  \
+  BDG_GU_CASE(F, SS, 1, 2) BDG_GU_CASE(F, SS, 2, 2) BDG_GU_CASE(F, SS, 4, 2)
   BDG_GU_V(kMXFP4, 1) BDG_GU_V(kMXFP4, 2) BDG_GU_V(kMXFP4, 3) BDG_GU_V(kMXFP4, 4)
   BDG_GU_V(kINT4G, 1) BDG_GU_V(kINT4G, 2) BDG_GU_V(kINT4G, 3) BDG_GU_V(kINT4G, 4)
 #undef BDG_GU_V
@@ -938,9 +973,11 @@ static DownOut down_out(const bdg_plan* p, int layer, int residual, float* x_out
   return o;
 }
 
+// seq_bump: the token sequence number to advance (after a self-routing first layer), or NULL
 static int launch_down(const bdg_plan* p, int layer, int m, int residual, float* x_out, float* y_out,
-                       float* trace_out, int route_next, hipStream_t s, Prof* prof) {
+                       float* trace_out, int route_next, hipStream_t s, Prof* prof, unsigned* seq_bump = nullptr) {
   DownParams dp{};
+  dp.seq_bump = seq_bump;
   dp.M = m;
   dp.H = p->d.hidden;
   dp.I = p->d.inter;
@@ -1186,7 +1223,8 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
     // (self-routing) the gate_up launch itself
     const bool fused = p->fuse_route && l > 0;
     const bool one_kernel = k.m == 1 && p->fused_ok;
-    const bool self = p->self_route && l > 0 && !fused && !one_kernel;
+    const bool self0 = l == 0 && p->self_route0 && !one_kernel;
+    const bool self = self0 || (p->self_route && l > 0 && !fused && !one_kernel);
     int st = BDG_OK;
     if (!fused && !self) {
       st = launch_route(p, l, k.x, k.x_dtype, k.m, trace(l), 1, s, prof);
@@ -1206,20 +1244,22 @@ static int enqueue_decode(const bdg_plan* p, const GraphKey& k, hipStream_t s, P
     if (self) {
       sr.log = p->sr_log + (size_t)l * p->d.max_m * (p->d.n_experts + 1);
       sr.seq = p->seq;
+      sr.tag_add = self0 ? 1u : 0u;   // the first layer's down kernel advances the number
       sr.blocks = p->sr_blocks;
       sr.polls = p->wait_polls;
       sr.fault = p->fault;
       sr.resid_trace = trace(l);
+      sr.x_copy = self0 ? p->resid[0] : nullptr;
     }
     st = launch_gateup(p, l, k.m, 0, fused ? p->dn_blocks : 1, nullptr, nullptr,
                        k.topk_trace ? k.topk_trace + (int64_t)l * k.m * K : nullptr,
                        k.wts_trace ? k.wts_trace + (int64_t)l * k.m * K : nullptr, stack, s, prof,
-                       self ? &sr : nullptr);
+                       self ? &sr : nullptr, self0 ? k.x : nullptr, k.x_dtype == BDG_BF16 ? 1 : 0);
     if (st) return st;
     const bool last = l + 1 == L;
     const bool feed = !last && p->fuse_route;
     st = launch_down(p, l, k.m, stack, last ? nullptr : p->resid[(l + 1) & 1], last ? k.y : nullptr,
-                     feed ? trace(l + 1) : nullptr, feed ? 1 : 0, s, prof);
+                     feed ? trace(l + 1) : nullptr, feed ? 1 : 0, s, prof, self0 ? p->seq : nullptr);
     if (st) return st;
   }
   return BDG_OK;
@@ -1383,12 +1423,14 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     // route kernel): every router row needs one wave of the launch's first
     // blocks, and a row of x fits kSelfRouteNF float4 per lane
     p->self_route = 0;
+    p->self_route0 = 0;
     p->sr_blocks = (d->n_experts + kWaves - 1) / kWaves;
     const int64_t gu_blocks =
         ((int64_t)d->top_k * d->inter + kWaves * kGuPairsPerWave - 1) / (kWaves * kGuPairsPerWave);
-    if (!(d->flags & BDG_MOE_ROUTE_KERNEL) && d->n_layers > 1 && !p->fuse_route &&
-        d->hidden <= kSelfRouteNF * 256 && p->topk_V <= 4 && p->sr_blocks <= gu_blocks)
-      p->self_route = 1;
+    const bool fits = !(d->flags & BDG_MOE_ROUTE_KERNEL) && d->hidden <= kSelfRouteNF * 256 && p->topk_V <= 4 &&
+                      p->sr_blocks <= gu_blocks;
+    p->self_route0 = fits ? 1 : 0;
+    p->self_route = fits && d->n_layers > 1 && !p->fuse_route ? 1 : 0;
   }
   {
     // fused per-layer kernel for one-token steps (BDG_MOE_FUSED_LAYER): one
@@ -1452,7 +1494,8 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
   const size_t o_fault = off; off = align256(off + sizeof(unsigned) * 64);
   const size_t o_seq = off; off = align256(off + sizeof(unsigned) * 64);
   const size_t o_srlog = off;
-  off = align256(off + sizeof(unsigned long long) * (p->self_route ? (size_t)d->n_layers * M * (E + 1) : 1));
+  off = align256(off + sizeof(unsigned long long) *
+                      (p->self_route || p->self_route0 ? (size_t)d->n_layers * M * (E + 1) : 1));
   const size_t o_xh = off; off = align256(off + sizeof(uint16_t) * (size_t)M * H);
   const size_t o_xl = off; off = align256(off + sizeof(uint16_t) * (size_t)M * H);
   const size_t o_hh = off; off = align256(off + sizeof(uint16_t) * (size_t)M * K * I);

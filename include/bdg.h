@@ -188,15 +188,16 @@ typedef struct bdg_layer_desc {
                             accumulation; within the fp32 tolerance of the exact result, not
                             bit for bit with the VALU kernels.  Needs hidden and inter
                             multiples of 64 (else ignored) */
-#define BDG_MOE_ROUTE_KERNEL 64  /* steps that run per-token kernels: layers >= 1 that need their
-                                    own router (more than 64 experts, or
-                                    BDG_MOE_ROUTE_EVERY_LAYER) launch the router kernel before
+#define BDG_MOE_ROUTE_KERNEL 64  /* steps that run per-token kernels: every layer that needs its own
+                                    router (the first layer; later layers with more than 64 experts,
+                                    or BDG_MOE_ROUTE_EVERY_LAYER) launches the router kernel before
                                     gate_up.  By default such a layer routes inside its gate_up
                                     launch instead: the launch's first blocks take one router row
                                     per wave and publish the sums, every block waits for them (a
-                                    bounded wait, see wait_polls); same routing and results bit for
-                                    bit, one launch per layer fewer.  Self-routing needs hidden <=
-                                    3072, n_experts <= 256 and 4 * ceil(n_experts / 4) <= 24 *
+                                    bounded wait, see wait_polls); the first layer reads the
+                                    caller's x there.  Same routing and results bit for bit, one
+                                    launch per such layer fewer.  Self-routing needs hidden <= 3072,
+                                    n_experts <= 256 and 4 * ceil(n_experts / 4) <= 24 *
                                     ceil(top_k * inter / 24); other shapes launch the router
                                     kernel */
 

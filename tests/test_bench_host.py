@@ -154,15 +154,18 @@ def test_kernel_kinds_of_rocprof_names():
 
 
 def test_self_routed_launches():
-    """gate_up launches per step that read their layer's router weights: none
-    when the down kernels hand on the router sums (a stack of <= 64 experts),
-    every layer after the first otherwise, none when every layer launches the
-    route kernel."""
+    """gate_up launches per step that read their layer's router weights: the
+    layers needing a router of their own (the first; every later one unless
+    the down kernels hand on router sums, a stack of <= 64 experts) less the
+    route kernels launched."""
     cfg = types.SimpleNamespace(norm=True, n_layers=48, n_experts=128)
-    assert bench.self_routed_launches(cfg, False, 48.0, 1.0) == 47.0
+    assert bench.self_routed_launches(cfg, False, 48.0, 0.0) == 48.0
     assert bench.self_routed_launches(cfg, False, 48.0, 48.0) == 0.0       # route kernel flag
     cfg = types.SimpleNamespace(norm=True, n_layers=24, n_experts=32)
-    assert bench.self_routed_launches(cfg, False, 24.0, 1.0) == 0.0        # router sums from the down kernel
-    assert bench.self_routed_launches(cfg, True, 24.0, 1.0) == 23.0        # every layer routed on its own
+    assert bench.self_routed_launches(cfg, False, 24.0, 0.0) == 1.0        # the first layer; sums from down after
+    assert bench.self_routed_launches(cfg, False, 24.0, 1.0) == 0.0
+    assert bench.self_routed_launches(cfg, True, 24.0, 0.0) == 24.0        # every layer routed on its own
+    assert bench.self_routed_launches(cfg, False, 0.0, 24.0) == 0.0        # fused per-layer kernel
     cfg = types.SimpleNamespace(norm=False, n_layers=1, n_experts=32)
+    assert bench.self_routed_launches(cfg, False, 1.0, 0.0) == 1.0
     assert bench.self_routed_launches(cfg, False, 1.0, 1.0) == 0.0

@@ -93,13 +93,13 @@ def test_stack_small_end_to_end(dev, fmt, fuse, E, m):
     """The per-token path of a 3-layer stack.  fuse=1: for E <= 64, layers
     after the first route from the partial router sums of the previous down
     kernel; E = 96 (more router rows than the down epilogue covers) and
-    fuse=0: every layer after the first routes inside its gate_up launch;
-    fuse=kernel (BDG_MOE_ROUTE_KERNEL with every layer routed on its own):
-    every layer runs the route kernel."""
+    fuse=0: every layer routes inside its gate_up launch (so does the first
+    layer in every case); fuse=kernel (BDG_MOE_ROUTE_KERNEL with every layer
+    routed on its own): every layer runs the route kernel."""
     cfg = small_cfg(fmt, 1100 + E, E=E, k=4, H=512, I=256, L=3, stack=True, m=m)
     plan, layers, x, y, tr = run_and_check(cfg, dev, m, route_every_layer=fuse != "1", per_token=True,
                                            route_kernel=fuse == "kernel")
-    assert route_launches(plan, x) == (cfg.n_layers if fuse == "kernel" else 1)
+    assert route_launches(plan, x) == (cfg.n_layers if fuse == "kernel" else 0)
     # end to end without teacher forcing on the residual (routing forced only in band)
     layers_o = [(synth.router(cfg, l)[0], None, oracle_expert_getter(cfg, l)) for l in range(3)]
     xv = synth.hidden_batch(cfg, list(range(m)))[0]

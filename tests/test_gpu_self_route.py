@@ -70,7 +70,7 @@ def test_self_route_equals_router_kernel_and_oracle(dev, name):
     plan_r, _ = sdev.build_plan(cfg, dev, max_m=1, layers=layers, route_every_layer=every, route_kernel=True)
     x0, _ = sdev.hidden_device(cfg, [0], dev)
     cnt_s, cnt_r = kernel_counts(plan_s, x0), kernel_counts(plan_r, x0)
-    assert cnt_s["route"] == 1 and cnt_s["gate_up"] == cfg.n_layers, f"self-routing not taken: {cnt_s}"
+    assert cnt_s["route"] == 0 and cnt_s["gate_up"] == cfg.n_layers, f"self-routing not taken: {cnt_s}"
     assert cnt_r["route"] == cfg.n_layers, cnt_r
     for tok in range(4):
         x, xv = sdev.hidden_device(cfg, [tok], dev)
@@ -105,7 +105,7 @@ def test_self_route_two_token_steps(dev):
         r = decode(plan_r, x)
         for a, b, what in zip(s, r, ("y", "topk", "wts", "resid")):
             assert same_bits(a, b), f"step {step}: {what}"
-    assert kernel_counts(plan_s, x)["route"] == 1
+    assert kernel_counts(plan_s, x)["route"] == 0
     assert plan_s.check()
     plan_s.close()
     plan_r.close()
@@ -173,7 +173,7 @@ def test_self_route_edges(dev, fmt, H, I, E, k):
     plan_s, layers = sdev.build_plan(cfg, dev, max_m=1)
     plan_r, _ = sdev.build_plan(cfg, dev, max_m=1, layers=layers, route_kernel=True)
     x0, _ = sdev.hidden_device(cfg, [0], dev)
-    assert kernel_counts(plan_s, x0)["route"] == 1
+    assert kernel_counts(plan_s, x0)["route"] == 0
     for tok in range(3):
         x, _ = sdev.hidden_device(cfg, [tok], dev)
         banner(f"self-routing gate_up edge {cfg.name} token {tok}")
@@ -205,3 +205,40 @@ def test_self_route_falls_back_when_the_grid_is_too_small(dev):
         check_layer(cfg, l, resid[l], out, topk[l], wts[l], cfg.norm, f"fallback layer {l}")
     assert plan.check()
     plan.close()
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("E,L,stack", [(32, 3, True), (128, 2, True), (32, 1, False)])
+def test_self_route_first_layer(dev, x_dtype, E, L, stack):
+    """The first layer routes inside its gate_up launch on the caller's input
+    (bf16 bits or fp32, widened exactly as the route kernel's copy) and writes
+    that copy for the down kernel's residual; its down kernel advances the
+    token number, so a single bare layer (no later layer) still tags every
+    token apart.  32 experts: later layers take router sums from the down
+    kernel; 128: every layer routes itself.  Bit for bit the route-kernel plan
+    over several tokens, within the oracle tolerance."""
+    cfg = synth.MoEConfig(name=f"sr_first_{E}_{L}_{x_dtype}", base=4100 + E + L, fmt="mxfp4", n_layers=L,
+                          hidden=2880, inter=2880, n_experts=E, top_k=4, group=32, norm=stack, m=1,
+                          x_dtype=x_dtype)
+    plan_s, layers = sdev.build_plan(cfg, dev, max_m=1)
+    plan_r, _ = sdev.build_plan(cfg, dev, max_m=1, layers=layers, route_kernel=True)
+    x0, _ = sdev.hidden_device(cfg, [0], dev)
+    assert kernel_counts(plan_s, x0)["route"] == 0
+    for tok in range(4):
+        x, xv = sdev.hidden_device(cfg, [tok], dev)
+        banner(f"self-routing first layer {cfg.name} token {tok}")
+        s = decode(plan_s, x)
+        r = decode(plan_r, x)
+        for a, b, what in zip(s, r, ("y", "topk", "wts", "resid")):
+            assert same_bits(a, b), f"token {tok}: {what}"
+        y, topk, wts, resid = s
+        assert np.array_equal(resid[0], xv)
+        if tok == 0:
+            for l in range(cfg.n_layers):
+                out = resid[l + 1] if l + 1 < cfg.n_layers else y
+                check_layer(cfg, l, resid[l], out, topk[l], wts[l], cfg.norm, f"{cfg.name} layer {l}")
+    assert plan_s.check() and plan_r.check()
+    plan_s.close()
+    plan_r.close()
+    del layers
+    torch.cuda.empty_cache()
