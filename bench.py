@@ -813,7 +813,11 @@ def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
         x_buf.copy_(x_all[t])
         acc = bdg.moe_expert_decode_profiled(plans[t % NL], x_buf, y_buf, acc)
     gu_bytes, dn_bytes = expert_bytes(cfg)
-    kernels, gap_us, _ = kernel_figures(bdg, acc, {"gate_up": cfg.top_k * gu_bytes, "down": cfg.top_k * dn_bytes,
+    # a self-routing gate_up launch also reads the layer's router weights
+    per_step = {k: acc.count[i] / K for i, k in enumerate(bdg.KERNEL_KINDS)}
+    sr = self_routed_launches(cfg, False, per_step["gate_up"], per_step["route"])
+    gu_launch = int(round(cfg.top_k * gu_bytes + (sr / per_step["gate_up"]) * router_bytes(cfg)))
+    kernels, gap_us, _ = kernel_figures(bdg, acc, {"gate_up": gu_launch, "down": cfg.top_k * dn_bytes,
                                                    "route": router_bytes(cfg)}, gpu_ms / K * 1e3, K)
     achieved = kernels["gate_up"]["GBps"]
     log(f"per-kernel: {kernels}")
@@ -825,7 +829,7 @@ def bench_layer_rotation(torch, bdg, synth, sdev, dev, cfg, args):
     out.update({"us_per_token": round(gpu_ms / K * 1e3, 2), "kernels": kernels, "cpu_baseline": cpu,
                 "roofline": {"kernel": "moe_gateup_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                              "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                             "traffic": None, "traffic_algorithmic_bytes": cfg.top_k * gu_bytes,
+                             "traffic": measured_traffic(cfg.name, "gate_up"), "traffic_algorithmic_bytes": gu_launch,
                              "duration_us": kernels["gate_up"]["share_us"], "gap_share_us": round(gap_us, 3),
                              "duration": SHARE_NOTE,
                              "achieved_kernel_only": kernels["gate_up"]["GBps_kernel_only"]}})
