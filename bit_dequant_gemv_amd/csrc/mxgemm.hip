@@ -629,8 +629,14 @@ static int launch_stage_scales(const uint8_t* src, int64_t src_stride_e, int64_t
 // pick_row[t K + j] = its grouped row.  One block; counts are exact, the
 // order of one expert's rows depends on atomic timing, which changes no
 // result (every grouped row is computed on its own and the combine reads
-// each pick's row in slot order).
+// each pick's row in slot order).  Up to kGroupLdsPicks picks, each thread
+// issues all its index loads at once (a loop that loads, then waits on an
+// LDS atomic of the loaded value, pays a round trip per pick), the experts
+// stay in LDS for the second pass, and row_src is assembled in LDS and then
+// written in order (not scattered from one CU).
 constexpr int kGroupThreads = 1024;
+constexpr int kGroupLdsPicks = 16384;
+constexpr int kGroupPer = kGroupLdsPicks / kGroupThreads;
 
 __global__ void __launch_bounds__(kGroupThreads)
 moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int tm, int32_t* __restrict__ row_off,
@@ -638,13 +644,34 @@ moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int
                        int32_t* __restrict__ pick_row) {
   __shared__ int cnt[BDG_MAX_EXPERTS];
   __shared__ int off[BDG_MAX_EXPERTS];
+  __shared__ uint16_t pe[kGroupLdsPicks];   // expert of each pick (E <= BDG_MAX_EXPERTS < 2^16)
+  __shared__ int32_t rows[kGroupLdsPicks];  // row_src, assembled
   const int tid = threadIdx.x;
+  const bool staged = P <= kGroupLdsPicks;
   for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
   __syncthreads();
-  for (int q = tid; q < P; q += kGroupThreads) {
-    int e = idx[q];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    atomicAdd(&cnt[e], 1);
+  if (staged) {
+    int ev[kGroupPer];
+#pragma unroll
+    for (int i = 0; i < kGroupPer; ++i) {
+      const int q = tid + i * kGroupThreads;
+      ev[i] = idx[q < P ? q : P - 1];        // in bounds; unused past P
+    }
+#pragma unroll
+    for (int i = 0; i < kGroupPer; ++i) {
+      const int q = tid + i * kGroupThreads;
+      if (q < P) {
+        const int e = ev[i] < 0 ? 0 : (ev[i] >= E ? E - 1 : ev[i]);
+        pe[q] = (uint16_t)e;
+        atomicAdd(&cnt[e], 1);
+      }
+    }
+  } else {
+    for (int q = tid; q < P; q += kGroupThreads) {
+      int e = idx[q];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      atomicAdd(&cnt[e], 1);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -660,12 +687,22 @@ moe_group_picks_kernel(const int32_t* __restrict__ idx, int P, int K, int E, int
     tile_off[E] = t;
   }
   __syncthreads();
-  for (int q = tid; q < P; q += kGroupThreads) {
-    int e = idx[q];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    const int r = atomicAdd(&off[e], 1);
-    row_src[r] = q / K;
-    pick_row[q] = r;
+  if (staged) {
+    for (int q = tid; q < P; q += kGroupThreads) {
+      const int r = atomicAdd(&off[pe[q]], 1);
+      rows[r] = q / K;
+      pick_row[q] = r;
+    }
+    __syncthreads();
+    for (int r = tid; r < P; r += kGroupThreads) row_src[r] = rows[r];
+  } else {
+    for (int q = tid; q < P; q += kGroupThreads) {
+      int e = idx[q];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      const int r = atomicAdd(&off[e], 1);
+      row_src[r] = q / K;
+      pick_row[q] = r;
+    }
   }
 }
 
