@@ -412,6 +412,13 @@ def test_moe_prefill_small(dev, m):
     _prefill_case(dev, "prefill_small", 8, 2, 256, 128, m, 2100 + m)
 
 
+def test_moe_prefill_many_picks(dev):
+    """More picks (4200 tokens x top-4 = 16,800) than the grouping kernel
+    assembles in LDS, so it takes its looped path; outputs of 256 sampled
+    tokens."""
+    _prefill_case(dev, "prefill_many_picks", 16, 4, 256, 128, 4200, 2150, sample=256)
+
+
 def test_moe_prefill_heavy_sharing(dev):
     """Every token on both experts: 300 grouped rows per expert (3 token tiles)."""
     _prefill_case(dev, "prefill_share", 2, 2, 384, 160, 300, 2200)
