@@ -7,17 +7,21 @@
 // 2 small-block GEMVs", dispatch-bound); running the active experts together
 // is named there as the untried lever (section 5), and the TinyTitan tracker
 // moves a layer's experts into one submission (entry D114).  Here a layer is
-// at most three kernels, each over ALL chosen experts of the layer:
+// two kernels on the per-token path (three for steps of M > 1), each over
+// ALL chosen experts of the layer:
 //   route  : the router GEMV (one router row per wavefront) and the input's
-//            sum of squares, as one slice of router partial sums; in an
-//            M = 1 stack it runs for the first layer only (or every layer
-//            when E > 64); for steps of M > 1 it also forms the layer input
-//            from the previous layer's per-pick down outputs;
-//   gate_up: adds the router slices, applies the RMSNorm scale and bias,
-//            and every wavefront computes the top-k + softmax itself; it
-//            issues the loads of all its (g, u) row pairs at once, then
-//            stages x and runs the grouped dequant-GEMV of all k experts
-//            with the SwiGLU epilogue h = silu(g) * u;
+//            sum of squares, as one slice of router partial sums; it runs
+//            for steps of M > 1 (where it also forms the layer input from
+//            the previous layer's per-pick down outputs), and on the
+//            per-token path only with BDG_MOE_ROUTE_KERNEL or the fused
+//            per-layer kernel;
+//   gate_up: adds the router slices (or, in a layer whose router no down
+//            kernel carries, computes the router rows itself: SelfRoute),
+//            applies the RMSNorm scale and bias, and every wavefront
+//            computes the top-k + softmax itself; it issues the loads of
+//            all its (g, u) row pairs at once, then stages x and runs the
+//            grouped dequant-GEMV of all k experts with the SwiGLU epilogue
+//            h = silu(g) * u;
 //   down   : one block per row block, waves split over the chosen experts:
 //            grouped dequant-GEMV over h, then the router-weighted combine
 //            and the residual add in LDS, in a fixed expert order; in a
@@ -748,7 +752,7 @@ struct bdg_plan {
   // the first layer (self_route0), later layers without router sums from a down kernel
   int self_route, self_route0;
   int sr_blocks;            // gate_up blocks per token that compute router rows
-  unsigned* seq;            // token sequence number (advanced by the layer-0 route kernel)
+  unsigned* seq;            // token sequence number (advanced once per token: see SelfRoute)
   unsigned long long* sr_log;   // [L][max_m][E + 1] tagged router sums
   // grouped products on the matrix cores (BDG_MOE_MFMA, steps of m > 1)
   int mfma;
@@ -1351,8 +1355,9 @@ extern "C" int moe_plan_create(const bdg_moe_desc* d, bdg_plan** out) {
     p->dn_blocks = (d->hidden + B - 1) / B;
     // a layer routes from the previous down kernel's partial sums when the
     // sums are small enough for every gate_up block to add them up (more
-    // than 64 experts keep the route kernel: fusing them needed fewer, taller
-    // down blocks and measured slower on the 128-expert int4 stack)
+    // than 64 experts route inside their gate_up launch instead: fusing them
+    // needed fewer, taller down blocks and measured slower on the 128-expert
+    // int4 stack)
     p->fuse_route = (d->flags & BDG_MOE_STACK) && d->n_layers > 1 && B <= kWave &&
                     p->dn_blocks <= 4 * kThreads && d->n_experts <= kDownWaves * kDnRouterPerWave &&
                     !(d->flags & BDG_MOE_ROUTE_EVERY_LAYER);
