@@ -41,30 +41,35 @@ struct GroupLoad {
 // chunk, so every load is in bounds and issued unconditionally; row_dot gives
 // such slots a neutral scale and their x registers are zero, so they add 0,
 // and results of rows past the end are never stored.
+// One slot of load_row (ld.ok and ld.zhi cleared beforehand).
+template <int FMT, int L, int S>
+__device__ __forceinline__ void load_row_slot(GroupLoad<FMT, S>& ld, const QMat& m, const QGeom& g,
+                                              int64_t row, bool row_ok, int li, int s) {
+  // offsets inside one matrix fit 32 bits (the plan checks matrix sizes)
+  const uint32_t r = row_ok ? (uint32_t)row : 0u;
+  const int c = li + L * s;
+  const bool ok = row_ok && c < g.chunks;
+  const uint32_t cc = (uint32_t)(c < g.chunks ? c : g.chunks - 1);
+  ld.ok |= (ok ? 1u : 0u) << s;
+  ld.q[s] = ldg_u128(m.codes + (r * (uint32_t)g.chunks + cc) * 16u);
+  if constexpr (FMT == kMXFP4) {
+    ld.sc[s] = ldg_u8(m.scales + (r * (uint32_t)g.chunks + cc));   // one 32-bit offset: scalar-base load
+    ld.zn[s] = 0;
+  } else {
+    const uint32_t gi = (cc * kChunkElems) / (uint32_t)g.group;
+    ld.sc[s] = ldg_u16(m.scales + (r * (uint32_t)g.groups + gi) * 2u);
+    ld.zn[s] = ldg_u8(m.zeros + (r * (uint32_t)g.zrow + (gi >> 1)));
+    ld.zhi |= (gi & 1u) << s;
+  }
+}
+
 template <int FMT, int L, int S>
 __device__ __forceinline__ void load_row(GroupLoad<FMT, S>& ld, const QMat& m, const QGeom& g,
                                          int64_t row, bool row_ok, int li) {
-  // offsets inside one matrix fit 32 bits (the plan checks matrix sizes)
-  const uint32_t r = row_ok ? (uint32_t)row : 0u;
   ld.ok = 0;
   ld.zhi = 0;
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int c = li + L * s;
-    const bool ok = row_ok && c < g.chunks;
-    const uint32_t cc = (uint32_t)(c < g.chunks ? c : g.chunks - 1);
-    ld.ok |= (ok ? 1u : 0u) << s;
-    ld.q[s] = ldg_u128(m.codes + (r * (uint32_t)g.chunks + cc) * 16u);
-    if constexpr (FMT == kMXFP4) {
-      ld.sc[s] = ldg_u8(m.scales + (r * (uint32_t)g.chunks + cc));   // one 32-bit offset: scalar-base load
-      ld.zn[s] = 0;
-    } else {
-      const uint32_t gi = (cc * kChunkElems) / (uint32_t)g.group;
-      ld.sc[s] = ldg_u16(m.scales + (r * (uint32_t)g.groups + gi) * 2u);
-      ld.zn[s] = ldg_u8(m.zeros + (r * (uint32_t)g.zrow + (gi >> 1)));
-      ld.zhi |= (gi & 1u) << s;
-    }
-  }
+  for (int s = 0; s < S; ++s) load_row_slot<FMT, L, S>(ld, m, g, row, row_ok, li, s);
 }
 
 // Mark a loaded row's registers as rewritten (an empty asm, no instruction):
@@ -161,6 +166,72 @@ __device__ __forceinline__ float row_dot(const GroupLoad<FMT, S>& ld, const XReg
     acc += chunk_contrib<FMT>(ld.q[s], sc, z, xr.v[s], xr.sum[s]);
   }
   return group_sum_last<L>(acc);
+}
+
+// row_dot of NR loaded rows against NT inputs staged in LDS (input t at
+// lds_x + t * xstride in the chunk layout, with a zero chunk at index
+// `chunks`), taken slot by slot: a slot's x values of the NT inputs are read
+// into registers once and each code chunk is decoded once for all of them.
+// Each row's slots are added in row_dot's order with row_dot's per-chunk
+// arithmetic and butterfly, so out[i][t] equals row_dot(ld[i], x_t) bit for
+// bit.  Rows whose loads were issued slot-major (every row's slot 0 first)
+// are consumed in that order, so the first slot's math waits only for the
+// first slot's loads.
+template <int FMT, int L, int S, int NR, int NT>
+__device__ __forceinline__ void rows_dot_multi(const GroupLoad<FMT, S> (&ld)[NR], const float* __restrict__ lds_x,
+                                               int xstride, int chunks, int li, float (&out)[NR][NT]) {
+  float acc[NR][NT];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = 0.f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    // one slot at a time: the scheduler would otherwise read every slot's x
+    // values up front and hold S times the registers
+    __builtin_amdgcn_sched_barrier(0);
+    const int c = li + L * s;
+    const int cc = c < chunks ? c : chunks;
+    float xv[NT][kChunkElems];
+    float xsum[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4* src = reinterpret_cast<const float4*>(lds_x + t * xstride + cc * kXStride);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = src[q];
+        xv[t][4 * q + 0] = v.x;
+        xv[t][4 * q + 1] = v.y;
+        xv[t][4 * q + 2] = v.z;
+        xv[t][4 * q + 3] = v.w;
+      }
+      xsum[t] = 0.f;
+      if constexpr (FMT == kINT4G) {
+#pragma unroll
+        for (int q = 0; q < kChunkElems; ++q) xsum[t] += xv[t][q];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const bool ok = (ld[i].ok >> s) & 1u;
+      const uint32_t sc = FMT == kMXFP4 ? ld[i].sc[s] : (ok ? ld[i].sc[s] : 0x3C00u);
+      const uint32_t z = (ld[i].zn[s] >> (((ld[i].zhi >> s) & 1u) * 4u)) & 15u;
+      // an empty asm per input count: where one kernel takes several
+      // counts on branches of its own, the decodes of the branches are no
+      // longer identical, so the compiler cannot hoist all of them above the
+      // branch (holding every decoded weight of the rows in registers)
+      uint4 q = ld[i].q[s];
+      asm volatile("; rows_dot_multi, %4 inputs" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w) : "i"(NT));
+      float dot[NT];
+      chunk_dot_multi<FMT, NT>(q, xv, dot);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[i][t] += chunk_finish<FMT>(dot[t], sc, z, xsum[t]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[i][t] = group_sum_last<L>(acc[i][t]);
 }
 
 // Lane (within its L-lane group) that holds row_dot's result.

@@ -485,6 +485,21 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
 
 constexpr int kGroupTT = 2;           // picks per chunk
 
+// f(std::integral_constant<int, n>{}) for a runtime n in [1, N]: one
+// unrolled instantiation per count.
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N > 1) {
+    if (n == N) {
+      f(std::integral_constant<int, N>{});
+      return;
+    }
+    with_count<N - 1>(n, f);
+  } else {
+    f(std::integral_constant<int, 1>{});
+  }
+}
+
 // (g, u) row pairs per wave in the grouped gate_up, and down rows per wave:
 // as many as fit 256 VGPRs with the loaded rows held across a chunk's picks.
 __host__ __device__ constexpr int gu_group_np(int fmt, int S) {
@@ -527,6 +542,7 @@ __host__ __device__ constexpr size_t group_lds_floats() { return (sizeof(GroupLd
 template <int FMT, int S, int NP, int V>
 __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p) {
   constexpr int L = 32;
+  constexpr bool kMulti = FMT == kMXFP4;                // all picks per pass (int4: one pick per pass)
   constexpr int NX = S;                                 // H <= 32 * L * S: float4 of x per thread
   extern __shared__ float lds[];
   GroupLds& gl = *reinterpret_cast<GroupLds*>(lds);
@@ -554,19 +570,27 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
     const int r0 = (item - c * p.bpc) * (kWaves * NP);
     if (r0 >= p.I) continue;                              // block-uniform
     const int e = gl.ce[c];
-    const int nt = gl.cn[c];
+    const int nt = __builtin_amdgcn_readfirstlane(gl.cn[c]);   // block-uniform: one path per chunk
     // the picks' inputs first, then the expert weights (vmcnt retires in order)
     StageF32<NX> xst[kGroupTT];
 #pragma unroll
     for (int k = 0; k < kGroupTT; ++k)
       if (k < nt) xst[k].load(p.x + (int64_t)(gl.cpk[c][k] / p.K) * p.H, p.H, threadIdx.x, kThreads);
     const int rw = r0 + wave * NP;                        // this wave's first pair
+    const QMat wm = expert_gu(Ld, e);
     GroupLoad<FMT, S> ld[NP];
+    if constexpr (kMulti) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int row = rw + i;
-      const bool ok = row < p.I;
-      load_row<FMT, L, S>(ld[i], expert_gu(Ld, e), p.g, is_up ? p.I + row : row, ok, li);
+      for (int i = 0; i < NP; ++i) ld[i].ok = ld[i].zhi = 0;
+#pragma unroll
+      for (int s = 0; s < S; ++s)                         // slot-major, the order rows_dot_multi takes them
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          load_row_slot<FMT, L, S>(ld[i], wm, p.g, is_up ? p.I + rw + i : rw + i, rw + i < p.I, li, s);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        load_row<FMT, L, S>(ld[i], wm, p.g, is_up ? p.I + rw + i : rw + i, rw + i < p.I, li);
     }
     block_sync_lds();                                     // the previous item's x reads are done
 #pragma unroll
@@ -574,17 +598,13 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
       if (k < nt) xst[k].store(xs + k * xstride, p.H, p.H, 0, gl.rt[gl.cpk[c][k] / p.K], threadIdx.x, kThreads);
     block_sync_lds();                                     // weights still in flight
     const int nq = min(max(p.I - rw, 0), NP);
-#pragma unroll 1
-    for (int k = 0; k < nt; ++k) {
-      XRegs<FMT, L, S> xr;
-      xr.load_zpad(xs + k * xstride, p.g.chunks, li);
+    // (g, u) of pair i to lane i, SwiGLU there, h of pick k stored
+    auto finish = [&](const float (&d)[NP], int k) {
       float g_sel = 0.f, u_sel = 0.f;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        pin_regs(ld[i]);
-        const float d = row_dot<FMT, L, S>(ld[i], xr);
-        const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), kRowSumLane<L>));
-        const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), L + kRowSumLane<L>));
+        const float gv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d[i]), kRowSumLane<L>));
+        const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d[i]), L + kRowSumLane<L>));
         if (lane == i) {
           g_sel = gv;
           u_sel = uv;
@@ -592,6 +612,34 @@ __global__ void __launch_bounds__(kThreads, 2) moe_gu_group_kernel(GroupParams p
       }
       if (lane < nq)
         p.h_out[(int64_t)gl.cpk[c][k] * p.I + rw + lane] = g_sel / (1.0f + expf(-g_sel)) * u_sel;
+    };
+    if constexpr (kMulti) {
+      // every pick of the chunk in one pass: each code chunk decoded once
+      with_count<kGroupTT>(nt, [&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        float d[NP][NT];
+        rows_dot_multi<FMT, L, S, NP, NT>(ld, xs, xstride, p.g.chunks, li, d);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+          float dk[NP];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) dk[i] = d[i][k];
+          finish(dk, k);
+        }
+      });
+    } else {
+#pragma unroll 1
+      for (int k = 0; k < nt; ++k) {
+        XRegs<FMT, L, S> xr;
+        xr.load_zpad(xs + k * xstride, p.g.chunks, li);
+        float d[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          pin_regs(ld[i]);
+          d[i] = row_dot<FMT, L, S>(ld[i], xr);
+        }
+        finish(d, k);
+      }
     }
   }
 }
@@ -612,6 +660,7 @@ struct DnGroupParams {
 template <int FMT, int L, int S, int NR>
 __global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams p) {
   constexpr int RPW = kWave / L;
+  constexpr bool kMulti = FMT == kMXFP4;                // all picks per pass (int4: one pick per pass)
   constexpr int NH = (L * S + 31) / 32;                // I <= 32 * L * S: float4 of h per thread
   extern __shared__ float lds[];
   int* tab = reinterpret_cast<int*>(lds);               // [1 + kGroupMaxPicks * kChunkInts]
@@ -637,34 +686,60 @@ __global__ void __launch_bounds__(kThreads, 2) moe_dn_group_kernel(DnGroupParams
     if (r0 >= p.H) continue;                              // block-uniform
     const int* ch = tab + 1 + c * kChunkInts;
     const int e = clamp_expert(ch[0], p.E);
-    const int nt = ch[1];
+    const int nt = __builtin_amdgcn_readfirstlane(ch[1]);      // block-uniform: one path per chunk
     StageF32<NH> hst[kGroupTT];
 #pragma unroll
     for (int k = 0; k < kGroupTT; ++k)
       if (k < nt) hst[k].load(p.h + (int64_t)ch[2 + k] * p.I, p.I, threadIdx.x, kThreads);
     GroupLoad<FMT, S> ld[NR];
     const QMat m = expert_dn(Ld, e);
+    if constexpr (kMulti) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int row = r0 + (i * kWaves + wave) * RPW + rr;
-      load_row<FMT, L, S>(ld[i], m, p.g, row, row < p.H, li);
+      for (int i = 0; i < NR; ++i) ld[i].ok = ld[i].zhi = 0;
+#pragma unroll
+      for (int s = 0; s < S; ++s)                         // slot-major, the order rows_dot_multi takes them
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          const int row = r0 + (i * kWaves + wave) * RPW + rr;
+          load_row_slot<FMT, L, S>(ld[i], m, p.g, row, row < p.H, li, s);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int row = r0 + (i * kWaves + wave) * RPW + rr;
+        load_row<FMT, L, S>(ld[i], m, p.g, row, row < p.H, li);
+      }
     }
     block_sync_lds();                                     // the previous item's h reads are done
 #pragma unroll
     for (int k = 0; k < kGroupTT; ++k)
       if (k < nt) hst[k].store(hs + k * hstride, p.I, p.I, 0, 1.0f, threadIdx.x, kThreads);
     block_sync_lds();                                     // weights still in flight
-#pragma unroll 1
-    for (int k = 0; k < nt; ++k) {
-      XRegs<FMT, L, S> xr;
-      xr.load_zpad(hs + k * hstride, p.g.chunks, li);
-      float* out = p.dout + (int64_t)ch[2 + k] * p.H;
+    auto store = [&](int i, int k, float d) {
+      const int row = r0 + (i * kWaves + wave) * RPW + rr;
+      if (li == kRowSumLane<L> && row < p.H) p.dout[(int64_t)ch[2 + k] * p.H + row] = d;
+    };
+    if constexpr (kMulti) {
+      // every pick of the chunk in one pass: each code chunk decoded once
+      with_count<kGroupTT>(nt, [&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        float d[NR][NT];
+        rows_dot_multi<FMT, L, S, NR, NT>(ld, hs, hstride, p.g.chunks, li, d);
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        pin_regs(ld[i]);
-        const float d = row_dot<FMT, L, S>(ld[i], xr);
-        const int row = r0 + (i * kWaves + wave) * RPW + rr;
-        if (li == kRowSumLane<L> && row < p.H) out[row] = d;
+        for (int k = 0; k < NT; ++k)
+#pragma unroll
+          for (int i = 0; i < NR; ++i) store(i, k, d[i][k]);
+      });
+    } else {
+#pragma unroll 1
+      for (int k = 0; k < nt; ++k) {
+        XRegs<FMT, L, S> xr;
+        xr.load_zpad(hs + k * hstride, p.g.chunks, li);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          pin_regs(ld[i]);
+          store(i, k, row_dot<FMT, L, S>(ld[i], xr));
+        }
       }
     }
   }
