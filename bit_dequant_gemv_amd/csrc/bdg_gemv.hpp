@@ -18,6 +18,65 @@
 
 namespace bdg {
 
+// The scaling step of chunk_contrib alone, applied to a chunk's unscaled dot
+// product (the same operations, so the same result).
+template <int FMT>
+__device__ __forceinline__ float chunk_finish(float dot, uint32_t scale_raw, uint32_t zero_nib, float xsum) {
+  if constexpr (FMT == kMXFP4) {
+    // block sum * 2^(e-127); e = 255 is NaN
+    const float r = __builtin_amdgcn_ldexpf(dot, (int)scale_raw - 127);
+    return scale_raw == 255u ? __uint_as_float(0x7FC00000u) : r;
+  } else {
+    const float s = f16_bits_to_f32((uint16_t)scale_raw);
+    const float part = dot - (float)zero_nib * xsum;
+    return part * s;
+  }
+}
+
+// Unscaled dot products of one code chunk with NT inputs at once: each code
+// pair is decoded once and used by every input.  Per input the two chains
+// and the order of their FMAs are those of fp4_chunk_dot / u4_chunk_dot, so
+// out[t] equals the single-input result bit for bit.
+template <int FMT, int NT>
+__device__ __forceinline__ void chunk_dot_multi(const uint4 q, const float (&x)[NT][kChunkElems], float (&out)[NT]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float a0[NT], a1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) a0[t] = a1[t] = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f32x2 e0, e1, e2, e3;   // elements (8d, 8d+1), (8d+2, 8d+3), (8d+4, 8d+5), (8d+6, 8d+7)
+    if constexpr (FMT == kMXFP4) {
+      e0 = fp4_pair<0>(w[d]);
+      e1 = fp4_pair<1>(w[d]);
+      e2 = fp4_pair<2>(w[d]);
+      e3 = fp4_pair<3>(w[d]);
+    } else {
+      const uint32_t lo = w[d] & 0x0F0F0F0Fu;
+      const uint32_t hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+      const f32x2 e02 = u4_pair<false>(lo), e46 = u4_pair<true>(lo);
+      const f32x2 e13 = u4_pair<false>(hi), e57 = u4_pair<true>(hi);
+      e0 = f32x2{e02.x, e13.x};
+      e1 = f32x2{e02.y, e13.y};
+      e2 = f32x2{e46.x, e57.x};
+      e3 = f32x2{e46.y, e57.y};
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      a0[t] = __builtin_fmaf(e0.x, x[t][8 * d + 0], a0[t]);
+      a1[t] = __builtin_fmaf(e0.y, x[t][8 * d + 1], a1[t]);
+      a0[t] = __builtin_fmaf(e1.x, x[t][8 * d + 2], a0[t]);
+      a1[t] = __builtin_fmaf(e1.y, x[t][8 * d + 3], a1[t]);
+      a0[t] = __builtin_fmaf(e2.x, x[t][8 * d + 4], a0[t]);
+      a1[t] = __builtin_fmaf(e2.y, x[t][8 * d + 5], a1[t]);
+      a0[t] = __builtin_fmaf(e3.x, x[t][8 * d + 6], a0[t]);
+      a1[t] = __builtin_fmaf(e3.y, x[t][8 * d + 7], a1[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) out[t] = a0[t] + a1[t];
+}
+
 // Geometry of one packed matrix family (all experts of one projection).
 struct QGeom {
   int k;          // reduction length
