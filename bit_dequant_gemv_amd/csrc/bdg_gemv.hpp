@@ -104,7 +104,7 @@ struct GroupLoad {
 template <int FMT, int L, int S>
 __device__ __forceinline__ void load_row_slot(GroupLoad<FMT, S>& ld, const QMat& m, const QGeom& g,
                                               int64_t row, bool row_ok, int li, int s) {
-  // offsets inside one matrix fit 32 bits (the plan checks matrix sizes)
+  // offsets inside one matrix fit 32 bits (check_qmat rejects n * k / 2 >= 2^32)
   const uint32_t r = row_ok ? (uint32_t)row : 0u;
   const int c = li + L * s;
   const bool ok = row_ok && c < g.chunks;
