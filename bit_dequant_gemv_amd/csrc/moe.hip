@@ -477,7 +477,9 @@ __global__ void __launch_bounds__(kThreads) moe_gateup_kernel(GateUpParams p) {
 // block routes all M tokens and builds the same deterministic list of
 // "chunks" - one expert and up to kGroupTT of its picks (token, slot) - then
 // the blocks share the (chunk, row block) items of the layer; the weights of
-// an item are loaded once and applied to each pick's input in turn.  The
+// an item are loaded once and applied to all of its picks (MXFP4: in one
+// pass, each code chunk decoded once for every pick; int4: one pick per
+// pass).  The
 // down kernel does the same over the chunk table gate_up wrote, and writes one
 // output row per pick; the weighted combine with the residual then happens
 // in the next layer's route kernel (or a final combine kernel), in slot
